@@ -1,0 +1,818 @@
+/*
+ * sg_oracle.c -- plain, slow, single-threaded CPU oracle for the sparse
+ * gradient synchronization hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file.  Only the test suite, the smoke check of the package entry
+ * and the CPU-baseline leg of the benchmark use it.  It shares no code, header,
+ * table or constant generator with the HIP library.
+ *
+ * Sources (the pages this follows; each function names its passage):
+ *   [Zen]  "Zen: Empowering Distributed Training with Sparsity-driven Data
+ *          Synchronization" (OSDI'25), digest page.
+ *   [Skip] "SkipReduce: (Interconnection) Network Sparsity to Accelerate
+ *          Distributed Machine Learning" (MICRO'25), digest page.
+ *   [Ring] CMU 15-442/642 "Machine Learning Systems: Distributed Training and
+ *          Parallelization -- Data Parallelism and Zero Redundancy
+ *          Optimization", section "Ring AllReduce", aggregation phase.
+ *
+ * Floating point: every sum is formed in IEEE double (fp64) from inputs that
+ * are converted exactly (fp32 and bf16 both embed exactly in double).  The
+ * file is compiled with -ffp-contract=off so no fused multiply-add changes a
+ * rounding.  Integer work (indices, partitions, counts, bitmaps) is exact.
+ *
+ * Pins: see tests/test_oracle_pins.py.  Every function below is pinned by at
+ * least one check that does not re-run this code (brute force, a published
+ * check value, a closed form or an invariant).  The one documented "parity
+ * unpinned" item is which hash the Zen authors actually ran: the page cites
+ * "MurmurHash 2.0" and nothing more, so h0 below is the reading that
+ * MurmurHash2 (32-bit) of the index's 4 little-endian bytes, then mod P, is
+ * that hash.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL -1
+#define ORC_ENOMEM -2
+#define ORC_EINCONSISTENT -3
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Hash and random-number definitions                                        */
+/* ------------------------------------------------------------------------ */
+
+/* MurmurHash2, 32-bit variant, written from Austin Appleby's public
+ * description (2008): multiply constant 0x5bd1e995, shift 24, 4-byte blocks
+ * read little-endian, a 1-3 byte tail, and a final three-step avalanche.
+ * [Zen] section 4 (Implementation) names MurmurHash 2.0 with per-function
+ * seeds as the hash family. */
+uint32_t orc_murmur2(const uint8_t* data, uint64_t len, uint32_t seed)
+{
+    const uint32_t m = 0x5bd1e995u;
+    uint32_t h = seed ^ (uint32_t)len;
+    while (len >= 4) {
+        uint32_t k = (uint32_t)data[0] | ((uint32_t)data[1] << 8) |
+                     ((uint32_t)data[2] << 16) | ((uint32_t)data[3] << 24);
+        k *= m;
+        k ^= k >> 24;
+        k *= m;
+        h *= m;
+        h ^= k;
+        data += 4;
+        len -= 4;
+    }
+    if (len == 3) h ^= (uint32_t)data[2] << 16;
+    if (len >= 2) h ^= (uint32_t)data[1] << 8;
+    if (len >= 1) {
+        h ^= (uint32_t)data[0];
+        h *= m;
+    }
+    h ^= h >> 13;
+    h *= m;
+    h ^= h >> 15;
+    return h;
+}
+
+/* h0: the first-level partition hash of [Zen] section 3.2 (Technique #3 and
+ * Algorithm 1, the line that picks the partition): the same function on every
+ * worker, so an index always reaches the same server. */
+uint32_t orc_h0(uint32_t idx, uint32_t seed, uint32_t P)
+{
+    uint8_t b[4];
+    b[0] = (uint8_t)(idx & 0xff);
+    b[1] = (uint8_t)((idx >> 8) & 0xff);
+    b[2] = (uint8_t)((idx >> 16) & 0xff);
+    b[3] = (uint8_t)((idx >> 24) & 0xff);
+    return orc_murmur2(b, 4, seed) % P;
+}
+
+/* h0 over an array, for tests that need many hashes at once. */
+void orc_h0_array(const uint32_t* idx, uint64_t count, uint32_t seed, uint32_t P, uint32_t* out)
+{
+    uint64_t i;
+    for (i = 0; i < count; ++i) out[i] = orc_h0(idx[i], seed, P);
+}
+
+/* SplitMix64 (Steele, Lea, Flood, OOPSLA 2014): the state advances by the
+ * golden-ratio increment and each output is the state passed through the
+ * published two-multiply mixer. */
+uint64_t orc_splitmix64_next(uint64_t* state)
+{
+    uint64_t z;
+    *state += 0x9e3779b97f4a7c15ull;
+    z = *state;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+/* The ctr-th output (0-based) of a SplitMix64 stream that starts at `seed`:
+ * advance the state ctr+1 times, mix once. */
+uint64_t orc_splitmix64_at(uint64_t seed, uint64_t ctr)
+{
+    uint64_t s = seed;
+    uint64_t i, out = 0;
+    for (i = 0; i <= ctr; ++i) out = orc_splitmix64_next(&s);
+    return out;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Small helpers                                                             */
+/* ------------------------------------------------------------------------ */
+
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double f32_to_double(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double load_val(const void* base, int dtype, uint64_t i)
+{
+    if (dtype == ORC_BF16) return bf16_to_double(((const uint16_t*)base)[i]);
+    return f32_to_double(((const uint32_t*)base)[i]);
+}
+
+/* Magnitude key of an element: the bit pattern with the sign bit cleared.
+ * For IEEE floats of one sign, the bit pattern orders like the value, so
+ * comparing these keys compares |x|. */
+static uint32_t mag_key(const void* base, int dtype, uint64_t i)
+{
+    if (dtype == ORC_BF16) return (uint32_t)(((const uint16_t*)base)[i] & 0x7fffu);
+    return ((const uint32_t*)base)[i] & 0x7fffffffu;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A1: top-k of a dense gradient into COO                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Quickselect on distinct 64-bit keys: afterwards a[r] holds the value of rank
+ * r (0-based, ascending).  Plain Lomuto partition with a middle pivot. */
+static void quickselect_u64(uint64_t* a, uint64_t n, uint64_t r)
+{
+    uint64_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        uint64_t mid = lo + (hi - lo) / 2;
+        uint64_t pivot = a[mid], t, store, i;
+        a[mid] = a[hi];
+        a[hi] = pivot;
+        store = lo;
+        for (i = lo; i < hi; ++i) {
+            if (a[i] < pivot) {
+                t = a[i];
+                a[i] = a[store];
+                a[store] = t;
+                ++store;
+            }
+        }
+        a[hi] = a[store];
+        a[store] = pivot;
+        if (store == r) return;
+        if (r < store) hi = store - 1;
+        else lo = store + 1;
+    }
+}
+
+/* Per worker, the k entries of largest |g|, emitted in ascending index order
+ * with the original signed value copied bit for bit.
+ * [Skip] section 2 (top-k sparsification keeps the largest-magnitude
+ * gradients) and [Zen] section 4 (DGC keeps the top 5%).
+ * Reading: equal magnitudes (including +0 and -0) are broken toward the lower
+ * index; this is encoded in the 64-bit key (magnitude, then complemented
+ * index), which makes every key distinct, so "the k largest keys" is a unique
+ * set. */
+int orc_topk_to_coo(const void* dense, int dtype, uint32_t n, uint64_t M, uint64_t k,
+                    uint32_t* out_idx, void* out_val)
+{
+    uint64_t* keys;
+    uint32_t w;
+    if (k > M || M > 0xffffffffull) return ORC_EINVAL;
+    if (k == 0 || n == 0) return ORC_OK;
+    keys = (uint64_t*)malloc(M * sizeof(uint64_t));
+    if (!keys) return ORC_ENOMEM;
+    for (w = 0; w < n; ++w) {
+        uint64_t i, thr, o = 0;
+        const uint64_t base = (uint64_t)w * M;
+        for (i = 0; i < M; ++i)
+            keys[i] = ((uint64_t)mag_key(dense, dtype, base + i) << 32) |
+                      (uint64_t)(0xffffffffu - (uint32_t)i);
+        /* the k-th largest key has ascending rank M - k */
+        quickselect_u64(keys, M, M - k);
+        thr = keys[M - k];
+        for (i = 0; i < M; ++i) {
+            uint64_t key = ((uint64_t)mag_key(dense, dtype, base + i) << 32) |
+                           (uint64_t)(0xffffffffu - (uint32_t)i);
+            if (key >= thr) {
+                out_idx[(uint64_t)w * k + o] = (uint32_t)i;
+                if (dtype == ORC_BF16)
+                    ((uint16_t*)out_val)[(uint64_t)w * k + o] = ((const uint16_t*)dense)[base + i];
+                else
+                    ((uint32_t*)out_val)[(uint64_t)w * k + o] = ((const uint32_t*)dense)[base + i];
+                ++o;
+            }
+        }
+        if (o != k) {
+            free(keys);
+            return ORC_EINCONSISTENT;
+        }
+    }
+    free(keys);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A2: hash partition                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Each worker's COO entries grouped by p = h0(idx), partition 0 first, the
+ * entries of one partition kept in input order.
+ * [Zen] section 3.1 (Problem 1: a map f from indices to [n] that is the same
+ * for all workers) and section 3.2 (Technique #3, Algorithm 1's first-level
+ * hash).  Reading: order inside a partition does not change the aggregate
+ * ([Zen] Technique #1 says so), so the contract fixes the stable order, which
+ * makes outputs comparable byte for byte.
+ * D is the row width (values per index); D == 0 means indices only.
+ * part_off is [n][P+1], absolute offsets into the output. */
+int orc_hash_partition(const uint32_t* idx, const void* val, int dtype, uint32_t D,
+                       const uint64_t* in_off, uint32_t n, uint32_t P, uint32_t seed,
+                       uint32_t* out_idx, void* out_val, uint64_t* part_off)
+{
+    uint32_t w, p;
+    const size_t esz = (dtype == ORC_BF16) ? 2 : 4;
+    if (P == 0) return ORC_EINVAL;
+    for (w = 0; w < n; ++w) {
+        uint64_t o = in_off[w];
+        uint64_t b = in_off[w], e = in_off[w + 1], i;
+        if (e < b) return ORC_EINVAL;
+        for (p = 0; p < P; ++p) {
+            part_off[(uint64_t)w * (P + 1) + p] = o;
+            for (i = b; i < e; ++i) {
+                if (orc_h0(idx[i], seed, P) != p) continue;
+                out_idx[o] = idx[i];
+                if (D > 0)
+                    memcpy((char*)out_val + o * D * esz, (const char*)val + i * D * esz, D * esz);
+                ++o;
+            }
+        }
+        part_off[(uint64_t)w * (P + 1) + P] = o;
+        if (o != e) return ORC_EINCONSISTENT;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A3: per-partition union-sum                                               */
+/* ------------------------------------------------------------------------ */
+
+/* For each partition p, the union of all workers' indices in that partition,
+ * ascending, each with its values summed over the workers that hold it.
+ * [Zen] section 3.1 (each server aggregates the partition it receives) and
+ * section 3.2 ("no accuracy impact": the sparse aggregate equals the dense
+ * AllReduce of the same gradients).  Written as that plain definition: a dense
+ * scatter-add over [0, M) in double, then the touched indices in order.
+ * Reading: membership means "some worker sent the index", not "the sum is
+ * non-zero"; an index whose values cancel to 0 stays in the aggregate.
+ * Outputs: agg_idx[cap], agg_val[cap*D] (double), agg_abs[cap*D] (double, the
+ * sum of |x| of the same terms, used for the tolerance), agg_off[P+1].
+ * Returns ORC_EINCONSISTENT if one index arrives in two partitions. */
+int orc_aggregate(const uint32_t* idx, const void* val, int dtype, uint32_t D,
+                  const uint64_t* part_off, uint32_t n, uint32_t P, uint64_t M,
+                  uint32_t* agg_idx, double* agg_val, double* agg_abs, uint64_t* agg_off)
+{
+    double *acc = NULL, *accabs = NULL;
+    uint32_t* owner = NULL; /* partition + 1 of a touched index, 0 if untouched */
+    uint64_t* cnt = NULL;
+    uint32_t w, p;
+    uint64_t i, d;
+    const uint32_t Dv = D ? D : 1;
+    int rc = ORC_OK;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    acc = (double*)calloc(M * Dv, sizeof(double));
+    accabs = (double*)calloc(M * Dv, sizeof(double));
+    owner = (uint32_t*)calloc(M, sizeof(uint32_t));
+    cnt = (uint64_t*)calloc(P + 1, sizeof(uint64_t));
+    if (!acc || !accabs || !owner || !cnt) {
+        rc = ORC_ENOMEM;
+        goto done;
+    }
+    for (w = 0; w < n; ++w) {
+        for (p = 0; p < P; ++p) {
+            uint64_t b = part_off[(uint64_t)w * (P + 1) + p];
+            uint64_t e = part_off[(uint64_t)w * (P + 1) + p + 1];
+            for (i = b; i < e; ++i) {
+                uint32_t x = idx[i];
+                if (x >= M) {
+                    rc = ORC_EINVAL;
+                    goto done;
+                }
+                if (owner[x] != 0 && owner[x] != p + 1) {
+                    rc = ORC_EINCONSISTENT;
+                    goto done;
+                }
+                owner[x] = p + 1;
+                for (d = 0; d < D; ++d) {
+                    double v = load_val(val, dtype, i * D + d);
+                    acc[(uint64_t)x * Dv + d] += v;
+                    accabs[(uint64_t)x * Dv + d] += fabs(v);
+                }
+            }
+        }
+    }
+    for (i = 0; i < M; ++i)
+        if (owner[i]) cnt[owner[i]]++;
+    agg_off[0] = 0;
+    for (p = 0; p < P; ++p) agg_off[p + 1] = agg_off[p] + cnt[p + 1];
+    for (p = 0; p < P; ++p) cnt[p + 1] = agg_off[p];
+    for (i = 0; i < M; ++i) {
+        uint64_t o;
+        if (!owner[i]) continue;
+        o = cnt[owner[i]]++;
+        agg_idx[o] = (uint32_t)i;
+        for (d = 0; d < D; ++d) {
+            agg_val[o * Dv + d] = acc[i * Dv + d];
+            agg_abs[o * Dv + d] = accabs[i * Dv + d];
+        }
+    }
+done:
+    free(acc);
+    free(accabs);
+    free(owner);
+    free(cnt);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A4: hash-bitmap encode (and decode, used by the pins)                     */
+/* ------------------------------------------------------------------------ */
+
+/* Class lists C_p = { idx in [0, M) : h0(idx) = p } in ascending order, as
+ * [Zen] section 3.3.2 defines them (computed once, offline, and the same for
+ * servers and workers).  Outputs: class_size[P], rank[M] = position of idx
+ * inside its class. */
+int orc_classmap(uint64_t M, uint32_t P, uint32_t seed, uint64_t* class_size, uint32_t* rank)
+{
+    uint64_t i;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    memset(class_size, 0, P * sizeof(uint64_t));
+    for (i = 0; i < M; ++i) {
+        uint32_t p = orc_h0((uint32_t)i, seed, P);
+        rank[i] = (uint32_t)class_size[p]++;
+    }
+    return ORC_OK;
+}
+
+/* Hash bitmap of [Zen] section 3.3.2 (the Fig. 10 walk-through): server p's
+ * bitmap has one bit per member of C_p, set when that member is in the
+ * server's aggregated index set.  Readings (the text fixes none of these): bit
+ * b lives in 32-bit word b/32 at bit b%32 (least significant first); bit
+ * positions are 0-based; each class's bitmap is padded with zero bits to a
+ * whole word and the classes are concatenated in order p = 0..P-1, starting at
+ * word_off[p] = sum over q < p of ceil(|C_q|/32).  Values need no re-encoding:
+ * the aggregate lists a partition's indices in ascending order, which is the
+ * order of C_p. */
+int orc_encode(const uint32_t* agg_idx, const uint64_t* agg_off, uint32_t P, uint64_t M,
+               uint32_t seed, uint32_t* bitmap, uint64_t* word_off)
+{
+    uint64_t* csize;
+    uint32_t* rank;
+    uint32_t p;
+    uint64_t i;
+    int rc;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    csize = (uint64_t*)malloc(P * sizeof(uint64_t));
+    rank = (uint32_t*)malloc((M ? M : 1) * sizeof(uint32_t));
+    if (!csize || !rank) {
+        free(csize);
+        free(rank);
+        return ORC_ENOMEM;
+    }
+    rc = orc_classmap(M, P, seed, csize, rank);
+    if (rc) goto done;
+    word_off[0] = 0;
+    for (p = 0; p < P; ++p) word_off[p + 1] = word_off[p] + (csize[p] + 31) / 32;
+    memset(bitmap, 0, word_off[P] * sizeof(uint32_t));
+    for (p = 0; p < P; ++p) {
+        for (i = agg_off[p]; i < agg_off[p + 1]; ++i) {
+            uint32_t x = agg_idx[i];
+            uint64_t b;
+            if (x >= M || orc_h0(x, seed, P) != p) {
+                rc = ORC_EINCONSISTENT;
+                goto done;
+            }
+            b = rank[x];
+            bitmap[word_off[p] + b / 32] |= 1u << (b % 32);
+        }
+    }
+done:
+    free(csize);
+    free(rank);
+    return rc;
+}
+
+/* Inverse of orc_encode: bit positions back to global indices through C_p
+ * ([Zen] section 3.3.2, hash_bitmap_decode).  out_off[P+1] is filled; out_idx
+ * must hold M entries. */
+int orc_decode(const uint32_t* bitmap, uint32_t P, uint64_t M, uint32_t seed,
+               uint32_t* out_idx, uint64_t* out_off)
+{
+    uint64_t *csize, *woff, *fill;
+    uint32_t** members;
+    uint32_t p;
+    uint64_t i, o = 0;
+    int rc = ORC_OK;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    csize = (uint64_t*)calloc(P, sizeof(uint64_t));
+    woff = (uint64_t*)calloc(P + 1, sizeof(uint64_t));
+    fill = (uint64_t*)calloc(P, sizeof(uint64_t));
+    members = (uint32_t**)calloc(P, sizeof(uint32_t*));
+    if (!csize || !woff || !fill || !members) {
+        rc = ORC_ENOMEM;
+        goto done;
+    }
+    for (i = 0; i < M; ++i) csize[orc_h0((uint32_t)i, seed, P)]++;
+    for (p = 0; p < P; ++p) {
+        members[p] = (uint32_t*)malloc((csize[p] ? csize[p] : 1) * sizeof(uint32_t));
+        if (!members[p]) {
+            rc = ORC_ENOMEM;
+            goto done;
+        }
+        woff[p + 1] = woff[p] + (csize[p] + 31) / 32;
+    }
+    for (i = 0; i < M; ++i) {
+        p = orc_h0((uint32_t)i, seed, P);
+        members[p][fill[p]++] = (uint32_t)i;
+    }
+    for (p = 0; p < P; ++p) {
+        uint64_t b;
+        out_off[p] = o;
+        for (b = 0; b < csize[p]; ++b)
+            if (bitmap[woff[p] + b / 32] & (1u << (b % 32))) out_idx[o++] = members[p][b];
+    }
+    out_off[P] = o;
+done:
+    if (members)
+        for (p = 0; p < P; ++p) free(members[p]);
+    free(members);
+    free(csize);
+    free(woff);
+    free(fill);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A5: ring reduce-scatter arithmetic with slice skipping                    */
+/* ------------------------------------------------------------------------ */
+
+/* Chunk j of the n ring chunks: [floor(jM/n), floor((j+1)M/n)). */
+static uint64_t chunk_begin(uint64_t M, uint32_t n, uint32_t j)
+{
+    return (uint64_t)(((unsigned __int128)M * j) / n);
+}
+
+/* Skip decision for contributor t of chunk j, slice q (seeded mode).
+ * [Skip] section 4.3 (Random SkipReduce: every rank draws the same random
+ * numbers from a seed shared by all ranks).  Reading: one Bernoulli(p) draw per
+ * (chunk, ring position t >= 1, slice), taken as the top 24 bits of the
+ * SplitMix64 output number (j*(n-1) + t-1)*S + q of the stream seeded by
+ * `seed`; the draw skips when those bits fall below floor(p * 2^24). */
+static int seeded_skip(uint64_t seed, uint32_t n, uint64_t S, uint32_t j, uint32_t t, uint64_t q,
+                       uint32_t thr24)
+{
+    uint64_t ctr = ((uint64_t)j * (n - 1) + (t - 1)) * S + q;
+    uint64_t u = orc_splitmix64_at(seed, ctr) >> 40;
+    return u < thr24;
+}
+
+/* Threshold of the seeded draw: floor(p * 2^24), clamped to [0, 2^24]. */
+uint32_t orc_skip_threshold(double p)
+{
+    double t;
+    if (!(p > 0.0)) return 0;
+    if (p >= 1.0) return 1u << 24;
+    t = floor(p * 16777216.0);
+    return (uint32_t)t;
+}
+
+/* Inclusion mask [n chunks][n ring positions][S slices] (1 = included).
+ * Seeded mode: position 0 (the chunk's origin rank, which only sends) is
+ * always included; positions 1..n-1 are skipped per seeded_skip. */
+int orc_skip_mask(uint32_t n, uint64_t S, double p, uint64_t seed, uint8_t* include)
+{
+    uint32_t j, t;
+    uint64_t q;
+    uint32_t thr = orc_skip_threshold(p);
+    for (j = 0; j < n; ++j)
+        for (t = 0; t < n; ++t)
+            for (q = 0; q < S; ++q) {
+                uint8_t inc = 1;
+                if (t > 0 && seeded_skip(seed, n, S, j, t, q, thr)) inc = 0;
+                include[((uint64_t)j * n + t) * S + q] = inc;
+            }
+    return ORC_OK;
+}
+
+/* Ring reduce-scatter of n equal-role buffers bufs[n][M] into out[M], with
+ * per-slice skipping.  Chunk j starts at rank j and travels j -> j+1 -> ... ;
+ * the rank at ring position t = 1..n-1 adds its own slice of chunk j to the
+ * partial it received ([Ring] aggregation phase; [Skip] section 4.2 Algorithm
+ * 1's ReduceOrSkip, where a skipped rank forwards what it received unchanged,
+ * and Algorithm 2, where SkipReduce drops whole ring steps).  Position 0 sends
+ * its slice unreduced.  For each slice the included contributions are summed
+ * in ring order; c = number included.  Rescale mode 1 multiplies by n/c (the
+ * DropReduce divisor change of [Skip] section 4.1 and the DropReduce
+ * discussion); mode 0 leaves the sum as is (plain SkipReduce treats a skipped
+ * gradient as zero).  c = 0 gives +0.
+ * Outputs are double; out_abs[M] holds (scale) * sum |x| of the included
+ * terms, for the tolerance; count[n][S] (optional) holds c.
+ * include (optional, [n][n][S]) overrides the seeded mask. */
+int orc_skip_reduce_scatter(const void* bufs, int dtype, uint32_t n, uint64_t M, uint64_t slice_elems,
+                            double p, uint64_t seed, const uint8_t* include, int mode,
+                            double* out, double* out_abs, uint8_t* count)
+{
+    uint64_t maxchunk, S, q, e;
+    uint32_t j, t;
+    uint8_t* mask = NULL;
+    const uint8_t* m;
+    if (n == 0 || slice_elems == 0) return ORC_EINVAL;
+    maxchunk = (M + n - 1) / n;
+    S = maxchunk ? (maxchunk + slice_elems - 1) / slice_elems : 0;
+    if (!include) {
+        mask = (uint8_t*)malloc((size_t)n * n * (S ? S : 1));
+        if (!mask) return ORC_ENOMEM;
+        orc_skip_mask(n, S, p, seed, mask);
+        m = mask;
+    } else {
+        m = include;
+    }
+    for (j = 0; j < n; ++j) {
+        uint64_t cb = chunk_begin(M, n, j), ce = chunk_begin(M, n, j + 1);
+        for (q = 0; q < S; ++q) {
+            uint64_t sb = cb + q * slice_elems, se = sb + slice_elems;
+            uint32_t c = 0;
+            double scale;
+            for (t = 0; t < n; ++t) c += m[((uint64_t)j * n + t) * S + q] ? 1 : 0;
+            if (count) count[(uint64_t)j * S + q] = (uint8_t)c;
+            scale = (mode == 1 && c > 0) ? (double)n / (double)c : 1.0;
+            if (se > ce) se = ce;
+            for (e = sb; e < se; ++e) {
+                double acc = 0.0, accabs = 0.0;
+                for (t = 0; t < n; ++t) {
+                    uint32_t r = (j + t) % n;
+                    double v;
+                    if (!m[((uint64_t)j * n + t) * S + q]) continue;
+                    v = load_val(bufs, dtype, (uint64_t)r * M + e);
+                    acc += v;
+                    accabs += fabs(v);
+                }
+                out[e] = (c > 0) ? acc * scale : 0.0;
+                out_abs[e] = (c > 0) ? accabs * scale : 0.0;
+            }
+        }
+    }
+    free(mask);
+    return ORC_OK;
+}
+
+/* The same reduce-scatter replayed step by step with explicit per-rank
+ * buffers and the slice indices of [Skip] Algorithms 1-2: at step s every rank
+ * r sends its chunk (r - s) mod n to r+1 and the receiver either adds its own
+ * copy of chunk (r - s - 1) mod n (ReduceOrSkip with no skip) or keeps the
+ * received data (skip).  A contributor excluded at position t = 0 sends zeros
+ * (nothing of its own).  Only the test suite uses this, to check that the
+ * closed form above is the ring's arithmetic.  Rescaling is not applied here;
+ * out[M] receives the raw sums, in double. */
+int orc_ring_replay(const void* bufs, int dtype, uint32_t n, uint64_t M, uint64_t slice_elems,
+                    const uint8_t* include, double* out)
+{
+    double* x; /* x[r][e]: rank r's working copy */
+    uint64_t maxchunk, S, e;
+    uint32_t r, s;
+    if (n == 0 || slice_elems == 0) return ORC_EINVAL;
+    maxchunk = (M + n - 1) / n;
+    S = maxchunk ? (maxchunk + slice_elems - 1) / slice_elems : 0;
+    x = (double*)malloc((size_t)n * (M ? M : 1) * sizeof(double));
+    if (!x) return ORC_ENOMEM;
+    for (r = 0; r < n; ++r)
+        for (e = 0; e < M; ++e) x[(uint64_t)r * M + e] = load_val(bufs, dtype, (uint64_t)r * M + e);
+    /* Position 0 of chunk j is rank j: if excluded it contributes nothing. */
+    for (r = 0; r < n; ++r) {
+        uint64_t cb = chunk_begin(M, n, r), ce = chunk_begin(M, n, r + 1);
+        for (e = cb; e < ce; ++e) {
+            uint64_t q = (e - cb) / slice_elems;
+            if (!include[((uint64_t)r * n + 0) * S + q]) x[(uint64_t)r * M + e] = 0.0;
+        }
+    }
+    for (s = 0; s + 1 < n; ++s) {
+        /* messages of this step, taken before any receiver updates */
+        double* msg = (double*)malloc((size_t)n * (maxchunk ? maxchunk : 1) * sizeof(double));
+        if (!msg) {
+            free(x);
+            return ORC_ENOMEM;
+        }
+        for (r = 0; r < n; ++r) {
+            uint32_t cs = (uint32_t)((r + n - (s % n)) % n); /* chunk sent by r */
+            uint64_t cb = chunk_begin(M, n, cs), ce = chunk_begin(M, n, cs + 1);
+            for (e = cb; e < ce; ++e) msg[(uint64_t)r * maxchunk + (e - cb)] = x[(uint64_t)r * M + e];
+        }
+        for (r = 0; r < n; ++r) {
+            uint32_t from = (r + n - 1) % n;
+            uint32_t cr = (uint32_t)((r + 2 * n - s - 1) % n); /* chunk received by r */
+            uint32_t t = (r + n - cr) % n;                     /* r's ring position for chunk cr */
+            uint64_t cb = chunk_begin(M, n, cr), ce = chunk_begin(M, n, cr + 1);
+            for (e = cb; e < ce; ++e) {
+                uint64_t q = (e - cb) / slice_elems;
+                double y = msg[(uint64_t)from * maxchunk + (e - cb)];
+                if (include[((uint64_t)cr * n + t) * S + q])
+                    x[(uint64_t)r * M + e] = x[(uint64_t)r * M + e] + y;
+                else
+                    x[(uint64_t)r * M + e] = y;
+            }
+        }
+        free(msg);
+    }
+    /* chunk j ends on rank (j - 1) mod n */
+    for (r = 0; r < n; ++r) {
+        uint32_t j = (r + 1) % n;
+        uint64_t cb = chunk_begin(M, n, j), ce = chunk_begin(M, n, j + 1);
+        for (e = cb; e < ce; ++e) out[e] = x[(uint64_t)r * M + e];
+    }
+    free(x);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A6: sparsity statistics                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Output record of orc_stats; arrays are caller-owned. */
+typedef struct {
+    uint64_t union_size, sum_nnz, max_nnz;
+    uint64_t* nnz;           /* [n] */
+    uint64_t* inter;         /* [n*n]  |I_a intersect I_b| */
+    double* overlap;         /* [n*n]  Def. 3 */
+    double overlap_mean, overlap_min, overlap_max; /* over pairs a < b */
+    double gamma_n;          /* Def. 4 */
+    uint64_t* contig_counts; /* [(n+1)*P] worker w (row w) and the union (row n) per contiguous part */
+    double* skew_contig;     /* [n+1] Def. 5 on contiguous parts */
+    uint64_t* class_size;    /* [P] |C_i| (hashed parts), filled when hashed != 0 */
+    uint64_t* hashed_counts; /* [(n+1)*P] per hash class */
+    double* skew_hashed;     /* [n+1] Def. 5 evaluated on the hash classes */
+    double push_imbalance, pull_imbalance; /* Def. 8 with f = h0 */
+} orc_stats_out;
+
+/* Def. 5 on one set J: max over parts i of (c_i * M) / (g_i * |J|); 0 if J is
+ * empty; parts with g_i = 0 are skipped. */
+static double skew_of(const uint64_t* c, const uint64_t* g, uint32_t P, uint64_t M, uint64_t J)
+{
+    double best = 0.0;
+    uint32_t i;
+    if (J == 0) return 0.0;
+    for (i = 0; i < P; ++i) {
+        double s;
+        if (g[i] == 0) continue;
+        s = ((double)c[i] * (double)M) / ((double)g[i] * (double)J);
+        if (s > best) best = s;
+    }
+    return best;
+}
+
+/* Sparsity statistics of n workers' index sets (each strictly ascending).
+ * Def. 3 (overlap ratio), Def. 4 (densification ratio), Def. 5 (n-partition
+ * skew ratio) of [Zen] section 2.1, and Def. 8 (push and pull imbalance) of
+ * [Zen] section 3.1.  Readings: for n > 2 the overlap ratio is reported for
+ * every pair (Fig. 2a plots a distribution over pairs); gamma_n uses the
+ * workers' mean density as d_G (gamma = n |I| / sum |I_w|); skew uses P
+ * contiguous parts [floor(iM/P), floor((i+1)M/P)); "skew after hashing" is
+ * Def. 5 evaluated on the hash classes C_i; an empty set gives 0. */
+int orc_stats(const uint32_t* idx, const uint64_t* in_off, uint32_t n, uint64_t M, uint32_t P,
+              int hashed, uint32_t seed, orc_stats_out* o)
+{
+    uint32_t a, b, i;
+    uint8_t* seen = NULL;
+    uint64_t* g = NULL;
+    uint64_t e, npairs = 0;
+    double sum_ov = 0.0;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    seen = (uint8_t*)calloc(M ? M : 1, 1);
+    g = (uint64_t*)calloc(P, sizeof(uint64_t));
+    if (!seen || !g) {
+        free(seen);
+        free(g);
+        return ORC_ENOMEM;
+    }
+    o->sum_nnz = 0;
+    o->max_nnz = 0;
+    for (a = 0; a < n; ++a) {
+        o->nnz[a] = in_off[a + 1] - in_off[a];
+        o->sum_nnz += o->nnz[a];
+        if (o->nnz[a] > o->max_nnz) o->max_nnz = o->nnz[a];
+    }
+    /* union */
+    o->union_size = 0;
+    for (a = 0; a < n; ++a)
+        for (e = in_off[a]; e < in_off[a + 1]; ++e)
+            if (idx[e] < M && !seen[idx[e]]) {
+                seen[idx[e]] = 1;
+                o->union_size++;
+            }
+    /* pairwise intersections by merging the two sorted lists */
+    for (a = 0; a < n; ++a)
+        for (b = 0; b < n; ++b) {
+            uint64_t x = in_off[a], y = in_off[b], c = 0;
+            while (x < in_off[a + 1] && y < in_off[b + 1]) {
+                if (idx[x] < idx[y]) ++x;
+                else if (idx[x] > idx[y]) ++y;
+                else {
+                    ++c;
+                    ++x;
+                    ++y;
+                }
+            }
+            o->inter[(uint64_t)a * n + b] = c;
+        }
+    o->overlap_min = 0.0;
+    o->overlap_max = 0.0;
+    for (a = 0; a < n; ++a)
+        for (b = 0; b < n; ++b) {
+            uint64_t mn = o->nnz[a] < o->nnz[b] ? o->nnz[a] : o->nnz[b];
+            double ov = mn ? (double)o->inter[(uint64_t)a * n + b] / (double)mn : 0.0;
+            o->overlap[(uint64_t)a * n + b] = ov;
+            if (a < b) {
+                if (npairs == 0 || ov < o->overlap_min) o->overlap_min = ov;
+                if (npairs == 0 || ov > o->overlap_max) o->overlap_max = ov;
+                sum_ov += ov;
+                ++npairs;
+            }
+        }
+    o->overlap_mean = npairs ? sum_ov / (double)npairs : 0.0;
+    o->gamma_n = o->sum_nnz ? ((double)n * (double)o->union_size) / (double)o->sum_nnz : 0.0;
+    /* contiguous parts */
+    memset(o->contig_counts, 0, (size_t)(n + 1) * P * sizeof(uint64_t));
+    for (a = 0; a < n; ++a)
+        for (e = in_off[a]; e < in_off[a + 1]; ++e) {
+            uint32_t part = (uint32_t)(((unsigned __int128)idx[e] * P) / (M ? M : 1));
+            /* idx in [floor(iM/P), floor((i+1)M/P)) <=> part i; correct the
+             * integer estimate against the exact boundaries */
+            while (part + 1 < P && idx[e] >= chunk_begin(M, P, part + 1)) ++part;
+            while (part > 0 && idx[e] < chunk_begin(M, P, part)) --part;
+            o->contig_counts[(uint64_t)a * P + part]++;
+        }
+    for (e = 0; e < M; ++e) {
+        uint32_t part;
+        if (!seen[e]) continue;
+        part = (uint32_t)(((unsigned __int128)e * P) / (M ? M : 1));
+        while (part + 1 < P && e >= chunk_begin(M, P, part + 1)) ++part;
+        while (part > 0 && e < chunk_begin(M, P, part)) --part;
+        o->contig_counts[(uint64_t)n * P + part]++;
+    }
+    for (i = 0; i < P; ++i) g[i] = chunk_begin(M, P, i + 1) - chunk_begin(M, P, i);
+    for (a = 0; a < n; ++a) o->skew_contig[a] = skew_of(o->contig_counts + (uint64_t)a * P, g, P, M, o->nnz[a]);
+    o->skew_contig[n] = skew_of(o->contig_counts + (uint64_t)n * P, g, P, M, o->union_size);
+    /* hash classes */
+    o->push_imbalance = 0.0;
+    o->pull_imbalance = 0.0;
+    if (hashed) {
+        memset(o->class_size, 0, P * sizeof(uint64_t));
+        memset(o->hashed_counts, 0, (size_t)(n + 1) * P * sizeof(uint64_t));
+        for (e = 0; e < M; ++e) o->class_size[orc_h0((uint32_t)e, seed, P)]++;
+        for (a = 0; a < n; ++a)
+            for (e = in_off[a]; e < in_off[a + 1]; ++e)
+                o->hashed_counts[(uint64_t)a * P + orc_h0(idx[e], seed, P)]++;
+        for (e = 0; e < M; ++e)
+            if (seen[e]) o->hashed_counts[(uint64_t)n * P + orc_h0((uint32_t)e, seed, P)]++;
+        for (a = 0; a < n; ++a)
+            o->skew_hashed[a] = skew_of(o->hashed_counts + (uint64_t)a * P, o->class_size, P, M, o->nnz[a]);
+        o->skew_hashed[n] = skew_of(o->hashed_counts + (uint64_t)n * P, o->class_size, P, M, o->union_size);
+        /* Def. 8: push = max over (w, j) of P |I_w^j| / |I_w|; pull = max
+         * over j of P |I'_j| / |I| */
+        for (a = 0; a < n; ++a) {
+            if (o->nnz[a] == 0) continue;
+            for (i = 0; i < P; ++i) {
+                double v = ((double)P * (double)o->hashed_counts[(uint64_t)a * P + i]) / (double)o->nnz[a];
+                if (v > o->push_imbalance) o->push_imbalance = v;
+            }
+        }
+        if (o->union_size)
+            for (i = 0; i < P; ++i) {
+                double v = ((double)P * (double)o->hashed_counts[(uint64_t)n * P + i]) / (double)o->union_size;
+                if (v > o->pull_imbalance) o->pull_imbalance = v;
+            }
+    }
+    free(seen);
+    free(g);
+    return ORC_OK;
+}

@@ -1,0 +1,474 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks an oracle function against a value the pages or the
+mathematics fix: a published check value, brute force on tiny inputs written
+with different primitives (numpy sorts, Python sets, fsum), closed forms, or
+invariants.  A plausible mistake in the oracle (a dropped term, a wrong sign or
+index, a transposed operand) fails at least one of these.  No GPU needed.
+"""
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# hash and random numbers: published check values
+# --------------------------------------------------------------------------
+
+def test_murmur2_verification_value():
+    g = _golden("hash_check_values.json")["murmur2_32"]
+    key = bytearray(256)
+    blob = b""
+    for i in range(256):
+        key[i] = i
+        blob += struct.pack("<I", oracle.murmur2(bytes(key[:i]), 256 - i))
+    assert oracle.murmur2(blob, 0) == int(g["verification"], 16)
+
+
+def test_splitmix64_published_outputs():
+    g = _golden("hash_check_values.json")["splitmix64"]
+    assert oracle.splitmix64_outputs(0, 3) == [int(x, 16) for x in g["seed_0_first3"]]
+    assert oracle.splitmix64_outputs(1234567, 5) == g["seed_1234567_first5"]
+    # the counter form used by the skip mask is the same stream
+    for c in range(5):
+        assert oracle.splitmix64_at(1234567, c) == g["seed_1234567_first5"][c]
+
+
+def test_h0_is_murmur2_of_le_bytes_mod_P():
+    rng = np.random.default_rng(0)
+    xs = rng.integers(0, 2**32, size=200, dtype=np.uint64).astype(np.uint32)
+    for P in (1, 3, 16, 255):
+        got = oracle.h0(xs, 7, P)
+        for x, g in zip(xs, got):
+            assert g == oracle.murmur2(struct.pack("<I", int(x)), 7) % P
+
+
+def test_h0_balance_matches_theorem2_scale():
+    # Zen section 3.2, Theorem 2: with a universal hash the heaviest of n
+    # partitions exceeds the mean by a factor 1 + Theta(sqrt(n ln n / N)).
+    N, P = 1 << 20, 16
+    parts = oracle.h0(np.arange(N, dtype=np.uint32), 4, P)
+    counts = np.bincount(parts, minlength=P)
+    imb = counts.max() * P / N
+    assert 1.0 <= imb < 1.0 + 4.0 * math.sqrt(P * math.log(P) / N)
+
+
+# --------------------------------------------------------------------------
+# A1 top-k
+# --------------------------------------------------------------------------
+
+def _topk_brute(row, k, bf16):
+    bits = row.view(np.uint16 if bf16 else np.uint32).astype(np.uint64)
+    mag = bits & (0x7FFF if bf16 else 0x7FFFFFFF)
+    order = np.lexsort((np.arange(row.size), -mag.astype(np.int64)))  # by -|x|, then index
+    return np.sort(order[:k])
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M,k", [(1, 1), (7, 0), (7, 3), (7, 7), (100, 37), (257, 256)])
+def test_topk_brute_force_with_ties(M, k, bf16):
+    rng = np.random.default_rng(M * 31 + k)
+    n = 3
+    # few distinct magnitudes so ties (and +0/-0) are common
+    vals = rng.integers(-3, 4, size=(n, M)).astype(np.float32)
+    vals[vals == 0] = np.where(rng.random((vals == 0).sum()) < 0.5, 0.0, -0.0)
+    dense = gen.to_bf16(vals) if bf16 else vals
+    idx, val = oracle.topk_to_coo(dense, k)
+    for w in range(n):
+        exp = _topk_brute(dense[w], k, bf16)
+        assert np.array_equal(idx[w], exp.astype(np.uint32))
+        assert np.array_equal(val[w].view(np.uint8), dense[w][exp].view(np.uint8))
+
+
+def test_topk_selection_invariant_random():
+    rng = np.random.default_rng(5)
+    dense = rng.standard_normal((2, 5000)).astype(np.float32)
+    k = 321
+    idx, val = oracle.topk_to_coo(dense, k)
+    for w in range(2):
+        sel = np.zeros(5000, bool)
+        sel[idx[w]] = True
+        assert np.all(np.diff(idx[w].astype(np.int64)) > 0)
+        assert np.abs(dense[w][sel]).min() >= np.abs(dense[w][~sel]).max()
+        assert np.array_equal(val[w], dense[w][idx[w]])
+
+
+def test_topk_k_equals_nnz_is_nonzero_extraction():
+    c = gen.config1(n=2, M=1 << 14)
+    idx, _ = oracle.topk_to_coo(c["dense"], c["k"])
+    for w in range(2):
+        assert np.array_equal(idx[w], np.flatnonzero(c["dense"][w]).astype(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# A2 hash partition
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [1, 3, 16])
+@pytest.mark.parametrize("D", [0, 1, 3])
+def test_partition_is_stable_grouping_by_h0(P, D):
+    c = gen.coo_zipf(9, 3, 5000, 300, 1.1, D=max(D, 1))
+    idx, in_off, val = c
+    if D == 0:
+        val = None
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, P, 11)
+    h = oracle.h0(idx, 11, P)
+    for w in range(3):
+        b, e = int(in_off[w]), int(in_off[w + 1])
+        order = b + np.argsort(h[b:e], kind="stable")
+        assert np.array_equal(oi[b:e], idx[order])
+        if D:
+            assert np.array_equal(ov[b:e], val[order])
+        counts = np.bincount(h[b:e], minlength=P)
+        assert np.array_equal(np.diff(po[w].astype(np.int64)), counts)
+        assert po[w, 0] == b and po[w, P] == e
+
+
+def test_partition_same_index_same_server():
+    idx = np.array([5, 9, 100, 5, 100, 7], dtype=np.uint32)
+    in_off = np.array([0, 3, 6], dtype=np.uint64)
+    oi, _, po = oracle.hash_partition(idx, None, in_off, 4, 3)
+    where = {}
+    for w in range(2):
+        for p in range(4):
+            for x in oi[int(po[w, p]):int(po[w, p + 1])]:
+                assert where.setdefault(int(x), p) == p
+
+
+# --------------------------------------------------------------------------
+# A3 aggregate
+# --------------------------------------------------------------------------
+
+def _agg_brute(idx, val, part_off, D):
+    n, P1 = part_off.shape
+    sums, abss, owner = {}, {}, {}
+    for w in range(n):
+        for p in range(P1 - 1):
+            for i in range(int(part_off[w, p]), int(part_off[w, p + 1])):
+                x = int(idx[i])
+                v = val[i] if D > 1 else [val[i]]
+                sums.setdefault(x, [[] for _ in range(max(D, 1))])
+                for d in range(max(D, 1)):
+                    sums[x][d].append(float(v[d]))
+                owner[x] = p
+    return sums, owner
+
+
+@pytest.mark.parametrize("D", [1, 4])
+def test_aggregate_brute_force(D):
+    idx, in_off, val = gen.coo_zipf(13, 5, 400, 60, 0.8, D=D)
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, 3, 2)
+    ai, av, aa, ao = oracle.aggregate(oi, ov, po, 400)
+    sums, owner = _agg_brute(oi, ov, po, D)
+    assert ai.size == len(sums)
+    for p in range(3):
+        keys = sorted(k for k, q in owner.items() if q == p)
+        assert list(ai[int(ao[p]):int(ao[p + 1])]) == keys
+    for j, x in enumerate(ai):
+        for d in range(D):
+            terms = sums[int(x)][d]
+            exact = math.fsum(terms)
+            got = av[j, d] if D > 1 else av[j]
+            absum = aa[j, d] if D > 1 else aa[j]
+            assert abs(got - exact) <= len(terms) * 2.0**-52 * sum(abs(t) for t in terms)
+            assert abs(absum - math.fsum(abs(t) for t in terms)) <= 1e-12 * absum + 1e-300
+
+
+def test_aggregate_union_bounds_and_extremes():
+    # disjoint supports: |I| = sum, values unchanged
+    a = np.array([1, 5, 9], np.uint32)
+    b = np.array([2, 6, 10], np.uint32)
+    idx = np.concatenate([a, b])
+    val = np.arange(6, dtype=np.float32) + 1
+    in_off = np.array([0, 3, 6], np.uint64)
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, 2, 1)
+    ai, av, _, _ = oracle.aggregate(oi, ov, po, 16)
+    assert ai.size == 6
+    m = dict(zip(idx.tolist(), val.tolist()))
+    assert all(av[j] == m[int(x)] for j, x in enumerate(ai))
+    # identical supports: |I| = |I_w|, values add
+    idx = np.concatenate([a, a, a])
+    val = np.ones(9, np.float32)
+    in_off = np.array([0, 3, 6, 9], np.uint64)
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, 2, 1)
+    ai, av, _, _ = oracle.aggregate(oi, ov, po, 16)
+    assert ai.size == 3 and np.all(av == 3.0)
+    # a cancelling index stays in the aggregate (membership, not value)
+    idx = np.array([4, 4], np.uint32)
+    val = np.array([2.5, -2.5], np.float32)
+    oi, ov, po = oracle.hash_partition(idx, val, np.array([0, 1, 2], np.uint64), 1, 0)
+    ai, av, _, _ = oracle.aggregate(oi, ov, po, 8)
+    assert list(ai) == [4] and av[0] == 0.0
+    # general bounds
+    idx, in_off, val = gen.coo_zipf(3, 6, 3000, 400, 1.0)
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, 4, 3)
+    ai, _, _, ao = oracle.aggregate(oi, ov, po, 3000)
+    nnz = np.diff(in_off.astype(np.int64))
+    assert nnz.max() <= ai.size <= nnz.sum() and ao[-1] == ai.size
+
+
+def test_aggregate_dense_allreduce_equivalence():
+    # Zen section 3.2: the sparse aggregate equals the dense AllReduce
+    n, M = 4, 2000
+    idx, in_off, val = gen.coo_zipf(21, n, M, 150, 1.2)
+    dense = gen.dense_from_coo(n, M, idx, in_off, val).astype(np.float64).sum(0)
+    oi, ov, po = oracle.hash_partition(idx, val, in_off, 5, 9)
+    ai, av, _, _ = oracle.aggregate(oi, ov, po, M)
+    out = np.zeros(M)
+    out[ai] = av
+    assert np.allclose(out, dense, rtol=0, atol=1e-12)
+
+
+def _skewed_expectations(n, M, c):
+    h = int(0.6 * c)
+    t = c - h
+    Rh, Rt = M // 8, M - M // 8
+    Uh = Rh * (1 - (1 - h / Rh) ** n)
+    Ut = Rt * (1 - (1 - t / Rt) ** n)
+    return h, t, Rh, Rt, Uh, Ut
+
+
+def test_config4_union_closed_form_scaled():
+    # Each region is sampled uniformly without replacement, so an index is in
+    # a worker's set with probability c_region / R_region, independently over
+    # workers: E|I| = sum over regions of R (1 - (1 - c/R)^n).
+    n, M = 16, 1 << 22
+    d = gen.config4(n=n, M=M)
+    oi, ov, po = oracle.hash_partition(d["idx"], d["val"], d["in_off"], 16, 4)
+    ai, _, _, _ = oracle.aggregate(oi, ov, po, M)
+    h, t, Rh, Rt, Uh, Ut = _skewed_expectations(n, M, M // 100)
+    ph, pt = 1 - (1 - h / Rh) ** n, 1 - (1 - t / Rt) ** n
+    sd = math.sqrt(Rh * ph * (1 - ph) + Rt * pt * (1 - pt))
+    assert abs(ai.size - (Uh + Ut)) < 6 * sd
+    # the full-size value of the same formula, as the survey states it
+    _, _, _, _, Uh4, Ut4 = _skewed_expectations(16, 1 << 28, (1 << 28) // 100)
+    assert abs((Uh4 + Ut4) - 34_884_067.5) < 1.0
+
+
+# --------------------------------------------------------------------------
+# A4 encode / decode
+# --------------------------------------------------------------------------
+
+def test_encode_fig10_walkthrough():
+    g = _golden("zen_fig10.json")
+    G, P, seed = g["G"], g["servers"], g["seed"]
+    nz = np.array([i - 1 for i in g["page_nonzero_indices_1based"]], np.uint32)
+    # server 0 holds exactly these two indices
+    agg_off = np.array([0, 2, 2, 2], np.uint64)
+    bitmap, word_off = oracle.encode(nz, agg_off, G, seed)
+    bits0 = [b for b in range(32) if bitmap[int(word_off[0])] >> b & 1]
+    assert bits0 == [b - 1 for b in g["page_set_bits_1based"]]
+    dec, off = oracle.decode(bitmap, P, G, seed)
+    assert list(dec[int(off[0]):int(off[1])]) == list(nz)
+
+
+@pytest.mark.parametrize("M,P", [(1, 1), (31, 2), (1000, 7), (1 << 15, 16)])
+def test_encode_popcount_size_and_roundtrip(M, P):
+    rng = np.random.default_rng(M + P)
+    keys = np.flatnonzero(rng.random(M) < 0.3).astype(np.uint32)
+    h = oracle.h0(keys, 5, P)
+    order = np.argsort(h, kind="stable")
+    agg_idx = keys[order]
+    agg_off = np.concatenate([[0], np.cumsum(np.bincount(h, minlength=P))]).astype(np.uint64)
+    bitmap, word_off = oracle.encode(agg_idx, agg_off, M, 5)
+    csize, rank = oracle.classmap(M, P, 5)
+    assert csize.sum() == M
+    assert np.array_equal(np.diff(word_off.astype(np.int64)), (csize.astype(np.int64) + 31) // 32)
+    assert M / 32 <= word_off[P] <= M / 32 + P
+    for p in range(P):
+        words = bitmap[int(word_off[p]):int(word_off[p + 1])]
+        pc = sum(bin(int(x)).count("1") for x in words)
+        assert pc == agg_off[p + 1] - agg_off[p]
+        # padding bits beyond |C_p| are zero
+        if csize[p] % 32:
+            assert int(words[-1]) >> int(csize[p] % 32) == 0
+    dec, off = oracle.decode(bitmap, P, M, 5)
+    assert np.array_equal(dec, agg_idx) and np.array_equal(off, agg_off)
+    # rank is the position inside the ascending class list
+    for p in range(P):
+        members = np.flatnonzero(oracle.h0(np.arange(M, dtype=np.uint32), 5, P) == p)
+        assert np.array_equal(rank[members], np.arange(members.size, dtype=np.uint32))
+
+
+# --------------------------------------------------------------------------
+# A5 skip reduce-scatter
+# --------------------------------------------------------------------------
+
+def _rs_brute(bufs, slice_elems, include, mode):
+    n, M = bufs.shape
+    b = bufs.astype(np.float64)
+    out = np.zeros(M)
+    S = include.shape[2]
+    for j in range(n):
+        cb, ce = (M * j) // n, (M * (j + 1)) // n
+        for q in range(S):
+            sb, se = cb + q * slice_elems, min(cb + (q + 1) * slice_elems, ce)
+            if sb >= se:
+                continue
+            ranks = [(j + t) % n for t in range(n) if include[j, t, q]]
+            c = len(ranks)
+            if c == 0:
+                continue
+            s = np.zeros(se - sb)
+            for r in ranks:  # ring order
+                s = s + b[r, sb:se]
+            out[sb:se] = s * (n / c if mode == 1 else 1.0)
+    return out
+
+
+@pytest.mark.parametrize("n,M,sl", [(1, 10, 3), (2, 9, 2), (4, 64, 4), (5, 103, 7), (8, 1000, 32)])
+def test_skip_rs_brute_force(n, M, sl):
+    rng = np.random.default_rng(n * 1000 + M)
+    bufs = rng.standard_normal((n, M)).astype(np.float32)
+    for p, mode in ((0.0, 1), (0.5, 1), (0.5, 0), (0.9, 1)):
+        out, out_abs, cnt = oracle.skip_reduce_scatter(bufs, sl, p, 77, mode=mode)
+        S = oracle.num_slices(n, M, sl)
+        inc = oracle.skip_mask(n, S, p, 77)
+        assert np.all(inc[:, 0, :] == 1)
+        assert np.array_equal(cnt, inc.sum(1).astype(np.uint8))
+        assert np.allclose(out, _rs_brute(bufs, sl, inc, mode), rtol=1e-13, atol=1e-13)
+        assert np.all(out_abs >= np.abs(out) - 1e-12)
+
+
+def test_skip_rs_p0_is_full_sum():
+    bufs = gen.dense_normal(99, 6, 5000)
+    out, _, cnt = oracle.skip_reduce_scatter(bufs, 100, 0.0, 1)
+    assert np.all(cnt == 6)
+    exact = np.array([math.fsum(col) for col in bufs.astype(np.float64).T])
+    assert np.allclose(out, exact, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_skip_rs_closed_form_equals_ring_replay(n):
+    # Skip Algorithms 1-2 replayed with explicit send/recv buffers gives the
+    # same arithmetic as the closed form (mode 0: no rescale), bit for bit.
+    rng = np.random.default_rng(n)
+    M, sl = 37 * n + 3, 5
+    bufs = rng.standard_normal((n, M)).astype(np.float32)
+    S = oracle.num_slices(n, M, sl)
+    for trial in range(3):
+        inc = (rng.random((n, n, S)) < 0.6).astype(np.uint8)
+        if trial == 0:
+            inc[:] = 1
+        out, _, _ = oracle.skip_reduce_scatter(bufs, sl, 0.0, 0, include=inc, mode=0)
+        rep = oracle.ring_replay(bufs, sl, inc)
+        assert np.array_equal(out, rep)
+
+
+def test_static_skipreduce_skips_k_over_n():
+    # Skip Algorithm 2 runs the reduce-scatter loop from s = k: chunk j keeps
+    # only ring positions t >= k, i.e. k/N of the contributions are skipped.
+    n, M, sl = 8, 8 * 64, 16
+    S = oracle.num_slices(n, M, sl)
+    bufs = gen.dense_normal(7, n, M)
+    for k in range(n):
+        inc = np.zeros((n, n, S), np.uint8)
+        inc[:, k:, :] = 1
+        out, _, cnt = oracle.skip_reduce_scatter(bufs, sl, 0.0, 0, include=inc, mode=0)
+        assert cnt.sum() == (n - k) * n * S
+        assert 1 - cnt.sum() / (n * n * S) == pytest.approx(k / n)
+        rep = oracle.ring_replay(bufs, sl, inc)
+        assert np.array_equal(out, rep)
+
+
+def test_seeded_mask_rate():
+    n, S, p = 8, 128, 0.5
+    inc = oracle.skip_mask(n, S, p, 5)
+    draws = inc[:, 1:, :]
+    rate = 1 - draws.mean()
+    sd = math.sqrt(p * (1 - p) / draws.size)
+    assert abs(rate - p) < 5 * sd
+    assert oracle.skip_threshold(0.5) == 1 << 23 and oracle.skip_threshold(1.0) == 1 << 24
+    assert oracle.skip_threshold(0.0) == 0
+
+
+def test_dead_rank_mask():
+    n, M, sl = 4, 400, 10
+    S = oracle.num_slices(n, M, sl)
+    bufs = gen.dense_normal(8, n, M)
+    dead = 2
+    inc = np.ones((n, n, S), np.uint8)
+    for j in range(n):
+        inc[j, (dead - j) % n, :] = 0
+    out, _, _ = oracle.skip_reduce_scatter(bufs, sl, 0.0, 0, include=inc, mode=1)
+    others = np.delete(bufs.astype(np.float64), dead, axis=0).sum(0) * n / (n - 1)
+    assert np.allclose(out, others, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# A6 stats
+# --------------------------------------------------------------------------
+
+def test_stats_brute_force():
+    idx, in_off, _ = gen.coo_zipf(31, 5, 700, 90, 0.9)
+    M, P = 700, 6
+    st = oracle.stats(idx, in_off, M, P, hashed=True, seed=3)
+    sets = [set(idx[int(in_off[w]):int(in_off[w + 1])].tolist()) for w in range(5)]
+    U = set().union(*sets)
+    assert st["union_size"] == len(U)
+    for a in range(5):
+        for b in range(5):
+            assert st["inter"][a, b] == len(sets[a] & sets[b])
+            assert st["overlap"][a, b] == len(sets[a] & sets[b]) / min(len(sets[a]), len(sets[b]))
+    assert st["gamma_n"] == 5 * len(U) / sum(len(s) for s in sets)
+    bounds = [(M * i) // P for i in range(P + 1)]
+    for w, s in enumerate(sets + [U]):
+        cnt = [sum(1 for x in s if bounds[i] <= x < bounds[i + 1]) for i in range(P)]
+        assert list(st["contig_counts"][w]) == cnt
+        sk = max((cnt[i] / (bounds[i + 1] - bounds[i])) / (len(s) / M) for i in range(P))
+        assert st["skew_contig"][w] == pytest.approx(sk, rel=1e-14)
+    cls = oracle.h0(np.arange(M, dtype=np.uint32), 3, P)
+    for w, s in enumerate(sets + [U]):
+        hc = np.bincount(oracle.h0(np.array(sorted(s), np.uint32), 3, P), minlength=P)
+        assert np.array_equal(st["hashed_counts"][w], hc)
+    g = np.bincount(cls, minlength=P)
+    push = max(P * st["hashed_counts"][w, i] / len(sets[w]) for w in range(5) for i in range(P))
+    pull = max(P * st["hashed_counts"][5, i] / len(U) for i in range(P))
+    assert st["push_imbalance"] == pytest.approx(push, rel=1e-14)
+    assert st["pull_imbalance"] == pytest.approx(pull, rel=1e-14)
+    assert np.array_equal(st["class_size"], g)
+
+
+def test_stats_identical_disjoint_and_gamma_bounds():
+    a = np.arange(0, 50, 2, dtype=np.uint32)
+    b = np.arange(1, 50, 2, dtype=np.uint32)
+    st = oracle.stats(np.concatenate([a, a, a]), np.array([0, 25, 50, 75], np.uint64), 64, 4)
+    assert st["overlap_min"] == st["overlap_max"] == 1.0 and st["gamma_n"] == 1.0
+    st = oracle.stats(np.concatenate([a, b]), np.array([0, 25, 50], np.uint64), 64, 4)
+    assert st["overlap_max"] == 0.0 and st["gamma_n"] == 2.0
+    idx, in_off, _ = gen.coo_zipf(5, 8, 5000, 500, 1.1)
+    st = oracle.stats(idx, in_off, 5000, 8)
+    # Zen section 2.1: densification stays below n when supports overlap
+    assert 1.0 <= st["gamma_n"] < 8.0 and st["overlap_max"] > 0
+
+
+def test_config4_stats_closed_forms_scaled():
+    n, M, P = 16, 1 << 22, 16
+    d = gen.config4(n=n, M=M)
+    st = oracle.stats(d["idx"], d["in_off"], M, P, hashed=True, seed=4)
+    c = M // 100
+    h, t, Rh, Rt, Uh, Ut = _skewed_expectations(n, M, c)
+    # overlap of two independent uniform samples: E|I_a & I_b| = h^2/Rh + t^2/Rt
+    assert st["overlap_mean"] == pytest.approx((h * h / Rh + t * t / Rt) / c, rel=0.02)
+    assert st["gamma_n"] == pytest.approx((Uh + Ut) / c, rel=0.002)
+    # contiguous skew: parts 0 and 1 split the head, each ~h/2 of c entries
+    assert np.all(np.abs(st["skew_contig"][:n] - 16 * (h / 2) / c) < 0.2)
+    assert st["skew_contig"][n] == pytest.approx(16 * (Uh / 2) / (Uh + Ut), rel=0.02)
+    # after hashing: Theorem 2 scale, close to 1
+    bound = 1 + 6 * math.sqrt(P * math.log(P) / c)
+    assert np.all(st["skew_hashed"] < bound) and st["push_imbalance"] < bound
+    assert st["pull_imbalance"] < 1 + 6 * math.sqrt(P * math.log(P) / st["union_size"])
