@@ -1,0 +1,253 @@
+/*
+ * sg.h -- C ABI of libsg: the on-device compute of sparsity-driven gradient
+ * synchronization on one AMD MI355X (gfx950).
+ *
+ * The n workers of the method are simulated resident on one GPU: every
+ * worker's buffers live in this GPU's HBM and there is no communication.  The
+ * library implements the compute a worker or server performs:
+ *
+ *   sg_topk_to_coo          top-k sparsification of dense gradients into COO
+ *   sg_hash_partition       data-independent hash partition of COO indices
+ *   sg_aggregate            per-partition union-sum of n workers' COO tensors
+ *   sg_classmap_build,
+ *   sg_encode               hash-bitmap encoding of the aggregate's indices
+ *   sg_skip_reduce_scatter  ring reduce-scatter arithmetic with seeded slice
+ *                           skipping (SkipReduce / DropReduce)
+ *   sg_stats                overlap, densification and skew ratios
+ *
+ * Sources: "Zen: Empowering Distributed Training with Sparsity-driven Data
+ * Synchronization" (OSDI'25) digest page [Zen]; "SkipReduce: (Interconnection)
+ * Network Sparsity to Accelerate Distributed Machine Learning" (MICRO'25)
+ * digest page [Skip]; CMU 15-442/642 lecture notes on data parallelism, "Ring
+ * AllReduce" aggregation phase [Ring].
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* are device memory on the current HIP device, owned by
+ *     the caller.  The library never allocates, frees or synchronizes, except
+ *     sg_stats and sg_device_error, which return host values and therefore
+ *     block on `stream`.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is queued on it in order; sizes that only the device knows (for
+ *     example agg_off[P]) are read by the caller after synchronizing.
+ *   - Indices are 0-based uint32; dense sizes M must be below 2^32.
+ *   - Each worker's COO index list is strictly ascending and every index is
+ *     below M (the sets I_i of [Zen] section 3.1).  sg_validate_coo checks
+ *     this.  Kernels keep every memory access in bounds whatever the input,
+ *     but results on invalid input are unspecified; a violation they notice is
+ *     recorded and returned by sg_device_error.
+ *   - Return value: SG_OK (0) or a negative sg_status.  Host-checkable
+ *     problems (null pointers, sizes, workspace) fail before any launch.
+ *   - Workspace: each call that needs scratch memory takes d_ws of at least
+ *     the size its *_workspace_bytes function returns for the same arguments.
+ *     Its contents on entry do not matter.
+ *   - Calls are not re-entrant on one workspace: two calls that overlap in
+ *     time must use different workspaces.
+ */
+#ifndef SG_H
+#define SG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sg_status {
+    SG_OK = 0,
+    SG_EINVAL = -1,       /* bad argument: null pointer, size out of range, unsupported shape */
+    SG_ECAPACITY = -2,    /* an output or workspace buffer is smaller than required */
+    SG_EUNSORTED = -3,    /* sg_validate_coo: a worker's indices are not strictly ascending */
+    SG_EHIP = -4,         /* a HIP launch or copy failed */
+    SG_EUNSUPPORTED = -5, /* parameters outside what this build implements (stated per call) */
+    SG_ERANGE = -6,       /* sg_validate_coo: an index is >= M, or offsets are inconsistent */
+    SG_EDEVICE = -7       /* a kernel noticed a violated precondition (see sg_device_error) */
+} sg_status;
+
+typedef enum sg_dtype {
+    SG_F32 = 0,  /* IEEE binary32 */
+    SG_BF16 = 1  /* bfloat16, accumulated in fp32 */
+} sg_dtype;
+
+typedef enum sg_rescale {
+    SG_RESCALE_NONE = 0, /* SkipReduce proper: a skipped contribution counts as zero ([Skip] section 4.1) */
+    SG_RESCALE_DROP = 1  /* DropReduce: the sum is multiplied by n/c, c = contributions kept ([Skip] section 4.1 and its DropReduce study) */
+} sg_rescale;
+
+/* Text for a status code.  Never NULL. */
+const char* sg_strerror(int status);
+
+/* Returns SG_OK, or SG_EDEVICE if any kernel of this library recorded a
+ * violated precondition on the current device since the last call; clears the
+ * record.  Synchronizes `stream`. */
+int sg_device_error(void* stream);
+
+/* Checks that every worker's index list is strictly ascending and below M and
+ * that in_off is non-decreasing with in_off[0] = 0 and in_off[n] = total.
+ * Returns SG_OK, SG_EUNSORTED or SG_ERANGE.  d_ws: sg_validate_workspace_bytes().
+ * Synchronizes `stream`. */
+size_t sg_validate_workspace_bytes(void);
+int sg_validate_coo(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                    void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A1. Top-k sparsification into COO.
+ * [Skip] section 2 (top-k keeps the largest-magnitude gradients; unselected
+ * ones stay local) and [Zen] section 4 (DGC selects the top 5% per tensor).
+ * For each worker w: the k entries of largest |dense[w][i]|, written in
+ * ascending index order to idx[w][0..k) with the signed value copied bit for
+ * bit to val[w][0..k) (same dtype as the input).  Equal magnitudes (+0 and -0
+ * included) are taken lowest index first.  NaN payloads order above +Inf
+ * (they are compared as bit patterns); finite inputs are the contract.
+ *   d_dense  [n][M] of dt, row-major (worker-major)
+ *   d_idx    [n][k] uint32 out;   d_val [n][k] of dt out
+ * Limits: 1 <= n, 1 <= M < 2^32, k <= M.  k == 0 writes nothing.
+ * ------------------------------------------------------------------------ */
+size_t sg_topk_workspace_bytes(uint32_t n, uint64_t M, uint64_t k, sg_dtype dt);
+int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint64_t M, uint64_t k, uint32_t* d_idx,
+                   void* d_val, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A2. Hash partition.
+ * [Zen] section 3.1 (Problem 1: one map f from indices to [P] shared by all
+ * workers) and section 3.2 (Technique #3 / Algorithm 1: the first-level hash
+ * h0 picks the partition).  h0(i) = MurmurHash2-32(4 little-endian bytes of
+ * i, seed) mod P.  Each worker's entries are grouped by partition 0..P-1 and
+ * kept in input order inside a partition (order inside a partition does not
+ * change the aggregate, [Zen] Technique #1; the stable order makes results
+ * reproducible and keeps every (worker, partition) run ascending).
+ *   d_idx      [total] uint32, worker w's entries at [in_off[w], in_off[w+1])
+ *   d_val      [total][D] of dt, or NULL when D == 0 (indices only)
+ *   d_in_off   [n+1] uint64, in_off[0] = 0, in_off[n] = total
+ *   d_out_idx  [total] out;  d_out_val [total][D] out (NULL when D == 0)
+ *   d_part_off [n][P+1] uint64 out, absolute offsets: run (w,p) is
+ *              [part_off[w][p], part_off[w][p+1]); part_off[w][P] = in_off[w+1]
+ * Limits: 1 <= P <= 256, n >= 1, total < 2^32, D <= 65536.
+ * ------------------------------------------------------------------------ */
+size_t sg_partition_workspace_bytes(uint32_t n, uint64_t total, uint32_t P);
+int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D, const uint64_t* d_in_off,
+                      uint32_t n, uint64_t total, uint32_t P, uint32_t seed, uint32_t* d_out_idx, void* d_out_val,
+                      uint64_t* d_part_off, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A3. Per-partition union-sum (the server side of Push).
+ * [Zen] section 3.1 (server p aggregates the partition-p tensors of all
+ * workers) and section 3.2 (the result equals the dense AllReduce).  For each
+ * partition p: the union of the n runs (w,p) in ascending index order, each
+ * index with its D values summed in fp32 over the workers holding it, in
+ * worker order.  Membership: an index sent by any worker is in the aggregate,
+ * even if its sum is zero.
+ *   inputs as produced by sg_hash_partition (each run strictly ascending,
+ *   runs of one partition hold only indices of that partition)
+ *   d_agg_idx  [capacity] uint32 out
+ *   d_agg_val  [capacity][D] fp32 out (NULL when D == 0)
+ *   d_agg_off  [P+1] uint64 out: partition p is [agg_off[p], agg_off[p+1])
+ * capacity must be >= total (the worst case, all indices distinct).
+ * Limits: 1 <= n <= 64, 1 <= P <= 256, M < 2^32, total < 2^32.
+ * ------------------------------------------------------------------------ */
+size_t sg_aggregate_workspace_bytes(uint32_t n, uint32_t P, uint64_t M, uint64_t total, uint32_t D);
+int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D, const uint64_t* d_part_off,
+                 uint32_t n, uint32_t P, uint64_t M, uint64_t total, uint32_t* d_agg_idx, float* d_agg_val,
+                 uint64_t capacity, uint64_t* d_agg_off, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A4. Hash-bitmap encode.
+ * [Zen] section 3.3.2 (hash bitmap, Fig. 10): the index set of server p is
+ * the class C_p = { i in [0,M) : h0(i) = p } in ascending order, fixed offline;
+ * the server's bitmap has bit b set iff C_p[b] is in its aggregate.  Layout:
+ * bit b of class p is bit (b % 32) of word word_off[p] + b/32; classes are
+ * concatenated p = 0..P-1, each padded with zero bits to whole words, so
+ * word_off[p] = sum_{q<p} ceil(|C_q| / 32) and the total is about M/32 words.
+ * Values need no re-encoding: the aggregate is already in C_p order.
+ *
+ * sg_classmap_build fills an opaque class map (setup, done once per (M, P,
+ * seed), like the offline computation of the page).  sg_encode reads it.
+ *   d_agg_idx, d_agg_off  as produced by sg_aggregate (indices of partition p
+ *                         ascending and with h0 = p)
+ *   d_bitmap   [bitmap_words] uint32 out, bitmap_words >= sg_encode_max_words(M, P)
+ *   d_word_off [P+1] uint64 out
+ * Limits: 1 <= P <= 256, 1 <= M < 2^32.
+ * ------------------------------------------------------------------------ */
+size_t sg_classmap_bytes(uint64_t M, uint32_t P);
+int sg_classmap_build(uint64_t M, uint32_t P, uint32_t seed, void* d_cmap, size_t cmap_bytes, void* stream);
+uint64_t sg_encode_max_words(uint64_t M, uint32_t P);
+size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P);
+int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t M, uint32_t P, const void* d_cmap,
+              uint32_t* d_bitmap, uint64_t bitmap_words, uint64_t* d_word_off, void* d_ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------------------
+ * A5. Ring reduce-scatter arithmetic with slice skipping.
+ * [Ring] aggregation phase (n-1 steps; chunk j starts at rank j, each rank
+ * adds its own copy and forwards; rank (j-1) mod n ends with the full chunk);
+ * [Skip] section 4.2 Algorithms 1-2 (ReduceOrSkip: a skipping rank forwards
+ * what it received without adding; SkipReduce drops whole ring steps),
+ * section 4.3 (Random SkipReduce: ranks draw identical random numbers from a
+ * shared seed), section 4.1 (skip vs drop).
+ * Chunk j = [floor(jM/n), floor((j+1)M/n)), cut into slices of slice_bytes
+ * (slice q of chunk j starts q*slice_elems after the chunk start; the last one
+ * may be short).  S = ceil(ceil(M/n) / slice_elems) slices per chunk.  Ring
+ * position t = 0..n-1 of chunk j is rank (j+t) mod n.
+ * Seeded mode (d_include == NULL): position 0 is always kept; position t >= 1
+ * of (j, q) is skipped iff the top 24 bits of SplitMix64 output number
+ * (j*(n-1) + t-1)*S + q of the stream started at `seed` are below
+ * floor(p_skip * 2^24).
+ * Explicit mode: d_include [n][n][S] uint8 (nonzero = kept) for (j, t, q).
+ * Kept contributions are summed in fp32 in ring order t = 0, 1, ...; c = the
+ * number kept; SG_RESCALE_DROP multiplies by fp32(n)/fp32(c); c == 0 gives +0.
+ * Skipped slices are never read.
+ *   d_bufs  [n][M] of dt (bf16 is widened to fp32 before adding)
+ *   d_out   [M] fp32 out: chunk j in place at its own offsets
+ *   d_count [n][S] uint8 out (c per (j, q)), or NULL
+ * Limits: 1 <= n <= 64, 1 <= M < 2^40, slice_bytes a positive multiple of the
+ * element size, 0 <= p_skip <= 1.
+ * ------------------------------------------------------------------------ */
+uint64_t sg_skip_num_slices(uint32_t n, uint64_t M, uint64_t slice_bytes, sg_dtype dt);
+int sg_skip_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M, uint64_t slice_bytes,
+                           double p_skip, uint64_t seed, const uint8_t* d_include, sg_rescale mode, float* d_out,
+                           uint8_t* d_count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * A6. Sparsity statistics.
+ * [Zen] section 2.1: Def. 3 overlap ratio |I_a & I_b| / min(|I_a|, |I_b|);
+ * Def. 4 densification ratio gamma_n = d_n / d_G; Def. 5 n-partition skew
+ * ratio max_i d_{G_i} / d_G; section 3.1 Def. 8 push and pull imbalance.
+ * Readings: overlap is reported for every pair; gamma_n = n |I| / sum |I_w|
+ * (d_G = the workers' mean density); skew uses P contiguous parts
+ * G_i = [floor(iM/P), floor((i+1)M/P)) and, with a class map, the hash classes
+ * C_i (skew "after hashing"); push/pull imbalance use f = h0 with P servers.
+ * Every value is computed from exact counts with these double expressions:
+ *   overlap[a][b] = (double)inter / (double)min(nnz_a, nnz_b), 0 if the min is 0
+ *   overlap_mean  = (sum over a<b in lexicographic order) / (double)npairs
+ *   gamma_n       = ((double)n * (double)|I|) / (double)sum_nnz, 0 if sum is 0
+ *   skew(J)       = max_i ((double)c_i * (double)M) / ((double)g_i * (double)|J|)
+ *   push          = max_{w,i} ((double)P * (double)|I_w^i|) / (double)nnz_w
+ *   pull          = max_i ((double)P * (double)|I'_i|) / (double)|I|
+ * Inputs: n workers' COO index lists (d_idx, d_in_off as in sg_hash_partition).
+ * d_cmap: a class map for (M, P) from sg_classmap_build, or NULL (then the
+ * hashed fields are left untouched).  Blocks on `stream`.
+ * Limits: 1 <= n <= 64, 1 <= P <= 256, total < 2^32.
+ * ------------------------------------------------------------------------ */
+typedef struct sg_stats_out {
+    uint64_t union_size, sum_nnz, max_nnz;
+    uint64_t* nnz;           /* [n]        caller-provided host array */
+    uint64_t* inter;         /* [n*n]      |I_a & I_b| */
+    double* overlap;         /* [n*n] */
+    double overlap_mean, overlap_min, overlap_max; /* over pairs a < b */
+    double gamma_n;
+    uint64_t* contig_counts; /* [(n+1)*P]  row w: worker w, row n: the union */
+    double* skew_contig;     /* [n+1] */
+    uint64_t* class_size;    /* [P]        |C_i| (with a class map) */
+    uint64_t* hashed_counts; /* [(n+1)*P] */
+    double* skew_hashed;     /* [n+1] */
+    double push_imbalance, pull_imbalance;
+} sg_stats_out;
+
+size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P);
+int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total, uint32_t P,
+             const void* d_cmap, sg_stats_out* h_out, void* d_ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SG_H */

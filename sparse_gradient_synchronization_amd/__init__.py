@@ -1,0 +1,296 @@
+"""Python binding of libsg (include/sg.h): sparse gradient synchronization
+compute on one AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the HIP kernels of libsg.so;
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if libsg.so is missing or no GPU is present, the calls raise.
+
+The functions carry the names of the C entry points.  Tensors must be CUDA
+(ROCm) tensors on the current device; outputs and workspaces are allocated
+with torch on the input's device; calls are queued on
+``torch.cuda.current_stream()``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsg.so")
+
+SG_F32, SG_BF16 = 0, 1
+SG_RESCALE_NONE, SG_RESCALE_DROP = 0, 1
+
+_STATUS = {0: "SG_OK", -1: "SG_EINVAL", -2: "SG_ECAPACITY", -3: "SG_EUNSORTED", -4: "SG_EHIP",
+           -5: "SG_EUNSUPPORTED", -6: "SG_ERANGE", -7: "SG_EDEVICE"}
+
+
+class SgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, _STATUS.get(status, "?"), status))
+
+
+class StatsOut(C.Structure):
+    _fields_ = [
+        ("union_size", C.c_uint64), ("sum_nnz", C.c_uint64), ("max_nnz", C.c_uint64),
+        ("nnz", C.c_void_p), ("inter", C.c_void_p), ("overlap", C.c_void_p),
+        ("overlap_mean", C.c_double), ("overlap_min", C.c_double), ("overlap_max", C.c_double),
+        ("gamma_n", C.c_double),
+        ("contig_counts", C.c_void_p), ("skew_contig", C.c_void_p),
+        ("class_size", C.c_void_p), ("hashed_counts", C.c_void_p), ("skew_hashed", C.c_void_p),
+        ("push_imbalance", C.c_double), ("pull_imbalance", C.c_double),
+    ]
+
+
+_u32, _u64, _sz, _vp, _int, _dbl = C.c_uint32, C.c_uint64, C.c_size_t, C.c_void_p, C.c_int, C.c_double
+
+# C signatures of include/sg.h
+SIGNATURES = {
+    "sg_strerror": (C.c_char_p, [_int]),
+    "sg_device_error": (_int, [_vp]),
+    "sg_validate_workspace_bytes": (_sz, []),
+    "sg_validate_coo": (_int, [_vp, _vp, _u32, _u64, _u64, _vp, _sz, _vp]),
+    "sg_topk_workspace_bytes": (_sz, [_u32, _u64, _u64, _int]),
+    "sg_topk_to_coo": (_int, [_vp, _int, _u32, _u64, _u64, _vp, _vp, _vp, _sz, _vp]),
+    "sg_partition_workspace_bytes": (_sz, [_u32, _u64, _u32]),
+    "sg_hash_partition": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _sz,
+                                 _vp]),
+    "sg_aggregate_workspace_bytes": (_sz, [_u32, _u32, _u64, _u64, _u32]),
+    "sg_aggregate": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u32, _u64, _u64, _vp, _vp, _u64, _vp, _vp, _sz,
+                            _vp]),
+    "sg_classmap_bytes": (_sz, [_u64, _u32]),
+    "sg_classmap_build": (_int, [_u64, _u32, _u32, _vp, _sz, _vp]),
+    "sg_encode_max_words": (_u64, [_u64, _u32]),
+    "sg_encode_workspace_bytes": (_sz, [_u64, _u32]),
+    "sg_encode": (_int, [_vp, _vp, _u64, _u32, _vp, _vp, _u64, _vp, _vp, _sz, _vp]),
+    "sg_skip_num_slices": (_u64, [_u32, _u64, _u64, _int]),
+    "sg_skip_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _u64, _dbl, _u64, _vp, _int, _vp, _vp, _vp]),
+    "sg_stats_workspace_bytes": (_sz, [_u32, _u64, _u64, _u32]),
+    "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, C.POINTER(StatsOut), _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libsg.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsg.so is not built (run __graft_entry__.build() or "
+                               "python -m sparse_gradient_synchronization_amd.build)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            try:
+                f = getattr(L, name)
+            except AttributeError:
+                continue
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(SIGNATURES)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise SgError(rc, what)
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SG_F32
+    if t.dtype == torch.bfloat16:
+        return SG_BF16
+    raise TypeError("values must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _contig(t):
+    return None if t is None else t.contiguous()
+
+
+# --------------------------------------------------------------------------
+# the entry points
+# --------------------------------------------------------------------------
+
+def sg_topk_to_coo(dense: torch.Tensor, k: int, workspace: torch.Tensor | None = None):
+    """dense [n, M] float32/bfloat16 -> (idx [n, k] int32 holding uint32 indices, val [n, k])."""
+    _need_cuda(dense)
+    dense = dense.contiguous()
+    n, M = dense.shape
+    dt = _dtype_code(dense)
+    idx = torch.empty((n, k), dtype=torch.int32, device=dense.device)
+    val = torch.empty((n, k), dtype=dense.dtype, device=dense.device)
+    need = lib().sg_topk_workspace_bytes(n, M, k, dt)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, dense.device)
+    _check(lib().sg_topk_to_coo(_p(dense), dt, n, M, k, _p(idx), _p(val), _p(ws), ws.numel(), _stream()),
+           "sg_topk_to_coo")
+    return idx, val
+
+
+def sg_hash_partition(idx: torch.Tensor, val, in_off: torch.Tensor, P: int, seed: int,
+                      workspace: torch.Tensor | None = None):
+    """idx [total] int32, val None / [total] / [total, D], in_off [n+1] int64 ->
+    (out_idx, out_val, part_off [n, P+1] int64)."""
+    _need_cuda(idx, val, in_off)
+    idx, val, in_off = _contig(idx), _contig(val), _contig(in_off)
+    n = in_off.numel() - 1
+    total = idx.numel()
+    if val is None:
+        D, dt, out_val = 0, SG_F32, None
+    else:
+        D = 1 if val.dim() == 1 else val.shape[1]
+        dt = _dtype_code(val)
+        out_val = torch.empty_like(val)
+    out_idx = torch.empty_like(idx)
+    part_off = torch.empty((n, P + 1), dtype=torch.int64, device=idx.device)
+    need = lib().sg_partition_workspace_bytes(n, total, P)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
+    _check(lib().sg_hash_partition(_p(idx), _p(val), dt, D, _p(in_off), n, total, P, seed, _p(out_idx),
+                                   _p(out_val), _p(part_off), _p(ws), ws.numel(), _stream()),
+           "sg_hash_partition")
+    return out_idx, out_val, part_off
+
+
+def sg_aggregate(idx: torch.Tensor, val, part_off: torch.Tensor, M: int, workspace: torch.Tensor | None = None,
+                 capacity: int | None = None):
+    """Partitioned COO -> (agg_idx [capacity] int32, agg_val [capacity(, D)] float32, agg_off [P+1] int64).
+    The valid length is agg_off[P] (read after synchronizing)."""
+    _need_cuda(idx, val, part_off)
+    idx, val, part_off = _contig(idx), _contig(val), _contig(part_off)
+    n, P1 = part_off.shape
+    P = P1 - 1
+    total = idx.numel()
+    cap = total if capacity is None else capacity
+    if val is None:
+        D, dt, agg_val = 0, SG_F32, None
+    else:
+        D = 1 if val.dim() == 1 else val.shape[1]
+        dt = _dtype_code(val)
+        agg_val = torch.empty((max(cap, 1),) if D == 1 else (max(cap, 1), D), dtype=torch.float32,
+                              device=idx.device)
+    agg_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=idx.device)
+    agg_off = torch.empty(P + 1, dtype=torch.int64, device=idx.device)
+    need = lib().sg_aggregate_workspace_bytes(n, P, M, total, D)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
+    _check(lib().sg_aggregate(_p(idx), _p(val), dt, D, _p(part_off), n, P, M, total, _p(agg_idx), _p(agg_val),
+                              cap, _p(agg_off), _p(ws), ws.numel(), _stream()), "sg_aggregate")
+    return agg_idx, agg_val, agg_off
+
+
+def sg_classmap_build(M: int, P: int, seed: int, device=None):
+    """Class map of h0 over [0, M) (opaque uint8 tensor)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    nbytes = lib().sg_classmap_bytes(M, P)
+    cmap = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _check(lib().sg_classmap_build(M, P, seed, _p(cmap), cmap.numel(), _stream()), "sg_classmap_build")
+    return cmap
+
+
+def sg_encode(agg_idx: torch.Tensor, agg_off: torch.Tensor, M: int, cmap: torch.Tensor,
+              workspace: torch.Tensor | None = None):
+    """-> (bitmap [max_words] int32 holding uint32 words, word_off [P+1] int64)."""
+    _need_cuda(agg_idx, agg_off, cmap)
+    P = agg_off.numel() - 1
+    words = lib().sg_encode_max_words(M, P)
+    bitmap = torch.empty(max(words, 1), dtype=torch.int32, device=agg_idx.device)
+    word_off = torch.empty(P + 1, dtype=torch.int64, device=agg_idx.device)
+    need = lib().sg_encode_workspace_bytes(M, P)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, agg_idx.device)
+    _check(lib().sg_encode(_p(agg_idx.contiguous()), _p(agg_off.contiguous()), M, P, _p(cmap), _p(bitmap), words,
+                           _p(word_off), _p(ws), ws.numel(), _stream()), "sg_encode")
+    return bitmap, word_off
+
+
+def sg_skip_num_slices(n: int, M: int, slice_bytes: int, dtype=torch.float32) -> int:
+    return int(lib().sg_skip_num_slices(n, M, slice_bytes, SG_BF16 if dtype == torch.bfloat16 else SG_F32))
+
+
+def sg_skip_reduce_scatter(bufs: torch.Tensor, slice_bytes: int, p_skip: float, seed: int, include=None,
+                           mode: int = SG_RESCALE_DROP, want_count: bool = True, out=None):
+    """bufs [n, M] float32/bfloat16 -> (out [M] float32, count [n, S] uint8 or None)."""
+    _need_cuda(bufs, include)
+    bufs = bufs.contiguous()
+    n, M = bufs.shape
+    dt = _dtype_code(bufs)
+    S = lib().sg_skip_num_slices(n, M, slice_bytes, dt)
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=bufs.device)
+    count = torch.empty((n, S), dtype=torch.uint8, device=bufs.device) if want_count else None
+    if include is not None:
+        include = include.contiguous().to(torch.uint8)
+        if include.numel() != n * n * S:
+            raise ValueError("include must have n*n*S = %d entries" % (n * n * S))
+    _check(lib().sg_skip_reduce_scatter(_p(bufs), dt, n, M, slice_bytes, float(p_skip), seed & (2**64 - 1),
+                                        _p(include), mode, _p(out), _p(count), _stream()),
+           "sg_skip_reduce_scatter")
+    return out, count
+
+
+def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
+             workspace: torch.Tensor | None = None):
+    """Defs. 3-5 and 8 of the Zen page from exact counts.  Returns a dict."""
+    import numpy as np
+    _need_cuda(idx, in_off, cmap)
+    idx, in_off = idx.contiguous(), in_off.contiguous()
+    n = in_off.numel() - 1
+    total = idx.numel()
+    arr = dict(
+        nnz=np.zeros(n, np.uint64), inter=np.zeros(n * n, np.uint64), overlap=np.zeros(n * n, np.float64),
+        contig_counts=np.zeros((n + 1) * P, np.uint64), skew_contig=np.zeros(n + 1, np.float64),
+        class_size=np.zeros(P, np.uint64), hashed_counts=np.zeros((n + 1) * P, np.uint64),
+        skew_hashed=np.zeros(n + 1, np.float64))
+    o = StatsOut()
+    for k, a in arr.items():
+        setattr(o, k, a.ctypes.data)
+    need = lib().sg_stats_workspace_bytes(n, M, total, P)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
+    _check(lib().sg_stats(_p(idx), _p(in_off), n, M, total, P, _p(cmap), C.byref(o), _p(ws), ws.numel(),
+                          _stream()), "sg_stats")
+    res = dict(arr)
+    res["inter"] = res["inter"].reshape(n, n)
+    res["overlap"] = res["overlap"].reshape(n, n)
+    res["contig_counts"] = res["contig_counts"].reshape(n + 1, P)
+    res["hashed_counts"] = res["hashed_counts"].reshape(n + 1, P)
+    for k in ("union_size", "sum_nnz", "max_nnz"):
+        res[k] = int(getattr(o, k))
+    for k in ("overlap_mean", "overlap_min", "overlap_max", "gamma_n", "push_imbalance", "pull_imbalance"):
+        res[k] = float(getattr(o, k))
+    return res
+
+
+def sg_validate_coo(idx: torch.Tensor, in_off: torch.Tensor, M: int) -> int:
+    """Returns the status code (0 = valid)."""
+    _need_cuda(idx, in_off)
+    ws = _ws(lib().sg_validate_workspace_bytes(), idx.device)
+    n = in_off.numel() - 1
+    return int(lib().sg_validate_coo(_p(idx.contiguous()), _p(in_off.contiguous()), n, M, idx.numel(), _p(ws),
+                                     ws.numel(), _stream()))
+
+
+def sg_device_error() -> int:
+    return int(lib().sg_device_error(_stream()))

@@ -1,0 +1,5 @@
+// sg_lib.hip -- single translation unit of libsg (gfx950).  Every kernel
+// and the device error record live in one code object.
+#include "sg_common.hip"
+#include "sg_skiprs.hip"
+#include "sg_partition.hip"

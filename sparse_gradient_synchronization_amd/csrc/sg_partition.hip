@@ -1,0 +1,327 @@
+// sg_partition.hip -- A2: hash partition of n workers' COO entries.
+//
+// Zen (OSDI'25) digest, section 3.1 Problem 1 and section 3.2 Technique #3:
+// one partition hash h0 shared by all workers sends every index to the same
+// server.  Zen realises it with slot memory, rehashing and an atomic serial
+// area (Algorithm 1) because its extraction then runs nonzero() over the slot
+// memory.  Here the same membership comes from a stable multi-split with no
+// slot memory and no collisions: per 4096-entry tile a histogram of h0, one
+// scan of the per-(tile, partition) counts, and a scatter that ranks entries
+// inside the tile with wave64 ballots, stages them partition-sorted in LDS and
+// writes each partition's run with consecutive lanes on consecutive
+// addresses.  Reads: idx twice (histogram, scatter) and values once; writes:
+// idx and values once.
+#include "sg_host.h"
+
+namespace sg {
+
+constexpr int PT_THREADS = 256;
+constexpr int PT_TILE = 4096; // entries per tile
+constexpr int PT_WAVES = PT_THREADS / SG_WAVE;
+constexpr int PT_STRIPS = PT_TILE / PT_THREADS; // 64-entry strips per wave
+
+struct PartParams {
+    const uint32_t* idx;
+    const void* val;
+    const uint64_t* in_off;
+    uint32_t* out_idx;
+    void* out_val;
+    uint64_t* part_off;
+    uint32_t* tile_start; // [n+1] first global tile of worker w
+    uint32_t* counts;     // [max_tiles][P] counts, then destination offsets
+    uint64_t total;
+    uint32_t n, P, seed, D, esz, nbits;
+    uint32_t row_w4; // rows can be copied as 4-byte words
+    uint32_t max_tiles;
+    Divider div;
+};
+
+__device__ __forceinline__ void worker_range(const PartParams& p, uint32_t w, uint64_t& b, uint64_t& e)
+{
+    uint64_t x = p.in_off[w], y = p.in_off[w + 1];
+    if (x > p.total) x = p.total;
+    if (y > p.total) y = p.total;
+    if (y < x) y = x;
+    b = x;
+    e = y;
+}
+
+// tile_start[w] = sum over workers before w of ceil(len/TILE)
+__global__ void part_plan_kernel(PartParams p)
+{
+    __shared__ uint32_t scan_lds[PT_WAVES + 1];
+    uint32_t carry = 0;
+    bool bad = false;
+    for (uint32_t base = 0; base < p.n; base += PT_THREADS) {
+        uint32_t w = base + threadIdx.x;
+        uint32_t tiles = 0;
+        if (w < p.n) {
+            uint64_t b, e;
+            worker_range(p, w, b, e);
+            tiles = (uint32_t)ceil_div_dev(e - b, PT_TILE);
+            if (p.in_off[w] > p.in_off[w + 1] || p.in_off[w + 1] > p.total) bad = true;
+        }
+        uint32_t tot;
+        uint32_t ex = block_excl_scan<PT_THREADS>(tiles, scan_lds, &tot);
+        if (w < p.n) p.tile_start[w] = carry + ex;
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        p.tile_start[p.n] = carry;
+        if (p.in_off[0] != 0 || p.in_off[p.n] != p.total) bad = true;
+    }
+    if (bad) report_error(kDevErrBadOffsets);
+}
+
+// worker of global tile t (tile_start is non-decreasing)
+__device__ __forceinline__ uint32_t tile_worker(const PartParams& p, uint32_t t)
+{
+    uint32_t lo = 0, hi = p.n;
+    while (lo + 1 < hi) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (p.tile_start[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ bool tile_bounds(const PartParams& p, uint32_t t, uint32_t& w, uint64_t& e0,
+                                            uint64_t& e1)
+{
+    if (t >= p.tile_start[p.n]) return false;
+    w = tile_worker(p, t);
+    uint64_t b, e;
+    worker_range(p, w, b, e);
+    e0 = b + (uint64_t)(t - p.tile_start[w]) * PT_TILE;
+    e1 = e0 + PT_TILE < e ? e0 + PT_TILE : e;
+    return e0 < e1;
+}
+
+__global__ __launch_bounds__(PT_THREADS) void part_hist_kernel(PartParams p)
+{
+    __shared__ uint32_t hist[256];
+    const uint32_t t = blockIdx.x;
+    uint32_t w;
+    uint64_t e0, e1;
+    for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) hist[i] = 0;
+    __syncthreads();
+    bool live = tile_bounds(p, t, w, e0, e1);
+    if (live)
+        for (uint64_t e = e0 + threadIdx.x; e < e1; e += PT_THREADS) atomicAdd(&hist[h0(p.idx[e], p.seed, p.div)], 1u);
+    __syncthreads();
+    if (t < p.max_tiles)
+        for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) p.counts[(uint64_t)t * p.P + i] = live ? hist[i] : 0u;
+}
+
+// One block per worker: for each partition q, exclusive scan of counts over
+// the worker's tiles, offset by the start of partition q inside the worker.
+__global__ __launch_bounds__(PT_THREADS) void part_scan_kernel(PartParams p)
+{
+    __shared__ uint32_t scan_lds[PT_WAVES + 1];
+    __shared__ uint32_t totals[256];
+    const uint32_t w = blockIdx.x;
+    const uint32_t t0 = p.tile_start[w], t1 = p.tile_start[w + 1];
+    uint64_t b, e;
+    worker_range(p, w, b, e);
+    const uint32_t q = threadIdx.x;
+    uint32_t tot = 0;
+    if (q < p.P)
+        for (uint32_t t = t0; t < t1; ++t) tot += p.counts[(uint64_t)t * p.P + q];
+    uint32_t all;
+    uint32_t ex = block_excl_scan<PT_THREADS>(q < p.P ? tot : 0u, scan_lds, &all);
+    if (q < p.P) {
+        uint32_t run = (uint32_t)b + ex;
+        p.part_off[(uint64_t)w * (p.P + 1) + q] = run;
+        for (uint32_t t = t0; t < t1; ++t) {
+            uint32_t c = p.counts[(uint64_t)t * p.P + q];
+            p.counts[(uint64_t)t * p.P + q] = run;
+            run += c;
+        }
+    }
+    if (q == 0) p.part_off[(uint64_t)w * (p.P + 1) + p.P] = e;
+    (void)totals;
+}
+
+template <bool STAGE_VALS, typename VT>
+__global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
+{
+    __shared__ uint32_t keys_s[PT_TILE];
+    __shared__ VT vals_s[STAGE_VALS ? PT_TILE : 1];
+    __shared__ uint8_t part_s[PT_TILE];
+    __shared__ uint16_t rank_s[PT_TILE]; // input order -> staging position
+    __shared__ uint32_t wave_cnt[PT_WAVES][256];
+    __shared__ uint32_t lps[256];   // staging start of partition q
+    __shared__ uint32_t dbase[256]; // global destination of the tile's run of q
+    __shared__ uint32_t scan_lds[PT_WAVES + 1];
+
+    const uint32_t t = blockIdx.x;
+    uint32_t w;
+    uint64_t e0, e1;
+    if (!tile_bounds(p, t, w, e0, e1)) return; // uniform per block
+    const uint32_t len = (uint32_t)(e1 - e0);
+    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
+
+    for (uint32_t i = threadIdx.x; i < PT_WAVES * 256; i += PT_THREADS) (&wave_cnt[0][0])[i] = 0;
+    for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) dbase[i] = p.counts[(uint64_t)t * p.P + i];
+    __syncthreads();
+
+    // 1. stable ranks inside each wave's quarter of the tile
+    uint32_t key_r[PT_STRIPS];
+    uint8_t part_r[PT_STRIPS];
+    uint16_t rank_r[PT_STRIPS];
+    VT val_r[STAGE_VALS ? PT_STRIPS : 1];
+#pragma unroll
+    for (int s = 0; s < PT_STRIPS; ++s) {
+        const uint32_t le = wid * (PT_TILE / PT_WAVES) + s * SG_WAVE + lane;
+        const bool valid = le < len;
+        uint32_t key = valid ? p.idx[e0 + le] : 0u;
+        if (STAGE_VALS) val_r[s] = valid ? static_cast<const VT*>(p.val)[e0 + le] : VT(0);
+        uint32_t q = valid ? h0(key, p.seed, p.div) : 0u;
+        uint64_t peers = ballot(valid);
+        for (uint32_t bit = 0; bit < p.nbits; ++bit) {
+            uint64_t m = ballot(valid && ((q >> bit) & 1u));
+            peers &= ((q >> bit) & 1u) ? m : ~m;
+        }
+        uint32_t below = popc64(peers & lanemask_lt());
+        uint32_t base = valid ? wave_cnt[wid][q] : 0u;
+        if (valid && below == 0) wave_cnt[wid][q] = base + popc64(peers);
+        key_r[s] = key;
+        part_r[s] = (uint8_t)q;
+        rank_r[s] = (uint16_t)(base + below);
+    }
+    __syncthreads();
+
+    // 2. per-partition wave prefixes and staging starts
+    uint32_t tile_cnt = 0;
+    if (threadIdx.x < p.P) {
+        uint32_t acc = 0;
+        for (int v = 0; v < PT_WAVES; ++v) {
+            uint32_t c = wave_cnt[v][threadIdx.x];
+            wave_cnt[v][threadIdx.x] = acc;
+            acc += c;
+        }
+        tile_cnt = acc;
+    }
+    uint32_t all;
+    uint32_t ex = block_excl_scan<PT_THREADS>(tile_cnt, scan_lds, &all);
+    if (threadIdx.x < p.P) lps[threadIdx.x] = ex;
+    __syncthreads();
+
+    // 3. stage partition-sorted
+#pragma unroll
+    for (int s = 0; s < PT_STRIPS; ++s) {
+        const uint32_t le = wid * (PT_TILE / PT_WAVES) + s * SG_WAVE + lane;
+        if (le < len) {
+            uint32_t q = part_r[s];
+            uint32_t sp = lps[q] + wave_cnt[wid][q] + rank_r[s];
+            keys_s[sp] = key_r[s];
+            part_s[sp] = (uint8_t)q;
+            if (STAGE_VALS) vals_s[sp] = val_r[s];
+            rank_s[le] = (uint16_t)sp;
+        }
+    }
+    __syncthreads();
+
+    // 4. write each partition's run: consecutive lanes, consecutive addresses
+    for (uint32_t i = threadIdx.x; i < len; i += PT_THREADS) {
+        uint32_t q = part_s[i];
+        uint32_t dst = dbase[q] + (i - lps[q]);
+        if (dst < p.total) {
+            p.out_idx[dst] = keys_s[i];
+            if (STAGE_VALS) static_cast<VT*>(p.out_val)[dst] = vals_s[i];
+        }
+    }
+
+    // 5. rows (D >= 2): one wave per row, 4-byte words across lanes
+    if (!STAGE_VALS && p.D > 0) {
+        const uint32_t row_bytes = p.D * p.esz;
+        const bool w4 = p.row_w4 != 0;
+        for (uint32_t le = wid; le < len; le += PT_WAVES) {
+            uint32_t sp = rank_s[le];
+            uint32_t q = part_s[sp];
+            uint64_t dst = (uint64_t)dbase[q] + (sp - lps[q]);
+            if (dst >= p.total) continue;
+            const char* src = static_cast<const char*>(p.val) + (e0 + le) * (uint64_t)row_bytes;
+            char* out = static_cast<char*>(p.out_val) + dst * (uint64_t)row_bytes;
+            if (w4) {
+                const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
+                uint32_t* o4 = reinterpret_cast<uint32_t*>(out);
+                for (uint32_t k = lane; k < row_bytes / 4; k += SG_WAVE) o4[k] = s4[k];
+            } else {
+                const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
+                uint16_t* o2 = reinterpret_cast<uint16_t*>(out);
+                for (uint32_t k = lane; k < row_bytes / 2; k += SG_WAVE) o2[k] = s2[k];
+            }
+        }
+    }
+}
+
+} // namespace sg
+
+using namespace sg;
+
+static uint32_t part_max_tiles(uint32_t n, uint64_t total) { return (uint32_t)(ceil_div(total, PT_TILE) + n); }
+
+static uint64_t part_carve(Carver& c, uint32_t n, uint64_t total, uint32_t P, uint32_t** tile_start,
+                           uint32_t** counts)
+{
+    *tile_start = c.take<uint32_t>((uint64_t)n + 1);
+    *counts = c.take<uint32_t>((uint64_t)part_max_tiles(n, total) * P);
+    return c.bytes();
+}
+
+extern "C" size_t sg_partition_workspace_bytes(uint32_t n, uint64_t total, uint32_t P)
+{
+    Carver c(nullptr);
+    uint32_t *a, *b;
+    return part_carve(c, n, total, P, &a, &b);
+}
+
+extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
+                                 const uint64_t* d_in_off, uint32_t n, uint64_t total, uint32_t P, uint32_t seed,
+                                 uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, void* d_ws,
+                                 size_t ws_bytes, void* stream)
+{
+    if (n == 0 || P == 0 || P > 256 || D > 65536 || (dt != SG_F32 && dt != SG_BF16)) return SG_EINVAL;
+    if (total >= (1ull << 32)) return SG_EUNSUPPORTED;
+    if (!d_in_off || !d_part_off || !d_ws) return SG_EINVAL;
+    if (total > 0 && (!d_idx || !d_out_idx)) return SG_EINVAL;
+    if (D > 0 && total > 0 && (!d_val || !d_out_val)) return SG_EINVAL;
+    if (ws_bytes < sg_partition_workspace_bytes(n, total, P)) return SG_ECAPACITY;
+
+    PartParams p;
+    Carver c(d_ws);
+    part_carve(c, n, total, P, &p.tile_start, &p.counts);
+    p.idx = d_idx;
+    p.val = d_val;
+    p.in_off = d_in_off;
+    p.out_idx = d_out_idx;
+    p.out_val = d_out_val;
+    p.part_off = d_part_off;
+    p.total = total;
+    p.n = n;
+    p.P = P;
+    p.seed = seed;
+    p.D = D;
+    p.esz = dt == SG_BF16 ? 2 : 4;
+    p.nbits = 0;
+    while ((1u << p.nbits) < P) ++p.nbits;
+    p.max_tiles = part_max_tiles(n, total);
+    p.div = make_divider(P);
+    p.row_w4 = ((uint64_t)D * p.esz % 4 == 0) && ((uintptr_t)d_val % 4 == 0) && ((uintptr_t)d_out_val % 4 == 0);
+    hipStream_t st = as_stream(stream);
+
+    part_plan_kernel<<<1, PT_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    part_hist_kernel<<<p.max_tiles, PT_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    part_scan_kernel<<<n, PT_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    if (D == 0) part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
+    else if (D == 1 && dt == SG_F32) part_scatter_kernel<true, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
+    else if (D == 1) part_scatter_kernel<true, uint16_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
+    else part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    return SG_OK;
+}
