@@ -3,3 +3,4 @@
 #include "sg_common.hip"
 #include "sg_skiprs.hip"
 #include "sg_partition.hip"
+#include "sg_topk.hip"

@@ -1,0 +1,600 @@
+// sg_topk.hip -- A1: exact per-worker top-k by magnitude into COO.
+//
+// What is computed: DGC-style top-k sparsification (Zen OSDI'25 digest,
+// section 4: the top 5% of each gradient; SkipReduce MICRO'25 digest,
+// section 2: top-k keeps the largest magnitudes), exact, with ties taken
+// lowest index first and the output in ascending index order.
+//
+// How, on gfx950: the dense gradient is read from HBM once.
+//   1. sample:  16K strided magnitudes per worker, bitonic-sorted in LDS, give
+//               a band [lo, hi] that holds the k-th largest key with very high
+//               probability.
+//   2. filter:  one streaming pass; per 4096-element tile, entries with
+//               key >= lo are compacted in index order (wave ballots, no
+//               atomics) into the tile's own slot, and the candidate keys
+//               (lo <= key <= hi) into a second slot.
+//   3. totals:  per worker, the number of sure entries (key > hi) and of
+//               candidates; if the band missed, the worker is re-filtered with
+//               the band [0, max] (exact, slower).
+//   4. select:  MSD radix select (11-bit digits) over the candidate keys only
+//               gives the exact threshold key T and how many entries equal to
+//               T are taken.
+//   5. write:   per tile counts above/equal T, a per-worker scan, and an
+//               ordered compaction of the tile slots into idx[w][*], val[w][*].
+// Keys are magnitude bit patterns (sign cleared), which order like |x|.
+#include "sg_host.h"
+
+namespace sg {
+
+constexpr int TK_THREADS = 256;
+constexpr int TK_TILE = 4096;
+constexpr int TK_SAMPLES = 16384;
+constexpr int TK_DIGIT_BITS = 11;
+constexpr int TK_BINS = 1 << TK_DIGIT_BITS;
+constexpr int TK_HIST_GROUP = 128; // tiles per histogram block
+
+struct SelState {
+    uint32_t lo, hi;       // band
+    uint32_t redo;         // 1: band missed, worker re-filtered with [0, max]
+    uint32_t sure, cand;   // counts of key > hi and lo <= key <= hi
+    uint32_t R;            // rank still to find among candidates (1-based)
+    uint32_t prefix;       // fixed high bits of (T - lo)
+    uint32_t top;          // bits >= top of (T - lo) are fixed
+    uint32_t T, need;      // threshold key; entries equal to T to take
+    uint32_t pad[6];
+};
+
+struct TopkParams {
+    const void* dense;
+    uint32_t* out_idx;
+    void* out_val;
+    SelState* st;          // [n]
+    uint32_t* tcnt;        // [n*NT] entries with key >= lo
+    uint32_t* ccnt;        // [n*NT] candidates
+    uint32_t* slot_idx;    // [n*NT*TILE]
+    uint32_t* slot_val;    // [n*NT*TILE] value bits (bf16 in the low half)
+    uint32_t* slot_key;    // [n*NT*TILE] candidate keys
+    uint32_t* hist;        // [n][TK_BINS]
+    uint32_t* gtx;         // [n*NT] exclusive prefix of entries > T
+    uint32_t* eqx;         // [n*NT] exclusive prefix of entries == T
+    uint64_t M, k;
+    uint32_t n, NT;
+    uint32_t keymax;       // 0x7fffffff (fp32) or 0x7fff (bf16)
+    int bf16;
+};
+
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t bits, int bf16)
+{
+    return bf16 ? (bits & 0x7fffu) : (bits & 0x7fffffffu);
+}
+
+__device__ __forceinline__ uint32_t load_bits(const TopkParams& p, uint64_t i)
+{
+    return p.bf16 ? (uint32_t) static_cast<const uint16_t*>(p.dense)[i] : static_cast<const uint32_t*>(p.dense)[i];
+}
+
+// --------------------------------------------------------------------------
+// 1. band from a strided sample
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
+{
+    __shared__ uint32_t s[TK_SAMPLES];
+    const uint32_t w = blockIdx.x;
+    const uint64_t M = p.M;
+    const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
+    uint32_t N = 1;
+    while (N < S) N <<= 1;
+    for (uint32_t i = threadIdx.x; i < N; i += 1024) {
+        uint32_t v = 0;
+        if (i < S) {
+            uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
+            v = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
+        }
+        s[i] = v;
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (uint32_t kk = 2; kk <= N; kk <<= 1) {
+        for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
+            for (uint32_t i = threadIdx.x; i < N; i += 1024) {
+                uint32_t ixj = i ^ j;
+                if (ixj > i) {
+                    uint32_t a = s[i], b = s[ixj];
+                    bool up = (i & kk) == 0;
+                    if (up ? (a > b) : (a < b)) {
+                        s[i] = b;
+                        s[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (threadIdx.x == 0) {
+        SelState st;
+        for (int i = 0; i < 6; ++i) st.pad[i] = 0;
+        // s holds N - S zero pads in front; sample i (ascending) is s[N - S + i]
+        const uint32_t off = N - S;
+        uint32_t lo, hi;
+        if (S == M) {
+            // the sample is the whole worker: the band is the exact k-th largest key
+            lo = hi = s[off + (uint32_t)(M - p.k)];
+        } else {
+            double r = (double)p.k * (double)S / (double)M; // expected descending rank
+            double q = (double)p.k / (double)M;
+            double delta = 4.0 * sqrt(r * (1.0 - q)) + 8.0;
+            double rhi = floor(r - delta), rlo = ceil(r + delta);
+            // descending rank d is ascending index S - 1 - d
+            hi = (rhi < 0.0) ? p.keymax : s[off + (S - 1u - (uint32_t)rhi)];
+            lo = (rlo >= (double)S) ? 0u : s[off + (S - 1u - (uint32_t)rlo)];
+        }
+        st.lo = lo;
+        st.hi = hi;
+        st.redo = 0;
+        st.sure = st.cand = 0;
+        st.R = 0;
+        st.prefix = 0;
+        st.top = 0;
+        st.T = 0;
+        st.need = 0;
+        p.st[w] = st;
+    }
+}
+
+// --------------------------------------------------------------------------
+// 2. filter: one pass over the dense data
+// --------------------------------------------------------------------------
+// Element e of a tile, for iteration i, thread t, vector lane v:
+//   e = i * (TK_THREADS * EPV) + t * EPV + v      (EPV = 16 bytes / element size)
+template <int EPV, bool VEC>
+__device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uint32_t t, uint32_t lo, uint32_t hi,
+                                            uint32_t* chunk_ge, uint32_t* chunk_ca)
+{
+    constexpr int ITERS = TK_TILE / (TK_THREADS * EPV);
+    constexpr int NCH = ITERS * (TK_THREADS / SG_WAVE);
+    const uint32_t wid = threadIdx.x / SG_WAVE;
+    const uint64_t tile0 = (uint64_t)t * TK_TILE;
+    const uint64_t len = (p.M - tile0) < (uint64_t)TK_TILE ? (p.M - tile0) : (uint64_t)TK_TILE;
+    const uint64_t gbase = (uint64_t)w * p.M + tile0;
+    const uint64_t slot = ((uint64_t)w * p.NT + t) * TK_TILE;
+
+    uint32_t bits[ITERS][EPV];
+    const bool full = VEC && len == TK_TILE;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
+        if (full) {
+            if constexpr (EPV == 4) {
+                uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(p.dense) + gbase + e0);
+                bits[i][0] = x.x;
+                bits[i][1] = x.y;
+                bits[i][2] = x.z;
+                bits[i][3] = x.w;
+            } else {
+                uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dense) + gbase + e0);
+                uint32_t q[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int v = 0; v < EPV; ++v) bits[i][v] = (q[v / 2] >> (16 * (v % 2))) & 0xffffu;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < EPV; ++v)
+                bits[i][v] = (e0 + v < len) ? load_bits(p, gbase + e0 + v) : 0u;
+        }
+    }
+    // per-chunk counts (chunk = iteration i, wave wid), ordered i-major
+    uint32_t pre_ge[ITERS][EPV], pre_ca[ITERS][EPV];
+    uint32_t fl_ge = 0, fl_ca = 0;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
+        uint32_t below_ge = 0, below_ca = 0, tot_ge = 0, tot_ca = 0;
+        uint32_t own_ge = 0, own_ca = 0;
+#pragma unroll
+        for (int v = 0; v < EPV; ++v) {
+            uint32_t key = key_of_bits(bits[i][v], p.bf16);
+            bool valid = e0 + v < len;
+            bool ge = valid && key >= lo;
+            bool ca = ge && key <= hi;
+            uint64_t mg = ballot(ge), mc = ballot(ca);
+            below_ge += popc64(mg & lanemask_lt());
+            below_ca += popc64(mc & lanemask_lt());
+            tot_ge += popc64(mg);
+            tot_ca += popc64(mc);
+            pre_ge[i][v] = own_ge;
+            pre_ca[i][v] = own_ca;
+            own_ge += ge;
+            own_ca += ca;
+            fl_ge |= (uint32_t)ge << (i * EPV + v);
+            fl_ca |= (uint32_t)ca << (i * EPV + v);
+        }
+#pragma unroll
+        for (int v = 0; v < EPV; ++v) {
+            pre_ge[i][v] += below_ge;
+            pre_ca[i][v] += below_ca;
+        }
+        if (lane_id() == 0) {
+            chunk_ge[i * (TK_THREADS / SG_WAVE) + wid] = tot_ge;
+            chunk_ca[i * (TK_THREADS / SG_WAVE) + wid] = tot_ca;
+        }
+    }
+    __syncthreads();
+    // chunk prefixes (at most 16 chunks)
+    uint32_t base_ge[ITERS], base_ca[ITERS], all_ge = 0, all_ca = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int i = c / (TK_THREADS / SG_WAVE), cw = c % (TK_THREADS / SG_WAVE);
+        if (cw == (int)wid) {
+            base_ge[i] = all_ge;
+            base_ca[i] = all_ca;
+        }
+        all_ge += chunk_ge[c];
+        all_ca += chunk_ca[c];
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
+#pragma unroll
+        for (int v = 0; v < EPV; ++v) {
+            const int b = i * EPV + v;
+            if ((fl_ge >> b) & 1u) {
+                uint32_t pos = base_ge[i] + pre_ge[i][v];
+                p.slot_idx[slot + pos] = (uint32_t)(tile0 + e0 + v);
+                p.slot_val[slot + pos] = bits[i][v];
+            }
+            if ((fl_ca >> b) & 1u) p.slot_key[slot + base_ca[i] + pre_ca[i][v]] = key_of_bits(bits[i][v], p.bf16);
+        }
+    }
+    if (threadIdx.x == 0) {
+        p.tcnt[(uint64_t)w * p.NT + t] = all_ge;
+        p.ccnt[(uint64_t)w * p.NT + t] = all_ca;
+    }
+    __syncthreads(); // chunk arrays are reused by the next tile
+}
+
+// redo_only: process only workers whose band missed (st.redo == 1)
+template <int EPV, bool VEC>
+__global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(TopkParams p, int redo_only)
+{
+    __shared__ uint32_t chunk_ge[16], chunk_ca[16];
+    const uint64_t ntiles = (uint64_t)p.n * p.NT;
+    for (uint64_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+        const uint32_t w = (uint32_t)(g / p.NT), t = (uint32_t)(g % p.NT);
+        const SelState& st = p.st[w];
+        if (redo_only && st.redo == 0) {
+            // skip the rest of this worker's tiles in this block's stride
+            continue;
+        }
+        filter_tile<EPV, VEC>(p, w, t, st.lo, st.hi, chunk_ge, chunk_ca);
+    }
+}
+
+// --------------------------------------------------------------------------
+// 3. totals per worker; a missed band schedules a re-filter with [0, max]
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void topk_totals_kernel(TopkParams p, int second)
+{
+    __shared__ uint32_t red[2][16];
+    const uint32_t w = blockIdx.x;
+    uint32_t sure = 0, cand = 0;
+    for (uint32_t t = threadIdx.x; t < p.NT; t += 1024) {
+        uint32_t a = p.tcnt[(uint64_t)w * p.NT + t], c = p.ccnt[(uint64_t)w * p.NT + t];
+        sure += a - c;
+        cand += c;
+    }
+    sure = wave_sum(sure);
+    cand = wave_sum(cand);
+    if (lane_id() == 0) {
+        red[0][threadIdx.x / SG_WAVE] = sure;
+        red[1][threadIdx.x / SG_WAVE] = cand;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t S = 0, Cn = 0;
+        for (int i = 0; i < 16; ++i) {
+            S += red[0][i];
+            Cn += red[1][i];
+        }
+        SelState& st = p.st[w];
+        if (second && !st.redo) return; // this worker's first result stands
+        st.sure = S;
+        st.cand = Cn;
+        const uint64_t k = p.k;
+        const bool ok = (uint64_t)S < k && k <= (uint64_t)S + Cn;
+        if (!ok) {
+            if (!second) {
+                st.redo = 1;
+                st.lo = 0;
+                st.hi = p.keymax;
+            } else {
+                report_error(kDevErrPartition); // cannot happen with the full band
+            }
+            st.R = 0;
+        } else {
+            st.redo = second ? 2u : 0u;
+            st.R = (uint32_t)(k - S);
+            uint32_t span = st.hi - st.lo;
+            uint32_t nb = 0;
+            while (nb < 32 && (span >> nb) != 0) ++nb;
+            st.top = nb; // bits >= top of (T - lo) are known (zero)
+            st.prefix = 0;
+            st.T = st.lo;   // final when nb == 0 (the band is one key)
+            st.need = st.R;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// 4. radix select among the candidates
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void digit_window(uint32_t top, uint32_t& shift, uint32_t& width)
+{
+    shift = top > (uint32_t)TK_DIGIT_BITS ? top - TK_DIGIT_BITS : 0u;
+    width = top - shift;
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
+{
+    __shared__ uint32_t h[TK_BINS];
+    const uint32_t groups = (p.NT + TK_HIST_GROUP - 1) / TK_HIST_GROUP;
+    const uint32_t w = blockIdx.x / groups, gi = blockIdx.x % groups;
+    const SelState st = p.st[w];
+    if (st.R == 0 || st.top == 0) return;
+    uint32_t shift, width;
+    digit_window(st.top, shift, width);
+    for (uint32_t i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0;
+    __syncthreads();
+    const uint32_t t0 = gi * TK_HIST_GROUP;
+    const uint32_t t1 = t0 + TK_HIST_GROUP < p.NT ? t0 + TK_HIST_GROUP : p.NT;
+    const uint32_t wid = threadIdx.x / SG_WAVE;
+    for (uint32_t t = t0 + wid; t < t1; t += TK_THREADS / SG_WAVE) {
+        const uint64_t g = (uint64_t)w * p.NT + t;
+        const uint32_t c = p.ccnt[g];
+        const uint32_t* keys = p.slot_key + g * TK_TILE;
+        for (uint32_t i = lane_id(); i < c; i += SG_WAVE) {
+            uint32_t r = keys[i] - st.lo;
+            uint32_t hi_part = st.top >= 32 ? 0u : (r >> st.top);
+            uint32_t pre_part = st.top >= 32 ? 0u : (st.prefix >> st.top);
+            if (hi_part != pre_part) continue;
+            uint32_t d = (r >> shift) & ((1u << width) - 1u);
+            atomicAdd(&h[d], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* gh = p.hist + (uint64_t)w * TK_BINS;
+    for (uint32_t i = threadIdx.x; i < (1u << width); i += TK_THREADS)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// One block per worker: pick the digit holding rank R, then clear the
+// histogram for the next pass.
+__global__ __launch_bounds__(TK_THREADS) void topk_pick_kernel(TopkParams p)
+{
+    __shared__ uint32_t h[TK_BINS];
+    __shared__ uint32_t scan_lds[TK_THREADS / SG_WAVE + 1];
+    const uint32_t w = blockIdx.x;
+    SelState st = p.st[w];
+    uint32_t* gh = p.hist + (uint64_t)w * TK_BINS;
+    if (st.R == 0 || st.top == 0) return;
+    uint32_t shift, width;
+    digit_window(st.top, shift, width);
+    const uint32_t nbins = 1u << width;
+    for (uint32_t i = threadIdx.x; i < TK_BINS; i += TK_THREADS) {
+        h[i] = i < nbins ? gh[i] : 0u;
+        gh[i] = 0u;
+    }
+    __syncthreads();
+    // counts from the top digit down: thread j owns digits [j*8, j*8+8) of the
+    // reversed order
+    constexpr int PER = TK_BINS / TK_THREADS;
+    uint32_t loc[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        uint32_t d = nbins - 1u - (threadIdx.x * PER + i); // reversed digit
+        loc[i] = (threadIdx.x * PER + i < nbins) ? h[d] : 0u;
+        sum += loc[i];
+    }
+    uint32_t tot;
+    uint32_t ex = block_excl_scan<TK_THREADS>(sum, scan_lds, &tot);
+    __shared__ uint32_t pick_d, pick_above;
+    uint32_t run = ex;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        uint32_t rd = threadIdx.x * PER + i;
+        if (rd < nbins && run < st.R && st.R <= run + loc[i]) {
+            pick_d = nbins - 1u - rd;
+            pick_above = run;
+        }
+        run += loc[i];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        SelState& g = p.st[w];
+        if (tot < st.R) { // cannot happen: candidates were counted
+            report_error(kDevErrPartition);
+            g.R = 0;
+            return;
+        }
+        g.prefix = st.prefix | (pick_d << shift);
+        g.R = st.R - pick_above;
+        g.top = shift;
+        if (shift == 0) {
+            g.T = st.lo + g.prefix;
+            g.need = g.R;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// 5. counts per tile, per-worker scan, ordered write
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(TK_THREADS) void topk_tilecount_kernel(TopkParams p)
+{
+    const uint64_t g = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
+    if (g >= (uint64_t)p.n * p.NT) return;
+    const uint32_t w = (uint32_t)(g / p.NT);
+    const uint32_t T = p.st[w].T;
+    const uint32_t c = p.ccnt[g];
+    const uint32_t* keys = p.slot_key + g * TK_TILE;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = lane_id(); i < c; i += SG_WAVE) {
+        uint32_t key = keys[i];
+        gt += key > T;
+        eq += key == T;
+    }
+    gt = wave_sum(gt);
+    eq = wave_sum(eq);
+    if (lane_id() == 0) {
+        p.gtx[g] = p.tcnt[g] - c + gt; // sure entries are all above T
+        p.eqx[g] = eq;
+    }
+}
+
+__global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
+{
+    __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
+    const uint32_t w = blockIdx.x;
+    uint32_t carry_gt = 0, carry_eq = 0;
+    for (uint32_t base = 0; base < p.NT; base += 1024) {
+        const uint32_t t = base + threadIdx.x;
+        const uint64_t g = (uint64_t)w * p.NT + t;
+        uint32_t a = t < p.NT ? p.gtx[g] : 0u, b = t < p.NT ? p.eqx[g] : 0u;
+        uint32_t ta, tb;
+        uint32_t xa = block_excl_scan<1024>(a, scan_lds, &ta);
+        __syncthreads();
+        uint32_t xb = block_excl_scan<1024>(b, scan_lds, &tb);
+        if (t < p.NT) {
+            p.gtx[g] = carry_gt + xa;
+            p.eqx[g] = carry_eq + xb;
+        }
+        carry_gt += ta;
+        carry_eq += tb;
+        __syncthreads();
+    }
+}
+
+// one wave per tile: ordered compaction of the tile slot by (key > T) or
+// (key == T and its equal-rank < need)
+__global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
+{
+    const uint64_t g = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
+    if (g >= (uint64_t)p.n * p.NT) return;
+    const uint32_t w = (uint32_t)(g / p.NT);
+    const uint32_t T = p.st[w].T, need = p.st[w].need;
+    const uint32_t cnt = p.tcnt[g];
+    uint32_t eqr = p.eqx[g];
+    uint64_t pos = (uint64_t)p.gtx[g] + (eqr < need ? eqr : need);
+    const uint32_t* si = p.slot_idx + g * TK_TILE;
+    const uint32_t* sv = p.slot_val + g * TK_TILE;
+    const uint64_t obase = (uint64_t)w * p.k;
+    for (uint32_t i0 = 0; i0 < cnt; i0 += SG_WAVE) {
+        const uint32_t i = i0 + lane_id();
+        const bool valid = i < cnt;
+        uint32_t bits = valid ? sv[i] : 0u;
+        uint32_t key = key_of_bits(bits, p.bf16);
+        bool eq = valid && key == T;
+        uint64_t meq = ballot(eq);
+        uint32_t my_eq = eqr + popc64(meq & lanemask_lt());
+        bool sel = valid && (key > T || (eq && my_eq < need));
+        uint64_t ms = ballot(sel);
+        if (sel) {
+            uint64_t o = pos + popc64(ms & lanemask_lt());
+            if (o < p.k) {
+                p.out_idx[obase + o] = si[i];
+                if (p.bf16) static_cast<uint16_t*>(p.out_val)[obase + o] = (uint16_t)bits;
+                else static_cast<uint32_t*>(p.out_val)[obase + o] = bits;
+            }
+        }
+        pos += popc64(ms);
+        eqr += popc64(meq);
+    }
+}
+
+} // namespace sg
+
+using namespace sg;
+
+static uint64_t topk_carve(Carver& c, uint32_t n, uint64_t M, TopkParams* p)
+{
+    const uint64_t NT = ceil_div(M, TK_TILE);
+    const uint64_t nt = (uint64_t)n * NT;
+    p->st = c.take<SelState>(n);
+    p->tcnt = c.take<uint32_t>(nt);
+    p->ccnt = c.take<uint32_t>(nt);
+    p->gtx = c.take<uint32_t>(nt);
+    p->eqx = c.take<uint32_t>(nt);
+    p->hist = c.take<uint32_t>((uint64_t)n * TK_BINS);
+    p->slot_idx = c.take<uint32_t>(nt * TK_TILE);
+    p->slot_val = c.take<uint32_t>(nt * TK_TILE);
+    p->slot_key = c.take<uint32_t>(nt * TK_TILE);
+    return c.bytes();
+}
+
+extern "C" size_t sg_topk_workspace_bytes(uint32_t n, uint64_t M, uint64_t k, sg_dtype dt)
+{
+    (void)k;
+    (void)dt;
+    TopkParams p;
+    Carver c(nullptr);
+    return topk_carve(c, n, M, &p);
+}
+
+extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint64_t M, uint64_t k,
+                              uint32_t* d_idx, void* d_val, void* d_ws, size_t ws_bytes, void* stream)
+{
+    if (n == 0 || M == 0 || M >= (1ull << 32) || k > M || (dt != SG_F32 && dt != SG_BF16)) return SG_EINVAL;
+    if (k == 0) return SG_OK;
+    if (!d_dense || !d_idx || !d_val || !d_ws) return SG_EINVAL;
+    if (ws_bytes < sg_topk_workspace_bytes(n, M, k, dt)) return SG_ECAPACITY;
+    if ((uintptr_t)d_dense % 16) return SG_EINVAL;
+
+    TopkParams p;
+    Carver c(d_ws);
+    topk_carve(c, n, M, &p);
+    p.dense = d_dense;
+    p.out_idx = d_idx;
+    p.out_val = d_val;
+    p.M = M;
+    p.k = k;
+    p.n = n;
+    p.NT = (uint32_t)ceil_div(M, TK_TILE);
+    p.bf16 = dt == SG_BF16;
+    p.keymax = p.bf16 ? 0x7fffu : 0x7fffffffu;
+    // a full 16-byte vector must start on a 16-byte boundary in every row
+    const bool rows_aligned = (M * (p.bf16 ? 2 : 4)) % 16 == 0;
+    hipStream_t st = as_stream(stream);
+
+    int rc = fill_u32(p.hist, (uint64_t)n * TK_BINS, 0, st);
+    if (rc) return rc;
+    topk_sample_kernel<<<n, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    const uint64_t ntiles = (uint64_t)n * p.NT;
+    const unsigned fgrid = (unsigned)(ntiles < 8192 ? ntiles : 8192);
+    for (int pass = 0; pass < 2; ++pass) {
+        if (p.bf16) {
+            if (rows_aligned) topk_filter_kernel<8, true><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+            else topk_filter_kernel<8, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+        } else {
+            if (rows_aligned) topk_filter_kernel<4, true><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+            else topk_filter_kernel<4, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+        }
+        SG_TRY_LAUNCH();
+        topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
+        SG_TRY_LAUNCH();
+    }
+    const unsigned hgrid = n * (unsigned)ceil_div(p.NT, TK_HIST_GROUP);
+    for (int pass = 0; pass < 3; ++pass) {
+        topk_hist_kernel<<<hgrid, TK_THREADS, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        topk_pick_kernel<<<n, TK_THREADS, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+    }
+    const unsigned wgrid = (unsigned)ceil_div(ntiles, TK_THREADS / SG_WAVE);
+    topk_tilecount_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    topk_scan_kernel<<<n, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    topk_write_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    return SG_OK;
+}
