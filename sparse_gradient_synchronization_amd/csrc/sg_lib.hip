@@ -4,3 +4,5 @@
 #include "sg_skiprs.hip"
 #include "sg_partition.hip"
 #include "sg_topk.hip"
+#include "sg_merge.hip"
+#include "sg_aggregate.hip"
