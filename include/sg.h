@@ -161,9 +161,12 @@ int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t
  * Values need no re-encoding: the aggregate is already in C_p order.
  *
  * sg_classmap_build fills an opaque class map (setup, done once per (M, P,
- * seed), like the offline computation of the page).  sg_encode reads it.
+ * seed), like the offline computation of the page).  sg_encode reads it;
+ * cmap_bytes is the size of the caller's class-map buffer.
  *   d_agg_idx, d_agg_off  as produced by sg_aggregate (indices of partition p
- *                         ascending and with h0 = p)
+ *                         ascending and with h0 = p); agg_capacity is the
+ *                         number of entries d_agg_idx holds (offsets beyond it
+ *                         are clamped)
  *   d_bitmap   [bitmap_words] uint32 out, bitmap_words >= sg_encode_max_words(M, P)
  *   d_word_off [P+1] uint64 out
  * Limits: 1 <= P <= 256, 1 <= M < 2^32.
@@ -172,9 +175,9 @@ size_t sg_classmap_bytes(uint64_t M, uint32_t P);
 int sg_classmap_build(uint64_t M, uint32_t P, uint32_t seed, void* d_cmap, size_t cmap_bytes, void* stream);
 uint64_t sg_encode_max_words(uint64_t M, uint32_t P);
 size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P);
-int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t M, uint32_t P, const void* d_cmap,
-              uint32_t* d_bitmap, uint64_t bitmap_words, uint64_t* d_word_off, void* d_ws, size_t ws_bytes,
-              void* stream);
+int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg_capacity, uint64_t M, uint32_t P,
+              const void* d_cmap, size_t cmap_bytes, uint32_t* d_bitmap, uint64_t bitmap_words, uint64_t* d_word_off, void* d_ws,
+              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * A5. Ring reduce-scatter arithmetic with slice skipping.
@@ -245,7 +248,7 @@ typedef struct sg_stats_out {
 
 size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P);
 int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total, uint32_t P,
-             const void* d_cmap, sg_stats_out* h_out, void* d_ws, size_t ws_bytes, void* stream);
+             const void* d_cmap, size_t cmap_bytes, sg_stats_out* h_out, void* d_ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,11 +65,11 @@ SIGNATURES = {
     "sg_classmap_build": (_int, [_u64, _u32, _u32, _vp, _sz, _vp]),
     "sg_encode_max_words": (_u64, [_u64, _u32]),
     "sg_encode_workspace_bytes": (_sz, [_u64, _u32]),
-    "sg_encode": (_int, [_vp, _vp, _u64, _u32, _vp, _vp, _u64, _vp, _vp, _sz, _vp]),
+    "sg_encode": (_int, [_vp, _vp, _u64, _u64, _u32, _vp, _sz, _vp, _u64, _vp, _vp, _sz, _vp]),
     "sg_skip_num_slices": (_u64, [_u32, _u64, _u64, _int]),
     "sg_skip_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _u64, _dbl, _u64, _vp, _int, _vp, _vp, _vp]),
     "sg_stats_workspace_bytes": (_sz, [_u32, _u64, _u64, _u32]),
-    "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, C.POINTER(StatsOut), _vp, _sz, _vp]),
+    "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, _sz, C.POINTER(StatsOut), _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -221,7 +221,8 @@ def sg_encode(agg_idx: torch.Tensor, agg_off: torch.Tensor, M: int, cmap: torch.
     word_off = torch.empty(P + 1, dtype=torch.int64, device=agg_idx.device)
     need = lib().sg_encode_workspace_bytes(M, P)
     ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, agg_idx.device)
-    _check(lib().sg_encode(_p(agg_idx.contiguous()), _p(agg_off.contiguous()), M, P, _p(cmap), _p(bitmap), words,
+    _check(lib().sg_encode(_p(agg_idx.contiguous()), _p(agg_off.contiguous()), agg_idx.numel(), M, P, _p(cmap),
+                           cmap.numel(), _p(bitmap), words,
                            _p(word_off), _p(ws), ws.numel(), _stream()), "sg_encode")
     return bitmap, word_off
 
@@ -269,7 +270,8 @@ def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
         setattr(o, k, a.ctypes.data)
     need = lib().sg_stats_workspace_bytes(n, M, total, P)
     ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
-    _check(lib().sg_stats(_p(idx), _p(in_off), n, M, total, P, _p(cmap), C.byref(o), _p(ws), ws.numel(),
+    _check(lib().sg_stats(_p(idx), _p(in_off), n, M, total, P, _p(cmap), 0 if cmap is None else cmap.numel(),
+                          C.byref(o), _p(ws), ws.numel(),
                           _stream()), "sg_stats")
     res = dict(arr)
     res["inter"] = res["inter"].reshape(n, n)

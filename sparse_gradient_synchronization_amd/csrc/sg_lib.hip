@@ -6,3 +6,4 @@
 #include "sg_topk.hip"
 #include "sg_merge.hip"
 #include "sg_aggregate.hip"
+#include "sg_encode.hip"
