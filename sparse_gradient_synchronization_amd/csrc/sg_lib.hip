@@ -7,3 +7,4 @@
 #include "sg_merge.hip"
 #include "sg_aggregate.hip"
 #include "sg_encode.hip"
+#include "sg_stats.hip"

@@ -1,0 +1,235 @@
+// sg_stats.hip -- A6: sparsity statistics of n workers' index sets, from
+// exact integer counts (Zen OSDI'25 digest, section 2.1 Defs. 3-5; section
+// 3.1 Def. 8).
+//
+// The union and every pairwise intersection come from the merge engine run
+// over the workers' lists (one group): per union index the set of workers
+// holding it is a 64-bit mask; per 64 indices a wave turns the masks into one
+// ballot word per worker and adds popcount(V_a & V_b) for each pair.  Per-part
+// counts of each worker come from one pass over the entries.  The host then
+// evaluates the definitions in double with fixed expressions.
+#include "sg_host.h"
+
+namespace sg {
+
+struct StatsCounts {
+    uint64_t* inter;    // [n*n] (a <= b filled)
+    uint64_t* uni;      // [1]
+    uint64_t* ucontig;  // [Ps]
+    uint64_t* uhashed;  // [Ps]
+    uint64_t* wcontig;  // [n*Ps]
+    uint64_t* whashed;  // [n*Ps]
+};
+
+// per-worker counts per contiguous part and per hash class; one block per
+// 4096-entry chunk of a worker (chunk plan of the merge engine, G = 1)
+__global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, StatsCounts c)
+{
+    __shared__ uint32_t hc[256], hh[256];
+    const uint32_t R = p.n;
+    const uint32_t ch = blockIdx.x;
+    if (ch >= p.chunk_start[R]) return;
+    uint32_t lo = 0, hi = R;
+    while (lo + 1 < hi) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (p.chunk_start[mid] <= ch) lo = mid;
+        else hi = mid;
+    }
+    const uint32_t w = lo;
+    for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
+    __syncthreads();
+    uint64_t s, e;
+    run_range(p, 0, w, s, e);
+    const uint64_t j0 = (uint64_t)(ch - p.chunk_start[w]) * MG_CHUNK;
+    for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && s + j < e; j += MG_THREADS) {
+        const uint32_t key = p.idx[s + j];
+        atomicAdd(&hc[contig_part(key, p.M, p.Ps)], 1u);
+        if (p.hashed) atomicAdd(&hh[h0(key, p.seed, p.div)], 1u);
+    }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
+        if (hc[i]) atomicAdd((unsigned long long*)&c.wcontig[(uint64_t)w * p.Ps + i], (unsigned long long)hc[i]);
+        if (p.hashed && hh[i]) atomicAdd((unsigned long long*)&c.whashed[(uint64_t)w * p.Ps + i], (unsigned long long)hh[i]);
+    }
+}
+
+} // namespace sg
+
+using namespace sg;
+
+static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total)
+{
+    *p = MergeParams();
+    p->n = n;
+    p->G = 1;
+    p->stride = 1;
+    p->M = M;
+    p->total = total;
+    choose_buckets(n, 1, M, total, &p->bs, &p->NB);
+}
+
+static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k)
+{
+    const uint32_t n = p->n;
+    merge_carve(c, p);
+    k->inter = c.take<uint64_t>((uint64_t)n * n);
+    k->uni = c.take<uint64_t>(1);
+    k->ucontig = c.take<uint64_t>(P);
+    k->uhashed = c.take<uint64_t>(P);
+    k->wcontig = c.take<uint64_t>((uint64_t)n * P);
+    k->whashed = c.take<uint64_t>((uint64_t)n * P);
+    return c.bytes();
+}
+
+extern "C" size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P)
+{
+    if (n == 0 || P == 0) return 256;
+    MergeParams p;
+    stats_setup(&p, n, M, total);
+    Carver c(nullptr);
+    StatsCounts k;
+    return stats_carve(c, &p, P, &k);
+}
+
+// Def. 5 on one set J: max over parts of (c_i M) / (g_i |J|); 0 if J is empty.
+static double skew_of(const uint64_t* c, const uint64_t* g, uint32_t P, uint64_t M, uint64_t J)
+{
+    double best = 0.0;
+    if (J == 0) return 0.0;
+    for (uint32_t i = 0; i < P; ++i) {
+        if (g[i] == 0) continue;
+        const double s = ((double)c[i] * (double)M) / ((double)g[i] * (double)J);
+        if (s > best) best = s;
+    }
+    return best;
+}
+
+extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                        uint32_t P, const void* d_cmap, size_t cmap_bytes, sg_stats_out* o, void* d_ws,
+                        size_t ws_bytes, void* stream)
+{
+    if (n == 0 || n > 64 || P == 0 || P > 256 || !o || !d_in_off || !d_ws) return SG_EINVAL;
+    if (M == 0 || M >= (1ull << 32) || total >= (1ull << 32)) return SG_EUNSUPPORTED;
+    if (total > 0 && !d_idx) return SG_EINVAL;
+    if (!o->nnz || !o->inter || !o->overlap || !o->contig_counts || !o->skew_contig) return SG_EINVAL;
+    if (d_cmap && (!o->class_size || !o->hashed_counts || !o->skew_hashed)) return SG_EINVAL;
+    if (ws_bytes < sg_stats_workspace_bytes(n, M, total, P)) return SG_ECAPACITY;
+    hipStream_t st = as_stream(stream);
+
+    uint32_t seed = 0;
+    std::vector<uint64_t> class_size(P, 0);
+    if (d_cmap) {
+        const CmapLayout L = cmap_layout(M, P);
+        if (cmap_bytes < L.bytes) return SG_ECAPACITY;
+        CmapHeader h;
+        CmapPtrs q = cmap_ptrs(const_cast<void*>(d_cmap), L);
+        SG_TRY(hipMemcpyAsync(&h, q.hdr, sizeof(h), hipMemcpyDeviceToHost, st));
+        SG_TRY(hipMemcpyAsync(class_size.data(), q.class_size, 8ull * P, hipMemcpyDeviceToHost, st));
+        SG_TRY(hipStreamSynchronize(st));
+        if (h.magic != CM_MAGIC || h.P != P || h.M != M) return SG_EINVAL;
+        seed = h.seed;
+    }
+
+    MergeParams p;
+    stats_setup(&p, n, M, total);
+    Carver c(d_ws);
+    StatsCounts k;
+    stats_carve(c, &p, P, &k);
+    p.idx = d_idx;
+    p.off = d_in_off;
+    p.Ps = P;
+    p.seed = seed;
+    p.hashed = d_cmap != nullptr;
+    p.div = make_divider(P);
+    p.st_inter = k.inter;
+    p.st_union = k.uni;
+    p.st_ucontig = k.ucontig;
+    p.st_uhashed = k.uhashed;
+    // counters live contiguously after the merge workspace: zero them at once
+    const uint64_t cnt_words = (uint64_t)((char*)(k.whashed + (uint64_t)n * P) - (char*)k.inter) / 8;
+    int rc = fill_u64(k.inter, cnt_words, 0, st);
+    if (rc) return rc;
+    rc = merge_run(p, MODE_STATS, st);
+    if (rc) return rc;
+    st_entries_kernel<<<(unsigned)(ceil_div(total, MG_CHUNK) + n), MG_THREADS, 0, st>>>(p, k);
+    SG_TRY_LAUNCH();
+
+    std::vector<uint64_t> inter((size_t)n * n), wc((size_t)n * P), wh((size_t)n * P), uc(P), uh(P), off(n + 1);
+    uint64_t uni = 0;
+    SG_TRY(hipMemcpyAsync(inter.data(), k.inter, 8ull * n * n, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(&uni, k.uni, 8, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(uc.data(), k.ucontig, 8ull * P, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(uh.data(), k.uhashed, 8ull * P, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(wc.data(), k.wcontig, 8ull * n * P, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(wh.data(), k.whashed, 8ull * n * P, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(off.data(), d_in_off, 8ull * (n + 1), hipMemcpyDeviceToHost, st));
+    SG_TRY(hipStreamSynchronize(st));
+
+    // exact counts
+    o->sum_nnz = 0;
+    o->max_nnz = 0;
+    for (uint32_t a = 0; a < n; ++a) {
+        uint64_t x = off[a] > total ? total : off[a], y = off[a + 1] > total ? total : off[a + 1];
+        o->nnz[a] = y > x ? y - x : 0;
+        o->sum_nnz += o->nnz[a];
+        if (o->nnz[a] > o->max_nnz) o->max_nnz = o->nnz[a];
+    }
+    o->union_size = uni;
+    for (uint32_t a = 0; a < n; ++a)
+        for (uint32_t b = 0; b < n; ++b) o->inter[(uint64_t)a * n + b] = a <= b ? inter[(size_t)a * n + b] : inter[(size_t)b * n + a];
+    // Def. 3 over all pairs
+    uint64_t npairs = 0;
+    double sum_ov = 0.0;
+    o->overlap_min = 0.0;
+    o->overlap_max = 0.0;
+    for (uint32_t a = 0; a < n; ++a)
+        for (uint32_t b = 0; b < n; ++b) {
+            const uint64_t mn = o->nnz[a] < o->nnz[b] ? o->nnz[a] : o->nnz[b];
+            const double ov = mn ? (double)o->inter[(uint64_t)a * n + b] / (double)mn : 0.0;
+            o->overlap[(uint64_t)a * n + b] = ov;
+            if (a < b) {
+                if (npairs == 0 || ov < o->overlap_min) o->overlap_min = ov;
+                if (npairs == 0 || ov > o->overlap_max) o->overlap_max = ov;
+                sum_ov += ov;
+                ++npairs;
+            }
+        }
+    o->overlap_mean = npairs ? sum_ov / (double)npairs : 0.0;
+    // Def. 4
+    o->gamma_n = o->sum_nnz ? ((double)n * (double)o->union_size) / (double)o->sum_nnz : 0.0;
+    // Def. 5, contiguous parts
+    std::vector<uint64_t> g(P);
+    for (uint32_t i = 0; i < P; ++i)
+        g[i] = (uint64_t)(((unsigned __int128)M * (i + 1)) / P) - (uint64_t)(((unsigned __int128)M * i) / P);
+    for (uint32_t a = 0; a < n; ++a) {
+        for (uint32_t i = 0; i < P; ++i) o->contig_counts[(uint64_t)a * P + i] = wc[(size_t)a * P + i];
+        o->skew_contig[a] = skew_of(&wc[(size_t)a * P], g.data(), P, M, o->nnz[a]);
+    }
+    for (uint32_t i = 0; i < P; ++i) o->contig_counts[(uint64_t)n * P + i] = uc[i];
+    o->skew_contig[n] = skew_of(uc.data(), g.data(), P, M, o->union_size);
+    // hash classes and Def. 8
+    o->push_imbalance = 0.0;
+    o->pull_imbalance = 0.0;
+    if (d_cmap) {
+        for (uint32_t i = 0; i < P; ++i) o->class_size[i] = class_size[i];
+        for (uint32_t a = 0; a < n; ++a) {
+            for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)a * P + i] = wh[(size_t)a * P + i];
+            o->skew_hashed[a] = skew_of(&wh[(size_t)a * P], class_size.data(), P, M, o->nnz[a]);
+        }
+        for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)n * P + i] = uh[i];
+        o->skew_hashed[n] = skew_of(uh.data(), class_size.data(), P, M, o->union_size);
+        for (uint32_t a = 0; a < n; ++a) {
+            if (o->nnz[a] == 0) continue;
+            for (uint32_t i = 0; i < P; ++i) {
+                const double v = ((double)P * (double)wh[(size_t)a * P + i]) / (double)o->nnz[a];
+                if (v > o->push_imbalance) o->push_imbalance = v;
+            }
+        }
+        if (o->union_size)
+            for (uint32_t i = 0; i < P; ++i) {
+                const double v = ((double)P * (double)uh[i]) / (double)o->union_size;
+                if (v > o->pull_imbalance) o->pull_imbalance = v;
+            }
+    }
+    return SG_OK;
+}

@@ -1,0 +1,63 @@
+"""GPU parity of sg_stats against the oracle: every count bit-exact and every
+ratio (Defs. 3, 4, 5 and 8 of the Zen page) equal as a double."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import sparse_gradient_synchronization_amd as sg
+from gpu_util import need_gpu, to_dev_u32, to_dev_u64
+
+pytestmark = pytest.mark.gpu
+
+INT_KEYS = ("nnz", "inter", "contig_counts")
+HASH_INT_KEYS = ("class_size", "hashed_counts")
+FLOAT_KEYS = ("overlap", "skew_contig")
+SCALARS = ("union_size", "sum_nnz", "max_nnz", "overlap_mean", "overlap_min", "overlap_max", "gamma_n")
+
+
+def _check(idx, in_off, M, P, seed=None):
+    need_gpu()
+    cmap = None if seed is None else sg.sg_classmap_build(M, P, seed)
+    got = sg.sg_stats(to_dev_u32(idx if idx.size else np.zeros(1, np.uint32))[: idx.size], to_dev_u64(in_off), M, P,
+                      cmap=cmap)
+    ref = oracle.stats(idx, in_off, M, P, hashed=seed is not None, seed=seed or 0)
+    for k in INT_KEYS + FLOAT_KEYS:
+        assert np.array_equal(got[k], ref[k]), k
+    for k in SCALARS:
+        assert got[k] == ref[k], (k, got[k], ref[k])
+    if seed is not None:
+        for k in HASH_INT_KEYS:
+            assert np.array_equal(got[k], ref[k]), k
+        assert np.array_equal(got["skew_hashed"], ref["skew_hashed"])
+        assert got["push_imbalance"] == ref["push_imbalance"]
+        assert got["pull_imbalance"] == ref["pull_imbalance"]
+    assert sg.sg_device_error() == 0
+    return got
+
+
+@pytest.mark.parametrize("n,P", [(1, 1), (2, 2), (4, 4), (7, 3), (16, 16), (64, 8)])
+def test_stats_zipf(n, P):
+    idx, in_off, _ = gen.coo_zipf(500 + n, n, 120000, 3000, 1.1)
+    _check(idx, in_off, 120000, P, seed=13)
+    _check(idx, in_off, 120000, P)
+
+
+def test_stats_identical_disjoint_empty():
+    a = np.arange(0, 5000, 2, dtype=np.uint32)
+    b = np.arange(1, 5000, 2, dtype=np.uint32)
+    idx, in_off, _ = gen.coo_from_lists([a, a, b, np.zeros(0, np.uint32)], [a, a, b, a[:0]])
+    g = _check(idx, in_off, 5000, 4, seed=2)
+    assert g["inter"][0, 1] == a.size and g["inter"][0, 2] == 0
+
+
+def test_stats_config1_full():
+    c = gen.config1()
+    _check(c["idx"], c["in_off"], c["M"], c["P"], seed=c["seed"])
+
+
+def test_stats_config4_full():
+    c = gen.config4()
+    g = _check(c["idx"], c["in_off"], c["M"], c["P"], seed=c["seed"])
+    # skewed before hashing, balanced after (Zen section 2.1 C3 and Theorem 2)
+    assert g["skew_contig"][:16].min() > 4.5 and g["skew_hashed"].max() < 1.05
