@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse gradient synchronization hot path on one MI355X.
+
+One step = one pass of every stage of the path over one batch of synthetic
+input already resident in HBM:
+
+  default workload "dgc-top5": n=8 workers, dense fp32 gradients of
+  4096 x 11008 each (per-row lognormal scale, 0.7 inter-worker correlation),
+    A1 top-5% per worker into COO            sg_topk_to_coo
+    A2 hash partition into 8                  sg_hash_partition
+    A3 per-partition union-sum                sg_aggregate
+    A4 hash-bitmap encode                     sg_encode
+    A6 overlap / densification / skew stats   sg_stats
+    A5 the dense counterpart on the same gradients: ring reduce-scatter
+       arithmetic, 256 KiB slices skipped w.p. 0.5, DropReduce rescale
+                                              sg_skip_reduce_scatter
+
+Metric: aggregated input nonzeros per second (the n*k COO entries that enter
+aggregation, divided by the step time), plus the HBM roofline of the step's
+dominant kernel timed with HIP events on the stream it runs on.
+
+Other workloads (--workload cfg1|cfg2|cfg4|cfg5) time the stages that apply
+to them; they are reported in the same format.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+
+METRIC = "aggregated input nonzeros/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Two raw HIP events (the probe hook of libsg records them around one
+    kernel inside a multi-kernel call)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.start = C.c_void_p()
+        self.stop = C.c_void_p()
+        assert self.hip.hipEventCreate(C.byref(self.start)) == 0
+        assert self.hip.hipEventCreate(C.byref(self.stop)) == 0
+
+    def elapsed_ms(self):
+        assert self.hip.hipEventSynchronize(self.stop) == 0
+        ms = C.c_float()
+        assert self.hip.hipEventElapsedTime(C.byref(ms), self.start, self.stop) == 0
+        return float(ms.value)
+
+
+def build_workload(name, torch, sg, gen):
+    """Inputs on the GPU, preallocated outputs/workspaces, and the stage list."""
+    L = sg.lib()
+    dev = torch.device("cuda", 0)
+    u32 = lambda a: torch.from_numpy(a.view("int32")).to(dev)  # noqa: E731
+    u64 = lambda a: torch.from_numpy(a.view("int64")).to(dev)  # noqa: E731
+    W = {"name": name}
+    stages = []
+    nbytes = {}
+
+    def vp(t):
+        return None if t is None else C.c_void_p(t.data_ptr())
+
+    stream = lambda: C.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+
+    def chk(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed with status %d" % (what, rc))
+
+    import numpy as np
+
+    if name in ("dgc-top5", "cfg1"):
+        c = gen.config3() if name == "dgc-top5" else gen.config1()
+        n, M, k, P, seed = c["n"], c["M"], c["k"], c["P"], c["seed"]
+        dense = torch.from_numpy(c["dense"]).to(dev)
+        W.update(n=n, M=M, k=k, P=P)
+        idx = torch.empty(n * k, dtype=torch.int32, device=dev)
+        val = torch.empty(n * k, dtype=torch.float32, device=dev)
+        ws_t = torch.empty(L.sg_topk_workspace_bytes(n, M, k, 0), dtype=torch.uint8, device=dev)
+        in_off_np = np.arange(n + 1, dtype=np.uint64) * np.uint64(k)
+        in_off = u64(in_off_np)
+        total = n * k
+
+        def topk():
+            chk(L.sg_topk_to_coo(vp(dense), 0, n, M, k, vp(idx), vp(val), vp(ws_t), ws_t.numel(), stream()),
+                "sg_topk_to_coo")
+        stages.append(("topk_to_coo", topk))
+        nbytes["topk_to_coo"] = n * M * 4 + n * k * 8
+        src_idx, src_val, D = idx, val, 1
+    elif name in ("cfg2", "cfg4"):
+        c = gen.config2() if name == "cfg2" else gen.config4()
+        n, M, P, seed = c["n"], c["M"], c["P"], c["seed"]
+        D = c.get("D", 1)
+        src_idx = u32(c["idx"])
+        src_val = torch.from_numpy(c["val"]).to(dev)
+        in_off = u64(c["in_off"])
+        total = int(c["in_off"][-1])
+        W.update(n=n, M=M, P=P, D=D, total=total)
+    elif name == "cfg5":
+        c = gen.config5()
+        n, M = c["n"], c["M"]
+        W.update(n=n, M=M, slice_bytes=c["slice_elems"] * 4, p_skip=c["p"])
+        total = None
+    else:
+        raise SystemExit("unknown workload %s" % name)
+
+    if name != "cfg5":
+        pidx = torch.empty(total, dtype=torch.int32, device=dev)
+        pval = torch.empty_like(src_val)
+        part_off = torch.empty((n, P + 1), dtype=torch.int64, device=dev)
+        ws_p = torch.empty(L.sg_partition_workspace_bytes(n, total, P), dtype=torch.uint8, device=dev)
+        agg_idx = torch.empty(total, dtype=torch.int32, device=dev)
+        agg_val = torch.empty((total, D) if D > 1 else (total,), dtype=torch.float32, device=dev)
+        agg_off = torch.empty(P + 1, dtype=torch.int64, device=dev)
+        ws_a = torch.empty(L.sg_aggregate_workspace_bytes(n, P, M, total, D), dtype=torch.uint8, device=dev)
+        cmap = sg.sg_classmap_build(M, P, seed)
+        words = L.sg_encode_max_words(M, P)
+        bitmap = torch.empty(words, dtype=torch.int32, device=dev)
+        word_off = torch.empty(P + 1, dtype=torch.int64, device=dev)
+        ws_e = torch.empty(L.sg_encode_workspace_bytes(M, P), dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(L.sg_stats_workspace_bytes(n, M, total, P), dtype=torch.uint8, device=dev)
+        st_arr = dict(
+            nnz=np.zeros(n, np.uint64), inter=np.zeros(n * n, np.uint64), overlap=np.zeros(n * n, np.float64),
+            contig_counts=np.zeros((n + 1) * P, np.uint64), skew_contig=np.zeros(n + 1, np.float64),
+            class_size=np.zeros(P, np.uint64), hashed_counts=np.zeros((n + 1) * P, np.uint64),
+            skew_hashed=np.zeros(n + 1, np.float64))
+        so = sg.StatsOut()
+        for key, a in st_arr.items():
+            setattr(so, key, a.ctypes.data)
+        W["stats_out"] = so
+        W["stats_arrays"] = st_arr  # keeps the host arrays alive
+
+        def part():
+            chk(L.sg_hash_partition(vp(src_idx), vp(src_val), 0, D, vp(in_off), n, total, P, seed, vp(pidx), vp(pval),
+                                    vp(part_off), vp(ws_p), ws_p.numel(), stream()), "sg_hash_partition")
+
+        def agg():
+            chk(L.sg_aggregate(vp(pidx), vp(pval), 0, D, vp(part_off), n, P, M, total, vp(agg_idx), vp(agg_val),
+                               total, vp(agg_off), vp(ws_a), ws_a.numel(), stream()), "sg_aggregate")
+
+        def enc():
+            chk(L.sg_encode(vp(agg_idx), vp(agg_off), total, M, P, vp(cmap), cmap.numel(), vp(bitmap), words,
+                            vp(word_off), vp(ws_e), ws_e.numel(), stream()), "sg_encode")
+
+        def stats():
+            chk(L.sg_stats(vp(src_idx), vp(in_off), n, M, total, P, vp(cmap), cmap.numel(), C.byref(so), vp(ws_s),
+                           ws_s.numel(), stream()), "sg_stats")
+
+        stages += [("hash_partition", part), ("aggregate", agg), ("encode", enc), ("stats", stats)]
+        esz = 4 * D
+        nbytes["hash_partition"] = 2 * total * (4 + esz)
+        W["agg_off"] = agg_off
+        W["word_off"] = word_off
+        W["bytes_agg"] = lambda U: total * (4 + esz) + U * (4 + 4 * D)  # noqa: E731
+        W["bytes_enc"] = lambda U, words_: U * 4 + words_ * 4  # noqa: E731
+        W["nnz"] = total
+
+    if name in ("dgc-top5", "cfg5"):
+        bufs = dense if name == "dgc-top5" else torch.from_numpy(c["bufs"]).to(dev)
+        slice_bytes = 256 * 1024
+        S = L.sg_skip_num_slices(n, M, slice_bytes, 0)
+        rs_out = torch.empty(M, dtype=torch.float32, device=dev)
+        rs_cnt = torch.empty((n, S), dtype=torch.uint8, device=dev)
+        rs_seed = 5
+
+        def rs():
+            chk(L.sg_skip_reduce_scatter(vp(bufs), 0, n, M, slice_bytes, 0.5, rs_seed, None, 1, vp(rs_out),
+                                         vp(rs_cnt), stream()), "sg_skip_reduce_scatter")
+        stages.append(("skip_reduce_scatter", rs))
+        W["rs_cnt"] = rs_cnt
+        W["rs_geom"] = (n, M, slice_bytes // 4, S)
+        W.update(slice_bytes=slice_bytes, p_skip=0.5)
+        if name == "cfg5":
+            W["elements"] = n * M
+    W["stages"] = stages
+    W["nbytes"] = nbytes
+    return W
+
+
+def rs_bytes(W):
+    """Bytes the skip reduce-scatter must move: the kept slices (read once)
+    plus the output (written once)."""
+    import numpy as np
+    n, M, se, S = W["rs_geom"]
+    cnt = W["rs_cnt"].cpu().numpy().astype(np.int64)
+    tot = 0
+    for j in range(n):
+        cb, ce = (M * j) // n, (M * (j + 1)) // n
+        lens = np.clip(ce - (cb + np.arange(S) * se), 0, se)
+        tot += int((cnt[j] * lens).sum()) * 4
+    return tot + M * 4
+
+
+PROBES = {  # stage -> (probe id, kernel name)
+    "topk_to_coo": (1, "topk_filter_kernel"),
+    "hash_partition": (2, "part_scatter_kernel"),
+    "aggregate": (3, "mg_merge_kernel"),
+    "encode": (4, "enc_kernel"),
+    "skip_reduce_scatter": (5, "skip_rs_kernel"),
+}
+
+
+def algorithmic_bytes(W, stage):
+    """Algorithmic bytes per launch of the probed kernel of a stage."""
+    if stage == "topk_to_coo":
+        return W["n"] * W["M"] * 4  # the dense read; slots are workspace
+    if stage == "hash_partition":
+        return W["nbytes"]["hash_partition"]
+    if stage == "aggregate":
+        return W["bytes_agg"](int(W["agg_off"][-1].item()))
+    if stage == "encode":
+        return W["bytes_enc"](int(W["agg_off"][-1].item()), int(W["word_off"][-1].item()))
+    if stage == "skip_reduce_scatter":
+        return rs_bytes(W)
+    raise KeyError(stage)
+
+
+def cpu_baseline(name, gen):
+    """The oracle, single-threaded, on one full step of the same workload."""
+    import numpy as np
+    import oracle
+    if name != "dgc-top5":
+        return None
+    c = gen.config3()
+    n, M, k, P, seed = c["n"], c["M"], c["k"], c["P"], c["seed"]
+    t0 = time.perf_counter()
+    idx, val = oracle.topk_to_coo(c["dense"], k)
+    in_off = np.arange(n + 1, dtype=np.uint64) * np.uint64(k)
+    oi, ov, po = oracle.hash_partition(idx.reshape(-1), val.reshape(-1), in_off, P, seed)
+    ai, av, aa, ao = oracle.aggregate(oi, ov, po, M)
+    oracle.encode(ai, ao, M, seed)
+    oracle.stats(idx.reshape(-1), in_off, M, P, hashed=True, seed=seed)
+    oracle.skip_reduce_scatter(c["dense"], (256 * 1024) // 4, 0.5, 5, mode=1)
+    t = time.perf_counter() - t0
+    return {"value": n * k / t, "unit": "nonzeros/s", "cores": 1, "kind": "oracle",
+            "sample": "one full step of the workload (all six stages, full size), single-threaded C oracle",
+            "seconds": round(t, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dgc-top5", choices=["dgc-top5", "cfg1", "cfg2", "cfg4", "cfg5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", default=None, help="stage whose kernel is timed for the roofline (default: slowest)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the n workers are simulated resident on it); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gen
+    import sparse_gradient_synchronization_amd as sg
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    log("building workload", args.workload)
+    W = build_workload(args.workload, torch, sg, gen)
+    stages = W["stages"]
+    L = sg.lib()
+    steps = args.steps
+    evs = [HipEvents() for _ in range(steps)]   # one probe pair per timed step
+    starts = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
+    stops = [[torch.cuda.Event(enable_timing=True) for _ in stages] for _ in range(steps)]
+
+    def step(s=None):
+        for i, (nm, f) in enumerate(stages):
+            if s is not None:
+                starts[s][i].record()
+            f()
+            if s is not None:
+                stops[s][i].record()
+
+    # warmup; then time each stage's probed kernel once to find the dominant one
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    probe_ms = {}
+    for nm, _ in stages:
+        if nm not in PROBES:
+            continue
+        L.sg_probe_set(PROBES[nm][0], evs[0].start, evs[0].stop)
+        step()
+        torch.cuda.synchronize()
+        probe_ms[nm] = evs[0].elapsed_ms()
+    L.sg_probe_set(0, None, None)
+    dom = args.probe or max(probe_ms, key=probe_ms.get)
+    log("probe times (ms):", {k: round(v, 4) for k, v in probe_ms.items()}, "dominant:", dom)
+
+    # timed region: K steps bracketed by synchronize; the dominant kernel of
+    # every step is bracketed by its own pair of HIP events on its stream
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        L.sg_probe_set(PROBES[dom][0], evs[s].start, evs[s].stop)
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.sg_probe_set(0, None, None)
+    if sg.sg_device_error() != 0:
+        raise SystemExit("a kernel recorded a violated precondition")
+
+    ms_per_step = (t1 - t0) * 1000.0 / steps
+    per = [e.elapsed_ms() for e in evs]
+    dom_avg = sum(per) / len(per)
+    dom_bytes = algorithmic_bytes(W, dom)
+    achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
+    stages_out = {nm: round(sum(starts[s][i].elapsed_time(stops[s][i]) for s in range(steps)) / steps, 4)
+                  for i, (nm, _) in enumerate(stages)}
+
+    if args.workload == "cfg5":
+        units, unit = W["elements"], "elements/s"
+    elif "k" in W:
+        units, unit = W["n"] * W["k"], "nonzeros/s"
+    else:
+        units, unit = W["nnz"], "nonzeros/s"
+    value = units / (ms_per_step * 1e-3)
+
+    # algorithmic bytes of the whole step (every stage's reads and writes)
+    step_bytes = 0
+    for nm, _ in stages:
+        if nm in ("topk_to_coo", "hash_partition"):
+            step_bytes += W["nbytes"][nm]
+        elif nm in ("aggregate", "encode", "skip_reduce_scatter"):
+            step_bytes += algorithmic_bytes(W, nm)
+
+    cfg = {"workload": args.workload}
+    for key in ("n", "M", "k", "P", "D", "total", "slice_bytes", "p_skip"):
+        if key in W:
+            cfg[key] = W[key]
+    if "agg_off" in W:
+        cfg["union_size"] = int(W["agg_off"][-1].item())
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators, shapes and distributions of the workload)",
+        "config": cfg,
+        "stages_ms": stages_out,
+        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": PROBES[dom][1], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_ms": dom_avg,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle (single-threaded) on one step")
+        res["cpu_baseline"] = cpu_baseline(args.workload, gen)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -82,6 +82,24 @@ const char* sg_strerror(int status);
  * record.  Synchronizes `stream`. */
 int sg_device_error(void* stream);
 
+/* Measurement hook (process-wide, not thread-safe).  While set, the calls of
+ * this library record the HIP events `start_event` and `stop_event`
+ * (hipEvent_t passed as void*) on their stream right before and right after
+ * launching the kernel named by kernel_id, so a caller can time one kernel
+ * inside a multi-kernel call.  kernel_id SG_PROBE_NONE clears the hook. */
+typedef enum sg_probe_kernel {
+    SG_PROBE_NONE = 0,
+    SG_PROBE_TOPK_FILTER = 1,        /* top-k: the streaming pass over the dense data (first pass) */
+    SG_PROBE_PARTITION_SCATTER = 2,  /* hash partition: the scatter pass */
+    SG_PROBE_AGGREGATE_MERGE = 3,    /* aggregate: the merge pass */
+    SG_PROBE_ENCODE = 4,             /* encode: the streaming pass over the key space */
+    SG_PROBE_SKIP_RS = 5,            /* skip reduce-scatter: its single kernel */
+    SG_PROBE_AGGREGATE_BND = 6,      /* aggregate: the bucket-boundary pass */
+    SG_PROBE_PARTITION_HIST = 7,     /* hash partition: the histogram pass */
+    SG_PROBE_TOPK_WRITE = 8          /* top-k: the ordered write */
+} sg_probe_kernel;
+int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
+
 /* Checks that every worker's index list is strictly ascending and below M and
  * that in_off is non-decreasing with in_off[0] = 0 and in_off[n] = total.
  * Returns SG_OK, SG_EUNSORTED or SG_ERANGE.  d_ws: sg_validate_workspace_bytes().

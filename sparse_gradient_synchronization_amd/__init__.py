@@ -51,6 +51,7 @@ _u32, _u64, _sz, _vp, _int, _dbl = C.c_uint32, C.c_uint64, C.c_size_t, C.c_void_
 SIGNATURES = {
     "sg_strerror": (C.c_char_p, [_int]),
     "sg_device_error": (_int, [_vp]),
+    "sg_probe_set": (_int, [_int, _vp, _vp]),
     "sg_validate_workspace_bytes": (_sz, []),
     "sg_validate_coo": (_int, [_vp, _vp, _u32, _u64, _u64, _vp, _sz, _vp]),
     "sg_topk_workspace_bytes": (_sz, [_u32, _u64, _u64, _int]),

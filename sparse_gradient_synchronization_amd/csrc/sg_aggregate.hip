@@ -25,15 +25,25 @@ static void choose_buckets(uint32_t n, uint32_t G, uint64_t M, uint64_t total, u
     }
 }
 
+static void merge_sizes(MergeParams* p)
+{
+    const uint64_t splits = 4 * ceil_div(p->total, MG_TARGET);
+    p->tcap = (uint32_t)(p->NB + splits + 2);
+    p->max_tiles = (uint32_t)((uint64_t)p->G * p->NB + splits + p->G);
+    p->max_rows = p->max_tiles + p->G;
+}
+
 static uint64_t merge_carve(Carver& c, MergeParams* p)
 {
+    merge_sizes(p);
     const uint64_t R = (uint64_t)p->n * p->G;
     p->chunk_start = c.take<uint32_t>(R + 1);
     p->bnd = c.take<uint32_t>(R * (p->NB + 1));
-    p->tile_b0 = c.take<uint32_t>((uint64_t)p->G * (p->NB + 1));
+    p->tile_key = c.take<uint64_t>((uint64_t)p->G * p->tcap);
     p->ntiles = c.take<uint32_t>(p->G);
     p->tile_prefix = c.take<uint32_t>((uint64_t)p->G + 1);
-    p->status = c.take<uint64_t>((uint64_t)p->G * p->NB);
+    p->tile_pos = c.take<uint32_t>((uint64_t)p->max_rows * p->n);
+    p->status = c.take<uint64_t>(p->max_tiles);
     p->ticket = c.take<uint32_t>(1);
     return c.bytes();
 }
@@ -42,12 +52,14 @@ static uint64_t merge_carve(Carver& c, MergeParams* p)
 static int merge_run(MergeParams& p, int mode, hipStream_t st)
 {
     const uint64_t R = (uint64_t)p.n * p.G;
-    p.max_tiles = p.G * p.NB;
+    merge_sizes(&p);
     mg_plan_kernel<<<1, MG_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     const uint64_t nchunks = ceil_div(p.total, MG_CHUNK) + R;
+    probe_begin(SG_PROBE_AGGREGATE_BND, st);
     mg_bnd_kernel<<<(unsigned)nchunks, MG_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_AGGREGATE_BND, st);
     const uint64_t cells = R * (p.NB + 1);
     mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
@@ -55,14 +67,18 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st)
     SG_TRY_LAUNCH();
     mg_tile_prefix_kernel<<<1, MG_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    mg_refine_kernel<<<p.max_rows < 4096u ? p.max_rows : 4096u, MG_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
     if (mode == MODE_AGG) {
-        int rc = fill_u64(p.status, (uint64_t)p.G * p.NB, 0, st);
+        int rc = fill_u64(p.status, p.max_tiles, 0, st);
         if (rc) return rc;
     }
     const unsigned grid = p.max_tiles < 512u ? p.max_tiles : 512u;
+    probe_begin((mode == MODE_AGG ? SG_PROBE_AGGREGATE_MERGE : -1), st);
     if (mode == MODE_AGG) mg_merge_kernel<MODE_AGG><<<grid, MG_THREADS, 0, st>>>(p);
     else mg_merge_kernel<MODE_STATS><<<grid, MG_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_end((mode == MODE_AGG ? SG_PROBE_AGGREGATE_MERGE : -1), st);
     return SG_OK;
 }
 

@@ -5,6 +5,7 @@
 namespace sg {
 
 __device__ int g_device_error = 0;
+Probe g_probe = {0, nullptr, nullptr};
 
 __global__ void fill_u32_kernel(uint32_t* d, uint64_t count, uint32_t v)
 {
@@ -93,6 +94,16 @@ extern "C" int sg_device_error(void* stream)
     SG_TRY(hipMemcpyToSymbolAsync(HIP_SYMBOL(g_device_error), &zero, sizeof(int), 0, hipMemcpyHostToDevice, st));
     SG_TRY(hipStreamSynchronize(st));
     return v ? SG_EDEVICE : SG_OK;
+}
+
+extern "C" int sg_probe_set(int kernel_id, void* start_event, void* stop_event)
+{
+    if (kernel_id < 0 || kernel_id > SG_PROBE_TOPK_WRITE) return SG_EINVAL;
+    if (kernel_id != SG_PROBE_NONE && (!start_event || !stop_event)) return SG_EINVAL;
+    g_probe.id = kernel_id;
+    g_probe.start = reinterpret_cast<hipEvent_t>(start_event);
+    g_probe.stop = reinterpret_cast<hipEvent_t>(stop_event);
+    return SG_OK;
 }
 
 extern "C" size_t sg_validate_workspace_bytes(void) { return 256; }

@@ -406,7 +406,9 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     const uint64_t zc = (uint64_t)e.nblocks * P;
     enc_zero_kernel<<<(unsigned)(ceil_div(zc, 256) < 1024 ? ceil_div(zc, 256) : 1024), 256, 0, st>>>(e);
     SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_ENCODE, st);
     enc_kernel<<<e.nblocks, EN_THREADS, 0, st>>>(e);
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_ENCODE, st);
     return SG_OK;
 }

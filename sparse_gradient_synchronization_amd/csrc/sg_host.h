@@ -68,4 +68,19 @@ int fill_u32(uint32_t* d, uint64_t count, uint32_t v, hipStream_t st);
 int fill_u64(uint64_t* d, uint64_t count, uint64_t v, hipStream_t st);
 
 
+// measurement hook (see sg_probe_set in sg.h)
+struct Probe {
+    int id;
+    hipEvent_t start, stop;
+};
+extern Probe g_probe;
+inline void probe_begin(int id, hipStream_t st)
+{
+    if (g_probe.id == id && g_probe.start) (void)hipEventRecord(g_probe.start, st);
+}
+inline void probe_end(int id, hipStream_t st)
+{
+    if (g_probe.id == id && g_probe.stop) (void)hipEventRecord(g_probe.stop, st);
+}
+
 } // namespace sg

@@ -58,12 +58,15 @@ struct MergeParams {
     // workspace
     uint32_t* chunk_start;  // [n*G + 1] bnd blocks per run (position order)
     uint32_t* bnd;          // [(g*n + w) * (NB+1) + b]
-    uint32_t* tile_b0;      // [G * (NB+1)]
+    uint64_t* tile_key;     // [G * tcap] first key of tile j of group g (j <= ntiles[g]: sentinel)
     uint32_t* ntiles;       // [G]
     uint32_t* tile_prefix;  // [G+1]
-    uint64_t* status;       // [G*NB] look-back words
+    uint32_t* tile_pos;     // [rows * n] start (relative to the run) of run w in tile row r
+    uint64_t* status;       // [max_tiles] look-back words
     uint32_t* ticket;       // [1]
-    uint32_t max_tiles;     // G*NB
+    uint32_t tcap;          // tile slots per group
+    uint32_t max_tiles;     // bound on the total number of tiles
+    uint32_t max_rows;      // max_tiles + G (one sentinel row per group)
     // statistics
     uint64_t* st_inter;     // [n*n]
     uint64_t* st_union;     // [1]
@@ -168,13 +171,24 @@ __device__ __forceinline__ uint32_t bnd_at(const MergeParams& p, uint32_t g, uin
     return (uint64_t)v > len ? (uint32_t)len : v;
 }
 
-// One block per group: bucket totals, their prefix, and tile starts.
+// One block per group: bucket totals, their prefix, and tiles.  Consecutive
+// buckets are grouped into tiles of about MG_TARGET entries; a bucket holding
+// more than MG_TARGET entries is split into 2^s equal key sub-ranges (dense
+// regions are dense inside the bucket too), so tiles stay near the target.
+__device__ __forceinline__ uint32_t split_log2(uint32_t tot, uint32_t bs)
+{
+    uint32_t need = (tot + MG_TARGET - 1) / MG_TARGET, s = 0;
+    while ((1u << s) < need && s < bs && s < 16) ++s;
+    return s;
+}
+
 __global__ __launch_bounds__(1024) void mg_tiles_kernel(MergeParams p)
 {
     __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
     __shared__ uint32_t prev_pre[1024], prev_tot[1024];
     __shared__ uint32_t carry_lds[4];
     const uint32_t g = blockIdx.x;
+    uint64_t* keys = p.tile_key + (uint64_t)g * p.tcap;
     uint32_t carry_pre = 0, carry_tiles = 0;
     uint32_t last_pre = 0, last_tot = 0;
     for (uint32_t base = 0; base < p.NB; base += 1024) {
@@ -196,13 +210,20 @@ __global__ __launch_bounds__(1024) void mg_tiles_kernel(MergeParams p)
         __syncthreads();
         uint32_t ppre = threadIdx.x ? prev_pre[threadIdx.x - 1] : last_pre;
         uint32_t ptot = threadIdx.x ? prev_tot[threadIdx.x - 1] : last_tot;
-        bool flag = false;
-        if (b < p.NB)
-            flag = (b == 0) || (pre / MG_TARGET != ppre / MG_TARGET) || tot > MG_TARGET || ptot > MG_TARGET;
+        uint32_t cnt = 0, sl = 0;
+        if (b < p.NB) {
+            const bool flag = (b == 0) || (pre / MG_TARGET != ppre / MG_TARGET) || tot > MG_TARGET || ptot > MG_TARGET;
+            if (flag) {
+                sl = tot > MG_TARGET ? split_log2(tot, p.bs) : 0u;
+                cnt = 1u << sl;
+            }
+        }
         uint32_t nf;
         __syncthreads();
-        uint32_t pos = carry_tiles + block_excl_scan<1024>(flag ? 1u : 0u, scan_lds, &nf);
-        if (flag) p.tile_b0[(uint64_t)g * (p.NB + 1) + pos] = b;
+        uint32_t pos = carry_tiles + block_excl_scan<1024>(cnt, scan_lds, &nf);
+        const uint64_t bw = 1ull << p.bs;
+        for (uint32_t i = 0; i < cnt; ++i)
+            if (pos + i < p.tcap) keys[pos + i] = ((uint64_t)b << p.bs) + (uint64_t)i * (bw >> sl);
         if (threadIdx.x == 1023) {
             carry_lds[0] = pre;
             carry_lds[1] = tot;
@@ -215,8 +236,10 @@ __global__ __launch_bounds__(1024) void mg_tiles_kernel(MergeParams p)
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        p.ntiles[g] = carry_tiles;
-        p.tile_b0[(uint64_t)g * (p.NB + 1) + carry_tiles] = p.NB;
+        uint32_t nt = carry_tiles < p.tcap ? carry_tiles : p.tcap - 1;
+        if (nt != carry_tiles) report_error(kDevErrPartition);
+        p.ntiles[g] = nt;
+        keys[nt] = (uint64_t)p.NB << p.bs;
     }
 }
 
@@ -235,6 +258,60 @@ __global__ __launch_bounds__(MG_THREADS) void mg_tile_prefix_kernel(MergeParams 
     if (threadIdx.x == 0) {
         p.tile_prefix[p.G] = carry;
         p.ticket[0] = 0;
+    }
+}
+
+// lower bound of `target` in the ascending keys a[lo, hi), by one wave:
+// 64 probes per round cut the range 65-fold, then one load finishes.
+__device__ uint64_t wave_lower_bound(const uint32_t* a, uint64_t lo, uint64_t hi, uint64_t target)
+{
+    const uint32_t lane = lane_id();
+    while (hi - lo > SG_WAVE) {
+        const uint64_t len = hi - lo;
+        const uint64_t pos = lo + ((uint64_t)(lane + 1) * len) / 65;
+        const uint32_t c = popc64(ballot((uint64_t)a[pos] < target));
+        const uint64_t nlo = c == 0 ? lo : lo + ((uint64_t)c * len) / 65 + 1;
+        const uint64_t nhi = c == SG_WAVE ? hi : lo + ((uint64_t)(c + 1) * len) / 65;
+        lo = nlo;
+        hi = nhi;
+    }
+    const uint64_t pos = lo + lane;
+    const bool less = pos < hi && (uint64_t)a[pos] < target;
+    return lo + popc64(ballot(less));
+}
+
+// Row r of tile_pos: for every run, where the tile starting at tile_key
+// begins (bucket boundaries come from bnd; split points are searched inside
+// their bucket).  Rows are global: row = tile_prefix[g] + g + j.
+__global__ __launch_bounds__(MG_THREADS) void mg_refine_kernel(MergeParams p)
+{
+    const uint32_t rows = p.tile_prefix[p.G] + p.G;
+    const uint32_t wid = threadIdx.x / SG_WAVE;
+    for (uint32_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        // group of row r: largest g with tile_prefix[g] + g <= r
+        uint32_t lo = 0, hi = p.G;
+        while (lo + 1 < hi) {
+            uint32_t mid = (lo + hi) >> 1;
+            if (p.tile_prefix[mid] + mid <= r) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t g = lo, j = r - (p.tile_prefix[g] + g);
+        const uint64_t key = p.tile_key[(uint64_t)g * p.tcap + j];
+        const uint32_t b = (uint32_t)(key >> p.bs);
+        const bool aligned = (key & ((1ull << p.bs) - 1ull)) == 0;
+        for (uint32_t w = wid; w < p.n; w += MG_THREADS / SG_WAVE) {
+            uint64_t s, e;
+            run_range(p, g, w, s, e);
+            const uint64_t len = e - s;
+            uint32_t v;
+            if (aligned || b >= p.NB) {
+                v = bnd_at(p, g, w, b < p.NB ? b : p.NB, len);
+            } else {
+                const uint32_t x = bnd_at(p, g, w, b, len), y = bnd_at(p, g, w, b + 1, len);
+                v = (uint32_t)(wave_lower_bound(p.idx + s, x, y > x ? y : x, key));
+            }
+            if (lane_id() == 0) p.tile_pos[(uint64_t)r * p.n + w] = v;
+        }
     }
 }
 
@@ -390,13 +467,16 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
             else hi = mid;
         }
         const uint32_t g = lo, jt = t - p.tile_prefix[g];
-        const uint32_t b0 = p.tile_b0[(uint64_t)g * (p.NB + 1) + jt];
-        const uint32_t b1 = p.tile_b0[(uint64_t)g * (p.NB + 1) + jt + 1];
+        const uint32_t row = p.tile_prefix[g] + g + jt;
+        const uint64_t klo = p.tile_key[(uint64_t)g * p.tcap + jt];
+        const uint64_t khi = p.tile_key[(uint64_t)g * p.tcap + jt + 1];
         if (threadIdx.x < n) {
             uint64_t s, e;
             run_range(p, g, threadIdx.x, s, e);
             const uint64_t len = e - s;
-            uint32_t x = bnd_at(p, g, threadIdx.x, b0, len), y = bnd_at(p, g, threadIdx.x, b1, len);
+            uint32_t x = p.tile_pos[(uint64_t)row * n + threadIdx.x], y = p.tile_pos[(uint64_t)(row + 1) * n + threadIdx.x];
+            if (x > len) x = (uint32_t)len;
+            if (y > len) y = (uint32_t)len;
             if (y < x) y = x;
             sm.src0[threadIdx.x] = s;
             sm.cur[threadIdx.x] = x;
@@ -409,10 +489,38 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
         const uint32_t win = MG_CAP / n;
 
         uint64_t X = 0;
+        bool early = false; // unique count published before the windows run
         if (MODE == MODE_AGG && !single) {
+            uint32_t U0 = 0;
+            const uint64_t span = khi > klo ? khi - klo : 0;
+            early = span <= (uint64_t)MG_CAP * 32;
+            if (early) {
+                // count the tile's distinct keys with a presence bitmap over
+                // [klo, khi) so successors need not wait for the whole tile
+                uint32_t* bm = sm.keys[1];
+                const uint32_t nwords = (uint32_t)((span + 31) / 32);
+                for (uint32_t i = threadIdx.x; i < nwords; i += MG_THREADS) bm[i] = 0u;
+                __syncthreads();
+                for (uint32_t w = 0; w < n; ++w) {
+                    const uint64_t gs = sm.src0[w] + sm.cur[w];
+                    const uint32_t cnt = sm.end[w] - sm.cur[w];
+                    for (uint32_t i = threadIdx.x; i < cnt; i += MG_THREADS) {
+                        const uint64_t off = (uint64_t)p.idx[gs + i] - klo;
+                        if (off < span) atomicOr(&bm[off >> 5], 1u << (off & 31u));
+                    }
+                }
+                __syncthreads();
+                uint32_t c = 0;
+                for (uint32_t i = threadIdx.x; i < nwords; i += MG_THREADS) c += __popc(bm[i]);
+                block_excl_scan<MG_THREADS>(c, sm.scan, &U0);
+            }
             if (threadIdx.x < SG_WAVE) {
-                uint64_t x = look_back(p, t);
-                if (threadIdx.x == 0) sm.bcast64[0] = x;
+                if (early && threadIdx.x == 0) store_agent(p.status + t, (t == 0 ? MG_FLAG_INC : MG_FLAG_AGG) | U0);
+                uint64_t x = t == 0 ? 0ull : look_back(p, t);
+                if (threadIdx.x == 0) {
+                    if (early && t != 0) store_agent(p.status + t, MG_FLAG_INC | (x + U0));
+                    sm.bcast64[0] = x;
+                }
             }
             __syncthreads();
             X = sm.bcast64[0];
@@ -623,7 +731,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
             if (single) break;
         }
         if (MODE == MODE_AGG) {
-            if (!single && threadIdx.x == 0) store_agent(p.status + t, MG_FLAG_INC | (X + produced));
+            if (!single && !early && threadIdx.x == 0) store_agent(p.status + t, MG_FLAG_INC | (X + produced));
             if (t == total_tiles - 1 && threadIdx.x == 0) p.agg_off[p.G] = X + produced;
             if (jt == 0 && threadIdx.x == 0) p.agg_off[g] = X;
         }

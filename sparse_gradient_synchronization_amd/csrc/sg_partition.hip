@@ -314,14 +314,18 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
 
     part_plan_kernel<<<1, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_PARTITION_HIST, st);
     part_hist_kernel<<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_PARTITION_HIST, st);
     part_scan_kernel<<<n, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_PARTITION_SCATTER, st);
     if (D == 0) part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     else if (D == 1 && dt == SG_F32) part_scatter_kernel<true, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     else if (D == 1) part_scatter_kernel<true, uint16_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     else part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_PARTITION_SCATTER, st);
     return SG_OK;
 }

@@ -236,6 +236,7 @@ extern "C" int sg_skip_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t 
     p.nblocks = (uint64_t)n * p.S * p.tiles_per_slice;
     uint64_t grid = p.nblocks < 65536 ? p.nblocks : 65536;
     hipStream_t st = as_stream(stream);
+    probe_begin(SG_PROBE_SKIP_RS, st);
     if (dt == SG_F32) {
         if (vec) skip_rs_kernel<float, true><<<(unsigned)grid, RS_THREADS, 0, st>>>(p);
         else skip_rs_kernel<float, false><<<(unsigned)grid, RS_THREADS, 0, st>>>(p);
@@ -244,5 +245,6 @@ extern "C" int sg_skip_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t 
         else skip_rs_kernel<uint16_t, false><<<(unsigned)grid, RS_THREADS, 0, st>>>(p);
     }
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_SKIP_RS, st);
     return SG_OK;
 }

@@ -571,6 +571,7 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     const uint64_t ntiles = (uint64_t)n * p.NT;
     const unsigned fgrid = (unsigned)(ntiles < 8192 ? ntiles : 8192);
     for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 0) probe_begin(SG_PROBE_TOPK_FILTER, st);
         if (p.bf16) {
             if (rows_aligned) topk_filter_kernel<8, true><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
             else topk_filter_kernel<8, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
@@ -579,6 +580,7 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
             else topk_filter_kernel<4, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
         }
         SG_TRY_LAUNCH();
+        if (pass == 0) probe_end(SG_PROBE_TOPK_FILTER, st);
         topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
         SG_TRY_LAUNCH();
     }
@@ -594,7 +596,9 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     SG_TRY_LAUNCH();
     topk_scan_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_TOPK_WRITE, st);
     topk_write_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_TOPK_WRITE, st);
     return SG_OK;
 }
