@@ -12,11 +12,12 @@ static void choose_buckets(uint32_t n, uint32_t G, uint64_t M, uint64_t total, u
 {
     const double want = total > 0 ? (double)(MG_TARGET / 2) * (double)M * (double)G / (double)total : (double)M;
     uint32_t b = 0;
-    while (b < 32 && (double)(1ull << (b + 1)) <= want) ++b;
+    while (b < MG_SPAN_LOG && (double)(1ull << (b + 1)) <= want) ++b;
     for (;;) {
         uint64_t nb = (M + (1ull << b) - 1) >> b;
         if (nb == 0) nb = 1;
-        if ((uint64_t)n * G * (nb + 1) <= (16ull << 20) || b >= 32) {
+        // a bucket never spans more keys than a tile may
+        if ((uint64_t)n * G * (nb + 1) <= (16ull << 20) || b >= MG_SPAN_LOG) {
             *bs = b;
             *NB = (uint32_t)nb;
             return;
@@ -43,6 +44,9 @@ static uint64_t merge_carve(Carver& c, MergeParams* p)
     p->ntiles = c.take<uint32_t>(p->G);
     p->tile_prefix = c.take<uint32_t>((uint64_t)p->G + 1);
     p->tile_pos = c.take<uint32_t>((uint64_t)p->max_rows * p->n);
+    p->tile_group = c.take<uint32_t>(p->max_tiles);
+    p->tile_lo = c.take<uint64_t>(p->max_tiles);
+    p->tile_hi = c.take<uint64_t>(p->max_tiles);
     p->status = c.take<uint64_t>(p->max_tiles);
     p->ticket = c.take<uint32_t>(1);
     return c.bytes();
@@ -73,7 +77,19 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st)
         int rc = fill_u64(p.status, p.max_tiles, 0, st);
         if (rc) return rc;
     }
-    const unsigned grid = p.max_tiles < 512u ? p.max_tiles : 512u;
+    // persistent grid: as many blocks as can be resident at once
+    static int resident[2] = {0, 0};
+    if (!resident[mode]) {
+        int dev = 0, cus = 0, per = 0;
+        SG_TRY(hipGetDevice(&dev));
+        SG_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        if (mode == MODE_AGG)
+            SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mg_merge_kernel<MODE_AGG>, MG_THREADS, 0));
+        else
+            SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mg_merge_kernel<MODE_STATS>, MG_THREADS, 0));
+        resident[mode] = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+    }
+    const unsigned grid = p.max_tiles < (uint32_t)resident[mode] ? p.max_tiles : (unsigned)resident[mode];
     probe_begin((mode == MODE_AGG ? SG_PROBE_AGGREGATE_MERGE : -1), st);
     if (mode == MODE_AGG) mg_merge_kernel<MODE_AGG><<<grid, MG_THREADS, 0, st>>>(p);
     else mg_merge_kernel<MODE_STATS><<<grid, MG_THREADS, 0, st>>>(p);

@@ -12,25 +12,32 @@
 //   bnd    one streaming pass over the run entries records, per run, where
 //          each key bucket of width 2^bs begins (plain stores, no atomics);
 //   tiles  per group, consecutive buckets are grouped into tiles of about
-//          2048 entries (never more than 4096 unless one bucket alone is
-//          larger), from the bucket totals;
-//   merge  persistent blocks take tiles in order through an atomic ticket,
-//          load the n sub-runs of a tile into LDS, merge them pairwise
-//          (merge path, ties to the lower worker, so equal keys end up in
-//          worker order), mark segment heads, and sum each segment's values
-//          in worker order.  Output offsets come from a decoupled look-back
-//          over the tiles' unique counts (bounded spin).  A tile larger than
-//          LDS is consumed in windows of 4096/n entries per run; each window
-//          ends at the smallest last-loaded key of a cut run, which
-//          guarantees progress.
+//          2048 entries (at most 4096, and at most 2^20 keys wide; a denser
+//          bucket is split into key sub-ranges), from the bucket totals;
+//   union  persistent blocks take tiles in order through an atomic ticket
+//          and hold a tile's entries in registers (8 per thread).  A
+//          two-level presence bitmap over the tile's key span (one bit per
+//          32-key group, then one word per non-empty group) gives every key
+//          its rank among the tile's distinct keys by prefix popcounts, with
+//          no sorting and no merge chains.  Values are summed into the rank
+//          slots one worker after another, so every sum is taken in worker
+//          order (deterministic, the order of a ring).  Output offsets come
+//          from a decoupled look-back over the tiles' unique counts (bounded
+//          spin).  A tile with more than 4096 entries (a key sub-range denser
+//          than its neighbours) is consumed in windows of 4096/n entries per
+//          run, each window ending at the smallest last-loaded key of a cut
+//          run, which guarantees progress.
 #include "sg_host.h"
 
 namespace sg {
 
-constexpr int MG_THREADS = 256;
-constexpr int MG_CAP = 4096;       // entries per LDS tile
-constexpr int MG_TARGET = 2048;    // target entries per tile
-constexpr int MG_CHUNK = 4096;     // run entries per bnd block
+constexpr int MG_THREADS = 512;
+constexpr int MG_CAP = 4096;        // entries of a tile (window) held at once, in registers
+constexpr int MG_TARGET = 2048;     // target entries per tile
+constexpr int MG_PER = MG_CAP / MG_THREADS;
+constexpr int MG_SPAN_LOG = 20;     // a tile spans at most 2^20 keys
+constexpr int MG_CWORDS = (1 << MG_SPAN_LOG) >> 10; // coarse bitmap words: one bit per 32 keys
+constexpr int MG_CHUNK = 4096;      // run entries per bnd block
 constexpr uint64_t MG_FLAG_AGG = 1ull << 62;
 constexpr uint64_t MG_FLAG_INC = 2ull << 62;
 constexpr uint64_t MG_VAL_MASK = (1ull << 62) - 1;
@@ -62,6 +69,9 @@ struct MergeParams {
     uint32_t* ntiles;       // [G]
     uint32_t* tile_prefix;  // [G+1]
     uint32_t* tile_pos;     // [rows * n] start (relative to the run) of run w in tile row r
+    uint32_t* tile_group;   // [max_tiles] group of global tile t (tile row = t + group)
+    uint64_t* tile_lo;      // [max_tiles] first key of tile t
+    uint64_t* tile_hi;      // [max_tiles] end key of tile t
     uint64_t* status;       // [max_tiles] look-back words
     uint32_t* ticket;       // [1]
     uint32_t tcap;          // tile slots per group
@@ -212,7 +222,9 @@ __global__ __launch_bounds__(1024) void mg_tiles_kernel(MergeParams p)
         uint32_t ptot = threadIdx.x ? prev_tot[threadIdx.x - 1] : last_tot;
         uint32_t cnt = 0, sl = 0;
         if (b < p.NB) {
-            const bool flag = (b == 0) || (pre / MG_TARGET != ppre / MG_TARGET) || tot > MG_TARGET || ptot > MG_TARGET;
+            const uint32_t span_buckets = p.bs >= MG_SPAN_LOG ? 1u : (1u << (MG_SPAN_LOG - p.bs));
+            const bool flag = (b == 0) || (pre / MG_TARGET != ppre / MG_TARGET) || tot > MG_TARGET ||
+                              ptot > MG_TARGET || (b % span_buckets) == 0;
             if (flag) {
                 sl = tot > MG_TARGET ? split_log2(tot, p.bs) : 0u;
                 cnt = 1u << sl;
@@ -297,6 +309,12 @@ __global__ __launch_bounds__(MG_THREADS) void mg_refine_kernel(MergeParams p)
         }
         const uint32_t g = lo, j = r - (p.tile_prefix[g] + g);
         const uint64_t key = p.tile_key[(uint64_t)g * p.tcap + j];
+        if (threadIdx.x == 0 && j < p.ntiles[g]) {
+            const uint32_t t = r - g;
+            p.tile_group[t] = g;
+            p.tile_lo[t] = key;
+            p.tile_hi[t] = p.tile_key[(uint64_t)g * p.tcap + j + 1];
+        }
         const uint32_t b = (uint32_t)(key >> p.bs);
         const bool aligned = (key & ((1ull << p.bs) - 1ull)) == 0;
         for (uint32_t w = wid; w < p.n; w += MG_THREADS / SG_WAVE) {
@@ -318,84 +336,6 @@ __global__ __launch_bounds__(MG_THREADS) void mg_refine_kernel(MergeParams p)
 // ---------------------------------------------------------------------------
 // the merge kernel
 // ---------------------------------------------------------------------------
-struct MergeSmem {
-    uint32_t keys[2][MG_CAP];
-    uint16_t lidx[2][MG_CAP]; // load position of the entry (into vals / source map)
-    float vals[MG_CAP];
-    uint16_t hpos[MG_CAP];    // sorted position of unique u
-    uint32_t lofs[65];        // list offsets (merge tree)
-    uint32_t wofs[65];        // load offsets per worker
-    uint64_t src0[64];        // absolute position of the first loaded entry of worker w
-    uint32_t cur[64], end[64], take[64];
-    uint32_t scan[MG_THREADS / SG_WAVE + 1];
-    uint32_t bcast[8];
-    uint64_t bcast64[2];
-    uint64_t vmask[MG_THREADS / SG_WAVE][64]; // statistics: per-wave worker bit vectors
-};
-
-__device__ __forceinline__ uint32_t merge_path(const uint32_t* A, uint32_t la, const uint32_t* B, uint32_t lb,
-                                               uint32_t d)
-{
-    uint32_t lo = d > lb ? d - lb : 0u, hi = d < la ? d : la;
-    while (lo < hi) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (A[mid] <= B[d - 1 - mid]) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
-// Merge the nl sorted lists held in keys[in] (offsets lofs[0..nl]) pairwise
-// until one remains.  Returns the buffer index holding the result.
-__device__ int merge_tree(MergeSmem& sm, uint32_t nl, uint32_t E)
-{
-    int in = 0;
-    while (nl > 1) {
-        const uint32_t per = (E + MG_THREADS - 1) / MG_THREADS;
-        const uint32_t o0 = threadIdx.x * per;
-        const uint32_t o1 = o0 + per < E ? o0 + per : E;
-        const uint32_t* K = sm.keys[in];
-        const uint16_t* L = sm.lidx[in];
-        uint32_t* KO = sm.keys[in ^ 1];
-        uint16_t* LO = sm.lidx[in ^ 1];
-        uint32_t o = o0;
-        uint32_t q = 0; // pair index containing o
-        while (o < o1) {
-            while (q + 1 < (nl + 1) / 2 && sm.lofs[2 * (q + 1)] <= o) ++q;
-            const uint32_t ps = sm.lofs[2 * q];
-            const uint32_t mid = sm.lofs[2 * q + 1 < nl ? 2 * q + 1 : nl];
-            const uint32_t pe = sm.lofs[2 * q + 2 < nl ? 2 * q + 2 : nl];
-            const uint32_t la = mid - ps, lb = pe - mid;
-            const uint32_t stop = o1 < pe ? o1 : pe;
-            uint32_t i = merge_path(K + ps, la, K + mid, lb, o - ps);
-            uint32_t j = (o - ps) - i;
-            for (; o < stop; ++o) {
-                bool takeA = (j >= lb) || (i < la && K[ps + i] <= K[mid + j]);
-                if (takeA) {
-                    KO[o] = K[ps + i];
-                    LO[o] = L[ps + i];
-                    ++i;
-                } else {
-                    KO[o] = K[mid + j];
-                    LO[o] = L[mid + j];
-                    ++j;
-                }
-            }
-        }
-        __syncthreads();
-        // rebuild offsets: new list k starts where old list 2k started
-        const uint32_t nn = (nl + 1) / 2;
-        uint32_t newoff = 0;
-        if (threadIdx.x <= nn) newoff = (2 * threadIdx.x < nl) ? sm.lofs[2 * threadIdx.x] : E;
-        __syncthreads();
-        if (threadIdx.x <= nn) sm.lofs[threadIdx.x] = newoff;
-        __syncthreads();
-        nl = nn;
-        in ^= 1;
-    }
-    return in;
-}
-
 // decoupled look-back by wave 0: exclusive prefix of tile `t`
 __device__ uint64_t look_back(const MergeParams& p, uint32_t t)
 {
@@ -428,99 +368,88 @@ __device__ uint64_t look_back(const MergeParams& p, uint32_t t)
     return sum;
 }
 
+// Contiguous part of `key` among P parts [floor(iM/P), floor((i+1)M/P)):
+// the largest i with i*M < (key+1)*P, i.e. floor(((key+1)P - 1) / M).
 __device__ __forceinline__ uint32_t contig_part(uint64_t key, uint64_t M, uint32_t P)
 {
-    uint64_t part = (uint64_t)(((unsigned __int128)key * P) / (M ? M : 1));
-    if (part >= P) part = P - 1;
-    // exact boundaries floor(i M / P)
-    while (part + 1 < P && key >= (uint64_t)(((unsigned __int128)M * (part + 1)) / P)) ++part;
-    while (part > 0 && key < (uint64_t)(((unsigned __int128)M * part) / P)) --part;
-    return (uint32_t)part;
+    const uint64_t part = ((key + 1) * P - 1) / (M ? M : 1);
+    return part < P ? (uint32_t)part : P - 1;
 }
+
+template <int MODE>
+struct UnionSmem {
+    uint32_t coarse[MG_CWORDS];  // bit per 32-key group of the tile span
+    uint16_t cpre[MG_CWORDS];    // non-empty groups before a coarse word
+    uint32_t fine[MG_CAP];       // bits of the non-empty groups; then the distinct keys by rank
+    uint16_t fpre[MG_CAP];       // distinct keys before a fine word
+    union {
+        float acc[MG_CAP];       // sums by rank (scalar values)
+        uint32_t ekey[MG_CAP];   // entry keys by load position (rows)
+    };
+    unsigned long long mask[MODE == MODE_STATS ? MG_CAP : 1]; // workers holding a key
+    uint32_t wofs[65];           // load offset of worker w's window
+    uint32_t take[64], taken[64];
+    uint32_t cur[64], end[64];
+    uint64_t src0[64];
+    uint32_t scan[MG_THREADS / SG_WAVE + 1];
+    uint32_t bcast[4];
+    uint64_t bcast64[2];
+    unsigned long long vmask[MODE == MODE_STATS ? MG_THREADS / SG_WAVE : 1][64];
+    uint32_t ucontig[MODE == MODE_STATS ? 256 : 1], uhashed[MODE == MODE_STATS ? 256 : 1];
+};
 
 template <int MODE>
 __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
 {
-    __shared__ MergeSmem sm;
-    __shared__ uint32_t inter_lds[MODE == MODE_STATS ? 64 * 64 : 1];
-    __shared__ uint32_t ucontig[MODE == MODE_STATS ? 256 : 1], uhashed[MODE == MODE_STATS ? 256 : 1];
-    __shared__ uint64_t union_lds;
+    __shared__ UnionSmem<MODE> sm;
     const uint32_t n = p.n;
+    const uint32_t tid = threadIdx.x, wid = tid / SG_WAVE;
     const uint32_t total_tiles = p.tile_prefix[p.G];
-
-    if (MODE == MODE_STATS) {
-        for (uint32_t i = threadIdx.x; i < 64 * 64; i += MG_THREADS) inter_lds[i] = 0;
-        for (uint32_t i = threadIdx.x; i < 256; i += MG_THREADS) ucontig[i] = uhashed[i] = 0;
-        if (threadIdx.x == 0) union_lds = 0;
-    }
+    // statistics: each lane owns up to 4 worker pairs (a <= b), pair index
+    // pi = lane + 64*i; further pairs (n > 22) go straight to global atomics
+    uint32_t pair_acc[4] = {0, 0, 0, 0};
+    const uint32_t npairs = n * (n + 1) / 2;
+    uint64_t union_cnt = 0;
+    if (MODE == MODE_STATS)
+        for (uint32_t i = tid; i < 256; i += MG_THREADS) sm.ucontig[i] = sm.uhashed[i] = 0;
 
     while (true) {
-        if (threadIdx.x == 0) sm.bcast[0] = atomicAdd(p.ticket, 1u);
+        if (tid == 0) sm.bcast[0] = atomicAdd(p.ticket, 1u);
         __syncthreads();
         const uint32_t t = sm.bcast[0];
         if (t >= total_tiles) break;
-        // group and tile index
-        uint32_t lo = 0, hi = p.G;
-        while (lo + 1 < hi) {
-            uint32_t mid = (lo + hi) >> 1;
-            if (p.tile_prefix[mid] <= t) lo = mid;
-            else hi = mid;
-        }
-        const uint32_t g = lo, jt = t - p.tile_prefix[g];
-        const uint32_t row = p.tile_prefix[g] + g + jt;
-        const uint64_t klo = p.tile_key[(uint64_t)g * p.tcap + jt];
-        const uint64_t khi = p.tile_key[(uint64_t)g * p.tcap + jt + 1];
-        if (threadIdx.x < n) {
+        const uint32_t g = p.tile_group[t];
+        const uint64_t klo = p.tile_lo[t], khi = p.tile_hi[t];
+        const uint32_t row = t + g;
+        const uint32_t jfirst = p.tile_prefix[g] == t; // first tile of its group
+        if (tid < n) {
             uint64_t s, e;
-            run_range(p, g, threadIdx.x, s, e);
+            run_range(p, g, tid, s, e);
             const uint64_t len = e - s;
-            uint32_t x = p.tile_pos[(uint64_t)row * n + threadIdx.x], y = p.tile_pos[(uint64_t)(row + 1) * n + threadIdx.x];
+            uint32_t x = p.tile_pos[(uint64_t)row * n + tid], y = p.tile_pos[(uint64_t)(row + 1) * n + tid];
             if (x > len) x = (uint32_t)len;
             if (y > len) y = (uint32_t)len;
             if (y < x) y = x;
-            sm.src0[threadIdx.x] = s;
-            sm.cur[threadIdx.x] = x;
-            sm.end[threadIdx.x] = y;
+            sm.src0[tid] = s;
+            sm.cur[tid] = x;
+            sm.end[tid] = y;
         }
         __syncthreads();
         uint32_t E = 0;
         for (uint32_t w = 0; w < n; ++w) E += sm.end[w] - sm.cur[w];
         const bool single = E <= (uint32_t)MG_CAP;
+        uint64_t span = khi > klo ? khi - klo : 0;
+        if (span > (1ull << MG_SPAN_LOG)) { // the tiler never builds one; keep LDS indices in range
+            report_error(kDevErrPartition);
+            span = 1ull << MG_SPAN_LOG;
+        }
         const uint32_t win = MG_CAP / n;
 
         uint64_t X = 0;
-        bool early = false; // unique count published before the windows run
         if (MODE == MODE_AGG && !single) {
-            uint32_t U0 = 0;
-            const uint64_t span = khi > klo ? khi - klo : 0;
-            early = span <= (uint64_t)MG_CAP * 32;
-            if (early) {
-                // count the tile's distinct keys with a presence bitmap over
-                // [klo, khi) so successors need not wait for the whole tile
-                uint32_t* bm = sm.keys[1];
-                const uint32_t nwords = (uint32_t)((span + 31) / 32);
-                for (uint32_t i = threadIdx.x; i < nwords; i += MG_THREADS) bm[i] = 0u;
-                __syncthreads();
-                for (uint32_t w = 0; w < n; ++w) {
-                    const uint64_t gs = sm.src0[w] + sm.cur[w];
-                    const uint32_t cnt = sm.end[w] - sm.cur[w];
-                    for (uint32_t i = threadIdx.x; i < cnt; i += MG_THREADS) {
-                        const uint64_t off = (uint64_t)p.idx[gs + i] - klo;
-                        if (off < span) atomicOr(&bm[off >> 5], 1u << (off & 31u));
-                    }
-                }
-                __syncthreads();
-                uint32_t c = 0;
-                for (uint32_t i = threadIdx.x; i < nwords; i += MG_THREADS) c += __popc(bm[i]);
-                block_excl_scan<MG_THREADS>(c, sm.scan, &U0);
-            }
-            if (threadIdx.x < SG_WAVE) {
-                if (early && threadIdx.x == 0) store_agent(p.status + t, (t == 0 ? MG_FLAG_INC : MG_FLAG_AGG) | U0);
+            if (tid < SG_WAVE) {
                 uint64_t x = t == 0 ? 0ull : look_back(p, t);
-                if (threadIdx.x == 0) {
-                    if (early && t != 0) store_agent(p.status + t, MG_FLAG_INC | (x + U0));
-                    sm.bcast64[0] = x;
-                }
+                if (tid == 0) sm.bcast64[0] = x;
             }
             __syncthreads();
             X = sm.bcast64[0];
@@ -528,115 +457,165 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
         uint64_t produced = 0;
 
         while (true) {
-            // windows per worker
-            if (threadIdx.x == 0) {
+            // window of each worker
+            if (tid == 0) {
                 uint32_t acc = 0;
                 for (uint32_t w = 0; w < n; ++w) {
-                    uint32_t rem = sm.end[w] - sm.cur[w];
-                    uint32_t a = single ? rem : (rem < win ? rem : win);
+                    const uint32_t rem = sm.end[w] - sm.cur[w];
+                    const uint32_t a = single ? rem : (rem < win ? rem : win);
                     sm.wofs[w] = acc;
                     sm.take[w] = a;
                     acc += a;
                 }
                 sm.wofs[n] = acc;
+                sm.bcast[1] = 0xffffffffu; // cut key
+            }
+            if (tid < 64) sm.taken[tid] = 0;
+            for (uint32_t i = tid; i < MG_CWORDS; i += MG_THREADS) sm.coarse[i] = 0;
+            for (uint32_t i = tid; i < MG_CAP; i += MG_THREADS) {
+                sm.fine[i] = 0;
+                if (MODE == MODE_AGG) sm.acc[i] = 0.0f;
+                else sm.mask[i] = 0ull;
             }
             __syncthreads();
             const uint32_t L = sm.wofs[n];
             if (L == 0 && !single) break; // a single tile runs once, even when empty
-            // load windows (keys; values for scalar aggregate)
-            for (uint32_t w = 0; w < n; ++w) {
-                const uint32_t a = sm.take[w], base = sm.wofs[w];
-                const uint64_t gs = sm.src0[w] + sm.cur[w];
-                for (uint32_t i = threadIdx.x; i < a; i += MG_THREADS) {
-                    sm.keys[0][base + i] = p.idx[gs + i];
-                    sm.lidx[0][base + i] = (uint16_t)(base + i);
+            // smallest last-loaded key of a run whose window does not reach its end
+            if (!single && tid < n) {
+                const uint32_t a = sm.take[tid];
+                if (a > 0 && sm.cur[tid] + a < sm.end[tid])
+                    atomicMin(&sm.bcast[1], p.idx[sm.src0[tid] + sm.cur[tid] + a - 1]);
+            }
+            // entries into registers
+            uint32_t key[MG_PER], wk[MG_PER];
+            float val[MG_PER];
+#pragma unroll
+            for (int i = 0; i < MG_PER; ++i) {
+                const uint32_t lp = tid + i * MG_THREADS;
+                key[i] = 0xffffffffu;
+                wk[i] = 0xffffffffu;
+                val[i] = 0.0f;
+                if (lp < L) {
+                    uint32_t lo = 0, hi = n;
+                    while (lo + 1 < hi) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (sm.wofs[mid] <= lp) lo = mid;
+                        else hi = mid;
+                    }
+                    const uint64_t pos = sm.src0[lo] + sm.cur[lo] + (lp - sm.wofs[lo]);
+                    key[i] = p.idx[pos];
+                    wk[i] = lo;
                     if (MODE == MODE_AGG && p.D == 1)
-                        sm.vals[base + i] = p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[gs + i])
-                                                   : static_cast<const float*>(p.val)[gs + i];
+                        val[i] = p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[pos])
+                                        : static_cast<const float*>(p.val)[pos];
                 }
             }
             __syncthreads();
-            // cut: keys <= kmax are complete in every window
-            if (threadIdx.x == 0) {
-                uint32_t kmax = 0xffffffffu;
-                bool cut = false;
-                for (uint32_t w = 0; w < n; ++w) {
-                    const uint32_t a = sm.take[w];
-                    if (a > 0 && sm.cur[w] + a < sm.end[w]) {
-                        uint32_t last = sm.keys[0][sm.wofs[w] + a - 1];
-                        if (!cut || last < kmax) kmax = last;
-                        cut = true;
+            const uint32_t kmax = sm.bcast[1];
+            // take entries up to the cut; coarse presence
+            uint32_t off[MG_PER];
+#pragma unroll
+            for (int i = 0; i < MG_PER; ++i) {
+                const bool tk = wk[i] != 0xffffffffu && key[i] <= kmax;
+                if (!tk) wk[i] = 0xffffffffu;
+                off[i] = 0;
+                if (tk) {
+                    atomicAdd(&sm.taken[wk[i]], 1u);
+                    const uint64_t o = (uint64_t)key[i] - klo;
+                    if (o < span) {
+                        off[i] = (uint32_t)o;
+                        const uint32_t grp = (uint32_t)(o >> 5);
+                        atomicOr(&sm.coarse[grp >> 5], 1u << (grp & 31u));
+                    } else {
+                        wk[i] = 0xffffffffu; // outside the tile: cannot happen for valid input
+                        report_error(kDevErrIndexRange);
                     }
                 }
-                sm.bcast[1] = kmax;
-                sm.bcast[2] = cut ? 1u : 0u;
             }
             __syncthreads();
-            const bool cut = sm.bcast[2] != 0;
-            if (cut) {
-                // per worker: entries <= kmax (a prefix of the window)
-                const uint32_t kmax = sm.bcast[1];
-                if (threadIdx.x < n) {
-                    const uint32_t w = threadIdx.x, a = sm.take[w], base = sm.wofs[w];
-                    uint32_t l = 0, h = a;
-                    while (l < h) {
-                        uint32_t m = (l + h) >> 1;
-                        if (sm.keys[0][base + m] <= kmax) l = m + 1;
-                        else h = m;
-                    }
-                    sm.take[w] = l;
+            // prefix over coarse words -> index of each non-empty group
+            {
+                constexpr int CW = MG_CWORDS / MG_THREADS;
+                uint32_t c[CW], sum = 0;
+#pragma unroll
+                for (int j = 0; j < CW; ++j) {
+                    c[j] = __popc(sm.coarse[tid * CW + j]);
+                    sum += c[j];
                 }
-                __syncthreads();
-                // compact the taken prefixes to the front, keeping worker order
-                if (threadIdx.x == 0) {
-                    uint32_t acc = 0;
-                    for (uint32_t w = 0; w < n; ++w) {
-                        sm.lofs[w] = acc; // new offsets (temporarily in lofs)
-                        acc += sm.take[w];
-                    }
-                    sm.lofs[n] = acc;
+                uint32_t F;
+                uint32_t ex = block_excl_scan<MG_THREADS>(sum, sm.scan, &F);
+#pragma unroll
+                for (int j = 0; j < CW; ++j) {
+                    sm.cpre[tid * CW + j] = (uint16_t)ex;
+                    ex += c[j];
                 }
-                __syncthreads();
-                for (uint32_t w = 0; w < n; ++w) {
-                    const uint32_t a = sm.take[w], from = sm.wofs[w], to = sm.lofs[w];
-                    for (uint32_t i = threadIdx.x; i < a; i += MG_THREADS) {
-                        sm.keys[1][to + i] = sm.keys[0][from + i];
-                        sm.lidx[1][to + i] = sm.lidx[0][from + i];
-                    }
-                }
-                __syncthreads();
-                const uint32_t E2 = sm.lofs[n];
-                for (uint32_t i = threadIdx.x; i < E2; i += MG_THREADS) {
-                    sm.keys[0][i] = sm.keys[1][i];
-                    sm.lidx[0][i] = sm.lidx[1][i];
-                }
-                __syncthreads();
-            } else {
-                if (threadIdx.x <= n) sm.lofs[threadIdx.x] = sm.wofs[threadIdx.x];
-                __syncthreads();
             }
-            const uint32_t E2 = sm.lofs[n];
-            // merge
-            const int fin = merge_tree(sm, n, E2);
-            const uint32_t* K = sm.keys[fin];
-            const uint16_t* LI = sm.lidx[fin];
-            // heads and unique ranks
-            const uint32_t per = (E2 + MG_THREADS - 1) / MG_THREADS;
-            const uint32_t o0 = threadIdx.x * per, o1 = o0 + per < E2 ? o0 + per : E2;
-            uint32_t hc = 0;
-            for (uint32_t o = o0; o < o1; ++o) hc += (o == 0 || K[o] != K[o - 1]);
+            __syncthreads();
+            uint32_t ci[MG_PER];
+#pragma unroll
+            for (int i = 0; i < MG_PER; ++i) {
+                ci[i] = 0;
+                if (wk[i] != 0xffffffffu) {
+                    const uint32_t grp = off[i] >> 5, cw = grp >> 5, cb = grp & 31u;
+                    ci[i] = sm.cpre[cw] + __popc(sm.coarse[cw] & ((1u << cb) - 1u));
+                    atomicOr(&sm.fine[ci[i]], 1u << (off[i] & 31u));
+                }
+            }
+            __syncthreads();
+            // prefix over fine words -> rank of each distinct key
             uint32_t U;
-            uint32_t u = block_excl_scan<MG_THREADS>(hc, sm.scan, &U);
-            for (uint32_t o = o0; o < o1; ++o)
-                if (o == 0 || K[o] != K[o - 1]) sm.hpos[u++] = (uint16_t)o;
+            {
+                uint32_t c[MG_PER], sum = 0;
+#pragma unroll
+                for (int j = 0; j < MG_PER; ++j) {
+                    c[j] = __popc(sm.fine[tid * MG_PER + j]);
+                    sum += c[j];
+                }
+                uint32_t ex = block_excl_scan<MG_THREADS>(sum, sm.scan, &U);
+#pragma unroll
+                for (int j = 0; j < MG_PER; ++j) {
+                    sm.fpre[tid * MG_PER + j] = (uint16_t)ex;
+                    ex += c[j];
+                }
+            }
+            // the unique count is known: let successors use it right away
+            if (MODE == MODE_AGG && single && tid == 0)
+                store_agent(p.status + t, (t == 0 ? MG_FLAG_INC : MG_FLAG_AGG) | U);
             __syncthreads();
+            uint32_t rk[MG_PER];
+#pragma unroll
+            for (int i = 0; i < MG_PER; ++i) {
+                rk[i] = 0;
+                if (wk[i] != 0xffffffffu)
+                    rk[i] = sm.fpre[ci[i]] + __popc(sm.fine[ci[i]] & ((1u << (off[i] & 31u)) - 1u));
+            }
+            __syncthreads();
+            // distinct keys by rank (every holder of a key writes the same value)
+#pragma unroll
+            for (int i = 0; i < MG_PER; ++i) {
+                if (wk[i] == 0xffffffffu) continue;
+                sm.fine[rk[i]] = key[i];
+                if (MODE == MODE_STATS) atomicOr(&sm.mask[rk[i]], 1ull << wk[i]);
+                if (MODE == MODE_AGG && p.D > 1) sm.ekey[tid + i * MG_THREADS] = key[i];
+            }
+            __syncthreads();
+            if (MODE == MODE_AGG && p.D == 1) {
+                // sums in worker order: worker w's entries have distinct keys,
+                // so one worker at a time needs no atomics
+                for (uint32_t w = 0; w < n; ++w) {
+                    if (sm.taken[w] == 0) continue;
+#pragma unroll
+                    for (int i = 0; i < MG_PER; ++i)
+                        if (wk[i] == w) sm.acc[rk[i]] += val[i];
+                    __syncthreads();
+                }
+            }
 
             if (MODE == MODE_AGG) {
                 if (single) {
-                    if (threadIdx.x < SG_WAVE) {
-                        if (threadIdx.x == 0) store_agent(p.status + t, (t == 0 ? MG_FLAG_INC : MG_FLAG_AGG) | U);
+                    if (tid < SG_WAVE) {
                         uint64_t x = t == 0 ? 0ull : look_back(p, t);
-                        if (threadIdx.x == 0) {
+                        if (tid == 0) {
                             if (t != 0) store_agent(p.status + t, MG_FLAG_INC | (x + U));
                             sm.bcast64[0] = x;
                         }
@@ -646,36 +625,32 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                 }
                 const uint64_t ob = X + produced;
                 if (p.D <= 1) {
-                    for (uint32_t q = threadIdx.x; q < U; q += MG_THREADS) {
-                        const uint32_t o = sm.hpos[q];
-                        const uint32_t key = K[o];
+                    for (uint32_t q = tid; q < U; q += MG_THREADS) {
                         const uint64_t dst = ob + q;
                         if (dst >= p.capacity) continue;
-                        p.agg_idx[dst] = key;
-                        if (p.D == 1) {
-                            float acc = 0.0f;
-                            for (uint32_t z = o; z < E2 && K[z] == key; ++z) acc += sm.vals[LI[z]];
-                            p.agg_val[dst] = acc;
-                        }
+                        p.agg_idx[dst] = sm.fine[q];
+                        if (p.D == 1) p.agg_val[dst] = sm.acc[q];
                     }
                 } else {
-                    // rows: one wave per unique, lanes across the row
-                    const uint32_t wid = threadIdx.x / SG_WAVE;
+                    // rows: one wave per distinct key, lanes across the row;
+                    // each worker's entry is found by binary search in its window
                     for (uint32_t q = wid; q < U; q += MG_THREADS / SG_WAVE) {
-                        const uint32_t o = sm.hpos[q];
-                        const uint32_t key = K[o];
+                        const uint32_t k = sm.fine[q];
                         const uint64_t dst = ob + q;
                         if (dst >= p.capacity) continue;
-                        if (lane_id() == 0) p.agg_idx[dst] = key;
+                        if (lane_id() == 0) p.agg_idx[dst] = k;
                         for (uint32_t c0 = 0; c0 < p.D; c0 += SG_WAVE) {
                             const uint32_t c = c0 + lane_id();
                             float acc = 0.0f;
-                            for (uint32_t z = o; z < E2 && K[z] == key; ++z) {
-                                const uint32_t li = LI[z];
-                                uint32_t w = 0;
-                                while (w + 1 < n && sm.wofs[w + 1] <= li) ++w;
-                                const uint64_t pos = sm.src0[w] + sm.cur[w] + (li - sm.wofs[w]);
-                                if (c < p.D) {
+                            for (uint32_t w = 0; w < n; ++w) {
+                                uint32_t lo = sm.wofs[w], hi = sm.wofs[w] + sm.taken[w];
+                                while (lo < hi) {
+                                    const uint32_t mid = (lo + hi) >> 1;
+                                    if (sm.ekey[mid] < k) lo = mid + 1;
+                                    else hi = mid;
+                                }
+                                if (lo < sm.wofs[w] + sm.taken[w] && sm.ekey[lo] == k && c < p.D) {
+                                    const uint64_t pos = sm.src0[w] + sm.cur[w] + (lo - sm.wofs[w]);
                                     const uint64_t vi = pos * p.D + c;
                                     acc += p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[vi])
                                                   : static_cast<const float*>(p.val)[vi];
@@ -686,31 +661,21 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                     }
                 }
             } else {
-                // statistics: union size, pairwise intersections, per-part counts
-                const uint32_t wid = threadIdx.x / SG_WAVE;
+                // statistics: pairwise intersections from per-key worker masks
                 for (uint32_t q0 = wid * SG_WAVE; q0 < U; q0 += MG_THREADS) {
                     const uint32_t q = q0 + lane_id();
-                    uint64_t m = 0;
-                    uint32_t key = 0;
+                    unsigned long long m = 0;
                     if (q < U) {
-                        const uint32_t o = sm.hpos[q];
-                        key = K[o];
-                        for (uint32_t z = o; z < E2 && K[z] == key; ++z) {
-                            const uint32_t li = LI[z];
-                            uint32_t w = 0;
-                            while (w + 1 < n && sm.wofs[w + 1] <= li) ++w;
-                            m |= 1ull << w;
-                        }
-                        atomicAdd(&ucontig[contig_part(key, p.M, p.Ps)], 1u);
-                        if (p.hashed) atomicAdd(&uhashed[h0(key, p.seed, p.div)], 1u);
+                        const uint32_t k = sm.fine[q];
+                        m = sm.mask[q];
+                        atomicAdd(&sm.ucontig[contig_part(k, p.M, p.Ps)], 1u);
+                        if (p.hashed) atomicAdd(&sm.uhashed[h0(k, p.seed, p.div)], 1u);
                     }
                     for (uint32_t a = 0; a < n; ++a) {
                         const uint64_t v = ballot((m >> a) & 1ull);
                         if (lane_id() == 0) sm.vmask[wid][a] = v;
                     }
-                    // lanes take pairs (a, b), a <= b
-                    const uint32_t npairs = n * (n + 1) / 2;
-                    for (uint32_t pi = lane_id(); pi < npairs; pi += SG_WAVE) {
+                    for (uint32_t i = 0, pi = lane_id(); pi < npairs; ++i, pi += SG_WAVE) {
                         uint32_t a = 0, rem = pi;
                         while (rem >= n - a) {
                             rem -= n - a;
@@ -718,36 +683,43 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                         }
                         const uint32_t b = a + rem;
                         const uint32_t c = popc64(sm.vmask[wid][a] & sm.vmask[wid][b]);
-                        if (c) atomicAdd(&inter_lds[a * 64 + b], c);
+                        if (i < 4) pair_acc[i] += c;
+                        else if (c) atomicAdd((unsigned long long*)&p.st_inter[a * n + b], (unsigned long long)c);
                     }
                 }
-                if (threadIdx.x == 0) union_lds += U;
+                union_cnt += U;
             }
             produced += U;
-            // advance (after every wave is done reading the cursors)
             __syncthreads();
-            if (threadIdx.x < n) sm.cur[threadIdx.x] += sm.take[threadIdx.x];
+            if (tid < n) sm.cur[tid] += sm.taken[tid];
             __syncthreads();
             if (single) break;
         }
-        if (MODE == MODE_AGG) {
-            if (!single && !early && threadIdx.x == 0) store_agent(p.status + t, MG_FLAG_INC | (X + produced));
-            if (t == total_tiles - 1 && threadIdx.x == 0) p.agg_off[p.G] = X + produced;
-            if (jt == 0 && threadIdx.x == 0) p.agg_off[g] = X;
+        if (MODE == MODE_AGG && tid == 0) {
+            if (!single) store_agent(p.status + t, MG_FLAG_INC | (X + produced));
+            if (t == total_tiles - 1) p.agg_off[p.G] = X + produced;
+            if (jfirst) p.agg_off[g] = X;
         }
         __syncthreads();
     }
     if (MODE == MODE_STATS) {
         __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n * n; i += MG_THREADS) {
-            const uint32_t a = i / n, b = i % n;
-            if (a <= b && inter_lds[a * 64 + b]) atomicAdd((unsigned long long*)&p.st_inter[a * n + b], (unsigned long long)inter_lds[a * 64 + b]);
+        for (uint32_t i = 0, pi = lane_id(); i < 4 && pi < npairs; ++i, pi += SG_WAVE) {
+            if (!pair_acc[i]) continue;
+            uint32_t a = 0, rem = pi;
+            while (rem >= n - a) {
+                rem -= n - a;
+                ++a;
+            }
+            const uint32_t b = a + rem;
+            atomicAdd((unsigned long long*)&p.st_inter[a * n + b], (unsigned long long)pair_acc[i]);
         }
-        for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
-            if (ucontig[i]) atomicAdd((unsigned long long*)&p.st_ucontig[i], (unsigned long long)ucontig[i]);
-            if (p.hashed && uhashed[i]) atomicAdd((unsigned long long*)&p.st_uhashed[i], (unsigned long long)uhashed[i]);
+        for (uint32_t i = tid; i < p.Ps; i += MG_THREADS) {
+            if (sm.ucontig[i]) atomicAdd((unsigned long long*)&p.st_ucontig[i], (unsigned long long)sm.ucontig[i]);
+            if (p.hashed && sm.uhashed[i])
+                atomicAdd((unsigned long long*)&p.st_uhashed[i], (unsigned long long)sm.uhashed[i]);
         }
-        if (threadIdx.x == 0 && union_lds) atomicAdd((unsigned long long*)p.st_union, (unsigned long long)union_lds);
+        if (tid == 0 && union_cnt) atomicAdd((unsigned long long*)p.st_union, (unsigned long long)union_cnt);
     }
 }
 

@@ -76,60 +76,78 @@ __device__ __forceinline__ uint32_t load_bits(const TopkParams& p, uint64_t i)
 // --------------------------------------------------------------------------
 // 1. band from a strided sample
 // --------------------------------------------------------------------------
+// Two order statistics of the sample (the band's ends) by MSD radix select in
+// LDS: 11-bit digits, both ranks at once, one block per worker.
 __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
 {
     __shared__ uint32_t s[TK_SAMPLES];
+    __shared__ uint32_t hist[2][TK_BINS];
+    __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
+    __shared__ uint32_t pick[2][2];
     const uint32_t w = blockIdx.x;
     const uint64_t M = p.M;
     const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
-    uint32_t N = 1;
-    while (N < S) N <<= 1;
-    for (uint32_t i = threadIdx.x; i < N; i += 1024) {
-        uint32_t v = 0;
-        if (i < S) {
-            uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
-            v = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
-        }
-        s[i] = v;
+    for (uint32_t i = threadIdx.x; i < S; i += 1024) {
+        const uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
+        s[i] = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
     }
+    // target ranks, 1-based from the smallest; 0 = not needed
+    uint32_t R[2];
+    bool none_hi = false, none_lo = false;
+    if (S == M) {
+        R[0] = R[1] = (uint32_t)(M - p.k) + 1;
+    } else {
+        const double r = (double)p.k * (double)S / (double)M; // expected descending rank
+        const double q = (double)p.k / (double)M;
+        const double delta = 4.0 * sqrt(r * (1.0 - q)) + 8.0;
+        const double rhi = floor(r - delta), rlo = ceil(r + delta);
+        none_hi = rhi < 0.0;
+        none_lo = rlo >= (double)S;
+        // descending rank d is ascending index S-1-d, 1-based rank S-d
+        R[0] = none_lo ? 1u : S - (uint32_t)rlo;
+        R[1] = none_hi ? S : S - (uint32_t)rhi;
+    }
+    uint32_t prefix[2] = {0u, 0u};
+    uint32_t top = p.bf16 ? 15u : 31u;
     __syncthreads();
-    // bitonic sort, ascending
-    for (uint32_t kk = 2; kk <= N; kk <<= 1) {
-        for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
-            for (uint32_t i = threadIdx.x; i < N; i += 1024) {
-                uint32_t ixj = i ^ j;
-                if (ixj > i) {
-                    uint32_t a = s[i], b = s[ixj];
-                    bool up = (i & kk) == 0;
-                    if (up ? (a > b) : (a < b)) {
-                        s[i] = b;
-                        s[ixj] = a;
-                    }
-                }
+    while (top > 0) {
+        const uint32_t shift = top > (uint32_t)TK_DIGIT_BITS ? top - TK_DIGIT_BITS : 0u;
+        const uint32_t width = top - shift;
+        for (uint32_t i = threadIdx.x; i < 2 * TK_BINS; i += 1024) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < S; i += 1024) {
+            const uint32_t key = s[i];
+            const uint32_t d = (key >> shift) & ((1u << width) - 1u);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if ((top >= 32 ? 0u : (key >> top)) == (top >= 32 ? 0u : (prefix[t] >> top))) atomicAdd(&hist[t][d], 1u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t d0 = 2 * threadIdx.x;
+            const uint32_t c0 = hist[t][d0], c1 = hist[t][d0 + 1];
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan<1024>(c0 + c1, scan_lds, &tot);
+            if (ex < R[t] && R[t] <= ex + c0) {
+                pick[t][0] = d0;
+                pick[t][1] = ex;
+            } else if (ex + c0 < R[t] && R[t] <= ex + c0 + c1) {
+                pick[t][0] = d0 + 1;
+                pick[t][1] = ex + c0;
             }
             __syncthreads();
+            prefix[t] |= pick[t][0] << shift;
+            R[t] -= pick[t][1];
+            __syncthreads();
         }
+        top = shift;
     }
     if (threadIdx.x == 0) {
         SelState st;
         for (int i = 0; i < 6; ++i) st.pad[i] = 0;
-        // s holds N - S zero pads in front; sample i (ascending) is s[N - S + i]
-        const uint32_t off = N - S;
-        uint32_t lo, hi;
-        if (S == M) {
-            // the sample is the whole worker: the band is the exact k-th largest key
-            lo = hi = s[off + (uint32_t)(M - p.k)];
-        } else {
-            double r = (double)p.k * (double)S / (double)M; // expected descending rank
-            double q = (double)p.k / (double)M;
-            double delta = 4.0 * sqrt(r * (1.0 - q)) + 8.0;
-            double rhi = floor(r - delta), rlo = ceil(r + delta);
-            // descending rank d is ascending index S - 1 - d
-            hi = (rhi < 0.0) ? p.keymax : s[off + (S - 1u - (uint32_t)rhi)];
-            lo = (rlo >= (double)S) ? 0u : s[off + (S - 1u - (uint32_t)rlo)];
-        }
-        st.lo = lo;
-        st.hi = hi;
+        st.lo = none_lo ? 0u : prefix[0];
+        st.hi = none_hi ? p.keymax : prefix[1];
         st.redo = 0;
         st.sure = st.cand = 0;
         st.R = 0;
