@@ -385,8 +385,8 @@ struct UnionSmem {
     union {
         float acc[MG_CAP];       // sums by rank (scalar values)
         uint32_t ekey[MG_CAP];   // entry keys by load position (rows)
+        unsigned long long mask[MODE == MODE_STATS ? MG_CAP : 1]; // statistics: workers holding a key
     };
-    unsigned long long mask[MODE == MODE_STATS ? MG_CAP : 1]; // workers holding a key
     uint32_t wofs[65];           // load offset of worker w's window
     uint32_t take[64], taken[64];
     uint32_t cur[64], end[64];

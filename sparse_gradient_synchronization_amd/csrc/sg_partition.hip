@@ -116,31 +116,56 @@ __global__ __launch_bounds__(PT_THREADS) void part_hist_kernel(PartParams p)
 
 // One block per worker: for each partition q, exclusive scan of counts over
 // the worker's tiles, offset by the start of partition q inside the worker.
-__global__ __launch_bounds__(PT_THREADS) void part_scan_kernel(PartParams p)
+// The block's 1024 threads are P partitions x S tile segments: each thread
+// sums its segment, the S segment sums of a partition are scanned, and each
+// thread writes its segment's running offsets.
+constexpr int PS_THREADS = 1024;
+__global__ __launch_bounds__(PS_THREADS) void part_scan_kernel(PartParams p)
 {
-    __shared__ uint32_t scan_lds[PT_WAVES + 1];
-    __shared__ uint32_t totals[256];
+    __shared__ uint32_t seg[PS_THREADS];
+    __shared__ uint32_t part_tot[256], part_base[256];
+    __shared__ uint32_t scan_lds[PS_THREADS / SG_WAVE + 1];
     const uint32_t w = blockIdx.x;
-    const uint32_t t0 = p.tile_start[w], t1 = p.tile_start[w + 1];
+    const uint32_t t0 = p.tile_start[w], t1 = p.tile_start[w + 1], nt = t1 - t0;
     uint64_t b, e;
     worker_range(p, w, b, e);
-    const uint32_t q = threadIdx.x;
-    uint32_t tot = 0;
-    if (q < p.P)
-        for (uint32_t t = t0; t < t1; ++t) tot += p.counts[(uint64_t)t * p.P + q];
+    const uint32_t S = PS_THREADS / p.P; // segments per partition (>= 4)
+    const uint32_t q = threadIdx.x % p.P, sgi = threadIdx.x / p.P;
+    const bool act = sgi < S;
+    const uint32_t per = (nt + S - 1) / S;
+    const uint32_t a0 = t0 + sgi * per, a1 = (a0 + per < t1) ? a0 + per : t1;
+    uint32_t sum = 0;
+    if (act)
+        for (uint32_t t = a0; t < a1; ++t) sum += p.counts[(uint64_t)t * p.P + q];
+    seg[threadIdx.x] = act ? sum : 0u;
+    __syncthreads();
+    // per partition: exclusive scan over its S segments (thread q walks them)
+    if (threadIdx.x < p.P) {
+        uint32_t run = 0;
+        for (uint32_t k = 0; k < S; ++k) {
+            const uint32_t v = seg[k * p.P + threadIdx.x];
+            seg[k * p.P + threadIdx.x] = run;
+            run += v;
+        }
+        part_tot[threadIdx.x] = run;
+    }
+    __syncthreads();
     uint32_t all;
-    uint32_t ex = block_excl_scan<PT_THREADS>(q < p.P ? tot : 0u, scan_lds, &all);
-    if (q < p.P) {
-        uint32_t run = (uint32_t)b + ex;
-        p.part_off[(uint64_t)w * (p.P + 1) + q] = run;
-        for (uint32_t t = t0; t < t1; ++t) {
-            uint32_t c = p.counts[(uint64_t)t * p.P + q];
+    const uint32_t ex = block_excl_scan<PS_THREADS>(threadIdx.x < p.P ? part_tot[threadIdx.x] : 0u, scan_lds, &all);
+    if (threadIdx.x < p.P) {
+        part_base[threadIdx.x] = (uint32_t)b + ex;
+        p.part_off[(uint64_t)w * (p.P + 1) + threadIdx.x] = (uint32_t)b + ex;
+    }
+    if (threadIdx.x == 0) p.part_off[(uint64_t)w * (p.P + 1) + p.P] = e;
+    __syncthreads();
+    if (act) {
+        uint32_t run = part_base[q] + seg[threadIdx.x];
+        for (uint32_t t = a0; t < a1; ++t) {
+            const uint32_t c = p.counts[(uint64_t)t * p.P + q];
             p.counts[(uint64_t)t * p.P + q] = run;
             run += c;
         }
     }
-    if (q == 0) p.part_off[(uint64_t)w * (p.P + 1) + p.P] = e;
-    (void)totals;
 }
 
 template <bool STAGE_VALS, typename VT>
@@ -318,7 +343,7 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
     part_hist_kernel<<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_PARTITION_HIST, st);
-    part_scan_kernel<<<n, PT_THREADS, 0, st>>>(p);
+    part_scan_kernel<<<n, PS_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_PARTITION_SCATTER, st);
     if (D == 0) part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);

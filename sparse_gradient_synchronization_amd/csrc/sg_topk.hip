@@ -55,6 +55,7 @@ struct TopkParams {
     uint32_t* slot_val;    // [n*NT*TILE] value bits (bf16 in the low half)
     uint32_t* slot_key;    // [n*NT*TILE] candidate keys
     uint32_t* hist;        // [n][TK_BINS]
+    uint32_t* samples;     // [n][TK_SAMPLES]
     uint32_t* gtx;         // [n*NT] exclusive prefix of entries > T
     uint32_t* eqx;         // [n*NT] exclusive prefix of entries == T
     uint64_t M, k;
@@ -76,6 +77,19 @@ __device__ __forceinline__ uint32_t load_bits(const TopkParams& p, uint64_t i)
 // --------------------------------------------------------------------------
 // 1. band from a strided sample
 // --------------------------------------------------------------------------
+// Strided sample of each worker's magnitudes, gathered by many blocks (one
+// 4-byte load per sample: spread over the chip, not one CU per worker).
+__global__ __launch_bounds__(256) void topk_gather_kernel(TopkParams p)
+{
+    const uint32_t w = blockIdx.y;
+    const uint64_t M = p.M;
+    const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= S) return;
+    const uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
+    p.samples[(uint64_t)w * TK_SAMPLES + i] = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
+}
+
 // Two order statistics of the sample (the band's ends) by MSD radix select in
 // LDS: 11-bit digits, both ranks at once, one block per worker.
 __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
@@ -87,10 +101,7 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     const uint32_t w = blockIdx.x;
     const uint64_t M = p.M;
     const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
-    for (uint32_t i = threadIdx.x; i < S; i += 1024) {
-        const uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
-        s[i] = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
-    }
+    for (uint32_t i = threadIdx.x; i < S; i += 1024) s[i] = p.samples[(uint64_t)w * TK_SAMPLES + i];
     // target ranks, 1-based from the smallest; 0 = not needed
     uint32_t R[2];
     bool none_hi = false, none_lo = false;
@@ -275,7 +286,16 @@ template <int EPV, bool VEC>
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(TopkParams p, int redo_only)
 {
     __shared__ uint32_t chunk_ge[16], chunk_ca[16];
+    __shared__ uint32_t any_redo;
     const uint64_t ntiles = (uint64_t)p.n * p.NT;
+    if (redo_only) {
+        if (threadIdx.x == 0) any_redo = 0;
+        __syncthreads();
+        for (uint32_t w = threadIdx.x; w < p.n; w += TK_THREADS)
+            if (p.st[w].redo) any_redo = 1;
+        __syncthreads();
+        if (!any_redo) return;
+    }
     for (uint64_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
         const uint32_t w = (uint32_t)(g / p.NT), t = (uint32_t)(g % p.NT);
         const SelState& st = p.st[w];
@@ -542,6 +562,7 @@ static uint64_t topk_carve(Carver& c, uint32_t n, uint64_t M, TopkParams* p)
     p->gtx = c.take<uint32_t>(nt);
     p->eqx = c.take<uint32_t>(nt);
     p->hist = c.take<uint32_t>((uint64_t)n * TK_BINS);
+    p->samples = c.take<uint32_t>((uint64_t)n * TK_SAMPLES);
     p->slot_idx = c.take<uint32_t>(nt * TK_TILE);
     p->slot_val = c.take<uint32_t>(nt * TK_TILE);
     p->slot_key = c.take<uint32_t>(nt * TK_TILE);
@@ -584,6 +605,8 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
 
     int rc = fill_u32(p.hist, (uint64_t)n * TK_BINS, 0, st);
     if (rc) return rc;
+    topk_gather_kernel<<<dim3(TK_SAMPLES / 256, n), 256, 0, st>>>(p);
+    SG_TRY_LAUNCH();
     topk_sample_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     const uint64_t ntiles = (uint64_t)n * p.NT;
