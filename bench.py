@@ -201,13 +201,62 @@ def rs_bytes(W):
     return tot + M * 4
 
 
-PROBES = {  # stage -> (probe id, kernel name)
-    "topk_to_coo": (1, "topk_filter_kernel"),
-    "hash_partition": (2, "part_scatter_kernel"),
-    "aggregate": (3, "mg_merge_kernel"),
-    "encode": (4, "enc_kernel"),
-    "skip_reduce_scatter": (5, "skip_rs_kernel"),
+PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built from)
+    "topk_to_coo": (1, "topk_filter_kernel", ["sg_topk.hip"]),
+    "hash_partition": (2, "part_scatter_kernel", ["sg_partition.hip"]),
+    "aggregate": (3, "mg_merge_kernel", ["sg_merge.hip", "sg_aggregate.hip"]),
+    "encode": (4, "enc_kernel", ["sg_encode.hip"]),
+    "skip_reduce_scatter": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
 }
+COMMON_SOURCES = ["sg_device.h", "sg_host.h"]
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_digest(stage):
+    """sha256 over the sources of the probed kernel of a stage: a recorded
+    HBM traffic figure is valid only for the source it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in PROBES[stage][2] + COMMON_SOURCES:
+        with open(os.path.join(HERE, "sparse_gradient_synchronization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(stage, workload):
+    """HBM bytes per launch of the probed kernel, from the rocprofv3 counter
+    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the same counter reads for a plain copy of known size).  None when no
+    summary exists for this kernel and workload, or when the kernel's source
+    has changed since the counters were taken."""
+    path = os.path.join(HERE, "profiles", "traffic_%s_%s.txt" % (PROBES[stage][1], workload))
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != kernel_source_digest(stage):
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, nbytes):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    counters of a profile run (FETCH_SIZE / WRITE_SIZE of this copy against
+    nbytes read and nbytes written)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 copies of %d bytes" % nbytes)
+    del src, dst
 
 
 def algorithmic_bytes(W, stage):
@@ -255,6 +304,8 @@ def main():
     ap.add_argument("--workload", default="dgc-top5", choices=["dgc-top5", "cfg1", "cfg2", "cfg4", "cfg5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", default=None, help="stage whose kernel is timed for the roofline (default: slowest)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device copy of BYTES (for scaling HBM counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the n workers are simulated resident on it); "
@@ -268,6 +319,8 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
     log("building workload", args.workload)
     W = build_workload(args.workload, torch, sg, gen)
     stages = W["stages"]
@@ -362,7 +415,7 @@ def main():
         "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, args.workload),
             "kernel": PROBES[dom][1], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": dom_avg,
         },

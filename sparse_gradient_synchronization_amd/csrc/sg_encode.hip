@@ -366,11 +366,12 @@ extern "C" int sg_classmap_build(uint64_t M, uint32_t P, uint32_t seed, void* d_
 
 extern "C" uint64_t sg_encode_max_words(uint64_t M, uint32_t P) { return M / 32 + P + 1; }
 
+// The encode pass keeps all its scratch in LDS.
 extern "C" size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P)
 {
     (void)M;
     (void)P;
-    return 256;
+    return 0;
 }
 
 extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg_capacity, uint64_t M,
@@ -378,9 +379,9 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
                          void* d_ws, size_t ws_bytes, void* stream)
 {
     (void)d_ws;
-    (void)ws_bytes;
     if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return SG_EINVAL;
     if (!d_agg_off || !d_cmap || !d_bitmap || !d_word_off || !d_agg_idx) return SG_EINVAL;
+    if (ws_bytes < sg_encode_workspace_bytes(M, P)) return SG_ECAPACITY;
     if (bitmap_words < sg_encode_max_words(M, P)) return SG_ECAPACITY;
     if (cmap_bytes < sg_classmap_bytes(M, P)) return SG_ECAPACITY;
     EncParams e;

@@ -6,13 +6,13 @@
 // lowest index first and the output in ascending index order.
 //
 // How, on gfx950: the dense gradient is read from HBM once.
-//   1. sample:  16K strided magnitudes per worker, bitonic-sorted in LDS, give
-//               a band [lo, hi] that holds the k-th largest key with very high
-//               probability.
-//   2. filter:  one streaming pass; per 4096-element tile, entries with
-//               key >= lo are compacted in index order (wave ballots, no
-//               atomics) into the tile's own slot, and the candidate keys
-//               (lo <= key <= hi) into a second slot.
+//   1. sample:  16K strided magnitudes per worker; two order statistics of
+//               the sample (radix select in LDS) give a band [lo, hi] that
+//               holds the k-th largest key with very high probability.
+//   2. filter:  one streaming pass; one wave per 1024-element tile compacts
+//               the entries with key >= lo in index order (wave ballots, no
+//               atomics, no barriers) into the tile's own slot, and the
+//               candidate keys (lo <= key <= hi) into a second slot.
 //   3. totals:  per worker, the number of sure entries (key > hi) and of
 //               candidates; if the band missed, the worker is re-filtered with
 //               the band [0, max] (exact, slower).
@@ -27,11 +27,13 @@
 namespace sg {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_TILE = 4096;
+constexpr int TK_TILE = 1024;      // elements per filter tile (one wave)
 constexpr int TK_SAMPLES = 16384;
 constexpr int TK_DIGIT_BITS = 11;
 constexpr int TK_BINS = 1 << TK_DIGIT_BITS;
-constexpr int TK_HIST_GROUP = 128; // tiles per histogram block
+constexpr int TK_HIST_GROUP = 512; // tiles per histogram block
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct SelState {
     uint32_t lo, hi;       // band
@@ -173,34 +175,55 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
 // --------------------------------------------------------------------------
 // 2. filter: one pass over the dense data
 // --------------------------------------------------------------------------
-// Element e of a tile, for iteration i, thread t, vector lane v:
-//   e = i * (TK_THREADS * EPV) + t * EPV + v      (EPV = 16 bytes / element size)
-template <int EPV, bool VEC>
-__device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uint32_t t, uint32_t lo, uint32_t hi,
-                                            uint32_t* chunk_ge, uint32_t* chunk_ca)
+// One wave owns one tile of TK_TILE elements; there is no LDS and no barrier,
+// so every wave streams independently.  Element e of a tile, for iteration i,
+// lane l and vector element v:
+//   e = i * (64 * EPV) + l * EPV + v          (EPV = 16 bytes / element size)
+// which is ascending in (i, l, v): the compacted slots keep index order.
+// A lane's count of selected elements (0..EPV) is prefix-summed over the wave
+// bit plane by bit plane, one ballot per plane.
+template <int EPV>
+__device__ __forceinline__ void wave_count_scan(uint32_t c, uint64_t lt, uint32_t& excl, uint32_t& total)
 {
-    constexpr int ITERS = TK_TILE / (TK_THREADS * EPV);
-    constexpr int NCH = ITERS * (TK_THREADS / SG_WAVE);
-    const uint32_t wid = threadIdx.x / SG_WAVE;
+    constexpr int CB = EPV == 4 ? 3 : 4; // bits of a count in [0, EPV]
+    excl = 0;
+    total = 0;
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+        const uint64_t m = ballot((c >> b) & 1u);
+        excl += popc64(m & lt) << b;
+        total += popc64(m) << b;
+    }
+}
+
+template <int EPV, bool VEC>
+__device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uint32_t t, uint32_t lo, uint32_t hi)
+{
+    constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
+    const uint32_t lane = lane_id();
+    const uint64_t lt = lanemask_lt();
     const uint64_t tile0 = (uint64_t)t * TK_TILE;
-    const uint64_t len = (p.M - tile0) < (uint64_t)TK_TILE ? (p.M - tile0) : (uint64_t)TK_TILE;
+    const uint32_t len = (p.M - tile0) < (uint64_t)TK_TILE ? (uint32_t)(p.M - tile0) : (uint32_t)TK_TILE;
     const uint64_t gbase = (uint64_t)w * p.M + tile0;
-    const uint64_t slot = ((uint64_t)w * p.NT + t) * TK_TILE;
+    const uint64_t g = (uint64_t)w * p.NT + t;
+    const uint64_t slot = g * TK_TILE;
 
     uint32_t bits[ITERS][EPV];
     const bool full = VEC && len == TK_TILE;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
+        const uint32_t e0 = i * (SG_WAVE * EPV) + lane * EPV;
         if (full) {
+            // 16 bytes per lane; the dense data is read once, so the load
+            // does not keep it in the caches
+            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                static_cast<const char*>(p.dense) + (gbase + e0) * (EPV == 4 ? 4u : 2u)));
             if constexpr (EPV == 4) {
-                uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(p.dense) + gbase + e0);
                 bits[i][0] = x.x;
                 bits[i][1] = x.y;
                 bits[i][2] = x.z;
                 bits[i][3] = x.w;
             } else {
-                uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dense) + gbase + e0);
                 uint32_t q[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
                 for (int v = 0; v < EPV; ++v) bits[i][v] = (q[v / 2] >> (16 * (v % 2))) & 0xffffu;
@@ -211,99 +234,69 @@ __device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uin
                 bits[i][v] = (e0 + v < len) ? load_bits(p, gbase + e0 + v) : 0u;
         }
     }
-    // per-chunk counts (chunk = iteration i, wave wid), ordered i-major
-    uint32_t pre_ge[ITERS][EPV], pre_ca[ITERS][EPV];
-    uint32_t fl_ge = 0, fl_ca = 0;
+    uint32_t run_ge = 0, run_ca = 0;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
-        uint32_t below_ge = 0, below_ca = 0, tot_ge = 0, tot_ca = 0;
-        uint32_t own_ge = 0, own_ca = 0;
+        const uint32_t e0 = i * (SG_WAVE * EPV) + lane * EPV;
+        uint32_t fge = 0, fca = 0;
 #pragma unroll
         for (int v = 0; v < EPV; ++v) {
-            uint32_t key = key_of_bits(bits[i][v], p.bf16);
-            bool valid = e0 + v < len;
-            bool ge = valid && key >= lo;
-            bool ca = ge && key <= hi;
-            uint64_t mg = ballot(ge), mc = ballot(ca);
-            below_ge += popc64(mg & lanemask_lt());
-            below_ca += popc64(mc & lanemask_lt());
-            tot_ge += popc64(mg);
-            tot_ca += popc64(mc);
-            pre_ge[i][v] = own_ge;
-            pre_ca[i][v] = own_ca;
-            own_ge += ge;
-            own_ca += ca;
-            fl_ge |= (uint32_t)ge << (i * EPV + v);
-            fl_ca |= (uint32_t)ca << (i * EPV + v);
+            const uint32_t key = key_of_bits(bits[i][v], p.bf16);
+            const bool ge = (e0 + v < len) && key >= lo;
+            fge |= (uint32_t)ge << v;
+            fca |= (uint32_t)(ge && key <= hi) << v;
         }
+        uint32_t x, tot;
+        wave_count_scan<EPV>((uint32_t)__popc(fge), lt, x, tot);
+        if (fge) {
+            uint32_t pos = run_ge + x;
 #pragma unroll
-        for (int v = 0; v < EPV; ++v) {
-            pre_ge[i][v] += below_ge;
-            pre_ca[i][v] += below_ca;
-        }
-        if (lane_id() == 0) {
-            chunk_ge[i * (TK_THREADS / SG_WAVE) + wid] = tot_ge;
-            chunk_ca[i * (TK_THREADS / SG_WAVE) + wid] = tot_ca;
-        }
-    }
-    __syncthreads();
-    // chunk prefixes (at most 16 chunks)
-    uint32_t base_ge[ITERS], base_ca[ITERS], all_ge = 0, all_ca = 0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int i = c / (TK_THREADS / SG_WAVE), cw = c % (TK_THREADS / SG_WAVE);
-        if (cw == (int)wid) {
-            base_ge[i] = all_ge;
-            base_ca[i] = all_ca;
-        }
-        all_ge += chunk_ge[c];
-        all_ca += chunk_ca[c];
-    }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        const uint32_t e0 = i * (TK_THREADS * EPV) + threadIdx.x * EPV;
-#pragma unroll
-        for (int v = 0; v < EPV; ++v) {
-            const int b = i * EPV + v;
-            if ((fl_ge >> b) & 1u) {
-                uint32_t pos = base_ge[i] + pre_ge[i][v];
-                p.slot_idx[slot + pos] = (uint32_t)(tile0 + e0 + v);
-                p.slot_val[slot + pos] = bits[i][v];
+            for (int v = 0; v < EPV; ++v) {
+                if ((fge >> v) & 1u) {
+                    p.slot_idx[slot + pos] = (uint32_t)(tile0 + e0 + v);
+                    p.slot_val[slot + pos] = bits[i][v];
+                    ++pos;
+                }
             }
-            if ((fl_ca >> b) & 1u) p.slot_key[slot + base_ca[i] + pre_ca[i][v]] = key_of_bits(bits[i][v], p.bf16);
+        }
+        run_ge += tot;
+        if (ballot(fca != 0)) { // candidates are rare: the band is narrow
+            wave_count_scan<EPV>((uint32_t)__popc(fca), lt, x, tot);
+            uint32_t pos = run_ca + x;
+#pragma unroll
+            for (int v = 0; v < EPV; ++v) {
+                if ((fca >> v) & 1u) {
+                    p.slot_key[slot + pos] = key_of_bits(bits[i][v], p.bf16);
+                    ++pos;
+                }
+            }
+            run_ca += tot;
         }
     }
-    if (threadIdx.x == 0) {
-        p.tcnt[(uint64_t)w * p.NT + t] = all_ge;
-        p.ccnt[(uint64_t)w * p.NT + t] = all_ca;
+    if (lane == 0) {
+        p.tcnt[g] = run_ge;
+        p.ccnt[g] = run_ca;
     }
-    __syncthreads(); // chunk arrays are reused by the next tile
 }
 
-// redo_only: process only workers whose band missed (st.redo == 1)
-template <int EPV, bool VEC>
-__global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(TopkParams p, int redo_only)
+// REDO: process only the workers whose band missed (st.redo == 1); the whole
+// launch returns at once when there are none.
+template <int EPV, bool VEC, bool REDO>
+__global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(TopkParams p)
 {
-    __shared__ uint32_t chunk_ge[16], chunk_ca[16];
-    __shared__ uint32_t any_redo;
-    const uint64_t ntiles = (uint64_t)p.n * p.NT;
-    if (redo_only) {
-        if (threadIdx.x == 0) any_redo = 0;
-        __syncthreads();
-        for (uint32_t w = threadIdx.x; w < p.n; w += TK_THREADS)
-            if (p.st[w].redo) any_redo = 1;
-        __syncthreads();
-        if (!any_redo) return;
+    if (REDO) {
+        bool any = false;
+        for (uint32_t w = lane_id(); w < p.n; w += SG_WAVE) any |= p.st[w].redo != 0;
+        if (!ballot(any)) return;
     }
-    for (uint64_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+    const uint64_t ntiles = (uint64_t)p.n * p.NT;
+    const uint64_t stride = (uint64_t)gridDim.x * (TK_THREADS / SG_WAVE);
+    for (uint64_t g = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE; g < ntiles;
+         g += stride) {
         const uint32_t w = (uint32_t)(g / p.NT), t = (uint32_t)(g % p.NT);
         const SelState& st = p.st[w];
-        if (redo_only && st.redo == 0) {
-            // skip the rest of this worker's tiles in this block's stride
-            continue;
-        }
-        filter_tile<EPV, VEC>(p, w, t, st.lo, st.hi, chunk_ge, chunk_ca);
+        if (REDO && st.redo == 0) continue;
+        filter_tile<EPV, VEC>(p, w, t, st.lo, st.hi);
     }
 }
 
@@ -488,22 +481,40 @@ __global__ __launch_bounds__(TK_THREADS) void topk_tilecount_kernel(TopkParams p
     }
 }
 
+// Per-worker exclusive scans of the per-tile counts; each thread takes 8
+// consecutive tiles per round.
 __global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
 {
+    constexpr uint32_t PT = 8;
     __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
     const uint32_t w = blockIdx.x;
     uint32_t carry_gt = 0, carry_eq = 0;
-    for (uint32_t base = 0; base < p.NT; base += 1024) {
-        const uint32_t t = base + threadIdx.x;
-        const uint64_t g = (uint64_t)w * p.NT + t;
-        uint32_t a = t < p.NT ? p.gtx[g] : 0u, b = t < p.NT ? p.eqx[g] : 0u;
+    for (uint32_t base = 0; base < p.NT; base += 1024 * PT) {
+        const uint32_t t0 = base + threadIdx.x * PT;
+        const uint64_t g0 = (uint64_t)w * p.NT + t0;
+        uint32_t a[PT], b[PT], sa = 0, sb = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < PT; ++j) {
+            const bool in = t0 + j < p.NT;
+            a[j] = in ? p.gtx[g0 + j] : 0u;
+            b[j] = in ? p.eqx[g0 + j] : 0u;
+            sa += a[j];
+            sb += b[j];
+        }
         uint32_t ta, tb;
-        uint32_t xa = block_excl_scan<1024>(a, scan_lds, &ta);
+        uint32_t xa = block_excl_scan<1024>(sa, scan_lds, &ta);
         __syncthreads();
-        uint32_t xb = block_excl_scan<1024>(b, scan_lds, &tb);
-        if (t < p.NT) {
-            p.gtx[g] = carry_gt + xa;
-            p.eqx[g] = carry_eq + xb;
+        uint32_t xb = block_excl_scan<1024>(sb, scan_lds, &tb);
+        xa += carry_gt;
+        xb += carry_eq;
+#pragma unroll
+        for (uint32_t j = 0; j < PT; ++j) {
+            if (t0 + j < p.NT) {
+                p.gtx[g0 + j] = xa;
+                p.eqx[g0 + j] = xb;
+            }
+            xa += a[j];
+            xb += b[j];
         }
         carry_gt += ta;
         carry_eq += tb;
@@ -610,18 +621,30 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     topk_sample_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     const uint64_t ntiles = (uint64_t)n * p.NT;
-    const unsigned fgrid = (unsigned)(ntiles < 8192 ? ntiles : 8192);
+    const uint64_t fblocks = ceil_div(ntiles, TK_THREADS / SG_WAVE);
+    const unsigned fgrid = (unsigned)(fblocks < 16384 ? fblocks : 16384);
     for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 0) probe_begin(SG_PROBE_TOPK_FILTER, st);
-        if (p.bf16) {
-            if (rows_aligned) topk_filter_kernel<8, true><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
-            else topk_filter_kernel<8, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+        if (pass == 0) {
+            probe_begin(SG_PROBE_TOPK_FILTER, st);
+            if (p.bf16) {
+                if (rows_aligned) topk_filter_kernel<8, true, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<8, false, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+            } else {
+                if (rows_aligned) topk_filter_kernel<4, true, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<4, false, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+            }
+            SG_TRY_LAUNCH();
+            probe_end(SG_PROBE_TOPK_FILTER, st);
         } else {
-            if (rows_aligned) topk_filter_kernel<4, true><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
-            else topk_filter_kernel<4, false><<<fgrid, TK_THREADS, 0, st>>>(p, pass);
+            if (p.bf16) {
+                if (rows_aligned) topk_filter_kernel<8, true, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<8, false, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+            } else {
+                if (rows_aligned) topk_filter_kernel<4, true, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<4, false, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+            }
+            SG_TRY_LAUNCH();
         }
-        SG_TRY_LAUNCH();
-        if (pass == 0) probe_end(SG_PROBE_TOPK_FILTER, st);
         topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
         SG_TRY_LAUNCH();
     }
