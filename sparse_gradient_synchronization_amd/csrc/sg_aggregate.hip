@@ -6,78 +6,67 @@
 
 namespace sg {
 
-// Bucket width 2^bs so that a (group, bucket) holds about MG_TARGET/2 entries
-// on average, with the boundary table n*G*(NB+1) words kept under 16M entries.
-static void choose_buckets(uint32_t n, uint32_t G, uint64_t M, uint64_t total, uint32_t* bs, uint32_t* NB)
+constexpr uint32_t MG_STATS_MAX_GRID = 2048; // persistent blocks of the statistics pass, at most
+
+// Tile width 2^tb so that a (group, tile) holds MG_TARGET to 2*MG_TARGET
+// entries on average, within [2^5, 2^MG_SPAN_LOG] keys.
+static void choose_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, uint32_t* NT)
 {
-    const double want = total > 0 ? (double)(MG_TARGET / 2) * (double)M * (double)G / (double)total : (double)M;
-    uint32_t b = 0;
-    while (b < MG_SPAN_LOG && (double)(1ull << (b + 1)) <= want) ++b;
-    for (;;) {
-        uint64_t nb = (M + (1ull << b) - 1) >> b;
-        if (nb == 0) nb = 1;
-        // a bucket never spans more keys than a tile may
-        if ((uint64_t)n * G * (nb + 1) <= (16ull << 20) || b >= MG_SPAN_LOG) {
-            *bs = b;
-            *NB = (uint32_t)nb;
-            return;
-        }
-        ++b;
+    uint32_t b = MG_SPAN_LOG;
+    if (total > 0) {
+        const double want = (double)MG_TARGET * (double)G * (double)M / (double)total;
+        b = 0;
+        while (b < 63 && (double)(1ull << (b + 1)) <= want) ++b;
+        ++b; // 2^b > want
+        if (b < 5) b = 5;
+        if (b > MG_SPAN_LOG) b = MG_SPAN_LOG;
     }
+    *tb = b;
+    uint64_t nt = (M + (1ull << b) - 1) >> b;
+    *NT = (uint32_t)(nt ? nt : 1);
 }
 
-static void merge_sizes(MergeParams* p)
+static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
 {
-    const uint64_t splits = 4 * ceil_div(p->total, MG_TARGET);
-    p->tcap = (uint32_t)(p->NB + splits + 2);
-    p->max_tiles = (uint32_t)((uint64_t)p->G * p->NB + splits + p->G);
-    p->max_rows = p->max_tiles + p->G;
-}
-
-static uint64_t merge_carve(Carver& c, MergeParams* p)
-{
-    merge_sizes(p);
     const uint64_t R = (uint64_t)p->n * p->G;
+    const uint64_t T = (uint64_t)p->G * p->NT;
+    p->nscan = (uint32_t)ceil_div(T, MG_SCAN_BLOCK);
     p->chunk_start = c.take<uint32_t>(R + 1);
-    p->bnd = c.take<uint32_t>(R * (p->NB + 1));
-    p->tile_key = c.take<uint64_t>((uint64_t)p->G * p->tcap);
-    p->ntiles = c.take<uint32_t>(p->G);
-    p->tile_prefix = c.take<uint32_t>((uint64_t)p->G + 1);
-    p->tile_pos = c.take<uint32_t>((uint64_t)p->max_rows * p->n);
-    p->tile_group = c.take<uint32_t>(p->max_tiles);
-    p->tile_lo = c.take<uint64_t>(p->max_tiles);
-    p->tile_hi = c.take<uint64_t>(p->max_tiles);
-    p->status = c.take<uint64_t>(p->max_tiles);
-    p->ticket = c.take<uint32_t>(1);
+    p->bnd = c.take<uint32_t>(R * (p->NT + 1));
+    p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
+    p->heavy = c.take<uint32_t>(T);
+    if (mode == MODE_AGG) {
+        p->tile_cnt = c.take<uint32_t>(T);
+        p->tile_sb = c.take<uint64_t>(T);
+        p->tile_out = c.take<uint64_t>(T);
+        p->blk_sum = c.take<uint64_t>(p->nscan);
+        p->stage_idx = c.take<uint32_t>(p->total);
+        p->stage_val = c.take<float>(p->total * (p->D > 1 ? p->D : 1));
+    } else {
+        p->st_part = c.take<uint64_t>((uint64_t)MG_STATS_MAX_GRID * p->st_row);
+    }
     return c.bytes();
 }
 
-// Queue the engine: plan, boundaries, tiles, merge.
-static int merge_run(MergeParams& p, int mode, hipStream_t st)
+// Queue the engine: plan, boundaries, merge (and, for the aggregate, the
+// scan and placement).  `stats_out` receives the reduced statistics row.
+static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_out)
 {
     const uint64_t R = (uint64_t)p.n * p.G;
-    merge_sizes(&p);
-    mg_plan_kernel<<<1, MG_THREADS, 0, st>>>(p);
+    const uint64_t T = (uint64_t)p.G * p.NT;
+    mg_plan_kernel<<<1, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     const uint64_t nchunks = ceil_div(p.total, MG_CHUNK) + R;
     probe_begin(SG_PROBE_AGGREGATE_BND, st);
-    mg_bnd_kernel<<<(unsigned)nchunks, MG_THREADS, 0, st>>>(p);
+    mg_bnd_kernel<<<(unsigned)nchunks, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_BND, st);
-    const uint64_t cells = R * (p.NB + 1);
+    const uint64_t cells = R * (p.NT + 1);
     mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    mg_tiles_kernel<<<p.G, 1024, 0, st>>>(p);
+    mg_heavy_kernel<<<(unsigned)ceil_div(T, 256), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    mg_tile_prefix_kernel<<<1, MG_THREADS, 0, st>>>(p);
-    SG_TRY_LAUNCH();
-    mg_refine_kernel<<<p.max_rows < 4096u ? p.max_rows : 4096u, MG_THREADS, 0, st>>>(p);
-    SG_TRY_LAUNCH();
-    if (mode == MODE_AGG) {
-        int rc = fill_u64(p.status, p.max_tiles, 0, st);
-        if (rc) return rc;
-    }
-    // persistent grid: as many blocks as can be resident at once
+    // persistent blocks: as many as can be resident at once
     static int resident[2] = {0, 0};
     if (!resident[mode]) {
         int dev = 0, cus = 0, per = 0;
@@ -89,12 +78,27 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st)
             SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mg_merge_kernel<MODE_STATS>, MG_THREADS, 0));
         resident[mode] = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
     }
-    const unsigned grid = p.max_tiles < (uint32_t)resident[mode] ? p.max_tiles : (unsigned)resident[mode];
-    probe_begin((mode == MODE_AGG ? SG_PROBE_AGGREGATE_MERGE : -1), st);
-    if (mode == MODE_AGG) mg_merge_kernel<MODE_AGG><<<grid, MG_THREADS, 0, st>>>(p);
-    else mg_merge_kernel<MODE_STATS><<<grid, MG_THREADS, 0, st>>>(p);
+    const uint64_t wblocks = ceil_div(T, MG_WAVES);
+    uint64_t grid = wblocks < (uint64_t)resident[mode] ? wblocks : (uint64_t)resident[mode];
+    if (mode == MODE_STATS && grid > MG_STATS_MAX_GRID) grid = MG_STATS_MAX_GRID;
+    if (grid == 0) grid = 1;
+    if (mode == MODE_AGG) {
+        probe_begin(SG_PROBE_AGGREGATE_MERGE, st);
+        mg_merge_kernel<MODE_AGG><<<(unsigned)grid, MG_THREADS, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        probe_end(SG_PROBE_AGGREGATE_MERGE, st);
+        mg_scan_local_kernel<<<p.nscan, 1024, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        mg_scan_top_kernel<<<1, 1024, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        mg_place_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        return SG_OK;
+    }
+    mg_merge_kernel<MODE_STATS><<<(unsigned)grid, MG_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    probe_end((mode == MODE_AGG ? SG_PROBE_AGGREGATE_MERGE : -1), st);
+    mg_stats_reduce_kernel<<<p.st_row, 256, 0, st>>>(p, (uint32_t)grid, stats_out);
+    SG_TRY_LAUNCH();
     return SG_OK;
 }
 
@@ -102,7 +106,7 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st)
 
 using namespace sg;
 
-static void agg_setup(MergeParams* p, uint32_t n, uint32_t P, uint64_t M, uint64_t total)
+static void agg_setup(MergeParams* p, uint32_t n, uint32_t P, uint64_t M, uint64_t total, uint32_t D)
 {
     *p = MergeParams();
     p->n = n;
@@ -110,17 +114,17 @@ static void agg_setup(MergeParams* p, uint32_t n, uint32_t P, uint64_t M, uint64
     p->stride = P + 1;
     p->M = M;
     p->total = total;
-    choose_buckets(n, P, M, total, &p->bs, &p->NB);
+    p->D = D;
+    choose_tiles(P, M, total, &p->tb, &p->NT);
 }
 
 extern "C" size_t sg_aggregate_workspace_bytes(uint32_t n, uint32_t P, uint64_t M, uint64_t total, uint32_t D)
 {
-    (void)D;
     if (n == 0 || P == 0) return 256;
     MergeParams p;
-    agg_setup(&p, n, P, M, total);
+    agg_setup(&p, n, P, M, total, D);
     Carver c(nullptr);
-    return merge_carve(c, &p);
+    return merge_carve(c, &p, MODE_AGG);
 }
 
 extern "C" int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
@@ -137,18 +141,17 @@ extern "C" int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype d
     if (ws_bytes < sg_aggregate_workspace_bytes(n, P, M, total, D)) return SG_ECAPACITY;
 
     MergeParams p;
-    agg_setup(&p, n, P, M, total);
+    agg_setup(&p, n, P, M, total, D);
     Carver c(d_ws);
-    merge_carve(c, &p);
+    merge_carve(c, &p, MODE_AGG);
     p.idx = d_idx;
     p.off = d_part_off;
     p.val = d_val;
-    p.D = D;
     p.bf16 = dt == SG_BF16;
     p.agg_idx = d_agg_idx;
     p.agg_val = d_agg_val;
     p.agg_off = d_agg_off;
     p.capacity = capacity;
     p.div = make_divider(P);
-    return merge_run(p, MODE_AGG, as_stream(stream));
+    return merge_run(p, MODE_AGG, as_stream(stream), nullptr);
 }

@@ -41,14 +41,29 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 __device__ __forceinline__ uint32_t popc64(uint64_t x) { return (uint32_t)__popcll(x); }
 
-// inclusive scan over the 64 lanes of a wave
+// Cross-lane moves by DPP (data-parallel primitives of the GFX9 ISA family):
+// a lane reads another lane's register inside the VALU, without the LDS
+// round trip of ds_bpermute.  Lanes whose source is outside its row, or whose
+// row is masked off, receive `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t old, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// inclusive scan over the 64 lanes of a wave: log steps inside each row of
+// 16 lanes, then row 0's total into row 1 (and row 2's into row 3), then the
+// first half's total into the second half
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
 {
-#pragma unroll
-    for (int d = 1; d < SG_WAVE; d <<= 1) {
-        uint32_t t = __shfl_up(v, d, SG_WAVE);
-        if ((int)lane_id() >= d) v += t;
-    }
+    v += dpp_move<kDppRowShr1>(0u, v);
+    v += dpp_move<kDppRowShr2>(0u, v);
+    v += dpp_move<kDppRowShr4>(0u, v);
+    v += dpp_move<kDppRowShr8>(0u, v);
+    v += dpp_move<kDppRowBcast15, 0xa>(0u, v);
+    v += dpp_move<kDppRowBcast31, 0xc>(0u, v);
     return v;
 }
 
@@ -62,21 +77,24 @@ __device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t v)
     return v;
 }
 
+// sum over the wave, the same in every lane
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-#pragma unroll
-    for (int d = SG_WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, SG_WAVE);
-    return v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), SG_WAVE - 1);
 }
 
+// minimum over the wave, the same in every lane
 __device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
-#pragma unroll
-    for (int d = SG_WAVE / 2; d > 0; d >>= 1) {
-        uint32_t t = __shfl_xor(v, d, SG_WAVE);
-        v = t < v ? t : v;
-    }
-    return v;
+    constexpr uint32_t top = 0xffffffffu;
+    uint32_t t;
+    t = dpp_move<kDppRowShr1>(top, v); v = t < v ? t : v;
+    t = dpp_move<kDppRowShr2>(top, v); v = t < v ? t : v;
+    t = dpp_move<kDppRowShr4>(top, v); v = t < v ? t : v;
+    t = dpp_move<kDppRowShr8>(top, v); v = t < v ? t : v;
+    t = dpp_move<kDppRowBcast15, 0xa>(top, v); v = t < v ? t : v;
+    t = dpp_move<kDppRowBcast31, 0xc>(top, v); v = t < v ? t : v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, SG_WAVE - 1);
 }
 
 // Exclusive scan over the threads of a block of NT threads (NT a multiple of

@@ -9,38 +9,48 @@
 // (statistics).
 //
 // Design for gfx950:
+//   tiles  the key space of every group is cut into fixed tiles of 2^tb keys
+//          (tb chosen from the mean density so a tile holds a few hundred
+//          entries); tile t = g * NT + b.
 //   bnd    one streaming pass over the run entries records, per run, where
-//          each key bucket of width 2^bs begins (plain stores, no atomics);
-//   tiles  per group, consecutive buckets are grouped into tiles of about
-//          2048 entries (at most 4096, and at most 2^20 keys wide; a denser
-//          bucket is split into key sub-ranges), from the bucket totals;
-//   union  persistent blocks take tiles in order through an atomic ticket
-//          and hold a tile's entries in registers (8 per thread).  A
-//          two-level presence bitmap over the tile's key span (one bit per
-//          32-key group, then one word per non-empty group) gives every key
-//          its rank among the tile's distinct keys by prefix popcounts, with
-//          no sorting and no merge chains.  Values are summed into the rank
-//          slots one worker after another, so every sum is taken in worker
-//          order (deterministic, the order of a ring).  Output offsets come
-//          from a decoupled look-back over the tiles' unique counts (bounded
-//          spin).  A tile with more than 4096 entries (a key sub-range denser
-//          than its neighbours) is consumed in windows of 4096/n entries per
-//          run, each window ending at the smallest last-loaded key of a cut
-//          run, which guarantees progress.
+//          each tile begins (plain stores, no atomics, no search).
+//   merge  a wave merges one tile at a time with no block barrier: it loads
+//          the tile's entries of all n runs (at most MG_WCAP at once; a
+//          denser tile is consumed in windows that end at the smallest
+//          last-loaded key of a cut run), sets one bit per key in an LDS
+//          bitmap of the tile's span, and prefix popcounts give every key its
+//          rank among the distinct keys.  A 64-bit mask per rank records the
+//          workers holding it; the entries are then laid out by (rank,
+//          worker), so each rank's contributions are summed in worker order
+//          (the order of a ring) by one lane, deterministically.  Aggregate
+//          output goes to a staging area at the tile's input offset (a tile
+//          never has more distinct keys than entries), so tiles are
+//          independent.  Waves are persistent: tiles with many entries are
+//          dealt out first, the rest come from 64 queues of contiguous tiles
+//          with a ticket counter each.
+//   place  a scan of the tiles' distinct counts and a copy of every tile's
+//          staged entries to its final offset.
 #include "sg_host.h"
 
 namespace sg {
 
-constexpr int MG_THREADS = 512;
-constexpr int MG_CAP = 4096;        // entries of a tile (window) held at once, in registers
-constexpr int MG_TARGET = 2048;     // target entries per tile
-constexpr int MG_PER = MG_CAP / MG_THREADS;
-constexpr int MG_SPAN_LOG = 20;     // a tile spans at most 2^20 keys
-constexpr int MG_CWORDS = (1 << MG_SPAN_LOG) >> 10; // coarse bitmap words: one bit per 32 keys
-constexpr int MG_CHUNK = 4096;      // run entries per bnd block
-constexpr uint64_t MG_FLAG_AGG = 1ull << 62;
-constexpr uint64_t MG_FLAG_INC = 2ull << 62;
-constexpr uint64_t MG_VAL_MASK = (1ull << 62) - 1;
+constexpr int MG_WAVES = 4;                          // waves per block
+constexpr int MG_THREADS = MG_WAVES * SG_WAVE;
+constexpr int MG_WCAP = 256;                         // entries of a window
+constexpr int MG_PER = MG_WCAP / SG_WAVE;            // entries per lane
+constexpr int MG_SPAN_LOG = 13;                      // a tile spans at most 2^13 keys
+constexpr int MG_WORDS = (1 << MG_SPAN_LOG) / 32;    // bitmap words of a span
+constexpr int MG_WPL = MG_WORDS / SG_WAVE;           // bitmap words per lane
+constexpr int MG_TARGET = 128;                       // mean entries per tile aimed at
+constexpr int MG_CHUNK = 4096;                       // run entries per bnd block
+constexpr int MG_HEAVY = 2 * MG_WCAP;                // a tile with more entries is scheduled first
+constexpr int MG_CHUNK_TILES = 4;                    // tiles per work ticket
+constexpr int MG_NQ = 64;                            // work queues (contiguous tile ranges)
+constexpr int MG_QSTRIDE = 64;                       // words between queue counters (separate lines)
+constexpr int MG_SCAN_PER = 8;                       // tiles per thread in the tile scan
+constexpr int MG_SCAN_BLOCK = 1024 * MG_SCAN_PER;    // tiles per scan block
+static_assert(MG_WCAP >= 64, "a window must hold one entry of each of up to 64 runs");
+static_assert(MG_WORDS >= MG_WCAP, "ranks reuse the bitmap words");
 
 enum MergeMode { MODE_AGG = 0, MODE_STATS = 1 };
 
@@ -52,8 +62,8 @@ struct MergeParams {
     uint32_t G, n;
     uint64_t total;
     uint64_t M;
-    uint32_t bs;            // bucket width 2^bs
-    uint32_t NB;            // buckets
+    uint32_t tb;            // tile width 2^tb keys
+    uint32_t NT;            // tiles per group
     // values (aggregate)
     const void* val;
     uint32_t D;
@@ -64,25 +74,22 @@ struct MergeParams {
     uint64_t capacity;
     // workspace
     uint32_t* chunk_start;  // [n*G + 1] bnd blocks per run (position order)
-    uint32_t* bnd;          // [(g*n + w) * (NB+1) + b]
-    uint64_t* tile_key;     // [G * tcap] first key of tile j of group g (j <= ntiles[g]: sentinel)
-    uint32_t* ntiles;       // [G]
-    uint32_t* tile_prefix;  // [G+1]
-    uint32_t* tile_pos;     // [rows * n] start (relative to the run) of run w in tile row r
-    uint32_t* tile_group;   // [max_tiles] group of global tile t (tile row = t + group)
-    uint64_t* tile_lo;      // [max_tiles] first key of tile t
-    uint64_t* tile_hi;      // [max_tiles] end key of tile t
-    uint64_t* status;       // [max_tiles] look-back words
-    uint32_t* ticket;       // [1]
-    uint32_t tcap;          // tile slots per group
-    uint32_t max_tiles;     // bound on the total number of tiles
-    uint32_t max_rows;      // max_tiles + G (one sentinel row per group)
+    uint32_t* bnd;          // [(g*n + w) * (NT+1) + b]
+    uint32_t* tile_cnt;     // [G*NT] distinct keys of a tile
+    uint64_t* tile_sb;      // [G*NT] staging offset of a tile
+    uint64_t* tile_out;     // [G*NT] exclusive prefix inside its scan block
+    uint64_t* blk_sum;      // [nscan] scan block totals, then their exclusive prefix
+    uint32_t nscan;
+    uint32_t* stage_idx;    // [total]
+    float* stage_val;       // [total * D]
+    uint32_t* queue;        // [MG_NQ * MG_QSTRIDE]: queue[0] heavy tiles listed; queue[q * MG_QSTRIDE + 1] chunk tickets of queue q
+    uint32_t* heavy;        // [G*NT] tiles with more than MG_HEAVY entries
     // statistics
-    uint64_t* st_inter;     // [n*n]
-    uint64_t* st_union;     // [1]
-    uint64_t* st_ucontig;   // [Ps]
-    uint64_t* st_uhashed;   // [Ps]
+    uint64_t* st_part;      // [grid][st_row] per-block partial counts
+    uint32_t st_row;        // words per partial row: npairs + 1 + 2*Ps
+    uint32_t npairs;
     uint32_t Ps;            // parts for skew
+    double inv_m;           // 1 / M
     uint32_t seed;
     int hashed;
     Divider div;
@@ -98,13 +105,22 @@ __device__ __forceinline__ void run_range(const MergeParams& p, uint32_t g, uint
     e = b;
 }
 
-// runs in position order: r' = w*G + g
-__global__ __launch_bounds__(MG_THREADS) void mg_plan_kernel(MergeParams p)
+// LDS written by some lanes of a wave and read by others: a wave executes its
+// LDS operations in order; this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_sync()
 {
-    __shared__ uint32_t scan_lds[MG_THREADS / SG_WAVE + 1];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// runs in position order: r' = w*G + g
+__global__ __launch_bounds__(512) void mg_plan_kernel(MergeParams p)
+{
+    __shared__ uint32_t scan_lds[512 / SG_WAVE + 1];
     const uint32_t R = p.n * p.G;
     uint32_t carry = 0;
-    for (uint32_t base = 0; base < R; base += MG_THREADS) {
+    for (uint32_t base = 0; base < R; base += 512) {
         const uint32_t r = base + threadIdx.x;
         uint32_t c = 0;
         if (r < R) {
@@ -113,26 +129,28 @@ __global__ __launch_bounds__(MG_THREADS) void mg_plan_kernel(MergeParams p)
             c = (uint32_t)ceil_div_dev(e - s, MG_CHUNK);
         }
         uint32_t tot;
-        uint32_t ex = block_excl_scan<MG_THREADS>(c, scan_lds, &tot);
+        uint32_t ex = block_excl_scan<512>(c, scan_lds, &tot);
         if (r < R) p.chunk_start[r] = carry + ex;
         carry += tot;
         __syncthreads();
     }
     if (threadIdx.x == 0) p.chunk_start[R] = carry;
+    for (uint32_t i = threadIdx.x; i < (uint32_t)(MG_NQ * MG_QSTRIDE); i += 512) p.queue[i] = 0;
 }
 
-__device__ __forceinline__ uint32_t bucket_of(const MergeParams& p, uint32_t key)
+__device__ __forceinline__ uint32_t tile_of(const MergeParams& p, uint32_t key)
 {
-    uint64_t b = p.bs >= 32 ? 0ull : ((uint64_t)key >> p.bs);
-    if (b >= p.NB) {
+    uint64_t b = (uint64_t)key >> p.tb;
+    if (b >= p.NT) {
         report_error(kDevErrIndexRange);
-        b = p.NB - 1;
+        b = p.NT - 1;
     }
     return (uint32_t)b;
 }
 
-// bnd[run][b] = first position (relative to the run) whose key is >= b * 2^bs
-__global__ __launch_bounds__(MG_THREADS) void mg_bnd_kernel(MergeParams p)
+// bnd[run][b] = first position (relative to the run) whose key is >= b * 2^tb;
+// bnd[run][NT] = the run's length.
+__global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 {
     const uint32_t R = p.n * p.G;
     const uint32_t c = blockIdx.x;
@@ -148,26 +166,23 @@ __global__ __launch_bounds__(MG_THREADS) void mg_bnd_kernel(MergeParams p)
     run_range(p, g, w, s, e);
     const uint64_t len = e - s;
     const uint64_t j0 = (uint64_t)(c - p.chunk_start[rp]) * MG_CHUNK;
-    uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NB + 1);
-    for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && j < len; j += MG_THREADS) {
-        const uint32_t b = bucket_of(p, p.idx[s + j]);
+    uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
+    for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && j < len; j += 512) {
+        const uint32_t b = tile_of(p, p.idx[s + j]);
         int64_t pb = -1;
-        if (j > 0) {
-            const uint32_t kp = p.idx[s + j - 1];
-            pb = bucket_of(p, kp);
-        }
+        if (j > 0) pb = tile_of(p, p.idx[s + j - 1]);
         for (int64_t x = pb + 1; x <= (int64_t)b; ++x) row[x] = (uint32_t)j;
         if (j == len - 1)
-            for (uint64_t x = (uint64_t)b + 1; x <= p.NB; ++x) row[x] = (uint32_t)len;
+            for (uint64_t x = (uint64_t)b + 1; x <= p.NT; ++x) row[x] = (uint32_t)len;
     }
 }
 
 // rows of empty runs are all zero
 __global__ void mg_bnd_empty_kernel(MergeParams p)
 {
-    const uint64_t cnt = (uint64_t)p.n * p.G * (p.NB + 1);
+    const uint64_t cnt = (uint64_t)p.n * p.G * (p.NT + 1);
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cnt; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t row = i / (p.NB + 1);
+        const uint64_t row = i / (p.NT + 1);
         const uint32_t g = (uint32_t)(row / p.n), w = (uint32_t)(row % p.n);
         uint64_t s, e;
         run_range(p, g, w, s, e);
@@ -175,551 +190,569 @@ __global__ void mg_bnd_empty_kernel(MergeParams p)
     }
 }
 
-__device__ __forceinline__ uint32_t bnd_at(const MergeParams& p, uint32_t g, uint32_t w, uint32_t b, uint64_t len)
+// Tiles with more than MG_HEAVY entries, listed so the merge starts them
+// first (longest first keeps the last waves short).
+__global__ __launch_bounds__(256) void mg_heavy_kernel(MergeParams p)
 {
-    uint32_t v = p.bnd[((uint64_t)g * p.n + w) * (p.NB + 1) + b];
-    return (uint64_t)v > len ? (uint32_t)len : v;
-}
-
-// One block per group: bucket totals, their prefix, and tiles.  Consecutive
-// buckets are grouped into tiles of about MG_TARGET entries; a bucket holding
-// more than MG_TARGET entries is split into 2^s equal key sub-ranges (dense
-// regions are dense inside the bucket too), so tiles stay near the target.
-__device__ __forceinline__ uint32_t split_log2(uint32_t tot, uint32_t bs)
-{
-    uint32_t need = (tot + MG_TARGET - 1) / MG_TARGET, s = 0;
-    while ((1u << s) < need && s < bs && s < 16) ++s;
-    return s;
-}
-
-__global__ __launch_bounds__(1024) void mg_tiles_kernel(MergeParams p)
-{
-    __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
-    __shared__ uint32_t prev_pre[1024], prev_tot[1024];
-    __shared__ uint32_t carry_lds[4];
-    const uint32_t g = blockIdx.x;
-    uint64_t* keys = p.tile_key + (uint64_t)g * p.tcap;
-    uint32_t carry_pre = 0, carry_tiles = 0;
-    uint32_t last_pre = 0, last_tot = 0;
-    for (uint32_t base = 0; base < p.NB; base += 1024) {
-        const uint32_t b = base + threadIdx.x;
-        uint32_t tot = 0;
-        if (b < p.NB) {
-            for (uint32_t w = 0; w < p.n; ++w) {
-                uint64_t s, e;
-                run_range(p, g, w, s, e);
-                const uint64_t len = e - s;
-                uint32_t x = bnd_at(p, g, w, b, len), y = bnd_at(p, g, w, b + 1, len);
-                tot += y > x ? y - x : 0u;
-            }
-        }
-        uint32_t all;
-        uint32_t pre = carry_pre + block_excl_scan<1024>(tot, scan_lds, &all);
-        prev_pre[threadIdx.x] = pre;
-        prev_tot[threadIdx.x] = tot;
-        __syncthreads();
-        uint32_t ppre = threadIdx.x ? prev_pre[threadIdx.x - 1] : last_pre;
-        uint32_t ptot = threadIdx.x ? prev_tot[threadIdx.x - 1] : last_tot;
-        uint32_t cnt = 0, sl = 0;
-        if (b < p.NB) {
-            const uint32_t span_buckets = p.bs >= MG_SPAN_LOG ? 1u : (1u << (MG_SPAN_LOG - p.bs));
-            const bool flag = (b == 0) || (pre / MG_TARGET != ppre / MG_TARGET) || tot > MG_TARGET ||
-                              ptot > MG_TARGET || (b % span_buckets) == 0;
-            if (flag) {
-                sl = tot > MG_TARGET ? split_log2(tot, p.bs) : 0u;
-                cnt = 1u << sl;
-            }
-        }
-        uint32_t nf;
-        __syncthreads();
-        uint32_t pos = carry_tiles + block_excl_scan<1024>(cnt, scan_lds, &nf);
-        const uint64_t bw = 1ull << p.bs;
-        for (uint32_t i = 0; i < cnt; ++i)
-            if (pos + i < p.tcap) keys[pos + i] = ((uint64_t)b << p.bs) + (uint64_t)i * (bw >> sl);
-        if (threadIdx.x == 1023) {
-            carry_lds[0] = pre;
-            carry_lds[1] = tot;
-        }
-        __syncthreads();
-        last_pre = carry_lds[0];
-        last_tot = carry_lds[1];
-        carry_pre += all;
-        carry_tiles += nf;
-        __syncthreads();
+    const uint32_t T = p.G * p.NT;
+    const uint32_t t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const uint32_t g = t / p.NT, b = t % p.NT;
+    uint32_t E = 0;
+    for (uint32_t w = 0; w < p.n; ++w) {
+        uint64_t s, e;
+        run_range(p, g, w, s, e);
+        const uint64_t len = e - s;
+        const uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
+        uint64_t x = row[b], y = row[b + 1];
+        if (x > len) x = len;
+        if (y > len) y = len;
+        E += y > x ? (uint32_t)(y - x) : 0u;
     }
-    if (threadIdx.x == 0) {
-        uint32_t nt = carry_tiles < p.tcap ? carry_tiles : p.tcap - 1;
-        if (nt != carry_tiles) report_error(kDevErrPartition);
-        p.ntiles[g] = nt;
-        keys[nt] = (uint64_t)p.NB << p.bs;
-    }
-}
-
-__global__ __launch_bounds__(MG_THREADS) void mg_tile_prefix_kernel(MergeParams p)
-{
-    __shared__ uint32_t scan_lds[MG_THREADS / SG_WAVE + 1];
-    uint32_t carry = 0;
-    for (uint32_t base = 0; base < p.G; base += MG_THREADS) {
-        const uint32_t g = base + threadIdx.x;
-        uint32_t c = g < p.G ? p.ntiles[g] : 0u, tot;
-        uint32_t ex = block_excl_scan<MG_THREADS>(c, scan_lds, &tot);
-        if (g < p.G) p.tile_prefix[g] = carry + ex;
-        carry += tot;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        p.tile_prefix[p.G] = carry;
-        p.ticket[0] = 0;
-    }
-}
-
-// lower bound of `target` in the ascending keys a[lo, hi), by one wave:
-// 64 probes per round cut the range 65-fold, then one load finishes.
-__device__ uint64_t wave_lower_bound(const uint32_t* a, uint64_t lo, uint64_t hi, uint64_t target)
-{
-    const uint32_t lane = lane_id();
-    while (hi - lo > SG_WAVE) {
-        const uint64_t len = hi - lo;
-        const uint64_t pos = lo + ((uint64_t)(lane + 1) * len) / 65;
-        const uint32_t c = popc64(ballot((uint64_t)a[pos] < target));
-        const uint64_t nlo = c == 0 ? lo : lo + ((uint64_t)c * len) / 65 + 1;
-        const uint64_t nhi = c == SG_WAVE ? hi : lo + ((uint64_t)(c + 1) * len) / 65;
-        lo = nlo;
-        hi = nhi;
-    }
-    const uint64_t pos = lo + lane;
-    const bool less = pos < hi && (uint64_t)a[pos] < target;
-    return lo + popc64(ballot(less));
-}
-
-// Row r of tile_pos: for every run, where the tile starting at tile_key
-// begins (bucket boundaries come from bnd; split points are searched inside
-// their bucket).  Rows are global: row = tile_prefix[g] + g + j.
-__global__ __launch_bounds__(MG_THREADS) void mg_refine_kernel(MergeParams p)
-{
-    const uint32_t rows = p.tile_prefix[p.G] + p.G;
-    const uint32_t wid = threadIdx.x / SG_WAVE;
-    for (uint32_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        // group of row r: largest g with tile_prefix[g] + g <= r
-        uint32_t lo = 0, hi = p.G;
-        while (lo + 1 < hi) {
-            uint32_t mid = (lo + hi) >> 1;
-            if (p.tile_prefix[mid] + mid <= r) lo = mid;
-            else hi = mid;
-        }
-        const uint32_t g = lo, j = r - (p.tile_prefix[g] + g);
-        const uint64_t key = p.tile_key[(uint64_t)g * p.tcap + j];
-        if (threadIdx.x == 0 && j < p.ntiles[g]) {
-            const uint32_t t = r - g;
-            p.tile_group[t] = g;
-            p.tile_lo[t] = key;
-            p.tile_hi[t] = p.tile_key[(uint64_t)g * p.tcap + j + 1];
-        }
-        const uint32_t b = (uint32_t)(key >> p.bs);
-        const bool aligned = (key & ((1ull << p.bs) - 1ull)) == 0;
-        for (uint32_t w = wid; w < p.n; w += MG_THREADS / SG_WAVE) {
-            uint64_t s, e;
-            run_range(p, g, w, s, e);
-            const uint64_t len = e - s;
-            uint32_t v;
-            if (aligned || b >= p.NB) {
-                v = bnd_at(p, g, w, b < p.NB ? b : p.NB, len);
-            } else {
-                const uint32_t x = bnd_at(p, g, w, b, len), y = bnd_at(p, g, w, b + 1, len);
-                v = (uint32_t)(wave_lower_bound(p.idx + s, x, y > x ? y : x, key));
-            }
-            if (lane_id() == 0) p.tile_pos[(uint64_t)r * p.n + w] = v;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// the merge kernel
-// ---------------------------------------------------------------------------
-// decoupled look-back by wave 0: exclusive prefix of tile `t`
-__device__ uint64_t look_back(const MergeParams& p, uint32_t t)
-{
-    uint64_t sum = 0;
-    int64_t j = (int64_t)t - 1;
-    while (j >= 0) {
-        const int64_t x = j - (int64_t)lane_id();
-        uint64_t s = MG_FLAG_INC; // before tile 0: inclusive 0
-        if (x >= 0) {
-            uint32_t spins = 0;
-            s = load_agent(p.status + x);
-            while ((s >> 62) == 0) {
-                __builtin_amdgcn_s_sleep(2);
-                s = load_agent(p.status + x);
-                if (++spins > (1u << 22)) {
-                    report_error(kDevErrSpin);
-                    s = MG_FLAG_INC;
-                    break;
-                }
-            }
-        }
-        const uint64_t inc = ballot((s >> 62) == 2);
-        const uint32_t first = inc ? (uint32_t)__builtin_ctzll(inc) : 64u;
-        uint64_t v = (lane_id() <= first) ? (s & MG_VAL_MASK) : 0ull;
-        for (int d = SG_WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, SG_WAVE);
-        sum += v;
-        if (inc) break;
-        j -= SG_WAVE;
-    }
-    return sum;
+    if (E > (uint32_t)MG_HEAVY) p.heavy[atomicAdd(&p.queue[0], 1u)] = t;
 }
 
 // Contiguous part of `key` among P parts [floor(iM/P), floor((i+1)M/P)):
-// the largest i with i*M < (key+1)*P, i.e. floor(((key+1)P - 1) / M).
-__device__ __forceinline__ uint32_t contig_part(uint64_t key, uint64_t M, uint32_t P)
+// the largest i with i*M < (key+1)*P, i.e. floor(((key+1)P - 1) / M).  The
+// quotient is estimated in double (x < 2^40, so it is off by at most one)
+// and corrected with exact integer products.
+__device__ __forceinline__ uint32_t contig_part(uint64_t key, uint64_t M, uint32_t P, double inv_m)
 {
-    const uint64_t part = ((key + 1) * P - 1) / (M ? M : 1);
-    return part < P ? (uint32_t)part : P - 1;
+    const uint64_t x = (key + 1) * P - 1;
+    uint64_t q = (uint64_t)((double)x * inv_m);
+    if (q * M > x) --q;
+    else if ((q + 1) * M <= x) ++q;
+    return q < P ? (uint32_t)q : P - 1;
 }
 
-template <int MODE>
-struct UnionSmem {
-    uint32_t coarse[MG_CWORDS];  // bit per 32-key group of the tile span
-    uint16_t cpre[MG_CWORDS];    // non-empty groups before a coarse word
-    uint32_t fine[MG_CAP];       // bits of the non-empty groups; then the distinct keys by rank
-    uint16_t fpre[MG_CAP];       // distinct keys before a fine word
-    union {
-        float acc[MG_CAP];       // sums by rank (scalar values)
-        uint32_t ekey[MG_CAP];   // entry keys by load position (rows)
-        unsigned long long mask[MODE == MODE_STATS ? MG_CAP : 1]; // statistics: workers holding a key
-    };
-    uint32_t wofs[65];           // load offset of worker w's window
-    uint32_t take[64], taken[64];
-    uint32_t cur[64], end[64];
-    uint64_t src0[64];
-    uint32_t scan[MG_THREADS / SG_WAVE + 1];
-    uint32_t bcast[4];
-    uint64_t bcast64[2];
-    unsigned long long vmask[MODE == MODE_STATS ? MG_THREADS / SG_WAVE : 1][64];
-    uint32_t ucontig[MODE == MODE_STATS ? 256 : 1], uhashed[MODE == MODE_STATS ? 256 : 1];
+// the lanes' (a, b) worker pair of pair index pi, a <= b, row-major
+__device__ __forceinline__ void pair_of(uint32_t pi, uint32_t n, uint32_t& a, uint32_t& b)
+{
+    uint32_t x = 0, rem = pi;
+    while (rem >= n - x) {
+        rem -= n - x;
+        ++x;
+    }
+    a = x;
+    b = x + rem;
+}
+
+struct WaveSmem {
+    uint32_t bits[MG_WORDS];         // presence bitmap of the window's keys; then keys by rank
+    uint16_t wpre[MG_WORDS];         // distinct keys before a bitmap word; then first slot of a rank
+    unsigned long long mask[MG_WCAP]; // workers holding a rank
+    uint32_t slot[MG_WCAP];          // by (rank, worker): value bits (D == 1) or entry position (rows)
+    uint32_t wofs[65];               // window offset of run w
+    uint32_t untaken[64];            // loaded entries of run w beyond the window's cut
+    uint32_t cut[64];                // run w continues after the window
+    uint64_t src[64];                // absolute position of run w's first loaded entry
+    unsigned long long vm[64];       // statistics: per worker, which of 64 ranks it holds
 };
 
 template <int MODE>
+struct BlockSmem {
+    WaveSmem wv[MG_WAVES];
+    uint32_t part[MODE == MODE_STATS ? 512 : 1];  // statistics: union counts per contiguous / hashed part
+    uint32_t pairs[MODE == MODE_STATS ? 2080 : 1];  // a block's pair counts stay below 2^32 (total does)
+};
+
+// A tile's part of each run, held by lane w < n (positions relative to the
+// run; below 2^32 since total is).
+struct TileRuns {
+    uint64_t rs;    // absolute start of run (g, w)
+    uint32_t cur;   // next entry
+    uint32_t end;   // end of the tile's part
+    uint32_t base;  // aggregate staging: the run's entries before this tile, earlier groups included
+};
+
+// Loads of a tile's run ranges (independent of each other: one round trip).
+__device__ __forceinline__ TileRuns tile_runs(const MergeParams& p, uint32_t t, uint32_t lane)
+{
+    TileRuns r = {0ull, 0u, 0u, 0u};
+    if (lane < p.n && t < p.G * p.NT) {
+        const uint32_t g = t / p.NT, b = t % p.NT;
+        uint64_t s, e;
+        run_range(p, g, lane, s, e);
+        const uint64_t len = e - s;
+        const uint32_t* row = p.bnd + ((uint64_t)g * p.n + lane) * (p.NT + 1);
+        uint64_t x = row[b], y = row[b + 1];
+        if (x > len) x = len;
+        if (y > len) y = len;
+        if (y < x) y = x;
+        r.rs = s;
+        r.cur = (uint32_t)x;
+        r.end = (uint32_t)y;
+        r.base = (uint32_t)(s - p.off[(uint64_t)lane * p.stride] + x);
+    }
+    return r;
+}
+
+// Layout of the next window of a tile (E = the tile's remaining entries): all
+// of them when they fit, else at most MG_WCAP, shared among the runs by water
+// filling (an even share first, then the rest to the runs that still have
+// entries).
+__device__ __forceinline__ uint32_t begin_window(WaveSmem& sm, const TileRuns& r, uint32_t n, uint32_t lane,
+                                                 uint32_t E, uint32_t& take, bool& windowed)
+{
+    const uint32_t rem = r.end - r.cur;
+    windowed = E > (uint32_t)MG_WCAP;
+    if (!windowed) {
+        take = rem;
+    } else {
+        const uint32_t nz = wave_sum(rem > 0 ? 1u : 0u);
+        const uint32_t q1 = (uint32_t)MG_WCAP / nz;
+        take = rem < q1 ? rem : q1;
+        const uint32_t left = (uint32_t)MG_WCAP - wave_sum(take);
+        const uint32_t nb = wave_sum(rem > take ? 1u : 0u);
+        if (left > 0 && nb > 0) {
+            const uint32_t q2 = left / nb, more = rem - take;
+            take += more < q2 ? more : q2;
+        }
+    }
+    const uint32_t incl = wave_incl_scan(take);
+    const uint32_t L = (uint32_t)__builtin_amdgcn_readlane((int)incl, SG_WAVE - 1);
+    if (lane < n) {
+        sm.wofs[lane] = incl - take;
+        sm.src[lane] = r.rs + r.cur;
+        sm.cut[lane] = take > 0 && r.cur + take < r.end; // the run continues after this window
+    }
+    if (lane == 0) sm.wofs[n] = L;
+    wave_sync();
+    return L;
+}
+
+// Issue the window's loads into registers: lane l holds window entries
+// l*MG_PER .. l*MG_PER + MG_PER - 1 (one run search per lane).
+template <int MODE>
+__device__ __forceinline__ void load_window(const MergeParams& p, const WaveSmem& sm, uint32_t L, uint32_t n,
+                                            uint32_t lane, uint32_t (&key)[MG_PER], uint32_t (&wk)[MG_PER],
+                                            uint32_t (&vb)[MG_PER])
+{
+    const uint32_t lp0 = lane * MG_PER;
+    uint32_t lo = 0;
+    if (lp0 < L) {
+        uint32_t hi = n;
+        while (lo + 1 < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (sm.wofs[mid] <= lp0) lo = mid;
+            else hi = mid;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MG_PER; ++i) {
+        const uint32_t lp = lp0 + i;
+        key[i] = 0;
+        wk[i] = 0xffffffffu;
+        vb[i] = 0;
+        if (lp < L) {
+            while (sm.wofs[lo + 1] <= lp) ++lo; // wofs[n] = L > lp ends it
+            const uint64_t pos = sm.src[lo] + (lp - sm.wofs[lo]);
+            key[i] = p.idx[pos];
+            wk[i] = lo;
+            if (MODE == MODE_AGG) {
+                if (p.D == 1)
+                    vb[i] = p.bf16 ? ((uint32_t) static_cast<const uint16_t*>(p.val)[pos] << 16)
+                                   : static_cast<const uint32_t*>(p.val)[pos];
+                else
+                    vb[i] = (uint32_t)pos;
+            }
+        }
+    }
+}
+
+// Once the loads are in (windowed tiles only): the window ends at the
+// smallest last-loaded key of a run that continues; entries above it go back
+// to their runs (counted per run in sm.untaken and dropped here).
+__device__ __forceinline__ void finish_window(WaveSmem& sm, uint32_t n, uint32_t lane, const uint32_t (&key)[MG_PER],
+                                              uint32_t (&wk)[MG_PER])
+{
+    uint32_t cutk = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < MG_PER; ++i) {
+        const uint32_t lp = lane * MG_PER + i;
+        if (wk[i] != 0xffffffffu && sm.cut[wk[i]] && lp + 1 == sm.wofs[wk[i] + 1])
+            cutk = key[i] < cutk ? key[i] : cutk;
+    }
+    const uint32_t kmax = wave_min(cutk);
+    if (lane < n) sm.untaken[lane] = 0;
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < MG_PER; ++i) {
+        if (wk[i] != 0xffffffffu && key[i] > kmax) {
+            atomicAdd(&sm.untaken[wk[i]], 1u);
+            wk[i] = 0xffffffffu;
+        }
+    }
+    wave_sync();
+}
+
+// Work of a wave.  Heavy tiles first, dealt out statically (wave w takes
+// heavy tiles w, w + W, ...: the longest work starts first).  Then the tiles
+// are split into MG_NQ contiguous queues, each with its own ticket counter
+// (no single hot address); a wave starts at queue w mod MG_NQ, takes chunks
+// of MG_CHUNK_TILES tiles, and when its queue runs dry finds an open one with
+// one lane-parallel probe of all counters.
+struct WaveWork {
+    uint32_t hnext;  // next heavy list index
+    uint32_t q;      // current queue
+    uint32_t next, end;
+    bool heavy_phase;
+};
+
+__device__ __forceinline__ uint32_t queue_first(uint32_t q, uint32_t T)
+{
+    return (uint32_t)(((uint64_t)q * T) / MG_NQ);
+}
+
+// Next tile of the wave, or T when none is left.
+__device__ __forceinline__ uint32_t acquire_tile(const MergeParams& p, uint32_t T, uint32_t W, WaveWork& k,
+                                                 bool& from_heavy)
+{
+    if (k.heavy_phase) {
+        if (k.hnext < p.queue[0]) {
+            const uint32_t t = p.heavy[k.hnext];
+            k.hnext += W;
+            from_heavy = true;
+            return t;
+        }
+        k.heavy_phase = false;
+    }
+    from_heavy = false;
+    if (k.next < k.end) return k.next++;
+    while (true) {
+        uint32_t c = 0;
+        if (lane_id() == 0) c = atomicAdd(&p.queue[k.q * MG_QSTRIDE + 1], 1u);
+        c = (uint32_t)__builtin_amdgcn_readfirstlane((int)c);
+        const uint64_t first = (uint64_t)queue_first(k.q, T) + (uint64_t)c * MG_CHUNK_TILES;
+        const uint32_t qend = queue_first(k.q + 1, T);
+        if (first < qend) {
+            k.next = (uint32_t)first;
+            k.end = (uint32_t)(first + MG_CHUNK_TILES < qend ? first + MG_CHUNK_TILES : qend);
+            return k.next++;
+        }
+        // this queue is empty: probe the others (plain loads, one per lane)
+        const uint32_t j = lane_id();
+        bool open = false;
+        uint32_t qq = 0;
+        if (j + 1 < (uint32_t)MG_NQ) {
+            qq = (k.q + 1 + j) % MG_NQ;
+            const uint32_t v = __atomic_load_n(&p.queue[qq * MG_QSTRIDE + 1], __ATOMIC_RELAXED);
+            open = (uint64_t)queue_first(qq, T) + (uint64_t)v * MG_CHUNK_TILES < queue_first(qq + 1, T);
+        }
+        const uint64_t m = ballot(open);
+        if (!m) return T;
+        k.q = (k.q + 1 + (uint32_t)__builtin_ctzll(m)) % MG_NQ;
+    }
+}
+
+// Persistent waves take tiles from the work queue.  Inside a tile the next
+// window's entries are loaded before the current window is merged.
+template <int MODE>
 __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
 {
-    __shared__ UnionSmem<MODE> sm;
+    __shared__ BlockSmem<MODE> bs;
+    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
+    WaveSmem& sm = bs.wv[wid];
     const uint32_t n = p.n;
-    const uint32_t tid = threadIdx.x, wid = tid / SG_WAVE;
-    const uint32_t total_tiles = p.tile_prefix[p.G];
-    // statistics: each lane owns up to 4 worker pairs (a <= b), pair index
-    // pi = lane + 64*i; further pairs (n > 22) go straight to global atomics
-    uint32_t pair_acc[4] = {0, 0, 0, 0};
-    const uint32_t npairs = n * (n + 1) / 2;
+    const uint32_t T = p.G * p.NT;
+    const uint64_t span = 1ull << p.tb;
     uint64_t union_cnt = 0;
-    if (MODE == MODE_STATS)
-        for (uint32_t i = tid; i < 256; i += MG_THREADS) sm.ucontig[i] = sm.uhashed[i] = 0;
+    if (MODE == MODE_STATS) {
+        for (uint32_t i = threadIdx.x; i < 2 * p.Ps; i += MG_THREADS) bs.part[i] = 0;
+        for (uint32_t i = threadIdx.x; i < p.npairs; i += MG_THREADS) bs.pairs[i] = 0;
+        __syncthreads();
+    }
+    const uint32_t W = gridDim.x * MG_WAVES;
+    const uint32_t gwave = blockIdx.x * MG_WAVES + wid;
+    WaveWork work = {gwave, gwave % MG_NQ, 0u, 0u, true};
+    bool from_heavy = false;
+    uint32_t key[MG_PER], wk[MG_PER], vb[MG_PER];
 
     while (true) {
-        if (tid == 0) sm.bcast[0] = atomicAdd(p.ticket, 1u);
-        __syncthreads();
-        const uint32_t t = sm.bcast[0];
-        if (t >= total_tiles) break;
-        const uint32_t g = p.tile_group[t];
-        const uint64_t klo = p.tile_lo[t], khi = p.tile_hi[t];
-        const uint32_t row = t + g;
-        const uint32_t jfirst = p.tile_prefix[g] == t; // first tile of its group
-        if (tid < n) {
-            uint64_t s, e;
-            run_range(p, g, tid, s, e);
-            const uint64_t len = e - s;
-            uint32_t x = p.tile_pos[(uint64_t)row * n + tid], y = p.tile_pos[(uint64_t)(row + 1) * n + tid];
-            if (x > len) x = (uint32_t)len;
-            if (y > len) y = (uint32_t)len;
-            if (y < x) y = x;
-            sm.src0[tid] = s;
-            sm.cur[tid] = x;
-            sm.end[tid] = y;
-        }
-        __syncthreads();
-        uint32_t E = 0;
-        for (uint32_t w = 0; w < n; ++w) E += sm.end[w] - sm.cur[w];
-        const bool single = E <= (uint32_t)MG_CAP;
-        uint64_t span = khi > klo ? khi - klo : 0;
-        if (span > (1ull << MG_SPAN_LOG)) { // the tiler never builds one; keep LDS indices in range
-            report_error(kDevErrPartition);
-            span = 1ull << MG_SPAN_LOG;
-        }
-        const uint32_t win = MG_CAP / n;
-
-        uint64_t X = 0;
-        if (MODE == MODE_AGG && !single) {
-            if (tid < SG_WAVE) {
-                uint64_t x = t == 0 ? 0ull : look_back(p, t);
-                if (tid == 0) sm.bcast64[0] = x;
+        const uint32_t t = acquire_tile(p, T, W, work, from_heavy);
+        if (t >= T) break;
+        TileRuns cr = tile_runs(p, t, lane);
+        uint32_t E = wave_sum(cr.end - cr.cur);
+        if (!from_heavy && E > (uint32_t)MG_HEAVY) continue; // merged in the heavy phase
+        const uint32_t csbase = MODE == MODE_AGG ? wave_sum(cr.base) : 0u;
+        const uint64_t klo = (uint64_t)(t % p.NT) << p.tb;
+        uint32_t produced = 0;
+        if (E == 0) {
+            if (MODE == MODE_AGG && lane == 0) {
+                p.tile_cnt[t] = 0;
+                p.tile_sb[t] = csbase;
             }
-            __syncthreads();
-            X = sm.bcast64[0];
+            continue;
         }
-        uint64_t produced = 0;
-
+        uint32_t take = 0;
+        bool windowed = false;
+        uint32_t L = begin_window(sm, cr, n, lane, E, take, windowed);
+        load_window<MODE>(p, sm, L, n, lane, key, wk, vb);
         while (true) {
-            // window of each worker
-            if (tid == 0) {
-                uint32_t acc = 0;
-                for (uint32_t w = 0; w < n; ++w) {
-                    const uint32_t rem = sm.end[w] - sm.cur[w];
-                    const uint32_t a = single ? rem : (rem < win ? rem : win);
-                    sm.wofs[w] = acc;
-                    sm.take[w] = a;
-                    acc += a;
-                }
-                sm.wofs[n] = acc;
-                sm.bcast[1] = 0xffffffffu; // cut key
+            if (windowed) {
+                finish_window(sm, n, lane, key, wk);
+                if (lane < n) cr.cur += take - sm.untaken[lane];
+            } else {
+                cr.cur += take;
             }
-            if (tid < 64) sm.taken[tid] = 0;
-            for (uint32_t i = tid; i < MG_CWORDS; i += MG_THREADS) sm.coarse[i] = 0;
-            for (uint32_t i = tid; i < MG_CAP; i += MG_THREADS) {
-                sm.fine[i] = 0;
-                if (MODE == MODE_AGG) sm.acc[i] = 0.0f;
-                else sm.mask[i] = 0ull;
-            }
-            __syncthreads();
-            const uint32_t L = sm.wofs[n];
-            if (L == 0 && !single) break; // a single tile runs once, even when empty
-            // smallest last-loaded key of a run whose window does not reach its end
-            if (!single && tid < n) {
-                const uint32_t a = sm.take[tid];
-                if (a > 0 && sm.cur[tid] + a < sm.end[tid])
-                    atomicMin(&sm.bcast[1], p.idx[sm.src0[tid] + sm.cur[tid] + a - 1]);
-            }
-            // entries into registers
-            uint32_t key[MG_PER], wk[MG_PER];
-            float val[MG_PER];
+            uint32_t ck[MG_PER], cw[MG_PER], cv[MG_PER];
 #pragma unroll
             for (int i = 0; i < MG_PER; ++i) {
-                const uint32_t lp = tid + i * MG_THREADS;
-                key[i] = 0xffffffffu;
-                wk[i] = 0xffffffffu;
-                val[i] = 0.0f;
-                if (lp < L) {
-                    uint32_t lo = 0, hi = n;
-                    while (lo + 1 < hi) {
-                        const uint32_t mid = (lo + hi) >> 1;
-                        if (sm.wofs[mid] <= lp) lo = mid;
-                        else hi = mid;
-                    }
-                    const uint64_t pos = sm.src0[lo] + sm.cur[lo] + (lp - sm.wofs[lo]);
-                    key[i] = p.idx[pos];
-                    wk[i] = lo;
-                    if (MODE == MODE_AGG && p.D == 1)
-                        val[i] = p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[pos])
-                                        : static_cast<const float*>(p.val)[pos];
-                }
+                ck[i] = key[i];
+                cw[i] = wk[i];
+                cv[i] = vb[i];
             }
-            __syncthreads();
-            const uint32_t kmax = sm.bcast[1];
-            // take entries up to the cut; coarse presence
+            // issue the tile's next window before merging this one
+            E = wave_sum(cr.end - cr.cur);
+            const bool tile_done = E == 0;
+            if (!tile_done) {
+                L = begin_window(sm, cr, n, lane, E, take, windowed);
+                load_window<MODE>(p, sm, L, n, lane, key, wk, vb);
+            }
+
+            // merge the current window
+#pragma unroll
+            for (int j = 0; j < MG_WPL; ++j) sm.bits[lane * MG_WPL + j] = 0;
+            wave_sync();
             uint32_t off[MG_PER];
 #pragma unroll
             for (int i = 0; i < MG_PER; ++i) {
-                const bool tk = wk[i] != 0xffffffffu && key[i] <= kmax;
-                if (!tk) wk[i] = 0xffffffffu;
                 off[i] = 0;
-                if (tk) {
-                    atomicAdd(&sm.taken[wk[i]], 1u);
-                    const uint64_t o = (uint64_t)key[i] - klo;
-                    if (o < span) {
-                        off[i] = (uint32_t)o;
-                        const uint32_t grp = (uint32_t)(o >> 5);
-                        atomicOr(&sm.coarse[grp >> 5], 1u << (grp & 31u));
-                    } else {
-                        wk[i] = 0xffffffffu; // outside the tile: cannot happen for valid input
-                        report_error(kDevErrIndexRange);
-                    }
+                if (cw[i] == 0xffffffffu) continue;
+                const uint64_t o = (uint64_t)ck[i] - klo;
+                if (ck[i] < klo || o >= span) { // outside the tile: cannot happen for valid input
+                    report_error(kDevErrIndexRange);
+                    cw[i] = 0xffffffffu; // consumed, not counted
+                    continue;
                 }
+                off[i] = (uint32_t)o;
+                atomicOr(&sm.bits[off[i] >> 5], 1u << (off[i] & 31u));
             }
-            __syncthreads();
-            // prefix over coarse words -> index of each non-empty group
-            {
-                constexpr int CW = MG_CWORDS / MG_THREADS;
-                uint32_t c[CW], sum = 0;
-#pragma unroll
-                for (int j = 0; j < CW; ++j) {
-                    c[j] = __popc(sm.coarse[tid * CW + j]);
-                    sum += c[j];
-                }
-                uint32_t F;
-                uint32_t ex = block_excl_scan<MG_THREADS>(sum, sm.scan, &F);
-#pragma unroll
-                for (int j = 0; j < CW; ++j) {
-                    sm.cpre[tid * CW + j] = (uint16_t)ex;
-                    ex += c[j];
-                }
-            }
-            __syncthreads();
-            uint32_t ci[MG_PER];
-#pragma unroll
-            for (int i = 0; i < MG_PER; ++i) {
-                ci[i] = 0;
-                if (wk[i] != 0xffffffffu) {
-                    const uint32_t grp = off[i] >> 5, cw = grp >> 5, cb = grp & 31u;
-                    ci[i] = sm.cpre[cw] + __popc(sm.coarse[cw] & ((1u << cb) - 1u));
-                    atomicOr(&sm.fine[ci[i]], 1u << (off[i] & 31u));
-                }
-            }
-            __syncthreads();
-            // prefix over fine words -> rank of each distinct key
+            wave_sync();
+            // prefix popcounts over the bitmap -> ranks
             uint32_t U;
             {
-                uint32_t c[MG_PER], sum = 0;
+                uint32_t c[MG_WPL], sum = 0;
 #pragma unroll
-                for (int j = 0; j < MG_PER; ++j) {
-                    c[j] = __popc(sm.fine[tid * MG_PER + j]);
+                for (int j = 0; j < MG_WPL; ++j) {
+                    c[j] = __popc(sm.bits[lane * MG_WPL + j]);
                     sum += c[j];
                 }
-                uint32_t ex = block_excl_scan<MG_THREADS>(sum, sm.scan, &U);
+                const uint32_t inc = wave_incl_scan(sum);
+                U = (uint32_t)__builtin_amdgcn_readlane((int)inc, SG_WAVE - 1);
+                uint32_t ex = inc - sum;
 #pragma unroll
-                for (int j = 0; j < MG_PER; ++j) {
-                    sm.fpre[tid * MG_PER + j] = (uint16_t)ex;
+                for (int j = 0; j < MG_WPL; ++j) {
+                    sm.wpre[lane * MG_WPL + j] = (uint16_t)ex;
                     ex += c[j];
                 }
             }
-            // the unique count is known: let successors use it right away
-            if (MODE == MODE_AGG && single && tid == 0)
-                store_agent(p.status + t, (t == 0 ? MG_FLAG_INC : MG_FLAG_AGG) | U);
-            __syncthreads();
+            wave_sync();
             uint32_t rk[MG_PER];
 #pragma unroll
             for (int i = 0; i < MG_PER; ++i) {
                 rk[i] = 0;
-                if (wk[i] != 0xffffffffu)
-                    rk[i] = sm.fpre[ci[i]] + __popc(sm.fine[ci[i]] & ((1u << (off[i] & 31u)) - 1u));
+                if (cw[i] != 0xffffffffu)
+                    rk[i] = sm.wpre[off[i] >> 5] + __popc(sm.bits[off[i] >> 5] & ((1u << (off[i] & 31u)) - 1u));
             }
-            __syncthreads();
-            // distinct keys by rank (every holder of a key writes the same value)
+            for (uint32_t r = lane; r < U; r += SG_WAVE) sm.mask[r] = 0ull;
+            wave_sync();
+            // keys by rank (every holder writes the same key), holders by rank
 #pragma unroll
             for (int i = 0; i < MG_PER; ++i) {
-                if (wk[i] == 0xffffffffu) continue;
-                sm.fine[rk[i]] = key[i];
-                if (MODE == MODE_STATS) atomicOr(&sm.mask[rk[i]], 1ull << wk[i]);
-                if (MODE == MODE_AGG && p.D > 1) sm.ekey[tid + i * MG_THREADS] = key[i];
+                if (cw[i] == 0xffffffffu) continue;
+                sm.bits[rk[i]] = ck[i];
+                atomicOr(&sm.mask[rk[i]], 1ull << cw[i]);
             }
-            __syncthreads();
-            if (MODE == MODE_AGG && p.D == 1) {
-                // sums in worker order: worker w's entries have distinct keys,
-                // so one worker at a time needs no atomics
-                for (uint32_t w = 0; w < n; ++w) {
-                    if (sm.taken[w] == 0) continue;
-#pragma unroll
-                    for (int i = 0; i < MG_PER; ++i)
-                        if (wk[i] == w) sm.acc[rk[i]] += val[i];
-                    __syncthreads();
-                }
-            }
-
+            wave_sync();
             if (MODE == MODE_AGG) {
-                if (single) {
-                    if (tid < SG_WAVE) {
-                        uint64_t x = t == 0 ? 0ull : look_back(p, t);
-                        if (tid == 0) {
-                            if (t != 0) store_agent(p.status + t, MG_FLAG_INC | (x + U));
-                            sm.bcast64[0] = x;
-                        }
+                // first slot of each rank: exclusive prefix of the holder counts
+                {
+                    constexpr int RPL = MG_WCAP / SG_WAVE;
+                    uint32_t c[RPL], sum = 0;
+#pragma unroll
+                    for (int j = 0; j < RPL; ++j) {
+                        const uint32_t r = lane * RPL + j;
+                        c[j] = r < U ? popc64(sm.mask[r]) : 0u;
+                        sum += c[j];
                     }
-                    __syncthreads();
-                    X = sm.bcast64[0];
+                    const uint32_t inc = wave_incl_scan(sum);
+                    uint32_t ex = inc - sum;
+#pragma unroll
+                    for (int j = 0; j < RPL; ++j) {
+                        sm.wpre[lane * RPL + j] = (uint16_t)ex;
+                        ex += c[j];
+                    }
                 }
-                const uint64_t ob = X + produced;
-                if (p.D <= 1) {
-                    for (uint32_t q = tid; q < U; q += MG_THREADS) {
-                        const uint64_t dst = ob + q;
-                        if (dst >= p.capacity) continue;
-                        p.agg_idx[dst] = sm.fine[q];
-                        if (p.D == 1) p.agg_val[dst] = sm.acc[q];
+                wave_sync();
+#pragma unroll
+                for (int i = 0; i < MG_PER; ++i) {
+                    if (cw[i] == 0xffffffffu) continue;
+                    const uint32_t s = sm.wpre[rk[i]] + popc64(sm.mask[rk[i]] & ((1ull << cw[i]) - 1ull));
+                    sm.slot[s] = cv[i];
+                }
+                wave_sync();
+                const uint64_t ob = (uint64_t)csbase + produced;
+                if (p.D == 1) {
+                    for (uint32_t r = lane; r < U; r += SG_WAVE) {
+                        const uint32_t s0 = sm.wpre[r], c = popc64(sm.mask[r]);
+                        float acc = 0.0f;
+                        for (uint32_t j = 0; j < c; ++j) acc += __uint_as_float(sm.slot[s0 + j]);
+                        if (ob + r >= p.total) break; // only for inconsistent offsets
+                        p.stage_idx[ob + r] = sm.bits[r];
+                        p.stage_val[ob + r] = acc;
+                    }
+                } else if (p.D > 1) {
+                    // rows: one rank at a time, lanes across the row
+                    for (uint32_t r = 0; r < U && ob + r < p.total; ++r) {
+                        const uint32_t s0 = sm.wpre[r], c = popc64(sm.mask[r]);
+                        if (lane == 0) p.stage_idx[ob + r] = sm.bits[r];
+                        for (uint32_t c0 = 0; c0 < p.D; c0 += SG_WAVE) {
+                            const uint32_t col = c0 + lane;
+                            if (col >= p.D) break;
+                            float acc = 0.0f;
+                            for (uint32_t j = 0; j < c; ++j) {
+                                const uint64_t vi = (uint64_t)sm.slot[s0 + j] * p.D + col;
+                                acc += p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[vi])
+                                              : static_cast<const float*>(p.val)[vi];
+                            }
+                            p.stage_val[(ob + r) * p.D + col] = acc;
+                        }
                     }
                 } else {
-                    // rows: one wave per distinct key, lanes across the row;
-                    // each worker's entry is found by binary search in its window
-                    for (uint32_t q = wid; q < U; q += MG_THREADS / SG_WAVE) {
-                        const uint32_t k = sm.fine[q];
-                        const uint64_t dst = ob + q;
-                        if (dst >= p.capacity) continue;
-                        if (lane_id() == 0) p.agg_idx[dst] = k;
-                        for (uint32_t c0 = 0; c0 < p.D; c0 += SG_WAVE) {
-                            const uint32_t c = c0 + lane_id();
-                            float acc = 0.0f;
-                            for (uint32_t w = 0; w < n; ++w) {
-                                uint32_t lo = sm.wofs[w], hi = sm.wofs[w] + sm.taken[w];
-                                while (lo < hi) {
-                                    const uint32_t mid = (lo + hi) >> 1;
-                                    if (sm.ekey[mid] < k) lo = mid + 1;
-                                    else hi = mid;
-                                }
-                                if (lo < sm.wofs[w] + sm.taken[w] && sm.ekey[lo] == k && c < p.D) {
-                                    const uint64_t pos = sm.src0[w] + sm.cur[w] + (lo - sm.wofs[w]);
-                                    const uint64_t vi = pos * p.D + c;
-                                    acc += p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[vi])
-                                                  : static_cast<const float*>(p.val)[vi];
-                                }
-                            }
-                            if (c < p.D) p.agg_val[dst * p.D + c] = acc;
-                        }
-                    }
+                    for (uint32_t r = lane; r < U && ob + r < p.total; r += SG_WAVE) p.stage_idx[ob + r] = sm.bits[r];
+                }
+                if (tile_done && lane == 0) {
+                    p.tile_cnt[t] = produced + U;
+                    p.tile_sb[t] = csbase;
                 }
             } else {
-                // statistics: pairwise intersections from per-key worker masks
-                for (uint32_t q0 = wid * SG_WAVE; q0 < U; q0 += MG_THREADS) {
-                    const uint32_t q = q0 + lane_id();
+                // statistics: union part counts and pairwise intersections
+                for (uint32_t q0 = 0; q0 < U; q0 += SG_WAVE) {
+                    const uint32_t q = q0 + lane;
                     unsigned long long m = 0;
                     if (q < U) {
-                        const uint32_t k = sm.fine[q];
+                        const uint32_t k = sm.bits[q];
                         m = sm.mask[q];
-                        atomicAdd(&sm.ucontig[contig_part(k, p.M, p.Ps)], 1u);
-                        if (p.hashed) atomicAdd(&sm.uhashed[h0(k, p.seed, p.div)], 1u);
+                        atomicAdd(&bs.part[contig_part(k, p.M, p.Ps, p.inv_m)], 1u);
+                        if (p.hashed) atomicAdd(&bs.part[p.Ps + h0(k, p.seed, p.div)], 1u);
                     }
                     for (uint32_t a = 0; a < n; ++a) {
                         const uint64_t v = ballot((m >> a) & 1ull);
-                        if (lane_id() == 0) sm.vmask[wid][a] = v;
+                        if (lane == 0) sm.vm[a] = v;
                     }
-                    for (uint32_t i = 0, pi = lane_id(); pi < npairs; ++i, pi += SG_WAVE) {
-                        uint32_t a = 0, rem = pi;
-                        while (rem >= n - a) {
-                            rem -= n - a;
-                            ++a;
-                        }
-                        const uint32_t b = a + rem;
-                        const uint32_t c = popc64(sm.vmask[wid][a] & sm.vmask[wid][b]);
-                        if (i < 4) pair_acc[i] += c;
-                        else if (c) atomicAdd((unsigned long long*)&p.st_inter[a * n + b], (unsigned long long)c);
+                    wave_sync();
+                    for (uint32_t pi = lane; pi < p.npairs; pi += SG_WAVE) {
+                        uint32_t a, bb;
+                        pair_of(pi, n, a, bb);
+                        const uint32_t c = popc64(sm.vm[a] & sm.vm[bb]);
+                        if (c) atomicAdd(&bs.pairs[pi], c);
                     }
+                    wave_sync();
                 }
                 union_cnt += U;
             }
             produced += U;
-            __syncthreads();
-            if (tid < n) sm.cur[tid] += sm.taken[tid];
-            __syncthreads();
-            if (single) break;
+            wave_sync();
+            if (tile_done) break;
         }
-        if (MODE == MODE_AGG && tid == 0) {
-            if (!single) store_agent(p.status + t, MG_FLAG_INC | (X + produced));
-            if (t == total_tiles - 1) p.agg_off[p.G] = X + produced;
-            if (jfirst) p.agg_off[g] = X;
-        }
-        __syncthreads();
     }
     if (MODE == MODE_STATS) {
         __syncthreads();
-        for (uint32_t i = 0, pi = lane_id(); i < 4 && pi < npairs; ++i, pi += SG_WAVE) {
-            if (!pair_acc[i]) continue;
-            uint32_t a = 0, rem = pi;
-            while (rem >= n - a) {
-                rem -= n - a;
-                ++a;
-            }
-            const uint32_t b = a + rem;
-            atomicAdd((unsigned long long*)&p.st_inter[a * n + b], (unsigned long long)pair_acc[i]);
+        uint64_t* row = p.st_part + (uint64_t)blockIdx.x * p.st_row;
+        for (uint32_t i = threadIdx.x; i < p.npairs; i += MG_THREADS) row[i] = bs.pairs[i];
+        for (uint32_t i = threadIdx.x; i < 2 * p.Ps; i += MG_THREADS) row[p.npairs + 1 + i] = bs.part[i];
+        // union count: per-wave totals summed in LDS
+        __syncthreads();
+        if (lane == 0) bs.wv[wid].src[0] = union_cnt;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t u = 0;
+            for (int i = 0; i < MG_WAVES; ++i) u += bs.wv[i].src[0];
+            row[p.npairs] = u;
         }
-        for (uint32_t i = tid; i < p.Ps; i += MG_THREADS) {
-            if (sm.ucontig[i]) atomicAdd((unsigned long long*)&p.st_ucontig[i], (unsigned long long)sm.ucontig[i]);
-            if (p.hashed && sm.uhashed[i])
-                atomicAdd((unsigned long long*)&p.st_uhashed[i], (unsigned long long)sm.uhashed[i]);
-        }
-        if (tid == 0 && union_cnt) atomicAdd((unsigned long long*)p.st_union, (unsigned long long)union_cnt);
+    }
+}
+
+// statistics: sum the blocks' partial rows, one block per word
+__global__ __launch_bounds__(256) void mg_stats_reduce_kernel(MergeParams p, uint32_t rows, uint64_t* out)
+{
+    __shared__ uint64_t red[256 / SG_WAVE];
+    const uint32_t i = blockIdx.x;
+    uint64_t s = 0;
+    for (uint32_t r = threadIdx.x; r < rows; r += 256) s += p.st_part[(uint64_t)r * p.st_row + i];
+#pragma unroll
+    for (int d = SG_WAVE / 2; d > 0; d >>= 1) s += __shfl_xor(s, d, SG_WAVE);
+    if (lane_id() == 0) red[threadIdx.x / SG_WAVE] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int w = 0; w < 256 / SG_WAVE; ++w) t += red[w];
+        out[i] = t;
+    }
+}
+
+// aggregate placement: exclusive prefix of tile counts inside each scan block
+__global__ __launch_bounds__(1024) void mg_scan_local_kernel(MergeParams p)
+{
+    __shared__ uint64_t scan_lds[1024 / SG_WAVE + 1];
+    const uint32_t T = p.G * p.NT;
+    const uint64_t t0 = (uint64_t)blockIdx.x * MG_SCAN_BLOCK + (uint64_t)threadIdx.x * MG_SCAN_PER;
+    uint32_t c[MG_SCAN_PER];
+    uint64_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < MG_SCAN_PER; ++j) {
+        c[j] = t0 + j < T ? p.tile_cnt[t0 + j] : 0u;
+        sum += c[j];
+    }
+    uint64_t tot;
+    uint64_t ex = block_excl_scan64<1024>(sum, scan_lds, &tot);
+#pragma unroll
+    for (int j = 0; j < MG_SCAN_PER; ++j) {
+        if (t0 + j < T) p.tile_out[t0 + j] = ex;
+        ex += c[j];
+    }
+    if (threadIdx.x == 0) p.blk_sum[blockIdx.x] = tot;
+}
+
+// exclusive prefix of the scan blocks' totals (in place); agg_off[G]
+__global__ __launch_bounds__(1024) void mg_scan_top_kernel(MergeParams p)
+{
+    __shared__ uint64_t scan_lds[1024 / SG_WAVE + 1];
+    uint64_t carry = 0;
+    for (uint32_t base = 0; base < p.nscan; base += 1024) {
+        const uint32_t i = base + threadIdx.x;
+        const uint64_t v = i < p.nscan ? p.blk_sum[i] : 0ull;
+        uint64_t tot;
+        const uint64_t ex = block_excl_scan64<1024>(v, scan_lds, &tot);
+        if (i < p.nscan) p.blk_sum[i] = carry + ex;
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) p.agg_off[p.G] = carry;
+}
+
+// one wave per tile: staged entries to their final offsets
+__global__ __launch_bounds__(256) void mg_place_kernel(MergeParams p)
+{
+    const uint32_t T = p.G * p.NT;
+    const uint32_t t = blockIdx.x * 4 + threadIdx.x / SG_WAVE;
+    if (t >= T) return;
+    const uint32_t lane = lane_id();
+    const uint64_t ob = p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK];
+    if (t % p.NT == 0 && lane == 0) p.agg_off[t / p.NT] = ob;
+    const uint32_t c = p.tile_cnt[t];
+    const uint64_t sb = p.tile_sb[t];
+    if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
+        if (lane == 0) report_error(kDevErrPartition);
+        return;
+    }
+    for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_idx[ob + i] = p.stage_idx[sb + i];
+    if (p.D == 1) {
+        for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_val[ob + i] = p.stage_val[sb + i];
+    } else if (p.D > 1) {
+        const uint64_t cnt = (uint64_t)c * p.D;
+        for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[ob * p.D + i] = p.stage_val[sb * p.D + i];
     }
 }
 

@@ -5,18 +5,17 @@
 // The union and every pairwise intersection come from the merge engine run
 // over the workers' lists (one group): per union index the set of workers
 // holding it is a 64-bit mask; per 64 indices a wave turns the masks into one
-// ballot word per worker and adds popcount(V_a & V_b) for each pair.  Per-part
-// counts of each worker come from one pass over the entries.  The host then
-// evaluates the definitions in double with fixed expressions.
+// ballot word per worker and adds popcount(V_a & V_b) for each pair.  Blocks
+// keep their counts in LDS and write one partial row each; a last pass sums
+// the rows.  Per-part counts of each worker come from one pass over the
+// entries.  The host then evaluates the definitions in double with fixed
+// expressions.
 #include "sg_host.h"
 
 namespace sg {
 
 struct StatsCounts {
-    uint64_t* inter;    // [n*n] (a <= b filled)
-    uint64_t* uni;      // [1]
-    uint64_t* ucontig;  // [Ps]
-    uint64_t* uhashed;  // [Ps]
+    uint64_t* row;      // [npairs + 1 + 2*Ps]: pair counts (a <= b, row-major), union, union per part
     uint64_t* wcontig;  // [n*Ps]
     uint64_t* whashed;  // [n*Ps]
 };
@@ -43,7 +42,7 @@ __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, S
     const uint64_t j0 = (uint64_t)(ch - p.chunk_start[w]) * MG_CHUNK;
     for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && s + j < e; j += MG_THREADS) {
         const uint32_t key = p.idx[s + j];
-        atomicAdd(&hc[contig_part(key, p.M, p.Ps)], 1u);
+        atomicAdd(&hc[contig_part(key, p.M, p.Ps, p.inv_m)], 1u);
         if (p.hashed) atomicAdd(&hh[h0(key, p.seed, p.div)], 1u);
     }
     __syncthreads();
@@ -57,7 +56,7 @@ __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, S
 
 using namespace sg;
 
-static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total)
+static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, uint32_t P)
 {
     *p = MergeParams();
     p->n = n;
@@ -65,17 +64,18 @@ static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total)
     p->stride = 1;
     p->M = M;
     p->total = total;
-    choose_buckets(n, 1, M, total, &p->bs, &p->NB);
+    p->Ps = P;
+    p->inv_m = 1.0 / (double)M;
+    p->npairs = n * (n + 1) / 2;
+    p->st_row = p->npairs + 1 + 2 * P;
+    choose_tiles(1, M, total, &p->tb, &p->NT);
 }
 
 static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k)
 {
     const uint32_t n = p->n;
-    merge_carve(c, p);
-    k->inter = c.take<uint64_t>((uint64_t)n * n);
-    k->uni = c.take<uint64_t>(1);
-    k->ucontig = c.take<uint64_t>(P);
-    k->uhashed = c.take<uint64_t>(P);
+    merge_carve(c, p, MODE_STATS);
+    k->row = c.take<uint64_t>(p->st_row);
     k->wcontig = c.take<uint64_t>((uint64_t)n * P);
     k->whashed = c.take<uint64_t>((uint64_t)n * P);
     return c.bytes();
@@ -85,7 +85,7 @@ extern "C" size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t tota
 {
     if (n == 0 || P == 0) return 256;
     MergeParams p;
-    stats_setup(&p, n, M, total);
+    stats_setup(&p, n, M, total, P);
     Carver c(nullptr);
     StatsCounts k;
     return stats_carve(c, &p, P, &k);
@@ -131,39 +131,37 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     }
 
     MergeParams p;
-    stats_setup(&p, n, M, total);
+    stats_setup(&p, n, M, total, P);
     Carver c(d_ws);
     StatsCounts k;
     stats_carve(c, &p, P, &k);
     p.idx = d_idx;
     p.off = d_in_off;
-    p.Ps = P;
     p.seed = seed;
     p.hashed = d_cmap != nullptr;
     p.div = make_divider(P);
-    p.st_inter = k.inter;
-    p.st_union = k.uni;
-    p.st_ucontig = k.ucontig;
-    p.st_uhashed = k.uhashed;
-    // counters live contiguously after the merge workspace: zero them at once
-    const uint64_t cnt_words = (uint64_t)((char*)(k.whashed + (uint64_t)n * P) - (char*)k.inter) / 8;
-    int rc = fill_u64(k.inter, cnt_words, 0, st);
+    // per-worker part counters are accumulated with atomics: zero them
+    int rc = fill_u64(k.wcontig, (uint64_t)n * P, 0, st);
     if (rc) return rc;
-    rc = merge_run(p, MODE_STATS, st);
+    rc = fill_u64(k.whashed, (uint64_t)n * P, 0, st);
+    if (rc) return rc;
+    rc = merge_run(p, MODE_STATS, st, k.row);
     if (rc) return rc;
     st_entries_kernel<<<(unsigned)(ceil_div(total, MG_CHUNK) + n), MG_THREADS, 0, st>>>(p, k);
     SG_TRY_LAUNCH();
 
-    std::vector<uint64_t> inter((size_t)n * n), wc((size_t)n * P), wh((size_t)n * P), uc(P), uh(P), off(n + 1);
-    uint64_t uni = 0;
-    SG_TRY(hipMemcpyAsync(inter.data(), k.inter, 8ull * n * n, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(&uni, k.uni, 8, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(uc.data(), k.ucontig, 8ull * P, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(uh.data(), k.uhashed, 8ull * P, hipMemcpyDeviceToHost, st));
+    std::vector<uint64_t> row(p.st_row), wc((size_t)n * P), wh((size_t)n * P), off(n + 1);
+    std::vector<uint64_t> inter((size_t)n * n, 0);
+    SG_TRY(hipMemcpyAsync(row.data(), k.row, 8ull * p.st_row, hipMemcpyDeviceToHost, st));
     SG_TRY(hipMemcpyAsync(wc.data(), k.wcontig, 8ull * n * P, hipMemcpyDeviceToHost, st));
     SG_TRY(hipMemcpyAsync(wh.data(), k.whashed, 8ull * n * P, hipMemcpyDeviceToHost, st));
     SG_TRY(hipMemcpyAsync(off.data(), d_in_off, 8ull * (n + 1), hipMemcpyDeviceToHost, st));
     SG_TRY(hipStreamSynchronize(st));
+    for (uint32_t a = 0, pi = 0; a < n; ++a)
+        for (uint32_t b = a; b < n; ++b, ++pi) inter[(size_t)a * n + b] = row[pi];
+    const uint64_t uni = row[p.npairs];
+    const uint64_t* uc = &row[p.npairs + 1];
+    const uint64_t* uh = &row[p.npairs + 1 + P];
 
     // exact counts
     o->sum_nnz = 0;
@@ -206,7 +204,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
         o->skew_contig[a] = skew_of(&wc[(size_t)a * P], g.data(), P, M, o->nnz[a]);
     }
     for (uint32_t i = 0; i < P; ++i) o->contig_counts[(uint64_t)n * P + i] = uc[i];
-    o->skew_contig[n] = skew_of(uc.data(), g.data(), P, M, o->union_size);
+    o->skew_contig[n] = skew_of(uc, g.data(), P, M, o->union_size);
     // hash classes and Def. 8
     o->push_imbalance = 0.0;
     o->pull_imbalance = 0.0;
@@ -217,7 +215,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
             o->skew_hashed[a] = skew_of(&wh[(size_t)a * P], class_size.data(), P, M, o->nnz[a]);
         }
         for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)n * P + i] = uh[i];
-        o->skew_hashed[n] = skew_of(uh.data(), class_size.data(), P, M, o->union_size);
+        o->skew_hashed[n] = skew_of(uh, class_size.data(), P, M, o->union_size);
         for (uint32_t a = 0; a < n; ++a) {
             if (o->nnz[a] == 0) continue;
             for (uint32_t i = 0; i < P; ++i) {

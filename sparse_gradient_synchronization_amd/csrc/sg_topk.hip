@@ -31,7 +31,8 @@ constexpr int TK_TILE = 1024;      // elements per filter tile (one wave)
 constexpr int TK_SAMPLES = 16384;
 constexpr int TK_DIGIT_BITS = 11;
 constexpr int TK_BINS = 1 << TK_DIGIT_BITS;
-constexpr int TK_HIST_GROUP = 512; // tiles per histogram block
+constexpr int TK_GROUP = 64;       // tiles per wave in the select and write passes (one per lane)
+constexpr int TK_HIST_GROUPS = 2;  // tile groups per wave in a histogram block
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,10 +59,12 @@ struct TopkParams {
     uint32_t* slot_key;    // [n*NT*TILE] candidate keys
     uint32_t* hist;        // [n][TK_BINS]
     uint32_t* samples;     // [n][TK_SAMPLES]
-    uint32_t* gtx;         // [n*NT] exclusive prefix of entries > T
-    uint32_t* eqx;         // [n*NT] exclusive prefix of entries == T
+    uint32_t* gtx;         // [n*NT] entries > T of a tile
+    uint32_t* eqx;         // [n*NT] entries == T of a tile
+    uint32_t* ggt;         // [n*NG] per tile group: entries > T, then their exclusive prefix
+    uint32_t* geq;         // [n*NG] per tile group: entries == T, then their exclusive prefix
     uint64_t M, k;
-    uint32_t n, NT;
+    uint32_t n, NT, NG;
     uint32_t keymax;       // 0x7fffffff (fp32) or 0x7fff (bf16)
     int bf16;
 };
@@ -364,31 +367,55 @@ __device__ __forceinline__ void digit_window(uint32_t top, uint32_t& shift, uint
     width = top - shift;
 }
 
+// digit of a candidate key for the current pass, or TK_BINS when its
+// higher digits differ from the prefix chosen so far
+__device__ __forceinline__ uint32_t cand_digit(const SelState& st, uint32_t key, uint32_t shift, uint32_t width)
+{
+    const uint32_t r = key - st.lo;
+    const uint32_t hi_part = st.top >= 32 ? 0u : (r >> st.top);
+    const uint32_t pre_part = st.top >= 32 ? 0u : (st.prefix >> st.top);
+    return hi_part != pre_part ? (uint32_t)TK_BINS : (r >> shift) & ((1u << width) - 1u);
+}
+
+// Histogram of the current digit over the candidates.  A wave takes groups
+// of 64 tiles (the tile counts in one load, one lane per tile) and loads the
+// candidates of 16 tiles at a time, so the loads overlap.
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
 {
     __shared__ uint32_t h[TK_BINS];
-    const uint32_t groups = (p.NT + TK_HIST_GROUP - 1) / TK_HIST_GROUP;
-    const uint32_t w = blockIdx.x / groups, gi = blockIdx.x % groups;
+    constexpr uint32_t GPB = (TK_THREADS / SG_WAVE) * TK_HIST_GROUPS; // groups per block
+    const uint32_t bpw = (p.NG + GPB - 1) / GPB;
+    const uint32_t w = blockIdx.x / bpw, bi = blockIdx.x % bpw;
     const SelState st = p.st[w];
     if (st.R == 0 || st.top == 0) return;
     uint32_t shift, width;
     digit_window(st.top, shift, width);
     for (uint32_t i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0;
     __syncthreads();
-    const uint32_t t0 = gi * TK_HIST_GROUP;
-    const uint32_t t1 = t0 + TK_HIST_GROUP < p.NT ? t0 + TK_HIST_GROUP : p.NT;
-    const uint32_t wid = threadIdx.x / SG_WAVE;
-    for (uint32_t t = t0 + wid; t < t1; t += TK_THREADS / SG_WAVE) {
-        const uint64_t g = (uint64_t)w * p.NT + t;
-        const uint32_t c = p.ccnt[g];
-        const uint32_t* keys = p.slot_key + g * TK_TILE;
-        for (uint32_t i = lane_id(); i < c; i += SG_WAVE) {
-            uint32_t r = keys[i] - st.lo;
-            uint32_t hi_part = st.top >= 32 ? 0u : (r >> st.top);
-            uint32_t pre_part = st.top >= 32 ? 0u : (st.prefix >> st.top);
-            if (hi_part != pre_part) continue;
-            uint32_t d = (r >> shift) & ((1u << width) - 1u);
-            atomicAdd(&h[d], 1u);
+    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
+    for (uint32_t q = 0; q < (uint32_t)TK_HIST_GROUPS; ++q) {
+        const uint32_t grp = (bi * (TK_THREADS / SG_WAVE) + wid) * TK_HIST_GROUPS + q;
+        if (grp >= p.NG) break;
+        const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
+        const uint32_t c = grp * TK_GROUP + lane < p.NT ? p.ccnt[g0 + lane] : 0u;
+        for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 16) {
+            uint32_t kk[16], cj[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
+                kk[u] = lane < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + lane] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (lane < cj[u]) {
+                    const uint32_t d = cand_digit(st, kk[u], shift, width);
+                    if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                }
+                for (uint32_t i = SG_WAVE + lane; i < cj[u]; i += SG_WAVE) { // tiles with more than 64 candidates
+                    const uint32_t d = cand_digit(st, p.slot_key[(g0 + j0 + u) * TK_TILE + i], shift, width);
+                    if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                }
+            }
         }
     }
     __syncthreads();
@@ -459,45 +486,70 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pick_kernel(TopkParams p)
 // --------------------------------------------------------------------------
 // 5. counts per tile, per-worker scan, ordered write
 // --------------------------------------------------------------------------
+// One wave per group of 64 tiles: per tile, entries above T (the sure ones
+// and the candidates above T) and equal to T; per group, their sums.
 __global__ __launch_bounds__(TK_THREADS) void topk_tilecount_kernel(TopkParams p)
 {
-    const uint64_t g = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
-    if (g >= (uint64_t)p.n * p.NT) return;
-    const uint32_t w = (uint32_t)(g / p.NT);
+    const uint64_t gw = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
+    if (gw >= (uint64_t)p.n * p.NG) return;
+    const uint32_t lane = lane_id();
+    const uint32_t w = (uint32_t)(gw / p.NG), grp = (uint32_t)(gw % p.NG);
     const uint32_t T = p.st[w].T;
-    const uint32_t c = p.ccnt[g];
-    const uint32_t* keys = p.slot_key + g * TK_TILE;
-    uint32_t gt = 0, eq = 0;
-    for (uint32_t i = lane_id(); i < c; i += SG_WAVE) {
-        uint32_t key = keys[i];
-        gt += key > T;
-        eq += key == T;
+    const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
+    const bool valid = grp * TK_GROUP + lane < p.NT;
+    const uint32_t c = valid ? p.ccnt[g0 + lane] : 0u;
+    uint32_t my_gt = valid ? p.tcnt[g0 + lane] - c : 0u, my_eq = 0;
+    for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 8) {
+        uint32_t kk[8], cj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
+            kk[u] = lane < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + lane] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            uint32_t gt = popc64(ballot(lane < cj[u] && kk[u] > T));
+            uint32_t eq = popc64(ballot(lane < cj[u] && kk[u] == T));
+            for (uint32_t i0 = SG_WAVE; i0 < cj[u]; i0 += SG_WAVE) { // tiles with more than 64 candidates
+                const uint32_t i = i0 + lane;
+                const uint32_t key = i < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + i] : 0u;
+                gt += popc64(ballot(i < cj[u] && key > T));
+                eq += popc64(ballot(i < cj[u] && key == T));
+            }
+            if (lane == j0 + u) {
+                my_gt += gt;
+                my_eq = eq;
+            }
+        }
     }
-    gt = wave_sum(gt);
-    eq = wave_sum(eq);
-    if (lane_id() == 0) {
-        p.gtx[g] = p.tcnt[g] - c + gt; // sure entries are all above T
-        p.eqx[g] = eq;
+    if (valid) {
+        p.gtx[g0 + lane] = my_gt;
+        p.eqx[g0 + lane] = my_eq;
+    }
+    const uint32_t sg = wave_sum(my_gt), se = wave_sum(my_eq);
+    if (lane == 0) {
+        p.ggt[gw] = sg;
+        p.geq[gw] = se;
     }
 }
 
-// Per-worker exclusive scans of the per-tile counts; each thread takes 8
-// consecutive tiles per round.
+// Per-worker exclusive scans of the group sums (in place); each thread takes
+// 8 consecutive groups per round.
 __global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
 {
     constexpr uint32_t PT = 8;
     __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
     const uint32_t w = blockIdx.x;
     uint32_t carry_gt = 0, carry_eq = 0;
-    for (uint32_t base = 0; base < p.NT; base += 1024 * PT) {
+    for (uint32_t base = 0; base < p.NG; base += 1024 * PT) {
         const uint32_t t0 = base + threadIdx.x * PT;
-        const uint64_t g0 = (uint64_t)w * p.NT + t0;
+        const uint64_t g0 = (uint64_t)w * p.NG + t0;
         uint32_t a[PT], b[PT], sa = 0, sb = 0;
 #pragma unroll
         for (uint32_t j = 0; j < PT; ++j) {
-            const bool in = t0 + j < p.NT;
-            a[j] = in ? p.gtx[g0 + j] : 0u;
-            b[j] = in ? p.eqx[g0 + j] : 0u;
+            const bool in = t0 + j < p.NG;
+            a[j] = in ? p.ggt[g0 + j] : 0u;
+            b[j] = in ? p.geq[g0 + j] : 0u;
             sa += a[j];
             sb += b[j];
         }
@@ -509,9 +561,9 @@ __global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
         xb += carry_eq;
 #pragma unroll
         for (uint32_t j = 0; j < PT; ++j) {
-            if (t0 + j < p.NT) {
-                p.gtx[g0 + j] = xa;
-                p.eqx[g0 + j] = xb;
+            if (t0 + j < p.NG) {
+                p.ggt[g0 + j] = xa;
+                p.geq[g0 + j] = xb;
             }
             xa += a[j];
             xb += b[j];
@@ -522,40 +574,88 @@ __global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
     }
 }
 
-// one wave per tile: ordered compaction of the tile slot by (key > T) or
-// (key == T and its equal-rank < need)
+// Ordered compaction of one chunk of up to 64 slot entries: entries above T,
+// and entries equal to T while fewer than `need` equal ones precede them.
+__device__ __forceinline__ void write_chunk(const TopkParams& p, uint32_t valid_n, uint32_t bits, uint32_t ix,
+                                            uint32_t T, uint32_t need, uint64_t obase, uint64_t& pos, uint32_t& eqr)
+{
+    const uint32_t lane = lane_id();
+    const bool valid = lane < valid_n;
+    const uint32_t key = key_of_bits(bits, p.bf16);
+    const bool eq = valid && key == T;
+    const uint64_t meq = ballot(eq);
+    const uint32_t my_eq = eqr + popc64(meq & lanemask_lt());
+    const bool sel = valid && (key > T || (eq && my_eq < need));
+    const uint64_t ms = ballot(sel);
+    if (sel) {
+        const uint64_t o = pos + popc64(ms & lanemask_lt());
+        if (o < p.k) {
+            p.out_idx[obase + o] = ix;
+            if (p.bf16) static_cast<uint16_t*>(p.out_val)[obase + o] = (uint16_t)bits;
+            else static_cast<uint32_t*>(p.out_val)[obase + o] = bits;
+        }
+    }
+    pos += popc64(ms);
+    eqr += popc64(meq);
+}
+
+// Four waves per group of 64 tiles; each wave writes 16 of them.  The tiles'
+// output offsets come from the group prefix and a wave scan over the group.
+// The wave's slot chunks (64 entries each) are numbered across its tiles and
+// loaded 16 at a time, so dense tiles (whole rows above the band) cost no
+// more load rounds than their size demands.
 __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
 {
-    const uint64_t g = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
-    if (g >= (uint64_t)p.n * p.NT) return;
-    const uint32_t w = (uint32_t)(g / p.NT);
+    constexpr uint32_t TPW = TK_GROUP / 4; // tiles per wave
+    constexpr int B = 16;                  // chunks per load round
+    const uint64_t gq = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
+    if (gq >= (uint64_t)p.n * p.NG * 4) return;
+    const uint64_t gw = gq / 4;
+    const uint32_t quarter = (uint32_t)(gq % 4);
+    const uint32_t lane = lane_id();
+    const uint32_t w = (uint32_t)(gw / p.NG), grp = (uint32_t)(gw % p.NG);
     const uint32_t T = p.st[w].T, need = p.st[w].need;
-    const uint32_t cnt = p.tcnt[g];
-    uint32_t eqr = p.eqx[g];
-    uint64_t pos = (uint64_t)p.gtx[g] + (eqr < need ? eqr : need);
-    const uint32_t* si = p.slot_idx + g * TK_TILE;
-    const uint32_t* sv = p.slot_val + g * TK_TILE;
+    const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
+    const bool valid = grp * TK_GROUP + lane < p.NT;
+    const uint32_t cnt = valid ? p.tcnt[g0 + lane] : 0u;
+    const uint32_t gt = valid ? p.gtx[g0 + lane] : 0u, eq = valid ? p.eqx[g0 + lane] : 0u;
+    const uint32_t xg = p.ggt[gw] + wave_incl_scan(gt) - gt;
+    const uint32_t xe = p.geq[gw] + wave_incl_scan(eq) - eq;
+    // chunks of this wave's tiles, numbered in tile order
+    const bool mine = lane / TPW == quarter;
+    const uint32_t nch = mine ? (cnt + SG_WAVE - 1) / SG_WAVE : 0u;
+    const uint32_t cinc = wave_incl_scan(nch);
+    const uint32_t cst = cinc - nch;
+    const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)cinc, SG_WAVE - 1);
     const uint64_t obase = (uint64_t)w * p.k;
-    for (uint32_t i0 = 0; i0 < cnt; i0 += SG_WAVE) {
-        const uint32_t i = i0 + lane_id();
-        const bool valid = i < cnt;
-        uint32_t bits = valid ? sv[i] : 0u;
-        uint32_t key = key_of_bits(bits, p.bf16);
-        bool eq = valid && key == T;
-        uint64_t meq = ballot(eq);
-        uint32_t my_eq = eqr + popc64(meq & lanemask_lt());
-        bool sel = valid && (key > T || (eq && my_eq < need));
-        uint64_t ms = ballot(sel);
-        if (sel) {
-            uint64_t o = pos + popc64(ms & lanemask_lt());
-            if (o < p.k) {
-                p.out_idx[obase + o] = si[i];
-                if (p.bf16) static_cast<uint16_t*>(p.out_val)[obase + o] = (uint16_t)bits;
-                else static_cast<uint32_t*>(p.out_val)[obase + o] = bits;
-            }
+    uint32_t cur_tile = 0xffffffffu, eqr = 0;
+    uint64_t pos = 0;
+    for (uint32_t b0 = 0; b0 < C; b0 += B) {
+        uint32_t vb[B], vi[B], tj[B], ch[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const uint32_t q = b0 + u;
+            const uint64_t has = ballot(nch > 0 && cst <= q);
+            tj[u] = has ? 63u - (uint32_t)__builtin_clzll(has) : 0u; // the last tile starting at or before chunk q
+            const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)cst, (int)tj[u]);
+            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
+            ch[u] = q < C ? (q - first) * SG_WAVE : cj; // entry offset of the chunk in its tile
+            const uint32_t i = ch[u] + lane;
+            const uint64_t sb = (g0 + tj[u]) * TK_TILE;
+            vb[u] = q < C && i < cj ? p.slot_val[sb + i] : 0u;
+            vi[u] = q < C && i < cj ? p.slot_idx[sb + i] : 0u;
         }
-        pos += popc64(ms);
-        eqr += popc64(meq);
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            if (b0 + u >= C) break;
+            if (tj[u] != cur_tile) {
+                cur_tile = tj[u];
+                eqr = (uint32_t)__builtin_amdgcn_readlane((int)xe, (int)cur_tile);
+                pos = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xg, (int)cur_tile) + (eqr < need ? eqr : need);
+            }
+            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
+            write_chunk(p, cj - ch[u], vb[u], vi[u], T, need, obase, pos, eqr);
+        }
     }
 }
 
@@ -572,6 +672,9 @@ static uint64_t topk_carve(Carver& c, uint32_t n, uint64_t M, TopkParams* p)
     p->ccnt = c.take<uint32_t>(nt);
     p->gtx = c.take<uint32_t>(nt);
     p->eqx = c.take<uint32_t>(nt);
+    const uint64_t ng = (uint64_t)n * ceil_div(NT, TK_GROUP);
+    p->ggt = c.take<uint32_t>(ng);
+    p->geq = c.take<uint32_t>(ng);
     p->hist = c.take<uint32_t>((uint64_t)n * TK_BINS);
     p->samples = c.take<uint32_t>((uint64_t)n * TK_SAMPLES);
     p->slot_idx = c.take<uint32_t>(nt * TK_TILE);
@@ -608,6 +711,7 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     p.k = k;
     p.n = n;
     p.NT = (uint32_t)ceil_div(M, TK_TILE);
+    p.NG = (uint32_t)ceil_div(p.NT, TK_GROUP);
     p.bf16 = dt == SG_BF16;
     p.keymax = p.bf16 ? 0x7fffu : 0x7fffffffu;
     // a full 16-byte vector must start on a 16-byte boundary in every row
@@ -648,20 +752,21 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
         topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
         SG_TRY_LAUNCH();
     }
-    const unsigned hgrid = n * (unsigned)ceil_div(p.NT, TK_HIST_GROUP);
+    const unsigned hgrid = n * (unsigned)ceil_div(p.NG, (TK_THREADS / SG_WAVE) * TK_HIST_GROUPS);
     for (int pass = 0; pass < 3; ++pass) {
         topk_hist_kernel<<<hgrid, TK_THREADS, 0, st>>>(p);
         SG_TRY_LAUNCH();
         topk_pick_kernel<<<n, TK_THREADS, 0, st>>>(p);
         SG_TRY_LAUNCH();
     }
-    const unsigned wgrid = (unsigned)ceil_div(ntiles, TK_THREADS / SG_WAVE);
+    const unsigned wgrid = (unsigned)ceil_div((uint64_t)n * p.NG, TK_THREADS / SG_WAVE);
+    const unsigned wgrid4 = (unsigned)ceil_div((uint64_t)n * p.NG * 4, TK_THREADS / SG_WAVE);
     topk_tilecount_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     topk_scan_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_TOPK_WRITE, st);
-    topk_write_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
+    topk_write_kernel<<<wgrid4, TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_TOPK_WRITE, st);
     return SG_OK;
