@@ -187,7 +187,9 @@ int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t
  *                         are clamped)
  *   d_bitmap   [bitmap_words] uint32 out, bitmap_words >= sg_encode_max_words(M, P)
  *   d_word_off [P+1] uint64 out
- *   d_ws       unused: sg_encode_workspace_bytes returns 0 (may be NULL)
+ *   d_ws       sg_encode_workspace_bytes(M, P) bytes: per key window of the
+ *              class map and partition, where the partition's aggregated
+ *              entries of that window begin
  * Limits: 1 <= P <= 256, 1 <= M < 2^32.
  * ------------------------------------------------------------------------ */
 size_t sg_classmap_bytes(uint64_t M, uint32_t P);

@@ -32,6 +32,8 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
     const uint64_t T = (uint64_t)p->G * p->NT;
     p->nscan = (uint32_t)ceil_div(T, MG_SCAN_BLOCK);
     p->chunk_start = c.take<uint32_t>(R + 1);
+    p->nchunks_max = (uint32_t)(ceil_div(p->total, MG_CHUNK) + R);
+    p->chunk_rec = c.take<uint4>(p->nchunks_max);
     p->bnd = c.take<uint32_t>(R * (p->NT + 1));
     p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
     p->heavy = c.take<uint32_t>(T);
@@ -56,15 +58,14 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
     const uint64_t T = (uint64_t)p.G * p.NT;
     mg_plan_kernel<<<1, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    const uint64_t nchunks = ceil_div(p.total, MG_CHUNK) + R;
     probe_begin(SG_PROBE_AGGREGATE_BND, st);
-    mg_bnd_kernel<<<(unsigned)nchunks, 512, 0, st>>>(p);
+    mg_bnd_kernel<<<p.nchunks_max < 1024 ? p.nchunks_max : 1024, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_BND, st);
     const uint64_t cells = R * (p.NT + 1);
     mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    mg_heavy_kernel<<<(unsigned)ceil_div(T, 256), 256, 0, st>>>(p);
+    mg_heavy_kernel<<<(unsigned)(ceil_div(T, 256) < 1024 ? ceil_div(T, 256) : 1024), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
     // persistent blocks: as many as can be resident at once
     static int resident[2] = {0, 0};
@@ -91,7 +92,8 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
         SG_TRY_LAUNCH();
         mg_scan_top_kernel<<<1, 1024, 0, st>>>(p);
         SG_TRY_LAUNCH();
-        mg_place_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, st>>>(p);
+        const uint64_t pblocks = ceil_div(T, 4 * MG_PLACE_TILES);
+        mg_place_kernel<<<(unsigned)pblocks, 256, 0, st>>>(p);
         SG_TRY_LAUNCH();
         return SG_OK;
     }

@@ -25,7 +25,7 @@ namespace sg {
 
 constexpr uint32_t CM_MAGIC = 0x53474d31u; // "SGM1"
 constexpr int EN_THREADS = 256;
-constexpr int EN_SEG_WORDS = 4096;
+constexpr int EN_SEG_WORDS = 512; // a window's bitmap words: at most W/32 + P <= 128 + 256
 
 struct CmapLayout {
     uint64_t M;
@@ -49,9 +49,9 @@ static CmapLayout cmap_layout(uint64_t M, uint32_t P)
     L.nbits = 0;
     while ((1u << L.nbits) < P) ++L.nbits;
     L.stride = L.nbits == 0 ? 0 : (L.nbits == 1 ? 1 : (L.nbits == 2 ? 2 : (L.nbits <= 4 ? 4 : 8)));
-    L.NCW = 2048 / P;
-    if (L.NCW > 128) L.NCW = 128;
-    if (L.NCW == 0) L.NCW = 1;
+    // chunks per window: a power of two in [8, 128] with NCW * P <= 2048
+    L.NCW = 128;
+    while (L.NCW > 8 && L.NCW * P > 2048) L.NCW >>= 1;
     L.W = 32 * L.NCW;
     L.NW = ceil_div(M, L.W);
     L.NC = ceil_div(M, 32);
@@ -165,12 +165,11 @@ struct EncParams {
     CmapPtrs q;
     const uint32_t* agg_idx;
     const uint64_t* agg_off;
-    uint64_t agg_cap; // entries d_agg_idx holds
+    uint64_t agg_cap;  // entries d_agg_idx holds
     uint32_t* bitmap;
     uint64_t bitmap_words;
     uint64_t* word_off_out;
-    uint32_t SR;      // windows per block
-    uint32_t nblocks;
+    uint64_t* cur;     // [(NW+1) * P] first aggregated entry of partition p at or after window w's first key
 };
 
 // class-p mask of one chunk from its planes (valid = keys of the chunk below M)
@@ -188,156 +187,282 @@ __device__ __forceinline__ uint32_t chunk_valid(const CmapLayout& L, uint64_t c)
     return left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
 }
 
-// zero the words that two neighbouring blocks share (they are merged with
-// atomicOr by the encode kernel)
+// partition offsets clamped to the aggregate's capacity (into LDS)
+__device__ __forceinline__ void load_agg_offsets(const EncParams& e, uint64_t* offs)
+{
+    const uint32_t P = e.L.P;
+    for (uint32_t i = threadIdx.x; i <= P; i += blockDim.x) {
+        uint64_t v = e.agg_off[i];
+        offs[i] = v > e.agg_cap ? e.agg_cap : v;
+    }
+    __syncthreads();
+}
+
+// Window cursors: one streaming pass over the aggregated entries; entry i of
+// partition p is the first of its partition in windows (win(i-1), win(i)].
+__global__ __launch_bounds__(256) void enc_cursor_kernel(EncParams e)
+{
+    __shared__ uint64_t offs[257];
+    load_agg_offsets(e, offs);
+    const uint32_t P = e.L.P;
+    const uint64_t NW = e.L.NW, W = e.L.W;
+    const uint64_t nagg = offs[P];
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < nagg; i += (uint64_t)gridDim.x * 256) {
+        uint32_t lo = 0, hi = P; // largest p with offs[p] <= i
+        while (lo + 1 < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (offs[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t p = lo;
+        const uint64_t s = offs[p], en = offs[p + 1] > s ? offs[p + 1] : s;
+        if (i < s || i >= en) continue; // inconsistent offsets
+        uint64_t win = e.agg_idx[i] / W;
+        if (win >= NW) win = NW - 1;
+        int64_t prev = -1;
+        if (i > s) {
+            const uint64_t pw = e.agg_idx[i - 1] / W;
+            prev = (int64_t)(pw < NW ? pw : NW - 1);
+        }
+        for (int64_t w = prev + 1; w <= (int64_t)win; ++w) e.cur[(uint64_t)w * P + p] = i;
+        if (i == en - 1)
+            for (uint64_t w = win + 1; w <= NW; ++w) e.cur[w * P + p] = en;
+    }
+}
+
+// cursors of empty partitions
+__global__ void enc_cursor_empty_kernel(EncParams e)
+{
+    __shared__ uint64_t offs[257];
+    load_agg_offsets(e, offs);
+    const uint32_t P = e.L.P;
+    const uint64_t cells = (e.L.NW + 1) * P;
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cells; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t p = (uint32_t)(i % P);
+        if (offs[p + 1] <= offs[p]) e.cur[i] = offs[p];
+    }
+}
+
+// zero the bitmap words that two neighbouring windows share (they are merged
+// with atomicOr by the encode kernel)
 __global__ void enc_zero_kernel(EncParams e)
 {
     const uint32_t P = e.L.P;
-    const uint64_t cnt = (uint64_t)e.nblocks * P;
+    const uint64_t cnt = e.L.NW * P;
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cnt; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint32_t blk = (uint32_t)(i / P), p = (uint32_t)(i % P);
-        if (blk == 0) continue;
-        const uint64_t w0 = (uint64_t)blk * e.SR;
-        if (w0 > e.L.NW) continue;
-        const uint32_t a = e.q.cpre[w0 * P + p];
+        const uint64_t w = i / P;
+        const uint32_t p = (uint32_t)(i % P);
+        if (w == 0) continue;
+        const uint32_t a = e.q.cpre[w * P + p];
         if ((a & 31u) == 0 || a >= e.q.class_size[p]) continue;
         const uint64_t gw = e.q.word_off[p] + (a >> 5);
         if (gw < e.bitmap_words) e.bitmap[gw] = 0u;
     }
 }
 
+// A block per window of W keys (blocks loop over windows), all partitions
+// together: class masks of
+// the window's chunks and their per-class prefix counts in LDS; every
+// aggregated key of the window (loaded in one round, its range known from the
+// cursors) sets the bit of its rank in an LDS copy of the window's bitmap
+// words; the words are then written out.
 __global__ __launch_bounds__(EN_THREADS) void enc_kernel(EncParams e)
 {
-    __shared__ uint32_t masks[128 * 16 > 2048 ? 2048 : 2048]; // [NCW][P], NCW*P <= 2048
-    __shared__ uint16_t pre[2048];                              // [NCW][P]
+    constexpr int KB = 4; // keys per thread per load round
+    __shared__ uint32_t masks[2048];  // [NCW][P], NCW*P <= 2048
+    __shared__ uint16_t pre[2048];    // [NCW][P]
     __shared__ uint32_t seg[EN_SEG_WORDS];
-    __shared__ uint32_t segofs[257];
-    __shared__ uint32_t a_bits[256], base_bits[256], wtot[256];
-    __shared__ uint64_t cursor[256], cend[256];
+    __shared__ uint32_t segofs[257], kof[257], a_bits[256], b_bits[256];
+    __shared__ uint64_t kbeg[256];
     __shared__ uint32_t scan_lds[EN_THREADS / SG_WAVE + 1];
 
     const CmapLayout& L = e.L;
     const uint32_t P = L.P, NCW = L.NCW;
-    const uint32_t blk = blockIdx.x;
-    const uint64_t w0 = (uint64_t)blk * e.SR;
-    uint64_t w1 = w0 + e.SR;
-    if (w1 > L.NW) w1 = L.NW;
-    if (w0 >= w1) return;
-    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
+    const uint32_t lane = lane_id();
+    for (uint64_t win = blockIdx.x; win < L.NW; win += gridDim.x) {
+    const uint64_t wstart = win * L.W;
 
-    if (blk == 0)
+    if (win == 0)
         for (uint32_t i = threadIdx.x; i <= P; i += EN_THREADS) e.word_off_out[i] = e.q.word_off[i];
-    if (blk == 0 && threadIdx.x == 0) {
+    if (win == 0 && threadIdx.x == 0) {
         const CmapHeader h = *e.q.hdr;
         if (h.magic != CM_MAGIC || h.P != P || h.M != L.M) report_error(kDevErrCmap);
     }
 
-    // segment layout and cursors
-    uint32_t nw = 0;
+    // every independent load first: the chunk's bit planes, the partition's
+    // offsets, cursors and class prefixes
+    uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t valid = 0;
+    if (threadIdx.x < NCW) {
+        const uint64_t c = win * NCW + threadIdx.x;
+        valid = chunk_valid(L, c);
+        if (valid)
+            for (uint32_t b = 0; b < L.nbits; ++b) pl[b] = e.q.planes[c * L.stride + b];
+    }
+    // key ranges and bitmap word ranges of the window per partition
+    uint32_t kc = 0, nw = 0;
     if (threadIdx.x < P) {
         const uint32_t p = threadIdx.x;
-        const uint32_t a = e.q.cpre[w0 * P + p], b = e.q.cpre[w1 * P + p];
-        a_bits[p] = a;
-        base_bits[p] = a;
-        nw = b > a ? ((b - 1) >> 5) - (a >> 5) + 1 : 0u;
-        // first aggregated key of partition p at or after the block's first key
-        uint64_t lo0 = e.agg_off[p], hi0 = e.agg_off[p + 1];
-        if (hi0 > e.agg_cap) hi0 = e.agg_cap;
-        if (lo0 > hi0) lo0 = hi0;
-        const uint64_t key0 = w0 * L.W;
-        uint64_t lo = lo0, hi = hi0;
-        while (lo < hi) {
-            const uint64_t mid = (lo + hi) >> 1;
-            if ((uint64_t)e.agg_idx[mid] < key0) lo = mid + 1;
-            else hi = mid;
-        }
-        cursor[p] = lo;
-        cend[p] = hi0;
+        uint64_t s = e.agg_off[p], en = e.agg_off[p + 1];
+        s = s > e.agg_cap ? e.agg_cap : s;
+        en = en > e.agg_cap ? e.agg_cap : (en < s ? s : en);
+        uint64_t a = e.cur[win * P + p], b = e.cur[(win + 1) * P + p];
+        a = a < s ? s : (a > en ? en : a);
+        b = b < a ? a : (b > en ? en : b);
+        if (b - a > L.W) b = a + L.W; // at most W keys fall in a window (valid input)
+        kbeg[p] = a;
+        kc = (uint32_t)(b - a);
+        const uint32_t ca = e.q.cpre[win * P + p], cb = e.q.cpre[(win + 1) * P + p];
+        a_bits[p] = ca;
+        b_bits[p] = cb;
+        nw = cb > ca ? ((cb - 1) >> 5) - (ca >> 5) + 1 : 0u;
     }
-    uint32_t tot;
-    const uint32_t so = block_excl_scan<EN_THREADS>(nw, scan_lds, &tot);
-    if (threadIdx.x < P) segofs[threadIdx.x] = so;
-    if (threadIdx.x == 0) segofs[P] = tot;
+    uint32_t K, nseg;
+    const uint32_t ko = block_excl_scan<EN_THREADS>(kc, scan_lds, &K);
+    __syncthreads();
+    const uint32_t so = block_excl_scan<EN_THREADS>(nw, scan_lds, &nseg);
+    if (threadIdx.x < P) {
+        kof[threadIdx.x] = ko;
+        segofs[threadIdx.x] = so;
+    }
+    if (threadIdx.x == 0) {
+        kof[P] = K;
+        segofs[P] = nseg;
+    }
     for (uint32_t i = threadIdx.x; i < EN_SEG_WORDS; i += EN_THREADS) seg[i] = 0u;
     __syncthreads();
-    if (tot > EN_SEG_WORDS) { // cannot happen with the host's choice of SR
+    if (nseg > EN_SEG_WORDS) { // cannot happen: at most W/32 + P words
         if (threadIdx.x == 0) report_error(kDevErrCmap);
-        return;
+        __syncthreads();
+        continue;
     }
-
-    for (uint64_t win = w0; win < w1; ++win) {
-        const uint64_t wstart = win * L.W;
-        // a) class masks of the window's chunks
-        for (uint32_t t = threadIdx.x; t < NCW; t += EN_THREADS) {
-            const uint64_t c = win * NCW + t;
-            const uint32_t valid = chunk_valid(L, c);
-            uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (valid)
-                for (uint32_t b = 0; b < L.nbits; ++b) pl[b] = e.q.planes[c * L.stride + b];
-            for (uint32_t p = 0; p < P; ++p) masks[t * P + p] = class_mask(pl, L.nbits, p, valid);
-        }
-        __syncthreads();
-        // b) per-partition prefix over the chunks of the window
-        if (threadIdx.x < P) {
-            const uint32_t p = threadIdx.x;
-            uint32_t run = 0;
-            for (uint32_t t = 0; t < NCW; ++t) {
-                pre[t * P + p] = (uint16_t)run;
-                run += __popc(masks[t * P + p]);
-            }
-            wtot[p] = run;
-        }
-        __syncthreads();
-        // c) aggregated keys of each partition inside the window
-        for (uint32_t p = wid; p < P; p += EN_THREADS / SG_WAVE) {
-            uint64_t cur = cursor[p];
-            const uint64_t end = cend[p];
-            const uint64_t wend = wstart + L.W;
-            const uint32_t seg_lo = a_bits[p] >> 5;
-            const uint32_t bb = base_bits[p];
-            while (cur < end) {
-                const uint64_t i = cur + lane;
-                const uint32_t key = i < end ? e.agg_idx[i] : 0xffffffffu;
-                const bool in = i < end && (uint64_t)key < wend && (uint64_t)key >= wstart;
-                const uint64_t m = ballot(in);
-                if (in) {
-                    const uint32_t o = (uint32_t)(key - wstart);
-                    const uint32_t t = o >> 5, bit = o & 31u;
-                    const uint32_t mk = masks[t * P + p];
-                    if (!((mk >> bit) & 1u)) report_error(kDevErrPartition);
-                    const uint32_t r = bb + pre[t * P + p] + __popc(mk & ((1u << bit) - 1u));
-                    const uint32_t lw = (r >> 5) - seg_lo;
-                    if (lw < segofs[p + 1] - segofs[p]) atomicOr(&seg[segofs[p] + lw], 1u << (r & 31u));
+    // issue the first round of key loads before building the masks
+    uint32_t key[KB], kp[KB];
+    auto load_round = [&](uint32_t j0) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const uint32_t j = j0 + u * EN_THREADS + threadIdx.x;
+            kp[u] = 0xffffffffu;
+            key[u] = 0;
+            if (j < K) {
+                uint32_t lo = 0, hi = P; // largest p with kof[p] <= j
+                while (lo + 1 < hi) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (kof[mid] <= j) lo = mid;
+                    else hi = mid;
                 }
-                const uint32_t took = popc64(m);
-                cur += took;
-                if (took < SG_WAVE) break;
+                kp[u] = lo;
+                key[u] = e.agg_idx[kbeg[lo] + (j - kof[lo])];
             }
-            if (lane == 0) cursor[p] = cur;
         }
-        __syncthreads();
-        if (threadIdx.x < P) base_bits[threadIdx.x] += wtot[threadIdx.x];
-        __syncthreads();
-    }
+    };
+    load_round(0);
 
-    // write the segments
-    for (uint32_t p = 0; p < P; ++p) {
-        const uint32_t a = a_bits[p], b = base_bits[p];
-        if (b <= a) continue;
-        const uint32_t q0 = a >> 5, nwp = segofs[p + 1] - segofs[p];
-        const uint64_t csize = e.q.class_size[p];
-        const uint64_t wbase = e.q.word_off[p];
-        for (uint32_t lw = threadIdx.x; lw < nwp; lw += EN_THREADS) {
-            const uint32_t qw = q0 + lw;
-            const bool excl = (uint64_t)qw * 32 >= a && ((uint64_t)(qw + 1) * 32 <= b || (uint64_t)b == csize);
-            const uint64_t gw = wbase + qw;
-            if (gw >= e.bitmap_words) continue;
-            const uint32_t v = seg[segofs[p] + lw];
-            if (excl) e.bitmap[gw] = v;
-            else if (v) atomicOr(&e.bitmap[gw], v);
+    // a) class masks of the window's chunks (NCW <= 128 < EN_THREADS); up to
+    //    16 classes by splitting: each level splits every mask by one plane
+    if (threadIdx.x < NCW) {
+        uint32_t* mrow = masks + threadIdx.x * P;
+        if (L.nbits <= 4) {
+            uint32_t m[16];
+            m[0] = valid;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if ((uint32_t)b < L.nbits) {
+#pragma unroll
+                    for (int k = (1 << b) - 1; k >= 0; --k) { // class id bit b set: m & plane_b
+                        m[k + (1 << b)] = m[k] & pl[b];
+                        m[k] &= ~pl[b];
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if ((uint32_t)k < P) mrow[k] = m[k];
+        } else {
+            for (uint32_t p = 0; p < P; ++p) mrow[p] = class_mask(pl, L.nbits, p, valid);
         }
+    }
+    __syncthreads();
+    // b) per-partition prefix over the chunks of the window: the NCW*P counts
+    //    as P segments of NCW (partition-major), 8 per thread, then a
+    //    segmented scan over the NCW/8 <= 16 threads of a segment (inside one
+    //    DPP row)
+    {
+        const uint32_t e0 = threadIdx.x * 8;
+        uint32_t c[8], run = 0;
+        const bool act = e0 < NCW * P;
+        const uint32_t p = act ? e0 / NCW : 0u, t0 = act ? e0 % NCW : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = act ? __popc(masks[(t0 + j) * P + p]) : 0u;
+            run += c[j];
+        }
+        const uint32_t sg = NCW / 8; // threads per segment: a power of two, at most 16
+        const uint32_t inrow = lane & 15u;
+        uint32_t inc = run, x;
+        x = dpp_move<kDppRowShr1>(0u, inc);
+        if (sg > 1 && (inrow & (sg - 1)) >= 1) inc += x;
+        x = dpp_move<kDppRowShr2>(0u, inc);
+        if (sg > 2 && (inrow & (sg - 1)) >= 2) inc += x;
+        x = dpp_move<kDppRowShr4>(0u, inc);
+        if (sg > 4 && (inrow & (sg - 1)) >= 4) inc += x;
+        x = dpp_move<kDppRowShr8>(0u, inc);
+        if (sg > 8 && (inrow & (sg - 1)) >= 8) inc += x;
+        if (act) {
+            uint32_t ex = inc - run;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pre[(t0 + j) * P + p] = (uint16_t)ex;
+                ex += c[j];
+            }
+        }
+    }
+    __syncthreads();
+    // c) the bit of every aggregated key: its rank in its class
+    for (uint32_t j0 = 0; j0 < K; j0 += KB * EN_THREADS) {
+        if (j0 > 0) load_round(j0);
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            if (kp[u] == 0xffffffffu) continue;
+            const uint32_t p = kp[u];
+            const uint64_t o = (uint64_t)key[u] - wstart;
+            if (key[u] < wstart || o >= L.W) { // not in this window: cannot happen for valid input
+                report_error(kDevErrPartition);
+                continue;
+            }
+            const uint32_t t = (uint32_t)(o >> 5), bit = (uint32_t)(o & 31u);
+            const uint32_t mk = masks[t * P + p];
+            if (!((mk >> bit) & 1u)) report_error(kDevErrPartition);
+            const uint32_t r = a_bits[p] + pre[t * P + p] + __popc(mk & ((1u << bit) - 1u));
+            const uint32_t lw = (r >> 5) - (a_bits[p] >> 5);
+            if (lw < segofs[p + 1] - segofs[p]) atomicOr(&seg[segofs[p] + lw], 1u << (r & 31u));
+        }
+    }
+    __syncthreads();
+    // d) write the window's words: plain stores for words inside the window,
+    //    atomicOr for the words shared with a neighbour (pre-zeroed)
+    for (uint32_t i = threadIdx.x; i < nseg; i += EN_THREADS) {
+        uint32_t lo = 0, hi = P; // partition of segment word i
+        while (lo + 1 < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (segofs[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t p = lo;
+        const uint32_t a = a_bits[p], b = b_bits[p];
+        const uint32_t qw = (a >> 5) + (i - segofs[p]);
+        const uint64_t csize = e.q.class_size[p];
+        const bool excl = (uint64_t)qw * 32 >= a && ((uint64_t)(qw + 1) * 32 <= b || (uint64_t)b == csize);
+        const uint64_t gw = e.q.word_off[p] + qw;
+        if (gw >= e.bitmap_words) continue;
+        const uint32_t v = seg[i];
+        if (excl) e.bitmap[gw] = v;
+        else if (v) atomicOr(&e.bitmap[gw], v);
+    }
+    __syncthreads(); // LDS is reused by the block's next window
     }
 }
+
 
 } // namespace sg
 
@@ -366,21 +491,20 @@ extern "C" int sg_classmap_build(uint64_t M, uint32_t P, uint32_t seed, void* d_
 
 extern "C" uint64_t sg_encode_max_words(uint64_t M, uint32_t P) { return M / 32 + P + 1; }
 
-// The encode pass keeps all its scratch in LDS.
+// Workspace: the window cursors, (NW + 1) * P words of 8 bytes.
 extern "C" size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P)
 {
-    (void)M;
-    (void)P;
-    return 0;
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return 0;
+    const CmapLayout L = cmap_layout(M, P);
+    return (size_t)(8ull * (L.NW + 1) * P);
 }
 
 extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg_capacity, uint64_t M,
                          uint32_t P, const void* d_cmap, size_t cmap_bytes, uint32_t* d_bitmap, uint64_t bitmap_words, uint64_t* d_word_off,
                          void* d_ws, size_t ws_bytes, void* stream)
 {
-    (void)d_ws;
     if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return SG_EINVAL;
-    if (!d_agg_off || !d_cmap || !d_bitmap || !d_word_off || !d_agg_idx) return SG_EINVAL;
+    if (!d_agg_off || !d_cmap || !d_bitmap || !d_word_off || !d_agg_idx || !d_ws) return SG_EINVAL;
     if (ws_bytes < sg_encode_workspace_bytes(M, P)) return SG_ECAPACITY;
     if (bitmap_words < sg_encode_max_words(M, P)) return SG_ECAPACITY;
     if (cmap_bytes < sg_classmap_bytes(M, P)) return SG_ECAPACITY;
@@ -393,22 +517,21 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     e.bitmap = d_bitmap;
     e.bitmap_words = bitmap_words;
     e.word_off_out = d_word_off;
-    // windows per block: enough blocks to fill the chip, and the block's
-    // bitmap segments must fit in LDS
-    uint64_t sr = e.L.NW / 2048;
-    if (sr < 1) sr = 1;
-    const uint64_t srmax = ((uint64_t)(EN_SEG_WORDS - 2 * P - 2) * 32) / e.L.W;
-    if (sr > srmax) sr = srmax;
-    if (sr > 64) sr = 64;
-    if (sr < 1) return SG_EUNSUPPORTED;
-    e.SR = (uint32_t)sr;
-    e.nblocks = (uint32_t)ceil_div(e.L.NW, sr);
+    e.cur = static_cast<uint64_t*>(d_ws);
+    // a window's words never exceed W/32 + P
+    if (e.L.W / 32 + P + 2 > (uint64_t)EN_SEG_WORDS) return SG_EUNSUPPORTED;
     hipStream_t st = as_stream(stream);
-    const uint64_t zc = (uint64_t)e.nblocks * P;
+    const uint64_t cells = (e.L.NW + 1) * P;
+    enc_cursor_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 1024 ? ceil_div(cells, 256) : 1024), 256, 0, st>>>(e);
+    SG_TRY_LAUNCH();
+    const uint64_t cblocks = ceil_div(agg_capacity, 256);
+    enc_cursor_kernel<<<(unsigned)(cblocks < 4096 ? (cblocks ? cblocks : 1) : 4096), 256, 0, st>>>(e);
+    SG_TRY_LAUNCH();
+    const uint64_t zc = e.L.NW * P;
     enc_zero_kernel<<<(unsigned)(ceil_div(zc, 256) < 1024 ? ceil_div(zc, 256) : 1024), 256, 0, st>>>(e);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_ENCODE, st);
-    enc_kernel<<<e.nblocks, EN_THREADS, 0, st>>>(e);
+    enc_kernel<<<(unsigned)e.L.NW, EN_THREADS, 0, st>>>(e);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_ENCODE, st);
     return SG_OK;

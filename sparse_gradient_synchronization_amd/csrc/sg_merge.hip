@@ -74,6 +74,8 @@ struct MergeParams {
     uint64_t capacity;
     // workspace
     uint32_t* chunk_start;  // [n*G + 1] bnd blocks per run (position order)
+    uint4* chunk_rec;       // [nchunks_max] bnd block c: {run (position order) or ~0, first entry in the run, run length, run start}
+    uint32_t nchunks_max;   // bnd blocks launched
     uint32_t* bnd;          // [(g*n + w) * (NT+1) + b]
     uint32_t* tile_cnt;     // [G*NT] distinct keys of a tile
     uint64_t* tile_sb;      // [G*NT] staging offset of a tile
@@ -136,6 +138,17 @@ __global__ __launch_bounds__(512) void mg_plan_kernel(MergeParams p)
     }
     if (threadIdx.x == 0) p.chunk_start[R] = carry;
     for (uint32_t i = threadIdx.x; i < (uint32_t)(MG_NQ * MG_QSTRIDE); i += 512) p.queue[i] = 0;
+    __syncthreads();
+    // block -> run table of the boundary pass
+    for (uint32_t r = threadIdx.x / SG_WAVE; r < R; r += 512 / SG_WAVE) { // one wave per run
+        const uint32_t c0 = p.chunk_start[r], c1 = p.chunk_start[r + 1];
+        uint64_t s, e;
+        run_range(p, r % p.G, r / p.G, s, e);
+        for (uint32_t c = c0 + lane_id(); c < c1; c += SG_WAVE)
+            p.chunk_rec[c] = make_uint4(r, (c - c0) * MG_CHUNK, (uint32_t)(e - s), (uint32_t)s);
+    }
+    for (uint32_t c = p.chunk_start[R] + threadIdx.x; c < p.nchunks_max; c += 512)
+        p.chunk_rec[c] = make_uint4(0xffffffffu, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ uint32_t tile_of(const MergeParams& p, uint32_t key)
@@ -149,31 +162,36 @@ __device__ __forceinline__ uint32_t tile_of(const MergeParams& p, uint32_t key)
 }
 
 // bnd[run][b] = first position (relative to the run) whose key is >= b * 2^tb;
-// bnd[run][NT] = the run's length.
+// bnd[run][NT] = the run's length.  Each thread takes 8 consecutive entries of
+// a 4096-entry chunk, loads them at once, then writes the tile starts that
+// fall between them.
 __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 {
-    const uint32_t R = p.n * p.G;
-    const uint32_t c = blockIdx.x;
-    if (c >= p.chunk_start[R]) return;
-    uint32_t lo = 0, hi = R;
-    while (lo + 1 < hi) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (p.chunk_start[mid] <= c) lo = mid;
-        else hi = mid;
-    }
-    const uint32_t rp = lo, g = rp % p.G, w = rp / p.G;
-    uint64_t s, e;
-    run_range(p, g, w, s, e);
-    const uint64_t len = e - s;
-    const uint64_t j0 = (uint64_t)(c - p.chunk_start[rp]) * MG_CHUNK;
+    constexpr int E = MG_CHUNK / 512;
+    for (uint32_t c = blockIdx.x; c < p.nchunks_max; c += gridDim.x) {
+    const uint4 rec = p.chunk_rec[c];
+    if (rec.x == 0xffffffffu) continue;
+    const uint32_t rp = rec.x, g = rp % p.G, w = rp / p.G;
+    const uint64_t s = rec.w, len = rec.z;
+    const uint64_t j0 = (uint64_t)rec.y + (uint64_t)threadIdx.x * E;
     uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
-    for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && j < len; j += 512) {
-        const uint32_t b = tile_of(p, p.idx[s + j]);
-        int64_t pb = -1;
-        if (j > 0) pb = tile_of(p, p.idx[s + j - 1]);
+    uint32_t key[E + 1];
+#pragma unroll
+    for (int u = 0; u <= E; ++u) { // key[0] is the entry before the thread's first
+        const int64_t j = (int64_t)j0 + u - 1;
+        key[u] = (j >= 0 && (uint64_t)j < len) ? p.idx[s + j] : 0u;
+    }
+    int64_t pb = j0 > 0 && j0 <= len ? (int64_t)tile_of(p, key[0]) : -1;
+#pragma unroll
+    for (int u = 1; u <= E; ++u) {
+        const uint64_t j = j0 + u - 1;
+        if (j >= len) break;
+        const uint32_t b = tile_of(p, key[u]);
         for (int64_t x = pb + 1; x <= (int64_t)b; ++x) row[x] = (uint32_t)j;
         if (j == len - 1)
             for (uint64_t x = (uint64_t)b + 1; x <= p.NT; ++x) row[x] = (uint32_t)len;
+        pb = b;
+    }
     }
 }
 
@@ -195,21 +213,26 @@ __global__ void mg_bnd_empty_kernel(MergeParams p)
 __global__ __launch_bounds__(256) void mg_heavy_kernel(MergeParams p)
 {
     const uint32_t T = p.G * p.NT;
-    const uint32_t t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= T) return;
+    for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
     const uint32_t g = t / p.NT, b = t % p.NT;
     uint32_t E = 0;
-    for (uint32_t w = 0; w < p.n; ++w) {
-        uint64_t s, e;
-        run_range(p, g, w, s, e);
-        const uint64_t len = e - s;
-        const uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
-        uint64_t x = row[b], y = row[b + 1];
-        if (x > len) x = len;
-        if (y > len) y = len;
-        E += y > x ? (uint32_t)(y - x) : 0u;
+    for (uint32_t w0 = 0; w0 < p.n; w0 += 8) { // 8 runs' loads at once
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            const uint32_t w = w0 + u;
+            if (w >= p.n) break;
+            uint64_t s, e;
+            run_range(p, g, w, s, e);
+            const uint64_t len = e - s;
+            const uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
+            uint64_t x = row[b], y = row[b + 1];
+            if (x > len) x = len;
+            if (y > len) y = len;
+            E += y > x ? (uint32_t)(y - x) : 0u;
+        }
     }
     if (E > (uint32_t)MG_HEAVY) p.heavy[atomicAdd(&p.queue[0], 1u)] = t;
+    }
 }
 
 // Contiguous part of `key` among P parts [floor(iM/P), floor((i+1)M/P)):
@@ -223,6 +246,37 @@ __device__ __forceinline__ uint32_t contig_part(uint64_t key, uint64_t M, uint32
     if (q * M > x) --q;
     else if ((q + 1) * M <= x) ++q;
     return q < P ? (uint32_t)q : P - 1;
+}
+
+// Counts of a wave's keys per part into LDS counters h.  Keys in ascending
+// order have non-decreasing contiguous parts: when the first and the last
+// agree (the usual case), one add counts them all.
+__device__ __forceinline__ void count_sorted_parts(uint32_t* h, uint32_t part, bool has)
+{
+    const uint64_t act = ballot(has);
+    if (!act) return;
+    const uint32_t fl = (uint32_t)__builtin_ctzll(act), ll = 63u - (uint32_t)__builtin_clzll(act);
+    const uint32_t pf = (uint32_t)__builtin_amdgcn_readlane((int)part, (int)fl);
+    const uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)part, (int)ll);
+    if (pf == pl) {
+        if (lane_id() == fl) atomicAdd(&h[pf], popc64(act));
+    } else if (has) {
+        atomicAdd(&h[part], 1u);
+    }
+}
+
+// Counts of a wave's keys per part for parts in any order: one ballot per
+// part when there are few, else one LDS atomic per key.
+__device__ __forceinline__ void count_parts(uint32_t* h, uint32_t part, bool has, uint32_t P)
+{
+    if (P <= 16) {
+        for (uint32_t b = 0; b < P; ++b) {
+            const uint32_t c = popc64(ballot(has && part == b));
+            if (c && lane_id() == 0) atomicAdd(&h[b], c);
+        }
+    } else if (has) {
+        atomicAdd(&h[part], 1u);
+    }
 }
 
 // the lanes' (a, b) worker pair of pair index pi, a <= b, row-major
@@ -464,6 +518,11 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
     }
     const uint32_t W = gridDim.x * MG_WAVES;
     const uint32_t gwave = blockIdx.x * MG_WAVES + wid;
+    // statistics: the lane's first four worker pairs
+    uint32_t pair_a[4] = {0, 0, 0, 0}, pair_b[4] = {0, 0, 0, 0};
+    if (MODE == MODE_STATS)
+        for (int j = 0; j < 4; ++j)
+            if (lane + 64u * j < p.npairs) pair_of(lane + 64u * j, n, pair_a[j], pair_b[j]);
     WaveWork work = {gwave, gwave % MG_NQ, 0u, 0u, true};
     bool from_heavy = false;
     uint32_t key[MG_PER], wk[MG_PER], vb[MG_PER];
@@ -630,19 +689,27 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                 // statistics: union part counts and pairwise intersections
                 for (uint32_t q0 = 0; q0 < U; q0 += SG_WAVE) {
                     const uint32_t q = q0 + lane;
+                    const bool has = q < U;
                     unsigned long long m = 0;
-                    if (q < U) {
-                        const uint32_t k = sm.bits[q];
+                    uint32_t k = 0;
+                    if (has) {
+                        k = sm.bits[q];
                         m = sm.mask[q];
-                        atomicAdd(&bs.part[contig_part(k, p.M, p.Ps, p.inv_m)], 1u);
-                        if (p.hashed) atomicAdd(&bs.part[p.Ps + h0(k, p.seed, p.div)], 1u);
                     }
+                    count_sorted_parts(bs.part, has ? contig_part(k, p.M, p.Ps, p.inv_m) : 0u, has);
+                    if (p.hashed) count_parts(bs.part + p.Ps, has ? h0(k, p.seed, p.div) : 0u, has, p.Ps);
                     for (uint32_t a = 0; a < n; ++a) {
                         const uint64_t v = ballot((m >> a) & 1ull);
                         if (lane == 0) sm.vm[a] = v;
                     }
                     wave_sync();
-                    for (uint32_t pi = lane; pi < p.npairs; pi += SG_WAVE) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (lane + 64u * j >= p.npairs) break;
+                        const uint32_t c = popc64(sm.vm[pair_a[j]] & sm.vm[pair_b[j]]);
+                        if (c) atomicAdd(&bs.pairs[lane + 64u * j], c);
+                    }
+                    for (uint32_t pi = lane + 256; pi < p.npairs; pi += SG_WAVE) { // n > 22
                         uint32_t a, bb;
                         pair_of(pi, n, a, bb);
                         const uint32_t c = popc64(sm.vm[a] & sm.vm[bb]);
@@ -732,27 +799,61 @@ __global__ __launch_bounds__(1024) void mg_scan_top_kernel(MergeParams p)
     if (threadIdx.x == 0) p.agg_off[p.G] = carry;
 }
 
-// one wave per tile: staged entries to their final offsets
+// One wave per 8 tiles: their offsets in one load round, then the first 64
+// staged entries of all 8 at once, so the copies of the tiles overlap.
+constexpr int MG_PLACE_TILES = 8;
+
 __global__ __launch_bounds__(256) void mg_place_kernel(MergeParams p)
 {
     const uint32_t T = p.G * p.NT;
-    const uint32_t t = blockIdx.x * 4 + threadIdx.x / SG_WAVE;
-    if (t >= T) return;
-    const uint32_t lane = lane_id();
-    const uint64_t ob = p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK];
-    if (t % p.NT == 0 && lane == 0) p.agg_off[t / p.NT] = ob;
-    const uint32_t c = p.tile_cnt[t];
-    const uint64_t sb = p.tile_sb[t];
-    if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
-        if (lane == 0) report_error(kDevErrPartition);
-        return;
+    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
+    for (uint64_t t0 = ((uint64_t)blockIdx.x * 4 + wid) * MG_PLACE_TILES; t0 < T;
+         t0 += (uint64_t)gridDim.x * 4 * MG_PLACE_TILES) {
+    const uint64_t t = t0 + lane;
+    const bool mine = lane < (uint32_t)MG_PLACE_TILES && t < T;
+    uint32_t c = 0;
+    uint64_t sb = 0, ob = 0;
+    if (mine) {
+        c = p.tile_cnt[t];
+        sb = p.tile_sb[t];
+        ob = p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK];
+        if (t % p.NT == 0) p.agg_off[t / p.NT] = ob;
+        if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
+            report_error(kDevErrPartition);
+            c = 0;
+        }
     }
-    for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_idx[ob + i] = p.stage_idx[sb + i];
-    if (p.D == 1) {
-        for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_val[ob + i] = p.stage_val[sb + i];
-    } else if (p.D > 1) {
-        const uint64_t cnt = (uint64_t)c * p.D;
-        for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[ob * p.D + i] = p.stage_val[sb * p.D + i];
+    const uint32_t sb_lo = (uint32_t)sb, sb_hi = (uint32_t)(sb >> 32), ob_lo = (uint32_t)ob, ob_hi = (uint32_t)(ob >> 32);
+    for (uint32_t k0 = 0; k0 < (uint32_t)MG_PLACE_TILES; k0 += 8) {
+        uint32_t ck[8], vi[8], vv[8];
+        uint64_t s0[8], d0[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = (int)k0 + u;
+            ck[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
+            s0[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sb_hi, k) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)sb_lo, k);
+            d0[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ob_hi, k) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)ob_lo, k);
+            vi[u] = lane < ck[u] ? p.stage_idx[s0[u] + lane] : 0u;
+            vv[u] = lane < ck[u] && p.D == 1 ? __float_as_uint(p.stage_val[s0[u] + lane]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (lane < ck[u]) {
+                p.agg_idx[d0[u] + lane] = vi[u];
+                if (p.D == 1) p.agg_val[d0[u] + lane] = __uint_as_float(vv[u]);
+            }
+            for (uint32_t i = SG_WAVE + lane; i < ck[u]; i += SG_WAVE) { // tiles with more than 64 keys
+                p.agg_idx[d0[u] + i] = p.stage_idx[s0[u] + i];
+                if (p.D == 1) p.agg_val[d0[u] + i] = p.stage_val[s0[u] + i];
+            }
+            if (p.D > 1) {
+                const uint64_t cnt = (uint64_t)ck[u] * p.D;
+                for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[d0[u] * p.D + i] = p.stage_val[s0[u] * p.D + i];
+            }
+        }
+    }
     }
 }
 

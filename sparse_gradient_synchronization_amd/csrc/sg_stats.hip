@@ -25,30 +25,44 @@ struct StatsCounts {
 __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, StatsCounts c)
 {
     __shared__ uint32_t hc[256], hh[256];
-    const uint32_t R = p.n;
-    const uint32_t ch = blockIdx.x;
-    if (ch >= p.chunk_start[R]) return;
-    uint32_t lo = 0, hi = R;
-    while (lo + 1 < hi) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (p.chunk_start[mid] <= ch) lo = mid;
-        else hi = mid;
-    }
-    const uint32_t w = lo;
     for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
     __syncthreads();
-    uint64_t s, e;
-    run_range(p, 0, w, s, e);
-    const uint64_t j0 = (uint64_t)(ch - p.chunk_start[w]) * MG_CHUNK;
-    for (uint64_t j = j0 + threadIdx.x; j < j0 + MG_CHUNK && s + j < e; j += MG_THREADS) {
-        const uint32_t key = p.idx[s + j];
-        atomicAdd(&hc[contig_part(key, p.M, p.Ps, p.inv_m)], 1u);
-        if (p.hashed) atomicAdd(&hh[h0(key, p.seed, p.div)], 1u);
-    }
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
-        if (hc[i]) atomicAdd((unsigned long long*)&c.wcontig[(uint64_t)w * p.Ps + i], (unsigned long long)hc[i]);
-        if (p.hashed && hh[i]) atomicAdd((unsigned long long*)&c.whashed[(uint64_t)w * p.Ps + i], (unsigned long long)hh[i]);
+    for (uint32_t ch = blockIdx.x; ch < p.nchunks_max; ch += gridDim.x) {
+        const uint4 rec = p.chunk_rec[ch];
+        if (rec.x == 0xffffffffu) continue;
+        const uint32_t w = rec.x; // one group: the run is the worker
+        const uint64_t s = rec.w, e = (uint64_t)rec.w + rec.z;
+        const uint64_t j0 = rec.y;
+        constexpr int U = 4; // loads in flight per thread
+        for (uint64_t jb = j0; jb < j0 + MG_CHUNK; jb += U * MG_THREADS) { // block-uniform trip count
+            uint32_t key[U];
+            bool has[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t j = jb + u * MG_THREADS + threadIdx.x;
+                has[u] = s + j < e;
+                key[u] = has[u] ? p.idx[s + j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                count_sorted_parts(hc, has[u] ? contig_part(key[u], p.M, p.Ps, p.inv_m) : 0u, has[u]);
+                if (p.hashed && has[u]) atomicAdd(&hh[h0(key[u], p.seed, p.div)], 1u);
+            }
+        }
+        // flush when the next chunk of this block belongs to another worker (or there is none)
+        const uint32_t nc = ch + gridDim.x;
+        const uint4 nrec = nc < p.nchunks_max ? p.chunk_rec[nc] : make_uint4(0xffffffffu, 0u, 0u, 0u);
+        if (nrec.x != w) {
+            __syncthreads();
+            for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
+                if (hc[i]) atomicAdd((unsigned long long*)&c.wcontig[(uint64_t)w * p.Ps + i], (unsigned long long)hc[i]);
+                if (p.hashed && hh[i])
+                    atomicAdd((unsigned long long*)&c.whashed[(uint64_t)w * p.Ps + i], (unsigned long long)hh[i]);
+            }
+            __syncthreads();
+            for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
+            __syncthreads();
+        }
     }
 }
 
@@ -147,7 +161,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     if (rc) return rc;
     rc = merge_run(p, MODE_STATS, st, k.row);
     if (rc) return rc;
-    st_entries_kernel<<<(unsigned)(ceil_div(total, MG_CHUNK) + n), MG_THREADS, 0, st>>>(p, k);
+    st_entries_kernel<<<p.nchunks_max < 2048 ? p.nchunks_max : 2048, MG_THREADS, 0, st>>>(p, k);
     SG_TRY_LAUNCH();
 
     std::vector<uint64_t> row(p.st_row), wc((size_t)n * P), wh((size_t)n * P), off(n + 1);

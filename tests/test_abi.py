@@ -95,7 +95,8 @@ def test_encode_words_cover_every_class(L):
     for M in (1, 31, 32, 33, 1000, 1 << 20):
         for P in (1, 2, 7, 16, 256):
             assert L.sg_encode_max_words(M, P) * 32 >= M + 31 * P
-    assert L.sg_encode_workspace_bytes(1 << 20, 8) == 0
+    # one 8-byte cursor per (key window, partition), windows of at most 4096 keys
+    assert L.sg_encode_workspace_bytes(1 << 20, 8) >= 8 * 8 * ((1 << 20) // 4096 + 1)
 
 
 def test_workspace_sizes_monotone(L):
@@ -143,10 +144,13 @@ def test_encode_host_checks(L):
     assert L.sg_classmap_build(M, P, 1, F, cb - 1, N) == SG_ECAPACITY
     assert L.sg_classmap_build(M, 0, 1, F, cb, N) == SG_EINVAL
     assert L.sg_classmap_build(1 << 32, P, 1, F, 1 << 40, N) == SG_EINVAL
-    assert L.sg_encode(F, F, 100, M, P, F, cb, F, mw - 1, F, N, 0, N) == SG_ECAPACITY
-    assert L.sg_encode(F, F, 100, M, P, F, cb - 1, F, mw, F, N, 0, N) == SG_ECAPACITY
-    assert L.sg_encode(F, F, 100, M, P, N, cb, F, mw, F, N, 0, N) == SG_EINVAL
-    assert L.sg_encode(F, F, 100, M, 257, F, 1 << 40, F, 1 << 40, F, N, 0, N) == SG_EINVAL
+    ew = L.sg_encode_workspace_bytes(M, P)
+    assert L.sg_encode(F, F, 100, M, P, F, cb, F, mw - 1, F, F, ew, N) == SG_ECAPACITY
+    assert L.sg_encode(F, F, 100, M, P, F, cb - 1, F, mw, F, F, ew, N) == SG_ECAPACITY
+    assert L.sg_encode(F, F, 100, M, P, F, cb, F, mw, F, F, ew - 1, N) == SG_ECAPACITY
+    assert L.sg_encode(F, F, 100, M, P, N, cb, F, mw, F, F, ew, N) == SG_EINVAL
+    assert L.sg_encode(F, F, 100, M, P, F, cb, F, mw, F, N, ew, N) == SG_EINVAL
+    assert L.sg_encode(F, F, 100, M, 257, F, 1 << 40, F, 1 << 40, F, F, 1 << 40, N) == SG_EINVAL
 
 
 def test_skip_rs_host_checks(L):
