@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "libsgoracle.so")
 F32, BF16 = 0, 1
 
 _u32p = np.ctypeslib.ndpointer(dtype=np.uint32, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _u64p = np.ctypeslib.ndpointer(dtype=np.uint64, flags="C_CONTIGUOUS")
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
@@ -90,6 +91,10 @@ def lib():
         L.orc_encode.argtypes = [_u32p, _u64p, C.c_uint32, C.c_uint64, C.c_uint32, _u32p, _u64p]
         L.orc_decode.restype = C.c_int
         L.orc_decode.argtypes = [_u32p, C.c_uint32, C.c_uint64, C.c_uint32, _u32p, _u64p]
+        L.orc_scatter_dense.restype = C.c_int
+        L.orc_scatter_dense.argtypes = [_u32p, _f32p, C.c_uint32, _u64p, C.c_uint32, C.c_uint64, _f32p]
+        L.orc_format_sizes.restype = C.c_int
+        L.orc_format_sizes.argtypes = [_u32p, _u64p, C.c_uint32, C.c_uint64, C.c_uint32, C.c_uint32, _u64p]
         L.orc_skip_threshold.restype = C.c_uint32
         L.orc_skip_threshold.argtypes = [C.c_double]
         L.orc_skip_mask.restype = C.c_int
@@ -262,6 +267,39 @@ def decode(bitmap: np.ndarray, P: int, M: int, seed: int):
     off = np.zeros(P + 1, dtype=np.uint64)
     _check(lib().orc_decode(bitmap, P, M, seed, out, off), "decode")
     return out[: int(off[P])].copy(), off
+
+
+def scatter_dense(idx: np.ndarray, val: np.ndarray, off: np.ndarray, M: int, D: int = 1):
+    """Pull-side scatter (Zen sections 3.1, 3.3.2): dense [M] (or [M, D])
+    zero except the aggregated indices, which take their values."""
+    idx = np.ascontiguousarray(idx, dtype=np.uint32)
+    val = np.ascontiguousarray(val, dtype=np.float32).reshape(-1)
+    off = np.ascontiguousarray(off, dtype=np.uint64)
+    if idx.size == 0:
+        idx = np.zeros(1, dtype=np.uint32)
+    if val.size == 0:
+        val = np.zeros(1, dtype=np.float32)
+    P = off.size - 1
+    out = np.zeros(max(M * max(D, 1), 1), dtype=np.float32)
+    _check(lib().orc_scatter_dense(idx, val, D, off, P, M, out), "scatter_dense")
+    out = out[: M * max(D, 1)]
+    return out if D <= 1 else out.reshape(M, D)
+
+
+FORMAT_NAMES = ("dense", "coo", "block", "bitmap", "hash_bitmap", "union", "nonempty_blocks")
+
+
+def format_sizes(agg_idx: np.ndarray, agg_off: np.ndarray, M: int, D: int, seed: int) -> dict:
+    """Bytes of an aggregate under the formats of Zen sections 3.3.1-3.3.2
+    (dense, COO, 256-gradient tensor blocks, contiguous-range bitmap, hash
+    bitmap), plus |I| and the number of non-empty blocks."""
+    agg_idx = np.ascontiguousarray(agg_idx, dtype=np.uint32)
+    if agg_idx.size == 0:
+        agg_idx = np.zeros(1, dtype=np.uint32)
+    agg_off = np.ascontiguousarray(agg_off, dtype=np.uint64)
+    out = np.zeros(7, dtype=np.uint64)
+    _check(lib().orc_format_sizes(agg_idx, agg_off, agg_off.size - 1, M, D, seed, out), "format_sizes")
+    return {k: int(v) for k, v in zip(FORMAT_NAMES, out)}
 
 
 def skip_threshold(p: float) -> int:

@@ -473,6 +473,85 @@ done:
     return rc;
 }
 
+/* Pull-side scatter ([Zen] section 3.1: after Pull every worker holds the
+ * aggregated gradient; section 3.3.2: the decoded indices select where the
+ * received values go).  The dense [M][D] tensor is zero except at the
+ * aggregated indices, which receive their aggregated values, copied as they
+ * are.  Entries [off[0], off[P]) of idx/val are scattered. */
+int orc_scatter_dense(const uint32_t* idx, const float* val, uint32_t D, const uint64_t* off, uint32_t P,
+                      uint64_t M, float* dense)
+{
+    uint64_t i, c;
+    if (P == 0) return ORC_EINVAL;
+    memset(dense, 0, M * (D ? D : 1) * sizeof(float));
+    for (i = off[0]; i < off[P]; ++i) {
+        if (idx[i] >= M) return ORC_EINCONSISTENT;
+        for (c = 0; c < D; ++c) dense[(uint64_t)idx[i] * D + c] = val[i * D + c];
+    }
+    return ORC_OK;
+}
+
+/* Encoded size of an aggregate under the sparse formats of [Zen] section
+ * 3.3.1 and the hash bitmap of section 3.3.2, in bytes, with 4-byte indices
+ * and D fp32 values per index:
+ *   dense        M * 4D
+ *   coo          |I| * (4 + 4D)
+ *   block        tensor blocks of 256 gradients (OmniReduce): every block of
+ *                [0, M) holding an aggregated index sends its 256 * D values
+ *                and a 4-byte block id
+ *   bitmap       each of the P servers owns the contiguous range
+ *                [floor(iM/P), floor((i+1)M/P)) and sends a bitmap of it,
+ *                ceil(len_i / 32) words, plus the values
+ *   hash_bitmap  server p's bitmap covers its class C_p, ceil(|C_p| / 32)
+ *                words, plus the values
+ * Reading: the block format is taken over the whole aggregated tensor (what
+ * one worker receives in Pull), the last block of [0, M) counting as a full
+ * block of 256.  out[0..5] = dense, coo, block, bitmap, hash_bitmap, |I|;
+ * out[6] = the number of non-empty blocks. */
+int orc_format_sizes(const uint32_t* agg_idx, const uint64_t* agg_off, uint32_t P, uint64_t M, uint32_t D,
+                     uint32_t seed, uint64_t* out)
+{
+    uint64_t i, U, nb, nblocks = 0, bitmap_words = 0, hash_words = 0;
+    uint8_t* used;
+    uint64_t* csize;
+    uint32_t p;
+    if (P == 0 || M > 0xffffffffull) return ORC_EINVAL;
+    nb = (M + 255) / 256;
+    used = (uint8_t*)calloc(nb ? nb : 1, 1);
+    csize = (uint64_t*)calloc(P, sizeof(uint64_t));
+    if (!used || !csize) {
+        free(used);
+        free(csize);
+        return ORC_ENOMEM;
+    }
+    U = agg_off[P] - agg_off[0];
+    for (i = agg_off[0]; i < agg_off[P]; ++i) {
+        if (agg_idx[i] >= M) {
+            free(used);
+            free(csize);
+            return ORC_EINCONSISTENT;
+        }
+        used[agg_idx[i] / 256] = 1;
+    }
+    for (i = 0; i < nb; ++i) nblocks += used[i];
+    for (p = 0; p < P; ++p) {
+        uint64_t lo = (uint64_t)(((unsigned __int128)M * p) / P), hi = (uint64_t)(((unsigned __int128)M * (p + 1)) / P);
+        bitmap_words += (hi - lo + 31) / 32;
+    }
+    for (i = 0; i < M; ++i) csize[orc_h0((uint32_t)i, seed, P)]++;
+    for (p = 0; p < P; ++p) hash_words += (csize[p] + 31) / 32;
+    out[0] = M * 4ull * D;
+    out[1] = U * (4ull + 4ull * D);
+    out[2] = nblocks * (256ull * 4ull * D + 4ull);
+    out[3] = bitmap_words * 4ull + U * 4ull * D;
+    out[4] = hash_words * 4ull + U * 4ull * D;
+    out[5] = U;
+    out[6] = nblocks;
+    free(used);
+    free(csize);
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* A5: ring reduce-scatter arithmetic with slice skipping                    */
 /* ------------------------------------------------------------------------ */

@@ -472,3 +472,93 @@ def test_config4_stats_closed_forms_scaled():
     bound = 1 + 6 * math.sqrt(P * math.log(P) / c)
     assert np.all(st["skew_hashed"] < bound) and st["push_imbalance"] < bound
     assert st["pull_imbalance"] < 1 + 6 * math.sqrt(P * math.log(P) / st["union_size"])
+
+
+# --------------------------------------------------------------------------
+# NEXT-1: Pull-side scatter to dense and encoded-size accounting
+# --------------------------------------------------------------------------
+
+def test_scatter_dense_places_values_and_zeros_elsewhere():
+    rng = np.random.default_rng(5)
+    M, P = 5000, 4
+    idx = np.sort(rng.choice(M, size=700, replace=False)).astype(np.uint32)
+    val = rng.standard_normal(700).astype(np.float32)
+    off = np.array([0, 100, 400, 400, 700], dtype=np.uint64)
+    dense = oracle.scatter_dense(idx, val, off, M)
+    assert dense.dtype == np.float32 and dense.shape == (M,)
+    assert np.array_equal(dense[idx].view(np.uint32), val.view(np.uint32))  # bit copies
+    rest = np.ones(M, bool)
+    rest[idx] = False
+    assert not np.any(dense[rest])
+    rows = rng.standard_normal((700, 3)).astype(np.float32)
+    dense3 = oracle.scatter_dense(idx, rows, off, M, D=3)
+    assert np.array_equal(dense3[idx], rows) and not np.any(dense3[rest])
+
+
+def test_scatter_of_aggregate_is_the_dense_allreduce():
+    # Zen section 3.2: the synchronized result equals the dense AllReduce; after
+    # Pull a worker's dense gradient is the sum of all workers' gradients
+    c = gen.config1(n=4, M=1 << 14)
+    n, M, P, seed = c["n"], c["M"], c["P"], c["seed"]
+    oi, ov, po = oracle.hash_partition(c["idx"], c["val"], c["in_off"], P, seed)
+    ai, av, aa, ao = oracle.aggregate(oi, ov, po, M)
+    dense = oracle.scatter_dense(ai, av, ao, M)
+    want = c["dense"].astype(np.float64).sum(axis=0)
+    tol = 1e-6 * np.abs(c["dense"].astype(np.float64)).sum(axis=0) + 1e-30
+    assert np.all(np.abs(dense.astype(np.float64) - want) <= tol)
+
+
+def test_format_sizes_against_page_examples():
+    g = _golden("zen_formats.json")
+    # density after aggregation: dense / values-only and dense / COO traffic
+    ex = g["coo_after_aggregation"]
+    M = 100_000
+    U = int(round(ex["density"] * M))
+    idx = np.arange(U, dtype=np.uint32) * (M // U)
+    s = oracle.format_sizes(np.sort(idx), np.array([0, U], np.uint64), M, 1, 7)
+    assert s["coo"] == U * 8 and s["dense"] == M * 4
+    assert round(s["dense"] / (U * 4), 1) == ex["values_only_reduction"]
+    assert round(s["dense"] / s["coo"], 1) == ex["coo_reduction"]
+    # contiguous bitmap: |G| = 15 over 3 servers
+    ex = g["contiguous_bitmap_example"]
+    s = oracle.format_sizes(np.zeros(0, np.uint32), np.zeros(ex["servers"] + 1, np.uint64), ex["G"], 1, 1)
+    assert s["bitmap"] == 4 * ex["words_per_server"] * ex["servers"]
+    # the hash bitmap of 15 indices over 3 classes: one word per non-empty class
+    assert s["hash_bitmap"] <= 4 * ex["servers"]
+
+
+def test_format_sizes_bitmaps_total_G_over_32():
+    # Zen sections 3.3.1-3.3.2: the bitmaps a worker receives add up to about
+    # |G|/32 words whatever the number of servers; the page's 856 MB table
+    g = _golden("zen_formats.json")["deepfm_bitmap"]
+    M = g["table_MB"] * 1_000_000 // 4
+    for P in (1, 8):
+        s = oracle.format_sizes(np.zeros(0, np.uint32), np.zeros(P + 1, np.uint64), M, 1, 2)
+        for fmt in ("bitmap", "hash_bitmap"):
+            assert M / 8 <= s[fmt] <= M / 8 + 4 * P
+            assert round(s[fmt] / 1e6) == g["bitmap_MB"]
+
+
+def test_format_sizes_brute_force_blocks_and_classes():
+    rng = np.random.default_rng(11)
+    for M, P, D in ((1000, 3, 1), (70_000, 8, 4), (256 * 40 + 13, 5, 2)):
+        U = M // 7
+        idx = np.sort(rng.choice(M, size=U, replace=False)).astype(np.uint32)
+        part = oracle.h0(idx, 9, P)
+        order = np.argsort(part, kind="stable")
+        idx = idx[order]
+        off = np.zeros(P + 1, np.uint64)
+        off[1:] = np.cumsum(np.bincount(part, minlength=P))
+        s = oracle.format_sizes(idx, off, M, D, 9)
+        blocks = np.unique(idx // 256).size
+        assert s["nonempty_blocks"] == blocks
+        assert s["block"] == blocks * (256 * 4 * D + 4)
+        csize = np.bincount(oracle.h0(np.arange(M, dtype=np.uint32), 9, P), minlength=P)
+        assert s["hash_bitmap"] == 4 * int(np.sum((csize + 31) // 32)) + U * 4 * D
+        bounds = [(M * i) // P for i in range(P + 1)]
+        assert s["bitmap"] == 4 * sum((bounds[i + 1] - bounds[i] + 31) // 32 for i in range(P)) + U * 4 * D
+        assert s["coo"] == U * (4 + 4 * D) and s["union"] == U
+    # full density: every block is used
+    M = 256 * 9 + 1
+    s = oracle.format_sizes(np.arange(M, dtype=np.uint32), np.array([0, M], np.uint64), M, 1, 3)
+    assert s["nonempty_blocks"] == 10
