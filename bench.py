@@ -157,6 +157,29 @@ def build_workload(name, torch, sg, gen):
                            ws_s.numel(), stream()), "sg_stats")
 
         stages += [("hash_partition", part), ("aggregate", agg), ("encode", enc), ("stats", stats)]
+
+        # the Pull side after the step (timed on its own, not part of the step)
+        dec_idx = torch.empty(total, dtype=torch.int32, device=dev)
+        dec_off = torch.empty(P + 1, dtype=torch.int64, device=dev)
+        ws_d = torch.empty(max(L.sg_decode_workspace_bytes(M, P), 1), dtype=torch.uint8, device=dev)
+        pull_dense = torch.empty((M, D) if D > 1 else (M,), dtype=torch.float32, device=dev)
+        ws_f = torch.empty(L.sg_format_sizes_workspace_bytes(M), dtype=torch.uint8, device=dev)
+
+        def dec():
+            chk(L.sg_decode(vp(bitmap), words, vp(cmap), cmap.numel(), M, P, vp(dec_idx), total, vp(dec_off), vp(ws_d),
+                            ws_d.numel(), stream()), "sg_decode")
+
+        def scat():
+            chk(L.sg_scatter_dense(vp(agg_idx), vp(agg_val), D, vp(agg_off), P, total, M, vp(pull_dense), stream()),
+                "sg_scatter_dense")
+
+        def fmt():
+            out = (C.c_uint64 * 7)()
+            chk(L.sg_format_sizes(vp(agg_idx), vp(agg_off), total, M, P, D, vp(cmap), cmap.numel(),
+                                  C.cast(out, C.c_void_p), vp(ws_f), ws_f.numel(), stream()), "sg_format_sizes")
+            return dict(zip(sg.FORMAT_NAMES, (int(v) for v in out)))
+        W["pull"] = [("decode", dec), ("scatter_dense", scat)]
+        W["format_sizes"] = fmt
         esz = 4 * D
         nbytes["hash_partition"] = 2 * total * (4 + esz)
         W["agg_off"] = agg_off
@@ -206,6 +229,8 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "hash_partition": (2, "part_scatter_kernel", ["sg_partition.hip"]),
     "aggregate": (3, "mg_merge_kernel", ["sg_merge.hip", "sg_aggregate.hip"]),
     "encode": (4, "enc_kernel", ["sg_encode.hip"]),
+    "decode": (9, "dec_emit_kernel", ["sg_decode.hip"]),
+    "scatter_dense": (10, "scatter_kernel", ["sg_decode.hip"]),
     "skip_reduce_scatter": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
 }
 COMMON_SOURCES = ["sg_device.h", "sg_host.h"]
@@ -271,6 +296,11 @@ def algorithmic_bytes(W, stage):
         return W["bytes_enc"](int(W["agg_off"][-1].item()), int(W["word_off"][-1].item()))
     if stage == "skip_reduce_scatter":
         return rs_bytes(W)
+    if stage == "decode":  # the bitmap words read, the indices written
+        return int(W["word_off"][-1].item()) * 4 + int(W["agg_off"][-1].item()) * 4
+    if stage == "scatter_dense":  # the scatter pass: the aggregate read, its values written in place
+        U = int(W["agg_off"][-1].item())
+        return U * (4 + 8 * W.get("D", 1))
     raise KeyError(stage)
 
 
@@ -294,6 +324,40 @@ def cpu_baseline(name, gen):
     return {"value": n * k / t, "unit": "nonzeros/s", "cores": 1, "kind": "oracle",
             "sample": "one full step of the workload (all six stages, full size), single-threaded C oracle",
             "seconds": round(t, 3)}
+
+
+def pull_side(W, L, torch, steps):
+    """Decode of the step's hash bitmap and the scatter of its aggregate into
+    a dense tensor, each timed alone (whole call with torch events, probed
+    kernel with HIP events), plus the aggregate's encoded sizes."""
+    out = {}
+    for nm, f in W["pull"]:
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        evs = [HipEvents() for _ in range(steps)]
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for s in range(steps):
+            L.sg_probe_set(PROBES[nm][0], evs[s].start, evs[s].stop)
+            a[s].record()
+            f()
+            b[s].record()
+        torch.cuda.synchronize()
+        L.sg_probe_set(0, None, None)
+        kms = sum(e.elapsed_ms() for e in evs) / steps
+        nbytes = algorithmic_bytes(W, nm)
+        gbps = nbytes / (kms * 1e-3) / 1e9
+        ms = sum(a[s].elapsed_time(b[s]) for s in range(steps)) / steps
+        out[nm] = {"ms": ms, "kernel": PROBES[nm][1], "kernel_ms": kms, "kernel_algorithmic_bytes": nbytes,
+                   "kernel_GBps": gbps, "kernel_frac": gbps / HBM_PEAK_GBS}
+        if nm == "scatter_dense":  # the whole call also zero-fills the dense tensor
+            U = int(W["agg_off"][-1].item())
+            call_bytes = W["M"] * 4 * W.get("D", 1) + U * (4 + 4 * W.get("D", 1))
+            out[nm]["call_algorithmic_bytes"] = call_bytes
+            out[nm]["call_GBps"] = call_bytes / (ms * 1e-3) / 1e9
+    out["format_sizes_bytes"] = W["format_sizes"]()
+    return out
 
 
 def main():
@@ -421,6 +485,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if "pull" in W:
+        res["pull_side"] = pull_side(W, L, torch, steps)
     if not args.no_cpu_baseline:
         log("timing the oracle (single-threaded) on one step")
         res["cpu_baseline"] = cpu_baseline(args.workload, gen)

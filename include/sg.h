@@ -14,6 +14,11 @@
  *   sg_skip_reduce_scatter  ring reduce-scatter arithmetic with seeded slice
  *                           skipping (SkipReduce / DropReduce)
  *   sg_stats                overlap, densification and skew ratios
+ *   sg_decode,
+ *   sg_scatter_dense,
+ *   sg_format_sizes         the Pull side: hash bitmap back to indices, the
+ *                           aggregate scattered into a dense tensor, and the
+ *                           aggregate's size under the sparse formats
  *
  * Sources: "Zen: Empowering Distributed Training with Sparsity-driven Data
  * Synchronization" (OSDI'25) digest page [Zen]; "SkipReduce: (Interconnection)
@@ -96,7 +101,9 @@ typedef enum sg_probe_kernel {
     SG_PROBE_SKIP_RS = 5,            /* skip reduce-scatter: its single kernel */
     SG_PROBE_AGGREGATE_BND = 6,      /* aggregate: the bucket-boundary pass */
     SG_PROBE_PARTITION_HIST = 7,     /* hash partition: the histogram pass */
-    SG_PROBE_TOPK_WRITE = 8          /* top-k: the ordered write */
+    SG_PROBE_TOPK_WRITE = 8,         /* top-k: the ordered write */
+    SG_PROBE_DECODE = 9,             /* decode: the pass that emits the indices */
+    SG_PROBE_SCATTER = 10            /* scatter to dense: the scatter pass */
 } sg_probe_kernel;
 int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
 
@@ -199,6 +206,53 @@ size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P);
 int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg_capacity, uint64_t M, uint32_t P,
               const void* d_cmap, size_t cmap_bytes, uint32_t* d_bitmap, uint64_t bitmap_words, uint64_t* d_word_off, void* d_ws,
               size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Pull side of A4 (after the aggregate and its encoding).
+ * [Zen] section 3.3.2 (hash_bitmap_decode: the set bits of server p's bitmap
+ * are ranks in C_p, and C_p[rank] is the global index); section 3.1 (after
+ * Pull every worker holds the aggregate); section 3.3.1 (the sparse formats
+ * the hash bitmap is compared with).
+ *
+ * sg_decode: bitmap and layout as written by sg_encode for the same (M, P,
+ * class map).  Outputs, per class p in order, the indices C_p[b] of the set
+ * bits b in ascending order:
+ *   d_out_idx  [capacity] uint32 out (capacity >= the number of set bits;
+ *              the aggregate's size is enough; extra indices are dropped)
+ *   d_out_off  [P+1] uint64 out: class p is [out_off[p], out_off[p+1])
+ *   d_ws       sg_decode_workspace_bytes(M, P) bytes
+ * Limits: 1 <= P <= 256, 1 <= M < 2^32.
+ *
+ * sg_scatter_dense: d_dense [M][D] fp32 out (16-byte aligned) becomes zero
+ * except at the entries [off[0], off[P]) of (d_idx, d_val [][D]), whose
+ * values are copied to their index (for an aggregate: off = agg_off).
+ * capacity is the number of entries d_idx holds (offsets are clamped to it).
+ * D == 0 only zeroes.  Indices must be distinct and below M (an index >= M is
+ * skipped and recorded for sg_device_error).
+ *
+ * sg_format_sizes: bytes of an aggregate (d_agg_idx, d_agg_off as produced
+ * by sg_aggregate) with D fp32 values per index and 4-byte indices, written
+ * to h_out[7] (host):
+ *   [0] dense        M * 4D
+ *   [1] coo          |I| * (4 + 4D)
+ *   [2] block        256-gradient tensor blocks over [0, M) holding an
+ *                    aggregated index, each 256 * 4D + a 4-byte block id
+ *   [3] bitmap       P contiguous ranges [floor(iM/P), floor((i+1)M/P)),
+ *                    ceil(len/32) words each, plus the values
+ *   [4] hash_bitmap  sum over classes of ceil(|C_p|/32) words, plus the values
+ *   [5] |I|, [6] the number of non-empty blocks
+ * Blocks on `stream`.  d_ws: sg_format_sizes_workspace_bytes(M).
+ * ------------------------------------------------------------------------ */
+size_t sg_decode_workspace_bytes(uint64_t M, uint32_t P);
+int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const void* d_cmap, size_t cmap_bytes, uint64_t M,
+              uint32_t P, uint32_t* d_out_idx, uint64_t capacity, uint64_t* d_out_off, void* d_ws, size_t ws_bytes,
+              void* stream);
+int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint32_t D, const uint64_t* d_off, uint32_t P,
+                     uint64_t capacity, uint64_t M, float* d_dense, void* stream);
+size_t sg_format_sizes_workspace_bytes(uint64_t M);
+int sg_format_sizes(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t capacity, uint64_t M, uint32_t P,
+                    uint32_t D, const void* d_cmap, size_t cmap_bytes, uint64_t* h_out, void* d_ws, size_t ws_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------------------
  * A5. Ring reduce-scatter arithmetic with slice skipping.

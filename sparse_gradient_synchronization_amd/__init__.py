@@ -70,6 +70,11 @@ SIGNATURES = {
     "sg_skip_num_slices": (_u64, [_u32, _u64, _u64, _int]),
     "sg_skip_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _u64, _dbl, _u64, _vp, _int, _vp, _vp, _vp]),
     "sg_stats_workspace_bytes": (_sz, [_u32, _u64, _u64, _u32]),
+    "sg_decode_workspace_bytes": (_sz, [_u64, _u32]),
+    "sg_decode": (_int, [_vp, _u64, _vp, _sz, _u64, _u32, _vp, _u64, _vp, _vp, _sz, _vp]),
+    "sg_scatter_dense": (_int, [_vp, _vp, _u32, _vp, _u32, _u64, _u64, _vp, _vp]),
+    "sg_format_sizes_workspace_bytes": (_sz, [_u64]),
+    "sg_format_sizes": (_int, [_vp, _vp, _u64, _u64, _u32, _u32, _vp, _sz, _vp, _vp, _sz, _vp]),
     "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, _sz, C.POINTER(StatsOut), _vp, _sz, _vp]),
 }
 
@@ -226,6 +231,51 @@ def sg_encode(agg_idx: torch.Tensor, agg_off: torch.Tensor, M: int, cmap: torch.
                            cmap.numel(), _p(bitmap), words,
                            _p(word_off), _p(ws), ws.numel(), _stream()), "sg_encode")
     return bitmap, word_off
+
+
+def sg_decode(bitmap: torch.Tensor, M: int, P: int, cmap: torch.Tensor, capacity: int | None = None,
+              workspace: torch.Tensor | None = None):
+    """Hash bitmap -> (indices [capacity] int32 holding uint32, off [P+1] int64);
+    class p's indices are idx[off[p]:off[p+1]], ascending."""
+    _need_cuda(bitmap, cmap)
+    cap = int(capacity) if capacity is not None else int(M)
+    out = torch.empty(max(cap, 1), dtype=torch.int32, device=bitmap.device)
+    off = torch.empty(P + 1, dtype=torch.int64, device=bitmap.device)
+    need = lib().sg_decode_workspace_bytes(M, P)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, bitmap.device)
+    bm = bitmap.contiguous()
+    _check(lib().sg_decode(_p(bm), bm.numel(), _p(cmap), cmap.numel(), M, P, _p(out), cap, _p(off), _p(ws),
+                           ws.numel(), _stream()), "sg_decode")
+    return out, off
+
+
+def sg_scatter_dense(idx: torch.Tensor, val, off: torch.Tensor, M: int, D: int = 1, out: torch.Tensor | None = None):
+    """Dense [M] (or [M, D]) fp32: zero except idx[off[0]:off[P]] <- val."""
+    _need_cuda(idx, off)
+    P = off.numel() - 1
+    dense = out if out is not None else torch.empty((M, D) if D > 1 else (max(M, 1),), dtype=torch.float32,
+                                                        device=idx.device)
+    v = None if val is None else _contig(val.float())
+    _check(lib().sg_scatter_dense(_p(idx.contiguous()), _p(v), D, _p(off.contiguous()), P, idx.numel(), M,
+                                  _p(dense), _stream()), "sg_scatter_dense")
+    return dense
+
+
+FORMAT_NAMES = ("dense", "coo", "block", "bitmap", "hash_bitmap", "union", "nonempty_blocks")
+
+
+def sg_format_sizes(agg_idx: torch.Tensor, agg_off: torch.Tensor, M: int, D: int, cmap: torch.Tensor) -> dict:
+    """Bytes of the aggregate as dense, COO, 256-gradient blocks, contiguous
+    bitmaps and hash bitmaps (and |I|, the non-empty blocks)."""
+    _need_cuda(agg_idx, agg_off, cmap)
+    P = agg_off.numel() - 1
+    need = lib().sg_format_sizes_workspace_bytes(M)
+    ws = _ws(need, agg_idx.device)
+    out = (C.c_uint64 * 7)()
+    _check(lib().sg_format_sizes(_p(agg_idx.contiguous()), _p(agg_off.contiguous()), agg_idx.numel(), M, P, D,
+                                 _p(cmap), cmap.numel(), C.cast(out, C.c_void_p), _p(ws), ws.numel(), _stream()),
+           "sg_format_sizes")
+    return {k: int(v) for k, v in zip(FORMAT_NAMES, out)}
 
 
 def sg_skip_num_slices(n: int, M: int, slice_bytes: int, dtype=torch.float32) -> int:

@@ -1,0 +1,501 @@
+// sg_decode.hip -- the Pull side after A4 (Zen OSDI'25 digest, section
+// 3.3.2, hash_bitmap_decode; section 3.1, every worker holds the aggregate
+// after Pull): hash bitmap back to indices, the scatter of aggregated values
+// into a dense tensor, and the encoded size of an aggregate under the formats
+// of section 3.3.1.
+//
+// Decode, on gfx950: the class map's key windows again.
+//   count  per (window, class), the set bits of the class's bitmap inside the
+//          window's bit range (the bits of class members that fall in it);
+//   scan   per class, an exclusive scan over the windows; the class totals
+//          give the output offsets;
+//   emit   a block per window builds the class masks of its chunks and their
+//          per-class prefixes in LDS (as encode does), numbers the set bits
+//          of the window's bitmap words with a block scan, and maps every set
+//          bit b of class p back to its key: the (b - first)-th class-p
+//          member of the window, found by a search over the chunk prefixes
+//          and a select inside the chunk's 32-bit class mask.
+#include "sg_host.h"
+
+namespace sg {
+
+struct DecParams {
+    CmapLayout L;
+    CmapPtrs q;
+    const uint32_t* bitmap;
+    uint64_t bitmap_words;
+    uint32_t* out_idx;
+    uint64_t capacity;
+    uint64_t* out_off;  // [P+1]
+    uint32_t* cnt;      // [NW][P] set bits per (window, class), then their exclusive prefix per class
+    uint64_t* tot;      // [P] set bits per class
+};
+
+// set bits of class p's words in bit range [a, b)
+__device__ __forceinline__ uint32_t range_popc(const DecParams& d, uint32_t p, uint32_t a, uint32_t b)
+{
+    if (b <= a) return 0;
+    const uint64_t base = d.q.word_off[p];
+    uint32_t c = 0;
+    for (uint32_t w = a >> 5; w <= (b - 1) >> 5; ++w) {
+        if (base + w >= d.bitmap_words) break;
+        uint32_t v = d.bitmap[base + w];
+        const uint32_t lo = w * 32 < a ? a - w * 32 : 0u;
+        const uint32_t hi = (w + 1) * 32 > b ? b - w * 32 : 32u;
+        if (hi < 32) v &= (1u << hi) - 1u;
+        v &= ~((1u << lo) - 1u);
+        c += __popc(v);
+    }
+    return c;
+}
+
+__global__ __launch_bounds__(256) void dec_count_kernel(DecParams d)
+{
+    const uint32_t P = d.L.P;
+    const uint64_t cells = d.L.NW * P;
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < cells; i += (uint64_t)gridDim.x * 256) {
+        const uint64_t w = i / P;
+        const uint32_t p = (uint32_t)(i % P);
+        d.cnt[i] = range_popc(d, p, d.q.cpre[w * P + p], d.q.cpre[(w + 1) * P + p]);
+    }
+}
+
+// one block per class: exclusive prefix of the window counts, in place
+__global__ __launch_bounds__(1024) void dec_scan_kernel(DecParams d)
+{
+    constexpr uint32_t PT = 8;
+    __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
+    const uint32_t P = d.L.P, p = blockIdx.x;
+    const uint64_t NW = d.L.NW;
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < NW; base += 1024 * PT) {
+        const uint64_t w0 = base + (uint64_t)threadIdx.x * PT;
+        uint32_t c[PT], sum = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < PT; ++j) {
+            c[j] = w0 + j < NW ? d.cnt[(w0 + j) * P + p] : 0u;
+            sum += c[j];
+        }
+        uint32_t tot;
+        uint32_t ex = block_excl_scan<1024>(sum, scan_lds, &tot);
+#pragma unroll
+        for (uint32_t j = 0; j < PT; ++j) {
+            if (w0 + j < NW) d.cnt[(w0 + j) * P + p] = (uint32_t)(carry + ex); // within a class: below 2^32
+            ex += c[j];
+        }
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) d.tot[p] = carry;
+}
+
+__global__ __launch_bounds__(256) void dec_off_kernel(DecParams d)
+{
+    __shared__ uint64_t scan_lds[256 / SG_WAVE + 1];
+    const uint32_t P = d.L.P;
+    const uint64_t v = threadIdx.x < P ? d.tot[threadIdx.x] : 0ull;
+    uint64_t all;
+    const uint64_t ex = block_excl_scan64<256>(v, scan_lds, &all);
+    if (threadIdx.x < P) d.out_off[threadIdx.x] = ex;
+    if (threadIdx.x == 0) d.out_off[P] = all;
+}
+
+// position of the k-th set bit (k from 0) of v, which has more than k set bits
+__device__ __forceinline__ uint32_t select_bit(uint32_t v, uint32_t k)
+{
+    uint32_t pos = 0;
+#pragma unroll
+    for (uint32_t half = 16; half > 0; half >>= 1) {
+        const uint32_t c = __popc(v & ((1u << half) - 1u));
+        if (k >= c) {
+            k -= c;
+            v >>= half;
+            pos += half;
+        }
+    }
+    return pos;
+}
+
+constexpr int DC_THREADS = 256;
+constexpr int DC_WORDS = 512; // a window's bitmap words: at most W/32 + P <= 128 + 256
+
+__global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
+{
+    __shared__ uint32_t masks[2048]; // [NCW][P]
+    __shared__ uint16_t pre[2048];   // [NCW][P]
+    __shared__ uint32_t segofs[257], a_bits[256], b_bits[256], cls_first[256];
+    __shared__ uint32_t wex[DC_WORDS];
+    __shared__ uint32_t scan_lds[DC_THREADS / SG_WAVE + 1];
+    const CmapLayout& L = d.L;
+    const uint32_t P = L.P, NCW = L.NCW;
+    const uint64_t win = blockIdx.x;
+    const uint32_t lane = lane_id();
+
+    uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t valid = 0;
+    if (threadIdx.x < NCW) {
+        const uint64_t c = win * NCW + threadIdx.x;
+        valid = c < L.NC ? (L.M - c * 32 >= 32 ? 0xffffffffu : ((1u << (L.M - c * 32)) - 1u)) : 0u;
+        if (valid)
+            for (uint32_t b = 0; b < L.nbits; ++b) pl[b] = d.q.planes[c * L.stride + b];
+    }
+    uint32_t nw = 0;
+    if (threadIdx.x < P) {
+        const uint32_t p = threadIdx.x;
+        const uint32_t ca = d.q.cpre[win * P + p], cb = d.q.cpre[(win + 1) * P + p];
+        a_bits[p] = ca;
+        b_bits[p] = cb;
+        nw = cb > ca ? ((cb - 1) >> 5) - (ca >> 5) + 1 : 0u;
+    }
+    uint32_t nseg;
+    const uint32_t so = block_excl_scan<DC_THREADS>(nw, scan_lds, &nseg);
+    if (threadIdx.x < P) segofs[threadIdx.x] = so;
+    if (threadIdx.x == 0) segofs[P] = nseg;
+    // class masks of the window's chunks by plane splitting (as in encode)
+    if (threadIdx.x < NCW) {
+        uint32_t* mrow = masks + threadIdx.x * P;
+        uint32_t m[16];
+        if (L.nbits <= 4) {
+            m[0] = valid;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if ((uint32_t)b < L.nbits) {
+#pragma unroll
+                    for (int k = (1 << b) - 1; k >= 0; --k) {
+                        m[k + (1 << b)] = m[k] & pl[b];
+                        m[k] &= ~pl[b];
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if ((uint32_t)k < P) mrow[k] = m[k];
+        } else {
+            for (uint32_t p = 0; p < P; ++p) {
+                uint32_t v = valid;
+                for (uint32_t b = 0; b < L.nbits; ++b) v &= ((p >> b) & 1u) ? pl[b] : ~pl[b];
+                mrow[p] = v;
+            }
+        }
+    }
+    __syncthreads();
+    if (nseg > DC_WORDS) { // cannot happen: at most W/32 + P words
+        if (threadIdx.x == 0) report_error(kDevErrCmap);
+        return;
+    }
+    // per-class prefix over the window's chunks: P segments of NCW, 8 per
+    // thread, segmented scan inside a DPP row (NCW/8 <= 16 threads)
+    {
+        const uint32_t e0 = threadIdx.x * 8;
+        uint32_t c[8], run = 0;
+        const bool act = e0 < NCW * P;
+        const uint32_t p = act ? e0 / NCW : 0u, t0 = act ? e0 % NCW : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = act ? __popc(masks[(t0 + j) * P + p]) : 0u;
+            run += c[j];
+        }
+        const uint32_t sg = NCW / 8;
+        const uint32_t inrow = lane & 15u;
+        uint32_t inc = run, x;
+        x = dpp_move<kDppRowShr1>(0u, inc);
+        if (sg > 1 && (inrow & (sg - 1)) >= 1) inc += x;
+        x = dpp_move<kDppRowShr2>(0u, inc);
+        if (sg > 2 && (inrow & (sg - 1)) >= 2) inc += x;
+        x = dpp_move<kDppRowShr4>(0u, inc);
+        if (sg > 4 && (inrow & (sg - 1)) >= 4) inc += x;
+        x = dpp_move<kDppRowShr8>(0u, inc);
+        if (sg > 8 && (inrow & (sg - 1)) >= 8) inc += x;
+        if (act) {
+            uint32_t ex = inc - run;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pre[(t0 + j) * P + p] = (uint16_t)ex;
+                ex += c[j];
+            }
+        }
+    }
+    // the window's words (class-major), their set bits inside the ranges, and
+    // a block scan numbering them
+    uint32_t wv[2], wp[2], wc[2], sum = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t i = threadIdx.x * 2 + h;
+        wv[h] = 0;
+        wp[h] = 0;
+        wc[h] = 0;
+        if (i < nseg) {
+            uint32_t lo = 0, hi = P; // class of word i
+            while (lo + 1 < hi) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (segofs[mid] <= i) lo = mid;
+                else hi = mid;
+            }
+            const uint32_t p = lo, a = a_bits[p], b = b_bits[p];
+            const uint32_t qw = (a >> 5) + (i - segofs[p]);
+            const uint64_t gw = d.q.word_off[p] + qw;
+            uint32_t v = gw < d.bitmap_words ? d.bitmap[gw] : 0u;
+            const uint32_t lo_b = qw * 32 < a ? a - qw * 32 : 0u;
+            const uint32_t hi_b = (qw + 1) * 32 > b ? b - qw * 32 : 32u;
+            if (hi_b < 32) v &= (1u << hi_b) - 1u;
+            v &= ~((1u << lo_b) - 1u);
+            wv[h] = v;
+            wp[h] = p;
+            wc[h] = __popc(v);
+        }
+        sum += wc[h];
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<DC_THREADS>(sum, scan_lds, &tot);
+    {
+        uint32_t e = ex;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t i = threadIdx.x * 2 + h;
+            if (i < DC_WORDS) wex[i] = e;
+            e += wc[h];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < P) cls_first[threadIdx.x] = segofs[threadIdx.x] < nseg ? wex[segofs[threadIdx.x]] : tot;
+    __syncthreads();
+    // every set bit back to its key
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t i = threadIdx.x * 2 + h;
+        if (i >= nseg) continue;
+        const uint32_t p = wp[h], a = a_bits[p];
+        const uint32_t qw = (a >> 5) + (i - segofs[p]);
+        uint64_t o = d.out_off[p] + d.cnt[win * P + p] + (wex[i] - cls_first[p]);
+        uint32_t v = wv[h];
+        while (v) {
+            const uint32_t bit = __ffs(v) - 1u;
+            v &= v - 1u;
+            const uint32_t m = qw * 32 + bit - a; // member of class p inside the window
+            uint32_t lo = 0, hi = NCW;            // chunk: last t with pre[t][p] <= m
+            while (lo + 1 < hi) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (pre[mid * P + p] <= m) lo = mid;
+                else hi = mid;
+            }
+            const uint32_t mk = masks[lo * P + p];
+            const uint32_t k = m - pre[lo * P + p];
+            if (k >= (uint32_t)__popc(mk)) { // bit past the class: cannot happen with the class map's prefixes
+                report_error(kDevErrCmap);
+                ++o;
+                continue;
+            }
+            const uint64_t key = win * L.W + (uint64_t)lo * 32 + select_bit(mk, k);
+            if (o < d.capacity) d.out_idx[o] = (uint32_t)key;
+            ++o;
+        }
+    }
+}
+
+// Pull-side scatter: dense [M][D] zero except entries [off[0], off[P])
+struct ScatterParams {
+    const uint32_t* idx;
+    const float* val;
+    const uint64_t* off;
+    uint32_t P, D;
+    uint64_t capacity, M;
+    float* dense;
+};
+
+__global__ __launch_bounds__(256) void scatter_zero_kernel(ScatterParams s)
+{
+    const uint64_t words = s.M * (s.D ? s.D : 1);
+    const uint64_t n4 = words / 4;
+    float4* d4 = reinterpret_cast<float4*>(s.dense);
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * 256)
+        d4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (uint64_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < words; i += (uint64_t)gridDim.x * 256)
+        s.dense[i] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(ScatterParams s)
+{
+    uint64_t b = s.off[0], e = s.off[s.P];
+    if (e > s.capacity) e = s.capacity;
+    if (b > e) b = e;
+    if (s.D <= 1) {
+        for (uint64_t i = b + blockIdx.x * 256ull + threadIdx.x; i < e; i += (uint64_t)gridDim.x * 256) {
+            const uint32_t x = s.idx[i];
+            if (x >= s.M) {
+                report_error(kDevErrIndexRange);
+                continue;
+            }
+            if (s.D == 1) s.dense[x] = s.val[i];
+        }
+    } else {
+        // rows: one wave per entry, lanes across the row
+        const uint32_t lane = lane_id();
+        for (uint64_t i = b + (blockIdx.x * 256ull + threadIdx.x) / SG_WAVE; i < e;
+             i += (uint64_t)gridDim.x * (256 / SG_WAVE)) {
+            const uint32_t x = s.idx[i];
+            if (x >= s.M) {
+                if (lane == 0) report_error(kDevErrIndexRange);
+                continue;
+            }
+            for (uint32_t c = lane; c < s.D; c += SG_WAVE) s.dense[(uint64_t)x * s.D + c] = s.val[i * s.D + c];
+        }
+    }
+}
+
+// non-empty 256-gradient blocks of an aggregate: one bit per block
+__global__ __launch_bounds__(256) void blocks_mark_kernel(const uint32_t* idx, const uint64_t* off, uint32_t P,
+                                                          uint64_t capacity, uint64_t M, uint32_t* used)
+{
+    uint64_t b = off[0], e = off[P];
+    if (e > capacity) e = capacity;
+    if (b > e) b = e;
+    for (uint64_t i = b + blockIdx.x * 256ull + threadIdx.x; i < e; i += (uint64_t)gridDim.x * 256) {
+        const uint32_t x = idx[i];
+        if (x >= M) {
+            report_error(kDevErrIndexRange);
+            continue;
+        }
+        const uint32_t blk = x >> 8;
+        atomicOr(&used[blk >> 5], 1u << (blk & 31u));
+    }
+}
+
+__global__ __launch_bounds__(256) void blocks_count_kernel(const uint32_t* used, uint64_t words, unsigned long long* out)
+{
+    uint32_t c = 0;
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < words; i += (uint64_t)gridDim.x * 256) c += __popc(used[i]);
+    c = wave_sum(c);
+    if (lane_id() == 0 && c) atomicAdd(out, (unsigned long long)c);
+}
+
+} // namespace sg
+
+using namespace sg;
+
+extern "C" size_t sg_decode_workspace_bytes(uint64_t M, uint32_t P)
+{
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return 0;
+    const CmapLayout L = cmap_layout(M, P);
+    return (size_t)(align_up(4ull * L.NW * P, 256) + 8ull * P);
+}
+
+extern "C" int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const void* d_cmap, size_t cmap_bytes,
+                         uint64_t M, uint32_t P, uint32_t* d_out_idx, uint64_t capacity, uint64_t* d_out_off,
+                         void* d_ws, size_t ws_bytes, void* stream)
+{
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return SG_EINVAL;
+    if (!d_bitmap || !d_cmap || !d_out_idx || !d_out_off || !d_ws) return SG_EINVAL;
+    if (cmap_bytes < sg_classmap_bytes(M, P)) return SG_ECAPACITY;
+    if (ws_bytes < sg_decode_workspace_bytes(M, P)) return SG_ECAPACITY;
+    DecParams d;
+    d.L = cmap_layout(M, P);
+    if (d.L.W / 32 + P + 2 > (uint64_t)DC_WORDS) return SG_EUNSUPPORTED;
+    d.q = cmap_ptrs(const_cast<void*>(d_cmap), d.L);
+    d.bitmap = d_bitmap;
+    d.bitmap_words = bitmap_words;
+    d.out_idx = d_out_idx;
+    d.capacity = capacity;
+    d.out_off = d_out_off;
+    Carver c(d_ws);
+    d.cnt = c.take<uint32_t>(d.L.NW * P);
+    d.tot = c.take<uint64_t>(P);
+    hipStream_t st = as_stream(stream);
+    const uint64_t cells = d.L.NW * P;
+    dec_count_kernel<<<(unsigned)(ceil_div(cells, 256) < 4096 ? ceil_div(cells, 256) : 4096), 256, 0, st>>>(d);
+    SG_TRY_LAUNCH();
+    dec_scan_kernel<<<P, 1024, 0, st>>>(d);
+    SG_TRY_LAUNCH();
+    dec_off_kernel<<<1, 256, 0, st>>>(d);
+    SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_DECODE, st);
+    dec_emit_kernel<<<(unsigned)d.L.NW, DC_THREADS, 0, st>>>(d);
+    SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_DECODE, st);
+    return SG_OK;
+}
+
+extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint32_t D, const uint64_t* d_off,
+                                uint32_t P, uint64_t capacity, uint64_t M, float* d_dense, void* stream)
+{
+    if (P == 0 || M == 0 || M >= (1ull << 32) || D > 65536 || !d_off || !d_dense) return SG_EINVAL;
+    if (capacity > 0 && (!d_idx || (D > 0 && !d_val))) return SG_EINVAL;
+    if ((uintptr_t)d_dense % 16) return SG_EINVAL;
+    ScatterParams s;
+    s.idx = d_idx;
+    s.val = d_val;
+    s.off = d_off;
+    s.P = P;
+    s.D = D;
+    s.capacity = capacity;
+    s.M = M;
+    s.dense = d_dense;
+    hipStream_t st = as_stream(stream);
+    const uint64_t words = M * (D ? D : 1);
+    scatter_zero_kernel<<<(unsigned)(ceil_div(words / 4 + 1, 256) < 8192 ? ceil_div(words / 4 + 1, 256) : 8192), 256, 0, st>>>(s);
+    SG_TRY_LAUNCH();
+    if (capacity > 0) {
+        probe_begin(SG_PROBE_SCATTER, st);
+        scatter_kernel<<<(unsigned)(ceil_div(capacity, 256) < 8192 ? ceil_div(capacity, 256) : 8192), 256, 0, st>>>(s);
+        SG_TRY_LAUNCH();
+        probe_end(SG_PROBE_SCATTER, st);
+    }
+    return SG_OK;
+}
+
+extern "C" size_t sg_format_sizes_workspace_bytes(uint64_t M)
+{
+    return (size_t)(align_up(4ull * ceil_div(ceil_div(M, 256), 32), 256) + 256);
+}
+
+extern "C" int sg_format_sizes(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t capacity, uint64_t M,
+                               uint32_t P, uint32_t D, const void* d_cmap, size_t cmap_bytes, uint64_t* h_out,
+                               void* d_ws, size_t ws_bytes, void* stream)
+{
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32) || !d_agg_off || !d_cmap || !h_out || !d_ws) return SG_EINVAL;
+    if (capacity > 0 && !d_agg_idx) return SG_EINVAL;
+    if (cmap_bytes < sg_classmap_bytes(M, P)) return SG_ECAPACITY;
+    if (ws_bytes < sg_format_sizes_workspace_bytes(M)) return SG_ECAPACITY;
+    hipStream_t st = as_stream(stream);
+    const CmapLayout L = cmap_layout(M, P);
+    CmapPtrs q = cmap_ptrs(const_cast<void*>(d_cmap), L);
+    Carver c(d_ws);
+    const uint64_t words = ceil_div(ceil_div(M, 256), 32);
+    uint32_t* used = c.take<uint32_t>(words);
+    unsigned long long* cnt = c.take<unsigned long long>(1);
+    int rc = fill_u32(used, words, 0, st);
+    if (rc) return rc;
+    rc = fill_u64(reinterpret_cast<uint64_t*>(cnt), 1, 0, st);
+    if (rc) return rc;
+    if (capacity > 0) {
+        blocks_mark_kernel<<<(unsigned)(ceil_div(capacity, 256) < 4096 ? ceil_div(capacity, 256) : 4096), 256, 0, st>>>(
+            d_agg_idx, d_agg_off, P, capacity, M, used);
+        SG_TRY_LAUNCH();
+    }
+    blocks_count_kernel<<<(unsigned)(ceil_div(words, 256) < 1024 ? (ceil_div(words, 256) ? ceil_div(words, 256) : 1) : 1024), 256, 0, st>>>(
+        used, words, cnt);
+    SG_TRY_LAUNCH();
+    uint64_t off0 = 0, offP = 0, nblocks = 0, hash_words = 0;
+    CmapHeader h;
+    SG_TRY(hipMemcpyAsync(&off0, d_agg_off, 8, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(&offP, d_agg_off + P, 8, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(&nblocks, cnt, 8, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(&hash_words, q.word_off + P, 8, hipMemcpyDeviceToHost, st));
+    SG_TRY(hipMemcpyAsync(&h, q.hdr, sizeof(h), hipMemcpyDeviceToHost, st));
+    SG_TRY(hipStreamSynchronize(st));
+    if (h.magic != CM_MAGIC || h.P != P || h.M != M) return SG_EINVAL;
+    if (offP > capacity) offP = capacity;
+    const uint64_t U = offP > off0 ? offP - off0 : 0;
+    uint64_t bitmap_words = 0;
+    for (uint32_t p = 0; p < P; ++p) {
+        const uint64_t lo = (uint64_t)(((unsigned __int128)M * p) / P), hi = (uint64_t)(((unsigned __int128)M * (p + 1)) / P);
+        bitmap_words += (hi - lo + 31) / 32;
+    }
+    h_out[0] = M * 4ull * D;
+    h_out[1] = U * (4ull + 4ull * D);
+    h_out[2] = nblocks * (256ull * 4ull * D + 4ull);
+    h_out[3] = bitmap_words * 4ull + U * 4ull * D;
+    h_out[4] = hash_words * 4ull + U * 4ull * D;
+    h_out[5] = U;
+    h_out[6] = nblocks;
+    return SG_OK;
+}

@@ -7,4 +7,5 @@
 #include "sg_merge.hip"
 #include "sg_aggregate.hip"
 #include "sg_encode.hip"
+#include "sg_decode.hip"
 #include "sg_stats.hip"

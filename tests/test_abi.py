@@ -193,3 +193,22 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 16)
     with pytest.raises((ValueError, RuntimeError)):
         sg.sg_topk_to_coo(x, 2)
+
+
+def test_pull_side_host_checks(L):
+    M, P = 1 << 20, 8
+    cb = L.sg_classmap_bytes(M, P)
+    dw = L.sg_decode_workspace_bytes(M, P)
+    assert dw > 0
+    assert L.sg_decode(F, 100, F, cb, M, P, F, 10, F, F, dw - 1, N) == SG_ECAPACITY
+    assert L.sg_decode(F, 100, F, cb - 1, M, P, F, 10, F, F, dw, N) == SG_ECAPACITY
+    assert L.sg_decode(N, 100, F, cb, M, P, F, 10, F, F, dw, N) == SG_EINVAL
+    assert L.sg_decode(F, 100, F, cb, M, 0, F, 10, F, F, dw, N) == SG_EINVAL
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, 0, F, N) == SG_EINVAL            # M = 0
+    assert L.sg_scatter_dense(F, F, 1, N, P, 10, M, F, N) == SG_EINVAL            # no offsets
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, M, C.c_void_p(0x10004), N) == SG_EINVAL  # misaligned dense
+    fw = L.sg_format_sizes_workspace_bytes(M)
+    out = (C.c_uint64 * 7)()
+    assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb, C.cast(out, C.c_void_p), F, fw - 1, N) == SG_ECAPACITY
+    assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb, None, F, fw, N) == SG_EINVAL
+    assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb - 1, C.cast(out, C.c_void_p), F, fw, N) == SG_ECAPACITY
