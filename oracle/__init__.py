@@ -95,6 +95,18 @@ def lib():
         L.orc_scatter_dense.argtypes = [_u32p, _f32p, C.c_uint32, _u64p, C.c_uint32, C.c_uint64, _f32p]
         L.orc_format_sizes.restype = C.c_int
         L.orc_format_sizes.argtypes = [_u32p, _u64p, C.c_uint32, C.c_uint64, C.c_uint32, C.c_uint32, _u64p]
+        L.orc_skip_mask_static.restype = C.c_int
+        L.orc_skip_mask_static.argtypes = [C.c_uint32, C.c_uint64, C.c_uint32, _u8p]
+        L.orc_skip_mask_random.restype = C.c_int
+        L.orc_skip_mask_random.argtypes = [C.c_uint32, C.c_uint64, C.c_uint32, C.c_uint64, _u8p]
+        L.orc_dropout_reduce_scatter.restype = C.c_int
+        L.orc_dropout_reduce_scatter.argtypes = [C.c_void_p, C.c_int, C.c_uint32, C.c_uint64, C.c_double, C.c_uint64,
+                                                 C.c_int, _f64p, _f64p, C.c_void_p]
+        L.orc_selective_reduce_scatter.restype = C.c_int
+        L.orc_selective_reduce_scatter.argtypes = [C.c_void_p, C.c_int, C.c_uint32, C.c_uint64, C.c_uint32, _u64p,
+                                                   _f64p, C.c_uint64, C.c_uint64, C.c_int, _f64p, _f64p]
+        L.orc_allgather.restype = C.c_int
+        L.orc_allgather.argtypes = [_f64p, C.c_void_p, C.c_int, C.c_uint32, C.c_uint64, C.c_void_p, _f64p]
         L.orc_skip_threshold.restype = C.c_uint32
         L.orc_skip_threshold.argtypes = [C.c_double]
         L.orc_skip_mask.restype = C.c_int
@@ -338,6 +350,60 @@ def skip_reduce_scatter(bufs: np.ndarray, slice_elems: int, p: float, seed: int,
     _check(lib().orc_skip_reduce_scatter(_ptr(bufs), _dtype_code(bufs), n, M, slice_elems, p, seed, inc_ptr,
                                          mode, out, out_abs, _ptr(count)), "skip_reduce_scatter")
     return out[:M], out_abs[:M], count[: n * S].reshape(n, S)
+
+
+def skip_mask_static(n: int, S: int, k: int) -> np.ndarray:
+    """Static SkipReduce(k) mask (Skip section 4.2, Algorithm 2): t >= k kept."""
+    m = np.zeros(max(1, n * n * S), dtype=np.uint8)
+    _check(lib().orc_skip_mask_static(n, S, k, m), "skip_mask_static")
+    return m[: n * n * S].reshape(n, n, S)
+
+
+def skip_mask_random(n: int, S: int, k: int, seed: int) -> np.ndarray:
+    """Random SkipReduce mask (Skip section 4.3): the static mask rotated by a
+    shared random offset."""
+    m = np.zeros(max(1, n * n * S), dtype=np.uint8)
+    _check(lib().orc_skip_mask_random(n, S, k, seed, m), "skip_mask_random")
+    return m[: n * n * S].reshape(n, n, S)
+
+
+def dropout_reduce_scatter(bufs: np.ndarray, p: float, seed: int, mode: int = 1):
+    """AllReduce_Dropout (Skip section 4.2, Algorithm 1): per-element skipping.
+    Returns out, out_abs (float64 [M]) and count (uint8 [M])."""
+    bufs = np.ascontiguousarray(bufs)
+    n, M = bufs.shape
+    out = np.zeros(max(M, 1), dtype=np.float64)
+    out_abs = np.zeros(max(M, 1), dtype=np.float64)
+    count = np.zeros(max(M, 1), dtype=np.uint8)
+    _check(lib().orc_dropout_reduce_scatter(_ptr(bufs), _dtype_code(bufs), n, M, p, seed, mode, out, out_abs,
+                                            _ptr(count)), "dropout_reduce_scatter")
+    return out[:M], out_abs[:M], count[:M]
+
+
+def selective_reduce_scatter(bufs: np.ndarray, bucket_off, p, seed: int, slice_elems: int, mode: int = 1):
+    """Selective SkipReduce (Skip section 4.4): a skip rate per bucket."""
+    bufs = np.ascontiguousarray(bufs)
+    n, M = bufs.shape
+    bo = np.ascontiguousarray(bucket_off, dtype=np.uint64)
+    pr = np.ascontiguousarray(p, dtype=np.float64)
+    out = np.zeros(max(M, 1), dtype=np.float64)
+    out_abs = np.zeros(max(M, 1), dtype=np.float64)
+    _check(lib().orc_selective_reduce_scatter(_ptr(bufs), _dtype_code(bufs), n, M, pr.size, bo, pr, seed, slice_elems,
+                                              mode, out, out_abs), "selective_reduce_scatter")
+    return out[:M], out_abs[:M]
+
+
+def allgather(reduced: np.ndarray, bufs: np.ndarray, ag_include=None) -> np.ndarray:
+    """The ring's AllGather of a reduced tensor (CMU broadcast phase), with an
+    optional delivery mask [n chunks, n positions]; returns [n, M] float64."""
+    bufs = np.ascontiguousarray(bufs)
+    n, M = bufs.shape
+    red = np.ascontiguousarray(reduced, dtype=np.float64)
+    out = np.zeros(max(n * M, 1), dtype=np.float64)
+    inc = None if ag_include is None else np.ascontiguousarray(ag_include, dtype=np.uint8)
+    _check(lib().orc_allgather(red if red.size else np.zeros(1), _ptr(bufs), _dtype_code(bufs), n, M,
+                               None if inc is None else _ptr(inc), out), "allgather")
+    return out[: n * M].reshape(n, M)
 
 
 def ring_replay(bufs: np.ndarray, slice_elems: int, include: np.ndarray) -> np.ndarray:

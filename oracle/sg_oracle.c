@@ -116,10 +116,10 @@ uint64_t orc_splitmix64_next(uint64_t* state)
  * advance the state ctr+1 times, mix once. */
 uint64_t orc_splitmix64_at(uint64_t seed, uint64_t ctr)
 {
-    uint64_t s = seed;
-    uint64_t i, out = 0;
-    for (i = 0; i <= ctr; ++i) out = orc_splitmix64_next(&s);
-    return out;
+    /* the state advances by the same constant per output, so after ctr + 1
+       outputs it is seed + (ctr + 1) * gamma (mod 2^64) */
+    uint64_t s = seed + ctr * 0x9e3779b97f4a7c15ull;
+    return orc_splitmix64_next(&s);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -618,6 +618,141 @@ int orc_skip_mask(uint32_t n, uint64_t S, double p, uint64_t seed, uint8_t* incl
  * Outputs are double; out_abs[M] holds (scale) * sum |x| of the included
  * terms, for the tolerance; count[n][S] (optional) holds c.
  * include (optional, [n][n][S]) overrides the seeded mask. */
+int orc_skip_reduce_scatter(const void* bufs, int dtype, uint32_t n, uint64_t M, uint64_t slice_elems,
+                            double p, uint64_t seed, const uint8_t* include, int mode,
+                            double* out, double* out_abs, uint8_t* count);
+
+/* Static SkipReduce(k) ([Skip] section 4.2, Algorithm 2): the
+ * reduce-scatter loop starts at step k, so the first k ring positions of
+ * every chunk (its origin included) never enter the sum: include[j][t][q] is
+ * 1 exactly for t >= k. */
+int orc_skip_mask_static(uint32_t n, uint64_t S, uint32_t k, uint8_t* include)
+{
+    uint32_t j, t;
+    uint64_t q;
+    if (n == 0) return ORC_EINVAL;
+    for (j = 0; j < n; ++j)
+        for (t = 0; t < n; ++t)
+            for (q = 0; q < S; ++q) include[((uint64_t)j * n + t) * S + q] = t >= k;
+    return ORC_OK;
+}
+
+/* Random SkipReduce ([Skip] section 4.3): Algorithm 2's slice indices are
+ * shifted by a random offset that every rank draws alike, once per call.
+ * Reading: off = (SplitMix64 output 0 of the stream at `seed`) mod n; the
+ * chain of chunk j then starts at rank j - off, so the rank at position t
+ * (rank j + t) holds chain position (t + off) mod n, and is kept exactly when
+ * that position is at least k. */
+int orc_skip_mask_random(uint32_t n, uint64_t S, uint32_t k, uint64_t seed, uint8_t* include)
+{
+    uint32_t j, t, off;
+    uint64_t q;
+    if (n == 0) return ORC_EINVAL;
+    off = (uint32_t)(orc_splitmix64_at(seed, 0) % n);
+    for (j = 0; j < n; ++j)
+        for (t = 0; t < n; ++t)
+            for (q = 0; q < S; ++q) include[((uint64_t)j * n + t) * S + q] = (t + off) % n >= k;
+    return ORC_OK;
+}
+
+/* AllReduce_Dropout ([Skip] section 4.2, Algorithm 1, ReduceOrSkip): each
+ * element of a received chunk is reduced or skipped on its own.  Reading:
+ * element e (its index in [0, M)) at ring position t >= 1 is skipped when the
+ * top 24 bits of SplitMix64 output number (t-1)*M + e of the stream at `seed`
+ * are below floor(p * 2^24); position 0, the origin's data, is always kept.
+ * out[e] = sum of the kept contributions (times n/c for DROP; 0 if c = 0);
+ * count[e] = c when count is not NULL. */
+int orc_dropout_reduce_scatter(const void* bufs, int dtype, uint32_t n, uint64_t M, double p, uint64_t seed,
+                               int mode, double* out, double* out_abs, uint8_t* count)
+{
+    uint32_t j, t;
+    uint64_t e;
+    uint32_t thr = orc_skip_threshold(p);
+    if (n == 0) return ORC_EINVAL;
+    for (j = 0; j < n; ++j) {
+        uint64_t cb = chunk_begin(M, n, j), ce = chunk_begin(M, n, j + 1);
+        for (e = cb; e < ce; ++e) {
+            double acc = 0.0, accabs = 0.0, scale;
+            uint32_t c = 0;
+            for (t = 0; t < n; ++t) {
+                double v;
+                if (t > 0 && (uint32_t)(orc_splitmix64_at(seed, (uint64_t)(t - 1) * M + e) >> 40) < thr) continue;
+                v = load_val(bufs, dtype, (uint64_t)((j + t) % n) * M + e);
+                acc += v;
+                accabs += fabs(v);
+                ++c;
+            }
+            scale = (mode == 1 && c > 0) ? (double)n / (double)c : 1.0;
+            out[e] = acc * scale;
+            out_abs[e] = accabs * scale;
+            if (count) count[e] = (uint8_t)c;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Selective SkipReduce ([Skip] section 4.4): gradients travel in buckets,
+ * each reduced by an AllReduce of its own, so each bucket can have its own
+ * skip rate.  Bucket b is [bucket_off[b], bucket_off[b+1]) of every rank's
+ * buffer, reduce-scattered as a tensor of its own (its own n chunks and
+ * slices) with skip rate p[b] and the seed seed + b. */
+int orc_selective_reduce_scatter(const void* bufs, int dtype, uint32_t n, uint64_t M, uint32_t nb,
+                                 const uint64_t* bucket_off, const double* p, uint64_t seed, uint64_t slice_elems,
+                                 int mode, double* out, double* out_abs)
+{
+    uint32_t b, r;
+    size_t esz = dtype == 1 ? 2 : 4;
+    if (n == 0 || slice_elems == 0) return ORC_EINVAL;
+    for (b = 0; b < nb; ++b) {
+        uint64_t lo = bucket_off[b], hi = bucket_off[b + 1], Mb;
+        void* tmp;
+        uint8_t* cnt;
+        int rc;
+        if (hi < lo || hi > M) return ORC_EINVAL;
+        Mb = hi - lo;
+        if (Mb == 0) continue;
+        tmp = malloc((size_t)n * Mb * esz);
+        cnt = (uint8_t*)malloc((size_t)n * ((Mb + n - 1) / n / slice_elems + 2));
+        if (!tmp || !cnt) {
+            free(tmp);
+            free(cnt);
+            return ORC_ENOMEM;
+        }
+        for (r = 0; r < n; ++r)
+            memcpy((char*)tmp + (size_t)r * Mb * esz, (const char*)bufs + ((size_t)r * M + lo) * esz, Mb * esz);
+        rc = orc_skip_reduce_scatter(tmp, dtype, n, Mb, slice_elems, p[b], seed + b, NULL, mode, out + lo,
+                                     out_abs + lo, cnt);
+        free(tmp);
+        free(cnt);
+        if (rc) return rc;
+    }
+    return ORC_OK;
+}
+
+/* AllGather phase of the ring ([Ring] broadcast phase; [Skip] Algorithms 1
+ * and 2 end with it unchanged): the holder of chunk j (ring position n-1,
+ * rank j-1) passes the reduced chunk on, and position u (rank (j+u) mod n,
+ * u = 0..n-2) receives it at step u.  ag_include[j][u] (NULL: all) says
+ * whether that delivery happens.  Reading of AllGather skipping: a rank whose
+ * delivery is skipped keeps its own local values of the chunk, and the chunk
+ * still reaches the ranks after it.  out[r][e] for every rank r. */
+int orc_allgather(const double* reduced, const void* bufs, int dtype, uint32_t n, uint64_t M,
+                  const uint8_t* ag_include, double* out)
+{
+    uint32_t j, u;
+    uint64_t e;
+    if (n == 0) return ORC_EINVAL;
+    for (j = 0; j < n; ++j) {
+        uint64_t cb = chunk_begin(M, n, j), ce = chunk_begin(M, n, j + 1);
+        for (u = 0; u < n; ++u) {
+            uint32_t r = (j + u) % n;
+            int got = u == n - 1 || !ag_include || ag_include[(uint64_t)j * n + u];
+            for (e = cb; e < ce; ++e) out[(uint64_t)r * M + e] = got ? reduced[e] : load_val(bufs, dtype, (uint64_t)r * M + e);
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_skip_reduce_scatter(const void* bufs, int dtype, uint32_t n, uint64_t M, uint64_t slice_elems,
                             double p, uint64_t seed, const uint8_t* include, int mode,
                             double* out, double* out_abs, uint8_t* count)

@@ -48,6 +48,16 @@ def test_splitmix64_published_outputs():
         assert oracle.splitmix64_at(1234567, c) == g["seed_1234567_first5"][c]
 
 
+def test_splitmix64_counter_form_is_the_stream():
+    # output number c of the stream started at seed, against stepping the
+    # stream c + 1 times
+    rng = np.random.default_rng(1)
+    for seed in [0, 1, 2**63 + 5] + [int(x) for x in rng.integers(0, 2**63, size=3, dtype=np.uint64)]:
+        outs = oracle.splitmix64_outputs(seed, 300)
+        for c in (0, 1, 2, 17, 150, 299):
+            assert oracle.splitmix64_at(seed, c) == outs[c]
+
+
 def test_h0_is_murmur2_of_le_bytes_mod_P():
     rng = np.random.default_rng(0)
     xs = rng.integers(0, 2**32, size=200, dtype=np.uint64).astype(np.uint32)
@@ -562,3 +572,141 @@ def test_format_sizes_brute_force_blocks_and_classes():
     M = 256 * 9 + 1
     s = oracle.format_sizes(np.arange(M, dtype=np.uint32), np.array([0, M], np.uint64), M, 1, 3)
     assert s["nonempty_blocks"] == 10
+
+
+# --------------------------------------------------------------------------
+# NEXT-2: the SkipReduce family
+# --------------------------------------------------------------------------
+
+def _replay_alg2_shifted(bufs, k, off):
+    """Skip Algorithm 2 with explicit per-rank buffers, the reduce-scatter loop
+    from step k and the slice indices shifted by `off` (Random SkipReduce,
+    section 4.3).  One slice per chunk.  Returns the reduced chunks, each from
+    the rank that ends holding it."""
+    n, M = bufs.shape
+    x = bufs.astype(np.float64).copy()
+    cb = [(M * j) // n for j in range(n + 1)]
+    for s in range(k, n - 1):
+        msgs = [x[r, cb[(r - s + off) % n]:cb[(r - s + off) % n + 1]].copy() for r in range(n)]
+        for r in range(n):
+            c = (r - s - 1 + off) % n
+            x[r, cb[c]:cb[c + 1]] += msgs[(r - 1) % n]
+    out = np.zeros(M)
+    for r in range(n):  # after the last step (N-2) rank r received chunk (r - (N-2) - 1 + off)
+        c = (r - (n - 2) - 1 + off) % n
+        out[cb[c]:cb[c + 1]] = x[r, cb[c]:cb[c + 1]]
+    return out
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8])
+def test_static_and_random_skipreduce_masks_replay_algorithm2(n):
+    rng = np.random.default_rng(40 + n)
+    M = 11 * n + 2
+    bufs = rng.standard_normal((n, M)).astype(np.float32)
+    sl = M  # one slice per chunk
+    for k in range(n):
+        st = oracle.skip_mask_static(n, 1, k)
+        assert st[:, :k].sum() == 0 and st[:, k:].all()
+        out, _, cnt = oracle.skip_reduce_scatter(bufs, sl, 0.0, 0, include=st, mode=0)
+        assert np.allclose(out, _replay_alg2_shifted(bufs, k, 0), rtol=1e-12, atol=1e-12)
+        for seed in (1, 2, 3, 99):
+            off = oracle.splitmix64_at(seed, 0) % n
+            rm = oracle.skip_mask_random(n, 1, k, seed)
+            assert np.array_equal(rm, np.roll(st, -off, axis=1))  # the static mask rotated
+            out, _, _ = oracle.skip_reduce_scatter(bufs, sl, 0.0, 0, include=rm, mode=0)
+            assert np.allclose(out, _replay_alg2_shifted(bufs, k, off), rtol=1e-12, atol=1e-12)
+
+
+def test_random_skipreduce_offsets_are_uniform():
+    n, trials = 8, 4000
+    offs = np.array([oracle.skip_mask_random(n, 1, 1, s)[0, :, 0].argmin() for s in range(trials)])
+    counts = np.bincount((n - offs) % n, minlength=n)
+    exp = trials / n
+    chi2 = ((counts - exp) ** 2 / exp).sum()
+    assert chi2 < 30  # 7 degrees of freedom
+
+
+def _replay_alg1(bufs, p, seed):
+    """Skip Algorithm 1 (AllReduce_Dropout) with explicit per-rank buffers:
+    ReduceOrSkip per element, drawing SplitMix64 output (t-1)*M + e for the
+    element e received at ring position t."""
+    n, M = bufs.shape
+    thr = oracle.skip_threshold(p)
+    x = bufs.astype(np.float64).copy()
+    cb = [(M * j) // n for j in range(n + 1)]
+    for s in range(n - 1):
+        msgs = [x[r, cb[(r - s) % n]:cb[(r - s) % n + 1]].copy() for r in range(n)]
+        for r in range(n):
+            c = (r - s - 1) % n
+            t = (r - c) % n
+            y = msgs[(r - 1) % n]
+            for i, e in enumerate(range(cb[c], cb[c + 1])):
+                skip = (oracle.splitmix64_at(seed, (t - 1) * M + e) >> 40) < thr
+                x[r, e] = y[i] if skip else x[r, e] + y[i]
+    out = np.zeros(M)
+    for r in range(n):
+        c = (r + 1) % n
+        out[cb[c]:cb[c + 1]] = x[r, cb[c]:cb[c + 1]]
+    return out
+
+
+@pytest.mark.parametrize("n,p", [(2, 0.5), (4, 0.3), (5, 0.9)])
+def test_dropout_reduce_scatter_replays_algorithm1(n, p):
+    rng = np.random.default_rng(n)
+    M = 7 * n + 3
+    bufs = rng.standard_normal((n, M)).astype(np.float32)
+    out, _, cnt = oracle.dropout_reduce_scatter(bufs, p, 17, mode=0)
+    assert np.allclose(out, _replay_alg1(bufs, p, 17), rtol=1e-12, atol=1e-12)
+    assert cnt.min() >= 1 and cnt.max() <= n
+
+
+def test_dropout_reduce_scatter_limits_and_rate():
+    n, M = 8, 50000
+    bufs = gen.dense_normal(9, n, M)
+    full = bufs.astype(np.float64).sum(0)
+    out, _, cnt = oracle.dropout_reduce_scatter(bufs, 0.0, 3, mode=1)
+    assert np.allclose(out, full, rtol=1e-12, atol=1e-12) and np.all(cnt == n)
+    out, _, cnt = oracle.dropout_reduce_scatter(bufs, 1.0, 3, mode=1)
+    own = np.concatenate([bufs[j, (M * j) // n:(M * (j + 1)) // n] for j in range(n)]).astype(np.float64)
+    assert np.all(cnt == 1) and np.allclose(out, own * n, rtol=1e-12, atol=1e-12)
+    _, _, cnt = oracle.dropout_reduce_scatter(bufs, 0.25, 4, mode=1)
+    mean = cnt.mean()  # 1 + Binomial(n-1, 0.75)
+    assert abs(mean - (1 + (n - 1) * 0.75)) < 5 * math.sqrt((n - 1) * 0.75 * 0.25 / M)
+
+
+def test_selective_reduce_scatter_is_per_bucket_skipreduce():
+    n, M, sl = 4, 3001, 32
+    bufs = gen.dense_normal(10, n, M)
+    # one bucket: plain seeded SkipReduce
+    a, _ = oracle.selective_reduce_scatter(bufs, [0, M], [0.5], 7, sl)
+    b, _, _ = oracle.skip_reduce_scatter(bufs, sl, 0.5, 7, mode=1)
+    assert np.array_equal(a, b)
+    # buckets: each one a tensor of its own, with its own rate and seed + b
+    bo = [0, 1000, 1000, 2500, M]
+    ps = [0.0, 0.9, 0.5, 0.25]
+    out, _ = oracle.selective_reduce_scatter(bufs, bo, ps, 7, sl)
+    for b_, (lo, hi) in enumerate(zip(bo[:-1], bo[1:])):
+        if hi == lo:
+            continue
+        want, _, _ = oracle.skip_reduce_scatter(np.ascontiguousarray(bufs[:, lo:hi]), sl, ps[b_], 7 + b_, mode=1)
+        assert np.array_equal(out[lo:hi], want)
+    assert np.allclose(out[:1000], bufs[:, :1000].astype(np.float64).sum(0), rtol=1e-12, atol=1e-12)
+
+
+def test_allgather_copies_the_reduced_chunks():
+    n, M = 5, 103
+    rng = np.random.default_rng(3)
+    bufs = rng.standard_normal((n, M)).astype(np.float32)
+    red = rng.standard_normal(M)
+    out = oracle.allgather(red, bufs)
+    assert np.array_equal(out, np.tile(red, (n, 1)))
+    # the ring's broadcast phase replayed: holder j-1 sends, position u receives at step u
+    inc = (rng.random((n, n)) < 0.6).astype(np.uint8)
+    out = oracle.allgather(red, bufs, inc)
+    cb = [(M * j) // n for j in range(n + 1)]
+    for j in range(n):
+        for u in range(n):
+            r = (j + u) % n
+            got = u == n - 1 or inc[j, u]
+            want = red[cb[j]:cb[j + 1]] if got else bufs[r, cb[j]:cb[j + 1]].astype(np.float64)
+            assert np.array_equal(out[r, cb[j]:cb[j + 1]], want)
