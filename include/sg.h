@@ -13,6 +13,12 @@
  *   sg_encode               hash-bitmap encoding of the aggregate's indices
  *   sg_skip_reduce_scatter  ring reduce-scatter arithmetic with seeded slice
  *                           skipping (SkipReduce / DropReduce)
+ *   sg_skip_reduce_k,
+ *   sg_selective_reduce_scatter,
+ *   sg_dropout_reduce_scatter,
+ *   sg_allgather            the rest of the SkipReduce family: static and
+ *                           random-offset step skipping, per-bucket rates,
+ *                           per-element dropout, and the all-gather phase
  *   sg_stats                overlap, densification and skew ratios
  *   sg_decode,
  *   sg_scatter_dense,
@@ -103,7 +109,9 @@ typedef enum sg_probe_kernel {
     SG_PROBE_PARTITION_HIST = 7,     /* hash partition: the histogram pass */
     SG_PROBE_TOPK_WRITE = 8,         /* top-k: the ordered write */
     SG_PROBE_DECODE = 9,             /* decode: the pass that emits the indices */
-    SG_PROBE_SCATTER = 10            /* scatter to dense: the scatter pass */
+    SG_PROBE_SCATTER = 10,           /* scatter to dense: the scatter pass */
+    SG_PROBE_DROPOUT_RS = 11,        /* per-element dropout reduce-scatter: its single kernel */
+    SG_PROBE_ALLGATHER = 12          /* all-gather: its single kernel */
 } sg_probe_kernel;
 int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
 
@@ -284,6 +292,59 @@ uint64_t sg_skip_num_slices(uint32_t n, uint64_t M, uint64_t slice_bytes, sg_dty
 int sg_skip_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M, uint64_t slice_bytes,
                            double p_skip, uint64_t seed, const uint8_t* d_include, sg_rescale mode, float* d_out,
                            uint8_t* d_count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The rest of the SkipReduce family, on the same ring arithmetic as
+ * sg_skip_reduce_scatter (same chunks, slices, ring order, fp32 sums, rescale
+ * modes and limits unless stated).
+ *
+ * sg_skip_reduce_k: SkipReduce(k) of [Skip] section 4.2, Algorithm 2: the
+ * reduce-scatter loop starts at step k, so the first k positions of each
+ * chunk's chain contribute nothing.  With random_offset == 0 (static
+ * SkipReduce) position t of chunk j is kept iff t >= k.  With random_offset
+ * != 0 (Random SkipReduce, [Skip] section 4.3: the slice indices are shifted
+ * by one random offset shared by every rank) the chain is rotated by
+ * off = sg_skip_random_offset(n, seed) = (SplitMix64 output 0 of `seed`) mod n
+ * and position t is kept iff (t + off) mod n >= k.  Every slice then has
+ * c = n - k; k == n gives +0 everywhere.  d_count as in sg_skip_reduce_scatter.
+ * Limits: 0 <= k <= n.
+ *
+ * sg_selective_reduce_scatter: Selective SkipReduce ([Skip] section 4.4):
+ * buckets of gradients with a skip rate each.  Bucket b covers elements
+ * [h_bucket_off[b], h_bucket_off[b+1]) of every rank's buffer (host array of
+ * nb+1 non-decreasing offsets <= M; elements outside every bucket are left
+ * untouched in d_out) and is reduce-scattered as a tensor of its own (its own
+ * n chunks and slices) in seeded mode with rate h_p_skip[b] and seed seed + b.
+ * One launch per non-empty bucket.
+ *
+ * sg_dropout_reduce_scatter: AllReduce_Dropout ([Skip] section 4.2,
+ * Algorithm 1, ReduceOrSkip per element).  Element e of chunk j at ring
+ * position t >= 1 is skipped iff the top 24 bits of SplitMix64 output number
+ * (t-1)*M + e of the stream at `seed` are below floor(p_skip * 2^24);
+ * position 0 is always kept.  Sums, c and the rescale are per element.
+ *   d_count [M] uint8 out (c per element), or NULL.
+ *
+ * sg_allgather: the all-gather phase that follows the reduce-scatter ([Ring]
+ * broadcast phase; [Skip] Algorithms 1-2 end with it).  Rank (j-1) mod n holds
+ * reduced chunk j; ring position u = 0..n-2 of chunk j (rank (j+u) mod n)
+ * receives it.  d_ag_include [n][n] uint8 (chunk j, position u; NULL = every
+ * delivery happens) skips deliveries: a rank whose delivery is skipped keeps
+ * its own values of the chunk from d_bufs; position n-1 always has it.
+ *   d_reduced [M] fp32 (for example the output of a reduce-scatter call)
+ *   d_bufs    [n][M] of dt (read only for skipped deliveries; may be NULL
+ *             when d_ag_include is NULL)
+ *   d_out     [n][M] fp32 out: every rank's tensor after the phase
+ * ------------------------------------------------------------------------ */
+uint32_t sg_skip_random_offset(uint32_t n, uint64_t seed);
+int sg_skip_reduce_k(const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M, uint64_t slice_bytes, uint32_t k,
+                     int random_offset, uint64_t seed, sg_rescale mode, float* d_out, uint8_t* d_count, void* stream);
+int sg_selective_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M, uint32_t nb,
+                                const uint64_t* h_bucket_off, const double* h_p_skip, uint64_t slice_bytes,
+                                uint64_t seed, sg_rescale mode, float* d_out, void* stream);
+int sg_dropout_reduce_scatter(const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M, double p_skip, uint64_t seed,
+                              sg_rescale mode, float* d_out, uint8_t* d_count, void* stream);
+int sg_allgather(const float* d_reduced, const void* d_bufs, sg_dtype dt, uint32_t n, uint64_t M,
+                 const uint8_t* d_ag_include, float* d_out, void* stream);
 
 /* ------------------------------------------------------------------------
  * A6. Sparsity statistics.

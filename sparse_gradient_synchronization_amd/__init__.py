@@ -69,6 +69,11 @@ SIGNATURES = {
     "sg_encode": (_int, [_vp, _vp, _u64, _u64, _u32, _vp, _sz, _vp, _u64, _vp, _vp, _sz, _vp]),
     "sg_skip_num_slices": (_u64, [_u32, _u64, _u64, _int]),
     "sg_skip_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _u64, _dbl, _u64, _vp, _int, _vp, _vp, _vp]),
+    "sg_skip_random_offset": (_u32, [_u32, _u64]),
+    "sg_skip_reduce_k": (_int, [_vp, _int, _u32, _u64, _u64, _u32, _int, _u64, _int, _vp, _vp, _vp]),
+    "sg_selective_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _u32, _vp, _vp, _u64, _u64, _int, _vp, _vp]),
+    "sg_dropout_reduce_scatter": (_int, [_vp, _int, _u32, _u64, _dbl, _u64, _int, _vp, _vp, _vp]),
+    "sg_allgather": (_int, [_vp, _vp, _int, _u32, _u64, _vp, _vp, _vp]),
     "sg_stats_workspace_bytes": (_sz, [_u32, _u64, _u64, _u32]),
     "sg_decode_workspace_bytes": (_sz, [_u64, _u32]),
     "sg_decode": (_int, [_vp, _u64, _vp, _sz, _u64, _u32, _vp, _u64, _vp, _vp, _sz, _vp]),
@@ -301,6 +306,82 @@ def sg_skip_reduce_scatter(bufs: torch.Tensor, slice_bytes: int, p_skip: float, 
                                         _p(include), mode, _p(out), _p(count), _stream()),
            "sg_skip_reduce_scatter")
     return out, count
+
+
+def sg_skip_random_offset(n: int, seed: int) -> int:
+    return int(lib().sg_skip_random_offset(n, seed & (2**64 - 1)))
+
+
+def sg_skip_reduce_k(bufs: torch.Tensor, slice_bytes: int, k: int, random_offset: bool = False, seed: int = 0,
+                     mode: int = SG_RESCALE_DROP, want_count: bool = True, out=None):
+    """SkipReduce(k), static or with a random offset: bufs [n, M] ->
+    (out [M] float32, count [n, S] uint8 or None)."""
+    _need_cuda(bufs)
+    bufs = bufs.contiguous()
+    n, M = bufs.shape
+    dt = _dtype_code(bufs)
+    S = lib().sg_skip_num_slices(n, M, slice_bytes, dt)
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=bufs.device)
+    count = torch.empty((n, S), dtype=torch.uint8, device=bufs.device) if want_count else None
+    _check(lib().sg_skip_reduce_k(_p(bufs), dt, n, M, slice_bytes, k, 1 if random_offset else 0,
+                                  seed & (2**64 - 1), mode, _p(out), _p(count), _stream()), "sg_skip_reduce_k")
+    return out, count
+
+
+def sg_selective_reduce_scatter(bufs: torch.Tensor, bucket_off, p_skip, slice_bytes: int, seed: int,
+                                mode: int = SG_RESCALE_DROP, out=None):
+    """Selective SkipReduce: bucket_off (nb+1 offsets) and p_skip (nb rates)
+    are host sequences.  Returns out [M] float32 (elements outside every
+    bucket are zero when out is allocated here)."""
+    import numpy as np
+    _need_cuda(bufs)
+    bufs = bufs.contiguous()
+    n, M = bufs.shape
+    dt = _dtype_code(bufs)
+    bo = np.ascontiguousarray(bucket_off, dtype=np.uint64)
+    pr = np.ascontiguousarray(p_skip, dtype=np.float64)
+    if bo.size != pr.size + 1:
+        raise ValueError("bucket_off must have one more entry than p_skip")
+    if out is None:
+        out = torch.zeros(M, dtype=torch.float32, device=bufs.device)
+    _check(lib().sg_selective_reduce_scatter(_p(bufs), dt, n, M, pr.size, C.c_void_p(bo.ctypes.data),
+                                             C.c_void_p(pr.ctypes.data), slice_bytes, seed & (2**64 - 1), mode,
+                                             _p(out), _stream()), "sg_selective_reduce_scatter")
+    return out
+
+
+def sg_dropout_reduce_scatter(bufs: torch.Tensor, p_skip: float, seed: int, mode: int = SG_RESCALE_DROP,
+                              want_count: bool = True, out=None):
+    """AllReduce_Dropout: bufs [n, M] -> (out [M] float32, count [M] uint8 or None)."""
+    _need_cuda(bufs)
+    bufs = bufs.contiguous()
+    n, M = bufs.shape
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=bufs.device)
+    count = torch.empty(M, dtype=torch.uint8, device=bufs.device) if want_count else None
+    _check(lib().sg_dropout_reduce_scatter(_p(bufs), _dtype_code(bufs), n, M, float(p_skip), seed & (2**64 - 1),
+                                           mode, _p(out), _p(count), _stream()), "sg_dropout_reduce_scatter")
+    return out, count
+
+
+def sg_allgather(reduced: torch.Tensor, bufs: torch.Tensor, ag_include=None, out=None):
+    """reduced [M] float32, bufs [n, M] -> out [n, M] float32, every rank's
+    tensor after the all-gather phase; ag_include [n, n] uint8 or None."""
+    _need_cuda(reduced, bufs, ag_include)
+    reduced, bufs = reduced.contiguous(), bufs.contiguous()
+    n, M = bufs.shape
+    if reduced.dtype != torch.float32 or reduced.numel() != M:
+        raise ValueError("reduced must be float32 [M]")
+    if ag_include is not None:
+        ag_include = ag_include.contiguous().to(torch.uint8)
+        if ag_include.numel() != n * n:
+            raise ValueError("ag_include must have n*n entries")
+    if out is None:
+        out = torch.empty((n, M), dtype=torch.float32, device=bufs.device)
+    _check(lib().sg_allgather(_p(reduced), _p(bufs), _dtype_code(bufs), n, M, _p(ag_include), _p(out), _stream()),
+           "sg_allgather")
+    return out
 
 
 def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,

@@ -187,7 +187,7 @@ __device__ __forceinline__ uint32_t h0(uint32_t idx, uint32_t seed, const Divide
 // SplitMix64 (Steele, Lea, Flood, OOPSLA 2014), counter form: output number
 // ctr (0-based) of the stream that starts at `seed`.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t ctr)
+__host__ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t ctr)
 {
     uint64_t z = seed + (ctr + 1ull) * 0x9e3779b97f4a7c15ull;
     z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;

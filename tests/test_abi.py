@@ -212,3 +212,49 @@ def test_pull_side_host_checks(L):
     assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb, C.cast(out, C.c_void_p), F, fw - 1, N) == SG_ECAPACITY
     assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb, None, F, fw, N) == SG_EINVAL
     assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb - 1, C.cast(out, C.c_void_p), F, fw, N) == SG_ECAPACITY
+
+
+def test_skip_family_host_checks(L):
+    # SkipReduce(k): k > n refused; the other checks are those of the seeded call
+    assert L.sg_skip_reduce_k(F, 0, 4, 1024, 64, 5, 0, 1, 0, F, N, N) == SG_EINVAL     # k > n
+    assert L.sg_skip_reduce_k(F, 0, 4, 1024, 66, 2, 0, 1, 0, F, N, N) == SG_EINVAL     # slice % 4
+    assert L.sg_skip_reduce_k(F, 0, 0, 1024, 64, 0, 0, 1, 0, F, N, N) == SG_EINVAL     # n = 0
+    assert L.sg_skip_reduce_k(N, 0, 4, 1024, 64, 2, 1, 1, 0, F, N, N) == SG_EINVAL     # no input
+    assert L.sg_skip_reduce_k(F, 0, 4, 0, 64, 2, 1, 1, 0, F, N, N) == SG_OK            # M = 0: nothing to do
+    # selective: offsets must be non-decreasing and within M, rates within [0, 1]
+    off = (C.c_uint64 * 3)(0, 512, 1024)
+    bad_off = (C.c_uint64 * 3)(0, 600, 512)
+    big_off = (C.c_uint64 * 3)(0, 512, 1025)
+    rates = (C.c_double * 2)(0.5, 0.25)
+    bad_rates = (C.c_double * 2)(0.5, 1.25)
+    vp = lambda a: C.cast(a, C.c_void_p)  # noqa: E731
+    assert L.sg_selective_reduce_scatter(F, 0, 4, 1024, 2, vp(bad_off), vp(rates), 64, 1, 0, F, N) == SG_EINVAL
+    assert L.sg_selective_reduce_scatter(F, 0, 4, 1024, 2, vp(big_off), vp(rates), 64, 1, 0, F, N) == SG_EINVAL
+    assert L.sg_selective_reduce_scatter(F, 0, 4, 1024, 2, vp(off), vp(bad_rates), 64, 1, 0, F, N) == SG_EINVAL
+    assert L.sg_selective_reduce_scatter(F, 0, 4, 1024, 0, vp(off), vp(rates), 64, 1, 0, F, N) == SG_EINVAL
+    assert L.sg_selective_reduce_scatter(F, 0, 4, 1024, 2, N, vp(rates), 64, 1, 0, F, N) == SG_EINVAL
+    # dropout and all-gather
+    assert L.sg_dropout_reduce_scatter(F, 0, 4, 1024, 1.5, 1, 0, F, N, N) == SG_EINVAL
+    assert L.sg_dropout_reduce_scatter(F, 0, 65, 1024, 0.5, 1, 0, F, N, N) == SG_EINVAL
+    assert L.sg_dropout_reduce_scatter(F, 0, 4, 1024, 0.5, 1, 3, F, N, N) == SG_EINVAL
+    assert L.sg_dropout_reduce_scatter(F, 0, 4, 1024, 0.5, 1, 0, N, N, N) == SG_EINVAL
+    assert L.sg_allgather(N, F, 0, 4, 1024, N, F, N) == SG_EINVAL
+    assert L.sg_allgather(F, N, 0, 4, 1024, F, F, N) == SG_EINVAL   # a delivery mask needs the local buffers
+    assert L.sg_allgather(F, F, 2, 4, 1024, N, F, N) == SG_EINVAL   # dtype
+
+
+def test_random_offset_matches_the_oracle_mask(L):
+    # Random SkipReduce: the library's shared offset, applied to the static
+    # mask, gives the oracle's mask for the same seed
+    import numpy as np
+    import oracle
+    for n in (1, 2, 3, 8, 13, 64):
+        for seed in (0, 1, 5, 12345, 2**63 + 7):
+            off = L.sg_skip_random_offset(n, seed)
+            assert 0 <= off < n
+            S = 3
+            for k in (0, n // 2, n):
+                want = oracle.skip_mask_random(n, S, k, seed)
+                t = np.arange(n)
+                got = np.broadcast_to((((t + off) % n) >= k)[None, :, None], (n, n, S)).astype(np.uint8)
+                assert np.array_equal(got, want)

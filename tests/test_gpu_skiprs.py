@@ -64,3 +64,105 @@ def test_skip_rs_full_config5():
     need_gpu()
     c = gen.config5()
     _run(c["bufs"], c["slice_elems"], c["p"], c["seed"], c["mode"])
+
+
+# ---------------------------------------------------------------------------
+# the rest of the SkipReduce family
+# ---------------------------------------------------------------------------
+
+def _close(out_t, ref, ref_abs, bf16, what):
+    assert_sum_close(out_t.cpu().numpy(), ref, ref_abs, 1e-3 if bf16 else 1e-6, what)
+
+
+@pytest.mark.parametrize("n,M,sl", [(1, 999, 64), (4, 4 * 4096, 1024), (3, 12345, 100), (8, 8 * 4096 * 3, 4096)])
+@pytest.mark.parametrize("random_offset", [False, True])
+def test_skip_reduce_k(n, M, sl, random_offset):
+    need_gpu()
+    bufs_np = gen.dense_normal(70 + n, n, M)
+    bufs = to_dev_vals(bufs_np)
+    S = oracle.num_slices(n, M, sl)
+    for k in range(n + 1):
+        seed = 1000 + 17 * k
+        inc = oracle.skip_mask_random(n, S, k, seed) if random_offset else oracle.skip_mask_static(n, S, k)
+        for mode in (0, 1):
+            out, cnt = sg.sg_skip_reduce_k(bufs, sl * 4, k, random_offset, seed, mode=mode)
+            torch.cuda.synchronize()
+            ref, ref_abs, ref_cnt = oracle.skip_reduce_scatter(bufs_np, sl, 0.0, 0, include=inc, mode=mode)
+            assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+            _close(out, ref, ref_abs, False, "skip_reduce_k")
+    assert sg.sg_device_error() == 0
+
+
+def test_skip_reduce_k_bf16():
+    need_gpu()
+    n, M, sl = 4, 4 * 8192, 2048
+    bufs_np = gen.to_bf16(gen.dense_normal(80, n, M))
+    S = oracle.num_slices(n, M, sl)
+    inc = oracle.skip_mask_random(n, S, 2, 5)
+    out, cnt = sg.sg_skip_reduce_k(to_dev_vals(bufs_np, True), sl * 2, 2, True, 5, mode=1)
+    ref, ref_abs, ref_cnt = oracle.skip_reduce_scatter(bufs_np, sl, 0.0, 0, include=inc, mode=1)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+    _close(out, ref, ref_abs, True, "skip_reduce_k bf16")
+
+
+@pytest.mark.parametrize("n,M", [(1, 1000), (2, 4096), (3, 12345), (8, 8 * 4096 * 5), (8, 8 * 4096 + 3), (64, 64 * 9)])
+@pytest.mark.parametrize("p", [0.0, 0.3, 1.0])
+def test_dropout_reduce_scatter(n, M, p):
+    need_gpu()
+    bufs_np = gen.dense_normal(90 + n, n, M)
+    bufs = to_dev_vals(bufs_np)
+    for mode in (0, 1):
+        out, cnt = sg.sg_dropout_reduce_scatter(bufs, p, 4321 + n, mode=mode)
+        torch.cuda.synchronize()
+        ref, ref_abs, ref_cnt = oracle.dropout_reduce_scatter(bufs_np, p, 4321 + n, mode=mode)
+        assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+        _close(out, ref, ref_abs, False, "dropout")
+    assert sg.sg_device_error() == 0
+
+
+@pytest.mark.parametrize("n,M", [(4, 4 * 8192), (3, 1001)])
+def test_dropout_reduce_scatter_bf16(n, M):
+    need_gpu()
+    bufs_np = gen.to_bf16(gen.dense_normal(95, n, M))
+    out, cnt = sg.sg_dropout_reduce_scatter(to_dev_vals(bufs_np, True), 0.5, 11, mode=1)
+    ref, ref_abs, ref_cnt = oracle.dropout_reduce_scatter(bufs_np, 0.5, 11, mode=1)
+    assert np.array_equal(cnt.cpu().numpy(), ref_cnt)
+    _close(out, ref, ref_abs, True, "dropout bf16")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_selective_reduce_scatter(bf16):
+    need_gpu()
+    n, M, sl = 8, 8 * 4096 * 4 + 40, 1024
+    bufs_np = gen.dense_normal(100, n, M)
+    if bf16:
+        bufs_np = gen.to_bf16(bufs_np)
+    # buckets with their own rates: an empty bucket, a ragged one, and a gap
+    # [8*4096*3+8, M) outside every bucket
+    off = [0, 8 * 4096, 8 * 4096, 8 * 4096 * 2 + 13, 8 * 4096 * 3 + 8]
+    rates = [0.0, 0.5, 1.0, 0.25]
+    for mode in (0, 1):
+        out = sg.sg_selective_reduce_scatter(to_dev_vals(bufs_np, bf16), off, rates, sl * (2 if bf16 else 4), 77,
+                                             mode=mode)
+        torch.cuda.synchronize()
+        ref, ref_abs = oracle.selective_reduce_scatter(bufs_np, off, rates, 77, sl, mode=mode)
+        _close(out, ref, ref_abs, bf16, "selective")
+    assert sg.sg_device_error() == 0
+
+
+@pytest.mark.parametrize("n,M", [(1, 100), (4, 4 * 4096), (3, 12345), (8, 8 * 1024 + 5)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_allgather(n, M, bf16):
+    need_gpu()
+    bufs_np = gen.dense_normal(110 + n, n, M)
+    if bf16:
+        bufs_np = gen.to_bf16(bufs_np)
+    reduced_np = gen.dense_normal(120 + n, 1, M)[0]
+    rng = np.random.default_rng(n)
+    for inc in (None, (rng.random((n, n)) < 0.5).astype(np.uint8)):
+        out = sg.sg_allgather(to_dev_vals(reduced_np), to_dev_vals(bufs_np, bf16),
+                              None if inc is None else torch.from_numpy(inc).cuda())
+        torch.cuda.synchronize()
+        ref = oracle.allgather(reduced_np.astype(np.float64), bufs_np, inc)
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), "allgather differs"
