@@ -8,4 +8,5 @@
 #include "sg_aggregate.hip"
 #include "sg_encode.hip"
 #include "sg_decode.hip"
+#include "sg_statsw.hip"
 #include "sg_stats.hip"

@@ -2,14 +2,15 @@
 // exact integer counts (Zen OSDI'25 digest, section 2.1 Defs. 3-5; section
 // 3.1 Def. 8).
 //
-// The union and every pairwise intersection come from the merge engine run
-// over the workers' lists (one group): per union index the set of workers
-// holding it is a 64-bit mask; per 64 indices a wave turns the masks into one
-// ballot word per worker and adds popcount(V_a & V_b) for each pair.  Blocks
-// keep their counts in LDS and write one partial row each; a last pass sums
-// the rows.  Per-part counts of each worker come from one pass over the
-// entries.  The host then evaluates the definitions in double with fixed
-// expressions.
+// The union and every pairwise intersection come, for up to 16 workers and
+// 16 hash classes, from the window pass of sg_statsw.hip (per-worker bitmaps
+// of 2048-key windows); otherwise from the merge engine run over the
+// workers' lists (one group): per union index the set of workers holding it
+// is a 64-bit mask; per 64 indices a wave turns the masks into one ballot
+// word per worker and adds popcount(V_a & V_b) for each pair.  Either way
+// the passes write partial rows of counts and a last pass sums the rows.
+// Per-part counts of each worker come from one pass over the entries.  The
+// host then evaluates the definitions in double with fixed expressions.
 #include "sg_host.h"
 
 namespace sg {
@@ -70,7 +71,14 @@ __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, S
 
 using namespace sg;
 
-static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, uint32_t P)
+// The window pass serves up to SW_MAXN workers and, with a class map, up to
+// SW_MAXP classes.
+static bool stats_windowed(uint32_t n, uint32_t P, bool hashed)
+{
+    return n <= (uint32_t)SW_MAXN && (!hashed || P <= (uint32_t)SW_MAXP);
+}
+
+static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, uint32_t P, bool windowed)
 {
     *p = MergeParams();
     p->n = n;
@@ -82,13 +90,35 @@ static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, 
     p->inv_m = 1.0 / (double)M;
     p->npairs = n * (n + 1) / 2;
     p->st_row = p->npairs + 1 + 2 * P;
-    choose_tiles(1, M, total, &p->tb, &p->NT);
+    if (windowed) {
+        p->tb = SW_TB;
+        const uint64_t nt = (M + (1ull << SW_TB) - 1) >> SW_TB;
+        p->NT = (uint32_t)(nt ? nt : 1);
+    } else {
+        choose_tiles(1, M, total, &p->tb, &p->NT);
+    }
 }
 
-static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k)
+static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k, SwParams* sw)
 {
     const uint32_t n = p->n;
-    merge_carve(c, p, MODE_STATS);
+    if (sw) { // the window pass: the boundary plan of the merge engine, the balance, partial rows
+        const uint64_t R = n;
+        p->nscan = (uint32_t)ceil_div(p->NT, MG_SCAN_BLOCK);
+        p->chunk_start = c.take<uint32_t>(R + 1);
+        p->nchunks_max = (uint32_t)(ceil_div(p->total, MG_CHUNK) + R);
+        p->chunk_rec = c.take<uint4>(p->nchunks_max);
+        p->bnd = c.take<uint32_t>(R * (p->NT + 1));
+        p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
+        sw->work = c.take<uint32_t>(p->NT);
+        sw->wcum = c.take<uint64_t>(p->NT);
+        sw->wblk = c.take<uint64_t>(p->nscan);
+        sw->wstart = c.take<uint32_t>(SW_MAX_WAVES + 1);
+        sw->wtotal = c.take<uint64_t>(1);
+        sw->rows = c.take<uint64_t>((uint64_t)SW_MAX_WAVES * p->st_row);
+    } else {
+        merge_carve(c, p, MODE_STATS);
+    }
     k->row = c.take<uint64_t>(p->st_row);
     k->wcontig = c.take<uint64_t>((uint64_t)n * P);
     k->whashed = c.take<uint64_t>((uint64_t)n * P);
@@ -98,11 +128,71 @@ static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* 
 extern "C" size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P)
 {
     if (n == 0 || P == 0) return 256;
-    MergeParams p;
-    stats_setup(&p, n, M, total, P);
-    Carver c(nullptr);
-    StatsCounts k;
-    return stats_carve(c, &p, P, &k);
+    // enough for either pass (the class map is not known here)
+    size_t best = 0;
+    for (int windowed = 0; windowed < 2; ++windowed) {
+        if (windowed && !stats_windowed(n, P, false)) continue;
+        MergeParams p;
+        stats_setup(&p, n, M, total, P, windowed != 0);
+        Carver c(nullptr);
+        StatsCounts k;
+        SwParams sw;
+        const size_t b = stats_carve(c, &p, P, &k, windowed ? &sw : nullptr);
+        if (b > best) best = b;
+    }
+    return best;
+}
+
+// The window pass: boundaries, balance, counts, the sum of the partial rows.
+static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64_t* out)
+{
+    static int resident[2] = {0, 0};
+    const int ix = p.n <= 8 ? 0 : 1;
+    const bool hashed = sw.planes != nullptr;
+    if (!resident[ix]) {
+        int dev = 0, cus = 0, per = 0;
+        SG_TRY(hipGetDevice(&dev));
+        SG_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        if (ix == 0) SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sw_stats_kernel<8, true>, SW_THREADS, 0));
+        else SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sw_stats_kernel<16, true>, SW_THREADS, 0));
+        resident[ix] = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+        if (resident[ix] > (int)(SW_MAX_WAVES / SW_WAVES)) resident[ix] = SW_MAX_WAVES / SW_WAVES;
+    }
+    const uint64_t T = p.NT;
+    const uint64_t wblocks = ceil_div(T, SW_WAVES);
+    uint64_t grid = wblocks < (uint64_t)resident[ix] ? wblocks : (uint64_t)resident[ix];
+    if (grid == 0) grid = 1;
+    const uint32_t W = (uint32_t)grid * SW_WAVES;
+    mg_plan_kernel<<<1, 512, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    mg_bnd_kernel<<<p.nchunks_max < 1024 ? p.nchunks_max : 1024, 512, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    const uint64_t cells = (uint64_t)p.n * (p.NT + 1);
+    mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    sw.m = p;
+    const unsigned tgrid = (unsigned)(ceil_div(T, 256) < 2048 ? ceil_div(T, 256) : 2048);
+    sw_weight_kernel<<<tgrid, 256, 0, st>>>(sw);
+    SG_TRY_LAUNCH();
+    sw_scan_local_kernel<<<p.nscan, 1024, 0, st>>>(sw);
+    SG_TRY_LAUNCH();
+    sw_scan_top_kernel<<<1, 1024, 0, st>>>(sw, p.nscan);
+    SG_TRY_LAUNCH();
+    sw_starts_kernel<<<tgrid, 256, 0, st>>>(sw, W);
+    SG_TRY_LAUNCH();
+    if (ix == 0) {
+        if (hashed) sw_stats_kernel<8, true><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);
+        else sw_stats_kernel<8, false><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);
+    } else {
+        if (hashed) sw_stats_kernel<16, true><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);
+        else sw_stats_kernel<16, false><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);
+    }
+    SG_TRY_LAUNCH();
+    MergeParams q = p;
+    q.st_part = sw.rows;
+    mg_stats_reduce_kernel<<<p.st_row, 256, 0, st>>>(q, W, out);
+    SG_TRY_LAUNCH();
+    return SG_OK;
 }
 
 // Def. 5 on one set J: max over parts of (c_i M) / (g_i |J|); 0 if J is empty.
@@ -144,11 +234,13 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
         seed = h.seed;
     }
 
+    const bool windowed = total > 0 && stats_windowed(n, P, d_cmap != nullptr);
     MergeParams p;
-    stats_setup(&p, n, M, total, P);
+    stats_setup(&p, n, M, total, P, windowed);
     Carver c(d_ws);
     StatsCounts k;
-    stats_carve(c, &p, P, &k);
+    SwParams sw;
+    stats_carve(c, &p, P, &k, windowed ? &sw : nullptr);
     p.idx = d_idx;
     p.off = d_in_off;
     p.seed = seed;
@@ -159,7 +251,20 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     if (rc) return rc;
     rc = fill_u64(k.whashed, (uint64_t)n * P, 0, st);
     if (rc) return rc;
-    rc = merge_run(p, MODE_STATS, st, k.row);
+    if (windowed) {
+        sw.planes = nullptr;
+        sw.nbits = 0;
+        sw.stride = 0;
+        if (d_cmap && P >= 2) { // P = 1: every key is in class 0 (the union's count, below)
+            const CmapLayout L = cmap_layout(M, P);
+            sw.planes = cmap_ptrs(const_cast<void*>(d_cmap), L).planes;
+            sw.nbits = L.nbits;
+            sw.stride = L.stride;
+        }
+        rc = stats_window_run(p, sw, st, k.row);
+    } else {
+        rc = merge_run(p, MODE_STATS, st, k.row);
+    }
     if (rc) return rc;
     st_entries_kernel<<<p.nchunks_max < 2048 ? p.nchunks_max : 2048, MG_THREADS, 0, st>>>(p, k);
     SG_TRY_LAUNCH();
@@ -174,6 +279,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     for (uint32_t a = 0, pi = 0; a < n; ++a)
         for (uint32_t b = a; b < n; ++b, ++pi) inter[(size_t)a * n + b] = row[pi];
     const uint64_t uni = row[p.npairs];
+    if (windowed && d_cmap && P == 1) row[p.npairs + 1 + P] = uni; // one class holds every key
     const uint64_t* uc = &row[p.npairs + 1];
     const uint64_t* uh = &row[p.npairs + 1 + P];
 
@@ -187,6 +293,8 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
         if (o->nnz[a] > o->max_nnz) o->max_nnz = o->nnz[a];
     }
     o->union_size = uni;
+    if (windowed) // the window pass leaves the diagonal to the list lengths: |I_a & I_a| = |I_a|
+        for (uint32_t a = 0; a < n; ++a) inter[(size_t)a * n + a] = o->nnz[a];
     for (uint32_t a = 0; a < n; ++a)
         for (uint32_t b = 0; b < n; ++b) o->inter[(uint64_t)a * n + b] = a <= b ? inter[(size_t)a * n + b] : inter[(size_t)b * n + a];
     // Def. 3 over all pairs

@@ -36,7 +36,9 @@ def _check(idx, in_off, M, P, seed=None):
     return got
 
 
-@pytest.mark.parametrize("n,P", [(1, 1), (2, 2), (4, 4), (7, 3), (16, 16), (64, 8)])
+# (n, P) spans both counting passes: the window pass (n <= 16, and P <= 16
+# with a class map) and the merge engine (more workers, or more classes)
+@pytest.mark.parametrize("n,P", [(1, 1), (2, 2), (4, 4), (7, 3), (16, 16), (64, 8), (17, 5), (5, 200), (9, 17)])
 def test_stats_zipf(n, P):
     idx, in_off, _ = gen.coo_zipf(500 + n, n, 120000, 3000, 1.1)
     _check(idx, in_off, 120000, P, seed=13)
