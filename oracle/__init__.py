@@ -107,6 +107,13 @@ def lib():
                                                    _f64p, C.c_uint64, C.c_uint64, C.c_int, _f64p, _f64p]
         L.orc_allgather.restype = C.c_int
         L.orc_allgather.argtypes = [_f64p, C.c_void_p, C.c_int, C.c_uint32, C.c_uint64, C.c_void_p, _f64p]
+        L.orc_dgc_sample_pos.restype = C.c_uint64
+        L.orc_dgc_sample_pos.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+        L.orc_dgc_rank.restype = C.c_uint64
+        L.orc_dgc_rank.argtypes = [C.c_double, C.c_uint64]
+        L.orc_dgc_select.restype = C.c_int
+        L.orc_dgc_select.argtypes = [_f32p, _f32p, C.c_uint32, C.c_uint64, C.c_double, C.c_uint64, _u32p, _f32p,
+                                     C.c_uint64, _u64p, C.POINTER(C.c_uint32)]
         L.orc_skip_threshold.restype = C.c_uint32
         L.orc_skip_threshold.argtypes = [C.c_double]
         L.orc_skip_mask.restype = C.c_int
@@ -189,6 +196,32 @@ def topk_to_coo(dense: np.ndarray, k: int):
     _check(lib().orc_topk_to_coo(_ptr(dense), _dtype_code(dense), n, M, k, idx.reshape(-1), _ptr(val)),
            "topk_to_coo")
     return idx, val
+
+
+def dgc_sample_pos(M: int, S: int, j: int) -> int:
+    return int(lib().orc_dgc_sample_pos(M, S, j))
+
+
+def dgc_rank(density: float, Ns: int) -> int:
+    return int(lib().orc_dgc_rank(density, Ns))
+
+
+def dgc_select(grad: np.ndarray, resid: np.ndarray, density: float, S: int, cap: int | None = None):
+    """One DGC iteration with a sampled global threshold and residuals (Zen
+    section 4; Skip section 2).  grad, resid: [n, M] float32 (resid is not
+    modified; the new residual is returned).  Returns (idx [n, cap] uint32,
+    val [n, cap] float32, count [n] uint64, new_resid [n, M], thr_key)."""
+    grad = np.ascontiguousarray(grad, dtype=np.float32)
+    r = np.array(resid, dtype=np.float32, copy=True, order="C")
+    n, M = grad.shape
+    cap = M if cap is None else cap
+    idx = np.zeros((n, max(cap, 1)), dtype=np.uint32)
+    val = np.zeros((n, max(cap, 1)), dtype=np.float32)
+    cnt = np.zeros(n, dtype=np.uint64)
+    thr = C.c_uint32(0)
+    _check(lib().orc_dgc_select(grad.reshape(-1), r.reshape(-1), n, M, density, S, idx.reshape(-1), val.reshape(-1),
+                                max(cap, 1) if cap else 0, cnt, C.byref(thr)), "dgc_select")
+    return idx[:, :cap], val[:, :cap], cnt, r, int(thr.value)
 
 
 def hash_partition(idx: np.ndarray, val, in_off: np.ndarray, P: int, seed: int):

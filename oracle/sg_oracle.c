@@ -235,6 +235,106 @@ int orc_topk_to_coo(const void* dense, int dtype, uint32_t n, uint64_t M, uint64
 }
 
 /* ------------------------------------------------------------------------ */
+/* DGC with a sampled global threshold and residual accumulation             */
+/* ------------------------------------------------------------------------ */
+
+/* Descending order of 32-bit keys, for qsort. */
+static int cmp_u32_desc(const void* x, const void* y)
+{
+    uint32_t a = *(const uint32_t*)x, b = *(const uint32_t*)y;
+    return a < b ? 1 : (a > b ? -1 : 0);
+}
+
+/* Position of sample j of S in a worker's M elements: the midpoint of the
+ * j-th of S equal strides, floor((2j + 1) M / (2S)); every position when
+ * S >= M. */
+uint64_t orc_dgc_sample_pos(uint64_t M, uint64_t S, uint64_t j)
+{
+    if (S >= M) return j;
+    return (uint64_t)(((unsigned __int128)(2 * j + 1) * M) / (2 * S));
+}
+
+/* Rank of the threshold among the pooled samples: ks = ceil(density * Ns)
+ * evaluated in double, clamped to [1, Ns]. */
+uint64_t orc_dgc_rank(double density, uint64_t Ns)
+{
+    double x = ceil(density * (double)Ns);
+    if (!(x >= 1.0)) return 1;
+    if (x >= (double)Ns) return Ns;
+    return (uint64_t)x;
+}
+
+/* One iteration of DGC-style top-k with a sampled global threshold and
+ * residual accumulation, for n workers at once.
+ *   [Zen] section 4 (Implementation): DGC adapted to tensor parallelism --
+ *   every device samples its gradient locally, the samples of all devices are
+ *   gathered, one global top-k threshold is computed from them, and every
+ *   device applies it locally to select its top-k values.
+ *   [Skip] section 2: gradients that are not selected are accumulated
+ *   locally into later iterations' gradients until their accumulated
+ *   magnitude is large enough to be selected (residuals).
+ * Steps, in the pages' order:
+ *   1. accumulate: a[w][i] = resid[w][i] + grad[w][i], one fp32 addition;
+ *   2. sample: worker w contributes |a[w][pos_j]| for the S positions of
+ *      orc_dgc_sample_pos (S clamped to M);
+ *   3. gather: the n*S samples form one pool;
+ *   4. threshold: thr = the ks-th largest pooled magnitude, ks = orc_dgc_rank;
+ *   5. select: every (w, i) with |a[w][i]| >= thr, in ascending i, emitted as
+ *      (i, a[w][i]) into out_idx[w][*], out_val[w][*] (at most cap per worker;
+ *      count[w] is the number selected, which may exceed cap);
+ *   6. residual: resid[w][i] = 0 where selected, a[w][i] elsewhere.
+ * Magnitudes are compared as fp32 bit patterns with the sign cleared (they
+ * order like |a|); inputs are finite.  thr_key (optional) receives the
+ * threshold's bit pattern. */
+int orc_dgc_select(const float* grad, float* resid, uint32_t n, uint64_t M, double density, uint64_t S,
+                   uint32_t* out_idx, float* out_val, uint64_t cap, uint64_t* count, uint32_t* thr_key)
+{
+    uint32_t w;
+    uint64_t i, j, Ns, ks;
+    uint32_t* pool;
+    uint32_t thr;
+    if (n == 0 || M == 0 || S == 0) return ORC_EINVAL;
+    if (S > M) S = M;
+    Ns = (uint64_t)n * S;
+    pool = (uint32_t*)malloc(Ns * sizeof(uint32_t));
+    if (!pool) return ORC_ENOMEM;
+    for (w = 0; w < n; ++w)
+        for (j = 0; j < S; ++j) {
+            uint64_t e = (uint64_t)w * M + orc_dgc_sample_pos(M, S, j);
+            float a = resid[e] + grad[e];
+            uint32_t bits;
+            memcpy(&bits, &a, 4);
+            pool[(uint64_t)w * S + j] = bits & 0x7fffffffu;
+        }
+    qsort(pool, Ns, sizeof(uint32_t), cmp_u32_desc);
+    ks = orc_dgc_rank(density, Ns);
+    thr = pool[ks - 1];
+    free(pool);
+    if (thr_key) *thr_key = thr;
+    for (w = 0; w < n; ++w) {
+        uint64_t c = 0;
+        for (i = 0; i < M; ++i) {
+            uint64_t e = (uint64_t)w * M + i;
+            float a = resid[e] + grad[e];
+            uint32_t bits;
+            memcpy(&bits, &a, 4);
+            if ((bits & 0x7fffffffu) >= thr) {
+                if (c < cap) {
+                    out_idx[(uint64_t)w * cap + c] = (uint32_t)i;
+                    out_val[(uint64_t)w * cap + c] = a;
+                }
+                ++c;
+                resid[e] = 0.0f;
+            } else {
+                resid[e] = a;
+            }
+        }
+        count[w] = c;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* A2: hash partition                                                        */
 /* ------------------------------------------------------------------------ */
 

@@ -710,3 +710,114 @@ def test_allgather_copies_the_reduced_chunks():
             got = u == n - 1 or inc[j, u]
             want = red[cb[j]:cb[j + 1]] if got else bufs[r, cb[j]:cb[j + 1]].astype(np.float64)
             assert np.array_equal(out[r, cb[j]:cb[j + 1]], want)
+
+
+# ---------------------------------------------------------------------------
+# DGC with a sampled global threshold and residuals (Zen section 4; Skip
+# section 2): pins written from the definition with numpy, not the oracle
+# ---------------------------------------------------------------------------
+
+def _dgc_reference(grad, resid, density, S):
+    """The definition in numpy float32: accumulate, sample, pool, threshold,
+    select, update the residual."""
+    n, M = grad.shape
+    a = (resid.astype(np.float32) + grad.astype(np.float32)).astype(np.float32)
+    keys = a.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    S = min(S, M)
+    if S >= M:
+        pos = np.arange(M)
+    else:
+        pos = np.array([((2 * j + 1) * M) // (2 * S) for j in range(S)], dtype=np.int64)
+    pool = np.sort(keys[:, pos].reshape(-1))[::-1]
+    ks = math.ceil(density * float(n * S))
+    ks = min(max(ks, 1), n * S)
+    thr = int(pool[ks - 1])
+    sel = keys >= thr
+    new_resid = np.where(sel, np.float32(0.0), a).astype(np.float32)
+    return a, sel, thr, new_resid
+
+
+@pytest.mark.parametrize("n,M,S,density", [(3, 1000, 1000, 0.05), (2, 777, 777, 0.3), (4, 5000, 5000, 0.01)])
+def test_dgc_full_sample_is_exact_global_topk(n, M, S, density):
+    rng = np.random.default_rng(n * 7 + M)
+    g = rng.standard_normal((n, M)).astype(np.float32)
+    r = (rng.standard_normal((n, M)) * 0.1).astype(np.float32)
+    idx, val, cnt, new_r, thr = oracle.dgc_select(g, r, density, S)
+    a, sel, thr_ref, r_ref = _dgc_reference(g, r, density, S)
+    assert thr == thr_ref
+    # with every element sampled, the threshold is the ks-th largest of all
+    # n*M magnitudes: exactly ks are selected when magnitudes are distinct
+    keys = (a.view(np.uint32) & np.uint32(0x7FFFFFFF)).reshape(-1)
+    if np.unique(keys).size == keys.size:
+        assert int(cnt.sum()) == min(max(math.ceil(density * float(n * M)), 1), n * M)
+    for w in range(n):
+        want = np.flatnonzero(sel[w])
+        assert int(cnt[w]) == want.size
+        assert np.array_equal(idx[w, : want.size], want)
+        assert np.array_equal(val[w, : want.size].view(np.uint32), a[w, want].view(np.uint32))
+    assert np.array_equal(new_r.view(np.uint32), r_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("S", [1, 7, 64, 1000])
+def test_dgc_sampled_threshold_is_the_pooled_order_statistic(S):
+    rng = np.random.default_rng(S)
+    n, M = 4, 3001
+    g = (rng.standard_normal((n, M)) * np.exp(rng.standard_normal((n, 1)))).astype(np.float32)
+    r = np.zeros((n, M), np.float32)
+    for density in (0.0, 0.05, 0.5, 1.0, 2.0):
+        idx, val, cnt, new_r, thr = oracle.dgc_select(g, r, density, S)
+        a, sel, thr_ref, r_ref = _dgc_reference(g, r, density, S)
+        assert thr == thr_ref, density
+        assert np.array_equal(cnt, sel.sum(axis=1).astype(np.uint64))
+        assert np.array_equal(new_r.view(np.uint32), r_ref.view(np.uint32))
+    # density 0 keeps only magnitudes at or above the largest sample; density
+    # >= 1 takes the smallest sample as the threshold
+    _, _, _, _, thr_hi = oracle.dgc_select(g, r, 0.0, S)
+    _, _, _, _, thr_lo = oracle.dgc_select(g, r, 1.0, S)
+    pos = [oracle.dgc_sample_pos(M, min(S, M), j) for j in range(min(S, M))]
+    smp = (g[:, pos].view(np.uint32) & np.uint32(0x7FFFFFFF))
+    assert thr_hi == int(smp.max()) and thr_lo == int(smp.min())
+
+
+def test_dgc_residuals_conserve_the_gradient():
+    # after one gradient and then zero gradients, every nonzero element
+    # leaves through exactly one emission carrying its accumulated value (a
+    # threshold of 0 also re-takes elements already at 0, adding nothing),
+    # and the residual drains: once most samples are 0 the threshold is 0
+    rng = np.random.default_rng(11)
+    n, M = 3, 4096
+    g0 = rng.standard_normal((n, M)).astype(np.float32)
+    r = np.zeros((n, M), np.float32)
+    nonzero_emits = np.zeros((n, M), dtype=np.int64)
+    total = np.zeros((n, M), dtype=np.float64)
+    g = g0
+    for it in range(200):
+        idx, val, cnt, r, thr = oracle.dgc_select(g, r, 0.05, 512)
+        for w in range(n):
+            c = int(cnt[w])
+            nonzero_emits[w, idx[w, :c]] += val[w, :c] != 0
+            total[w, idx[w, :c]] += val[w, :c].astype(np.float64)
+        g = np.zeros_like(g0)
+        if not r.any():
+            break
+    assert not r.any(), "the residual did not drain"
+    assert nonzero_emits.max() <= 1
+    assert np.array_equal(total, g0.astype(np.float64))
+
+
+def test_dgc_selected_fraction_tracks_density():
+    # a strided sample of N(0,1) values puts the threshold near the
+    # (1 - density) quantile: the selected fraction is close to the density
+    rng = np.random.default_rng(5)
+    n, M = 4, 1 << 16
+    g = rng.standard_normal((n, M)).astype(np.float32)
+    _, _, cnt, _, _ = oracle.dgc_select(g, np.zeros_like(g), 0.05, 4096, cap=0)
+    frac = cnt.sum() / (n * M)
+    assert abs(frac - 0.05) < 0.005, frac
+
+
+def test_dgc_sample_positions_and_rank():
+    assert [oracle.dgc_sample_pos(10, 4, j) for j in range(4)] == [1, 3, 6, 8]
+    assert [oracle.dgc_sample_pos(5, 9, j) for j in range(5)] == [0, 1, 2, 3, 4]
+    assert oracle.dgc_rank(0.05, 100) == 5 and oracle.dgc_rank(0.051, 100) == 6
+    assert oracle.dgc_rank(0.0, 100) == 1 and oracle.dgc_rank(3.0, 100) == 100
