@@ -7,6 +7,8 @@
  * library implements the compute a worker or server performs:
  *
  *   sg_topk_to_coo          top-k sparsification of dense gradients into COO
+ *   sg_dgc_select           DGC-style top-k: sampled global threshold and
+ *                           residual accumulation
  *   sg_hash_partition       data-independent hash partition of COO indices
  *   sg_aggregate            per-partition union-sum of n workers' COO tensors
  *   sg_classmap_build,
@@ -111,7 +113,8 @@ typedef enum sg_probe_kernel {
     SG_PROBE_DECODE = 9,             /* decode: the pass that emits the indices */
     SG_PROBE_SCATTER = 10,           /* scatter to dense: the scatter pass */
     SG_PROBE_DROPOUT_RS = 11,        /* per-element dropout reduce-scatter: its single kernel */
-    SG_PROBE_ALLGATHER = 12          /* all-gather: its single kernel */
+    SG_PROBE_ALLGATHER = 12,         /* all-gather: its single kernel */
+    SG_PROBE_DGC_FILTER = 13         /* DGC select: the streaming pass over gradient and residual */
 } sg_probe_kernel;
 int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
 
@@ -139,6 +142,36 @@ int sg_validate_coo(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n,
 size_t sg_topk_workspace_bytes(uint32_t n, uint64_t M, uint64_t k, sg_dtype dt);
 int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint64_t M, uint64_t k, uint32_t* d_idx,
                    void* d_val, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * DGC-style top-k with a sampled global threshold and residuals (one
+ * iteration for all n workers).
+ * [Zen] section 4 (Implementation): DGC adapted to tensor parallelism --
+ * every device samples locally, the samples are gathered, one global top-k
+ * threshold is computed from them and applied locally.  [Skip] section 2:
+ * unselected gradients accumulate locally into later iterations.
+ *   1. a[w][i] = d_resid[w][i] + d_grad[w][i] (one fp32 addition);
+ *   2. S samples per worker (S clamped to M) at positions
+ *      floor((2j+1) M / (2S)), j < S; their magnitudes are pooled (n*S);
+ *   3. threshold = the ks-th largest pooled magnitude,
+ *      ks = sg_dgc_rank(density, n*S) = ceil(density * n*S) in double,
+ *      clamped to [1, n*S];
+ *   4. entries with |a| >= threshold are selected: written in ascending index
+ *      order as (i, a) to d_idx[w][*], d_val[w][*] (row stride cap; at most
+ *      cap per worker); d_count[w] = the number selected (may exceed cap);
+ *   5. d_resid[w][i] becomes 0 where selected, a elsewhere (in place).
+ * Magnitudes are compared as fp32 bit patterns without the sign; inputs are
+ * finite.  d_thr (optional) receives the threshold's bit pattern.
+ *   d_grad, d_resid [n][M] fp32 (d_resid in/out)
+ *   d_idx [n][cap] uint32, d_val [n][cap] fp32 out (may be NULL if cap == 0)
+ *   d_count [n] uint64 out; d_thr [1] uint32 out or NULL
+ * Limits: 1 <= n <= 64, 1 <= M < 2^32, S >= 1, n*S < 2^32, density >= 0.
+ * ------------------------------------------------------------------------ */
+uint64_t sg_dgc_rank(double density, uint64_t Ns);
+size_t sg_dgc_workspace_bytes(uint32_t n, uint64_t M, uint64_t S);
+int sg_dgc_select(const float* d_grad, float* d_resid, uint32_t n, uint64_t M, double density, uint64_t S,
+                  uint32_t* d_idx, float* d_val, uint64_t cap, uint64_t* d_count, uint32_t* d_thr, void* d_ws,
+                  size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * A2. Hash partition.

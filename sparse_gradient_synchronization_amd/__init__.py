@@ -56,6 +56,9 @@ SIGNATURES = {
     "sg_validate_coo": (_int, [_vp, _vp, _u32, _u64, _u64, _vp, _sz, _vp]),
     "sg_topk_workspace_bytes": (_sz, [_u32, _u64, _u64, _int]),
     "sg_topk_to_coo": (_int, [_vp, _int, _u32, _u64, _u64, _vp, _vp, _vp, _sz, _vp]),
+    "sg_dgc_rank": (_u64, [_dbl, _u64]),
+    "sg_dgc_workspace_bytes": (_sz, [_u32, _u64, _u64]),
+    "sg_dgc_select": (_int, [_vp, _vp, _u32, _u64, _dbl, _u64, _vp, _vp, _u64, _vp, _vp, _vp, _sz, _vp]),
     "sg_partition_workspace_bytes": (_sz, [_u32, _u64, _u32]),
     "sg_hash_partition": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _sz,
                                  _vp]),
@@ -382,6 +385,31 @@ def sg_allgather(reduced: torch.Tensor, bufs: torch.Tensor, ag_include=None, out
     _check(lib().sg_allgather(_p(reduced), _p(bufs), _dtype_code(bufs), n, M, _p(ag_include), _p(out), _stream()),
            "sg_allgather")
     return out
+
+
+def sg_dgc_select(grad: torch.Tensor, resid: torch.Tensor, density: float, S: int, cap: int,
+                  workspace: torch.Tensor | None = None):
+    """One DGC iteration (sampled global threshold, residuals) for grad and
+    resid [n, M] float32; resid is updated in place.  Returns (idx [n, cap]
+    int32 (uint32 bits), val [n, cap] float32, count [n] int64, thr_key
+    [1] int32)."""
+    _need_cuda(grad, resid)
+    if grad.dtype != torch.float32 or resid.dtype != torch.float32 or grad.shape != resid.shape:
+        raise ValueError("grad and resid must be float32 tensors of one shape [n, M]")
+    if not resid.is_contiguous():
+        raise ValueError("resid must be contiguous (it is updated in place)")
+    grad = grad.contiguous()
+    n, M = grad.shape
+    dev = grad.device
+    idx = torch.empty((n, max(cap, 1)), dtype=torch.int32, device=dev)
+    val = torch.empty((n, max(cap, 1)), dtype=torch.float32, device=dev)
+    cnt = torch.empty(n, dtype=torch.int64, device=dev)
+    thr = torch.empty(1, dtype=torch.int32, device=dev)
+    need = lib().sg_dgc_workspace_bytes(n, M, S)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, dev)
+    _check(lib().sg_dgc_select(_p(grad), _p(resid), n, M, float(density), S, _p(idx), _p(val), cap, _p(cnt),
+                               _p(thr), _p(ws), ws.numel(), _stream()), "sg_dgc_select")
+    return idx[:, :cap], val[:, :cap], cnt, thr
 
 
 def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,

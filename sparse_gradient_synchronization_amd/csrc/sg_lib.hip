@@ -4,6 +4,7 @@
 #include "sg_skiprs.hip"
 #include "sg_partition.hip"
 #include "sg_topk.hip"
+#include "sg_dgc.hip"
 #include "sg_merge.hip"
 #include "sg_aggregate.hip"
 #include "sg_encode.hip"
