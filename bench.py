@@ -190,6 +190,9 @@ def build_workload(name, torch, sg, gen):
 
     if name in ("dgc-top5", "cfg5"):
         bufs = dense if name == "dgc-top5" else torch.from_numpy(c["bufs"]).to(dev)
+        W["bufs"] = bufs
+        if name == "dgc-top5":
+            W["dense"] = dense
         slice_bytes = 256 * 1024
         S = L.sg_skip_num_slices(n, M, slice_bytes, 0)
         rs_out = torch.empty(M, dtype=torch.float32, device=dev)
@@ -225,6 +228,10 @@ def rs_bytes(W):
 
 
 PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built from)
+    "dgc_select": (13, "dgc_filter_kernel", ["sg_dgc.hip", "sg_topk.hip"]),
+    "skip_reduce_k": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
+    "dropout_reduce_scatter": (11, "dropout_rs_kernel", ["sg_skiprs.hip"]),
+    "allgather": (12, "allgather_kernel", ["sg_skiprs.hip"]),
     "topk_to_coo": (1, "topk_filter_kernel", ["sg_topk.hip"]),
     "hash_partition": (2, "part_scatter_kernel", ["sg_partition.hip"]),
     "aggregate": (3, "mg_merge_kernel", ["sg_merge.hip", "sg_aggregate.hip"]),
@@ -360,6 +367,97 @@ def pull_side(W, L, torch, steps):
     return out
 
 
+def time_call(L, torch, f, steps, probe=None):
+    """Average time of a call (torch events on the current stream) and of
+    its probed kernel (HIP events the library records around it)."""
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    evs = [HipEvents() for _ in range(steps)] if probe else []
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for s in range(steps):
+        if probe and L.sg_probe_set(PROBES[probe][0], evs[s].start, evs[s].stop) != 0:
+            raise RuntimeError("sg_probe_set refused probe %s" % probe)
+        a[s].record()
+        f()
+        b[s].record()
+    torch.cuda.synchronize()
+    L.sg_probe_set(0, None, None)
+    ms = sum(a[s].elapsed_time(b[s]) for s in range(steps)) / steps
+    kms = sum(e.elapsed_ms() for e in evs) / steps if probe else None
+    return ms, kms
+
+
+def next_rows(name, W, L, torch, sg, steps):
+    """The rows built after the hot path, each timed alone on this
+    workload's buffers: DGC's sampled threshold with residuals (dgc-top5),
+    the rest of the SkipReduce family (cfg5)."""
+    out = {}
+
+    def entry(nm, ms, kms, nbytes, what):
+        e = {"ms": ms, "kernel": PROBES[nm][1] if nm in PROBES else None, "kernel_ms": kms,
+             "kernel_algorithmic_bytes": nbytes, "bytes_are": what}
+        if kms and nbytes:
+            e["kernel_GBps"] = nbytes / (kms * 1e-3) / 1e9
+            e["kernel_frac"] = e["kernel_GBps"] / HBM_PEAK_GBS
+        return e
+
+    if name == "dgc-top5":
+        dense = W["dense"]
+        n, M, k = W["n"], W["M"], W["k"]
+        resid = torch.zeros_like(dense)
+        ws = torch.empty(L.sg_dgc_workspace_bytes(n, M, 16384), dtype=torch.uint8, device=dense.device)
+        box = {}
+
+        def dgc():
+            box["r"] = sg.sg_dgc_select(dense, resid, 0.05, 16384, k + k // 4, workspace=ws)
+        ms, kms = time_call(L, torch, dgc, steps, "dgc_select")
+        cnt = box["r"][2].cpu().tolist()
+        # the filter reads the gradient and the residual and writes the residual
+        out["dgc_select"] = entry("dgc_select", ms, kms, 12 * n * M, "grad and resid read, resid written")
+        out["dgc_select"].update(samples_per_worker=16384, density=0.05, selected_per_worker=cnt,
+                                 note="iterations carry the residual from call to call")
+    if name == "cfg5":
+        bufs = W["bufs"]
+        n, M = W["n"], W["M"]
+        slice_bytes = W["slice_bytes"]
+        rs_out = torch.empty(M, dtype=torch.float32, device=bufs.device)
+        S = L.sg_skip_num_slices(n, M, slice_bytes, 0)
+        cnt = torch.empty((n, S), dtype=torch.uint8, device=bufs.device)
+        kk = n // 2
+
+        def sk():
+            sg.sg_skip_reduce_k(bufs, slice_bytes, kk, True, 5, want_count=False, out=rs_out)
+        ms, kms = time_call(L, torch, sk, steps, "skip_reduce_k")
+        kept = (n - kk) * n * M // n * 4  # every slice keeps n - k contributions
+        out["skip_reduce_k"] = entry("skip_reduce_k", ms, kms, kept + 4 * M, "kept slices read, output written")
+        out["skip_reduce_k"].update(k=kk, random_offset=True)
+
+        def dr():
+            sg.sg_dropout_reduce_scatter(bufs, 0.5, 5, want_count=False, out=rs_out)
+        ms, kms = time_call(L, torch, dr, steps, "dropout_reduce_scatter")
+        out["dropout_reduce_scatter"] = entry("dropout_reduce_scatter", ms, kms, 4 * n * M + 4 * M,
+                                              "every contribution read (a dropped element shares its line), "
+                                              "output written")
+        out["dropout_reduce_scatter"]["p"] = 0.5
+        offs = [0, M // 4, M // 2, 3 * M // 4, M]
+        rates = [0.0, 0.25, 0.5, 0.75]
+
+        def se():
+            sg.sg_selective_reduce_scatter(bufs, offs, rates, slice_bytes, 5, out=rs_out)
+        ms, _ = time_call(L, torch, se, steps)
+        out["selective_reduce_scatter"] = {"ms": ms, "bucket_off": offs, "p_skip": rates}
+        red = torch.randn(M, dtype=torch.float32, device=bufs.device)
+        ag = torch.empty((n, M), dtype=torch.float32, device=bufs.device)
+
+        def al():
+            sg.sg_allgather(red, bufs, None, out=ag)
+        ms, kms = time_call(L, torch, al, steps, "allgather")
+        out["allgather"] = entry("allgather", ms, kms, 4 * M + 4 * n * M, "reduced tensor read, n copies written")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +585,9 @@ def main():
     }
     if "pull" in W:
         res["pull_side"] = pull_side(W, L, torch, steps)
+    nr = next_rows(args.workload, W, L, torch, sg, steps)
+    if nr:
+        res["next_rows"] = nr
     if not args.no_cpu_baseline:
         log("timing the oracle (single-threaded) on one step")
         res["cpu_baseline"] = cpu_baseline(args.workload, gen)
