@@ -107,6 +107,10 @@ def lib():
                                                    _f64p, C.c_uint64, C.c_uint64, C.c_int, _f64p, _f64p]
         L.orc_allgather.restype = C.c_int
         L.orc_allgather.argtypes = [_f64p, C.c_void_p, C.c_int, C.c_uint32, C.c_uint64, C.c_void_p, _f64p]
+        L.orc_hierarchical_hash.restype = C.c_int
+        L.orc_hierarchical_hash.argtypes = [_u32p, C.c_void_p, C.c_int, C.c_uint32, _u64p, C.c_uint32, C.c_uint32,
+                                            C.c_uint32, C.c_uint32, C.c_uint64, C.c_uint64, _u32p, C.c_void_p, _u64p,
+                                            _u32p, _u64p]
         L.orc_dgc_sample_pos.restype = C.c_uint64
         L.orc_dgc_sample_pos.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
         L.orc_dgc_rank.restype = C.c_uint64
@@ -245,6 +249,32 @@ def hash_partition(idx: np.ndarray, val, in_off: np.ndarray, P: int, seed: int):
                                     None if out_val is None else _ptr(out_val), part_off.reshape(-1)),
            "hash_partition")
     return out_idx, out_val, part_off
+
+
+def hierarchical_hash(idx: np.ndarray, val, in_off: np.ndarray, P: int, seed: int, k: int, r1: int, r2: int):
+    """Algorithm 1 of the Zen page (section 3.2), run sequentially.  val: None,
+    [total] or [total, D].  Returns out_idx, out_val, part_off [n, P+1],
+    slot_of [total] and counts [n, 2] (serial writes, lost entries)."""
+    idx = np.ascontiguousarray(idx, dtype=np.uint32)
+    in_off = np.ascontiguousarray(in_off, dtype=np.uint64)
+    n = in_off.size - 1
+    total = idx.size
+    D = 0 if val is None else (1 if val.ndim == 1 else val.shape[1])
+    out_idx = np.zeros(max(total, 1), dtype=np.uint32)
+    slot_of = np.zeros(max(total, 1), dtype=np.uint32)
+    part_off = np.zeros(n * (P + 1), dtype=np.uint64)
+    counts = np.zeros(max(2 * n, 1), dtype=np.uint64)
+    if val is None:
+        out_val, vp, dt = None, None, F32
+    else:
+        v = np.ascontiguousarray(val)
+        out_val = np.zeros_like(v) if total else np.zeros((1,) + v.shape[1:], v.dtype)
+        vp, dt = _ptr(v), _dtype_code(v)
+    _check(lib().orc_hierarchical_hash(idx if total else np.zeros(1, np.uint32), vp, dt, D, in_off, n, P, seed, k, r1,
+                                       r2, out_idx, None if out_val is None else _ptr(out_val), part_off, slot_of,
+                                       counts), "hierarchical_hash")
+    return (out_idx[:total], None if out_val is None else out_val[:total], part_off.reshape(n, P + 1),
+            slot_of[:total], counts[: 2 * n].reshape(n, 2))
 
 
 def aggregate(idx: np.ndarray, val, part_off: np.ndarray, M: int):

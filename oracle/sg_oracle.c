@@ -374,6 +374,93 @@ int orc_hash_partition(const uint32_t* idx, const void* val, int dtype, uint32_t
     return ORC_OK;
 }
 
+/* Algorithm 1 of [Zen] section 3.2 (hierarchical hashing with the four
+ * techniques), run sequentially, worker by worker, entries in input order.
+ * Partition memory x[p] has r1 parallel slots and r2 serial slots (Technique
+ * #1); entry e with index idx goes to partition p = h0(idx) (Technique #3)
+ * and tries the slots h_i(idx) for i = 1..k in turn (Technique #2), taking
+ * the first empty one; after k occupied slots it takes the next serial slot
+ * r1 + c_p (the atomic counter of lines 9-10, starting at r1), and is lost
+ * (counted in overflow) when the serial slots are used up.  Technique #4's
+ * read-after-write check concerns concurrent writers only; sequentially
+ * every write sticks.  Extraction (lines 19-23) reads each partition's slots
+ * in slot order.
+ * Readings: indices are 0-based, and a slot holds (entry position + 1), 0
+ * meaning empty, so the extraction gathers both the index and its values;
+ * h_i(idx) = MurmurHash2(idx as 4 LE bytes, seed + i) mod r1 (the text maps
+ * h_i to [r1]).
+ * Outputs as orc_hash_partition (out_idx, out_val, part_off [n][P+1]
+ * absolute), slot_of[out position] = the slot that held the entry;
+ * counts[w*2] = serial writes, counts[w*2+1] = entries lost. */
+int orc_hierarchical_hash(const uint32_t* idx, const void* val, int dtype, uint32_t D, const uint64_t* in_off,
+                          uint32_t n, uint32_t P, uint32_t seed, uint32_t k, uint64_t r1, uint64_t r2,
+                          uint32_t* out_idx, void* out_val, uint64_t* part_off, uint32_t* slot_of,
+                          uint64_t* counts)
+{
+    uint32_t w, p, i;
+    uint64_t e, q;
+    const uint64_t R = r1 + r2;
+    size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    uint32_t* x;
+    uint64_t* c;
+    if (P == 0 || r1 == 0 || k == 0) return ORC_EINVAL;
+    x = (uint32_t*)malloc((size_t)P * R * sizeof(uint32_t));
+    c = (uint64_t*)malloc((size_t)P * sizeof(uint64_t));
+    if (!x || !c) {
+        free(x);
+        free(c);
+        return ORC_ENOMEM;
+    }
+    for (w = 0; w < n; ++w) {
+        uint64_t o = in_off[w];
+        memset(x, 0, (size_t)P * R * sizeof(uint32_t));
+        for (p = 0; p < P; ++p) c[p] = r1;
+        counts[2 * w] = 0;
+        counts[2 * w + 1] = 0;
+        for (e = in_off[w]; e < in_off[w + 1]; ++e) {
+            uint32_t id = idx[e];
+            int placed = 0;
+            p = orc_h0(id, seed, P);
+            for (i = 1; i <= k && !placed; ++i) {
+                uint8_t b[4];
+                b[0] = (uint8_t)id;
+                b[1] = (uint8_t)(id >> 8);
+                b[2] = (uint8_t)(id >> 16);
+                b[3] = (uint8_t)(id >> 24);
+                q = orc_murmur2(b, 4, seed + i) % r1;
+                if (x[(uint64_t)p * R + q] == 0) {
+                    x[(uint64_t)p * R + q] = (uint32_t)(e - in_off[w] + 1);
+                    placed = 1;
+                }
+            }
+            if (!placed) {
+                counts[2 * w] += 1;
+                q = c[p]++;
+                if (q < R) x[(uint64_t)p * R + q] = (uint32_t)(e - in_off[w] + 1);
+                else counts[2 * w + 1] += 1;
+            }
+        }
+        for (p = 0; p < P; ++p) {
+            part_off[(uint64_t)w * (P + 1) + p] = o;
+            for (q = 0; q < R; ++q) {
+                uint32_t s = x[(uint64_t)p * R + q];
+                uint64_t src;
+                if (!s) continue;
+                src = in_off[w] + s - 1;
+                out_idx[o] = idx[src];
+                if (D > 0 && val)
+                    memcpy((char*)out_val + o * D * esz, (const char*)val + src * D * esz, D * esz);
+                if (slot_of) slot_of[o] = (uint32_t)q;
+                ++o;
+            }
+        }
+        part_off[(uint64_t)w * (P + 1) + P] = o;
+    }
+    free(x);
+    free(c);
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* A3: per-partition union-sum                                               */
 /* ------------------------------------------------------------------------ */

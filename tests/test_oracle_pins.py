@@ -821,3 +821,98 @@ def test_dgc_sample_positions_and_rank():
     assert [oracle.dgc_sample_pos(5, 9, j) for j in range(5)] == [0, 1, 2, 3, 4]
     assert oracle.dgc_rank(0.05, 100) == 5 and oracle.dgc_rank(0.051, 100) == 6
     assert oracle.dgc_rank(0.0, 100) == 1 and oracle.dgc_rank(3.0, 100) == 100
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 1 (Zen section 3.2): hierarchical hash memory
+# ---------------------------------------------------------------------------
+
+def _alg1_python(idx, in_off, P, seed, k, r1, r2):
+    """Algorithm 1 written again in plain Python (sequential, input order),
+    with the hashes from MurmurHash2 (pinned by its published check value)."""
+    n = len(in_off) - 1
+    out, slots, counts = [], [], []
+    for w in range(n):
+        R = r1 + r2
+        x = [[0] * R for _ in range(P)]
+        c = [r1] * P
+        serial = lost = 0
+        for e in range(int(in_off[w]), int(in_off[w + 1])):
+            i_ = int(idx[e])
+            b = struct.pack("<I", i_)
+            p = oracle.murmur2(b, seed) % P
+            placed = False
+            for i in range(1, k + 1):
+                q = oracle.murmur2(b, seed + i) % r1
+                if x[p][q] == 0:
+                    x[p][q] = e - int(in_off[w]) + 1
+                    placed = True
+                    break
+            if not placed:
+                serial += 1
+                q = c[p]
+                c[p] += 1
+                if q < R:
+                    x[p][q] = e - int(in_off[w]) + 1
+                else:
+                    lost += 1
+        for p in range(P):
+            for q in range(R):
+                if x[p][q]:
+                    out.append(int(idx[int(in_off[w]) + x[p][q] - 1]))
+                    slots.append(q)
+        counts.append((serial, lost))
+    return out, slots, counts
+
+
+@pytest.mark.parametrize("k,r1,r2", [(1, 16, 64), (2, 8, 8), (4, 40, 4), (3, 5, 0)])
+def test_alg1_matches_a_plain_python_replay(k, r1, r2):
+    rng = np.random.default_rng(k * 100 + r1)
+    lists = [np.sort(rng.choice(5000, size=s, replace=False)).astype(np.uint32) for s in (60, 0, 37)]
+    idx, in_off, val = gen.coo_from_lists(lists, [l.astype(np.float32) for l in lists])
+    oi, ov, po, so, cnt = oracle.hierarchical_hash(idx, val, in_off, 4, 21, k, r1, r2)
+    want, wslots, wcnt = _alg1_python(idx, in_off, 4, 21, k, r1, r2)
+    # a worker's output starts at its input offset; lost entries leave a gap
+    got = np.concatenate([oi[int(po[w, 0]):int(po[w, -1])] for w in range(po.shape[0])])
+    gslots = np.concatenate([so[int(po[w, 0]):int(po[w, -1])] for w in range(po.shape[0])])
+    gval = np.concatenate([ov[int(po[w, 0]):int(po[w, -1])] for w in range(po.shape[0])])
+    assert list(got) == want and list(gslots) == wslots
+    assert [tuple(int(v) for v in r) for r in cnt] == wcnt
+    assert np.array_equal(gval, got.astype(np.float32))  # values follow their index
+
+
+def test_alg1_membership_is_the_hash_partition():
+    # with room in the serial memory nothing is lost, and every partition
+    # holds exactly the entries that the stable grouping by h0 puts there
+    idx, in_off, val = gen.coo_zipf(77, 5, 300000, 4000, 1.1)
+    P, seed = 8, 3
+    oi, ov, po, so, cnt = oracle.hierarchical_hash(idx, val, in_off, P, seed, 2, 600, 600)
+    assert cnt[:, 1].sum() == 0
+    hi, hv, hpo = oracle.hash_partition(idx, val, in_off, P, seed)
+    assert np.array_equal(po, hpo)
+    for w in range(5):
+        for p in range(P):
+            a, b = int(po[w, p]), int(po[w, p + 1])
+            order = np.argsort(oi[a:b], kind="stable")
+            assert np.array_equal(oi[a:b][order], hi[a:b])
+            assert np.array_equal(ov[a:b][order], hv[a:b])
+
+
+def test_alg1_losses_and_rehash_collision_rate():
+    rng = np.random.default_rng(1)
+    lst = np.sort(rng.choice(1 << 22, size=40000, replace=False)).astype(np.uint32)
+    idx, in_off, val = gen.coo_from_lists([lst], [lst.astype(np.float32)])
+    P = 16
+    # no serial memory, one hash: whatever collides is lost, and the rest
+    # is kept
+    oi, _, po, so, cnt = oracle.hierarchical_hash(idx, val, in_off, P, 9, 1, 40000 // P, 0)
+    assert int(cnt[0, 1]) == int(cnt[0, 0]) and int(po[0, -1]) == 40000 - int(cnt[0, 1])
+    # parallel memory four times the nonzeros and four hashes: under 1% of
+    # the entries reach the serial memory (the page reports < 1% with four
+    # hash functions)
+    _, _, _, _, cnt4 = oracle.hierarchical_hash(idx, val, in_off, P, 9, 4, 4 * 40000 // P, 4000)
+    assert cnt4[0, 1] == 0 and cnt4[0, 0] < 0.01 * 40000
+    # more hash functions never put more entries into the serial memory here
+    serial = [int(oracle.hierarchical_hash(idx, val, in_off, P, 9, kk, 2 * 40000 // P, 40000)[4][0, 0])
+              for kk in (1, 2, 3, 4)]
+    assert serial == sorted(serial, reverse=True), serial
