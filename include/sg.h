@@ -10,6 +10,7 @@
  *   sg_dgc_select           DGC-style top-k: sampled global threshold and
  *                           residual accumulation
  *   sg_hash_partition       data-independent hash partition of COO indices
+ *   sg_hierarchical_hash    the same partition by Algorithm 1's slot memory
  *   sg_aggregate            per-partition union-sum of n workers' COO tensors
  *   sg_classmap_build,
  *   sg_encode               hash-bitmap encoding of the aggregate's indices
@@ -114,7 +115,8 @@ typedef enum sg_probe_kernel {
     SG_PROBE_SCATTER = 10,           /* scatter to dense: the scatter pass */
     SG_PROBE_DROPOUT_RS = 11,        /* per-element dropout reduce-scatter: its single kernel */
     SG_PROBE_ALLGATHER = 12,         /* all-gather: its single kernel */
-    SG_PROBE_DGC_FILTER = 13         /* DGC select: the streaming pass over gradient and residual */
+    SG_PROBE_DGC_FILTER = 13,        /* DGC select: the streaming pass over gradient and residual */
+    SG_PROBE_HHASH_INSERT = 14       /* hierarchical hash: the insertion into the slot memory */
 } sg_probe_kernel;
 int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
 
@@ -194,6 +196,36 @@ size_t sg_partition_workspace_bytes(uint32_t n, uint64_t total, uint32_t P);
 int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D, const uint64_t* d_in_off,
                       uint32_t n, uint64_t total, uint32_t P, uint32_t seed, uint32_t* d_out_idx, void* d_out_val,
                       uint64_t* d_part_off, void* d_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Algorithm 1 of [Zen] section 3.2 (hierarchical hashing), a comparison
+ * variant of sg_hash_partition with the same partition membership.
+ * Per worker, partition p has a slot memory of r1 parallel and r2 serial
+ * slots (Technique #1).  Entry e goes to p = h0(idx) (Technique #3, the same
+ * h0 as sg_hash_partition), then tries slots h_i(idx) = MurmurHash2(idx as 4
+ * LE bytes, seed + i) mod r1 for i = 1..k (Technique #2), taking one with a
+ * compare-and-swap from empty (Technique #4: no write is lost to a concurrent
+ * writer); after k occupied slots it takes the next serial slot from the
+ * partition's atomic counter (starting at r1), and is lost when the r2 serial
+ * slots are used up.  Extraction reads each partition's slots in slot order.
+ * Which entry wins a contested slot depends on thread timing, so the order
+ * inside a partition (and which entries go serial) is not fixed; the set of
+ * entries of each partition is, when nothing is lost.
+ *   inputs as sg_hash_partition (d_idx, d_val rows of D values of dt, d_in_off)
+ *   d_out_idx, d_out_val out: worker w's partitions from d_in_off[w] on, in
+ *             partition order, slot order inside a partition (lost entries
+ *             leave the worker's tail unwritten)
+ *   d_part_off [n][P+1] out (absolute; [w][P] - [w][0] = entries kept)
+ *   d_slot_of [total] out (the slot each written entry came from) or NULL
+ *   d_counts [n][2] out: serial writes, lost entries
+ * Limits: 1 <= P <= 65536, 1 <= k <= 64, r1 >= 1, r1 + r2 < 2^32,
+ * r1 + total < 2^32.
+ * ------------------------------------------------------------------------ */
+size_t sg_hierarchical_hash_workspace_bytes(uint32_t n, uint32_t P, uint64_t r1, uint64_t r2);
+int sg_hierarchical_hash(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D, const uint64_t* d_in_off,
+                         uint32_t n, uint64_t total, uint32_t P, uint32_t seed, uint32_t k, uint64_t r1, uint64_t r2,
+                         uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, uint32_t* d_slot_of,
+                         uint64_t* d_counts, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * A3. Per-partition union-sum (the server side of Push).

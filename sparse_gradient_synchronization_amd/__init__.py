@@ -56,6 +56,9 @@ SIGNATURES = {
     "sg_validate_coo": (_int, [_vp, _vp, _u32, _u64, _u64, _vp, _sz, _vp]),
     "sg_topk_workspace_bytes": (_sz, [_u32, _u64, _u64, _int]),
     "sg_topk_to_coo": (_int, [_vp, _int, _u32, _u64, _u64, _vp, _vp, _vp, _sz, _vp]),
+    "sg_hierarchical_hash_workspace_bytes": (_sz, [_u32, _u32, _u64, _u64]),
+    "sg_hierarchical_hash": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u64, _u32, _u32, _u32, _u64, _u64, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "sg_dgc_rank": (_u64, [_dbl, _u64]),
     "sg_dgc_workspace_bytes": (_sz, [_u32, _u64, _u64]),
     "sg_dgc_select": (_int, [_vp, _vp, _u32, _u64, _dbl, _u64, _vp, _vp, _u64, _vp, _vp, _vp, _sz, _vp]),
@@ -385,6 +388,35 @@ def sg_allgather(reduced: torch.Tensor, bufs: torch.Tensor, ag_include=None, out
     _check(lib().sg_allgather(_p(reduced), _p(bufs), _dtype_code(bufs), n, M, _p(ag_include), _p(out), _stream()),
            "sg_allgather")
     return out
+
+
+def sg_hierarchical_hash(idx: torch.Tensor, val, in_off: torch.Tensor, P: int, seed: int, k: int, r1: int, r2: int,
+                         want_slots: bool = False, workspace: torch.Tensor | None = None):
+    """Algorithm 1 of the Zen page (hierarchical hashing).  Returns out_idx,
+    out_val (or None), part_off [n, P+1] int64, slot_of (or None) and
+    counts [n, 2] int64 (serial writes, lost entries)."""
+    _need_cuda(idx, in_off, val)
+    idx, in_off = idx.contiguous(), in_off.contiguous()
+    n = in_off.numel() - 1
+    total = idx.numel()
+    dev = idx.device
+    D = 0 if val is None else (1 if val.dim() == 1 else val.shape[1])
+    dt = SG_F32 if val is None else _dtype_code(val)
+    if val is not None:
+        val = val.contiguous()
+    out_idx = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    out_val = None if val is None else torch.empty((max(total, 1),) + tuple(val.shape[1:]), dtype=val.dtype,
+                                                   device=dev)
+    part_off = torch.empty((n, P + 1), dtype=torch.int64, device=dev)
+    slot_of = torch.empty(max(total, 1), dtype=torch.int32, device=dev) if want_slots else None
+    counts = torch.empty((n, 2), dtype=torch.int64, device=dev)
+    need = lib().sg_hierarchical_hash_workspace_bytes(n, P, r1, r2)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, dev)
+    _check(lib().sg_hierarchical_hash(_p(idx), _p(val), dt, D, _p(in_off), n, total, P, seed, k, r1, r2, _p(out_idx),
+                                      _p(out_val), _p(part_off), _p(slot_of), _p(counts), _p(ws), ws.numel(),
+                                      _stream()), "sg_hierarchical_hash")
+    return (out_idx[:total], None if out_val is None else out_val[:total], part_off,
+            None if slot_of is None else slot_of[:total], counts)
 
 
 def sg_dgc_select(grad: torch.Tensor, resid: torch.Tensor, density: float, S: int, cap: int,

@@ -3,6 +3,7 @@
 #include "sg_common.hip"
 #include "sg_skiprs.hip"
 #include "sg_partition.hip"
+#include "sg_hhash.hip"
 #include "sg_topk.hip"
 #include "sg_dgc.hip"
 #include "sg_merge.hip"
