@@ -229,6 +229,7 @@ def rs_bytes(W):
 
 PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built from)
     "dgc_select": (13, "dgc_filter_kernel", ["sg_dgc.hip", "sg_topk.hip"]),
+    "hierarchical_hash": (14, "hh_insert_kernel", ["sg_hhash.hip"]),
     "skip_reduce_k": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
     "dropout_reduce_scatter": (11, "dropout_rs_kernel", ["sg_skiprs.hip"]),
     "allgather": (12, "allgather_kernel", ["sg_skiprs.hip"]),
@@ -455,7 +456,45 @@ def next_rows(name, W, L, torch, sg, steps):
             sg.sg_allgather(red, bufs, None, out=ag)
         ms, kms = time_call(L, torch, al, steps, "allgather")
         out["allgather"] = entry("allgather", ms, kms, 4 * M + 4 * n * M, "reduced tensor read, n copies written")
+    if name == "cfg4":
+        out["alg1_study"] = alg1_study(L, torch, sg, steps)
     return out
+
+
+def alg1_study(L, torch, sg, steps):
+    """Algorithm 1's parameter study on a synthetic 214M-element tensor (one
+    worker, 1% density, uniform distinct indices, 16 partitions): the time of
+    sg_hierarchical_hash for parallel memories of 1, 2 and 4 times the
+    nonzeros and k = 1..4 rehash functions, serial memory equal to the
+    nonzeros; beside it sg_hash_partition on the same entries."""
+    import numpy as np
+    import gen
+    M, P, seed = 214_000_000, 16, 6
+    nnz = M // 100
+    idx_np = np.sort(gen.uniform_distinct(gen.stream_seed(6, 1), 0, M, nnz)).astype(np.uint32)
+    dev = torch.device("cuda", 0)
+    idx = torch.from_numpy(idx_np.view(np.int32)).to(dev)
+    val = torch.from_numpy(gen.normal(gen.stream_seed(6, 2), nnz)).to(dev)
+    in_off = torch.tensor([0, nnz], dtype=torch.int64, device=dev)
+    res = {"M": M, "nnz": nnz, "P": P, "r2": nnz, "runs": []}
+    ws = torch.empty(L.sg_hierarchical_hash_workspace_bytes(1, P, 4 * nnz // P, nnz), dtype=torch.uint8, device=dev)
+    for alpha in (1, 2, 4):
+        r1 = alpha * nnz // P
+        for k in (1, 2, 3, 4):
+            box = {}
+
+            def run():
+                box["r"] = sg.sg_hierarchical_hash(idx, val, in_off, P, seed, k, r1, nnz, workspace=ws)
+            ms, kms = time_call(L, torch, run, steps, "hierarchical_hash")
+            cnt = box["r"][4].cpu().tolist()[0]
+            res["runs"].append({"alpha": alpha, "r1": r1, "k": k, "ms": ms, "insert_kernel_ms": kms,
+                                "serial_writes": cnt[0], "lost": cnt[1]})
+    wsp = torch.empty(L.sg_partition_workspace_bytes(1, nnz, P), dtype=torch.uint8, device=dev)
+
+    def a2():
+        sg.sg_hash_partition(idx, val, in_off, P, seed, workspace=wsp)
+    res["hash_partition_ms"], _ = time_call(L, torch, a2, steps)
+    return res
 
 
 def main():
