@@ -41,6 +41,26 @@ int fill_u64(uint64_t* d, uint64_t count, uint64_t v, hipStream_t st)
     return SG_OK;
 }
 
+static std::mutex g_stage_mu;
+static void* g_stage = nullptr;
+static size_t g_stage_cap = 0;
+
+int host_stage(size_t bytes, HostStage* out)
+{
+    out->lock = std::unique_lock<std::mutex>(g_stage_mu);
+    if (bytes > g_stage_cap) {
+        // earlier users synchronized their copies before releasing the lock
+        if (g_stage) SG_TRY(hipHostFree(g_stage));
+        g_stage = nullptr;
+        g_stage_cap = 0;
+        const size_t cap = align_up(bytes < 65536 ? 65536 : bytes, 4096);
+        SG_TRY(hipHostMalloc(&g_stage, cap, hipHostMallocDefault));
+        g_stage_cap = cap;
+    }
+    out->ptr = g_stage;
+    return SG_OK;
+}
+
 // flags[0]: offsets bad, flags[1]: index >= M, flags[2]: not strictly ascending
 __global__ void validate_kernel(const uint32_t* __restrict__ idx, const uint64_t* __restrict__ in_off, uint32_t n,
                                 uint64_t M, uint64_t total, uint32_t* flags)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/sg.h"
@@ -66,6 +68,15 @@ inline Divider make_divider(uint32_t P)
 // memset node is recorded when a caller captures the stream).
 int fill_u32(uint32_t* d, uint64_t count, uint32_t v, hipStream_t st);
 int fill_u64(uint64_t* d, uint64_t count, uint64_t v, hipStream_t st);
+
+// Small results that an entry point returns on the host travel in one copy
+// into a pinned staging buffer of the process (grown on demand).  The lock
+// is held from the copy to the end of the unpacking.
+struct HostStage {
+    std::unique_lock<std::mutex> lock;
+    void* ptr = nullptr;
+};
+int host_stage(size_t bytes, HostStage* out);
 
 
 // measurement hook (see sg_probe_set in sg.h)

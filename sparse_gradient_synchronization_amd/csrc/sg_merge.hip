@@ -93,6 +93,7 @@ struct MergeParams {
     uint32_t Ps;            // parts for skew
     double inv_m;           // 1 / M
     uint32_t seed;
+    const uint32_t* seed_at; // when set, the seed is read here on the device (a class map header)
     int hashed;
     Divider div;
 };
@@ -511,6 +512,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
     const uint32_t T = p.G * p.NT;
     const uint64_t span = 1ull << p.tb;
     uint64_t union_cnt = 0;
+    const uint32_t hseed = (MODE == MODE_STATS && p.seed_at) ? p.seed_at[0] : p.seed;
     if (MODE == MODE_STATS) {
         for (uint32_t i = threadIdx.x; i < 2 * p.Ps; i += MG_THREADS) bs.part[i] = 0;
         for (uint32_t i = threadIdx.x; i < p.npairs; i += MG_THREADS) bs.pairs[i] = 0;
@@ -697,7 +699,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                         m = sm.mask[q];
                     }
                     count_sorted_parts(bs.part, has ? contig_part(k, p.M, p.Ps, p.inv_m) : 0u, has);
-                    if (p.hashed) count_parts(bs.part + p.Ps, has ? h0(k, p.seed, p.div) : 0u, has, p.Ps);
+                    if (p.hashed) count_parts(bs.part + p.Ps, has ? h0(k, hseed, p.div) : 0u, has, p.Ps);
                     for (uint32_t a = 0; a < n; ++a) {
                         const uint64_t v = ballot((m >> a) & 1ull);
                         if (lane == 0) sm.vm[a] = v;

@@ -188,7 +188,6 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
     const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
 
     for (uint32_t i = threadIdx.x; i < PT_WAVES * 256; i += PT_THREADS) (&wave_cnt[0][0])[i] = 0;
-    for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) dbase[i] = p.counts[(uint64_t)t * p.P + i];
     __syncthreads();
 
     // 1. stable ranks inside each wave's quarter of the tile
@@ -196,12 +195,20 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
     uint8_t part_r[PT_STRIPS];
     uint16_t rank_r[PT_STRIPS];
     VT val_r[STAGE_VALS ? PT_STRIPS : 1];
+    // every strip's loads first (unconditional, clamped to the tile), so
+    // they are in flight together
+#pragma unroll
+    for (int s = 0; s < PT_STRIPS; ++s) {
+        const uint32_t le = wid * (PT_TILE / PT_WAVES) + s * SG_WAVE + lane;
+        const uint64_t src = e0 + (le < len ? le : len - 1);
+        key_r[s] = p.idx[src];
+        if (STAGE_VALS) val_r[s] = static_cast<const VT*>(p.val)[src];
+    }
 #pragma unroll
     for (int s = 0; s < PT_STRIPS; ++s) {
         const uint32_t le = wid * (PT_TILE / PT_WAVES) + s * SG_WAVE + lane;
         const bool valid = le < len;
-        uint32_t key = valid ? p.idx[e0 + le] : 0u;
-        if (STAGE_VALS) val_r[s] = valid ? static_cast<const VT*>(p.val)[e0 + le] : VT(0);
+        const uint32_t key = key_r[s];
         uint32_t q = valid ? h0(key, p.seed, p.div) : 0u;
         uint64_t peers = ballot(valid);
         for (uint32_t bit = 0; bit < p.nbits; ++bit) {
@@ -211,10 +218,10 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
         uint32_t below = popc64(peers & lanemask_lt());
         uint32_t base = valid ? wave_cnt[wid][q] : 0u;
         if (valid && below == 0) wave_cnt[wid][q] = base + popc64(peers);
-        key_r[s] = key;
         part_r[s] = (uint8_t)q;
         rank_r[s] = (uint16_t)(base + below);
     }
+    for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) dbase[i] = p.counts[(uint64_t)t * p.P + i];
     __syncthreads();
 
     // 2. per-partition wave prefixes and staging starts

@@ -15,17 +15,37 @@
 
 namespace sg {
 
+// The counts and everything else the host needs after the passes sit in one
+// block of u64, copied to the host at once: row, wcontig, whashed, then the
+// tail written by st_pack_kernel.
 struct StatsCounts {
     uint64_t* row;      // [npairs + 1 + 2*Ps]: pair counts (a <= b, row-major), union, union per part
     uint64_t* wcontig;  // [n*Ps]
     uint64_t* whashed;  // [n*Ps]
+    uint64_t* tail;     // [n + 1 + Ps + 4]: worker offsets, class sizes, map magic, P, M, seed
+    uint64_t words;     // of the whole block
 };
+
+__global__ void st_pack_kernel(const uint64_t* __restrict__ in_off, uint32_t n, const uint64_t* __restrict__ class_size,
+                               const CmapHeader* __restrict__ hdr, uint32_t P, uint64_t* __restrict__ tail)
+{
+    for (uint32_t i = threadIdx.x; i <= n; i += blockDim.x) tail[i] = in_off[i];
+    for (uint32_t i = threadIdx.x; i < P; i += blockDim.x) tail[n + 1 + i] = class_size ? class_size[i] : 0ull;
+    if (threadIdx.x == 0) {
+        uint64_t* h = tail + n + 1 + P;
+        h[0] = hdr ? hdr->magic : 0ull;
+        h[1] = hdr ? hdr->P : 0ull;
+        h[2] = hdr ? hdr->M : 0ull;
+        h[3] = hdr ? hdr->seed : 0ull;
+    }
+}
 
 // per-worker counts per contiguous part and per hash class; one block per
 // 4096-entry chunk of a worker (chunk plan of the merge engine, G = 1)
 __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, StatsCounts c)
 {
     __shared__ uint32_t hc[256], hh[256];
+    const uint32_t hseed = p.seed_at ? p.seed_at[0] : p.seed;
     for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
     __syncthreads();
     for (uint32_t ch = blockIdx.x; ch < p.nchunks_max; ch += gridDim.x) {
@@ -47,7 +67,7 @@ __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, S
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 count_sorted_parts(hc, has[u] ? contig_part(key[u], p.M, p.Ps, p.inv_m) : 0u, has[u]);
-                if (p.hashed && has[u]) atomicAdd(&hh[h0(key[u], p.seed, p.div)], 1u);
+                if (p.hashed && has[u]) atomicAdd(&hh[h0(key[u], hseed, p.div)], 1u);
             }
         }
         // flush when the next chunk of this block belongs to another worker (or there is none)
@@ -119,9 +139,11 @@ static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* 
     } else {
         merge_carve(c, p, MODE_STATS);
     }
-    k->row = c.take<uint64_t>(p->st_row);
-    k->wcontig = c.take<uint64_t>((uint64_t)n * P);
-    k->whashed = c.take<uint64_t>((uint64_t)n * P);
+    k->words = (uint64_t)p->st_row + 2ull * n * P + n + 1 + P + 4;
+    k->row = c.take<uint64_t>(k->words);
+    k->wcontig = k->row ? k->row + p->st_row : nullptr;
+    k->whashed = k->wcontig ? k->wcontig + (uint64_t)n * P : nullptr;
+    k->tail = k->whashed ? k->whashed + (uint64_t)n * P : nullptr;
     return c.bytes();
 }
 
@@ -220,18 +242,15 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     if (ws_bytes < sg_stats_workspace_bytes(n, M, total, P)) return SG_ECAPACITY;
     hipStream_t st = as_stream(stream);
 
-    uint32_t seed = 0;
-    std::vector<uint64_t> class_size(P, 0);
+    // The class map's header (seed, and its magic, P and M, checked after the
+    // passes) and class sizes are read on the device: no copy before the
+    // kernels.  Its layout follows from (M, P) alone, so a wrong map cannot
+    // send a read out of the cmap_bytes checked here.
+    CmapPtrs cm{};
     if (d_cmap) {
         const CmapLayout L = cmap_layout(M, P);
         if (cmap_bytes < L.bytes) return SG_ECAPACITY;
-        CmapHeader h;
-        CmapPtrs q = cmap_ptrs(const_cast<void*>(d_cmap), L);
-        SG_TRY(hipMemcpyAsync(&h, q.hdr, sizeof(h), hipMemcpyDeviceToHost, st));
-        SG_TRY(hipMemcpyAsync(class_size.data(), q.class_size, 8ull * P, hipMemcpyDeviceToHost, st));
-        SG_TRY(hipStreamSynchronize(st));
-        if (h.magic != CM_MAGIC || h.P != P || h.M != M) return SG_EINVAL;
-        seed = h.seed;
+        cm = cmap_ptrs(const_cast<void*>(d_cmap), L);
     }
 
     const bool windowed = total > 0 && stats_windowed(n, P, d_cmap != nullptr);
@@ -243,13 +262,12 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     stats_carve(c, &p, P, &k, windowed ? &sw : nullptr);
     p.idx = d_idx;
     p.off = d_in_off;
-    p.seed = seed;
+    p.seed = 0;
+    p.seed_at = d_cmap ? &cm.hdr->seed : nullptr;
     p.hashed = d_cmap != nullptr;
     p.div = make_divider(P);
     // per-worker part counters are accumulated with atomics: zero them
-    int rc = fill_u64(k.wcontig, (uint64_t)n * P, 0, st);
-    if (rc) return rc;
-    rc = fill_u64(k.whashed, (uint64_t)n * P, 0, st);
+    int rc = fill_u64(k.wcontig, 2ull * n * P, 0, st); // wcontig and whashed are adjacent
     if (rc) return rc;
     if (windowed) {
         sw.planes = nullptr;
@@ -269,13 +287,27 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     st_entries_kernel<<<p.nchunks_max < 2048 ? p.nchunks_max : 2048, MG_THREADS, 0, st>>>(p, k);
     SG_TRY_LAUNCH();
 
-    std::vector<uint64_t> row(p.st_row), wc((size_t)n * P), wh((size_t)n * P), off(n + 1);
+    st_pack_kernel<<<1, 256, 0, st>>>(d_in_off, n, d_cmap ? cm.class_size : nullptr, d_cmap ? cm.hdr : nullptr, P,
+                                      k.tail);
+    SG_TRY_LAUNCH();
+
+    std::vector<uint64_t> blk(k.words);
+    {
+        HostStage hs;
+        rc = host_stage(8ull * k.words, &hs);
+        if (rc) return rc;
+        SG_TRY(hipMemcpyAsync(hs.ptr, k.row, 8ull * k.words, hipMemcpyDeviceToHost, st));
+        SG_TRY(hipStreamSynchronize(st));
+        std::memcpy(blk.data(), hs.ptr, 8ull * k.words);
+    }
+    uint64_t* row = blk.data();
+    const uint64_t* wc = row + p.st_row;
+    const uint64_t* wh = wc + (size_t)n * P;
+    const uint64_t* off = wh + (size_t)n * P;
+    const uint64_t* class_size = off + n + 1;
+    const uint64_t* hdr = class_size + P;
+    if (d_cmap && (hdr[0] != CM_MAGIC || hdr[1] != P || hdr[2] != M)) return SG_EINVAL;
     std::vector<uint64_t> inter((size_t)n * n, 0);
-    SG_TRY(hipMemcpyAsync(row.data(), k.row, 8ull * p.st_row, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(wc.data(), k.wcontig, 8ull * n * P, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(wh.data(), k.whashed, 8ull * n * P, hipMemcpyDeviceToHost, st));
-    SG_TRY(hipMemcpyAsync(off.data(), d_in_off, 8ull * (n + 1), hipMemcpyDeviceToHost, st));
-    SG_TRY(hipStreamSynchronize(st));
     for (uint32_t a = 0, pi = 0; a < n; ++a)
         for (uint32_t b = a; b < n; ++b, ++pi) inter[(size_t)a * n + b] = row[pi];
     const uint64_t uni = row[p.npairs];
@@ -334,10 +366,10 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
         for (uint32_t i = 0; i < P; ++i) o->class_size[i] = class_size[i];
         for (uint32_t a = 0; a < n; ++a) {
             for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)a * P + i] = wh[(size_t)a * P + i];
-            o->skew_hashed[a] = skew_of(&wh[(size_t)a * P], class_size.data(), P, M, o->nnz[a]);
+            o->skew_hashed[a] = skew_of(&wh[(size_t)a * P], class_size, P, M, o->nnz[a]);
         }
         for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)n * P + i] = uh[i];
-        o->skew_hashed[n] = skew_of(uh, class_size.data(), P, M, o->union_size);
+        o->skew_hashed[n] = skew_of(uh, class_size, P, M, o->union_size);
         for (uint32_t a = 0; a < n; ++a) {
             if (o->nnz[a] == 0) continue;
             for (uint32_t i = 0; i < P; ++i) {
