@@ -233,7 +233,7 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "skip_reduce_k": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
     "dropout_reduce_scatter": (11, "dropout_rs_kernel", ["sg_skiprs.hip"]),
     "allgather": (12, "allgather_kernel", ["sg_skiprs.hip"]),
-    "topk_to_coo": (1, "topk_filter_kernel", ["sg_topk.hip"]),
+    "topk_to_coo": (1, "topk_filter_pipe_kernel", ["sg_topk.hip"]),
     "hash_partition": (2, "part_scatter_kernel", ["sg_partition.hip"]),
     "aggregate": (3, "mg_merge_kernel", ["sg_merge.hip", "sg_aggregate.hip"]),
     "encode": (4, "enc_kernel", ["sg_encode.hip"]),

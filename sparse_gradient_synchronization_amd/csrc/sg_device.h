@@ -40,6 +40,13 @@ __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 __device__ __forceinline__ uint32_t popc64(uint64_t x) { return (uint32_t)__popcll(x); }
+// set bits of m in the lanes below this one (two mbcnt instructions)
+__device__ __forceinline__ uint32_t count_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+// a value every lane holds alike, moved to a scalar register
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
 // Cross-lane moves by DPP (data-parallel primitives of the GFX9 ISA family):
 // a lane reads another lane's register inside the VALU, without the LDS

@@ -282,6 +282,174 @@ __device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uin
     }
 }
 
+// A full tile whose 16-byte vectors are already in registers: the same
+// selection and slot order as filter_tile.  The tile's slot bases are scalar
+// and stores take 32-bit byte offsets; each lane stores its selected
+// elements one per round, so a round's store carries every lane that still
+// has one.
+template <int EPV>
+__device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w, uint32_t t, uint32_t lo, uint32_t hi,
+                                                 const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+{
+    constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
+    constexpr int CB = EPV == 4 ? 3 : 4; // bits of a per-lane count in [0, EPV]
+    const uint32_t lane = lane_id();
+    const uint32_t tile0 = t * TK_TILE;
+    const uint64_t g = (uint64_t)w * p.NT + t;
+    char* const sidx = reinterpret_cast<char*>(p.slot_idx + g * TK_TILE);
+    char* const sval = reinterpret_cast<char*>(p.slot_val + g * TK_TILE);
+    char* const skey = reinterpret_cast<char*>(p.slot_key + g * TK_TILE);
+    uint32_t run_ge = 0, run_ca = 0;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        uint32_t bits[EPV];
+        if constexpr (EPV == 4) {
+            bits[0] = x[i].x;
+            bits[1] = x[i].y;
+            bits[2] = x[i].z;
+            bits[3] = x[i].w;
+        } else {
+            const uint32_t q[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+            for (int v = 0; v < EPV; ++v) bits[v] = (q[v / 2] >> (16 * (v % 2))) & 0xffffu;
+        }
+        const uint32_t e0 = tile0 + i * (SG_WAVE * EPV) + lane * EPV;
+        uint32_t fge = 0, fca = 0;
+#pragma unroll
+        for (int v = 0; v < EPV; ++v) {
+            const uint32_t key = key_of_bits(bits[v], p.bf16);
+            fge |= (uint32_t)(key >= lo) << v;
+            fca |= (uint32_t)(key >= lo && key <= hi) << v;
+        }
+        const uint32_t c = (uint32_t)__popc(fge);
+        uint32_t pos = run_ge;
+#pragma unroll
+        for (int b = 0; b < CB; ++b) {
+            const uint64_t m = ballot((c >> b) & 1u);
+            pos += count_below(m) << b;
+            run_ge += popc64(m) << b;
+        }
+        for (uint32_t f = fge; ballot(f != 0);) {
+            if (f) {
+                const uint32_t v = (uint32_t)__builtin_ctz(f);
+                uint32_t b = bits[0];
+#pragma unroll
+                for (int u = 1; u < EPV; ++u) b = v == (uint32_t)u ? bits[u] : b;
+                *reinterpret_cast<uint32_t*>(sidx + pos * 4u) = e0 + v;
+                *reinterpret_cast<uint32_t*>(sval + pos * 4u) = b;
+                ++pos;
+                f &= f - 1u;
+            }
+        }
+        if (ballot(fca != 0)) { // candidates are rare: the band is narrow
+            const uint32_t cc = (uint32_t)__popc(fca);
+            uint32_t cpos = run_ca;
+#pragma unroll
+            for (int b = 0; b < CB; ++b) {
+                const uint64_t m = ballot((cc >> b) & 1u);
+                cpos += count_below(m) << b;
+                run_ca += popc64(m) << b;
+            }
+            for (uint32_t f = fca; ballot(f != 0);) {
+                if (f) {
+                    const uint32_t v = (uint32_t)__builtin_ctz(f);
+                    uint32_t b = bits[0];
+#pragma unroll
+                    for (int u = 1; u < EPV; ++u) b = v == (uint32_t)u ? bits[u] : b;
+                    *reinterpret_cast<uint32_t*>(skey + cpos * 4u) = key_of_bits(b, p.bf16);
+                    ++cpos;
+                    f &= f - 1u;
+                }
+            }
+        }
+    }
+    if (lane == 0) {
+        p.tcnt[g] = run_ge;
+        p.ccnt[g] = run_ca;
+    }
+}
+
+template <int EPV>
+__device__ __forceinline__ void load_full_tile(const TopkParams& p, uint32_t w, uint32_t t,
+                                               u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+{
+    constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
+    // 16 bytes per lane; the dense data is read once, so the load does not
+    // keep it in the caches
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(p.dense) +
+                                                      ((uint64_t)w * p.M + (uint64_t)t * TK_TILE) * (EPV == 4 ? 4u : 2u));
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) x[i] = __builtin_nontemporal_load(src + i * SG_WAVE + lane_id());
+}
+
+// A wave's walk over the tiles g = w * NT + t, g0, g0 + stride, ...: (w, t)
+// advanced without a division per step.
+struct TileWalk {
+    uint32_t w, t, dw, dt, NT, n;
+    __device__ bool valid() const { return w < n; }
+    __device__ void next()
+    {
+        t += dt;
+        w += dw;
+        if (t >= NT) {
+            t -= NT;
+            ++w;
+        }
+    }
+};
+
+// The main pass over 16-byte aligned rows with M >= TK_TILE: while a wave
+// works on one tile, the loads of its next tile are in flight (two register
+// buffers used in turn).  Every step issues the same loads (a tile that is
+// not full, or past the end, reads the full tile 0 of worker 0 instead and
+// ignores it), so the waits before each tile's use count only the loads
+// issued after it.  Tiles at the end of a row shorter than TK_TILE go
+// through filter_tile.
+template <int EPV>
+__device__ __forceinline__ void prefetch_tile(const TopkParams& p, const TileWalk& c, uint32_t full_tiles,
+                                              uint32_t& lo, uint32_t& hi, u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+{
+    const uint32_t w = c.valid() ? c.w : 0u;
+    const uint2 band = *reinterpret_cast<const uint2*>(&p.st[w].lo);
+    lo = band.x;
+    hi = band.y;
+    const bool full = c.valid() && c.t < full_tiles;
+    load_full_tile<EPV>(p, full ? c.w : 0u, full ? c.t : 0u, x);
+}
+
+template <int EPV>
+__device__ __forceinline__ void filter_step(const TopkParams& p, const TileWalk& c, uint32_t full_tiles, uint32_t lo,
+                                            uint32_t hi, const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+{
+    if (c.t < full_tiles) filter_full_tile<EPV>(p, c.w, c.t, lo, hi, x);
+    else filter_tile<EPV, false>(p, c.w, c.t, lo, hi);
+}
+
+template <int EPV>
+__global__ __launch_bounds__(TK_THREADS) void topk_filter_pipe_kernel(TopkParams p)
+{
+    constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
+    const uint32_t full_tiles = (uint32_t)(p.M / TK_TILE); // tiles t < full_tiles of a row are full
+    const uint32_t g0 = blockIdx.x * (TK_THREADS / SG_WAVE) + uniform(threadIdx.x / SG_WAVE);
+    const uint32_t stride = gridDim.x * (TK_THREADS / SG_WAVE);
+    TileWalk cur = {g0 / p.NT, g0 % p.NT, stride / p.NT, stride % p.NT, p.NT, p.n};
+    u32x4 a[ITERS], b[ITERS];
+    uint32_t lo_a, hi_a, lo_b, hi_b;
+    prefetch_tile<EPV>(p, cur, full_tiles, lo_a, hi_a, a);
+    while (cur.valid()) {
+        TileWalk nx = cur;
+        nx.next();
+        prefetch_tile<EPV>(p, nx, full_tiles, lo_b, hi_b, b);
+        filter_step<EPV>(p, cur, full_tiles, lo_a, hi_a, a);
+        cur = nx;
+        if (!cur.valid()) break;
+        nx.next();
+        prefetch_tile<EPV>(p, nx, full_tiles, lo_a, hi_a, a);
+        filter_step<EPV>(p, cur, full_tiles, lo_b, hi_b, b);
+        cur = nx;
+    }
+}
+
 // REDO: process only the workers whose band missed (st.redo == 1); the whole
 // launch returns at once when there are none.
 template <int EPV, bool VEC, bool REDO>
@@ -731,10 +899,10 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
         if (pass == 0) {
             probe_begin(SG_PROBE_TOPK_FILTER, st);
             if (p.bf16) {
-                if (rows_aligned) topk_filter_kernel<8, true, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+                if (rows_aligned && M >= TK_TILE) topk_filter_pipe_kernel<8><<<fgrid, TK_THREADS, 0, st>>>(p);
                 else topk_filter_kernel<8, false, false><<<fgrid, TK_THREADS, 0, st>>>(p);
             } else {
-                if (rows_aligned) topk_filter_kernel<4, true, false><<<fgrid, TK_THREADS, 0, st>>>(p);
+                if (rows_aligned && M >= TK_TILE) topk_filter_pipe_kernel<4><<<fgrid, TK_THREADS, 0, st>>>(p);
                 else topk_filter_kernel<4, false, false><<<fgrid, TK_THREADS, 0, st>>>(p);
             }
             SG_TRY_LAUNCH();

@@ -24,7 +24,7 @@ def _check(dense, k, bf16=False):
     assert sg.sg_device_error() == 0
 
 
-@pytest.mark.parametrize("M", [1, 5, 100, 4096, 4097, 16383, 16384, 16385, 100003, 1 << 18])
+@pytest.mark.parametrize("M", [1, 5, 100, 1024, 2048, 4096, 4097, 5000, 12288, 16383, 16384, 16385, 100003, 1 << 18])
 def test_topk_shapes(M):
     dense = gen.dense_normal(200 + M % 97, 3, M)
     for k in sorted({1, max(1, M // 20), M // 2, M - 1, M} - {0}):
