@@ -59,7 +59,7 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
     mg_plan_kernel<<<1, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_AGGREGATE_BND, st);
-    mg_bnd_kernel<<<p.nchunks_max < 1024 ? p.nchunks_max : 1024, 512, 0, st>>>(p);
+    mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_BND, st);
     const uint64_t cells = R * (p.NT + 1);
@@ -92,7 +92,7 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
         SG_TRY_LAUNCH();
         mg_scan_top_kernel<<<1, 1024, 0, st>>>(p);
         SG_TRY_LAUNCH();
-        const uint64_t pblocks = ceil_div(T, 4 * MG_PLACE_TILES);
+        const uint64_t pblocks = ceil_div(T, 4) < 65536 ? ceil_div(T, 4) : 65536;
         mg_place_kernel<<<(unsigned)pblocks, 256, 0, st>>>(p);
         SG_TRY_LAUNCH();
         return SG_OK;

@@ -45,8 +45,19 @@ __device__ __forceinline__ uint32_t count_below(uint64_t m)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+// Waits until every vector memory operation of the wave is done (the GFX9
+// s_waitcnt with vmcnt = 0 and the other counters left at their maxima).
+// The vector memory counter covers stores as well as loads, so once a store
+// is issued the compiler can no longer wait for an earlier load alone: a
+// kernel that loads a batch and then stores waits for the batch here, before
+// its first store, and needs no wait after.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 // a value every lane holds alike, moved to a scalar register
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    return ((uint64_t)uniform((uint32_t)(v >> 32)) << 32) | uniform((uint32_t)v);
+}
 
 // Cross-lane moves by DPP (data-parallel primitives of the GFX9 ISA family):
 // a lane reads another lane's register inside the VALU, without the LDS

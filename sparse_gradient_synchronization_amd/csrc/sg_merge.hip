@@ -163,9 +163,10 @@ __device__ __forceinline__ uint32_t tile_of(const MergeParams& p, uint32_t key)
 }
 
 // bnd[run][b] = first position (relative to the run) whose key is >= b * 2^tb;
-// bnd[run][NT] = the run's length.  Each thread takes 8 consecutive entries of
-// a 4096-entry chunk, loads them at once, then writes the tile starts that
-// fall between them.
+// bnd[run][NT] = the run's length.  A block takes a 4096-entry chunk; thread
+// t looks at entries t, t + 512, ... of it (coalesced loads), each with the
+// entry before it, and writes the tile starts that fall between the two.
+// All loads are issued and waited for before the first store.
 __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 {
     constexpr int E = MG_CHUNK / 512;
@@ -174,24 +175,25 @@ __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
     if (rec.x == 0xffffffffu) continue;
     const uint32_t rp = rec.x, g = rp % p.G, w = rp / p.G;
     const uint64_t s = rec.w, len = rec.z;
-    const uint64_t j0 = (uint64_t)rec.y + (uint64_t)threadIdx.x * E;
     uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
-    uint32_t key[E + 1];
+    uint32_t key[E], prev[E];
 #pragma unroll
-    for (int u = 0; u <= E; ++u) { // key[0] is the entry before the thread's first
-        const int64_t j = (int64_t)j0 + u - 1;
-        key[u] = (j >= 0 && (uint64_t)j < len) ? p.idx[s + j] : 0u;
+    for (int u = 0; u < E; ++u) {
+        const uint64_t j = (uint64_t)rec.y + (uint64_t)u * 512 + threadIdx.x;
+        const uint64_t jc = j < len ? j : len - 1; // len > 0: the run has this chunk
+        key[u] = p.idx[s + jc];
+        prev[u] = p.idx[s + (jc > 0 ? jc - 1 : 0)];
     }
-    int64_t pb = j0 > 0 && j0 <= len ? (int64_t)tile_of(p, key[0]) : -1;
+    wait_vmem();
 #pragma unroll
-    for (int u = 1; u <= E; ++u) {
-        const uint64_t j = j0 + u - 1;
+    for (int u = 0; u < E; ++u) {
+        const uint64_t j = (uint64_t)rec.y + (uint64_t)u * 512 + threadIdx.x;
         if (j >= len) break;
         const uint32_t b = tile_of(p, key[u]);
-        for (int64_t x = pb + 1; x <= (int64_t)b; ++x) row[x] = (uint32_t)j;
+        const uint32_t x0 = j > 0 ? tile_of(p, prev[u]) + 1 : 0u;
+        for (uint32_t x = x0; x <= b; ++x) row[x] = (uint32_t)j;
         if (j == len - 1)
             for (uint64_t x = (uint64_t)b + 1; x <= p.NT; ++x) row[x] = (uint32_t)len;
-        pb = b;
     }
     }
 }
@@ -801,61 +803,53 @@ __global__ __launch_bounds__(1024) void mg_scan_top_kernel(MergeParams p)
     if (threadIdx.x == 0) p.agg_off[p.G] = carry;
 }
 
-// One wave per 8 tiles: their offsets in one load round, then the first 64
-// staged entries of all 8 at once, so the copies of the tiles overlap.
-constexpr int MG_PLACE_TILES = 8;
+// One wave per tile: the tile's staged keys (and values) are read in
+// batches of MG_PLACE_CHUNKS x 64 entries, all loads of a batch in flight
+// before it is waited for once and written out.
+constexpr int MG_PLACE_CHUNKS = 16;
 
 __global__ __launch_bounds__(256) void mg_place_kernel(MergeParams p)
 {
     const uint32_t T = p.G * p.NT;
-    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
-    for (uint64_t t0 = ((uint64_t)blockIdx.x * 4 + wid) * MG_PLACE_TILES; t0 < T;
-         t0 += (uint64_t)gridDim.x * 4 * MG_PLACE_TILES) {
-    const uint64_t t = t0 + lane;
-    const bool mine = lane < (uint32_t)MG_PLACE_TILES && t < T;
-    uint32_t c = 0;
-    uint64_t sb = 0, ob = 0;
-    if (mine) {
-        c = p.tile_cnt[t];
-        sb = p.tile_sb[t];
-        ob = p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK];
-        if (t % p.NT == 0) p.agg_off[t / p.NT] = ob;
+    const uint32_t lane = lane_id();
+    for (uint32_t t = blockIdx.x * 4 + uniform(threadIdx.x / SG_WAVE); t < T; t += gridDim.x * 4) {
+        uint32_t c = uniform(p.tile_cnt[t]);
+        const uint64_t sb = uniform64(p.tile_sb[t]);
+        const uint64_t ob = uniform64(p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK]);
+        if (t % p.NT == 0 && lane == 0) p.agg_off[t / p.NT] = ob;
         if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
-            report_error(kDevErrPartition);
+            if (lane == 0) report_error(kDevErrPartition);
             c = 0;
         }
-    }
-    const uint32_t sb_lo = (uint32_t)sb, sb_hi = (uint32_t)(sb >> 32), ob_lo = (uint32_t)ob, ob_hi = (uint32_t)(ob >> 32);
-    for (uint32_t k0 = 0; k0 < (uint32_t)MG_PLACE_TILES; k0 += 8) {
-        uint32_t ck[8], vi[8], vv[8];
-        uint64_t s0[8], d0[8];
+        if (c == 0) continue;
+        if (p.D <= 1) {
+            for (uint32_t k0 = 0; k0 < c; k0 += MG_PLACE_CHUNKS * SG_WAVE) {
+                uint32_t vi[MG_PLACE_CHUNKS], vv[MG_PLACE_CHUNKS];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int k = (int)k0 + u;
-            ck[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
-            s0[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sb_hi, k) << 32) |
-                    (uint32_t)__builtin_amdgcn_readlane((int)sb_lo, k);
-            d0[u] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ob_hi, k) << 32) |
-                    (uint32_t)__builtin_amdgcn_readlane((int)ob_lo, k);
-            vi[u] = lane < ck[u] ? p.stage_idx[s0[u] + lane] : 0u;
-            vv[u] = lane < ck[u] && p.D == 1 ? __float_as_uint(p.stage_val[s0[u] + lane]) : 0u;
-        }
+                for (int u = 0; u < MG_PLACE_CHUNKS; ++u) {
+                    vi[u] = vv[u] = 0u;
+                    if (k0 + u * SG_WAVE < c) { // uniform: the chunks the tile has
+                        const uint32_t i = k0 + u * SG_WAVE + lane;
+                        const uint64_t src = sb + (i < c ? i : c - 1);
+                        vi[u] = p.stage_idx[src];
+                        vv[u] = p.D == 1 ? __float_as_uint(p.stage_val[src]) : 0u;
+                    }
+                }
+                wait_vmem();
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (lane < ck[u]) {
-                p.agg_idx[d0[u] + lane] = vi[u];
-                if (p.D == 1) p.agg_val[d0[u] + lane] = __uint_as_float(vv[u]);
+                for (int u = 0; u < MG_PLACE_CHUNKS; ++u) {
+                    const uint32_t i = k0 + u * SG_WAVE + lane;
+                    if (i < c) {
+                        p.agg_idx[ob + i] = vi[u];
+                        if (p.D == 1) p.agg_val[ob + i] = __uint_as_float(vv[u]);
+                    }
+                }
             }
-            for (uint32_t i = SG_WAVE + lane; i < ck[u]; i += SG_WAVE) { // tiles with more than 64 keys
-                p.agg_idx[d0[u] + i] = p.stage_idx[s0[u] + i];
-                if (p.D == 1) p.agg_val[d0[u] + i] = p.stage_val[s0[u] + i];
-            }
-            if (p.D > 1) {
-                const uint64_t cnt = (uint64_t)ck[u] * p.D;
-                for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[d0[u] * p.D + i] = p.stage_val[s0[u] * p.D + i];
-            }
+        } else {
+            for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_idx[ob + i] = p.stage_idx[sb + i];
+            const uint64_t cnt = (uint64_t)c * p.D;
+            for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[ob * p.D + i] = p.stage_val[sb * p.D + i];
         }
-    }
     }
 }
 

@@ -107,8 +107,19 @@ __global__ __launch_bounds__(PT_THREADS) void part_hist_kernel(PartParams p)
     for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) hist[i] = 0;
     __syncthreads();
     bool live = tile_bounds(p, t, w, e0, e1);
-    if (live)
-        for (uint64_t e = e0 + threadIdx.x; e < e1; e += PT_THREADS) atomicAdd(&hist[h0(p.idx[e], p.seed, p.div)], 1u);
+    if (live) {
+        // every load first (clamped to the tile), then the counts
+        const uint32_t len = (uint32_t)(e1 - e0);
+        uint32_t key[PT_STRIPS];
+#pragma unroll
+        for (int s = 0; s < PT_STRIPS; ++s) {
+            const uint32_t le = s * PT_THREADS + threadIdx.x;
+            key[s] = p.idx[e0 + (le < len ? le : len - 1)];
+        }
+#pragma unroll
+        for (int s = 0; s < PT_STRIPS; ++s)
+            if (s * PT_THREADS + threadIdx.x < len) atomicAdd(&hist[h0(key[s], p.seed, p.div)], 1u);
+    }
     __syncthreads();
     if (t < p.max_tiles)
         for (uint32_t i = threadIdx.x; i < p.P; i += PT_THREADS) p.counts[(uint64_t)t * p.P + i] = live ? hist[i] : 0u;

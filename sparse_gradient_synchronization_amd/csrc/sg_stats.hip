@@ -9,8 +9,9 @@
 // is a 64-bit mask; per 64 indices a wave turns the masks into one ballot
 // word per worker and adds popcount(V_a & V_b) for each pair.  Either way
 // the passes write partial rows of counts and a last pass sums the rows.
-// Per-part counts of each worker come from one pass over the entries.  The
-// host then evaluates the definitions in double with fixed expressions.
+// Each worker's counts per contiguous part come from binary searches in its
+// ascending list, its counts per hash class from one pass over the entries.
+// The host then evaluates the definitions in double with fixed expressions.
 #include "sg_host.h"
 
 namespace sg {
@@ -40,50 +41,80 @@ __global__ void st_pack_kernel(const uint64_t* __restrict__ in_off, uint32_t n, 
     }
 }
 
-// per-worker counts per contiguous part and per hash class; one block per
-// 4096-entry chunk of a worker (chunk plan of the merge engine, G = 1)
+// Per-worker counts per contiguous part: a worker's list is ascending, so the
+// entries of part q = [floor(qM/P), floor((q+1)M/P)) lie between the lower
+// bounds of the two ends.  One wave per (worker, part) finds both by 64-ary
+// search: each round the lanes probe 64 evenly spaced positions of the
+// remaining range of each bound (both bounds' probes in the same round).
+__global__ __launch_bounds__(256) void st_contig_kernel(MergeParams p, StatsCounts c)
+{
+    const uint32_t i = blockIdx.x * 4 + uniform(threadIdx.x / SG_WAVE);
+    if (i >= p.n * p.Ps) return;
+    const uint32_t lane = lane_id();
+    const uint32_t w = i / p.Ps, q = i % p.Ps;
+    uint64_t s, e;
+    run_range(p, 0, w, s, e);
+    const uint64_t key[2] = {p.M * q / p.Ps, p.M * (q + 1) / p.Ps}; // M < 2^32, P <= 256
+    uint64_t lo[2] = {0, 0}, hi[2] = {e - s, e - s}; // the bound lies in [lo, hi]
+    while (hi[0] > lo[0] || hi[1] > lo[1]) {
+        uint64_t step[2], pos[2];
+        bool lt[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // probes lo + l*step for l < 64 and < hi; a[pos] < key is true on a prefix
+            step[h] = (hi[h] - lo[h] + SG_WAVE - 1) / SG_WAVE;
+            pos[h] = lo[h] + (uint64_t)lane * step[h];
+            const bool in = hi[h] > lo[h] && pos[h] < hi[h];
+            lt[h] = in && (uint64_t)p.idx[s + pos[h]] < key[h];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (hi[h] <= lo[h]) continue;
+            const uint32_t cnt = popc64(ballot(lt[h])); // probes below the key
+            if (cnt == 0) {
+                hi[h] = lo[h];
+            } else {
+                const uint64_t last = lo[h] + (uint64_t)(cnt - 1) * step[h]; // a[last] < key
+                const uint64_t nxt = lo[h] + (uint64_t)cnt * step[h];
+                lo[h] = last + 1;
+                if (nxt < hi[h]) hi[h] = nxt; // a[nxt] >= key when it is a probe
+            }
+        }
+    }
+    if (lane == 0) c.wcontig[i] = lo[1] - lo[0];
+}
+
+// Per-worker counts per hash class: one block per 4096-entry chunk of a
+// worker (chunk plan of the merge engine, G = 1); all of a thread's loads in
+// flight at once, then one LDS atomic per key; the block's counts are added
+// to the worker's after each chunk.
 __global__ __launch_bounds__(MG_THREADS) void st_entries_kernel(MergeParams p, StatsCounts c)
 {
-    __shared__ uint32_t hc[256], hh[256];
+    constexpr int U = MG_CHUNK / MG_THREADS;
+    __shared__ uint32_t hh[256];
     const uint32_t hseed = p.seed_at ? p.seed_at[0] : p.seed;
-    for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
+    for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hh[i] = 0;
     __syncthreads();
     for (uint32_t ch = blockIdx.x; ch < p.nchunks_max; ch += gridDim.x) {
         const uint4 rec = p.chunk_rec[ch];
         if (rec.x == 0xffffffffu) continue;
         const uint32_t w = rec.x; // one group: the run is the worker
-        const uint64_t s = rec.w, e = (uint64_t)rec.w + rec.z;
-        const uint64_t j0 = rec.y;
-        constexpr int U = 4; // loads in flight per thread
-        for (uint64_t jb = j0; jb < j0 + MG_CHUNK; jb += U * MG_THREADS) { // block-uniform trip count
-            uint32_t key[U];
-            bool has[U];
+        const uint64_t s = rec.w, len = rec.z, j0 = rec.y;
+        uint32_t key[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint64_t j = jb + u * MG_THREADS + threadIdx.x;
-                has[u] = s + j < e;
-                key[u] = has[u] ? p.idx[s + j] : 0u;
-            }
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * MG_THREADS + threadIdx.x;
+            key[u] = p.idx[s + (j < len ? j : len - 1)];
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                count_sorted_parts(hc, has[u] ? contig_part(key[u], p.M, p.Ps, p.inv_m) : 0u, has[u]);
-                if (p.hashed && has[u]) atomicAdd(&hh[h0(key[u], hseed, p.div)], 1u);
-            }
+        for (int u = 0; u < U; ++u)
+            if (j0 + (uint64_t)u * MG_THREADS + threadIdx.x < len) atomicAdd(&hh[h0(key[u], hseed, p.div)], 1u);
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
+            if (hh[i]) atomicAdd((unsigned long long*)&c.whashed[(uint64_t)w * p.Ps + i], (unsigned long long)hh[i]);
+            hh[i] = 0;
         }
-        // flush when the next chunk of this block belongs to another worker (or there is none)
-        const uint32_t nc = ch + gridDim.x;
-        const uint4 nrec = nc < p.nchunks_max ? p.chunk_rec[nc] : make_uint4(0xffffffffu, 0u, 0u, 0u);
-        if (nrec.x != w) {
-            __syncthreads();
-            for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) {
-                if (hc[i]) atomicAdd((unsigned long long*)&c.wcontig[(uint64_t)w * p.Ps + i], (unsigned long long)hc[i]);
-                if (p.hashed && hh[i])
-                    atomicAdd((unsigned long long*)&c.whashed[(uint64_t)w * p.Ps + i], (unsigned long long)hh[i]);
-            }
-            __syncthreads();
-            for (uint32_t i = threadIdx.x; i < p.Ps; i += MG_THREADS) hc[i] = hh[i] = 0;
-            __syncthreads();
-        }
+        __syncthreads();
     }
 }
 
@@ -187,7 +218,7 @@ static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64
     const uint32_t W = (uint32_t)grid * SW_WAVES;
     mg_plan_kernel<<<1, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    mg_bnd_kernel<<<p.nchunks_max < 1024 ? p.nchunks_max : 1024, 512, 0, st>>>(p);
+    mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     const uint64_t cells = (uint64_t)p.n * (p.NT + 1);
     mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
@@ -284,8 +315,12 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
         rc = merge_run(p, MODE_STATS, st, k.row);
     }
     if (rc) return rc;
-    st_entries_kernel<<<p.nchunks_max < 2048 ? p.nchunks_max : 2048, MG_THREADS, 0, st>>>(p, k);
+    st_contig_kernel<<<(unsigned)ceil_div((uint64_t)n * P, 4), 256, 0, st>>>(p, k);
     SG_TRY_LAUNCH();
+    if (d_cmap && total > 0) {
+        st_entries_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, MG_THREADS, 0, st>>>(p, k);
+        SG_TRY_LAUNCH();
+    }
 
     st_pack_kernel<<<1, 256, 0, st>>>(d_in_off, n, d_cmap ? cm.class_size : nullptr, d_cmap ? cm.hdr : nullptr, P,
                                       k.tail);
