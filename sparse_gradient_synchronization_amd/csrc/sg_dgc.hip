@@ -337,7 +337,8 @@ extern "C" int sg_dgc_select(const float* d_grad, float* d_resid, uint32_t n, ui
     SG_TRY_LAUNCH();
     topk_scan_kernel<<<n, 1024, 0, st>>>(p.t);
     SG_TRY_LAUNCH();
-    topk_write_kernel<<<wgrid4, TK_THREADS, 0, st>>>(p.t);
+    if (p.t.bf16) topk_write_kernel<true><<<wgrid4, TK_THREADS, 0, st>>>(p.t);
+    else topk_write_kernel<false><<<wgrid4, TK_THREADS, 0, st>>>(p.t);
     SG_TRY_LAUNCH();
     return SG_OK;
 }

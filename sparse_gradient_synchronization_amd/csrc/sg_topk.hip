@@ -744,23 +744,24 @@ __global__ __launch_bounds__(1024) void topk_scan_kernel(TopkParams p)
 
 // Ordered compaction of one chunk of up to 64 slot entries: entries above T,
 // and entries equal to T while fewer than `need` equal ones precede them.
-__device__ __forceinline__ void write_chunk(const TopkParams& p, uint32_t valid_n, uint32_t bits, uint32_t ix,
-                                            uint32_t T, uint32_t need, uint64_t obase, uint64_t& pos, uint32_t& eqr)
+// oidx / oval are the worker's output rows.
+template <bool BF16>
+__device__ __forceinline__ void write_chunk(uint32_t* oidx, void* oval, uint64_t k, uint32_t valid_n, uint32_t bits,
+                                            uint32_t ix, uint32_t T, uint32_t need, uint64_t& pos, uint32_t& eqr)
 {
-    const uint32_t lane = lane_id();
-    const bool valid = lane < valid_n;
-    const uint32_t key = key_of_bits(bits, p.bf16);
+    const bool valid = lane_id() < valid_n;
+    const uint32_t key = key_of_bits(bits, BF16);
     const bool eq = valid && key == T;
     const uint64_t meq = ballot(eq);
-    const uint32_t my_eq = eqr + popc64(meq & lanemask_lt());
+    const uint32_t my_eq = eqr + count_below(meq);
     const bool sel = valid && (key > T || (eq && my_eq < need));
     const uint64_t ms = ballot(sel);
     if (sel) {
-        const uint64_t o = pos + popc64(ms & lanemask_lt());
-        if (o < p.k) {
-            p.out_idx[obase + o] = ix;
-            if (p.bf16) static_cast<uint16_t*>(p.out_val)[obase + o] = (uint16_t)bits;
-            else static_cast<uint32_t*>(p.out_val)[obase + o] = bits;
+        const uint64_t o = pos + count_below(ms);
+        if (o < k) {
+            oidx[o] = ix;
+            if (BF16) static_cast<uint16_t*>(oval)[o] = (uint16_t)bits;
+            else static_cast<uint32_t*>(oval)[o] = bits;
         }
     }
     pos += popc64(ms);
@@ -772,11 +773,12 @@ __device__ __forceinline__ void write_chunk(const TopkParams& p, uint32_t valid_
 // The wave's slot chunks (64 entries each) are numbered across its tiles and
 // loaded 16 at a time, so dense tiles (whole rows above the band) cost no
 // more load rounds than their size demands.
+template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
 {
     constexpr uint32_t TPW = TK_GROUP / 4; // tiles per wave
     constexpr int B = 16;                  // chunks per load round
-    const uint64_t gq = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + threadIdx.x / SG_WAVE;
+    const uint64_t gq = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + uniform(threadIdx.x / SG_WAVE);
     if (gq >= (uint64_t)p.n * p.NG * 4) return;
     const uint64_t gw = gq / 4;
     const uint32_t quarter = (uint32_t)(gq % 4);
@@ -795,7 +797,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
     const uint32_t cinc = wave_incl_scan(nch);
     const uint32_t cst = cinc - nch;
     const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)cinc, SG_WAVE - 1);
-    const uint64_t obase = (uint64_t)w * p.k;
+    uint32_t* const oidx = p.out_idx + (uint64_t)w * p.k;
+    void* const oval = static_cast<char*>(p.out_val) + (uint64_t)w * p.k * (BF16 ? 2u : 4u);
     uint32_t cur_tile = 0xffffffffu, eqr = 0;
     uint64_t pos = 0;
     for (uint32_t b0 = 0; b0 < C; b0 += B) {
@@ -822,7 +825,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
                 pos = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xg, (int)cur_tile) + (eqr < need ? eqr : need);
             }
             const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
-            write_chunk(p, cj - ch[u], vb[u], vi[u], T, need, obase, pos, eqr);
+            write_chunk<BF16>(oidx, oval, p.k, cj - ch[u], vb[u], vi[u], T, need, pos, eqr);
         }
     }
 }
@@ -934,7 +937,8 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     topk_scan_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_TOPK_WRITE, st);
-    topk_write_kernel<<<wgrid4, TK_THREADS, 0, st>>>(p);
+    if (p.bf16) topk_write_kernel<true><<<wgrid4, TK_THREADS, 0, st>>>(p);
+    else topk_write_kernel<false><<<wgrid4, TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_TOPK_WRITE, st);
     return SG_OK;
