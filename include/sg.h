@@ -451,6 +451,24 @@ size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t
 int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total, uint32_t P,
              const void* d_cmap, size_t cmap_bytes, sg_stats_out* h_out, void* d_ws, size_t ws_bytes, void* stream);
 
+/* The same statistics in two halves, so a caller can queue more work before
+ * it waits.  sg_stats_async validates like sg_stats, queues the passes on
+ * `stream` and a copy of the raw counts into h_block (host memory of at
+ * least sg_stats_block_bytes(n, P) bytes, owned by the caller; pinned memory
+ * keeps the copy asynchronous) and returns without waiting.  Once the stream
+ * has passed that point (an event or a synchronize of the caller's),
+ * sg_stats_collect evaluates the definitions above from h_block into h_out;
+ * n, M, total and P are those of the sg_stats_async call and hashed is 1 iff
+ * it had a class map (a block whose class map header does not match (M, P)
+ * gives SG_EINVAL).  The workspace and h_block must not be reused before
+ * that point.  sg_stats_block_bytes returns 0 for n or P out of range. */
+size_t sg_stats_block_bytes(uint32_t n, uint32_t P);
+int sg_stats_async(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                   uint32_t P, const void* d_cmap, size_t cmap_bytes, void* h_block, size_t block_bytes, void* d_ws,
+                   size_t ws_bytes, void* stream);
+int sg_stats_collect(const void* h_block, uint32_t n, uint64_t M, uint64_t total, uint32_t P, int hashed,
+                     sg_stats_out* h_out);
+
 #ifdef __cplusplus
 }
 #endif

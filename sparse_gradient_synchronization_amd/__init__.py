@@ -87,6 +87,9 @@ SIGNATURES = {
     "sg_format_sizes_workspace_bytes": (_sz, [_u64]),
     "sg_format_sizes": (_int, [_vp, _vp, _u64, _u64, _u32, _u32, _vp, _sz, _vp, _vp, _sz, _vp]),
     "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, _sz, C.POINTER(StatsOut), _vp, _sz, _vp]),
+    "sg_stats_block_bytes": (_sz, [_u32, _u32]),
+    "sg_stats_async": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, _sz, _vp, _sz, _vp, _sz, _vp]),
+    "sg_stats_collect": (_int, [_vp, _u32, _u64, _u64, _u32, _int, C.POINTER(StatsOut)]),
 }
 
 _lib = None
@@ -444,14 +447,8 @@ def sg_dgc_select(grad: torch.Tensor, resid: torch.Tensor, density: float, S: in
     return idx[:, :cap], val[:, :cap], cnt, thr
 
 
-def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
-             workspace: torch.Tensor | None = None):
-    """Defs. 3-5 and 8 of the Zen page from exact counts.  Returns a dict."""
+def _stats_out(n, P):
     import numpy as np
-    _need_cuda(idx, in_off, cmap)
-    idx, in_off = idx.contiguous(), in_off.contiguous()
-    n = in_off.numel() - 1
-    total = idx.numel()
     arr = dict(
         nnz=np.zeros(n, np.uint64), inter=np.zeros(n * n, np.uint64), overlap=np.zeros(n * n, np.float64),
         contig_counts=np.zeros((n + 1) * P, np.uint64), skew_contig=np.zeros(n + 1, np.float64),
@@ -460,11 +457,53 @@ def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
     o = StatsOut()
     for k, a in arr.items():
         setattr(o, k, a.ctypes.data)
+    return arr, o
+
+
+def sg_stats(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
+             workspace: torch.Tensor | None = None):
+    """Defs. 3-5 and 8 of the Zen page from exact counts.  Returns a dict."""
+    _need_cuda(idx, in_off, cmap)
+    idx, in_off = idx.contiguous(), in_off.contiguous()
+    n = in_off.numel() - 1
+    total = idx.numel()
+    arr, o = _stats_out(n, P)
     need = lib().sg_stats_workspace_bytes(n, M, total, P)
     ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
     _check(lib().sg_stats(_p(idx), _p(in_off), n, M, total, P, _p(cmap), 0 if cmap is None else cmap.numel(),
                           C.byref(o), _p(ws), ws.numel(),
                           _stream()), "sg_stats")
+    return _stats_result(arr, o, n, P)
+
+
+def sg_stats_async(idx: torch.Tensor, in_off: torch.Tensor, M: int, P: int, cmap=None,
+                   workspace: torch.Tensor | None = None, block: torch.Tensor | None = None):
+    """Queues the statistics passes and the copy of the raw counts into a
+    pinned host block; returns (block, args) for sg_stats_collect, to be
+    called after the current stream has passed this point."""
+    _need_cuda(idx, in_off, cmap)
+    idx, in_off = idx.contiguous(), in_off.contiguous()
+    n = in_off.numel() - 1
+    total = idx.numel()
+    nb = lib().sg_stats_block_bytes(n, P)
+    if block is None or block.numel() < nb:
+        block = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+    need = lib().sg_stats_workspace_bytes(n, M, total, P)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _ws(need, idx.device)
+    _check(lib().sg_stats_async(_p(idx), _p(in_off), n, M, total, P, _p(cmap), 0 if cmap is None else cmap.numel(),
+                                _p(block), block.numel(), _p(ws), ws.numel(), _stream()), "sg_stats_async")
+    return block, (n, M, total, P, 0 if cmap is None else 1)
+
+
+def sg_stats_collect(block: torch.Tensor, args) -> dict:
+    """The statistics from a block filled by sg_stats_async (host only)."""
+    n, M, total, P, hashed = args
+    arr, o = _stats_out(n, P)
+    _check(lib().sg_stats_collect(_p(block), n, M, total, P, hashed, C.byref(o)), "sg_stats_collect")
+    return _stats_result(arr, o, n, P)
+
+
+def _stats_result(arr, o, n, P):
     res = dict(arr)
     res["inter"] = res["inter"].reshape(n, n)
     res["overlap"] = res["overlap"].reshape(n, n)

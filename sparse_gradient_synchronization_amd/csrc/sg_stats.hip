@@ -261,17 +261,30 @@ static double skew_of(const uint64_t* c, const uint64_t* g, uint32_t P, uint64_t
     return best;
 }
 
-extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
-                        uint32_t P, const void* d_cmap, size_t cmap_bytes, sg_stats_out* o, void* d_ws,
-                        size_t ws_bytes, void* stream)
+// The block of raw counts the host evaluates: see StatsCounts.
+static uint64_t stats_block_words(uint32_t n, uint32_t P)
 {
-    if (n == 0 || n > 64 || P == 0 || P > 256 || !o || !d_in_off || !d_ws) return SG_EINVAL;
+    return (uint64_t)n * (n + 1) / 2 + 1 + 2ull * P + 2ull * n * P + n + 1 + P + 4;
+}
+
+static int stats_check_out(const sg_stats_out* o, bool hashed)
+{
+    if (!o || !o->nnz || !o->inter || !o->overlap || !o->contig_counts || !o->skew_contig) return SG_EINVAL;
+    if (hashed && (!o->class_size || !o->hashed_counts || !o->skew_hashed)) return SG_EINVAL;
+    return SG_OK;
+}
+
+// Validation and every pass on `stream`; on return *d_block is the device
+// block of raw counts (stats_block_words long), complete once the stream
+// passes this point.
+static int stats_enqueue(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                         uint32_t P, const void* d_cmap, size_t cmap_bytes, void* d_ws, size_t ws_bytes, hipStream_t st,
+                         const uint64_t** d_block)
+{
+    if (n == 0 || n > 64 || P == 0 || P > 256 || !d_in_off || !d_ws) return SG_EINVAL;
     if (M == 0 || M >= (1ull << 32) || total >= (1ull << 32)) return SG_EUNSUPPORTED;
     if (total > 0 && !d_idx) return SG_EINVAL;
-    if (!o->nnz || !o->inter || !o->overlap || !o->contig_counts || !o->skew_contig) return SG_EINVAL;
-    if (d_cmap && (!o->class_size || !o->hashed_counts || !o->skew_hashed)) return SG_EINVAL;
     if (ws_bytes < sg_stats_workspace_bytes(n, M, total, P)) return SG_ECAPACITY;
-    hipStream_t st = as_stream(stream);
 
     // The class map's header (seed, and its magic, P and M, checked after the
     // passes) and class sizes are read on the device: no copy before the
@@ -326,29 +339,32 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
                                       k.tail);
     SG_TRY_LAUNCH();
 
-    std::vector<uint64_t> blk(k.words);
-    {
-        HostStage hs;
-        rc = host_stage(8ull * k.words, &hs);
-        if (rc) return rc;
-        SG_TRY(hipMemcpyAsync(hs.ptr, k.row, 8ull * k.words, hipMemcpyDeviceToHost, st));
-        SG_TRY(hipStreamSynchronize(st));
-        std::memcpy(blk.data(), hs.ptr, 8ull * k.words);
-    }
-    uint64_t* row = blk.data();
-    const uint64_t* wc = row + p.st_row;
+    *d_block = k.row;
+    return SG_OK;
+}
+
+// The definitions evaluated on the host from a block of raw counts.
+static int stats_collect(const uint64_t* blk, uint32_t n, uint64_t M, uint64_t total, uint32_t P, bool hashed,
+                         sg_stats_out* o)
+{
+    const bool windowed = total > 0 && stats_windowed(n, P, hashed);
+    const uint32_t npairs = n * (n + 1) / 2;
+    const uint32_t st_row = npairs + 1 + 2 * P;
+    std::vector<uint64_t> rowv(blk, blk + st_row);
+    uint64_t* row = rowv.data();
+    const uint64_t* wc = blk + st_row;
     const uint64_t* wh = wc + (size_t)n * P;
     const uint64_t* off = wh + (size_t)n * P;
     const uint64_t* class_size = off + n + 1;
     const uint64_t* hdr = class_size + P;
-    if (d_cmap && (hdr[0] != CM_MAGIC || hdr[1] != P || hdr[2] != M)) return SG_EINVAL;
+    if (hashed && (hdr[0] != CM_MAGIC || hdr[1] != P || hdr[2] != M)) return SG_EINVAL;
     std::vector<uint64_t> inter((size_t)n * n, 0);
     for (uint32_t a = 0, pi = 0; a < n; ++a)
         for (uint32_t b = a; b < n; ++b, ++pi) inter[(size_t)a * n + b] = row[pi];
-    const uint64_t uni = row[p.npairs];
-    if (windowed && d_cmap && P == 1) row[p.npairs + 1 + P] = uni; // one class holds every key
-    const uint64_t* uc = &row[p.npairs + 1];
-    const uint64_t* uh = &row[p.npairs + 1 + P];
+    const uint64_t uni = row[npairs];
+    if (windowed && hashed && P == 1) row[npairs + 1 + P] = uni; // one class holds every key
+    const uint64_t* uc = &row[npairs + 1];
+    const uint64_t* uh = &row[npairs + 1 + P];
 
     // exact counts
     o->sum_nnz = 0;
@@ -365,7 +381,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     for (uint32_t a = 0; a < n; ++a)
         for (uint32_t b = 0; b < n; ++b) o->inter[(uint64_t)a * n + b] = a <= b ? inter[(size_t)a * n + b] : inter[(size_t)b * n + a];
     // Def. 3 over all pairs
-    uint64_t npairs = 0;
+    uint64_t npo = 0; // pairs a < b seen
     double sum_ov = 0.0;
     o->overlap_min = 0.0;
     o->overlap_max = 0.0;
@@ -375,13 +391,13 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
             const double ov = mn ? (double)o->inter[(uint64_t)a * n + b] / (double)mn : 0.0;
             o->overlap[(uint64_t)a * n + b] = ov;
             if (a < b) {
-                if (npairs == 0 || ov < o->overlap_min) o->overlap_min = ov;
-                if (npairs == 0 || ov > o->overlap_max) o->overlap_max = ov;
+                if (npo == 0 || ov < o->overlap_min) o->overlap_min = ov;
+                if (npo == 0 || ov > o->overlap_max) o->overlap_max = ov;
                 sum_ov += ov;
-                ++npairs;
+                ++npo;
             }
         }
-    o->overlap_mean = npairs ? sum_ov / (double)npairs : 0.0;
+    o->overlap_mean = npo ? sum_ov / (double)npo : 0.0;
     // Def. 4
     o->gamma_n = o->sum_nnz ? ((double)n * (double)o->union_size) / (double)o->sum_nnz : 0.0;
     // Def. 5, contiguous parts
@@ -397,7 +413,7 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
     // hash classes and Def. 8
     o->push_imbalance = 0.0;
     o->pull_imbalance = 0.0;
-    if (d_cmap) {
+    if (hashed) {
         for (uint32_t i = 0; i < P; ++i) o->class_size[i] = class_size[i];
         for (uint32_t a = 0; a < n; ++a) {
             for (uint32_t i = 0; i < P; ++i) o->hashed_counts[(uint64_t)a * P + i] = wh[(size_t)a * P + i];
@@ -419,4 +435,57 @@ extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_
             }
     }
     return SG_OK;
+}
+
+extern "C" size_t sg_stats_block_bytes(uint32_t n, uint32_t P)
+{
+    if (n == 0 || n > 64 || P == 0 || P > 256) return 0;
+    return (size_t)(8 * stats_block_words(n, P));
+}
+
+extern "C" int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                        uint32_t P, const void* d_cmap, size_t cmap_bytes, sg_stats_out* o, void* d_ws,
+                        size_t ws_bytes, void* stream)
+{
+    int rc = stats_check_out(o, d_cmap != nullptr);
+    if (rc) return rc;
+    hipStream_t st = as_stream(stream);
+    const uint64_t* d_block = nullptr;
+    rc = stats_enqueue(d_idx, d_in_off, n, M, total, P, d_cmap, cmap_bytes, d_ws, ws_bytes, st, &d_block);
+    if (rc) return rc;
+    const uint64_t words = stats_block_words(n, P);
+    std::vector<uint64_t> blk(words);
+    {
+        HostStage hs;
+        rc = host_stage(8ull * words, &hs);
+        if (rc) return rc;
+        SG_TRY(hipMemcpyAsync(hs.ptr, d_block, 8ull * words, hipMemcpyDeviceToHost, st));
+        SG_TRY(hipStreamSynchronize(st));
+        std::memcpy(blk.data(), hs.ptr, 8ull * words);
+    }
+    return stats_collect(blk.data(), n, M, total, P, d_cmap != nullptr, o);
+}
+
+extern "C" int sg_stats_async(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total,
+                              uint32_t P, const void* d_cmap, size_t cmap_bytes, void* h_block, size_t block_bytes,
+                              void* d_ws, size_t ws_bytes, void* stream)
+{
+    if (!h_block) return SG_EINVAL;
+    if (block_bytes < sg_stats_block_bytes(n, P)) return SG_ECAPACITY;
+    hipStream_t st = as_stream(stream);
+    const uint64_t* d_block = nullptr;
+    const int rc = stats_enqueue(d_idx, d_in_off, n, M, total, P, d_cmap, cmap_bytes, d_ws, ws_bytes, st, &d_block);
+    if (rc) return rc;
+    SG_TRY(hipMemcpyAsync(h_block, d_block, sg_stats_block_bytes(n, P), hipMemcpyDeviceToHost, st));
+    return SG_OK;
+}
+
+extern "C" int sg_stats_collect(const void* h_block, uint32_t n, uint64_t M, uint64_t total, uint32_t P, int hashed,
+                                sg_stats_out* o)
+{
+    if (!h_block || n == 0 || n > 64 || P == 0 || P > 256) return SG_EINVAL;
+    if (M == 0 || M >= (1ull << 32) || total >= (1ull << 32)) return SG_EUNSUPPORTED;
+    const int rc = stats_check_out(o, hashed != 0);
+    if (rc) return rc;
+    return stats_collect(static_cast<const uint64_t*>(h_block), n, M, total, P, hashed != 0, o);
 }

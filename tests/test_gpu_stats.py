@@ -63,3 +63,23 @@ def test_stats_config4_full():
     g = _check(c["idx"], c["in_off"], c["M"], c["P"], seed=c["seed"])
     # skewed before hashing, balanced after (Zen section 2.1 C3 and Theorem 2)
     assert g["skew_contig"][:16].min() > 4.5 and g["skew_hashed"].max() < 1.05
+
+
+@pytest.mark.parametrize("n,P", [(4, 4), (16, 16), (64, 8), (9, 17)])
+def test_stats_async_matches_blocking(n, P):
+    """sg_stats_async + sg_stats_collect give what sg_stats gives, twice in a
+    row into the same block and workspace, with and without a class map."""
+    need_gpu()
+    import torch
+    idx, in_off, _ = gen.coo_zipf(900 + n, n, 120000, 3000, 1.1)
+    d_idx, d_off = to_dev_u32(idx), to_dev_u64(in_off)
+    for seed in (None, 13):
+        cmap = None if seed is None else sg.sg_classmap_build(120000, P, seed)
+        ref = sg.sg_stats(d_idx, d_off, 120000, P, cmap=cmap)
+        block = None
+        for _ in range(2):
+            block, args = sg.sg_stats_async(d_idx, d_off, 120000, P, cmap=cmap, block=block)
+            torch.cuda.synchronize()
+            got = sg.sg_stats_collect(block, args)
+            for k, v in ref.items():
+                assert np.array_equal(np.asarray(got[k]), np.asarray(v)), k
