@@ -308,6 +308,42 @@ def copy_calibration(torch, nbytes):
     del src, dst
 
 
+def copy_bandwidth(torch, nbytes=2 << 30, reps=5):
+    """The box's achievable HBM bandwidth: a plain device-to-device copy of
+    nbytes, read + write bytes over the median time of reps copies."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    t = sorted(ms)[len(ms) // 2]
+    return {"bytes_copied": nbytes, "median_ms": t, "GBps": 2 * nbytes / (t * 1e-3) / 1e9}
+
+
+def cold_steps(torch, step, steps, flush_bytes=1 << 30):
+    """Each step timed alone with HIP events after a 1 GiB scratch write has
+    pushed its working set out of the caches; returns the median in ms."""
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    ms = []
+    for _ in range(steps):
+        scratch.fill_(0.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del scratch
+    return sorted(ms)[len(ms) // 2]
+
+
 def algorithmic_bytes(W, stage):
     """Algorithmic bytes per launch of the probed kernel of a stage."""
     if stage == "topk_to_coo":
@@ -644,6 +680,12 @@ def main():
         },
         "cpu_baseline": None,
     }
+    res["hbm_copy"] = copy_bandwidth(torch)
+    if args.workload in ("cfg1", "cfg2"):
+        # working sets below 256 MB fit the caches: the hot figure above, and
+        # each step alone after a cache-flushing write
+        res["cold_ms_per_step"] = cold_steps(torch, step, steps)
+        res["cold_value"] = units / (res["cold_ms_per_step"] * 1e-3)
     if "pull" in W:
         res["pull_side"] = pull_side(W, L, torch, steps)
     nr = next_rows(args.workload, W, L, torch, sg, steps)

@@ -162,7 +162,12 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     if (threadIdx.x == 0) {
         SelState st;
         for (int i = 0; i < 6; ++i) st.pad[i] = 0;
-        st.lo = none_lo ? 0u : prefix[0];
+        // A sampled low end of 0 (many zero keys, as in a sparse tensor with
+        // k near its nonzero count) would make every zero a candidate; the
+        // band starts at the smallest positive key instead.  If the k-th key
+        // is in fact 0 the band misses and the worker is filtered again with
+        // the full band, which stays exact.
+        st.lo = none_lo ? 0u : (prefix[0] == 0u ? 1u : prefix[0]);
         st.hi = none_hi ? p.keymax : prefix[1];
         st.redo = 0;
         st.sure = st.cand = 0;
