@@ -43,7 +43,15 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
         p->tile_out = c.take<uint64_t>(T);
         p->blk_sum = c.take<uint64_t>(p->nscan);
         p->stage_idx = c.take<uint32_t>(p->total);
-        p->stage_val = c.take<float>(p->total * (p->D > 1 ? p->D : 1));
+        if (p->D > 1) {
+            p->stage_val = nullptr;
+            p->stage_src = c.take<uint32_t>(p->total);
+            p->stage_first = c.take<uint32_t>(p->total);
+            p->tile_ent = c.take<uint32_t>(T);
+            p->row_rng = c.take<uint2>(p->total);
+        } else {
+            p->stage_val = c.take<float>(p->total);
+        }
     } else {
         p->st_part = c.take<uint64_t>((uint64_t)MG_STATS_MAX_GRID * p->st_row);
     }
@@ -95,6 +103,11 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
         const uint64_t pblocks = ceil_div(T, 4) < 65536 ? ceil_div(T, 4) : 65536;
         mg_place_kernel<<<(unsigned)pblocks, 256, 0, st>>>(p);
         SG_TRY_LAUNCH();
+        if (p.D > 1 && p.total > 0) {
+            const uint64_t rblocks = ceil_div(p.total, 4) < 65536 ? ceil_div(p.total, 4) : 65536;
+            mg_rows_kernel<<<(unsigned)rblocks, 256, 0, st>>>(p);
+            SG_TRY_LAUNCH();
+        }
         return SG_OK;
     }
     mg_merge_kernel<MODE_STATS><<<(unsigned)grid, MG_THREADS, 0, st>>>(p);

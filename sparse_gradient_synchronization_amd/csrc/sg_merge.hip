@@ -83,7 +83,12 @@ struct MergeParams {
     uint64_t* blk_sum;      // [nscan] scan block totals, then their exclusive prefix
     uint32_t nscan;
     uint32_t* stage_idx;    // [total]
-    float* stage_val;       // [total * D]
+    float* stage_val;       // [total] (D <= 1)
+    // rows (D >= 2): sums are formed after the merge, one output row per wave
+    uint32_t* stage_src;    // [total] contributors' entry positions, by (staged key, worker), tile-relative layout
+    uint32_t* stage_first;  // [total] a staged key's first contributor, relative to its tile's staging base
+    uint32_t* tile_ent;     // [G*NT] entries of a tile
+    uint2* row_rng;         // [total] output row o: its contributors are stage_src[x .. y)
     uint32_t* queue;        // [MG_NQ * MG_QSTRIDE]: queue[0] heavy tiles listed; queue[q * MG_QSTRIDE + 1] chunk tickets of queue q
     uint32_t* heavy;        // [G*NT] tiles with more than MG_HEAVY entries
     // statistics
@@ -540,6 +545,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
         const uint32_t csbase = MODE == MODE_AGG ? wave_sum(cr.base) : 0u;
         const uint64_t klo = (uint64_t)(t % p.NT) << p.tb;
         uint32_t produced = 0;
+        uint32_t consumed = 0; // entries of the tile merged in earlier windows
         if (E == 0) {
             if (MODE == MODE_AGG && lane == 0) {
                 p.tile_cnt[t] = 0;
@@ -629,6 +635,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
             }
             wave_sync();
             if (MODE == MODE_AGG) {
+                uint32_t slots; // entries of this window
                 // first slot of each rank: exclusive prefix of the holder counts
                 {
                     constexpr int RPL = MG_WCAP / SG_WAVE;
@@ -640,6 +647,7 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                         sum += c[j];
                     }
                     const uint32_t inc = wave_incl_scan(sum);
+                    slots = (uint32_t)__builtin_amdgcn_readlane((int)inc, SG_WAVE - 1);
                     uint32_t ex = inc - sum;
 #pragma unroll
                     for (int j = 0; j < RPL; ++j) {
@@ -666,22 +674,15 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                         p.stage_val[ob + r] = acc;
                     }
                 } else if (p.D > 1) {
-                    // rows: one rank at a time, lanes across the row
-                    for (uint32_t r = 0; r < U && ob + r < p.total; ++r) {
-                        const uint32_t s0 = sm.wpre[r], c = popc64(sm.mask[r]);
-                        if (lane == 0) p.stage_idx[ob + r] = sm.bits[r];
-                        for (uint32_t c0 = 0; c0 < p.D; c0 += SG_WAVE) {
-                            const uint32_t col = c0 + lane;
-                            if (col >= p.D) break;
-                            float acc = 0.0f;
-                            for (uint32_t j = 0; j < c; ++j) {
-                                const uint64_t vi = (uint64_t)sm.slot[s0 + j] * p.D + col;
-                                acc += p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[vi])
-                                              : static_cast<const float*>(p.val)[vi];
-                            }
-                            p.stage_val[(ob + r) * p.D + col] = acc;
-                        }
+                    // rows: each staged key's contributors in worker order; the
+                    // sums are formed by mg_rows_kernel
+                    for (uint32_t q = lane; q < slots; q += SG_WAVE) p.stage_src[csbase + consumed + q] = sm.slot[q];
+                    for (uint32_t r = lane; r < U && ob + r < p.total; r += SG_WAVE) {
+                        p.stage_idx[ob + r] = sm.bits[r];
+                        p.stage_first[ob + r] = consumed + sm.wpre[r];
                     }
+                    consumed += slots;
+                    if (tile_done && lane == 0) p.tile_ent[t] = consumed;
                 } else {
                     for (uint32_t r = lane; r < U && ob + r < p.total; r += SG_WAVE) p.stage_idx[ob + r] = sm.bits[r];
                 }
@@ -846,9 +847,55 @@ __global__ __launch_bounds__(256) void mg_place_kernel(MergeParams p)
                 }
             }
         } else {
-            for (uint32_t i = lane; i < c; i += SG_WAVE) p.agg_idx[ob + i] = p.stage_idx[sb + i];
-            const uint64_t cnt = (uint64_t)c * p.D;
-            for (uint64_t i = lane; i < cnt; i += SG_WAVE) p.agg_val[ob * p.D + i] = p.stage_val[sb * p.D + i];
+            // rows: the key, and where the row's contributors are listed
+            const uint32_t ent = uniform(p.tile_ent[t]);
+            for (uint32_t i = lane; i < c; i += SG_WAVE) {
+                p.agg_idx[ob + i] = p.stage_idx[sb + i];
+                const uint32_t f0 = p.stage_first[sb + i], f1 = i + 1 < c ? p.stage_first[sb + i + 1] : ent;
+                p.row_rng[ob + i] = make_uint2((uint32_t)(sb + f0), (uint32_t)(sb + (f1 > f0 ? f1 : f0)));
+            }
+        }
+    }
+}
+
+// Rows (D >= 2): one wave per output row.  The row's contributors (at most
+// one per worker) are listed in stage_src in worker order; their rows are
+// read 16 at a time and summed in that order, lanes across the columns.
+constexpr int MG_ROW_BATCH = 16;
+
+__global__ __launch_bounds__(256) void mg_rows_kernel(MergeParams p)
+{
+    const uint64_t U = p.agg_off[p.G] < p.capacity ? p.agg_off[p.G] : p.capacity;
+    const uint32_t lane = lane_id();
+    for (uint64_t o = (uint64_t)blockIdx.x * 4 + uniform(threadIdx.x / SG_WAVE); o < U; o += (uint64_t)gridDim.x * 4) {
+        const uint2 rng = p.row_rng[o];
+        const uint32_t x = uniform(rng.x), y = uniform(rng.y);
+        const uint32_t cnt = y > x ? y - x : 0u;
+        if (cnt > 64u || y > p.total) { // cannot happen: one contributor per worker
+            if (lane == 0) report_error(kDevErrPartition);
+            continue;
+        }
+        const uint32_t my = lane < cnt ? p.stage_src[x + lane] : 0u;
+        for (uint32_t c0 = 0; c0 < p.D; c0 += SG_WAVE) {
+            const uint32_t col = c0 + lane;
+            const uint32_t cc = col < p.D ? col : p.D - 1;
+            float acc = 0.0f;
+            for (uint32_t j0 = 0; j0 < cnt; j0 += MG_ROW_BATCH) {
+                float v[MG_ROW_BATCH];
+#pragma unroll
+                for (int j = 0; j < MG_ROW_BATCH; ++j) {
+                    v[j] = 0.0f;
+                    if (j0 + j < cnt) { // uniform
+                        const uint64_t vi = (uint64_t)__builtin_amdgcn_readlane((int)my, (int)(j0 + j)) * p.D + cc;
+                        v[j] = p.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.val)[vi])
+                                      : static_cast<const float*>(p.val)[vi];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < MG_ROW_BATCH; ++j)
+                    if (j0 + j < cnt) acc += v[j];
+            }
+            if (col < p.D) p.agg_val[o * p.D + col] = acc;
         }
     }
 }

@@ -29,6 +29,7 @@ struct PartParams {
     uint64_t* part_off;
     uint32_t* tile_start; // [n+1] first global tile of worker w
     uint32_t* counts;     // [max_tiles][P] counts, then destination offsets
+    uint32_t* src_of;     // [total] rows (D >= 2): the input entry each output entry comes from
     uint64_t total;
     uint32_t n, P, seed, D, esz, nbits;
     uint32_t row_w4; // rows can be copied as 4-byte words
@@ -276,27 +277,36 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
         }
     }
 
-    // 5. rows (D >= 2): one wave per row, 4-byte words across lanes
-    if (!STAGE_VALS && p.D > 0) {
-        const uint32_t row_bytes = p.D * p.esz;
-        const bool w4 = p.row_w4 != 0;
-        for (uint32_t le = wid; le < len; le += PT_WAVES) {
-            uint32_t sp = rank_s[le];
-            uint32_t q = part_s[sp];
-            uint64_t dst = (uint64_t)dbase[q] + (sp - lps[q]);
-            if (dst >= p.total) continue;
-            const char* src = static_cast<const char*>(p.val) + (e0 + le) * (uint64_t)row_bytes;
-            char* out = static_cast<char*>(p.out_val) + dst * (uint64_t)row_bytes;
-            if (w4) {
-                const uint32_t* s4 = reinterpret_cast<const uint32_t*>(src);
-                uint32_t* o4 = reinterpret_cast<uint32_t*>(out);
-                for (uint32_t k = lane; k < row_bytes / 4; k += SG_WAVE) o4[k] = s4[k];
-            } else {
-                const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
-                uint16_t* o2 = reinterpret_cast<uint16_t*>(out);
-                for (uint32_t k = lane; k < row_bytes / 2; k += SG_WAVE) o2[k] = s2[k];
-            }
+    // 5. rows (D >= 2): the source of every output entry, for part_rows_kernel
+    if (!STAGE_VALS && p.D > 1) {
+        for (uint32_t le = threadIdx.x; le < len; le += PT_THREADS) {
+            const uint32_t sp = rank_s[le];
+            const uint32_t q = part_s[sp];
+            const uint64_t dst = (uint64_t)dbase[q] + (sp - lps[q]);
+            if (dst < p.total) p.src_of[dst] = (uint32_t)(e0 + le);
         }
+    }
+}
+
+// Rows (D >= 2): output row r is input row src_of[r].  One thread per word
+// of the output (4 bytes, or 2 when a row is not a whole number of 4-byte
+// words); consecutive threads, consecutive addresses.
+template <typename W>
+__global__ __launch_bounds__(256) void part_rows_kernel(PartParams p)
+{
+    const uint32_t wpr = p.D * p.esz / (uint32_t)sizeof(W); // words per row
+    const uint64_t words = p.total * wpr;
+    const W* src = static_cast<const W*>(p.val);
+    W* out = static_cast<W*>(p.out_val);
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < words; i += (uint64_t)gridDim.x * 256) {
+        const uint64_t r = i / wpr;
+        const uint32_t k = (uint32_t)(i - r * wpr);
+        const uint32_t from = p.src_of[r];
+        if (from >= p.total) { // cannot happen: every output entry has a source
+            report_error(kDevErrPartition);
+            continue;
+        }
+        out[i] = src[(uint64_t)from * wpr + k];
     }
 }
 
@@ -307,18 +317,19 @@ using namespace sg;
 static uint32_t part_max_tiles(uint32_t n, uint64_t total) { return (uint32_t)(ceil_div(total, PT_TILE) + n); }
 
 static uint64_t part_carve(Carver& c, uint32_t n, uint64_t total, uint32_t P, uint32_t** tile_start,
-                           uint32_t** counts)
+                           uint32_t** counts, uint32_t** src_of)
 {
     *tile_start = c.take<uint32_t>((uint64_t)n + 1);
     *counts = c.take<uint32_t>((uint64_t)part_max_tiles(n, total) * P);
+    *src_of = c.take<uint32_t>(total); // used for rows (D >= 2)
     return c.bytes();
 }
 
 extern "C" size_t sg_partition_workspace_bytes(uint32_t n, uint64_t total, uint32_t P)
 {
     Carver c(nullptr);
-    uint32_t *a, *b;
-    return part_carve(c, n, total, P, &a, &b);
+    uint32_t *a, *b, *d;
+    return part_carve(c, n, total, P, &a, &b, &d);
 }
 
 extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
@@ -335,7 +346,7 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
 
     PartParams p;
     Carver c(d_ws);
-    part_carve(c, n, total, P, &p.tile_start, &p.counts);
+    part_carve(c, n, total, P, &p.tile_start, &p.counts, &p.src_of);
     p.idx = d_idx;
     p.val = d_val;
     p.in_off = d_in_off;
@@ -370,5 +381,12 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
     else part_scatter_kernel<false, uint32_t><<<p.max_tiles, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_PARTITION_SCATTER, st);
+    if (D > 1 && total > 0) {
+        const uint64_t words = total * D * p.esz / (p.row_w4 ? 4 : 2);
+        const unsigned grid = (unsigned)(ceil_div(words, 256) < 65536 ? ceil_div(words, 256) : 65536);
+        if (p.row_w4) part_rows_kernel<uint32_t><<<grid, 256, 0, st>>>(p);
+        else part_rows_kernel<uint16_t><<<grid, 256, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+    }
     return SG_OK;
 }

@@ -48,6 +48,23 @@ def test_aggregate_bf16():
     _check(idx, in_off, gen.to_bf16(val), 100000, 8, 3, bf16=True)
 
 
+@pytest.mark.parametrize("D", [2, 3, 64])
+def test_aggregate_rows_bf16(D):
+    idx, in_off, val = gen.coo_zipf(330 + D, 5, 40000, 2000, 1.05, D=D)
+    _check(idx, in_off, gen.to_bf16(val), 40000, 4, 6, bf16=True)
+
+
+def test_aggregate_rows_in_windows():
+    # rows whose buckets are denser than a window: their contributor lists
+    # are recorded window by window
+    n, M, D = 16, 1 << 16, 5
+    lists = [np.arange(0, 3000, dtype=np.uint32) for _ in range(n)]
+    vals = [gen.normal(500 + w, 3000 * D).reshape(3000, D) for w in range(n)]
+    idx, in_off, val = gen.coo_from_lists(lists, vals)
+    _check(idx, in_off, val, M, 1, 1)
+    _check(idx, in_off, val, M, 3, 1)
+
+
 def test_aggregate_identical_and_oversized_buckets():
     # every worker holds the same dense block of keys: one bucket far larger
     # than an LDS tile, consumed in windows
