@@ -310,38 +310,41 @@ def copy_calibration(torch, nbytes):
 
 def concurrent_step(stages, torch):
     """The step with its independent rows overlapped on their own streams
-    (default priority): the skip reduce-scatter from the start of the step,
-    the statistics once their COO input exists (after top-k, when the step
-    has it); everything else runs in order on the current stream.  The
-    streams join at the end of the step, and the host half of the statistics
-    runs last.  None when the step has nothing to overlap."""
+    (default priority): the statistics once their COO input exists (after
+    top-k, when the step has it), the skip reduce-scatter once the aggregate
+    is queued (it then overlaps the encode and the statistics, which leave
+    HBM bandwidth free; started earlier it competes with the top-k filter
+    for bandwidth and delays top-k's small kernels); everything else runs in
+    order on the current stream.  The streams join at the end of the step,
+    and the host half of the statistics runs last.  None when the step has
+    nothing to overlap."""
     fns = dict(stages)
     side_names = [nm for nm in ("skip_reduce_scatter", "stats") if nm in fns]
     if not side_names or len(fns) - len(side_names) - ("stats_collect" in fns) < 1:
         return None
     side = {nm: torch.cuda.Stream() for nm in side_names}
-    ev_start, ev_input = torch.cuda.Event(), torch.cuda.Event()
+    after = {"stats": "topk_to_coo", "skip_reduce_scatter": "aggregate"}
+    evs = {nm: torch.cuda.Event() for nm in side_names}
 
-    def launch(nm, ev):
+    def launch(nm):
+        evs[nm].record(torch.cuda.current_stream())
         s = side[nm]
-        s.wait_event(ev)
+        s.wait_event(evs[nm])
         with torch.cuda.stream(s):
             fns[nm]()
 
     def run():
         main = torch.cuda.current_stream()
-        ev_start.record(main)
-        if "skip_reduce_scatter" in side:
-            launch("skip_reduce_scatter", ev_start)
-        if "stats" in side and "topk_to_coo" not in fns:
-            launch("stats", ev_start)
+        for nm in side_names:
+            if after[nm] not in fns:
+                launch(nm)
         for nm, f in stages:
             if nm in side or nm == "stats_collect":
                 continue
             f()
-            if nm == "topk_to_coo" and "stats" in side:
-                ev_input.record(main)
-                launch("stats", ev_input)
+            for nm2 in side_names:
+                if after[nm2] == nm:
+                    launch(nm2)
         for s in side.values():
             main.wait_stream(s)
         if "stats_collect" in fns:
