@@ -70,9 +70,6 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
     mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_BND, st);
-    const uint64_t cells = R * (p.NT + 1);
-    mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
-    SG_TRY_LAUNCH();
     mg_heavy_kernel<<<(unsigned)(ceil_div(T, 256) < 1024 ? ceil_div(T, 256) : 1024), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
     // persistent blocks: as many as can be resident at once

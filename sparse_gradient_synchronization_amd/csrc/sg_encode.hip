@@ -17,7 +17,8 @@
 // each wave walks its partitions' aggregated keys (a cursor per partition,
 // sorted input) and sets bits in an LDS copy of the block's bitmap segments,
 // and the segments are written out at the end.  Words shared with a
-// neighbouring block are merged with atomicOr after a pre-zeroing pass; all
+// neighbouring block are merged with atomicOr after the preparation kernel
+// has zeroed them; all
 // other words are plain stores.
 #include "sg_host.h"
 
@@ -200,14 +201,18 @@ __device__ __forceinline__ void load_agg_offsets(const EncParams& e, uint64_t* o
 
 // Window cursors: one streaming pass over the aggregated entries; entry i of
 // partition p is the first of its partition in windows (win(i-1), win(i)].
-__global__ __launch_bounds__(256) void enc_cursor_kernel(EncParams e)
+// The same launch fills the cursors of empty partitions and zeroes the
+// bitmap words that two neighbouring windows share (the encode kernel merges
+// them with atomicOr).
+__global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
 {
     __shared__ uint64_t offs[257];
     load_agg_offsets(e, offs);
     const uint32_t P = e.L.P;
     const uint64_t NW = e.L.NW, W = e.L.W;
     const uint64_t nagg = offs[P];
-    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < nagg; i += (uint64_t)gridDim.x * 256) {
+    const uint64_t tid = blockIdx.x * 256ull + threadIdx.x, nthreads = (uint64_t)gridDim.x * 256;
+    for (uint64_t i = tid; i < nagg; i += nthreads) {
         uint32_t lo = 0, hi = P; // largest p with offs[p] <= i
         while (lo + 1 < hi) {
             const uint32_t mid = (lo + hi) >> 1;
@@ -228,28 +233,13 @@ __global__ __launch_bounds__(256) void enc_cursor_kernel(EncParams e)
         if (i == en - 1)
             for (uint64_t w = win + 1; w <= NW; ++w) e.cur[w * P + p] = en;
     }
-}
-
-// cursors of empty partitions
-__global__ void enc_cursor_empty_kernel(EncParams e)
-{
-    __shared__ uint64_t offs[257];
-    load_agg_offsets(e, offs);
-    const uint32_t P = e.L.P;
-    const uint64_t cells = (e.L.NW + 1) * P;
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cells; i += (uint64_t)gridDim.x * blockDim.x) {
+    // cursors of empty partitions
+    for (uint64_t i = tid; i < (NW + 1) * P; i += nthreads) {
         const uint32_t p = (uint32_t)(i % P);
         if (offs[p + 1] <= offs[p]) e.cur[i] = offs[p];
     }
-}
-
-// zero the bitmap words that two neighbouring windows share (they are merged
-// with atomicOr by the encode kernel)
-__global__ void enc_zero_kernel(EncParams e)
-{
-    const uint32_t P = e.L.P;
-    const uint64_t cnt = e.L.NW * P;
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cnt; i += (uint64_t)gridDim.x * blockDim.x) {
+    // shared bitmap words
+    for (uint64_t i = tid; i < NW * P; i += nthreads) {
         const uint64_t w = i / P;
         const uint32_t p = (uint32_t)(i % P);
         if (w == 0) continue;
@@ -521,14 +511,9 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     // a window's words never exceed W/32 + P
     if (e.L.W / 32 + P + 2 > (uint64_t)EN_SEG_WORDS) return SG_EUNSUPPORTED;
     hipStream_t st = as_stream(stream);
-    const uint64_t cells = (e.L.NW + 1) * P;
-    enc_cursor_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 1024 ? ceil_div(cells, 256) : 1024), 256, 0, st>>>(e);
-    SG_TRY_LAUNCH();
-    const uint64_t cblocks = ceil_div(agg_capacity, 256);
-    enc_cursor_kernel<<<(unsigned)(cblocks < 4096 ? (cblocks ? cblocks : 1) : 4096), 256, 0, st>>>(e);
-    SG_TRY_LAUNCH();
-    const uint64_t zc = e.L.NW * P;
-    enc_zero_kernel<<<(unsigned)(ceil_div(zc, 256) < 1024 ? ceil_div(zc, 256) : 1024), 256, 0, st>>>(e);
+    const uint64_t work = agg_capacity > (e.L.NW + 1) * P ? agg_capacity : (e.L.NW + 1) * P;
+    const uint64_t pblocks = ceil_div(work, 256);
+    enc_prep_kernel<<<(unsigned)(pblocks < 4096 ? (pblocks ? pblocks : 1) : 4096), 256, 0, st>>>(e);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_ENCODE, st);
     enc_kernel<<<(unsigned)e.L.NW, EN_THREADS, 0, st>>>(e);

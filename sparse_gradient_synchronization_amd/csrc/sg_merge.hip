@@ -175,6 +175,14 @@ __device__ __forceinline__ uint32_t tile_of(const MergeParams& p, uint32_t key)
 __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 {
     constexpr int E = MG_CHUNK / 512;
+    // the rows of empty runs (which have no chunk) are all zero; block r
+    // looks after run r (the grid has at least one block per run)
+    for (uint32_t r = blockIdx.x; r < p.n * p.G; r += gridDim.x) {
+        uint64_t s, e;
+        run_range(p, r / p.n, r % p.n, s, e); // row r = g * n + w
+        if (s == e)
+            for (uint32_t x = threadIdx.x; x <= p.NT; x += 512) p.bnd[(uint64_t)r * (p.NT + 1) + x] = 0;
+    }
     for (uint32_t c = blockIdx.x; c < p.nchunks_max; c += gridDim.x) {
     const uint4 rec = p.chunk_rec[c];
     if (rec.x == 0xffffffffu) continue;
@@ -200,19 +208,6 @@ __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
         if (j == len - 1)
             for (uint64_t x = (uint64_t)b + 1; x <= p.NT; ++x) row[x] = (uint32_t)len;
     }
-    }
-}
-
-// rows of empty runs are all zero
-__global__ void mg_bnd_empty_kernel(MergeParams p)
-{
-    const uint64_t cnt = (uint64_t)p.n * p.G * (p.NT + 1);
-    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < cnt; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t row = i / (p.NT + 1);
-        const uint32_t g = (uint32_t)(row / p.n), w = (uint32_t)(row % p.n);
-        uint64_t s, e;
-        run_range(p, g, w, s, e);
-        if (s == e) p.bnd[i] = 0;
     }
 }
 

@@ -220,9 +220,6 @@ static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64
     SG_TRY_LAUNCH();
     mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
-    const uint64_t cells = (uint64_t)p.n * (p.NT + 1);
-    mg_bnd_empty_kernel<<<(unsigned)(ceil_div(cells, 256) < 2048 ? ceil_div(cells, 256) : 2048), 256, 0, st>>>(p);
-    SG_TRY_LAUNCH();
     sw.m = p;
     const unsigned tgrid = (unsigned)(ceil_div(T, 256) < 2048 ? ceil_div(T, 256) : 2048);
     sw_weight_kernel<<<tgrid, 256, 0, st>>>(sw);

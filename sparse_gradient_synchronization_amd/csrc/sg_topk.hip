@@ -107,6 +107,8 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     const uint64_t M = p.M;
     const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
     for (uint32_t i = threadIdx.x; i < S; i += 1024) s[i] = p.samples[(uint64_t)w * TK_SAMPLES + i];
+    // the worker's histogram row of the selection passes starts at zero
+    for (uint32_t i = threadIdx.x; i < TK_BINS; i += 1024) p.hist[(uint64_t)w * TK_BINS + i] = 0;
     // target ranks, 1-based from the smallest; 0 = not needed
     uint32_t R[2];
     bool none_hi = false, none_lo = false;
@@ -894,8 +896,6 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     const bool rows_aligned = (M * (p.bf16 ? 2 : 4)) % 16 == 0;
     hipStream_t st = as_stream(stream);
 
-    int rc = fill_u32(p.hist, (uint64_t)n * TK_BINS, 0, st);
-    if (rc) return rc;
     topk_gather_kernel<<<dim3(TK_SAMPLES / 256, n), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
     topk_sample_kernel<<<n, 1024, 0, st>>>(p);
