@@ -18,8 +18,7 @@
 // sorted input) and sets bits in an LDS copy of the block's bitmap segments,
 // and the segments are written out at the end.  Words shared with a
 // neighbouring block are merged with atomicOr after the preparation kernel
-// has zeroed them; all
-// other words are plain stores.
+// has zeroed them; all other words are plain stores.
 #include "sg_host.h"
 
 namespace sg {
