@@ -32,7 +32,7 @@ constexpr int TK_SAMPLES = 16384;
 constexpr int TK_DIGIT_BITS = 11;
 constexpr int TK_BINS = 1 << TK_DIGIT_BITS;
 constexpr int TK_GROUP = 64;       // tiles per wave in the select and write passes (one per lane)
-constexpr int TK_HIST_GROUPS = 2;  // tile groups per wave in a histogram block
+constexpr int TK_HIST_TPW = 64;    // tiles per wave in the histogram pass (one tile group)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -558,8 +558,9 @@ __device__ __forceinline__ uint32_t cand_digit(const SelState& st, uint32_t key,
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
 {
     __shared__ uint32_t h[TK_BINS];
-    constexpr uint32_t GPB = (TK_THREADS / SG_WAVE) * TK_HIST_GROUPS; // groups per block
-    const uint32_t bpw = (p.NG + GPB - 1) / GPB;
+    constexpr uint32_t UPG = TK_GROUP / TK_HIST_TPW; // waves per tile group
+    const uint32_t units = p.NG * UPG;               // waves per worker
+    const uint32_t bpw = (units + (TK_THREADS / SG_WAVE) - 1) / (TK_THREADS / SG_WAVE);
     const uint32_t w = blockIdx.x / bpw, bi = blockIdx.x % bpw;
     const SelState st = p.st[w];
     if (st.R == 0 || st.top == 0) return;
@@ -567,13 +568,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
     digit_window(st.top, shift, width);
     for (uint32_t i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0;
     __syncthreads();
-    const uint32_t wid = threadIdx.x / SG_WAVE, lane = lane_id();
-    for (uint32_t q = 0; q < (uint32_t)TK_HIST_GROUPS; ++q) {
-        const uint32_t grp = (bi * (TK_THREADS / SG_WAVE) + wid) * TK_HIST_GROUPS + q;
-        if (grp >= p.NG) break;
+    const uint32_t wid = uniform(threadIdx.x / SG_WAVE), lane = lane_id();
+    const uint32_t unit = bi * (TK_THREADS / SG_WAVE) + wid;
+    if (unit < units) {
+        const uint32_t grp = unit / UPG, jb = (unit % UPG) * TK_HIST_TPW;
         const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
         const uint32_t c = grp * TK_GROUP + lane < p.NT ? p.ccnt[g0 + lane] : 0u;
-        for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 16) {
+        for (uint32_t j0 = jb; j0 < jb + TK_HIST_TPW; j0 += 16) {
             uint32_t kk[16], cj[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -928,7 +929,7 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
         topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
         SG_TRY_LAUNCH();
     }
-    const unsigned hgrid = n * (unsigned)ceil_div(p.NG, (TK_THREADS / SG_WAVE) * TK_HIST_GROUPS);
+    const unsigned hgrid = n * (unsigned)ceil_div((uint64_t)p.NG * (TK_GROUP / TK_HIST_TPW), TK_THREADS / SG_WAVE);
     for (int pass = 0; pass < 3; ++pass) {
         topk_hist_kernel<<<hgrid, TK_THREADS, 0, st>>>(p);
         SG_TRY_LAUNCH();
