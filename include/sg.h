@@ -139,7 +139,8 @@ int sg_validate_coo(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n,
  * (they are compared as bit patterns); finite inputs are the contract.
  *   d_dense  [n][M] of dt, row-major (worker-major)
  *   d_idx    [n][k] uint32 out;   d_val [n][k] of dt out
- * Limits: 1 <= n, 1 <= M < 2^32, k <= M.  k == 0 writes nothing.
+ * Limits: 1 <= n, 1 <= M < 2^32, k <= M (else SG_EINVAL); n * ceil(M / 1024)
+ * < 2^31 (else SG_EUNSUPPORTED).  k == 0 writes nothing.
  * ------------------------------------------------------------------------ */
 size_t sg_topk_workspace_bytes(uint32_t n, uint64_t M, uint64_t k, sg_dtype dt);
 int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint64_t M, uint64_t k, uint32_t* d_idx,

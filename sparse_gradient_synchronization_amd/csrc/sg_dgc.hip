@@ -331,14 +331,13 @@ extern "C" int sg_dgc_select(const float* d_grad, float* d_resid, uint32_t n, ui
     dgc_count_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     if (cap == 0) return SG_OK;
-    const unsigned wgrid = (unsigned)ceil_div((uint64_t)n * p.t.NG, TK_THREADS / SG_WAVE);
-    const unsigned wgrid4 = (unsigned)ceil_div((uint64_t)n * p.t.NG * 4, TK_THREADS / SG_WAVE);
-    topk_tilecount_kernel<<<wgrid, TK_THREADS, 0, st>>>(p.t);
+    const unsigned wgridw = (unsigned)ceil_div((uint64_t)n * p.t.NG * TK_WRITE_WAVES, TK_THREADS / SG_WAVE);
+    topk_tilecount_kernel<<<(unsigned)ceil_div((uint64_t)n * p.t.NG, TK_THREADS / SG_WAVE), TK_THREADS, 0, st>>>(p.t);
     SG_TRY_LAUNCH();
     topk_scan_kernel<<<n, 1024, 0, st>>>(p.t);
     SG_TRY_LAUNCH();
-    if (p.t.bf16) topk_write_kernel<true><<<wgrid4, TK_THREADS, 0, st>>>(p.t);
-    else topk_write_kernel<false><<<wgrid4, TK_THREADS, 0, st>>>(p.t);
+    if (p.t.bf16) topk_write_kernel<true><<<wgridw, TK_THREADS, 0, st>>>(p.t);
+    else topk_write_kernel<false><<<wgridw, TK_THREADS, 0, st>>>(p.t);
     SG_TRY_LAUNCH();
     return SG_OK;
 }

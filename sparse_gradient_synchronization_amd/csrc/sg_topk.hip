@@ -33,6 +33,7 @@ constexpr int TK_DIGIT_BITS = 11;
 constexpr int TK_BINS = 1 << TK_DIGIT_BITS;
 constexpr int TK_GROUP = 64;       // tiles per wave in the select and write passes (one per lane)
 constexpr int TK_HIST_TPW = 64;    // tiles per wave in the histogram pass (one tile group)
+constexpr int TK_WRITE_WAVES = 16; // waves per tile group in the write pass
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -554,7 +555,8 @@ __device__ __forceinline__ uint32_t cand_digit(const SelState& st, uint32_t key,
 
 // Histogram of the current digit over the candidates.  A wave takes groups
 // of 64 tiles (the tile counts in one load, one lane per tile) and loads the
-// candidates of 16 tiles at a time, so the loads overlap.
+// first 128 candidates of 16 tiles at a time, so the loads overlap (a tile
+// with more candidates loads the rest afterwards).
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
 {
     __shared__ uint32_t h[TK_BINS];
@@ -575,11 +577,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
         const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
         const uint32_t c = grp * TK_GROUP + lane < p.NT ? p.ccnt[g0 + lane] : 0u;
         for (uint32_t j0 = jb; j0 < jb + TK_HIST_TPW; j0 += 16) {
-            uint32_t kk[16], cj[16];
+            uint32_t kk[16], k2[16], cj[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
-                kk[u] = lane < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + lane] : 0u;
+                const uint32_t* sk = p.slot_key + (g0 + j0 + u) * TK_TILE;
+                kk[u] = lane < cj[u] ? sk[lane] : 0u;
+                k2[u] = SG_WAVE + lane < cj[u] ? sk[SG_WAVE + lane] : 0u;
             }
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -587,7 +591,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(TopkParams p)
                     const uint32_t d = cand_digit(st, kk[u], shift, width);
                     if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
                 }
-                for (uint32_t i = SG_WAVE + lane; i < cj[u]; i += SG_WAVE) { // tiles with more than 64 candidates
+                if (SG_WAVE + lane < cj[u]) {
+                    const uint32_t d = cand_digit(st, k2[u], shift, width);
+                    if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                }
+                for (uint32_t i = 2 * SG_WAVE + lane; i < cj[u]; i += SG_WAVE) { // tiles with more than 128 candidates
                     const uint32_t d = cand_digit(st, p.slot_key[(g0 + j0 + u) * TK_TILE + i], shift, width);
                     if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
                 }
@@ -676,17 +684,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_tilecount_kernel(TopkParams p
     const uint32_t c = valid ? p.ccnt[g0 + lane] : 0u;
     uint32_t my_gt = valid ? p.tcnt[g0 + lane] - c : 0u, my_eq = 0;
     for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 8) {
-        uint32_t kk[8], cj[8];
+        uint32_t kk[8], k2[8], cj[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
-            kk[u] = lane < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + lane] : 0u;
+            const uint32_t* sk = p.slot_key + (g0 + j0 + u) * TK_TILE;
+            kk[u] = lane < cj[u] ? sk[lane] : 0u;
+            k2[u] = SG_WAVE + lane < cj[u] ? sk[SG_WAVE + lane] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            uint32_t gt = popc64(ballot(lane < cj[u] && kk[u] > T));
-            uint32_t eq = popc64(ballot(lane < cj[u] && kk[u] == T));
-            for (uint32_t i0 = SG_WAVE; i0 < cj[u]; i0 += SG_WAVE) { // tiles with more than 64 candidates
+            uint32_t gt = popc64(ballot(lane < cj[u] && kk[u] > T)) + popc64(ballot(SG_WAVE + lane < cj[u] && k2[u] > T));
+            uint32_t eq = popc64(ballot(lane < cj[u] && kk[u] == T)) + popc64(ballot(SG_WAVE + lane < cj[u] && k2[u] == T));
+            for (uint32_t i0 = 2 * SG_WAVE; i0 < cj[u]; i0 += SG_WAVE) { // tiles with more than 128 candidates
                 const uint32_t i = i0 + lane;
                 const uint32_t key = i < cj[u] ? p.slot_key[(g0 + j0 + u) * TK_TILE + i] : 0u;
                 gt += popc64(ballot(i < cj[u] && key > T));
@@ -776,20 +786,20 @@ __device__ __forceinline__ void write_chunk(uint32_t* oidx, void* oval, uint64_t
     eqr += popc64(meq);
 }
 
-// Four waves per group of 64 tiles; each wave writes 16 of them.  The tiles'
+// TK_WRITE_WAVES waves per group of 64 tiles; wave j writes the tiles j,
+// j + TK_WRITE_WAVES, ... of it, so the tiles of a dense row (one chunk per
+// 64 entries, up to 16 per tile) are spread over several waves.  The tiles'
 // output offsets come from the group prefix and a wave scan over the group.
-// The wave's slot chunks (64 entries each) are numbered across its tiles and
-// loaded 16 at a time, so dense tiles (whole rows above the band) cost no
-// more load rounds than their size demands.
+// The wave's slot chunks are numbered across its tiles and loaded 8 at a
+// time, so dense tiles cost no more load rounds than their size demands.
 template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
 {
-    constexpr uint32_t TPW = TK_GROUP / 4; // tiles per wave
-    constexpr int B = 16;                  // chunks per load round
+    constexpr int B = 8;                                // chunks per load round
     const uint64_t gq = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + uniform(threadIdx.x / SG_WAVE);
-    if (gq >= (uint64_t)p.n * p.NG * 4) return;
-    const uint64_t gw = gq / 4;
-    const uint32_t quarter = (uint32_t)(gq % 4);
+    if (gq >= (uint64_t)p.n * p.NG * TK_WRITE_WAVES) return;
+    const uint64_t gw = gq / TK_WRITE_WAVES;
+    const uint32_t part = (uint32_t)(gq % TK_WRITE_WAVES);
     const uint32_t lane = lane_id();
     const uint32_t w = (uint32_t)(gw / p.NG), grp = (uint32_t)(gw % p.NG);
     const uint32_t T = p.st[w].T, need = p.st[w].need;
@@ -800,7 +810,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
     const uint32_t xg = p.ggt[gw] + wave_incl_scan(gt) - gt;
     const uint32_t xe = p.geq[gw] + wave_incl_scan(eq) - eq;
     // chunks of this wave's tiles, numbered in tile order
-    const bool mine = lane / TPW == quarter;
+    const bool mine = lane % TK_WRITE_WAVES == part;
     const uint32_t nch = mine ? (cnt + SG_WAVE - 1) / SG_WAVE : 0u;
     const uint32_t cinc = wave_incl_scan(nch);
     const uint32_t cst = cinc - nch;
@@ -879,6 +889,7 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
     if (!d_dense || !d_idx || !d_val || !d_ws) return SG_EINVAL;
     if (ws_bytes < sg_topk_workspace_bytes(n, M, k, dt)) return SG_ECAPACITY;
     if ((uintptr_t)d_dense % 16) return SG_EINVAL;
+    if ((uint64_t)n * ceil_div(M, TK_TILE) >= (1ull << 31)) return SG_EUNSUPPORTED; // tiles and tile groups index grids
 
     TopkParams p;
     Carver c(d_ws);
@@ -936,15 +947,14 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
         topk_pick_kernel<<<n, TK_THREADS, 0, st>>>(p);
         SG_TRY_LAUNCH();
     }
-    const unsigned wgrid = (unsigned)ceil_div((uint64_t)n * p.NG, TK_THREADS / SG_WAVE);
-    const unsigned wgrid4 = (unsigned)ceil_div((uint64_t)n * p.NG * 4, TK_THREADS / SG_WAVE);
-    topk_tilecount_kernel<<<wgrid, TK_THREADS, 0, st>>>(p);
+    const unsigned wgridw = (unsigned)ceil_div((uint64_t)n * p.NG * TK_WRITE_WAVES, TK_THREADS / SG_WAVE);
+    topk_tilecount_kernel<<<(unsigned)ceil_div((uint64_t)n * p.NG, TK_THREADS / SG_WAVE), TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     topk_scan_kernel<<<n, 1024, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_TOPK_WRITE, st);
-    if (p.bf16) topk_write_kernel<true><<<wgrid4, TK_THREADS, 0, st>>>(p);
-    else topk_write_kernel<false><<<wgrid4, TK_THREADS, 0, st>>>(p);
+    if (p.bf16) topk_write_kernel<true><<<wgridw, TK_THREADS, 0, st>>>(p);
+    else topk_write_kernel<false><<<wgridw, TK_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_TOPK_WRITE, st);
     return SG_OK;
