@@ -186,7 +186,7 @@ __device__ __forceinline__ void dgc_tile(const DgcParams& p, uint32_t w, uint32_
 #pragma unroll
             for (int v = 0; v < EPV; ++v) {
                 if ((f >> v) & 1u) {
-                    p.t.slot_idx[slot + pos] = (uint32_t)(tile0 + e0 + v);
+                    p.t.slot_idx[slot + pos] = (uint16_t)(e0 + v);
                     p.t.slot_val[slot + pos] = __float_as_uint(a[i][v]);
                     ++pos;
                 }
@@ -245,7 +245,7 @@ static uint64_t dgc_carve(Carver& c, uint32_t n, uint64_t M, uint64_t S, DgcPara
     p->t.eqx = c.take<uint32_t>(nt);
     p->t.ggt = c.take<uint32_t>(ng);
     p->t.geq = c.take<uint32_t>(ng);
-    p->t.slot_idx = c.take<uint32_t>(nt * TK_TILE);
+    p->t.slot_idx = c.take<uint16_t>(nt * TK_TILE);
     p->t.slot_val = c.take<uint32_t>(nt * TK_TILE);
     p->samples = c.take<uint32_t>((uint64_t)n * S);
     p->hist = c.take<uint32_t>(TK_BINS);

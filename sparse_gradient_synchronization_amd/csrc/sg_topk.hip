@@ -55,7 +55,7 @@ struct TopkParams {
     SelState* st;          // [n]
     uint32_t* tcnt;        // [n*NT] entries with key >= lo
     uint32_t* ccnt;        // [n*NT] candidates
-    uint32_t* slot_idx;    // [n*NT*TILE]
+    uint16_t* slot_idx;    // [n*NT*TILE] position of a slot entry in its tile
     uint32_t* slot_val;    // [n*NT*TILE] value bits (bf16 in the low half)
     uint32_t* slot_key;    // [n*NT*TILE] candidate keys
     uint32_t* hist;        // [n][TK_BINS]
@@ -264,7 +264,7 @@ __device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uin
 #pragma unroll
             for (int v = 0; v < EPV; ++v) {
                 if ((fge >> v) & 1u) {
-                    p.slot_idx[slot + pos] = (uint32_t)(tile0 + e0 + v);
+                    p.slot_idx[slot + pos] = (uint16_t)(e0 + v);
                     p.slot_val[slot + pos] = bits[i][v];
                     ++pos;
                 }
@@ -302,7 +302,6 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
     constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
     constexpr int CB = EPV == 4 ? 3 : 4; // bits of a per-lane count in [0, EPV]
     const uint32_t lane = lane_id();
-    const uint32_t tile0 = t * TK_TILE;
     const uint64_t g = (uint64_t)w * p.NT + t;
     char* const sidx = reinterpret_cast<char*>(p.slot_idx + g * TK_TILE);
     char* const sval = reinterpret_cast<char*>(p.slot_val + g * TK_TILE);
@@ -321,7 +320,7 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
 #pragma unroll
             for (int v = 0; v < EPV; ++v) bits[v] = (q[v / 2] >> (16 * (v % 2))) & 0xffffu;
         }
-        const uint32_t e0 = tile0 + i * (SG_WAVE * EPV) + lane * EPV;
+        const uint32_t e0 = i * (SG_WAVE * EPV) + lane * EPV; // in the tile
         uint32_t fge = 0, fca = 0;
 #pragma unroll
         for (int v = 0; v < EPV; ++v) {
@@ -343,7 +342,7 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
                 uint32_t b = bits[0];
 #pragma unroll
                 for (int u = 1; u < EPV; ++u) b = v == (uint32_t)u ? bits[u] : b;
-                *reinterpret_cast<uint32_t*>(sidx + pos * 4u) = e0 + v;
+                *reinterpret_cast<uint16_t*>(sidx + pos * 2u) = (uint16_t)(e0 + v);
                 *reinterpret_cast<uint32_t*>(sval + pos * 4u) = b;
                 ++pos;
                 f &= f - 1u;
@@ -832,7 +831,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
             const uint32_t i = ch[u] + lane;
             const uint64_t sb = (g0 + tj[u]) * TK_TILE;
             vb[u] = q < C && i < cj ? p.slot_val[sb + i] : 0u;
-            vi[u] = q < C && i < cj ? p.slot_idx[sb + i] : 0u;
+            vi[u] = q < C && i < cj ? (uint32_t)p.slot_idx[sb + i] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < B; ++u) {
@@ -843,7 +842,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
                 pos = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xg, (int)cur_tile) + (eqr < need ? eqr : need);
             }
             const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
-            write_chunk<BF16>(oidx, oval, p.k, cj - ch[u], vb[u], vi[u], T, need, pos, eqr);
+            const uint32_t tile0 = (grp * TK_GROUP + tj[u]) * TK_TILE; // first index of the tile
+            write_chunk<BF16>(oidx, oval, p.k, cj - ch[u], vb[u], tile0 + vi[u], T, need, pos, eqr);
         }
     }
 }
@@ -866,7 +866,7 @@ static uint64_t topk_carve(Carver& c, uint32_t n, uint64_t M, TopkParams* p)
     p->geq = c.take<uint32_t>(ng);
     p->hist = c.take<uint32_t>((uint64_t)n * TK_BINS);
     p->samples = c.take<uint32_t>((uint64_t)n * TK_SAMPLES);
-    p->slot_idx = c.take<uint32_t>(nt * TK_TILE);
+    p->slot_idx = c.take<uint16_t>(nt * TK_TILE);
     p->slot_val = c.take<uint32_t>(nt * TK_TILE);
     p->slot_key = c.take<uint32_t>(nt * TK_TILE);
     return c.bytes();
