@@ -97,7 +97,8 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
         SG_TRY_LAUNCH();
         mg_scan_top_kernel<<<1, 1024, 0, st>>>(p);
         SG_TRY_LAUNCH();
-        const uint64_t pblocks = ceil_div(T, 4) < 65536 ? ceil_div(T, 4) : 65536;
+        const uint64_t pwaves = ceil_div(T, MG_PLACE_TILES);
+        const uint64_t pblocks = ceil_div(pwaves, 4) < 65536 ? ceil_div(pwaves, 4) : 65536;
         mg_place_kernel<<<(unsigned)pblocks, 256, 0, st>>>(p);
         SG_TRY_LAUNCH();
         if (p.D > 1 && p.total > 0) {

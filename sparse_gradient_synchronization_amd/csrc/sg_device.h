@@ -59,6 +59,17 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
     return ((uint64_t)uniform((uint32_t)(v >> 32)) << 32) | uniform((uint32_t)v);
 }
 
+// v of lane l (l wave-uniform), in scalar registers
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
+}
+
+__device__ __forceinline__ uint64_t lane_value64(uint64_t v, uint32_t l)
+{
+    return ((uint64_t)lane_value((uint32_t)(v >> 32), l) << 32) | lane_value((uint32_t)v, l);
+}
+
 // Cross-lane moves by DPP (data-parallel primitives of the GFX9 ISA family):
 // a lane reads another lane's register inside the VALU, without the LDS
 // round trip of ds_bpermute.  Lanes whose source is outside its row, or whose

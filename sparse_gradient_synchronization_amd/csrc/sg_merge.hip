@@ -212,29 +212,39 @@ __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 }
 
 // Tiles with more than MG_HEAVY entries, listed so the merge starts them
-// first (longest first keeps the last waves short).
+// first (longest first keeps the last waves short).  A tile's entry count is
+// the sum over its runs of bnd[b + 1] - bnd[b]; the loads of 8 runs are
+// issued together (rows past the last run read run 0's row and are not
+// counted).  The count only orders the work, so a row is not checked here
+// against its run's length (the merge does that).
 __global__ __launch_bounds__(256) void mg_heavy_kernel(MergeParams p)
 {
     const uint32_t T = p.G * p.NT;
     for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
     const uint32_t g = t / p.NT, b = t % p.NT;
     uint32_t E = 0;
-    for (uint32_t w0 = 0; w0 < p.n; w0 += 8) { // 8 runs' loads at once
+    const uint32_t* rows = p.bnd + (uint64_t)g * p.n * (p.NT + 1) + b;
+    for (uint32_t w0 = 0; w0 < p.n; w0 += 8) {
+        uint32_t x[8], y[8];
 #pragma unroll
         for (uint32_t u = 0; u < 8; ++u) {
-            const uint32_t w = w0 + u;
-            if (w >= p.n) break;
-            uint64_t s, e;
-            run_range(p, g, w, s, e);
-            const uint64_t len = e - s;
-            const uint32_t* row = p.bnd + ((uint64_t)g * p.n + w) * (p.NT + 1);
-            uint64_t x = row[b], y = row[b + 1];
-            if (x > len) x = len;
-            if (y > len) y = len;
-            E += y > x ? (uint32_t)(y - x) : 0u;
+            const uint32_t* row = rows + (uint64_t)(w0 + u < p.n ? w0 + u : 0u) * (p.NT + 1);
+            x[u] = row[0];
+            y[u] = row[1];
         }
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u)
+            if (w0 + u < p.n && y[u] > x[u]) E += y[u] - x[u];
     }
-    if (E > (uint32_t)MG_HEAVY) p.heavy[atomicAdd(&p.queue[0], 1u)] = t;
+    // one list append per wave: the heavy lanes take consecutive slots
+    const bool hv = E > (uint32_t)MG_HEAVY;
+    const uint64_t m = ballot(hv);
+    if (m) {
+        uint32_t base = 0;
+        if (count_below(ballot(true)) == 0) base = atomicAdd(&p.queue[0], (uint32_t)popc64(m)); // first active lane
+        base = uniform(base);
+        if (hv) p.heavy[base + count_below(m)] = t;
+    }
     }
 }
 
@@ -799,55 +809,74 @@ __global__ __launch_bounds__(1024) void mg_scan_top_kernel(MergeParams p)
     if (threadIdx.x == 0) p.agg_off[p.G] = carry;
 }
 
-// One wave per tile: the tile's staged keys (and values) are read in
-// batches of MG_PLACE_CHUNKS x 64 entries, all loads of a batch in flight
-// before it is waited for once and written out.
+// A wave places MG_PLACE_TILES consecutive tiles: their counts and offsets
+// in one load (lane j holds tile t0 + j), then their staged keys (and
+// values) in chunks of 64 entries numbered across the tiles, MG_PLACE_CHUNKS
+// chunks per round with all loads of a round in flight before it is waited
+// for once and written out.
+constexpr int MG_PLACE_TILES = 16;
 constexpr int MG_PLACE_CHUNKS = 16;
 
 __global__ __launch_bounds__(256) void mg_place_kernel(MergeParams p)
 {
     const uint32_t T = p.G * p.NT;
     const uint32_t lane = lane_id();
-    for (uint32_t t = blockIdx.x * 4 + uniform(threadIdx.x / SG_WAVE); t < T; t += gridDim.x * 4) {
-        uint32_t c = uniform(p.tile_cnt[t]);
-        const uint64_t sb = uniform64(p.tile_sb[t]);
-        const uint64_t ob = uniform64(p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK]);
-        if (t % p.NT == 0 && lane == 0) p.agg_off[t / p.NT] = ob;
-        if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
-            if (lane == 0) report_error(kDevErrPartition);
-            c = 0;
+    const uint32_t stride = gridDim.x * 4 * MG_PLACE_TILES;
+    for (uint32_t t0 = (blockIdx.x * 4 + uniform(threadIdx.x / SG_WAVE)) * MG_PLACE_TILES; t0 < T; t0 += stride) {
+        const uint32_t t = t0 + lane;
+        uint32_t c = 0;
+        uint64_t sb = 0, ob = 0;
+        if (lane < (uint32_t)MG_PLACE_TILES && t < T) {
+            c = p.tile_cnt[t];
+            sb = p.tile_sb[t];
+            ob = p.tile_out[t] + p.blk_sum[t / MG_SCAN_BLOCK];
+            if (t % p.NT == 0) p.agg_off[t / p.NT] = ob;
+            if (ob + c > p.capacity || sb + c > p.total) { // cannot happen: a tile has no more keys than entries
+                report_error(kDevErrPartition);
+                c = 0;
+            }
         }
-        if (c == 0) continue;
         if (p.D <= 1) {
-            for (uint32_t k0 = 0; k0 < c; k0 += MG_PLACE_CHUNKS * SG_WAVE) {
-                uint32_t vi[MG_PLACE_CHUNKS], vv[MG_PLACE_CHUNKS];
+            const uint32_t nch = (c + SG_WAVE - 1) / SG_WAVE;
+            const uint32_t cinc = wave_incl_scan(nch);
+            const uint32_t cst = cinc - nch;
+            const uint32_t C = lane_value(cinc, SG_WAVE - 1);
+            for (uint32_t b0 = 0; b0 < C; b0 += MG_PLACE_CHUNKS) {
+                uint32_t vi[MG_PLACE_CHUNKS], vv[MG_PLACE_CHUNKS], ci[MG_PLACE_CHUNKS], tj[MG_PLACE_CHUNKS];
 #pragma unroll
                 for (int u = 0; u < MG_PLACE_CHUNKS; ++u) {
-                    vi[u] = vv[u] = 0u;
-                    if (k0 + u * SG_WAVE < c) { // uniform: the chunks the tile has
-                        const uint32_t i = k0 + u * SG_WAVE + lane;
-                        const uint64_t src = sb + (i < c ? i : c - 1);
-                        vi[u] = p.stage_idx[src];
-                        vv[u] = p.D == 1 ? __float_as_uint(p.stage_val[src]) : 0u;
-                    }
+                    const uint32_t q = b0 + u;
+                    // the last tile whose chunks start at or before chunk q
+                    // (for q >= C: the last tile with entries)
+                    const uint64_t has = ballot(nch > 0 && cst <= q);
+                    tj[u] = has ? 63u - (uint32_t)__builtin_clzll(has) : 0u;
+                    const uint32_t cj = lane_value(c, tj[u]);
+                    const uint32_t i = (q - lane_value(cst, tj[u])) * SG_WAVE + lane;
+                    ci[u] = q < C && i < cj ? i : 0xffffffffu;
+                    const uint64_t src = lane_value64(sb, tj[u]) + (ci[u] != 0xffffffffu ? i : 0u);
+                    vi[u] = p.stage_idx[src];
+                    vv[u] = p.D == 1 ? __float_as_uint(p.stage_val[src]) : 0u;
                 }
                 wait_vmem();
 #pragma unroll
                 for (int u = 0; u < MG_PLACE_CHUNKS; ++u) {
-                    const uint32_t i = k0 + u * SG_WAVE + lane;
-                    if (i < c) {
-                        p.agg_idx[ob + i] = vi[u];
-                        if (p.D == 1) p.agg_val[ob + i] = __uint_as_float(vv[u]);
-                    }
+                    if (ci[u] == 0xffffffffu) continue;
+                    const uint64_t o = lane_value64(ob, tj[u]) + ci[u];
+                    p.agg_idx[o] = vi[u];
+                    if (p.D == 1) p.agg_val[o] = __uint_as_float(vv[u]);
                 }
             }
         } else {
             // rows: the key, and where the row's contributors are listed
-            const uint32_t ent = uniform(p.tile_ent[t]);
-            for (uint32_t i = lane; i < c; i += SG_WAVE) {
-                p.agg_idx[ob + i] = p.stage_idx[sb + i];
-                const uint32_t f0 = p.stage_first[sb + i], f1 = i + 1 < c ? p.stage_first[sb + i + 1] : ent;
-                p.row_rng[ob + i] = make_uint2((uint32_t)(sb + f0), (uint32_t)(sb + (f1 > f0 ? f1 : f0)));
+            for (uint32_t j = 0; j < (uint32_t)MG_PLACE_TILES && t0 + j < T; ++j) {
+                const uint32_t cj = lane_value(c, j);
+                const uint64_t sbj = lane_value64(sb, j), obj = lane_value64(ob, j);
+                const uint32_t ent = cj ? uniform(p.tile_ent[t0 + j]) : 0u;
+                for (uint32_t i = lane; i < cj; i += SG_WAVE) {
+                    p.agg_idx[obj + i] = p.stage_idx[sbj + i];
+                    const uint32_t f0 = p.stage_first[sbj + i], f1 = i + 1 < cj ? p.stage_first[sbj + i + 1] : ent;
+                    p.row_rng[obj + i] = make_uint2((uint32_t)(sbj + f0), (uint32_t)(sbj + (f1 > f0 ? f1 : f0)));
+                }
             }
         }
     }

@@ -3,15 +3,20 @@
 // 3.1 Def. 8).
 //
 // The union and every pairwise intersection come, for up to 16 workers and
-// 16 hash classes, from the window pass of sg_statsw.hip (per-worker bitmaps
-// of 2048-key windows); otherwise from the merge engine run over the
-// workers' lists (one group): per union index the set of workers holding it
-// is a 64-bit mask; per 64 indices a wave turns the masks into one ballot
-// word per worker and adds popcount(V_a & V_b) for each pair.  Either way
-// the passes write partial rows of counts and a last pass sums the rows.
-// Each worker's counts per contiguous part come from binary searches in its
-// ascending list, its counts per hash class from one pass over the entries.
-// The host then evaluates the definitions in double with fixed expressions.
+// 16 parts when the lists hold at least one entry per 16 * 32 keys of the
+// key space per worker on average, from the dense pass of sg_statsd.hip
+// (per-worker bitmaps of the whole key space, which also give each worker's
+// counts per part and per class); otherwise, for up to 16 workers and 16
+// hash classes, from the window pass of sg_statsw.hip (per-worker bitmaps of
+// 2048-key windows); otherwise from the merge engine run over the workers'
+// lists (one group): per union index the set of workers holding it is a
+// 64-bit mask; per 64 indices a wave turns the masks into one ballot word per
+// worker and adds popcount(V_a & V_b) for each pair.  Every pass writes
+// partial rows of counts and a last pass sums the rows.  Outside the dense
+// pass each worker's counts per contiguous part come from binary searches in
+// its ascending list, its counts per hash class from one pass over the
+// entries.  The host then evaluates the definitions in double with fixed
+// expressions.
 #include "sg_host.h"
 
 namespace sg {
@@ -129,6 +134,13 @@ static bool stats_windowed(uint32_t n, uint32_t P, bool hashed)
     return n <= (uint32_t)SW_MAXN && (!hashed || P <= (uint32_t)SW_MAXP);
 }
 
+// The dense pass: few enough workers and parts, and bitmaps of the key space
+// no more than 16 times the entries (n * ceil(M/32) words <= 16 * total).
+static bool stats_dense(uint32_t n, uint64_t M, uint64_t total, uint32_t P)
+{
+    return total > 0 && n <= DN_MAXN && P <= DN_MAXP && (uint64_t)n * ceil_div(M, 32) <= 16ull * total;
+}
+
 static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, uint32_t P, bool windowed)
 {
     *p = MergeParams();
@@ -150,10 +162,15 @@ static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, 
     }
 }
 
-static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k, SwParams* sw)
+static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* k, SwParams* sw, DnParams* dn)
 {
     const uint32_t n = p->n;
-    if (sw) { // the window pass: the boundary plan of the merge engine, the balance, partial rows
+    if (dn) { // the dense pass: bitmaps, partial rows (with each worker's counts per part)
+        dn->words = ceil_div(p->M, 32);
+        dn->st_row = p->st_row + n * P;
+        dn->bm = c.take<uint32_t>((uint64_t)n * dn->words);
+        dn->rows = c.take<uint64_t>((uint64_t)DN_MAX_WAVES * dn->st_row);
+    } else if (sw) { // the window pass: the boundary plan of the merge engine, the balance, partial rows
         const uint64_t R = n;
         p->nscan = (uint32_t)ceil_div(p->NT, MG_SCAN_BLOCK);
         p->chunk_start = c.take<uint32_t>(R + 1);
@@ -181,16 +198,18 @@ static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* 
 extern "C" size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P)
 {
     if (n == 0 || P == 0) return 256;
-    // enough for either pass (the class map is not known here)
+    // enough for any pass the call can take (the class map is not known here)
     size_t best = 0;
-    for (int windowed = 0; windowed < 2; ++windowed) {
-        if (windowed && !stats_windowed(n, P, false)) continue;
+    for (int mode = 0; mode < 3; ++mode) { // merge, window, dense
+        if (mode == 1 && !stats_windowed(n, P, false)) continue;
+        if (mode == 2 && !stats_dense(n, M, total, P)) continue;
         MergeParams p;
-        stats_setup(&p, n, M, total, P, windowed != 0);
+        stats_setup(&p, n, M, total, P, mode == 1);
         Carver c(nullptr);
         StatsCounts k;
         SwParams sw;
-        const size_t b = stats_carve(c, &p, P, &k, windowed ? &sw : nullptr);
+        DnParams dn;
+        const size_t b = stats_carve(c, &p, P, &k, mode == 1 ? &sw : nullptr, mode == 2 ? &dn : nullptr);
         if (b > best) best = b;
     }
     return best;
@@ -245,6 +264,36 @@ static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64
     return SG_OK;
 }
 
+// The dense pass: zeroed bitmaps, their build (with each worker's counts per
+// class), the count pass, the sum of the partial rows into `out` (the row and
+// then each worker's counts per contiguous part).
+static int stats_dense_run(MergeParams& p, DnParams& d, hipStream_t st, uint64_t* out)
+{
+    int rc = fill_u32(d.bm, (uint64_t)d.n * d.words, 0, st);
+    if (rc) return rc;
+    dn_build_kernel<<<(unsigned)ceil_div(d.total, DN_CHUNK), 256, 0, st>>>(d);
+    SG_TRY_LAUNCH();
+    uint64_t W = ceil_div(d.words, SG_WAVE);
+    if (W > DN_MAX_WAVES) W = DN_MAX_WAVES;
+    d.wpw = ceil_div(ceil_div(d.words, W), SG_WAVE) * SG_WAVE;
+    const unsigned grid = (unsigned)ceil_div(ceil_div(d.words, d.wpw), 4);
+    const bool hashed = d.planes != nullptr;
+    if (d.n <= 8) {
+        if (hashed) dn_count_kernel<8, true><<<grid, 256, 0, st>>>(d);
+        else dn_count_kernel<8, false><<<grid, 256, 0, st>>>(d);
+    } else {
+        if (hashed) dn_count_kernel<16, true><<<grid, 256, 0, st>>>(d);
+        else dn_count_kernel<16, false><<<grid, 256, 0, st>>>(d);
+    }
+    SG_TRY_LAUNCH();
+    MergeParams q = p;
+    q.st_part = d.rows;
+    q.st_row = d.st_row;
+    mg_stats_reduce_kernel<<<d.st_row, 256, 0, st>>>(q, grid * 4, out);
+    SG_TRY_LAUNCH();
+    return SG_OK;
+}
+
 // Def. 5 on one set J: max over parts of (c_i M) / (g_i |J|); 0 if J is empty.
 static double skew_of(const uint64_t* c, const uint64_t* g, uint32_t P, uint64_t M, uint64_t J)
 {
@@ -294,13 +343,15 @@ static int stats_enqueue(const uint32_t* d_idx, const uint64_t* d_in_off, uint32
         cm = cmap_ptrs(const_cast<void*>(d_cmap), L);
     }
 
-    const bool windowed = total > 0 && stats_windowed(n, P, d_cmap != nullptr);
+    const bool dense = stats_dense(n, M, total, P);
+    const bool windowed = !dense && total > 0 && stats_windowed(n, P, d_cmap != nullptr);
     MergeParams p;
     stats_setup(&p, n, M, total, P, windowed);
     Carver c(d_ws);
     StatsCounts k;
     SwParams sw;
-    stats_carve(c, &p, P, &k, windowed ? &sw : nullptr);
+    DnParams dn;
+    stats_carve(c, &p, P, &k, windowed ? &sw : nullptr, dense ? &dn : nullptr);
     p.idx = d_idx;
     p.off = d_in_off;
     p.seed = 0;
@@ -310,7 +361,30 @@ static int stats_enqueue(const uint32_t* d_idx, const uint64_t* d_in_off, uint32
     // per-worker part counters are accumulated with atomics: zero them
     int rc = fill_u64(k.wcontig, 2ull * n * P, 0, st); // wcontig and whashed are adjacent
     if (rc) return rc;
-    if (windowed) {
+    if (dense) {
+        dn.idx = d_idx;
+        dn.in_off = d_in_off;
+        dn.total = total;
+        dn.M = M;
+        dn.n = n;
+        dn.P = P;
+        dn.inv_m = p.inv_m;
+        dn.planes = nullptr;
+        dn.nbits = 0;
+        dn.stride = 0;
+        if (d_cmap && P >= 2) { // P = 1: every key is in class 0 (the union's count, below)
+            const CmapLayout L = cmap_layout(M, P);
+            dn.planes = cmap_ptrs(const_cast<void*>(d_cmap), L).planes;
+            dn.nbits = L.nbits;
+            dn.stride = L.stride;
+        }
+        dn.seed_at = p.seed_at;
+        dn.classes = d_cmap != nullptr;
+        dn.div = p.div;
+        dn.whashed = k.whashed;
+        dn.npairs = p.npairs;
+        rc = stats_dense_run(p, dn, st, k.row);
+    } else if (windowed) {
         sw.planes = nullptr;
         sw.nbits = 0;
         sw.stride = 0;
@@ -325,9 +399,11 @@ static int stats_enqueue(const uint32_t* d_idx, const uint64_t* d_in_off, uint32
         rc = merge_run(p, MODE_STATS, st, k.row);
     }
     if (rc) return rc;
-    st_contig_kernel<<<(unsigned)ceil_div((uint64_t)n * P, 4), 256, 0, st>>>(p, k);
-    SG_TRY_LAUNCH();
-    if (d_cmap && total > 0) {
+    if (!dense) {
+        st_contig_kernel<<<(unsigned)ceil_div((uint64_t)n * P, 4), 256, 0, st>>>(p, k);
+        SG_TRY_LAUNCH();
+    }
+    if (!dense && d_cmap && total > 0) {
         st_entries_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, MG_THREADS, 0, st>>>(p, k);
         SG_TRY_LAUNCH();
     }

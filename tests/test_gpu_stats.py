@@ -36,13 +36,47 @@ def _check(idx, in_off, M, P, seed=None):
     return got
 
 
-# (n, P) spans both counting passes: the window pass (n <= 16, and P <= 16
-# with a class map) and the merge engine (more workers, or more classes)
+# (n, P) spans the counting passes: the dense pass (n <= 16, P <= 16, lists
+# not too sparse for M: 3000 entries per worker over 120000 keys are), the
+# merge engine (more workers, or more classes with a class map) and the
+# window pass (n <= 16 and more parts without a class map)
 @pytest.mark.parametrize("n,P", [(1, 1), (2, 2), (4, 4), (7, 3), (16, 16), (64, 8), (17, 5), (5, 200), (9, 17)])
 def test_stats_zipf(n, P):
     idx, in_off, _ = gen.coo_zipf(500 + n, n, 120000, 3000, 1.1)
     _check(idx, in_off, 120000, P, seed=13)
     _check(idx, in_off, 120000, P)
+
+
+# lists too sparse for the dense pass (3000 entries per worker over 2^24
+# keys): the window pass (n <= 16, P <= 16)
+@pytest.mark.parametrize("n,P", [(3, 4), (8, 8), (16, 16), (11, 1)])
+def test_stats_window_sparse(n, P):
+    M = 1 << 24
+    idx, in_off, _ = gen.coo_zipf(700 + n, n, M, 3000, 1.1)
+    _check(idx, in_off, M, P, seed=29)
+    _check(idx, in_off, M, P)
+
+
+# the dense pass at its edges: M not a multiple of 32 with the last key
+# present, runs of consecutive keys longer than a 32-key word and than a
+# wave, an empty worker between others, part boundaries inside words, n and
+# P at and below the compile-time bounds
+@pytest.mark.parametrize("n,P", [(16, 16), (9, 7), (2, 16)])
+def test_stats_dense_edges(n, P):
+    M = 100003
+    rng = np.random.default_rng(40 + n)
+    lists = []
+    for w in range(n):
+        if w == n // 2 and n > 2:
+            lists.append(np.zeros(0, np.uint32))
+            continue
+        runs = [np.arange(s, min(s + ln, M), dtype=np.uint32)
+                for s, ln in zip(rng.integers(0, M, 40), rng.integers(1, 200, 40))]
+        runs.append(np.array([0, M - 1], np.uint32))
+        lists.append(np.unique(np.concatenate(runs + [rng.integers(0, M, 2000).astype(np.uint32)])))
+    idx, in_off, _ = gen.coo_from_lists(lists, [a.astype(np.float32) for a in lists])
+    _check(idx, in_off, M, P, seed=5)
+    _check(idx, in_off, M, P)
 
 
 def test_stats_identical_disjoint_empty():
