@@ -448,6 +448,9 @@ typedef struct sg_stats_out {
     double push_imbalance, pull_imbalance;
 } sg_stats_out;
 
+/* Workspace of sg_stats / sg_stats_async for these sizes.  With n <= 16,
+ * P <= 16 and n * ceil(M/32) <= 16 * total it holds one bitmap of the key
+ * space per worker (n * ceil(M/32) * 4 bytes) for the dense counting pass. */
 size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t total, uint32_t P);
 int sg_stats(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n, uint64_t M, uint64_t total, uint32_t P,
              const void* d_cmap, size_t cmap_bytes, sg_stats_out* h_out, void* d_ws, size_t ws_bytes, void* stream);
