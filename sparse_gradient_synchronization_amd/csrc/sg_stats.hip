@@ -271,7 +271,8 @@ static int stats_dense_run(MergeParams& p, DnParams& d, hipStream_t st, uint64_t
 {
     int rc = fill_u32(d.bm, (uint64_t)d.n * d.words, 0, st);
     if (rc) return rc;
-    dn_build_kernel<<<(unsigned)ceil_div(d.total, DN_CHUNK), 256, 0, st>>>(d);
+    const uint64_t chunks = ceil_div(d.total, DN_CHUNK);
+    dn_build_kernel<<<(unsigned)(chunks < DN_BUILD_BLOCKS ? chunks : DN_BUILD_BLOCKS), 256, 0, st>>>(d);
     SG_TRY_LAUNCH();
     uint64_t W = ceil_div(d.words, SG_WAVE);
     if (W > DN_MAX_WAVES) W = DN_MAX_WAVES;

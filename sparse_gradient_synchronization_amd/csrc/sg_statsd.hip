@@ -36,7 +36,8 @@ namespace sg {
 constexpr uint32_t DN_MAXN = 16;          // workers
 constexpr uint32_t DN_MAXP = 16;          // parts and hash classes
 constexpr uint32_t DN_MAX_WAVES = 2048;   // waves (partial rows) of the count pass, at most
-constexpr uint32_t DN_CHUNK = 4096;       // list entries per build block
+constexpr uint32_t DN_CHUNK = 4096;       // list entries per chunk of the build
+constexpr uint32_t DN_BUILD_BLOCKS = 1024; // build blocks (they stride over the chunks), at most
 constexpr uint32_t DN_SPAN = 8192;        // LDS words of a build block's window of keys
 constexpr uint32_t DN_WINDOWS = 64;       // windows of a worker's run in a build block, at most
 
@@ -59,7 +60,9 @@ struct DnParams {
     uint64_t wpw;             // words per wave (a multiple of 64)
 };
 
-// A block takes DN_CHUNK consecutive list entries (all loads at once) and,
+// A block takes chunks of DN_CHUNK consecutive list entries (all loads of a
+// chunk at once; blocks stride over the chunks, so the class counts are
+// added to the result once per block) and,
 // for each worker's part of them (a sorted run of keys), ORs their bits into
 // an LDS copy of the words the run spans (DN_SPAN words at a time), then
 // writes the nonzero words out: plain stores inside the span (no other entry
@@ -86,58 +89,65 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
     for (uint32_t i = threadIdx.x; i < DN_MAXN * DN_MAXP; i += 256) hh[i] = 0;
     __syncthreads();
     const uint32_t hseed = classes ? d.seed_at[0] : 0u;
-    const uint64_t c0 = (uint64_t)blockIdx.x * DN_CHUNK;
-    const uint64_t c1 = c0 + DN_CHUNK < d.total ? c0 + DN_CHUNK : d.total; // c0 < total: one block per chunk
-    uint32_t key[U];
-#pragma unroll
-    for (uint32_t j = 0; j < U; ++j) {
-        const uint64_t e = c0 + j * 256 + threadIdx.x;
-        key[j] = d.idx[e < c1 ? e : c1 - 1];
-    }
-    for (uint32_t w = 0; w < d.n; ++w) { // the workers whose lists meet the chunk (uniform)
-        const uint64_t ea = off[w] > c0 ? off[w] : c0, eb = off[w + 1] < c1 ? off[w + 1] : c1;
-        if (ea >= eb) continue;
-        const uint32_t ka = d.idx[ea], kb = d.idx[eb - 1];
-        const uint32_t wa = ka >> 5, wb = kb >> 5;
-        uint32_t* const row = d.bm + (uint64_t)w * d.words;
-        // the run's words in windows of DN_SPAN; a run that does not ascend,
-        // or spans more than DN_WINDOWS windows, goes one entry at a time
-        const bool staged = ka <= kb && kb < d.M && wb - wa < DN_WINDOWS * DN_SPAN;
-        const uint32_t S = staged ? wb - wa + 1 : 0u;
-        if (!staged) {
-#pragma unroll
-            for (uint32_t j = 0; j < U; ++j) {
-                const uint64_t e = c0 + j * 256 + threadIdx.x;
-                if (e < ea || e >= eb) continue;
-                if (key[j] < d.M) atomicOr(&row[key[j] >> 5], 1u << (key[j] & 31u));
-            }
-        }
-        for (uint32_t base = 0; base < S; base += DN_SPAN) {
-            const uint32_t len = S - base < DN_SPAN ? S - base : DN_SPAN;
-            for (uint32_t i = threadIdx.x; i < len; i += 256) span[i] = 0;
-            __syncthreads();
-#pragma unroll
-            for (uint32_t j = 0; j < U; ++j) {
-                const uint64_t e = c0 + j * 256 + threadIdx.x;
-                const uint32_t o = (key[j] >> 5) - wa - base; // wraps for words below the window
-                if (e >= ea && e < eb && o < len) atomicOr(&span[o], 1u << (key[j] & 31u));
-            }
-            __syncthreads();
-            for (uint32_t i = threadIdx.x; i < len; i += 256) {
-                const uint32_t v = span[i];
-                if (!v) continue; // the bitmap starts zeroed
-                if (base + i == 0 || base + i == S - 1) atomicOr(&row[wa + base + i], v);
-                else row[wa + base + i] = v;
-            }
-            __syncthreads(); // the span is reused
-        }
-        // range check and class counts, once per entry
-#pragma unroll
+    for (uint64_t c0 = (uint64_t)blockIdx.x * DN_CHUNK; c0 < d.total; c0 += (uint64_t)gridDim.x * DN_CHUNK) {
+        const uint32_t len_c = (uint32_t)(d.total - c0 < DN_CHUNK ? d.total - c0 : DN_CHUNK);
+        const uint32_t* const src = d.idx + c0;
+        uint32_t key[U]; // entry r = j * 256 + threadIdx.x of the chunk
+    #pragma unroll
         for (uint32_t j = 0; j < U; ++j) {
-            const uint64_t e = c0 + j * 256 + threadIdx.x;
-            if (e < ea || e >= eb) continue;
-            if (key[j] >= d.M) report_error(kDevErrIndexRange);
-            else if (classes) atomicAdd(&hh[w * d.P + h0(key[j], hseed, d.div)], 1u);
+            const uint32_t r = j * 256 + threadIdx.x;
+            key[j] = src[r < len_c ? r : len_c - 1];
+        }
+        for (uint32_t w = 0; w < d.n; ++w) { // the workers whose lists meet the chunk (uniform)
+            const uint64_t ea = off[w] > c0 ? off[w] : c0, eb = off[w + 1] < c0 + len_c ? off[w + 1] : c0 + len_c;
+            if (ea >= eb) continue;
+            const uint32_t ra = (uint32_t)(ea - c0), rb = (uint32_t)(eb - c0); // the run: entries [ra, rb)
+            const uint32_t ka = src[ra], kb = src[rb - 1];
+            const uint32_t wa = ka >> 5, wb = kb >> 5;
+            uint32_t* const row = d.bm + (uint64_t)w * d.words;
+            uint32_t mine = 0; // bit j: entry j * 256 + threadIdx.x is in the run
+    #pragma unroll
+            for (uint32_t j = 0; j < U; ++j) mine |= (uint32_t)(j * 256 + threadIdx.x - ra < rb - ra) << j;
+            // the run's words in windows of DN_SPAN; a run that does not ascend,
+            // or spans more than DN_WINDOWS windows, goes one entry at a time
+            const bool staged = ka <= kb && kb < d.M && wb - wa < DN_WINDOWS * DN_SPAN;
+            const uint32_t S = staged ? wb - wa + 1 : 0u;
+            if (!staged) {
+    #pragma unroll
+                for (uint32_t j = 0; j < U; ++j)
+                    if (((mine >> j) & 1u) && key[j] < d.M) atomicOr(&row[key[j] >> 5], 1u << (key[j] & 31u));
+            }
+            for (uint32_t base = 0; base < S; base += DN_SPAN) {
+                const uint32_t len = S - base < DN_SPAN ? S - base : DN_SPAN;
+                for (uint32_t i = threadIdx.x; i < len; i += 256) span[i] = 0;
+                __syncthreads();
+    #pragma unroll
+                for (uint32_t j = 0; j < U; ++j) {
+                    const uint32_t o = (key[j] >> 5) - wa - base; // wraps for words below the window
+                    if (((mine >> j) & 1u) && o < len) atomicOr(&span[o], 1u << (key[j] & 31u));
+                }
+                __syncthreads();
+                for (uint32_t i0 = threadIdx.x; i0 < len; i0 += 4 * 256) { // four LDS reads in flight
+                    uint32_t v[4];
+    #pragma unroll
+                    for (uint32_t u = 0; u < 4; ++u) v[u] = i0 + u * 256 < len ? span[i0 + u * 256] : 0u;
+    #pragma unroll
+                    for (uint32_t u = 0; u < 4; ++u) {
+                        const uint32_t i = i0 + u * 256;
+                        if (!v[u]) continue; // the bitmap starts zeroed (and words past the window read 0)
+                        if (base + i == 0 || base + i == S - 1) atomicOr(&row[wa + base + i], v[u]);
+                        else row[wa + base + i] = v[u];
+                    }
+                }
+                __syncthreads(); // the span is reused
+            }
+            // range check and class counts, once per entry
+    #pragma unroll
+            for (uint32_t j = 0; j < U; ++j) {
+                if (!((mine >> j) & 1u)) continue;
+                if (key[j] >= d.M) report_error(kDevErrIndexRange);
+                else if (classes) atomicAdd(&hh[w * d.P + h0(key[j], hseed, d.div)], 1u);
+            }
         }
     }
     if (!classes) return;
