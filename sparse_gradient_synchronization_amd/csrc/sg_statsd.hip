@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
         const uint32_t len_c = (uint32_t)(d.total - c0 < DN_CHUNK ? d.total - c0 : DN_CHUNK);
         const uint32_t* const src = d.idx + c0;
         uint32_t key[U]; // entry r = j * 256 + threadIdx.x of the chunk
-    #pragma unroll
+#pragma unroll
         for (uint32_t j = 0; j < U; ++j) {
             const uint32_t r = j * 256 + threadIdx.x;
             key[j] = src[r < len_c ? r : len_c - 1];
@@ -106,14 +106,14 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
             const uint32_t wa = ka >> 5, wb = kb >> 5;
             uint32_t* const row = d.bm + (uint64_t)w * d.words;
             uint32_t mine = 0; // bit j: entry j * 256 + threadIdx.x is in the run
-    #pragma unroll
+#pragma unroll
             for (uint32_t j = 0; j < U; ++j) mine |= (uint32_t)(j * 256 + threadIdx.x - ra < rb - ra) << j;
             // the run's words in windows of DN_SPAN; a run that does not ascend,
             // or spans more than DN_WINDOWS windows, goes one entry at a time
             const bool staged = ka <= kb && kb < d.M && wb - wa < DN_WINDOWS * DN_SPAN;
             const uint32_t S = staged ? wb - wa + 1 : 0u;
             if (!staged) {
-    #pragma unroll
+#pragma unroll
                 for (uint32_t j = 0; j < U; ++j)
                     if (((mine >> j) & 1u) && key[j] < d.M) atomicOr(&row[key[j] >> 5], 1u << (key[j] & 31u));
             }
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
                 const uint32_t len = S - base < DN_SPAN ? S - base : DN_SPAN;
                 for (uint32_t i = threadIdx.x; i < len; i += 256) span[i] = 0;
                 __syncthreads();
-    #pragma unroll
+#pragma unroll
                 for (uint32_t j = 0; j < U; ++j) {
                     const uint32_t o = (key[j] >> 5) - wa - base; // wraps for words below the window
                     if (((mine >> j) & 1u) && o < len) atomicOr(&span[o], 1u << (key[j] & 31u));
@@ -129,9 +129,9 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
                 __syncthreads();
                 for (uint32_t i0 = threadIdx.x; i0 < len; i0 += 4 * 256) { // four LDS reads in flight
                     uint32_t v[4];
-    #pragma unroll
+#pragma unroll
                     for (uint32_t u = 0; u < 4; ++u) v[u] = i0 + u * 256 < len ? span[i0 + u * 256] : 0u;
-    #pragma unroll
+#pragma unroll
                     for (uint32_t u = 0; u < 4; ++u) {
                         const uint32_t i = i0 + u * 256;
                         if (!v[u]) continue; // the bitmap starts zeroed (and words past the window read 0)
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
                 __syncthreads(); // the span is reused
             }
             // range check and class counts, once per entry
-    #pragma unroll
+#pragma unroll
             for (uint32_t j = 0; j < U; ++j) {
                 if (!((mine >> j) & 1u)) continue;
                 if (key[j] >= d.M) report_error(kDevErrIndexRange);
