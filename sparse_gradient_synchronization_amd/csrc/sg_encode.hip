@@ -255,7 +255,9 @@ __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
 // aggregated key of the window (loaded in one round, its range known from the
 // cursors) sets the bit of its rank in an LDS copy of the window's bitmap
 // words; the words are then written out.
-__global__ __launch_bounds__(EN_THREADS) void enc_kernel(EncParams e)
+// six waves per SIMD (80 registers, a few spilled) keep more windows in
+// flight than the five the unconstrained allocation allows
+__global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void enc_kernel(EncParams e)
 {
     constexpr int KB = 4; // keys per thread per load round
     __shared__ uint32_t masks[2048];  // [NCW][P], NCW*P <= 2048
