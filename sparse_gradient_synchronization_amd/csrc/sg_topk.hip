@@ -785,65 +785,95 @@ __device__ __forceinline__ void write_chunk(uint32_t* oidx, void* oval, uint64_t
     eqr += popc64(meq);
 }
 
+// One load round of the ordered write: chunks b0 .. b0 + B - 1 of the wave's
+// chunk numbering (all B loads issued, then the chunks written in order).
+struct WriteWave {
+    uint32_t nch, cst, cnt, xg, xe, C, grp, T, need;
+    uint64_t g0;
+    uint32_t* oidx;
+    void* oval;
+};
+
+template <bool BF16, int B>
+__device__ __forceinline__ void write_round(const TopkParams& p, const WriteWave& v, uint32_t b0, uint32_t& cur_tile,
+                                            uint32_t& eqr, uint64_t& pos)
+{
+    const uint32_t lane = lane_id();
+    uint32_t vb[B], vi[B], tj[B], ch[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const uint32_t q = b0 + u;
+        const uint64_t has = ballot(v.nch > 0 && v.cst <= q);
+        tj[u] = has ? 63u - (uint32_t)__builtin_clzll(has) : 0u; // the last tile starting at or before chunk q
+        const uint32_t first = lane_value(v.cst, tj[u]);
+        const uint32_t cj = lane_value(v.cnt, tj[u]);
+        ch[u] = q < v.C ? (q - first) * SG_WAVE : cj; // entry offset of the chunk in its tile
+        const uint32_t i = ch[u] + lane;
+        const uint64_t sb = (v.g0 + tj[u]) * TK_TILE;
+        vb[u] = q < v.C && i < cj ? p.slot_val[sb + i] : 0u;
+        vi[u] = q < v.C && i < cj ? (uint32_t)p.slot_idx[sb + i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        if (b0 + u >= v.C) break;
+        if (tj[u] != cur_tile) {
+            cur_tile = tj[u];
+            eqr = lane_value(v.xe, cur_tile);
+            pos = (uint64_t)lane_value(v.xg, cur_tile) + (eqr < v.need ? eqr : v.need);
+        }
+        const uint32_t cj = lane_value(v.cnt, tj[u]);
+        const uint32_t tile0 = (v.grp * TK_GROUP + tj[u]) * TK_TILE; // first index of the tile
+        write_chunk<BF16>(v.oidx, v.oval, p.k, cj - ch[u], vb[u], tile0 + vi[u], v.T, v.need, pos, eqr);
+    }
+}
+
 // TK_WRITE_WAVES waves per group of 64 tiles; wave j writes the tiles j,
 // j + TK_WRITE_WAVES, ... of it, so the tiles of a dense row (one chunk per
 // 64 entries, up to 16 per tile) are spread over several waves.  The tiles'
 // output offsets come from the group prefix and a wave scan over the group.
-// The wave's slot chunks are numbered across its tiles and loaded 8 at a
-// time, so dense tiles cost no more load rounds than their size demands.
+// The wave's slot chunks are numbered across its tiles and loaded up to 8 at
+// a time (rounds of 2 or 4 when fewer remain, as for most waves), so dense
+// tiles cost no more load rounds than their size demands.
 template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(TopkParams p)
 {
-    constexpr int B = 8;                                // chunks per load round
     const uint64_t gq = (uint64_t)blockIdx.x * (TK_THREADS / SG_WAVE) + uniform(threadIdx.x / SG_WAVE);
     if (gq >= (uint64_t)p.n * p.NG * TK_WRITE_WAVES) return;
     const uint64_t gw = gq / TK_WRITE_WAVES;
     const uint32_t part = (uint32_t)(gq % TK_WRITE_WAVES);
     const uint32_t lane = lane_id();
-    const uint32_t w = (uint32_t)(gw / p.NG), grp = (uint32_t)(gw % p.NG);
-    const uint32_t T = p.st[w].T, need = p.st[w].need;
-    const uint64_t g0 = (uint64_t)w * p.NT + (uint64_t)grp * TK_GROUP;
-    const bool valid = grp * TK_GROUP + lane < p.NT;
-    const uint32_t cnt = valid ? p.tcnt[g0 + lane] : 0u;
-    const uint32_t gt = valid ? p.gtx[g0 + lane] : 0u, eq = valid ? p.eqx[g0 + lane] : 0u;
-    const uint32_t xg = p.ggt[gw] + wave_incl_scan(gt) - gt;
-    const uint32_t xe = p.geq[gw] + wave_incl_scan(eq) - eq;
+    const uint32_t w = (uint32_t)(gw / p.NG);
+    WriteWave v;
+    v.grp = (uint32_t)(gw % p.NG);
+    v.T = p.st[w].T;
+    v.need = p.st[w].need;
+    v.g0 = (uint64_t)w * p.NT + (uint64_t)v.grp * TK_GROUP;
+    const bool valid = v.grp * TK_GROUP + lane < p.NT;
+    v.cnt = valid ? p.tcnt[v.g0 + lane] : 0u;
+    const uint32_t gt = valid ? p.gtx[v.g0 + lane] : 0u, eq = valid ? p.eqx[v.g0 + lane] : 0u;
+    v.xg = p.ggt[gw] + wave_incl_scan(gt) - gt;
+    v.xe = p.geq[gw] + wave_incl_scan(eq) - eq;
     // chunks of this wave's tiles, numbered in tile order
     const bool mine = lane % TK_WRITE_WAVES == part;
-    const uint32_t nch = mine ? (cnt + SG_WAVE - 1) / SG_WAVE : 0u;
-    const uint32_t cinc = wave_incl_scan(nch);
-    const uint32_t cst = cinc - nch;
-    const uint32_t C = (uint32_t)__builtin_amdgcn_readlane((int)cinc, SG_WAVE - 1);
-    uint32_t* const oidx = p.out_idx + (uint64_t)w * p.k;
-    void* const oval = static_cast<char*>(p.out_val) + (uint64_t)w * p.k * (BF16 ? 2u : 4u);
+    v.nch = mine ? (v.cnt + SG_WAVE - 1) / SG_WAVE : 0u;
+    const uint32_t cinc = wave_incl_scan(v.nch);
+    v.cst = cinc - v.nch;
+    v.C = lane_value(cinc, SG_WAVE - 1);
+    v.oidx = p.out_idx + (uint64_t)w * p.k;
+    v.oval = static_cast<char*>(p.out_val) + (uint64_t)w * p.k * (BF16 ? 2u : 4u);
     uint32_t cur_tile = 0xffffffffu, eqr = 0;
     uint64_t pos = 0;
-    for (uint32_t b0 = 0; b0 < C; b0 += B) {
-        uint32_t vb[B], vi[B], tj[B], ch[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const uint32_t q = b0 + u;
-            const uint64_t has = ballot(nch > 0 && cst <= q);
-            tj[u] = has ? 63u - (uint32_t)__builtin_clzll(has) : 0u; // the last tile starting at or before chunk q
-            const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)cst, (int)tj[u]);
-            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
-            ch[u] = q < C ? (q - first) * SG_WAVE : cj; // entry offset of the chunk in its tile
-            const uint32_t i = ch[u] + lane;
-            const uint64_t sb = (g0 + tj[u]) * TK_TILE;
-            vb[u] = q < C && i < cj ? p.slot_val[sb + i] : 0u;
-            vi[u] = q < C && i < cj ? (uint32_t)p.slot_idx[sb + i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            if (b0 + u >= C) break;
-            if (tj[u] != cur_tile) {
-                cur_tile = tj[u];
-                eqr = (uint32_t)__builtin_amdgcn_readlane((int)xe, (int)cur_tile);
-                pos = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)xg, (int)cur_tile) + (eqr < need ? eqr : need);
-            }
-            const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)tj[u]);
-            const uint32_t tile0 = (grp * TK_GROUP + tj[u]) * TK_TILE; // first index of the tile
-            write_chunk<BF16>(oidx, oval, p.k, cj - ch[u], vb[u], tile0 + vi[u], T, need, pos, eqr);
+    for (uint32_t b0 = 0; b0 < v.C;) {
+        const uint32_t left = v.C - b0;
+        if (left <= 2) {
+            write_round<BF16, 2>(p, v, b0, cur_tile, eqr, pos);
+            b0 += 2;
+        } else if (left <= 4) {
+            write_round<BF16, 4>(p, v, b0, cur_tile, eqr, pos);
+            b0 += 4;
+        } else {
+            write_round<BF16, 8>(p, v, b0, cur_tile, eqr, pos);
+            b0 += 8;
         }
     }
 }
