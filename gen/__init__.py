@@ -6,8 +6,7 @@ arrays; neither calls the other).  Generation runs in C (``gen/csrc/sg_gen.c``)
 with counter-based SplitMix64 streams, so results do not depend on the thread
 count.
 
-Workloads (sizes from the method's own settings; the recipe is restated in
-DESIGN.md):
+Workloads (sizes from the method's own settings):
   1  n=4 workers, dense fp32 M=2^20, 1% nonzeros per worker drawn Zipf(1.1)
      without replacement, N(0,1) values; P=4.
   2  embedding rows: table 1,000,000 x 64 fp32, n=8, 4096 distinct Zipf(1.05)
