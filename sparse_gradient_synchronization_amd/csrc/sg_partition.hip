@@ -268,12 +268,24 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
     __syncthreads();
 
     // 4. write each partition's run: consecutive lanes, consecutive addresses
-    for (uint32_t i = threadIdx.x; i < len; i += PT_THREADS) {
-        uint32_t q = part_s[i];
-        uint32_t dst = dbase[q] + (i - lps[q]);
-        if (dst < p.total) {
-            p.out_idx[dst] = keys_s[i];
-            if (STAGE_VALS) static_cast<VT*>(p.out_val)[dst] = vals_s[i];
+    //    (four staged entries per thread read before any is written)
+    for (uint32_t i0 = threadIdx.x; i0 < len; i0 += 4 * PT_THREADS) {
+        uint32_t dst[4], kv[4];
+        VT vv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + u * PT_THREADS;
+            const uint32_t ic = i < len ? i : 0u;
+            const uint32_t q = part_s[ic];
+            dst[u] = i < len ? dbase[q] + (i - lps[q]) : 0xffffffffu;
+            kv[u] = keys_s[ic];
+            if (STAGE_VALS) vv[u] = vals_s[ic];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (dst[u] >= p.total) continue; // past the tile, or inconsistent offsets
+            p.out_idx[dst[u]] = kv[u];
+            if (STAGE_VALS) static_cast<VT*>(p.out_val)[dst[u]] = vv[u];
         }
     }
 
