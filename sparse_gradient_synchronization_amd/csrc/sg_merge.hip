@@ -304,7 +304,7 @@ __device__ __forceinline__ void pair_of(uint32_t pi, uint32_t n, uint32_t& a, ui
     b = x + rem;
 }
 
-struct WaveSmem {
+struct alignas(16) WaveSmem {
     uint32_t bits[MG_WORDS];         // presence bitmap of the window's keys; then keys by rank
     uint16_t wpre[MG_WORDS];         // distinct keys before a bitmap word; then first slot of a rank
     unsigned long long mask[MG_WCAP]; // workers holding a rank
@@ -585,8 +585,10 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
             }
 
             // merge the current window
-#pragma unroll
-            for (int j = 0; j < MG_WPL; ++j) sm.bits[lane * MG_WPL + j] = 0;
+            // a lane's words as one 16-byte access (consecutive lanes,
+            // consecutive addresses: no bank conflicts)
+            static_assert(MG_WPL == 4 && MG_WCAP / SG_WAVE == 4, "four words and four ranks per lane");
+            *reinterpret_cast<uint4*>(&sm.bits[lane * MG_WPL]) = make_uint4(0u, 0u, 0u, 0u);
             wave_sync();
             uint32_t off[MG_PER];
 #pragma unroll
@@ -606,20 +608,14 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
             // prefix popcounts over the bitmap -> ranks
             uint32_t U;
             {
-                uint32_t c[MG_WPL], sum = 0;
-#pragma unroll
-                for (int j = 0; j < MG_WPL; ++j) {
-                    c[j] = __popc(sm.bits[lane * MG_WPL + j]);
-                    sum += c[j];
-                }
+                const uint4 bw = *reinterpret_cast<const uint4*>(&sm.bits[lane * MG_WPL]);
+                const uint32_t c[4] = {(uint32_t)__popc(bw.x), (uint32_t)__popc(bw.y), (uint32_t)__popc(bw.z),
+                                       (uint32_t)__popc(bw.w)};
+                const uint32_t sum = c[0] + c[1] + c[2] + c[3];
                 const uint32_t inc = wave_incl_scan(sum);
                 U = (uint32_t)__builtin_amdgcn_readlane((int)inc, SG_WAVE - 1);
-                uint32_t ex = inc - sum;
-#pragma unroll
-                for (int j = 0; j < MG_WPL; ++j) {
-                    sm.wpre[lane * MG_WPL + j] = (uint16_t)ex;
-                    ex += c[j];
-                }
+                const uint32_t e0 = inc - sum, e1 = e0 + c[0], e2 = e1 + c[1], e3 = e2 + c[2];
+                *reinterpret_cast<uint2*>(&sm.wpre[lane * MG_WPL]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
             }
             wave_sync();
             uint32_t rk[MG_PER];
@@ -644,21 +640,20 @@ __global__ __launch_bounds__(MG_THREADS) void mg_merge_kernel(MergeParams p)
                 // first slot of each rank: exclusive prefix of the holder counts
                 {
                     constexpr int RPL = MG_WCAP / SG_WAVE;
+                    // the lane's four masks in two 16-byte reads (masks of ranks >= U are stale)
+                    const ulonglong2 m01 = *reinterpret_cast<const ulonglong2*>(&sm.mask[lane * RPL]);
+                    const ulonglong2 m23 = *reinterpret_cast<const ulonglong2*>(&sm.mask[lane * RPL + 2]);
+                    const uint64_t mv[4] = {m01.x, m01.y, m23.x, m23.y};
                     uint32_t c[RPL], sum = 0;
 #pragma unroll
                     for (int j = 0; j < RPL; ++j) {
-                        const uint32_t r = lane * RPL + j;
-                        c[j] = r < U ? popc64(sm.mask[r]) : 0u;
+                        c[j] = lane * RPL + j < U ? popc64(mv[j]) : 0u;
                         sum += c[j];
                     }
                     const uint32_t inc = wave_incl_scan(sum);
                     slots = (uint32_t)__builtin_amdgcn_readlane((int)inc, SG_WAVE - 1);
-                    uint32_t ex = inc - sum;
-#pragma unroll
-                    for (int j = 0; j < RPL; ++j) {
-                        sm.wpre[lane * RPL + j] = (uint16_t)ex;
-                        ex += c[j];
-                    }
+                    const uint32_t e0 = inc - sum, e1 = e0 + c[0], e2 = e1 + c[1], e3 = e2 + c[2];
+                    *reinterpret_cast<uint2*>(&sm.wpre[lane * RPL]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
                 }
                 wave_sync();
 #pragma unroll
