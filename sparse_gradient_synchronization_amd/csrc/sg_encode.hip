@@ -260,8 +260,11 @@ __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
 __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void enc_kernel(EncParams e)
 {
     constexpr int KB = 4; // keys per thread per load round
-    __shared__ uint32_t masks[2048];  // [NCW][P], NCW*P <= 2048
-    __shared__ uint16_t pre[2048];    // [NCW][P]
+    // partition-major [P][NCW] (NCW*P <= 2048): a thread's 8 chunks of one
+    // partition are 16-byte accesses, consecutive threads on consecutive
+    // addresses
+    __shared__ __align__(16) uint32_t masks[2048];
+    __shared__ __align__(16) uint16_t pre[2048];
     __shared__ uint32_t seg[EN_SEG_WORDS];
     __shared__ uint32_t segofs[257], kof[257], a_bits[256], b_bits[256];
     __shared__ uint64_t kbeg[256];
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
     // a) class masks of the window's chunks (NCW <= 128 < EN_THREADS); up to
     //    16 classes by splitting: each level splits every mask by one plane
     if (threadIdx.x < NCW) {
-        uint32_t* mrow = masks + threadIdx.x * P;
+        uint32_t* mrow = masks + threadIdx.x; // class k at mrow[k * NCW]
         if (L.nbits <= 4) {
             uint32_t m[16];
             m[0] = valid;
@@ -368,9 +371,9 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k)
-                if ((uint32_t)k < P) mrow[k] = m[k];
+                if ((uint32_t)k < P) mrow[k * NCW] = m[k];
         } else {
-            for (uint32_t p = 0; p < P; ++p) mrow[p] = class_mask(pl, L.nbits, p, valid);
+            for (uint32_t p = 0; p < P; ++p) mrow[p * NCW] = class_mask(pl, L.nbits, p, valid);
         }
     }
     __syncthreads();
@@ -382,10 +385,12 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         const uint32_t e0 = threadIdx.x * 8;
         uint32_t c[8], run = 0;
         const bool act = e0 < NCW * P;
-        const uint32_t p = act ? e0 / NCW : 0u, t0 = act ? e0 % NCW : 0u;
+        const uint4 ma = act ? *reinterpret_cast<const uint4*>(&masks[e0]) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 mb = act ? *reinterpret_cast<const uint4*>(&masks[e0 + 4]) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t mw[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w}; // 8 chunks of one partition
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            c[j] = act ? __popc(masks[(t0 + j) * P + p]) : 0u;
+            c[j] = __popc(mw[j]);
             run += c[j];
         }
         const uint32_t sg = NCW / 8; // threads per segment: a power of two, at most 16
@@ -400,12 +405,12 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         x = dpp_move<kDppRowShr8>(0u, inc);
         if (sg > 8 && (inrow & (sg - 1)) >= 8) inc += x;
         if (act) {
-            uint32_t ex = inc - run;
+            uint32_t ex[8];
+            ex[0] = inc - run;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pre[(t0 + j) * P + p] = (uint16_t)ex;
-                ex += c[j];
-            }
+            for (int j = 1; j < 8; ++j) ex[j] = ex[j - 1] + c[j - 1];
+            *reinterpret_cast<uint4*>(&pre[e0]) = make_uint4(ex[0] | (ex[1] << 16), ex[2] | (ex[3] << 16),
+                                                            ex[4] | (ex[5] << 16), ex[6] | (ex[7] << 16));
         }
     }
     __syncthreads();
@@ -422,9 +427,9 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
                 continue;
             }
             const uint32_t t = (uint32_t)(o >> 5), bit = (uint32_t)(o & 31u);
-            const uint32_t mk = masks[t * P + p];
+            const uint32_t mk = masks[p * NCW + t];
             if (!((mk >> bit) & 1u)) report_error(kDevErrPartition);
-            const uint32_t r = a_bits[p] + pre[t * P + p] + __popc(mk & ((1u << bit) - 1u));
+            const uint32_t r = a_bits[p] + pre[p * NCW + t] + __popc(mk & ((1u << bit) - 1u));
             const uint32_t lw = (r >> 5) - (a_bits[p] >> 5);
             if (lw < segofs[p + 1] - segofs[p]) atomicOr(&seg[segofs[p] + lw], 1u << (r & 31u));
         }
