@@ -121,8 +121,10 @@ constexpr int DC_WORDS = 512; // a window's bitmap words: at most W/32 + P <= 12
 
 __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
 {
-    __shared__ uint32_t masks[2048]; // [NCW][P]
-    __shared__ uint16_t pre[2048];   // [NCW][P]
+    // partition-major [P][NCW]: a thread's 8 chunks of one class are 16-byte
+    // accesses, consecutive threads on consecutive addresses
+    __shared__ __align__(16) uint32_t masks[2048];
+    __shared__ __align__(16) uint16_t pre[2048];
     __shared__ uint32_t segofs[257], a_bits[256], b_bits[256], cls_first[256];
     __shared__ uint32_t wex[DC_WORDS];
     __shared__ uint32_t scan_lds[DC_THREADS / SG_WAVE + 1];
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
     if (threadIdx.x == 0) segofs[P] = nseg;
     // class masks of the window's chunks by plane splitting (as in encode)
     if (threadIdx.x < NCW) {
-        uint32_t* mrow = masks + threadIdx.x * P;
+        uint32_t* mrow = masks + threadIdx.x; // class k at mrow[k * NCW]
         uint32_t m[16];
         if (L.nbits <= 4) {
             m[0] = valid;
@@ -169,12 +171,12 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k)
-                if ((uint32_t)k < P) mrow[k] = m[k];
+                if ((uint32_t)k < P) mrow[k * NCW] = m[k];
         } else {
             for (uint32_t p = 0; p < P; ++p) {
                 uint32_t v = valid;
                 for (uint32_t b = 0; b < L.nbits; ++b) v &= ((p >> b) & 1u) ? pl[b] : ~pl[b];
-                mrow[p] = v;
+                mrow[p * NCW] = v;
             }
         }
     }
@@ -189,10 +191,12 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
         const uint32_t e0 = threadIdx.x * 8;
         uint32_t c[8], run = 0;
         const bool act = e0 < NCW * P;
-        const uint32_t p = act ? e0 / NCW : 0u, t0 = act ? e0 % NCW : 0u;
+        const uint4 ma = act ? *reinterpret_cast<const uint4*>(&masks[e0]) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 mb = act ? *reinterpret_cast<const uint4*>(&masks[e0 + 4]) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t mw[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w}; // 8 chunks of one class
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            c[j] = act ? __popc(masks[(t0 + j) * P + p]) : 0u;
+            c[j] = __popc(mw[j]);
             run += c[j];
         }
         const uint32_t sg = NCW / 8;
@@ -207,12 +211,12 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
         x = dpp_move<kDppRowShr8>(0u, inc);
         if (sg > 8 && (inrow & (sg - 1)) >= 8) inc += x;
         if (act) {
-            uint32_t ex = inc - run;
+            uint32_t ex[8];
+            ex[0] = inc - run;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pre[(t0 + j) * P + p] = (uint16_t)ex;
-                ex += c[j];
-            }
+            for (int j = 1; j < 8; ++j) ex[j] = ex[j - 1] + c[j - 1];
+            *reinterpret_cast<uint4*>(&pre[e0]) = make_uint4(ex[0] | (ex[1] << 16), ex[2] | (ex[3] << 16),
+                                                            ex[4] | (ex[5] << 16), ex[6] | (ex[7] << 16));
         }
     }
     // the window's words (class-major), their set bits inside the ranges, and
@@ -272,14 +276,15 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
             const uint32_t bit = __ffs(v) - 1u;
             v &= v - 1u;
             const uint32_t m = qw * 32 + bit - a; // member of class p inside the window
-            uint32_t lo = 0, hi = NCW;            // chunk: last t with pre[t][p] <= m
+            const uint16_t* prow = pre + p * NCW;  // class p's prefixes over the chunks
+            uint32_t lo = 0, hi = NCW;            // chunk: last t with prow[t] <= m
             while (lo + 1 < hi) {
                 const uint32_t mid = (lo + hi) >> 1;
-                if (pre[mid * P + p] <= m) lo = mid;
+                if (prow[mid] <= m) lo = mid;
                 else hi = mid;
             }
-            const uint32_t mk = masks[lo * P + p];
-            const uint32_t k = m - pre[lo * P + p];
+            const uint32_t mk = masks[p * NCW + lo];
+            const uint32_t k = m - prow[lo];
             if (k >= (uint32_t)__popc(mk)) { // bit past the class: cannot happen with the class map's prefixes
                 report_error(kDevErrCmap);
                 ++o;
