@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void topk_gather_kernel(TopkParams p)
 }
 
 // Two order statistics of the sample (the band's ends) by MSD radix select in
-// LDS: 11-bit digits, both ranks at once, one block per worker.
+// LDS: 11-bit digits, both ranks at once, one block per worker.  Two digits
+// suffice: the band only has to hold the k-th key, so its low end is the
+// first order statistic with the undecided low bits cleared and its high end
+// the second with them set (a band wider by at most 2^10 units of the key).
 __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
 {
     __shared__ uint32_t s[TK_SAMPLES];
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     uint32_t prefix[2] = {0u, 0u};
     uint32_t top = p.bf16 ? 15u : 31u;
     __syncthreads();
-    while (top > 0) {
+    for (int pass = 0; pass < 2 && top > 0; ++pass) {
         const uint32_t shift = top > (uint32_t)TK_DIGIT_BITS ? top - TK_DIGIT_BITS : 0u;
         const uint32_t width = top - shift;
         for (uint32_t i = threadIdx.x; i < 2 * TK_BINS; i += 1024) (&hist[0][0])[i] = 0;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
         // is in fact 0 the band misses and the worker is filtered again with
         // the full band, which stays exact.
         st.lo = none_lo ? 0u : (prefix[0] == 0u ? 1u : prefix[0]);
-        st.hi = none_hi ? p.keymax : prefix[1];
+        st.hi = none_hi ? p.keymax : (prefix[1] | ((1u << top) - 1u)); // top <= 9: the bits not decided
         st.redo = 0;
         st.sure = st.cand = 0;
         st.R = 0;
