@@ -489,10 +489,21 @@ __global__ __launch_bounds__(1024) void topk_totals_kernel(TopkParams p, int sec
     __shared__ uint32_t red[2][16];
     const uint32_t w = blockIdx.x;
     uint32_t sure = 0, cand = 0;
-    for (uint32_t t = threadIdx.x; t < p.NT; t += 1024) {
-        uint32_t a = p.tcnt[(uint64_t)w * p.NT + t], c = p.ccnt[(uint64_t)w * p.NT + t];
-        sure += a - c;
-        cand += c;
+    const uint32_t* const tc = p.tcnt + (uint64_t)w * p.NT;
+    const uint32_t* const cc = p.ccnt + (uint64_t)w * p.NT;
+    for (uint32_t t0 = threadIdx.x; t0 < p.NT; t0 += 8 * 1024) { // eight tiles' loads in flight
+        uint32_t a[8], c[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            const uint32_t t = t0 + u * 1024;
+            a[u] = t < p.NT ? tc[t] : 0u;
+            c[u] = t < p.NT ? cc[t] : 0u;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            sure += a[u] - c[u];
+            cand += c[u];
+        }
     }
     sure = wave_sum(sure);
     cand = wave_sum(cand);
