@@ -217,7 +217,14 @@ __global__ __launch_bounds__(1024) void dgc_count_kernel(DgcParams p)
     __shared__ uint64_t red[1024 / SG_WAVE];
     const uint32_t w = blockIdx.x;
     uint64_t s = 0;
-    for (uint32_t t = threadIdx.x; t < p.t.NT; t += 1024) s += p.t.tcnt[(uint64_t)w * p.t.NT + t];
+    const uint32_t* const tc = p.t.tcnt + (uint64_t)w * p.t.NT;
+    for (uint32_t t0 = threadIdx.x; t0 < p.t.NT; t0 += 8 * 1024) { // eight tiles' loads in flight
+        uint32_t a[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) a[u] = t0 + u * 1024 < p.t.NT ? tc[t0 + u * 1024] : 0u;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) s += a[u];
+    }
 #pragma unroll
     for (int o = SG_WAVE / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, SG_WAVE);
     if (lane_id() == 0) red[threadIdx.x / SG_WAVE] = s;

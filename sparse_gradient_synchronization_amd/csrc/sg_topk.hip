@@ -110,7 +110,18 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     const uint32_t w = blockIdx.x;
     const uint64_t M = p.M;
     const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
-    for (uint32_t i = threadIdx.x; i < S; i += 1024) s[i] = p.samples[(uint64_t)w * TK_SAMPLES + i];
+    {
+        constexpr uint32_t SPT = TK_SAMPLES / 1024; // every load in flight before the first store
+        uint32_t v[SPT];
+#pragma unroll
+        for (uint32_t j = 0; j < SPT; ++j) {
+            const uint32_t i = j * 1024 + threadIdx.x;
+            v[j] = p.samples[(uint64_t)w * TK_SAMPLES + (i < S ? i : 0u)];
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < SPT; ++j)
+            if (j * 1024 + threadIdx.x < S) s[j * 1024 + threadIdx.x] = v[j];
+    }
     // the worker's histogram row of the selection passes starts at zero
     for (uint32_t i = threadIdx.x; i < TK_BINS; i += 1024) p.hist[(uint64_t)w * TK_BINS + i] = 0;
     // target ranks, 1-based from the smallest; 0 = not needed
