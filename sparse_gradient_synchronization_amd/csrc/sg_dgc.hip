@@ -50,10 +50,13 @@ struct DgcParams {
 // when S == M), key of a = resid + grad there.
 __global__ __launch_bounds__(256) void dgc_sample_kernel(DgcParams p)
 {
+    const bool fits = p.M <= ~0ull / (2 * p.S); // (2j + 1) M fits 64 bits
     for (uint64_t q = (uint64_t)blockIdx.x * 256 + threadIdx.x; q < p.Ns; q += (uint64_t)gridDim.x * 256) {
         const uint32_t w = (uint32_t)(q / p.S);
         const uint64_t j = q % p.S;
-        const uint64_t pos = p.S >= p.M ? j : (uint64_t)(((unsigned __int128)(2 * j + 1) * p.M) / (2 * p.S));
+        const uint64_t pos = p.S >= p.M ? j
+                             : fits   ? ((2 * j + 1) * p.M) / (2 * p.S)
+                                      : (uint64_t)(((unsigned __int128)(2 * j + 1) * p.M) / (2 * p.S));
         const uint64_t e = (uint64_t)w * p.M + pos;
         const float a = p.resid[e] + p.grad[e];
         p.samples[q] = __float_as_uint(a) & 0x7fffffffu;

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void topk_gather_kernel(TopkParams p)
     const uint32_t S = M < (uint64_t)TK_SAMPLES ? (uint32_t)M : (uint32_t)TK_SAMPLES;
     const uint32_t i = blockIdx.x * 256 + threadIdx.x;
     if (i >= S) return;
-    const uint64_t pos = (S == M) ? i : (uint64_t)(((unsigned __int128)(2ull * i + 1) * M) / (2ull * S));
+    // (2i + 1) M < 2^15 * 2^32: the product fits 64 bits
+    const uint64_t pos = (S == M) ? i : ((2ull * i + 1) * M) / (2ull * S);
     p.samples[(uint64_t)w * TK_SAMPLES + i] = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
 }
 
