@@ -310,20 +310,22 @@ def copy_calibration(torch, nbytes):
 
 def concurrent_step(stages, torch):
     """The step with its independent rows overlapped on their own streams
-    (default priority): the statistics once their COO input exists (after
-    top-k, when the step has it), the skip reduce-scatter once the aggregate
-    is queued (it then overlaps the encode and the statistics, which leave
-    HBM bandwidth free; started earlier it competes with the top-k filter
-    for bandwidth and delays top-k's small kernels); everything else runs in
-    order on the current stream.  The streams join at the end of the step,
-    and the host half of the statistics runs last.  None when the step has
-    nothing to overlap."""
+    (default priority): the statistics and the skip reduce-scatter once the
+    aggregate is queued (they then overlap the encode and each other: the
+    statistics are latency-bound, the reduce-scatter bandwidth-bound; the
+    reduce-scatter started earlier competes with the top-k filter for
+    bandwidth and delays top-k's small kernels, and the statistics started
+    after top-k slow the partition and the merge a little more than they
+    gain); everything else runs in order on the current stream.  The streams
+    join at the end of the step, and the host half of the statistics runs
+    last.  A workload without an aggregate starts them with the step.  None
+    when the step has nothing to overlap."""
     fns = dict(stages)
     side_names = [nm for nm in ("skip_reduce_scatter", "stats") if nm in fns]
     if not side_names or len(fns) - len(side_names) - ("stats_collect" in fns) < 1:
         return None
     side = {nm: torch.cuda.Stream() for nm in side_names}
-    after = {"stats": "topk_to_coo", "skip_reduce_scatter": "aggregate"}
+    after = {"stats": "aggregate", "skip_reduce_scatter": "aggregate"}
     evs = {nm: torch.cuda.Event() for nm in side_names}
 
     def launch(nm):
@@ -719,8 +721,9 @@ def main():
         "data": "synthetic (seeded generators, shapes and distributions of the workload)",
         "config": cfg,
         "stages_ms": stages_out,
-        "overlap": ("skip reduce-scatter and statistics on their own streams, overlapped with the other stages; "
-                    "stages_ms from a sequential pass") if overlapped else None,
+        "overlap": ("skip reduce-scatter and statistics on their own streams once the aggregate is queued, "
+                    "overlapped with the encode and each other; stages_ms from a sequential pass")
+        if overlapped else None,
         "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
