@@ -216,35 +216,48 @@ __global__ __launch_bounds__(512) void mg_bnd_kernel(MergeParams p)
 // the sum over its runs of bnd[b + 1] - bnd[b]; the loads of 8 runs are
 // issued together (rows past the last run read run 0's row and are not
 // counted).  The count only orders the work, so a row is not checked here
-// against its run's length (the merge does that).
+// against its run's length (the merge does that).  Appends to the list are
+// gathered per block (one device-scope atomic per block and round: a single
+// counter hit by every wave of the chip serializes).
 __global__ __launch_bounds__(256) void mg_heavy_kernel(MergeParams p)
 {
+    __shared__ uint32_t wcnt[256 / SG_WAVE], wofs[256 / SG_WAVE + 1];
     const uint32_t T = p.G * p.NT;
-    for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
-    const uint32_t g = t / p.NT, b = t % p.NT;
-    uint32_t E = 0;
-    const uint32_t* rows = p.bnd + (uint64_t)g * p.n * (p.NT + 1) + b;
-    for (uint32_t w0 = 0; w0 < p.n; w0 += 8) {
-        uint32_t x[8], y[8];
+    const uint32_t wid = uniform(threadIdx.x / SG_WAVE);
+    for (uint32_t t0 = blockIdx.x * 256; t0 < T; t0 += gridDim.x * 256) { // uniform per block
+        const uint32_t t = t0 + threadIdx.x;
+        const bool valid = t < T;
+        const uint32_t tc = valid ? t : T - 1;
+        const uint32_t g = tc / p.NT, b = tc % p.NT;
+        uint32_t E = 0;
+        const uint32_t* rows = p.bnd + (uint64_t)g * p.n * (p.NT + 1) + b;
+        for (uint32_t w0 = 0; w0 < p.n; w0 += 8) {
+            uint32_t x[8], y[8];
 #pragma unroll
-        for (uint32_t u = 0; u < 8; ++u) {
-            const uint32_t* row = rows + (uint64_t)(w0 + u < p.n ? w0 + u : 0u) * (p.NT + 1);
-            x[u] = row[0];
-            y[u] = row[1];
+            for (uint32_t u = 0; u < 8; ++u) {
+                const uint32_t* row = rows + (uint64_t)(w0 + u < p.n ? w0 + u : 0u) * (p.NT + 1);
+                x[u] = row[0];
+                y[u] = row[1];
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u)
+                if (w0 + u < p.n && y[u] > x[u]) E += y[u] - x[u];
         }
-#pragma unroll
-        for (uint32_t u = 0; u < 8; ++u)
-            if (w0 + u < p.n && y[u] > x[u]) E += y[u] - x[u];
-    }
-    // one list append per wave: the heavy lanes take consecutive slots
-    const bool hv = E > (uint32_t)MG_HEAVY;
-    const uint64_t m = ballot(hv);
-    if (m) {
-        uint32_t base = 0;
-        if (count_below(ballot(true)) == 0) base = atomicAdd(&p.queue[0], (uint32_t)popc64(m)); // first active lane
-        base = uniform(base);
-        if (hv) p.heavy[base + count_below(m)] = t;
-    }
+        const bool hv = valid && E > (uint32_t)MG_HEAVY;
+        const uint64_t m = ballot(hv);
+        if (lane_id() == 0) wcnt[wid] = (uint32_t)popc64(m);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t sum = 0;
+            for (uint32_t i = 0; i < 256 / SG_WAVE; ++i) {
+                wofs[i] = sum;
+                sum += wcnt[i];
+            }
+            wofs[256 / SG_WAVE] = sum ? atomicAdd(&p.queue[0], sum) : 0u;
+        }
+        __syncthreads();
+        if (hv) p.heavy[wofs[256 / SG_WAVE] + wofs[wid] + count_below(m)] = t;
+        __syncthreads(); // wcnt and wofs are reused
     }
 }
 
