@@ -2,10 +2,9 @@
 """Benchmark of the sparse gradient synchronization hot path on one MI355X.
 
 One step = one pass of every stage of the path over one batch of synthetic
-input already resident in HBM:
-
-  default workload "dgc-top5": n=8 workers, dense fp32 gradients of
-  4096 x 11008 each (per-row lognormal scale, 0.7 inter-worker correlation),
+input already resident in HBM.  The headline workload "dgc-top5": n=8
+workers, dense fp32 gradients of 4096 x 11008 each (per-row lognormal scale,
+0.7 inter-worker correlation),
     A1 top-5% per worker into COO            sg_topk_to_coo
     A2 hash partition into 8                  sg_hash_partition
     A3 per-partition union-sum                sg_aggregate
@@ -14,15 +13,26 @@ input already resident in HBM:
     A5 the dense counterpart on the same gradients: ring reduce-scatter
        arithmetic, 256 KiB slices skipped w.p. 0.5, DropReduce rescale
                                               sg_skip_reduce_scatter
-    A6 the statistics evaluated on the host   sg_stats_collect (once the
-       copy of the counts is done; A5 still runs on the GPU meanwhile)
+    A6 the statistics evaluated on the host   sg_stats_collect
 
-Metric: aggregated input nonzeros per second (the n*k COO entries that enter
-aggregation, divided by the step time), plus the HBM roofline of the step's
-dominant kernel timed with HIP events on the stream it runs on.
+The other workloads run the stages that apply to them, each measured the
+same way and reported under "configs":
+    cfg1  n=4, dense M=2^20 with 1% Zipf(1.1) nonzeros: A1 (k = nnz), A2-A4, A6
+    cfg2  embedding rows 1,000,000 x 64, n=8, 4096 Zipf(1.05) rows: A2-A4, A6
+    cfg4  n=16, M=2^28, 1% per worker, 60% in the first M/8: A2-A4, A6
+    cfg5  n=8 buffers of 2^26 fp32, 256 KiB slices, p=0.5: A5
 
-Other workloads (--workload cfg1|cfg2|cfg4|cfg5) time the stages that apply
-to them; they are reported in the same format.
+Metric: aggregated input nonzeros per second (the COO entries that enter
+aggregation, divided by the step time; elements per second for cfg5), plus
+the HBM roofline of the step's dominant kernel timed with HIP events on the
+stream it runs on, and every stage's and kernel's fraction of HBM peak from
+its algorithmic bytes.
+
+After the timed steps the outputs of the last step are compared with the
+oracle's outputs for the same inputs (bit-exact indices, offsets, bitmaps,
+counts and statistics; fp32 sums within 1e-6 * sum|x| + 1e-30), and the
+oracle's step is timed single-threaded on the host ("cpu_baseline").  A
+parity failure is reported in the line and makes the exit status 3.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -36,6 +46,7 @@ import time
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 
 METRIC = "aggregated input nonzeros/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+WORKLOADS = ("dgc-top5", "cfg1", "cfg2", "cfg4", "cfg5")
 
 
 def log(*a):
@@ -59,6 +70,13 @@ class HipEvents:
         assert self.hip.hipEventElapsedTime(C.byref(ms), self.start, self.stop) == 0
         return float(ms.value)
 
+    def __del__(self):
+        try:
+            self.hip.hipEventDestroy(self.start)
+            self.hip.hipEventDestroy(self.stop)
+        except Exception:
+            pass
+
 
 def build_workload(name, torch, sg, gen):
     """Inputs on the GPU, preallocated outputs/workspaces, and the stage list."""
@@ -67,6 +85,8 @@ def build_workload(name, torch, sg, gen):
     u32 = lambda a: torch.from_numpy(a.view("int32")).to(dev)  # noqa: E731
     u64 = lambda a: torch.from_numpy(a.view("int64")).to(dev)  # noqa: E731
     W = {"name": name}
+    out = {}  # device outputs of the last step, for the parity check
+    W["out"] = out
     stages = []
     nbytes = {}
 
@@ -83,6 +103,7 @@ def build_workload(name, torch, sg, gen):
 
     if name in ("dgc-top5", "cfg1"):
         c = gen.config3() if name == "dgc-top5" else gen.config1()
+        W["host"] = c
         n, M, k, P, seed = c["n"], c["M"], c["k"], c["P"], c["seed"]
         dense = torch.from_numpy(c["dense"]).to(dev)
         W.update(n=n, M=M, k=k, P=P)
@@ -99,8 +120,12 @@ def build_workload(name, torch, sg, gen):
         stages.append(("topk_to_coo", topk))
         nbytes["topk_to_coo"] = n * M * 4 + n * k * 8
         src_idx, src_val, D = idx, val, 1
+        out.update(topk_idx=idx, topk_val=val)
+        W["in_off_host"] = in_off_np
     elif name in ("cfg2", "cfg4"):
         c = gen.config2() if name == "cfg2" else gen.config4()
+        W["host"] = c
+        W["in_off_host"] = c["in_off"]
         n, M, P, seed = c["n"], c["M"], c["P"], c["seed"]
         D = c.get("D", 1)
         src_idx = u32(c["idx"])
@@ -110,6 +135,7 @@ def build_workload(name, torch, sg, gen):
         W.update(n=n, M=M, P=P, D=D, total=total)
     elif name == "cfg5":
         c = gen.config5()
+        W["host"] = c
         n, M = c["n"], c["M"]
         W.update(n=n, M=M, slice_bytes=c["slice_elems"] * 4, p_skip=c["p"])
         total = None
@@ -171,6 +197,9 @@ def build_workload(name, torch, sg, gen):
 
         stages += [("hash_partition", part), ("aggregate", agg), ("encode", enc), ("stats", stats)]
         W["stats_collect"] = stats_collect
+        W.update(seed=seed)
+        out.update(pidx=pidx, pval=pval, part_off=part_off, agg_idx=agg_idx, agg_val=agg_val, agg_off=agg_off,
+                   bitmap=bitmap, word_off=word_off)
 
         # the Pull side after the step (timed on its own, not part of the step)
         dec_idx = torch.empty(total, dtype=torch.int32, device=dev)
@@ -218,6 +247,8 @@ def build_workload(name, torch, sg, gen):
                                          vp(rs_cnt), stream()), "sg_skip_reduce_scatter")
         stages.append(("skip_reduce_scatter", rs))
         W["rs_cnt"] = rs_cnt
+        out.update(rs_out=rs_out, rs_cnt=rs_cnt)
+        W["rs_seed"] = rs_seed
         W["rs_geom"] = (n, M, slice_bytes // 4, S)
         W.update(slice_bytes=slice_bytes, p_skip=0.5)
         if name == "cfg5":
@@ -390,48 +421,6 @@ def cold_steps(torch, step, steps, flush_bytes=1 << 30):
     return sorted(ms)[len(ms) // 2]
 
 
-def algorithmic_bytes(W, stage):
-    """Algorithmic bytes per launch of the probed kernel of a stage."""
-    if stage == "topk_to_coo":
-        return W["n"] * W["M"] * 4  # the dense read; slots are workspace
-    if stage == "hash_partition":
-        return W["nbytes"]["hash_partition"]
-    if stage == "aggregate":
-        return W["bytes_agg"](int(W["agg_off"][-1].item()))
-    if stage == "encode":
-        return W["bytes_enc"](int(W["agg_off"][-1].item()), int(W["word_off"][-1].item()))
-    if stage == "skip_reduce_scatter":
-        return rs_bytes(W)
-    if stage == "decode":  # the bitmap words read, the indices written
-        return int(W["word_off"][-1].item()) * 4 + int(W["agg_off"][-1].item()) * 4
-    if stage == "scatter_dense":  # the scatter pass: the aggregate read, its values written in place
-        U = int(W["agg_off"][-1].item())
-        return U * (4 + 8 * W.get("D", 1))
-    raise KeyError(stage)
-
-
-def cpu_baseline(name, gen):
-    """The oracle, single-threaded, on one full step of the same workload."""
-    import numpy as np
-    import oracle
-    if name != "dgc-top5":
-        return None
-    c = gen.config3()
-    n, M, k, P, seed = c["n"], c["M"], c["k"], c["P"], c["seed"]
-    t0 = time.perf_counter()
-    idx, val = oracle.topk_to_coo(c["dense"], k)
-    in_off = np.arange(n + 1, dtype=np.uint64) * np.uint64(k)
-    oi, ov, po = oracle.hash_partition(idx.reshape(-1), val.reshape(-1), in_off, P, seed)
-    ai, av, aa, ao = oracle.aggregate(oi, ov, po, M)
-    oracle.encode(ai, ao, M, seed)
-    oracle.stats(idx.reshape(-1), in_off, M, P, hashed=True, seed=seed)
-    oracle.skip_reduce_scatter(c["dense"], (256 * 1024) // 4, 0.5, 5, mode=1)
-    t = time.perf_counter() - t0
-    return {"value": n * k / t, "unit": "nonzeros/s", "cores": 1, "kind": "oracle",
-            "sample": "one full step of the workload (all six stages, full size), single-threaded C oracle",
-            "seconds": round(t, 3)}
-
-
 def pull_side(W, L, torch, steps):
     """Decode of the step's hash bitmap and the scatter of its aggregate into
     a dense tensor, each timed alone (whole call with torch events, probed
@@ -595,33 +584,161 @@ def alg1_study(L, torch, sg, steps):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dgc-top5", choices=["dgc-top5", "cfg1", "cfg2", "cfg4", "cfg5"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", default=None, help="stage whose kernel is timed for the roofline (default: slowest)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="first run a plain device copy of BYTES (for scaling HBM counters under rocprofv3 --pmc)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the n workers are simulated resident on it); "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def union_size(W):
+    return int(W["agg_off"][-1].item())
 
-    import torch
-    import gen
-    import sparse_gradient_synchronization_amd as sg
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        copy_calibration(torch, args.copy_calibration)
-    log("building workload", args.workload)
-    W = build_workload(args.workload, torch, sg, gen)
+def stage_bytes(W, stage):
+    """Algorithmic bytes of a whole stage call: what the method itself must
+    read and write (inputs once, outputs once; workspaces excluded)."""
+    n = W.get("n")
+    D = W.get("D", 1)
+    if stage == "topk_to_coo":
+        return n * W["M"] * 4 + n * W["k"] * 8
+    if stage == "hash_partition":
+        return W["nbytes"]["hash_partition"]
+    if stage == "aggregate":
+        return W["bytes_agg"](union_size(W))
+    if stage == "encode":
+        return W["bytes_enc"](union_size(W), int(W["word_off"][-1].item()))
+    if stage == "skip_reduce_scatter":
+        return rs_bytes(W)
+    if stage == "stats":  # report-only: the index lists read once
+        return W["nnz"] * 4
+    return None
+
+
+def algorithmic_bytes(W, stage):
+    """Algorithmic bytes per launch of the primary probed kernel of a stage
+    (and of the Pull-side kernels)."""
+    if stage == "topk_to_coo":
+        return W["n"] * W["M"] * 4  # the dense read; slots are workspace
+    if stage in ("hash_partition", "aggregate", "encode", "skip_reduce_scatter"):
+        return stage_bytes(W, stage)
+    if stage == "decode":  # the bitmap words read, the indices written
+        return int(W["word_off"][-1].item()) * 4 + union_size(W) * 4
+    if stage == "scatter_dense":  # the scatter pass: the aggregate read, its values written in place
+        return union_size(W) * (4 + 8 * W.get("D", 1))
+    raise KeyError(stage)
+
+
+# every probed hot-path kernel: (stage, probe id, kernel, algorithmic bytes per launch)
+KERNELS = [
+    ("topk_to_coo", 1, "topk_filter_pipe_kernel", lambda W: W["n"] * W["M"] * 4),
+    ("topk_to_coo", 8, "topk_write_kernel", lambda W: 2 * W["n"] * W["k"] * 8),
+    ("hash_partition", 7, "part_hist_kernel", lambda W: W["nnz"] * 4),
+    ("hash_partition", 2, "part_scatter_kernel", lambda W: W["nbytes"]["hash_partition"]),
+    ("aggregate", 6, "mg_bnd_kernel", lambda W: W["nnz"] * 4),
+    ("aggregate", 3, PROBES["aggregate"][1], lambda W: stage_bytes(W, "aggregate")),
+    ("encode", 4, "enc_kernel", lambda W: stage_bytes(W, "encode")),
+    ("skip_reduce_scatter", 5, "skip_rs_kernel", lambda W: rs_bytes(W)),
+]
+
+
+def host_cpu():
+    """The host's CPU model and core counts (the oracle baseline's machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def oracle_step(name, W):
+    """The oracle on one full step of the workload (every stage the GPU step
+    runs, full size, single-threaded C), on the same host inputs.  Returns its
+    outputs and its wall time."""
+    import numpy as np
+    import oracle
+    c = W["host"]
+    ref = {}
+    t0 = time.perf_counter()
+    if name in ("dgc-top5", "cfg1"):
+        idx, val = oracle.topk_to_coo(c["dense"], W["k"])
+        ref["topk"] = (idx, val)
+        src_idx, src_val = idx.reshape(-1), val.reshape(-1)
+    elif name in ("cfg2", "cfg4"):
+        src_idx, src_val = c["idx"], c["val"]
+    if name != "cfg5":
+        M, P, seed, in_off = W["M"], W["P"], W["seed"], W["in_off_host"]
+        oi, ov, po = oracle.hash_partition(src_idx, src_val, in_off, P, seed)
+        ai, av, aa, ao = oracle.aggregate(oi, ov, po, M)
+        bm, wo = oracle.encode(ai, ao, M, seed)
+        st = oracle.stats(src_idx, in_off, M, P, hashed=True, seed=seed)
+        ref.update(part=(oi, ov, po), agg=(ai, av, aa, ao), enc=(bm, wo), stats=st)
+    if name in ("dgc-top5", "cfg5"):
+        bufs = c["dense"] if name == "dgc-top5" else c["bufs"]
+        ref["rs"] = oracle.skip_reduce_scatter(bufs, W["slice_bytes"] // 4, W["p_skip"], W["rs_seed"], mode=1)
+    return ref, time.perf_counter() - t0
+
+
+def compare_outputs(W, ref):
+    """The GPU step's outputs against the oracle's: bit-exact where the result
+    is integer or a bit copy, within |d| <= 1e-6 * sum|x| + 1e-30 for fp32
+    sums.  Returns {check: bool} plus the largest error / bound ratio."""
+    import numpy as np
+    o = W["out"]
+    ok = {}
+    worst = 0.0
+
+    def u32(t):
+        return t.cpu().numpy().view(np.uint32)
+
+    def within(got, exact, abs_sum):
+        nonlocal worst
+        got = np.asarray(got, dtype=np.float64).reshape(-1)
+        bound = 1e-6 * np.asarray(abs_sum, dtype=np.float64).reshape(-1) + 1e-30
+        r = np.abs(got - np.asarray(exact).reshape(-1)) / bound
+        worst = max(worst, float(r.max()) if r.size else 0.0)
+        return bool(np.all(r <= 1.0))
+
+    if "topk" in ref:
+        ri, rv = ref["topk"]
+        ok["topk_indices"] = bool(np.array_equal(u32(o["topk_idx"]).reshape(-1), ri.reshape(-1)))
+        ok["topk_values"] = bool(np.array_equal(u32(o["topk_val"]).reshape(-1), rv.reshape(-1).view(np.uint32)))
+    if "part" in ref:
+        oi, ov, po = ref["part"]
+        ok["partition_offsets"] = bool(np.array_equal(o["part_off"].cpu().numpy().view(np.uint64), po))
+        ok["partition_indices"] = bool(np.array_equal(u32(o["pidx"]), oi))
+        ok["partition_values"] = bool(np.array_equal(u32(o["pval"]).reshape(-1), ov.reshape(-1).view(np.uint32)))
+        ai, av, aa, ao = ref["agg"]
+        gao = o["agg_off"].cpu().numpy().view(np.uint64)
+        ok["aggregate_offsets"] = bool(np.array_equal(gao, ao))
+        u = int(ao[-1])
+        ok["aggregate_indices"] = bool(np.array_equal(u32(o["agg_idx"])[:u], ai))
+        ok["aggregate_sums"] = within(o["agg_val"].cpu().numpy()[:u], av, aa)
+        bm, wo = ref["enc"]
+        ok["encode_word_offsets"] = bool(np.array_equal(o["word_off"].cpu().numpy().view(np.uint64), wo))
+        ok["encode_bitmap"] = bool(np.array_equal(u32(o["bitmap"])[: int(wo[-1])], bm))
+        st, got = ref["stats"], W["stats_arrays"]
+        so = W["stats_out"]
+        same = all(np.array_equal(got[k], np.asarray(st[k]).reshape(-1)) for k in got)
+        for k in ("union_size", "sum_nnz", "max_nnz", "overlap_mean", "overlap_min", "overlap_max", "gamma_n",
+                  "push_imbalance", "pull_imbalance"):
+            same = same and getattr(so, k) == st[k]
+        ok["stats"] = bool(same)
+    if "rs" in ref:
+        out, oabs, cnt = ref["rs"]
+        ok["skip_rs_counts"] = bool(np.array_equal(o["rs_cnt"].cpu().numpy(), cnt))
+        ok["skip_rs_sums"] = within(o["rs_out"].cpu().numpy(), out, oabs)
+    return ok, worst
+
+
+def measure_workload(name, args, torch, sg, gen, headline):
+    """Build one workload, time its step, time every probed kernel, compare
+    the outputs with the oracle and time the oracle.  Returns the workload's
+    record (the JSON line's fields for the headline workload)."""
+    log("building workload", name)
+    W = build_workload(name, torch, sg, gen)
     stages = W["stages"]
     L = sg.lib()
     steps = args.steps
@@ -640,21 +757,29 @@ def main():
     overlapped = concurrent_step(stages, torch)
     run_step = overlapped or step
 
-    # warmup; then time each stage's probed kernel once to find the dominant one
     for _ in range(max(args.warmup, 1)):
         run_step()
     torch.cuda.synchronize()
-    probe_ms = {}
-    for nm, _ in stages:
-        if nm not in PROBES:
+
+    # every probed kernel of the workload, each timed over `steps` sequential
+    # steps with HIP events the library records around it
+    kernels = {}
+    have = {nm for nm, _ in stages}
+    for stg, pid, kname, fbytes in KERNELS:
+        if stg not in have:
             continue
-        L.sg_probe_set(PROBES[nm][0], evs[0].start, evs[0].stop)
-        step()
+        for s in range(steps):
+            L.sg_probe_set(pid, evs[s].start, evs[s].stop)
+            step()
         torch.cuda.synchronize()
-        probe_ms[nm] = evs[0].elapsed_ms()
-    L.sg_probe_set(0, None, None)
-    dom = args.probe or max(probe_ms, key=probe_ms.get)
-    log("probe times (ms):", {k: round(v, 4) for k, v in probe_ms.items()}, "dominant:", dom)
+        L.sg_probe_set(0, None, None)
+        kms = sum(e.elapsed_ms() for e in evs) / steps
+        nb = fbytes(W)
+        kernels[kname] = {"stage": stg, "avg_ms": kms, "algorithmic_bytes": nb,
+                          "GBps": nb / (kms * 1e-3) / 1e9, "frac": nb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    prim = {nm: PROBES[nm][1] for nm in have if nm in PROBES}
+    dom = args.probe or max(prim, key=lambda nm: kernels[prim[nm]]["avg_ms"])
+    log("kernels (ms):", {k: round(v["avg_ms"], 4) for k, v in kernels.items()}, "dominant stage:", dom)
 
     # timed region: K steps bracketed by synchronize; the dominant kernel of
     # every step is bracketed by its own pair of HIP events on its stream
@@ -681,10 +806,19 @@ def main():
     dom_avg = sum(per) / len(per)
     dom_bytes = algorithmic_bytes(W, dom)
     achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
-    stages_out = {nm: round(sum(starts[s][i].elapsed_time(stops[s][i]) for s in range(steps)) / steps, 4)
-                  for i, (nm, _) in enumerate(stages)}
+    stages_ms = {nm: sum(starts[s][i].elapsed_time(stops[s][i]) for s in range(steps)) / steps
+                 for i, (nm, _) in enumerate(stages)}
+    stages_out = {}
+    for nm, ms in stages_ms.items():
+        e = {"ms": round(ms, 4)}
+        nb = stage_bytes(W, nm)
+        if nb is not None and ms > 0:
+            e.update(algorithmic_bytes=nb, GBps=nb / (ms * 1e-3) / 1e9, frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            if nm == "stats":
+                e["note"] = "report-only: the index lists read once"
+        stages_out[nm] = e
 
-    if args.workload == "cfg5":
+    if name == "cfg5":
         units, unit = W["elements"], "elements/s"
     elif "k" in W:
         units, unit = W["n"] * W["k"], "nonzeros/s"
@@ -692,62 +826,115 @@ def main():
         units, unit = W["nnz"], "nonzeros/s"
     value = units / (ms_per_step * 1e-3)
 
-    # algorithmic bytes of the whole step (every stage's reads and writes)
-    step_bytes = 0
-    for nm, _ in stages:
-        if nm in ("topk_to_coo", "hash_partition"):
-            step_bytes += W["nbytes"][nm]
-        elif nm in ("aggregate", "encode", "skip_reduce_scatter"):
-            step_bytes += algorithmic_bytes(W, nm)
-
-    cfg = {"workload": args.workload}
+    step_bytes = sum(stage_bytes(W, nm) or 0 for nm in stages_ms if nm != "stats")
+    cfg = {"workload": name}
     for key in ("n", "M", "k", "P", "D", "total", "slice_bytes", "p_skip"):
         if key in W:
             cfg[key] = W[key]
     if "agg_off" in W:
-        cfg["union_size"] = int(W["agg_off"][-1].item())
-    res = {
-        "metric": METRIC,
+        cfg["union_size"] = union_size(W)
+    rec = {
         "value": value,
         "unit": unit,
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "config": cfg,
+        "stages": stages_out,
+        "kernels": kernels,
+        "overlap": ("skip reduce-scatter and statistics on their own streams once the aggregate is queued, "
+                    "overlapped with the encode and each other; stage times from a sequential pass")
+        if overlapped else None,
+        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, name),
+            "kernel": PROBES[dom][1], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_ms": dom_avg,
+        },
+        "cpu_baseline": None,
+        "parity": None,
+    }
+    if name in ("cfg1", "cfg2"):
+        # working sets below 256 MB fit the caches: the hot figure above, and
+        # each step alone after a cache-flushing write
+        rec["cold_ms_per_step"] = cold_steps(torch, run_step, steps)
+        rec["cold_value"] = units / (rec["cold_ms_per_step"] * 1e-3)
+    if headline and "pull" in W:
+        rec["pull_side"] = pull_side(W, L, torch, steps)
+    nr = next_rows(name, W, L, torch, sg, steps)
+    if nr:
+        rec["next_rows"] = nr
+    if not args.no_cpu_baseline:
+        log("oracle step (single-threaded) on", name)
+        ref, secs = oracle_step(name, W)
+        ok, worst = compare_outputs(W, ref)
+        rec["parity"] = {"ok": all(ok.values()), "checks": ok, "max_err_over_bound": worst,
+                         "against": "oracle outputs for the same inputs, full size"}
+        cb = {"value": units / secs, "unit": unit, "cores": 1, "kind": "oracle",
+              "sample": "one full step of the workload (every stage the GPU step runs, full size), "
+                        "single-threaded C oracle",
+              "seconds": round(secs, 3)}
+        cb.update(host_cpu())
+        rec["cpu_baseline"] = cb
+        log("parity", name, "ok" if rec["parity"]["ok"] else "FAILED %s" % ok)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all", choices=("all",) + WORKLOADS,
+                    help="one workload only (default: all five, dgc-top5 as the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (parity and baseline)")
+    ap.add_argument("--probe", default=None, help="stage whose kernel is timed for the roofline (default: slowest)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device copy of BYTES (for scaling HBM counters under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the n workers are simulated resident on it); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gen
+    import sparse_gradient_synchronization_amd as sg
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+    names = WORKLOADS if args.workload == "all" else (args.workload,)
+    recs = {}
+    for nm in names:
+        recs[nm] = measure_workload(nm, args, torch, sg, gen, headline=nm == names[0])
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = recs[names[0]]
+    res = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators, shapes and distributions of the workload)",
-        "config": cfg,
-        "stages_ms": stages_out,
-        "overlap": ("skip reduce-scatter and statistics on their own streams once the aggregate is queued, "
-                    "overlapped with the encode and each other; stages_ms from a sequential pass")
-        if overlapped else None,
-        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, args.workload),
-            "kernel": PROBES[dom][1], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
-            "avg_launch_ms": dom_avg,
-        },
-        "cpu_baseline": None,
     }
+    res.update({k: v for k, v in head.items() if k not in res})
     res["hbm_copy"] = copy_bandwidth(torch)
-    if args.workload in ("cfg1", "cfg2"):
-        # working sets below 256 MB fit the caches: the hot figure above, and
-        # each step alone after a cache-flushing write
-        res["cold_ms_per_step"] = cold_steps(torch, run_step, steps)
-        res["cold_value"] = units / (res["cold_ms_per_step"] * 1e-3)
-    if "pull" in W:
-        res["pull_side"] = pull_side(W, L, torch, steps)
-    nr = next_rows(args.workload, W, L, torch, sg, steps)
-    if nr:
-        res["next_rows"] = nr
-    if not args.no_cpu_baseline:
-        log("timing the oracle (single-threaded) on one step")
-        res["cpu_baseline"] = cpu_baseline(args.workload, gen)
+    if len(names) > 1:
+        res["configs"] = {nm: recs[nm] for nm in names[1:]}
+    bad = [nm for nm, r in recs.items() if r["parity"] is not None and not r["parity"]["ok"]]
     print(json.dumps(res), flush=True)
+    if bad:
+        log("parity FAILED on", bad)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

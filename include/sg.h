@@ -141,6 +141,11 @@ int sg_validate_coo(const uint32_t* d_idx, const uint64_t* d_in_off, uint32_t n,
  *   d_idx    [n][k] uint32 out;   d_val [n][k] of dt out
  * Limits: 1 <= n, 1 <= M < 2^32, k <= M (else SG_EINVAL); n * ceil(M / 1024)
  * < 2^31 (else SG_EUNSUPPORTED).  k == 0 writes nothing.
+ * Workspace (sg_topk_workspace_bytes): sized for the worst case, in which
+ * the sampled magnitude band misses the k-th key and every element becomes a
+ * candidate: three slot arrays of n*M 32-bit words (about 12 * n * M bytes,
+ * 4.03 GiB for n = 8, M = 4096 * 11008) plus per-tile counts; the usual case
+ * touches a few percent of it.
  * ------------------------------------------------------------------------ */
 size_t sg_topk_workspace_bytes(uint32_t n, uint64_t M, uint64_t k, sg_dtype dt);
 int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint64_t M, uint64_t k, uint32_t* d_idx,

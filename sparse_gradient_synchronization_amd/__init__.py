@@ -103,11 +103,12 @@ def lib():
             raise RuntimeError("libsg.so is not built (run __graft_entry__.build() or "
                                "python -m sparse_gradient_synchronization_amd.build)")
         L = C.CDLL(LIB_PATH)
+        missing = [name for name in SIGNATURES if not hasattr(L, name)]
+        if missing:
+            raise RuntimeError("libsg.so at %s does not export %s: it is stale, rebuild it "
+                               "(python -m sparse_gradient_synchronization_amd.build)" % (LIB_PATH, ", ".join(missing)))
         for name, (res, args) in SIGNATURES.items():
-            try:
-                f = getattr(L, name)
-            except AttributeError:
-                continue
+            f = getattr(L, name)
             f.restype = res
             f.argtypes = args
         _lib = L

@@ -73,19 +73,15 @@ static int merge_run(MergeParams& p, int mode, hipStream_t st, uint64_t* stats_o
     mg_heavy_kernel<<<(unsigned)(ceil_div(T, 256) < 1024 ? ceil_div(T, 256) : 1024), 256, 0, st>>>(p);
     SG_TRY_LAUNCH();
     // persistent blocks: as many as can be resident at once
-    static int resident[2] = {0, 0};
-    if (!resident[mode]) {
-        int dev = 0, cus = 0, per = 0;
-        SG_TRY(hipGetDevice(&dev));
-        SG_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-        if (mode == MODE_AGG)
-            SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mg_merge_kernel<MODE_AGG>, MG_THREADS, 0));
-        else
-            SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, mg_merge_kernel<MODE_STATS>, MG_THREADS, 0));
-        resident[mode] = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+    int resident = 0;
+    if (mode == MODE_AGG) {
+        if (resident_blocks((const void*)mg_merge_kernel<MODE_AGG>, MG_THREADS, 1 << 30, &resident) != SG_OK)
+            return SG_EHIP;
+    } else if (resident_blocks((const void*)mg_merge_kernel<MODE_STATS>, MG_THREADS, 1 << 30, &resident) != SG_OK) {
+        return SG_EHIP;
     }
     const uint64_t wblocks = ceil_div(T, MG_WAVES);
-    uint64_t grid = wblocks < (uint64_t)resident[mode] ? wblocks : (uint64_t)resident[mode];
+    uint64_t grid = wblocks < (uint64_t)resident ? wblocks : (uint64_t)resident;
     if (mode == MODE_STATS && grid > MG_STATS_MAX_GRID) grid = MG_STATS_MAX_GRID;
     if (grid == 0) grid = 1;
     if (mode == MODE_AGG) {

@@ -41,6 +41,29 @@ int fill_u64(uint64_t* d, uint64_t count, uint64_t v, hipStream_t st)
     return SG_OK;
 }
 
+// Blocks of `kernel` (launched with `threads` threads) that fit on the
+// current device at once, at most `cap`: the grid of a persistent kernel.
+// Cached per (device, kernel) under a lock, so concurrent callers on several
+// host threads and several devices each see their own device's figure.
+static std::mutex g_resident_mu;
+static std::map<std::pair<int, const void*>, int> g_resident;
+
+int resident_blocks(const void* kernel, int threads, int cap, int* out)
+{
+    int dev = 0;
+    SG_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_resident_mu);
+    auto it = g_resident.find({dev, kernel});
+    if (it == g_resident.end()) {
+        int cus = 0, per = 0;
+        SG_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0));
+        it = g_resident.emplace(std::make_pair(dev, kernel), (per > 0 ? per : 1) * (cus > 0 ? cus : 1)).first;
+    }
+    *out = it->second < cap ? it->second : cap;
+    return SG_OK;
+}
+
 static std::mutex g_stage_mu;
 static void* g_stage = nullptr;
 static size_t g_stage_cap = 0;

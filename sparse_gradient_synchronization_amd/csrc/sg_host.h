@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -68,6 +69,10 @@ inline Divider make_divider(uint32_t P)
 // memset node is recorded when a caller captures the stream).
 int fill_u32(uint32_t* d, uint64_t count, uint32_t v, hipStream_t st);
 int fill_u64(uint64_t* d, uint64_t count, uint64_t v, hipStream_t st);
+
+// Blocks of a persistent kernel resident on the current device at once
+// (occupancy x compute units), at most cap; cached per device and kernel.
+int resident_blocks(const void* kernel, int threads, int cap, int* out);
 
 // Small results that an entry point returns on the host travel in one copy
 // into a pinned staging buffer of the process (grown on demand).  The lock

@@ -218,21 +218,14 @@ extern "C" size_t sg_stats_workspace_bytes(uint32_t n, uint64_t M, uint64_t tota
 // The window pass: boundaries, balance, counts, the sum of the partial rows.
 static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64_t* out)
 {
-    static int resident[2] = {0, 0};
     const int ix = p.n <= 8 ? 0 : 1;
     const bool hashed = sw.planes != nullptr;
-    if (!resident[ix]) {
-        int dev = 0, cus = 0, per = 0;
-        SG_TRY(hipGetDevice(&dev));
-        SG_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-        if (ix == 0) SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sw_stats_kernel<8, true>, SW_THREADS, 0));
-        else SG_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sw_stats_kernel<16, true>, SW_THREADS, 0));
-        resident[ix] = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
-        if (resident[ix] > (int)(SW_MAX_WAVES / SW_WAVES)) resident[ix] = SW_MAX_WAVES / SW_WAVES;
-    }
+    int resident = 0;
+    const void* kern = ix == 0 ? (const void*)sw_stats_kernel<8, true> : (const void*)sw_stats_kernel<16, true>;
+    if (resident_blocks(kern, SW_THREADS, (int)(SW_MAX_WAVES / SW_WAVES), &resident) != SG_OK) return SG_EHIP;
     const uint64_t T = p.NT;
     const uint64_t wblocks = ceil_div(T, SW_WAVES);
-    uint64_t grid = wblocks < (uint64_t)resident[ix] ? wblocks : (uint64_t)resident[ix];
+    uint64_t grid = wblocks < (uint64_t)resident ? wblocks : (uint64_t)resident;
     if (grid == 0) grid = 1;
     const uint32_t W = (uint32_t)grid * SW_WAVES;
     mg_plan_kernel<<<1, 512, 0, st>>>(p);
