@@ -204,6 +204,31 @@ int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uin
                       uint64_t* d_part_off, void* d_ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the hash
+ * partition above with no workspace argument.  Same arguments, results,
+ * limits and errors as sg_hash_partition, minus d_ws / ws_bytes.
+ * Its scratch (the per-tile partition counts, and for rows the source of
+ * every output entry) is a fixed device array of the library,
+ * SG_PARTITION_SCRATCH_BYTES (16 MiB) per GPU, held until the process ends;
+ * the call itself allocates nothing.  It needs 4 * (n + 1) +
+ * 4 * P * (ceil(total / 4096) + n) bytes, plus 4 * total when D >= 2 (each
+ * part rounded up to 256 bytes, plus 256); larger inputs return SG_ECAPACITY
+ * before any launch (for P = 16 that is over 10^9 scalar entries, for P = 256
+ * about 6.7 * 10^7; rows with D >= 2 up to about 4 * 10^6).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (two streams, or two host threads) race and give wrong results; order
+ * them on one stream.  The array keeps the last call's contents; a call
+ * writes every word it reads before reading it, so nothing is cleared.
+ * The stream must belong to the current device (the array is looked up on
+ * the current device).
+ * ------------------------------------------------------------------------ */
+#define SG_PARTITION_SCRATCH_BYTES (16u << 20)
+int sg_hash_partition_noalloc(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
+                              const uint64_t* d_in_off, uint32_t n, uint64_t total, uint32_t P, uint32_t seed,
+                              uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, void* stream);
+
+/* ------------------------------------------------------------------------
  * Algorithm 1 of [Zen] section 3.2 (hierarchical hashing), a comparison
  * variant of sg_hash_partition with the same partition membership.
  * Per worker, partition p has a slot memory of r1 parallel and r2 serial

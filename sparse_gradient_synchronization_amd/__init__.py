@@ -65,6 +65,7 @@ SIGNATURES = {
     "sg_partition_workspace_bytes": (_sz, [_u32, _u64, _u32]),
     "sg_hash_partition": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _vp, _sz,
                                  _vp]),
+    "sg_hash_partition_noalloc": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _vp]),
     "sg_aggregate_workspace_bytes": (_sz, [_u32, _u32, _u64, _u64, _u32]),
     "sg_aggregate": (_int, [_vp, _vp, _int, _u32, _vp, _u32, _u32, _u64, _u64, _vp, _vp, _u64, _vp, _vp, _sz,
                             _vp]),
@@ -194,6 +195,29 @@ def sg_hash_partition(idx: torch.Tensor, val, in_off: torch.Tensor, P: int, seed
     _check(lib().sg_hash_partition(_p(idx), _p(val), dt, D, _p(in_off), n, total, P, seed, _p(out_idx),
                                    _p(out_val), _p(part_off), _p(ws), ws.numel(), _stream()),
            "sg_hash_partition")
+    return out_idx, out_val, part_off
+
+
+def sg_hash_partition_noalloc(idx: torch.Tensor, val, in_off: torch.Tensor, P: int, seed: int, out=None):
+    """sg_hash_partition through the entry point that allocates nothing (its
+    scratch is the library's fixed per-GPU array).  out: optional (out_idx,
+    out_val, part_off) to write into; else they are allocated here, by the
+    caller's side of the boundary."""
+    _need_cuda(idx, val, in_off)
+    idx, val, in_off = _contig(idx), _contig(val), _contig(in_off)
+    n = in_off.numel() - 1
+    total = idx.numel()
+    if val is None:
+        D, dt = 0, SG_F32
+    else:
+        D = 1 if val.dim() == 1 else val.shape[1]
+        dt = _dtype_code(val)
+    if out is None:
+        out = (torch.empty_like(idx), None if val is None else torch.empty_like(val),
+               torch.empty((n, P + 1), dtype=torch.int64, device=idx.device))
+    out_idx, out_val, part_off = out
+    _check(lib().sg_hash_partition_noalloc(_p(idx), _p(val), dt, D, _p(in_off), n, total, P, seed, _p(out_idx),
+                                           _p(out_val), _p(part_off), _stream()), "sg_hash_partition_noalloc")
     return out_idx, out_val, part_off
 
 

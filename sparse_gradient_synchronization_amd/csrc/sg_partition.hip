@@ -328,20 +328,38 @@ using namespace sg;
 
 static uint32_t part_max_tiles(uint32_t n, uint64_t total) { return (uint32_t)(ceil_div(total, PT_TILE) + n); }
 
-static uint64_t part_carve(Carver& c, uint32_t n, uint64_t total, uint32_t P, uint32_t** tile_start,
+// rows: whether the source of every output entry is recorded (D >= 2)
+static uint64_t part_carve(Carver& c, uint32_t n, uint64_t total, uint32_t P, bool rows, uint32_t** tile_start,
                            uint32_t** counts, uint32_t** src_of)
 {
     *tile_start = c.take<uint32_t>((uint64_t)n + 1);
     *counts = c.take<uint32_t>((uint64_t)part_max_tiles(n, total) * P);
-    *src_of = c.take<uint32_t>(total); // used for rows (D >= 2)
+    *src_of = c.take<uint32_t>(rows ? total : 0);
     return c.bytes();
 }
+
+static int part_check(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D, const uint64_t* d_in_off,
+                      uint32_t n, uint64_t total, uint32_t P, const uint32_t* d_out_idx, const void* d_out_val,
+                      const uint64_t* d_part_off)
+{
+    if (n == 0 || P == 0 || P > 256 || D > 65536 || (dt != SG_F32 && dt != SG_BF16)) return SG_EINVAL;
+    if (total >= (1ull << 32)) return SG_EUNSUPPORTED;
+    if (!d_in_off || !d_part_off) return SG_EINVAL;
+    if (total > 0 && (!d_idx || !d_out_idx)) return SG_EINVAL;
+    if (D > 0 && total > 0 && (!d_val || !d_out_val)) return SG_EINVAL;
+    return SG_OK;
+}
+
+// The launches, with the workspace already carved into p.
+static int part_run(PartParams& p, const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
+                    const uint64_t* d_in_off, uint32_t n, uint64_t total, uint32_t P, uint32_t seed,
+                    uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, hipStream_t st);
 
 extern "C" size_t sg_partition_workspace_bytes(uint32_t n, uint64_t total, uint32_t P)
 {
     Carver c(nullptr);
     uint32_t *a, *b, *d;
-    return part_carve(c, n, total, P, &a, &b, &d);
+    return part_carve(c, n, total, P, true, &a, &b, &d);
 }
 
 extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
@@ -349,16 +367,74 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
                                  uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, void* d_ws,
                                  size_t ws_bytes, void* stream)
 {
-    if (n == 0 || P == 0 || P > 256 || D > 65536 || (dt != SG_F32 && dt != SG_BF16)) return SG_EINVAL;
-    if (total >= (1ull << 32)) return SG_EUNSUPPORTED;
-    if (!d_in_off || !d_part_off || !d_ws) return SG_EINVAL;
-    if (total > 0 && (!d_idx || !d_out_idx)) return SG_EINVAL;
-    if (D > 0 && total > 0 && (!d_val || !d_out_val)) return SG_EINVAL;
+    const int rc = part_check(d_idx, d_val, dt, D, d_in_off, n, total, P, d_out_idx, d_out_val, d_part_off);
+    if (rc != SG_OK) return rc;
+    if (!d_ws) return SG_EINVAL;
     if (ws_bytes < sg_partition_workspace_bytes(n, total, P)) return SG_ECAPACITY;
-
     PartParams p;
     Carver c(d_ws);
-    part_carve(c, n, total, P, &p.tile_start, &p.counts, &p.src_of);
+    part_carve(c, n, total, P, true, &p.tile_start, &p.counts, &p.src_of);
+    return part_run(p, d_idx, d_val, dt, D, d_in_off, n, total, P, seed, d_out_idx, d_out_val, d_part_off,
+                    as_stream(stream));
+}
+
+// ---------------------------------------------------------------------------
+// The same partition with no workspace argument and no allocation: the
+// per-tile counts (and, for rows, the output entries' sources) live in a
+// fixed device array of the library, `scratch`, one per GPU for the life of
+// the process.  Its device address is looked up once per device with the
+// device current (the host-side name of a __device__ array is not a device
+// address) and kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SG_PARTITION_SCRATCH_BYTES];
+
+static constexpr int PT_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[PT_MAX_DEVICES] = {};
+
+static int scratch_of_current_device(void** out)
+{
+    int dev = 0;
+    SG_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= PT_MAX_DEVICES) return SG_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        SG_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return SG_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SG_OK;
+}
+
+extern "C" int sg_hash_partition_noalloc(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
+                                         const uint64_t* d_in_off, uint32_t n, uint64_t total, uint32_t P,
+                                         uint32_t seed, uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off,
+                                         void* stream)
+{
+    const int rc = part_check(d_idx, d_val, dt, D, d_in_off, n, total, P, d_out_idx, d_out_val, d_part_off);
+    if (rc != SG_OK) return rc;
+    uint32_t *a, *b, *d;
+    Carver sz(nullptr);
+    if (part_carve(sz, n, total, P, D > 1, &a, &b, &d) > SG_PARTITION_SCRATCH_BYTES) return SG_ECAPACITY;
+    void* base = nullptr;
+    const int src = scratch_of_current_device(&base);
+    if (src != SG_OK) return src;
+    // every word the kernels read is written first by the same call (tile
+    // starts by the plan kernel, all counts by the histogram kernel, the
+    // sources by the scatter), so nothing is cleared
+    PartParams p;
+    Carver c(base);
+    part_carve(c, n, total, P, D > 1, &p.tile_start, &p.counts, &p.src_of);
+    return part_run(p, d_idx, d_val, dt, D, d_in_off, n, total, P, seed, d_out_idx, d_out_val, d_part_off,
+                    as_stream(stream));
+}
+
+static int part_run(PartParams& p, const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
+                    const uint64_t* d_in_off, uint32_t n, uint64_t total, uint32_t P, uint32_t seed,
+                    uint32_t* d_out_idx, void* d_out_val, uint64_t* d_part_off, hipStream_t st)
+{
     p.idx = d_idx;
     p.val = d_val;
     p.in_off = d_in_off;
@@ -376,7 +452,6 @@ extern "C" int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dt
     p.max_tiles = part_max_tiles(n, total);
     p.div = make_divider(P);
     p.row_w4 = ((uint64_t)D * p.esz % 4 == 0) && ((uintptr_t)d_val % 4 == 0) && ((uintptr_t)d_out_val % 4 == 0);
-    hipStream_t st = as_stream(stream);
 
     part_plan_kernel<<<1, PT_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();

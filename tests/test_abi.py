@@ -129,6 +129,19 @@ def test_partition_host_checks(L):
     assert L.sg_hash_partition(F, F, 0, 1, F, 4, 100, 8, 1, F, F, F, F, ws - 1, N) == SG_ECAPACITY
 
 
+def test_partition_noalloc_host_checks(L):
+    f = L.sg_hash_partition_noalloc
+    assert f(F, F, 0, 1, F, 4, 100, 0, 1, F, F, F, N) == SG_EINVAL      # P = 0
+    assert f(F, F, 0, 1, F, 4, 100, 257, 1, F, F, F, N) == SG_EINVAL    # P > 256
+    assert f(F, N, 0, 1, F, 4, 100, 8, 1, F, F, F, N) == SG_EINVAL      # D > 0, no values
+    assert f(F, F, 0, 1, N, 4, 100, 8, 1, F, F, F, N) == SG_EINVAL      # no offsets
+    assert f(F, F, 0, 1, F, 4, 1 << 32, 8, 1, F, F, F, N) == SG_EUNSUPPORTED
+    # beyond the fixed scratch: counts of 2^31 entries over 256 partitions,
+    # or the sources of 2^23 rows
+    assert f(F, F, 0, 1, F, 1, 1 << 31, 256, 1, F, F, F, N) == SG_ECAPACITY
+    assert f(F, F, 0, 2, F, 1, 1 << 23, 4, 1, F, F, F, N) == SG_ECAPACITY
+
+
 def test_aggregate_host_checks(L):
     ws = L.sg_aggregate_workspace_bytes(4, 8, 1 << 20, 100, 1)
     assert L.sg_aggregate(F, F, 0, 1, F, 65, 8, 1 << 20, 100, F, F, 100, F, F, 1 << 30, N) == SG_EINVAL  # n > 64
