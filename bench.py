@@ -282,7 +282,7 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "allgather": (12, "allgather_kernel", ["sg_skiprs.hip"]),
     "topk_to_coo": (1, "topk_filter_pipe_kernel", ["sg_topk.hip"]),
     "hash_partition": (2, "part_scatter_kernel", ["sg_partition.hip"]),
-    "aggregate": (3, "mg_merge_kernel", ["sg_merge.hip", "sg_aggregate.hip"]),
+    "aggregate": (3, "un_write_kernel", ["sg_union.hip", "sg_merge.hip", "sg_aggregate.hip"]),
     "encode": (4, "enc_kernel", ["sg_encode.hip"]),
     "decode": (9, "dec_emit_kernel", ["sg_decode.hip"]),
     "scatter_dense": (10, "scatter_kernel", ["sg_decode.hip"]),
@@ -629,7 +629,8 @@ KERNELS = [
     ("hash_partition", 7, "part_hist_kernel", lambda W: W["nnz"] * 4),
     ("hash_partition", 2, "part_scatter_kernel", lambda W: W["nbytes"]["hash_partition"]),
     ("aggregate", 6, "mg_bnd_kernel", lambda W: W["nnz"] * 4),
-    ("aggregate", 3, PROBES["aggregate"][1], lambda W: stage_bytes(W, "aggregate")),
+    ("aggregate", 15, "un_count_kernel", lambda W: W["nnz"] * 4),
+    ("aggregate", 3, "un_write_kernel", lambda W: stage_bytes(W, "aggregate")),
     ("encode", 4, "enc_kernel", lambda W: stage_bytes(W, "encode")),
     ("skip_reduce_scatter", 5, "skip_rs_kernel", lambda W: rs_bytes(W)),
 ]
@@ -765,9 +766,12 @@ def measure_workload(name, args, torch, sg, gen, headline):
     # steps with HIP events the library records around it
     kernels = {}
     have = {nm for nm, _ in stages}
+    rows = W.get("D", 1) > 1
     for stg, pid, kname, fbytes in KERNELS:
-        if stg not in have:
+        if stg not in have or (rows and kname == "un_count_kernel"):
             continue
+        if rows and kname == "un_write_kernel":
+            kname = "mg_merge_kernel"  # rows (D >= 2) take the merge engine
         for s in range(steps):
             L.sg_probe_set(pid, evs[s].start, evs[s].stop)
             step()
@@ -778,6 +782,8 @@ def measure_workload(name, args, torch, sg, gen, headline):
         kernels[kname] = {"stage": stg, "avg_ms": kms, "algorithmic_bytes": nb,
                           "GBps": nb / (kms * 1e-3) / 1e9, "frac": nb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     prim = {nm: PROBES[nm][1] for nm in have if nm in PROBES}
+    if rows and "aggregate" in prim:
+        prim["aggregate"] = "mg_merge_kernel"
     dom = args.probe or max(prim, key=lambda nm: kernels[prim[nm]]["avg_ms"])
     log("kernels (ms):", {k: round(v["avg_ms"], 4) for k, v in kernels.items()}, "dominant stage:", dom)
 
@@ -847,7 +853,7 @@ def measure_workload(name, args, torch, sg, gen, headline):
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, name),
-            "kernel": PROBES[dom][1], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
+            "kernel": prim[dom], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": dom_avg,
         },
         "cpu_baseline": None,

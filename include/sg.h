@@ -116,7 +116,8 @@ typedef enum sg_probe_kernel {
     SG_PROBE_DROPOUT_RS = 11,        /* per-element dropout reduce-scatter: its single kernel */
     SG_PROBE_ALLGATHER = 12,         /* all-gather: its single kernel */
     SG_PROBE_DGC_FILTER = 13,        /* DGC select: the streaming pass over gradient and residual */
-    SG_PROBE_HHASH_INSERT = 14       /* hierarchical hash: the insertion into the slot memory */
+    SG_PROBE_HHASH_INSERT = 14,      /* hierarchical hash: the insertion into the slot memory */
+    SG_PROBE_AGGREGATE_COUNT = 15    /* aggregate: the pass counting each tile's union (scalar values) */
 } sg_probe_kernel;
 int sg_probe_set(int kernel_id, void* start_event, void* stop_event);
 

@@ -35,6 +35,7 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
     p->nchunks_max = (uint32_t)(ceil_div(p->total, MG_CHUNK) + R);
     p->chunk_rec = c.take<uint4>(p->nchunks_max);
     p->bnd = c.take<uint32_t>(R * (p->NT + 1));
+    p->nqsets = 1;
     p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
     p->heavy = c.take<uint32_t>(T);
     if (mode == MODE_AGG) {
@@ -56,6 +57,104 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
         p->st_part = c.take<uint64_t>((uint64_t)MG_STATS_MAX_GRID * p->st_row);
     }
     return c.bytes();
+}
+
+// Scalar values and bare indices (D <= 1): tiles of 2^tb keys holding
+// UN_TARGET to 2 * UN_TARGET entries on average, at most 2^UN_SPAN_LOG_MAX
+// keys; the bitmap words a wave keeps per lane follow from the span.
+static void union_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, uint32_t* NT)
+{
+    uint32_t b = UN_SPAN_LOG_MAX;
+    if (total > 0) {
+        const double want = (double)UN_TARGET * (double)G * (double)M / (double)total;
+        b = 0;
+        while (b < 63 && (double)(1ull << (b + 1)) <= want) ++b;
+        ++b; // 2^b > want
+        if (b < 5) b = 5;
+        if (b > UN_SPAN_LOG_MAX) b = UN_SPAN_LOG_MAX;
+    }
+    *tb = b;
+    uint64_t nt = (M + (1ull << b) - 1) >> b;
+    *NT = (uint32_t)(nt ? nt : 1);
+}
+
+// bitmap words per thread of the union passes for tiles of 2^tb keys
+static int union_wpt(uint32_t tb) { return tb <= 15 ? 4 : (tb == 16 ? 8 : 16); }
+
+constexpr uint32_t UN_MAX_BLOCKS = 16384; // blocks of the union passes, at most
+
+static uint64_t union_carve(Carver& c, MergeParams* p)
+{
+    const uint64_t R = (uint64_t)p->n * p->G;
+    const uint64_t T = (uint64_t)p->G * p->NT;
+    p->nscan = (uint32_t)ceil_div(T, MG_SCAN_BLOCK);
+    p->chunk_start = c.take<uint32_t>(R + 1);
+    p->nchunks_max = (uint32_t)(ceil_div(p->total, MG_CHUNK) + R);
+    p->chunk_rec = c.take<uint4>(p->nchunks_max);
+    p->bnd = c.take<uint32_t>(R * (p->NT + 1));
+    p->nqsets = 1;
+    p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE); // zeroed by the plan kernel, unused
+    p->wcum = c.take<uint64_t>(T);
+    p->wblk = c.take<uint64_t>(p->nscan);
+    p->wtotal = c.take<uint64_t>(1);
+    p->wstart = c.take<uint32_t>(UN_MAX_BLOCKS + 1);
+    p->wave_tot = c.take<uint64_t>(UN_MAX_BLOCKS + 1);
+    return c.bytes();
+}
+
+template <int WPT>
+static int union_launch(MergeParams& p, hipStream_t st)
+{
+    const uint64_t T = (uint64_t)p.G * p.NT;
+    int resident = 0;
+    const void* wk = p.D == 0  ? (const void*)un_write_kernel<WPT, VM_NONE>
+                     : p.bf16 ? (const void*)un_write_kernel<WPT, VM_BF16>
+                              : (const void*)un_write_kernel<WPT, VM_F32>;
+    if (resident_blocks(wk, UN_THREADS, (int)(UN_MAX_BLOCKS / 2), &resident) != SG_OK) return SG_EHIP;
+    // twice the resident blocks: ranges of half the size even out what the
+    // work estimate misses
+    uint64_t W = 2ull * (uint64_t)resident;
+    if (W > T) W = T;
+    if (W == 0) W = 1;
+    p.nwaves = (uint32_t)W;
+    un_work_scan_kernel<<<p.nscan, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    un_work_top_kernel<<<1, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    const uint64_t sblocks = ceil_div(T, 256);
+    un_starts_kernel<<<(unsigned)(sblocks < 2048 ? sblocks : 2048), 256, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_AGGREGATE_COUNT, st);
+    un_count_kernel<WPT><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_AGGREGATE_COUNT, st);
+    un_tot_scan_kernel<<<1, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_AGGREGATE_MERGE, st);
+    if (p.D == 0) un_write_kernel<WPT, VM_NONE><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    else if (p.bf16) un_write_kernel<WPT, VM_BF16><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    else un_write_kernel<WPT, VM_F32><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_AGGREGATE_MERGE, st);
+    return SG_OK;
+}
+
+// Plan and boundaries of the merge engine, then the balance, the count and
+// the write passes.
+static int union_run(MergeParams& p, hipStream_t st)
+{
+    if (p.total == 0) return fill_u64(p.agg_off, (uint64_t)p.G + 1, 0ull, st);
+    mg_plan_kernel<<<1, 512, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_begin(SG_PROBE_AGGREGATE_BND, st);
+    mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    probe_end(SG_PROBE_AGGREGATE_BND, st);
+    switch (union_wpt(p.tb)) {
+    case 4: return union_launch<4>(p, st);
+    case 8: return union_launch<8>(p, st);
+    default: return union_launch<16>(p, st);
+    }
 }
 
 // Queue the engine: plan, boundaries, merge (and, for the aggregate, the
@@ -124,7 +223,8 @@ static void agg_setup(MergeParams* p, uint32_t n, uint32_t P, uint64_t M, uint64
     p->M = M;
     p->total = total;
     p->D = D;
-    choose_tiles(P, M, total, &p->tb, &p->NT);
+    if (D <= 1) union_tiles(P, M, total, &p->tb, &p->NT);
+    else choose_tiles(P, M, total, &p->tb, &p->NT);
 }
 
 extern "C" size_t sg_aggregate_workspace_bytes(uint32_t n, uint32_t P, uint64_t M, uint64_t total, uint32_t D)
@@ -133,7 +233,7 @@ extern "C" size_t sg_aggregate_workspace_bytes(uint32_t n, uint32_t P, uint64_t 
     MergeParams p;
     agg_setup(&p, n, P, M, total, D);
     Carver c(nullptr);
-    return merge_carve(c, &p, MODE_AGG);
+    return D <= 1 ? union_carve(c, &p) : merge_carve(c, &p, MODE_AGG);
 }
 
 extern "C" int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t D,
@@ -152,7 +252,8 @@ extern "C" int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype d
     MergeParams p;
     agg_setup(&p, n, P, M, total, D);
     Carver c(d_ws);
-    merge_carve(c, &p, MODE_AGG);
+    if (D <= 1) union_carve(c, &p);
+    else merge_carve(c, &p, MODE_AGG);
     p.idx = d_idx;
     p.off = d_part_off;
     p.val = d_val;
@@ -162,5 +263,6 @@ extern "C" int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype d
     p.agg_off = d_agg_off;
     p.capacity = capacity;
     p.div = make_divider(P);
+    if (D <= 1) return union_run(p, as_stream(stream));
     return merge_run(p, MODE_AGG, as_stream(stream), nullptr);
 }

@@ -141,7 +141,7 @@ extern "C" int sg_device_error(void* stream)
 
 extern "C" int sg_probe_set(int kernel_id, void* start_event, void* stop_event)
 {
-    if (kernel_id < 0 || kernel_id > SG_PROBE_HHASH_INSERT) return SG_EINVAL; // the last id of sg_probe_kernel
+    if (kernel_id < 0 || kernel_id > SG_PROBE_AGGREGATE_COUNT) return SG_EINVAL; // the last id of sg_probe_kernel
     if (kernel_id != SG_PROBE_NONE && (!start_event || !stop_event)) return SG_EINVAL;
     g_probe.id = kernel_id;
     g_probe.start = reinterpret_cast<hipEvent_t>(start_event);

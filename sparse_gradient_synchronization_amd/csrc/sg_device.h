@@ -126,6 +126,19 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, SG_WAVE - 1);
 }
 
+// maximum over the wave, the same in every lane
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+    uint32_t t;
+    t = dpp_move<kDppRowShr1>(0u, v); v = t > v ? t : v;
+    t = dpp_move<kDppRowShr2>(0u, v); v = t > v ? t : v;
+    t = dpp_move<kDppRowShr4>(0u, v); v = t > v ? t : v;
+    t = dpp_move<kDppRowShr8>(0u, v); v = t > v ? t : v;
+    t = dpp_move<kDppRowBcast15, 0xa>(0u, v); v = t > v ? t : v;
+    t = dpp_move<kDppRowBcast31, 0xc>(0u, v); v = t > v ? t : v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, SG_WAVE - 1);
+}
+
 // Exclusive scan over the threads of a block of NT threads (NT a multiple of
 // 64, at most 1024).  `lds` must hold NT/64 + 1 words.  Returns the exclusive
 // prefix; *total receives the block total.  Contains two barriers.

@@ -89,7 +89,17 @@ struct MergeParams {
     uint32_t* stage_first;  // [total] a staged key's first contributor, relative to its tile's staging base
     uint32_t* tile_ent;     // [G*NT] entries of a tile
     uint2* row_rng;         // [total] output row o: its contributors are stage_src[x .. y)
-    uint32_t* queue;        // [MG_NQ * MG_QSTRIDE]: queue[0] heavy tiles listed; queue[q * MG_QSTRIDE + 1] chunk tickets of queue q
+    uint32_t* queue;        // [nqsets * MG_NQ * MG_QSTRIDE]: queue[0] heavy tiles listed; queue[(s * MG_NQ + q) * MG_QSTRIDE + 1]
+                            // chunk tickets of queue q in set s (one set per pass over the tiles)
+    uint32_t nqsets;        // counter sets in queue
+    // union engine (sg_union.hip): waves take contiguous tile ranges of equal work
+    uint32_t* work;         // [G*NT] work of a tile
+    uint64_t* wcum;         // [G*NT] exclusive prefix of the work inside its scan block
+    uint64_t* wblk;         // [nscan] scan block totals, then their exclusive prefix
+    uint64_t* wtotal;       // [1] total work
+    uint32_t* wstart;       // [nwaves+1] first tile of wave k
+    uint64_t* wave_tot;     // [nwaves+1] union size of wave k's tiles, then its exclusive prefix
+    uint32_t nwaves;
     uint32_t* heavy;        // [G*NT] tiles with more than MG_HEAVY entries
     // statistics
     uint64_t* st_part;      // [grid][st_row] per-block partial counts
@@ -143,7 +153,8 @@ __global__ __launch_bounds__(512) void mg_plan_kernel(MergeParams p)
         __syncthreads();
     }
     if (threadIdx.x == 0) p.chunk_start[R] = carry;
-    for (uint32_t i = threadIdx.x; i < (uint32_t)(MG_NQ * MG_QSTRIDE); i += 512) p.queue[i] = 0;
+    const uint32_t qwords = (p.nqsets > 1 ? p.nqsets : 1u) * (uint32_t)(MG_NQ * MG_QSTRIDE);
+    for (uint32_t i = threadIdx.x; i < qwords; i += 512) p.queue[i] = 0;
     __syncthreads();
     // block -> run table of the boundary pass
     for (uint32_t r = threadIdx.x / SG_WAVE; r < R; r += 512 / SG_WAVE) { // one wave per run
@@ -484,10 +495,12 @@ __device__ __forceinline__ uint32_t queue_first(uint32_t q, uint32_t T)
     return (uint32_t)(((uint64_t)q * T) / MG_NQ);
 }
 
-// Next tile of the wave, or T when none is left.
+// Next tile of the wave, or T when none is left.  `set` picks the ticket
+// counters (each pass over the tiles has its own; the heavy list is shared).
 __device__ __forceinline__ uint32_t acquire_tile(const MergeParams& p, uint32_t T, uint32_t W, WaveWork& k,
-                                                 bool& from_heavy)
+                                                 bool& from_heavy, uint32_t set = 0)
 {
+    uint32_t* const ctr = p.queue + (uint64_t)set * MG_NQ * MG_QSTRIDE + 1;
     if (k.heavy_phase) {
         if (k.hnext < p.queue[0]) {
             const uint32_t t = p.heavy[k.hnext];
@@ -501,7 +514,7 @@ __device__ __forceinline__ uint32_t acquire_tile(const MergeParams& p, uint32_t 
     if (k.next < k.end) return k.next++;
     while (true) {
         uint32_t c = 0;
-        if (lane_id() == 0) c = atomicAdd(&p.queue[k.q * MG_QSTRIDE + 1], 1u);
+        if (lane_id() == 0) c = atomicAdd(&ctr[k.q * MG_QSTRIDE], 1u);
         c = (uint32_t)__builtin_amdgcn_readfirstlane((int)c);
         const uint64_t first = (uint64_t)queue_first(k.q, T) + (uint64_t)c * MG_CHUNK_TILES;
         const uint32_t qend = queue_first(k.q + 1, T);
@@ -516,7 +529,7 @@ __device__ __forceinline__ uint32_t acquire_tile(const MergeParams& p, uint32_t 
         uint32_t qq = 0;
         if (j + 1 < (uint32_t)MG_NQ) {
             qq = (k.q + 1 + j) % MG_NQ;
-            const uint32_t v = __atomic_load_n(&p.queue[qq * MG_QSTRIDE + 1], __ATOMIC_RELAXED);
+            const uint32_t v = __atomic_load_n(&ctr[qq * MG_QSTRIDE], __ATOMIC_RELAXED);
             open = (uint64_t)queue_first(qq, T) + (uint64_t)v * MG_CHUNK_TILES < queue_first(qq + 1, T);
         }
         const uint64_t m = ballot(open);

@@ -177,6 +177,7 @@ static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* 
         p->nchunks_max = (uint32_t)(ceil_div(p->total, MG_CHUNK) + R);
         p->chunk_rec = c.take<uint4>(p->nchunks_max);
         p->bnd = c.take<uint32_t>(R * (p->NT + 1));
+        p->nqsets = 1;
         p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
         sw->work = c.take<uint32_t>(p->NT);
         sw->wcum = c.take<uint64_t>(p->NT);
