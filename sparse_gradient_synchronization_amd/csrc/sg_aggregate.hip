@@ -59,17 +59,17 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
     return c.bytes();
 }
 
-// Scalar values and bare indices (D <= 1): tiles of 2^tb keys holding
-// UN_TARGET to 2 * UN_TARGET entries on average, at most 2^UN_SPAN_LOG_MAX
-// keys; the bitmap words a wave keeps per lane follow from the span.
+// Scalar values and bare indices (D <= 1): tiles of 2^tb keys holding about
+// UN_TARGET entries on average (2^tb the power of two nearest to the span
+// that holds that many), within [2^5, 2^UN_SPAN_LOG_MAX] keys.
 static void union_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, uint32_t* NT)
 {
     uint32_t b = UN_SPAN_LOG_MAX;
     if (total > 0) {
         const double want = (double)UN_TARGET * (double)G * (double)M / (double)total;
         b = 0;
-        while (b < 63 && (double)(1ull << (b + 1)) <= want) ++b;
-        ++b; // 2^b > want
+        while (b < 63 && (double)(1ull << (b + 1)) <= want) ++b; // 2^b <= want < 2^(b+1)
+        if (want >= 1.4142135623730951 * (double)(1ull << b)) ++b;
         if (b < 5) b = 5;
         if (b > UN_SPAN_LOG_MAX) b = UN_SPAN_LOG_MAX;
     }
@@ -78,10 +78,9 @@ static void union_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, ui
     *NT = (uint32_t)(nt ? nt : 1);
 }
 
-// bitmap words per thread of the union passes for tiles of 2^tb keys
-static int union_wpt(uint32_t tb) { return tb <= 15 ? 4 : (tb == 16 ? 8 : 16); }
-
-constexpr uint32_t UN_MAX_BLOCKS = 16384; // blocks of the union passes, at most
+// bitmap words per lane of the union passes for tiles of 2^tb keys (64 lanes
+// of 32-bit words; spans below 2^11 keys leave words unused)
+static int union_wpl(uint32_t tb) { return tb <= 11 ? 1 : 1 << (tb - 11); }
 
 static uint64_t union_carve(Carver& c, MergeParams* p)
 {
@@ -94,53 +93,53 @@ static uint64_t union_carve(Carver& c, MergeParams* p)
     p->bnd = c.take<uint32_t>(R * (p->NT + 1));
     p->nqsets = 1;
     p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE); // zeroed by the plan kernel, unused
-    p->wcum = c.take<uint64_t>(T);
-    p->wblk = c.take<uint64_t>(p->nscan);
-    p->wtotal = c.take<uint64_t>(1);
-    p->wstart = c.take<uint32_t>(UN_MAX_BLOCKS + 1);
-    p->wave_tot = c.take<uint64_t>(UN_MAX_BLOCKS + 1);
+    p->tile_cnt = c.take<uint32_t>(T);
+    p->tile_out = c.take<uint64_t>(T);
+    p->blk_sum = c.take<uint64_t>(p->nscan);
     return c.bytes();
 }
 
-template <int WPT>
+// blocks of a union pass: as many as can be resident, no more than the tiles
+// need (UN_WPB tiles per block at once)
+static int union_blocks(const void* kernel, uint64_t T, unsigned* blocks)
+{
+    int resident = 0;
+    if (resident_blocks(kernel, UN_THREADS, 1 << 30, &resident) != SG_OK) return SG_EHIP;
+    uint64_t b = ceil_div(T, UN_WPB);
+    if (b > (uint64_t)resident) b = (uint64_t)resident;
+    *blocks = (unsigned)(b ? b : 1);
+    return SG_OK;
+}
+
+template <int WPL>
 static int union_launch(MergeParams& p, hipStream_t st)
 {
     const uint64_t T = (uint64_t)p.G * p.NT;
-    int resident = 0;
-    const void* wk = p.D == 0  ? (const void*)un_write_kernel<WPT, VM_NONE>
-                     : p.bf16 ? (const void*)un_write_kernel<WPT, VM_BF16>
-                              : (const void*)un_write_kernel<WPT, VM_F32>;
-    if (resident_blocks(wk, UN_THREADS, (int)(UN_MAX_BLOCKS / 2), &resident) != SG_OK) return SG_EHIP;
-    // twice the resident blocks: ranges of half the size even out what the
-    // work estimate misses
-    uint64_t W = 2ull * (uint64_t)resident;
-    if (W > T) W = T;
-    if (W == 0) W = 1;
-    p.nwaves = (uint32_t)W;
-    un_work_scan_kernel<<<p.nscan, 1024, 0, st>>>(p);
-    SG_TRY_LAUNCH();
-    un_work_top_kernel<<<1, 1024, 0, st>>>(p);
-    SG_TRY_LAUNCH();
-    const uint64_t sblocks = ceil_div(T, 256);
-    un_starts_kernel<<<(unsigned)(sblocks < 2048 ? sblocks : 2048), 256, 0, st>>>(p);
-    SG_TRY_LAUNCH();
+    const void* wk = p.D == 0  ? (const void*)un_write_kernel<WPL, VM_NONE>
+                     : p.bf16 ? (const void*)un_write_kernel<WPL, VM_BF16>
+                              : (const void*)un_write_kernel<WPL, VM_F32>;
+    unsigned cb = 0, wb = 0;
+    if (union_blocks((const void*)un_count_kernel<WPL>, T, &cb) != SG_OK) return SG_EHIP;
+    if (union_blocks(wk, T, &wb) != SG_OK) return SG_EHIP;
     probe_begin(SG_PROBE_AGGREGATE_COUNT, st);
-    un_count_kernel<WPT><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    un_count_kernel<WPL><<<cb, UN_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_COUNT, st);
-    un_tot_scan_kernel<<<1, 1024, 0, st>>>(p);
+    mg_scan_local_kernel<<<p.nscan, 1024, 0, st>>>(p);
+    SG_TRY_LAUNCH();
+    mg_scan_top_kernel<<<1, 1024, 0, st>>>(p); // agg_off[G]
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_AGGREGATE_MERGE, st);
-    if (p.D == 0) un_write_kernel<WPT, VM_NONE><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
-    else if (p.bf16) un_write_kernel<WPT, VM_BF16><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
-    else un_write_kernel<WPT, VM_F32><<<(unsigned)W, UN_THREADS, 0, st>>>(p);
+    if (p.D == 0) un_write_kernel<WPL, VM_NONE><<<wb, UN_THREADS, 0, st>>>(p);
+    else if (p.bf16) un_write_kernel<WPL, VM_BF16><<<wb, UN_THREADS, 0, st>>>(p);
+    else un_write_kernel<WPL, VM_F32><<<wb, UN_THREADS, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_MERGE, st);
     return SG_OK;
 }
 
-// Plan and boundaries of the merge engine, then the balance, the count and
-// the write passes.
+// Plan and boundaries of the merge engine, then the count pass, the scan of
+// the tiles' union sizes and the write pass.
 static int union_run(MergeParams& p, hipStream_t st)
 {
     if (p.total == 0) return fill_u64(p.agg_off, (uint64_t)p.G + 1, 0ull, st);
@@ -150,10 +149,13 @@ static int union_run(MergeParams& p, hipStream_t st)
     mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_AGGREGATE_BND, st);
-    switch (union_wpt(p.tb)) {
+    switch (union_wpl(p.tb)) {
+    case 1: return union_launch<1>(p, st);
+    case 2: return union_launch<2>(p, st);
     case 4: return union_launch<4>(p, st);
     case 8: return union_launch<8>(p, st);
-    default: return union_launch<16>(p, st);
+    case 16: return union_launch<16>(p, st);
+    default: return union_launch<32>(p, st);
     }
 }
 

@@ -3,48 +3,53 @@
 // values of each index summed (the server side of Push in the Zen OSDI'25
 // digest, section 3.1; equal to the dense AllReduce, section 3.2).
 //
-// The key space of every partition is cut into tiles of 2^tb keys; the
-// merge engine's boundary pass (sg_merge.hip) records where each tile starts
-// in each run.  Tiles are taken in (partition, key) order, which is the
-// output order, and dealt to blocks as contiguous ranges of equal work (the
-// tile's entries plus a fixed cost), from a scan of the per-tile work.  Two
-// passes, a block of 256 threads per range, no atomics on global memory:
-//   count  a tile's keys OR-ed into an LDS presence bitmap of its span (up
-//          to 2^17 keys); the popcounts summed over the block's tiles give
-//          its union size, and a scan of those gives every block its output
-//          offset.
-//   write  a tile's entries in windows of at most 2048 (a window takes up to
-//          8 g entries of every run, g = 256 / n rounded to a power of two,
-//          and ends at the smallest last-loaded key of a run it cut short,
-//          so every key is whole inside one window): the presence bitmap and
-//          its prefix popcounts give each entry the rank of its key; values
-//          are added into an LDS slot per rank, one wave after the other in
-//          the order of the runs they hold, so every sum is taken in worker
-//          order; keys and sums are written once, in order, at the block's
-//          offset, with consecutive threads on consecutive addresses.
-// A window gives run w the g threads [w g, (w+1) g): thread s of the group
-// reads entries s, s + g, s + 2g, ... of the run's part of the window, so an
-// entry's address is its run's position plus a constant.
+// The key space of every partition is cut into tiles of 2^tb keys (a few
+// hundred entries on average); the merge engine's boundary pass
+// (sg_merge.hip) records where each tile starts in each run.  A wave owns a
+// whole tile at a time, with no block barrier and no global atomic: the waves
+// of the grid take tiles t = k, k + NW, k + 2 NW, ... (k the wave's number,
+// NW the waves of the grid), and the run ranges of a wave's next tile are
+// loaded while it works on the current one.  Two passes:
+//   count  the tile's keys OR-ed into an LDS presence bitmap of its span; the
+//          popcount is the tile's union size.  A scan of the sizes gives
+//          every tile its output offset (and every partition its start).
+//   write  the tile's entries again, with their values: the bitmap and its
+//          prefix popcounts give each entry the rank of its key, the keys go
+//          to an LDS slot per rank and the values are added there, in worker
+//          order (below); keys and sums are then written once, in order, at
+//          the tile's offset, with consecutive lanes on consecutive
+//          addresses.
+// A window holds at most 64 S entries (S slots per lane: 16 in the count
+// pass, 8 in the write pass): the run parts of the tile laid end to end, lane
+// l taking entries l, l + 64, l + 128, ... of the window, so every load
+// instruction reads 256 consecutive bytes (split only where one run's part
+// ends and the next begins).  A tile with more entries is taken in several
+// windows, each run giving a share in proportion to what it has left; in the
+// write pass such a window ends at the smallest last-loaded key of the runs
+// it cut short (later entries go back to their runs), so every key is whole
+// inside one window.
+//
+// Both passes are bound by instruction issue, not by memory: the code keeps
+// the instructions per entry few (part lookup by mbcnt over part-end marks,
+// invalid slots folded into an out-of-span offset, bitmap word and prefix
+// read together).  LDS float atomics are avoided: they cost far more than
+// the plain read-add-write rounds used instead.
 #include "sg_host.h"
 
 namespace sg {
 
-constexpr int UN_THREADS = 256;              // threads per block
-constexpr int UN_WAVES = UN_THREADS / SG_WAVE;
-constexpr int UN_PER = 8;                    // slots per thread
-constexpr int UN_CAP = UN_PER * UN_THREADS;  // entries of a window
+constexpr int UN_WPB = 4;                    // waves per block (each on tiles of its own)
+constexpr int UN_THREADS = UN_WPB * SG_WAVE; // threads per block
+constexpr int UN_SC = 16;                    // entry slots per lane, count pass
+constexpr int UN_SW = 8;                     // entry slots per lane, write pass
+constexpr int UN_CAP = UN_SW * SG_WAVE;      // entries of a write window (distinct keys of a window, at most)
 #ifndef SG_UN_TARGET
-#define SG_UN_TARGET 1536
+#define SG_UN_TARGET 320
 #endif
 constexpr int UN_TARGET = SG_UN_TARGET;      // mean entries per tile aimed at
-#ifndef SG_UN_SPAN_LOG_MAX
-#define SG_UN_SPAN_LOG_MAX 17
-#endif
-constexpr int UN_SPAN_LOG_MAX = SG_UN_SPAN_LOG_MAX; // a tile spans at most 2^17 keys (WPT = 16)
-#ifndef SG_UN_FIXED
-#define SG_UN_FIXED 512
-#endif
-constexpr uint32_t UN_FIXED = SG_UN_FIXED;   // a tile's fixed cost, in entries, for the balance of blocks
+constexpr int UN_SPAN_LOG_MAX = 16;          // a tile spans at most 2^16 keys (32 bitmap words per lane)
+static_assert(UN_CAP >= 2 * SG_WAVE, "a window must hold one entry of each of up to 64 runs and more");
+static_assert(UN_CAP < 65536, "ranks inside a window fit in the bitmap prefix words");
 
 // Value modes: VM_NONE (indices only), VM_F32, VM_BF16 (widened to fp32 where
 // the values are added, so the loaded registers are not touched before).
@@ -56,507 +61,439 @@ __device__ __forceinline__ float un_value(uint32_t b)
     return __uint_as_float(VM == VM_BF16 ? b << 16 : b);
 }
 
-// Threads per run: 256 / (n rounded up to a power of two), as a log.
-__device__ __forceinline__ uint32_t un_glog(uint32_t n)
-{
-    uint32_t l = 0;
-    while ((1u << l) < n) ++l;
-    return 8 - l; // n <= 64
-}
-
-// Run bookkeeping of a block, in LDS: run w's next position (absolute),
-// remaining entries of the tile, and the window's take.
-struct UnRuns {
-    uint32_t pos[64];
-    uint32_t rem[64];
-    uint32_t take[64];
-    uint32_t drop[64];
-    uint32_t kmax;   // the window's last key (cut windows)
-    uint32_t more;   // entries left in the tile after the window
-    uint32_t cut;    // some run continues after the window
+// Window tables and the next tile's parts, shared by both passes.
+template <int S>
+struct UnTables {
+    uint32_t sb[2 * S];        // bit j set where entry j + 1 of the window begins a part
+    uint32_t base[SG_WAVE];    // k-th non-empty part: its first position minus its window start
+    uint32_t drop[SG_WAVE];    // entries of the k-th part returned by a cut window
+    uint32_t npos[SG_WAVE];    // the next tile: lane w's part, its position
+    uint32_t nrem[SG_WAVE];    // and length
+    uint64_t nout, nend;       // the next tile's output slot (write pass)
 };
 
-// Wave 0 (threads below n hold runs): the raw run range of tile t (lanes
-// past n repeat run n-1, tiles past the last repeat the last), issued
-// without waiting; un_runs_put clamps it into LDS once it is needed.
+// LDS of a wave in the count pass: the presence bitmap of the tile's span.
+template <int WPL>
+struct UnCountWave {
+    uint32_t bits[WPL * SG_WAVE];
+    UnTables<UN_SC> tb;
+};
+
+// LDS of a wave in the write pass: bitmap word w with the distinct keys
+// before it (read together when an entry is ranked), keys and sums by rank.
+template <int WPL>
+struct UnWriteWave {
+    uint2 bw[WPL * SG_WAVE];
+    uint32_t keys[UN_CAP];
+    float acc[UN_CAP];
+    UnTables<UN_SW> tb;
+};
+
+// The raw run ranges of tile t in the lanes below n (lanes past n repeat run
+// n-1) and the tile's output slot (write pass), issued without waiting;
+// un_raw_put clamps the ranges once they are needed.
 struct URaw {
-    uint64_t a, e; // the run's absolute range
-    uint32_t x, y; // the tile's part, relative to the run
+    uint64_t a, e;  // the run's absolute range
+    uint32_t x, y;  // the tile's part, relative to the run
+    uint64_t out;   // the tile's output offset inside its scan block, then the block's
+    uint64_t blk;
+    uint32_t cnt;   // the tile's union size
 };
 
-__device__ __forceinline__ URaw un_runs_issue(const MergeParams& p, uint32_t t)
+template <bool WRITE>
+__device__ __forceinline__ URaw un_raw_issue(const MergeParams& p, uint32_t t)
 {
-    const uint32_t w = threadIdx.x & (SG_WAVE - 1);
-    const uint32_t T = p.G * p.NT;
-    const uint32_t tt = t < T ? t : T - 1;
+    const uint32_t w = lane_id();
     const uint32_t ww = w < p.n ? w : p.n - 1;
-    const uint32_t g = tt / p.NT, b = tt % p.NT;
+    const uint32_t g = t / p.NT, b = t % p.NT;
     URaw r;
     r.a = p.off[(uint64_t)ww * p.stride + g];
     r.e = p.off[(uint64_t)ww * p.stride + g + 1];
     const uint32_t* row = p.bnd + ((uint64_t)g * p.n + ww) * (p.NT + 1);
     r.x = row[b];
     r.y = row[b + 1];
+    r.out = r.blk = 0;
+    r.cnt = 0;
+    if (WRITE) { // every lane (one request): a load under a branch would be copied, and waited for, at once
+        r.out = p.tile_out[t];
+        r.blk = p.blk_sum[t / MG_SCAN_BLOCK];
+        r.cnt = p.tile_cnt[t];
+    }
     return r;
 }
 
-__device__ __forceinline__ void un_runs_put(const MergeParams& p, const URaw& r, UnRuns& R)
+// Marks loaded registers as used here, so their wait is taken on every path:
+// a load whose first use sits under a branch some paths skip stays pending
+// on those paths, and the register's next write then waits for every
+// vector memory operation in flight (prefetches and stores included).
+template <int N>
+__device__ __forceinline__ void un_hold(uint32_t (&r)[N])
 {
-    const uint32_t w = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// lane w < n: the part's absolute start and length (empty in the other lanes)
+__device__ __forceinline__ void un_raw_put(const MergeParams& p, const URaw& r, uint32_t& pos, uint32_t& rem)
+{
     uint64_t a = r.a > p.total ? p.total : r.a, e = r.e > p.total ? p.total : r.e;
     if (e < a) e = a;
     const uint64_t len = e - a;
     uint64_t x = r.x > len ? len : r.x, y = r.y > len ? len : r.y;
     if (y < x) y = x;
-    if (w < p.n) {
-        R.pos[w] = (uint32_t)(a + x);
-        R.rem[w] = (uint32_t)(y - x);
+    const bool mine = lane_id() < p.n;
+    pos = mine ? (uint32_t)(a + x) : 0u;
+    rem = mine ? (uint32_t)(y - x) : 0u;
+}
+
+// The next tile's parts and output slot, from the prefetched registers into
+// LDS.  The compiler waits for those loads here; a window calls this once
+// its own loads (issued after the prefetch) have been used, so the wait
+// costs nothing.  Kept in registers until the next tile, they would be
+// copied between registers at the top of the tile loop, and a copy of a
+// pending load waits for every vector memory operation in flight, the
+// tile's output stores included (loads and stores share one counter).
+template <bool WRITE, int S>
+__device__ __forceinline__ void un_stash(const MergeParams& p, UnTables<S>& tb, const URaw& nxt)
+{
+    // every vector memory operation issued before the window's loads is
+    // done once those loads are (they complete in order), so this wait is
+    // free here and leaves nothing pending for the compiler to wait for later
+    wait_vmem();
+    // a copy marked as changed here, so nothing computed from it is moved
+    // ahead of this point
+    URaw r = nxt;
+    asm volatile("" : "+v"(r.a), "+v"(r.e), "+v"(r.x), "+v"(r.y));
+    if (WRITE) asm volatile("" : "+v"(r.out), "+v"(r.blk), "+v"(r.cnt));
+    uint32_t pos, rem;
+    un_raw_put(p, r, pos, rem);
+    const uint32_t lane = lane_id();
+    tb.npos[lane] = pos;
+    tb.nrem[lane] = rem;
+    if (WRITE && lane == 0) {
+        tb.nout = r.out + r.blk;
+        tb.nend = r.out + r.blk + r.cnt;
     }
 }
 
-// Wave 0: the tile's run parts into LDS (loads and waits).
-__device__ __forceinline__ void un_runs_load(const MergeParams& p, uint32_t t, UnRuns& R)
+// One window of a tile.  In: the run parts left (lane w < n: position `pos`,
+// `rem` entries; rtot = their sum > 0, wave-uniform).  Takes `take` entries
+// of every part (all of them when they fit, else a share), lays them end to
+// end and loads entry j = l + 64 i into slot i of lane l: keys, and values
+// unless VM is VM_NONE.  Returns the window's entry count E (slots with
+// j >= E hold no entry).  part[i] is the entry's part (its place among the
+// non-empty parts, in worker order; `kr` is the lane's own), sbs[i] the
+// slot's part-end marks.  The loaded registers are not touched here, so the
+// loads stay in flight together until their first use.
+template <int S, int VM>
+__device__ __forceinline__ uint32_t un_window(const MergeParams& p, UnTables<S>& tb, uint32_t pos, uint32_t rem,
+                                              uint32_t rtot, uint32_t& take, uint32_t& kr, uint32_t (&key)[S],
+                                              uint32_t (&vb)[S], uint32_t (&part)[S], uint64_t (&sbs)[S])
 {
-    if (threadIdx.x >= SG_WAVE) return;
-    const URaw r = un_runs_issue(p, t);
-    un_runs_put(p, r, R);
-}
-
-// Wave 0: the next window's take of every run (at most 8 g entries), whether
-// a run continues after it; the cut key starts at "none".
-__device__ __forceinline__ void un_runs_window(uint32_t n, uint32_t glog, UnRuns& R)
-{
-    const uint32_t w = threadIdx.x;
-    if (w >= SG_WAVE) return;
-    const uint32_t cap = (uint32_t)UN_PER << glog;
-    const uint32_t rem = w < n ? R.rem[w] : 0u;
-    const uint32_t take = rem < cap ? rem : cap;
-    if (w < n) {
-        R.take[w] = take;
-        R.drop[w] = 0u;
+    constexpr uint32_t CAP = (uint32_t)S * SG_WAVE;
+    const uint32_t lane = lane_id();
+    take = rem;
+    if (rtot > CAP) { // uniform: a share in proportion, at least one entry of every part
+        const uint32_t share = 1u + (uint32_t)(((uint64_t)(CAP - p.n) * rem) / rtot);
+        take = rem == 0 ? 0u : (share < rem ? share : rem);
     }
-    const bool cut = ballot(take < rem) != 0;
-    if (w == 0) {
-        R.cut = cut ? 1u : 0u;
-        R.kmax = 0xffffffffu;
+    const uint32_t inc = wave_incl_scan(take);
+    const uint32_t E = lane_value(inc, SG_WAVE - 1);
+    const uint32_t pre = inc - take;
+    kr = count_below(ballot(take > 0));
+    if (lane < 2u * S) tb.sb[lane] = 0u;
+    tb.drop[lane] = 0u;
+    wave_sync();
+    if (take > 0) {
+        if (pre > 0) atomicOr(&tb.sb[(pre - 1) >> 5], 1u << ((pre - 1) & 31u)); // the entry before the part
+        tb.base[kr] = pos - pre;
     }
-}
-
-// Every thread: its run's window entries into registers, slot i holding entry
-// i g + s of the run's part (s = the thread's place in its group).  Returns
-// the slots that hold an entry.  The loaded registers are not touched here,
-// so the loads stay in flight together until their first use; slots past
-// the run's take load the run's first window entry (or the last entry of
-// the input).
-template <int VM>
-__device__ __forceinline__ uint32_t un_window_load(const MergeParams& p, const UnRuns& R, uint32_t glog,
-                                                   uint32_t (&key)[UN_PER], uint32_t (&vb)[UN_PER])
-{
-    const uint32_t w = threadIdx.x >> glog, s = threadIdx.x & ((1u << glog) - 1u);
-    const uint32_t take = w < p.n ? R.take[w] : 0u;
-    const uint32_t base = w < p.n ? R.pos[w] : 0u;
-    const uint32_t last = p.total > 0 ? (uint32_t)(p.total - 1) : 0u;
-    uint32_t valid = 0;
+    wave_sync();
+    const uint32_t last = (uint32_t)(p.total - 1); // total > 0 here
+    uint32_t pc = 0; // marks in earlier slots
 #pragma unroll
-    for (int i = 0; i < UN_PER; ++i) {
-        const uint32_t e = ((uint32_t)i << glog) + s;
-        uint32_t pos = base + (e < take ? e : 0u);
-        pos = pos < last ? pos : last;
-        key[i] = p.idx[pos];
-        if (VM == VM_F32) vb[i] = static_cast<const uint32_t*>(p.val)[pos];
-        if (VM == VM_BF16) vb[i] = static_cast<const uint16_t*>(p.val)[pos];
-        valid |= (e < take ? 1u : 0u) << i;
+    for (int i = 0; i < S; ++i) {
+        const uint2 sw = *reinterpret_cast<const uint2*>(&tb.sb[2 * i]);
+        const uint32_t lo = uniform(sw.x), hi = uniform(sw.y);
+        const uint32_t j = lane + (uint32_t)i * SG_WAVE;
+        // the part of entry j: the marks before it (mbcnt counts the set
+        // bits of the lanes below this one)
+        part[i] = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, pc));
+        sbs[i] = (uint64_t)lo | ((uint64_t)hi << 32);
+        pc += (uint32_t)(__popc(lo) + __popc(hi));
+        uint32_t q = tb.base[part[i]] + j;
+        q = q < last ? q : last;
+        key[i] = p.idx[q];
+        if (VM == VM_F32) vb[i] = static_cast<const uint32_t*>(p.val)[q];
+        if (VM == VM_BF16) vb[i] = static_cast<const uint16_t*>(p.val)[q];
     }
-    return valid;
+    return E;
 }
 
-// Wave 0, once the window's entries are accounted for: advance every run by
-// the entries it used, and whether the tile has entries left.
-__device__ __forceinline__ void un_runs_advance(uint32_t n, UnRuns& R)
+// Bitmap word w (keys 32 w .. 32 w + 31 of the span) belongs to lane w / WPL,
+// which takes its WPL words in order for the prefix popcounts; it is stored
+// at (w % WPL) * 64 + w / WPL, so the lanes read their q-th words from 64
+// consecutive places (no LDS bank conflict).
+template <int WPL>
+__device__ __forceinline__ uint32_t un_phys(uint32_t w)
 {
-    const uint32_t w = threadIdx.x;
-    if (w >= SG_WAVE) return;
-    uint32_t rem = 0;
-    if (w < n) {
-        const uint32_t used = R.take[w] - R.drop[w];
-        R.pos[w] += used;
-        rem = R.rem[w] - used;
-        R.rem[w] = rem;
-    }
-    const bool more = ballot(rem > 0) != 0;
-    if (w == 0) R.more = more ? 1u : 0u;
+    constexpr uint32_t L = WPL == 1 ? 0 : WPL == 2 ? 1 : WPL == 4 ? 2 : WPL == 8 ? 3 : WPL == 16 ? 4 : 5;
+    return WPL == 1 ? w : ((w & (WPL - 1)) << 6) | (w >> L);
 }
 
-// ---------------------------------------------------------------------------
-// the balance: work of every tile, its scan, the first tile of every block
-// ---------------------------------------------------------------------------
-
-// work of tile t = its entries + UN_FIXED; exclusive prefix inside scan
-// blocks of MG_SCAN_BLOCK tiles (MG_SCAN_PER consecutive tiles per thread,
-// the loads of 8 runs in flight together)
-__global__ __launch_bounds__(1024) void un_work_scan_kernel(MergeParams p)
+// The lane's WPL bitmap words of the count pass: their popcount; cleared.
+template <int WPL>
+__device__ __forceinline__ uint32_t un_count_words(uint32_t* bits)
 {
-    __shared__ uint64_t scan_lds[1024 / SG_WAVE + 1];
-    const uint32_t T = p.G * p.NT;
-    const uint64_t t0 = (uint64_t)blockIdx.x * MG_SCAN_BLOCK + (uint64_t)threadIdx.x * MG_SCAN_PER;
-    uint32_t c[MG_SCAN_PER];
-    uint64_t sum = 0;
+    const uint32_t lane = lane_id();
+    uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < MG_SCAN_PER; ++j) {
-        c[j] = 0;
-        const uint64_t t = t0 + j;
-        if (t >= T) continue;
-        const uint32_t g = (uint32_t)(t / p.NT), b = (uint32_t)(t % p.NT);
-        const uint32_t* rows = p.bnd + (uint64_t)g * p.n * (p.NT + 1) + b;
-        uint32_t E = 0;
-        for (uint32_t w0 = 0; w0 < p.n; w0 += 8) {
-            uint32_t x[8], y[8];
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) {
-                const uint32_t* row = rows + (uint64_t)(w0 + u < p.n ? w0 + u : 0u) * (p.NT + 1);
-                x[u] = row[0];
-                y[u] = row[1];
-            }
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u)
-                if (w0 + u < p.n && y[u] > x[u]) E += y[u] - x[u];
-        }
-        c[j] = E + UN_FIXED;
-        sum += c[j];
+    for (int q = 0; q < WPL; ++q) {
+        c += (uint32_t)__popc(bits[q * SG_WAVE + lane]);
+        bits[q * SG_WAVE + lane] = 0u;
     }
-    uint64_t tot;
-    uint64_t ex = block_excl_scan64<1024>(sum, scan_lds, &tot);
-#pragma unroll
-    for (int j = 0; j < MG_SCAN_PER; ++j) {
-        if (t0 + j < T) p.wcum[t0 + j] = ex;
-        ex += c[j];
-    }
-    if (threadIdx.x == 0) p.wblk[blockIdx.x] = tot;
-}
-
-// exclusive prefix of the scan blocks' totals (in place) and the total
-__global__ __launch_bounds__(1024) void un_work_top_kernel(MergeParams p)
-{
-    __shared__ uint64_t scan_lds[1024 / SG_WAVE + 1];
-    uint64_t carry = 0;
-    for (uint32_t base = 0; base < p.nscan; base += 1024) {
-        const uint32_t i = base + threadIdx.x;
-        const uint64_t v = i < p.nscan ? p.wblk[i] : 0ull;
-        uint64_t tot;
-        const uint64_t ex = block_excl_scan64<1024>(v, scan_lds, &tot);
-        if (i < p.nscan) p.wblk[i] = carry + ex;
-        carry += tot;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *p.wtotal = carry;
-}
-
-// Block k of W takes the tiles whose cumulative work starts in
-// [k*C/W, (k+1)*C/W): wstart[k] is its first tile, wstart[W] = T.  The
-// thread of tile t writes wstart[k] for k(t-1) < k <= k(t), with
-// k(t) = floor(cum[t]*W/C), so every k is written once.
-__global__ __launch_bounds__(256) void un_starts_kernel(MergeParams p)
-{
-    const uint32_t T = p.G * p.NT, W = p.nwaves;
-    const uint64_t C = *p.wtotal;
-    for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
-        const uint64_t cum = p.wcum[t] + p.wblk[t / MG_SCAN_BLOCK];
-        const uint64_t kt = C ? cum * W / C : 0;
-        int64_t kp = -1;
-        if (t > 0) {
-            const uint64_t cp = p.wcum[t - 1] + p.wblk[(t - 1) / MG_SCAN_BLOCK];
-            kp = (int64_t)(C ? cp * W / C : 0);
-        }
-        for (int64_t k = kp + 1; k <= (int64_t)kt && k < (int64_t)W; ++k) p.wstart[k] = t;
-        if (t == T - 1)
-            for (uint64_t k = kt + 1; k <= W; ++k) p.wstart[k] = T;
-    }
-}
-
-// exclusive prefix of the blocks' union sizes (in place); wave_tot[W] = |I|
-// and agg_off[G]
-__global__ __launch_bounds__(1024) void un_tot_scan_kernel(MergeParams p)
-{
-    __shared__ uint64_t scan_lds[1024 / SG_WAVE + 1];
-    uint64_t carry = 0;
-    for (uint32_t base = 0; base < p.nwaves; base += 1024) {
-        const uint32_t i = base + threadIdx.x;
-        const uint64_t v = i < p.nwaves ? p.wave_tot[i] : 0ull;
-        uint64_t tot;
-        const uint64_t ex = block_excl_scan64<1024>(v, scan_lds, &tot);
-        if (i < p.nwaves) p.wave_tot[i] = carry + ex;
-        carry += tot;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        p.wave_tot[p.nwaves] = carry;
-        p.agg_off[p.G] = carry;
-    }
+    return c;
 }
 
 // ---------------------------------------------------------------------------
 // the two passes
 // ---------------------------------------------------------------------------
 
-// LDS of the count pass: the bitmap of a tile's span, WPT words per thread,
-// and the run parts of the tile being counted and of the next one.
-template <int WPT>
-struct UnCountSmem {
-    uint32_t bits[WPT * UN_THREADS];
-    UnRuns R[2];
-    uint32_t red[UN_WAVES];
-};
-
-// One tile of the count pass.  Tile t's first window is in flight in kc
-// (its runs in Rc); wave 0's raw ranges of tile t+1 are in flight in rr.
-// Before counting tile t the block puts tile t+1's runs in Rn and issues
-// its first window into kn, and wave 0 issues the ranges of tile t+2.
-template <int WPT>
-__device__ __forceinline__ void un_count_tile(const MergeParams& p, UnCountSmem<WPT>& sm, uint32_t t, uint32_t te,
-                                              uint32_t glog, UnRuns& Rc, UnRuns& Rn, uint32_t& vc,
-                                              uint32_t (&kc)[UN_PER], uint32_t& vn, uint32_t (&kn)[UN_PER],
-                                              URaw& rr, uint64_t& total)
-{
-    constexpr int NCH = WPT / 4;
-    const uint32_t tid = threadIdx.x, lane = lane_id(), wid = tid / SG_WAVE;
-    const uint32_t n = p.n, span = 1u << p.tb;
-    const bool next = t + 1 < te; // uniform
-    if (next && tid < SG_WAVE) {
-        un_runs_put(p, rr, Rn);
-        un_runs_window(n, glog, Rn);
-        rr = un_runs_issue(p, t + 2);
-    }
-    __syncthreads();
-    uint32_t vb[UN_PER];
-    if (next) vn = un_window_load<VM_NONE>(p, Rn, glog, kn, vb);
-    const uint32_t klo = (t % p.NT) << p.tb;
-    uint32_t valid = vc;
-    while (true) {
-        bool bad = false;
-#pragma unroll
-        for (int i = 0; i < UN_PER; ++i) {
-            const uint32_t o = kc[i] - klo;
-            const bool has = (valid >> i) & 1u;
-            bad |= has && o >= span; // outside the tile: cannot happen for valid input
-            if (has && o < span) atomicOr(&sm.bits[o >> 5], 1u << (o & 31u));
-        }
-        if (ballot(bad) && lane == 0) report_error(kDevErrIndexRange);
-        __syncthreads(); // every thread is done reading Rc for this window
-        un_runs_advance(n, Rc); // wave 0
-        __syncthreads();
-        if (!Rc.more) break;
-        // a tile of more than one window: its later windows one at a time
-        un_runs_window(n, glog, Rc);
-        __syncthreads();
-        valid = un_window_load<VM_NONE>(p, Rc, glog, kc, vb);
-    }
-    uint32_t c = 0;
-#pragma unroll
-    for (int q = 0; q < NCH; ++q) {
-        uint4* w4 = reinterpret_cast<uint4*>(&sm.bits[4 * (q * UN_THREADS + tid)]);
-        const uint4 v = *w4;
-        c += (uint32_t)(__popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w));
-        *w4 = make_uint4(0u, 0u, 0u, 0u);
-    }
-    const uint32_t ws = wave_sum(c);
-    if (lane == 0) sm.red[wid] = ws;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < UN_WAVES; ++i) total += sm.red[i];
-}
-
-// Union size of each block's tiles (keys only).  The next tile's first
-// window is loading while a tile is counted.
-template <int WPT>
+// Union size of every tile (keys only) into tile_cnt.
+template <int WPL>
 __global__ __launch_bounds__(UN_THREADS) void un_count_kernel(MergeParams p)
 {
-    static_assert(WPT % 4 == 0, "the bitmap is read as 16-byte chunks");
-    __shared__ __align__(16) UnCountSmem<WPT> sm;
-    const uint32_t tid = threadIdx.x;
-    for (uint32_t i = tid; i < (uint32_t)(WPT * UN_THREADS); i += UN_THREADS) sm.bits[i] = 0u;
-    const uint32_t n = p.n, glog = un_glog(n);
-    const uint32_t k = blockIdx.x;
-    const uint32_t ts = p.wstart[k], te = p.wstart[k + 1];
-    uint64_t total = 0;
-    if (ts < te) { // uniform
-        URaw rr = {0ull, 0ull, 0u, 0u};
-        if (tid < SG_WAVE) {
-            un_runs_load(p, ts, sm.R[0]);
-            un_runs_window(n, glog, sm.R[0]);
-            rr = un_runs_issue(p, ts + 1);
+    constexpr int S = UN_SC;
+    __shared__ __align__(16) UnCountWave<WPL> smw[UN_WPB];
+    const uint32_t wid = uniform(threadIdx.x / SG_WAVE), lane = lane_id();
+    UnCountWave<WPL>& sm = smw[wid];
+    const uint32_t T = p.G * p.NT, NW = gridDim.x * UN_WPB;
+    const uint32_t span = 1u << p.tb;
+    uint32_t t = blockIdx.x * UN_WPB + wid;
+    if (t >= T) return; // uniform
+    for (uint32_t q = lane; q < (uint32_t)(WPL * SG_WAVE); q += SG_WAVE) sm.bits[q] = 0u;
+    un_stash<false>(p, sm.tb, un_raw_issue<false>(p, t));
+    for (; t < T; t += NW) { // uniform
+        wave_sync();
+        uint32_t pos = sm.tb.npos[lane], rem = sm.tb.nrem[lane];
+        wave_sync();
+        const URaw nxt = un_raw_issue<false>(p, t + NW < T ? t + NW : t); // unconditional: no register merge
+        const uint32_t klo = (t % p.NT) << p.tb;
+        uint32_t rtot = wave_sum(rem);
+        bool bad = false;
+        if (rtot == 0) { // uniform: an empty tile
+            un_stash<false>(p, sm.tb, nxt);
+        } else {
+            do {
+                uint32_t take, kr, key[S], vb[S], part[S];
+                uint64_t sbs[S];
+                const uint32_t E = un_window<S, VM_NONE>(p, sm.tb, pos, rem, rtot, take, kr, key, vb, part, sbs);
+                un_hold(key);
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    const uint32_t o = key[i] - klo;
+                    const bool has = lane + (uint32_t)i * SG_WAVE < E;
+                    bad |= has && o >= span; // outside the tile: cannot happen for valid input
+                    if (has && o < span) atomicOr(&sm.bits[un_phys<WPL>(o >> 5)], 1u << (o & 31u));
+                }
+                un_stash<false>(p, sm.tb, nxt);
+                pos += take;
+                rem -= take;
+                rtot -= E;
+            } while (rtot > 0);
         }
-        __syncthreads();
-        uint32_t ka[UN_PER], kb[UN_PER], vb[UN_PER], va = 0, vbb = 0;
-        va = un_window_load<VM_NONE>(p, sm.R[0], glog, ka, vb);
-        for (uint32_t t = ts; t < te; t += 2) {
-            un_count_tile<WPT>(p, sm, t, te, glog, sm.R[0], sm.R[1], va, ka, vbb, kb, rr, total);
-            if (t + 1 >= te) break;
-            un_count_tile<WPT>(p, sm, t + 1, te, glog, sm.R[1], sm.R[0], vbb, kb, va, ka, rr, total);
-        }
+        if (ballot(bad) && lane == 0) report_error(kDevErrIndexRange);
+        wave_sync();
+        const uint32_t U = wave_sum(un_count_words<WPL>(sm.bits));
+        if (lane == 0) p.tile_cnt[t] = U;
     }
-    if (tid == 0) p.wave_tot[k] = total;
 }
 
-// LDS of the write pass.
-template <int WPT>
-struct UnWriteSmem {
-    uint32_t bits[WPT * UN_THREADS];  // presence bitmap of the tile's span
-    uint16_t wpre[WPT * UN_THREADS];  // distinct keys before each bitmap word
-    float acc[UN_CAP];                // sums by rank
-    uint32_t keys[UN_CAP];            // keys by rank
-    uint32_t tot[(WPT >= 4 ? WPT / 4 : 1)][UN_WAVES]; // popcounts of a chunk round per wave
-    UnRuns R;
-};
+// The lane's WPL bitmap words of the write pass: their popcount, then the
+// exclusive prefix (from `below`) into the words' prefix halves.
+template <int WPL>
+__device__ __forceinline__ uint32_t un_words_count(const uint2* bw)
+{
+    const uint32_t lane = lane_id();
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) c += (uint32_t)__popc(bw[q * SG_WAVE + lane].x);
+    return c;
+}
 
-// Keys (and sums) of each block's tiles at the block's offset.
-template <int WPT, int VM>
+template <int WPL>
+__device__ __forceinline__ void un_words_prefix(uint2* bw, uint32_t below)
+{
+    const uint32_t lane = lane_id();
+    uint32_t e = below;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) {
+        const uint32_t x = bw[q * SG_WAVE + lane].x;
+        bw[q * SG_WAVE + lane].y = e;
+        e += (uint32_t)__popc(x);
+    }
+}
+
+template <int WPL>
+__device__ __forceinline__ void un_words_clear(uint2* bw)
+{
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) bw[q * SG_WAVE + lane] = make_uint2(0u, 0u);
+}
+
+// Keys (and sums) of every tile at its offset.
+template <int WPL, int VM>
 __global__ __launch_bounds__(UN_THREADS) void un_write_kernel(MergeParams p)
 {
+    constexpr int S = UN_SW;
     constexpr bool VALS = VM != VM_NONE;
-    constexpr int NCH = WPT >= 4 ? WPT / 4 : 1;
-    static_assert(WPT >= 4, "the write pass reads the bitmap as 16-byte chunks");
-    __shared__ __align__(16) UnWriteSmem<WPT> sm;
-    const uint32_t tid = threadIdx.x, lane = lane_id(), wid = tid / SG_WAVE;
-    for (uint32_t i = tid; i < (uint32_t)(WPT * UN_THREADS); i += UN_THREADS) sm.bits[i] = 0u;
-    for (uint32_t i = tid; i < (uint32_t)UN_CAP; i += UN_THREADS) sm.acc[i] = 0.0f;
-    const uint32_t n = p.n, glog = un_glog(n);
-    const uint32_t gmask = (1u << glog) - 1u;
-    const uint32_t my_w = tid >> glog, my_s = tid & gmask;
-    const uint32_t k = blockIdx.x;
-    const uint32_t ts = p.wstart[k], te = p.wstart[k + 1];
-    uint64_t out = p.wave_tot[k];
-    const uint64_t out_end = p.wave_tot[k + 1];
-    if (out_end < out || out_end > p.capacity) { // cannot happen: the union is no larger than the input
-        if (tid == 0) report_error(kDevErrPartition);
-        return; // uniform
-    }
+    constexpr uint32_t NONE = 0xffffffffu; // the offset of a slot with no entry (never inside a span)
+    __shared__ __align__(16) UnWriteWave<WPL> smw[UN_WPB];
+    const uint32_t wid = uniform(threadIdx.x / SG_WAVE), lane = lane_id();
+    UnWriteWave<WPL>& sm = smw[wid];
+    const uint32_t T = p.G * p.NT, NW = gridDim.x * UN_WPB;
     const uint32_t span = 1u << p.tb;
-    for (uint32_t t = ts; t < te; ++t) {
-        if (t % p.NT == 0 && tid == 0) p.agg_off[t / p.NT] = out;
-        un_runs_load(p, t, sm.R);
-        const uint32_t klo = (t % p.NT) << p.tb;
-        while (true) {
-            un_runs_window(n, glog, sm.R);
-            __syncthreads();
-            uint32_t key[UN_PER], vb[UN_PER];
-            uint32_t valid = un_window_load<VM>(p, sm.R, glog, key, vb);
-            if (sm.R.cut) { // uniform: some run continues after the window
-                // the window ends at the smallest last-loaded key of such a
-                // run; later keys go back to their runs.  The last loaded
-                // entry of run w is entry take_w - 1 of its part: slot
-                // (take_w - 1) / g of thread w g + (take_w - 1) % g.
-                if (my_w < n) {
-                    const uint32_t tk = sm.R.take[my_w];
-                    if (tk > 0 && tk < sm.R.rem[my_w] && ((tk - 1) & gmask) == my_s) {
-                        uint32_t lk = 0;
-#pragma unroll
-                        for (int i = 0; i < UN_PER; ++i)
-                            if ((uint32_t)i == ((tk - 1) >> glog)) lk = key[i];
-                        atomicMin(&sm.R.kmax, lk);
-                    }
-                }
-                __syncthreads();
-                const uint32_t kmax = sm.R.kmax;
-                uint32_t gone = 0;
-#pragma unroll
-                for (int i = 0; i < UN_PER; ++i) gone |= (key[i] > kmax ? 1u : 0u) << i;
-                gone &= valid;
-                valid &= ~gone;
-                if (gone) atomicAdd(&sm.R.drop[my_w], (uint32_t)__popc(gone));
-            }
-            // presence bitmap of the window's keys
-            uint32_t off[UN_PER];
-            uint32_t inr = 0; // slots whose key lies in the tile
-#pragma unroll
-            for (int i = 0; i < UN_PER; ++i) {
-                off[i] = key[i] - klo;
-                inr |= (off[i] < span ? 1u : 0u) << i;
-            }
-            if (ballot((valid & ~inr) != 0u) && lane == 0) report_error(kDevErrIndexRange); // cannot happen
-            valid &= inr;
-#pragma unroll
-            for (int i = 0; i < UN_PER; ++i)
-                if ((valid >> i) & 1u) atomicOr(&sm.bits[off[i] >> 5], 1u << (off[i] & 31u));
-            __syncthreads();
-            un_runs_advance(n, sm.R); // wave 0; read after the next barrier
-            // prefix popcounts of the bitmap words: 16-byte chunk q * 256 +
-            // tid per thread and round; a wave scan per round, the waves'
-            // round totals through LDS
-            uint32_t c[NCH][4], inc[NCH];
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                const uint4 bw = *reinterpret_cast<const uint4*>(&sm.bits[4 * (q * UN_THREADS + tid)]);
-                c[q][0] = __popc(bw.x);
-                c[q][1] = __popc(bw.y);
-                c[q][2] = __popc(bw.z);
-                c[q][3] = __popc(bw.w);
-                inc[q] = wave_incl_scan(c[q][0] + c[q][1] + c[q][2] + c[q][3]);
-                if (lane == SG_WAVE - 1) sm.tot[q][wid] = inc[q];
-            }
-            __syncthreads();
-            uint32_t U = 0;
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                uint32_t before = U; // everything of earlier rounds, then earlier waves of this round
-#pragma unroll
-                for (int v = 0; v < UN_WAVES; ++v) {
-                    const uint32_t x = sm.tot[q][v];
-                    if ((uint32_t)v < wid) before += x;
-                    U += x;
-                }
-                const uint32_t e0 = before + inc[q] - (c[q][0] + c[q][1] + c[q][2] + c[q][3]);
-                const uint32_t e1 = e0 + c[q][0], e2 = e1 + c[q][1], e3 = e2 + c[q][2];
-                *reinterpret_cast<uint2*>(&sm.wpre[4 * (q * UN_THREADS + tid)]) =
-                    make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-            }
-            __syncthreads();
-            // ranks; keys by rank; the sums, one wave after the other (the
-            // waves hold the runs in order, so each sum is in worker order)
-            uint32_t rk[UN_PER];
-#pragma unroll
-            for (int i = 0; i < UN_PER; ++i) {
-                rk[i] = 0;
-                if ((valid >> i) & 1u) {
-                    const uint32_t wd = off[i] >> 5;
-                    rk[i] = (uint32_t)sm.wpre[wd] + (uint32_t)__popc(sm.bits[wd] & ((1u << (off[i] & 31u)) - 1u));
-                    sm.keys[rk[i]] = key[i]; // every holder of a key writes the same value
-                }
-            }
-            if (VALS) {
-#pragma unroll
-                for (int v = 0; v < UN_WAVES; ++v) {
-                    if ((uint32_t)v == wid) {
-#pragma unroll
-                        for (int i = 0; i < UN_PER; ++i)
-                            if ((valid >> i) & 1u) atomicAdd(&sm.acc[rk[i]], un_value<VM>(vb[i]));
-                    }
-                    __syncthreads();
-                }
-            } else {
-                __syncthreads();
-            }
-            // the block's slot holds the keys its count pass found (a run
-            // that broke the input's order could make the passes disagree;
-            // nothing is written past the slot)
-            const uint64_t room = out_end - out;
-            const uint32_t lim = room < U ? (uint32_t)room : U;
-            for (uint32_t q = tid; q < U; q += UN_THREADS) {
-                if (q < lim) {
-                    p.agg_idx[out + q] = sm.keys[q];
-                    if (VALS) p.agg_val[out + q] = sm.acc[q];
-                }
-                if (VALS) sm.acc[q] = 0.0f;
-            }
-#pragma unroll
-            for (int q = 0; q < NCH; ++q)
-                *reinterpret_cast<uint4*>(&sm.bits[4 * (q * UN_THREADS + tid)]) = make_uint4(0u, 0u, 0u, 0u);
-            out += lim;
-            const bool more = sm.R.more != 0;
-            __syncthreads();
-            if (!more) break;
+    uint32_t t = blockIdx.x * UN_WPB + wid;
+    if (t >= T) return; // uniform
+    un_words_clear<WPL>(sm.bw);
+    for (uint32_t q = lane; q < (uint32_t)UN_CAP; q += SG_WAVE) sm.acc[q] = 0.0f;
+    un_stash<true>(p, sm.tb, un_raw_issue<true>(p, t));
+    for (; t < T; t += NW) { // uniform
+        wave_sync();
+        uint32_t pos = sm.tb.npos[lane], rem = sm.tb.nrem[lane];
+        uint64_t out = uniform64(sm.tb.nout), out_end = uniform64(sm.tb.nend);
+        wave_sync();
+        const URaw nxt = un_raw_issue<true>(p, t + NW < T ? t + NW : t); // unconditional: no register merge
+        if (out_end > p.capacity || out_end < out) { // cannot happen: the union is no larger than the input
+            if (lane == 0) report_error(kDevErrPartition);
+            out_end = out = p.capacity;
         }
+        if (t % p.NT == 0 && lane == 0) p.agg_off[t / p.NT] = out;
+        const uint32_t klo = (t % p.NT) << p.tb;
+        uint32_t rtot = wave_sum(rem);
+        if (rtot == 0) { // uniform: an empty tile
+            un_stash<true>(p, sm.tb, nxt);
+        } else {
+            do {
+                uint32_t take, kr, key[S], vb[S], part[S];
+                uint64_t sbs[S];
+                const uint32_t E = un_window<S, VM>(p, sm.tb, pos, rem, rtot, take, kr, key, vb, part, sbs);
+                un_hold(key);
+                // the key's offset in the tile's span; NONE for an empty slot
+                uint32_t off[S];
+                bool bad = false;
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    const bool has = lane + (uint32_t)i * SG_WAVE < E;
+                    const uint32_t o = key[i] - klo;
+                    bad |= has && o >= span; // outside the tile: cannot happen for valid input
+                    off[i] = has ? o : NONE;
+                }
+                if (ballot(bad) && lane == 0) report_error(kDevErrIndexRange);
+                uint32_t used = take;
+                if (rtot > (uint32_t)UN_CAP) { // uniform: a cut window
+                    // it ends at the smallest last-loaded key of a part it
+                    // cut short; that part's later keys, and every later key
+                    // of the other cut parts, go back to their runs
+                    const bool cut = take < rem;
+                    uint32_t lk = 0xffffffffu;
+                    if (cut) lk = p.idx[pos + take - 1];
+                    const uint32_t kmax = wave_min(lk);
+#pragma unroll
+                    for (int i = 0; i < S; ++i) {
+                        if (off[i] != NONE && key[i] > kmax) {
+                            atomicAdd(&sm.tb.drop[part[i]], 1u);
+                            off[i] = NONE;
+                        }
+                    }
+                    wave_sync();
+                    if (take > 0) used = take - sm.tb.drop[kr];
+                    // the part whose last loaded key is kmax keeps that entry,
+                    // so a window always uses one; only input changed while
+                    // it is read could break that: report it and take the
+                    // whole window, so the loop still ends
+                    if (wave_sum(used) == 0) { // uniform
+                        if (lane == 0) report_error(kDevErrUnsorted);
+                        used = take;
+                    }
+                }
+                pos += used;
+                rem -= used;
+                // presence bitmap of the window's keys
+#pragma unroll
+                for (int i = 0; i < S; ++i)
+                    if (off[i] < span) atomicOr(&sm.bw[un_phys<WPL>(off[i] >> 5)].x, 1u << (off[i] & 31u));
+                wave_sync();
+                // prefix popcounts of the words
+                const uint32_t c = un_words_count<WPL>(sm.bw);
+                const uint32_t inc = wave_incl_scan(c);
+                const uint32_t U = lane_value(inc, SG_WAVE - 1);
+                un_words_prefix<WPL>(sm.bw, inc - c);
+                wave_sync();
+                // ranks; keys by rank
+                uint32_t rk[S];
+#pragma unroll
+                for (int i = 0; i < S; ++i) {
+                    rk[i] = 0;
+                    if (off[i] < span) {
+                        const uint2 d = sm.bw[un_phys<WPL>(off[i] >> 5)];
+                        rk[i] = d.y + (uint32_t)__popc(d.x & ((1u << (off[i] & 31u)) - 1u));
+                        sm.keys[rk[i]] = key[i]; // every holder of a key writes the same value
+                    }
+                }
+                // the sums, slot by slot and, inside a slot, part by part:
+                // a part's keys are distinct, so a plain read-add-write of
+                // one part's lanes has no race, and the parts come in
+                // worker order, so every sum is taken in worker order
+                if (VALS) {
+                    un_hold(vb);
+                    uint32_t pcb = 0; // marks in earlier slots: the part of the slot's first entry
+#pragma unroll
+                    for (int i = 0; i < S; ++i) {
+                        const uint64_t sw = sbs[i];
+                        if ((uint32_t)i * SG_WAVE < E) { // uniform
+                            const uint64_t inner = sw & ~(1ull << 63); // part ends before the slot's last lane
+                            if (inner == 0) { // one part: every lane at once
+                                if (off[i] < span) sm.acc[rk[i]] += un_value<VM>(vb[i]);
+                            } else {
+                                const uint32_t nr = 1u + popc64(inner);
+                                for (uint32_t r = 0; r < nr; ++r) { // uniform
+                                    if (off[i] < span && part[i] == pcb + r) sm.acc[rk[i]] += un_value<VM>(vb[i]);
+                                }
+                            }
+                        }
+                        pcb += popc64(sw);
+                    }
+                }
+                un_stash<true>(p, sm.tb, nxt);
+                wave_sync();
+                // the tile's slot holds the keys its count found (a run that
+                // broke the input's order could make the passes disagree;
+                // nothing is written past the slot)
+                const uint64_t room = out_end - out;
+                const uint32_t lim = room < U ? (uint32_t)room : U;
+                uint32_t* const oi = p.agg_idx + out;
+                float* const ov = p.agg_val + out;
+#pragma unroll
+                for (int m = 0; m < S; ++m) {
+                    const uint32_t q = lane + (uint32_t)m * SG_WAVE;
+                    if ((uint32_t)m * SG_WAVE < U) { // uniform
+                        if (q < lim) {
+                            oi[q] = sm.keys[q];
+                            if (VALS) ov[q] = sm.acc[q];
+                        }
+                        if (VALS && q < U) sm.acc[q] = 0.0f;
+                    }
+                }
+                un_words_clear<WPL>(sm.bw);
+                out += lim;
+                rtot = wave_sum(rem);
+                wave_sync();
+            } while (rtot > 0);
+        }
+        if (out != out_end && lane == 0) report_error(kDevErrPartition); // the two passes disagree: cannot happen
     }
-    if (out != out_end && tid == 0) report_error(kDevErrPartition); // the two passes disagree: cannot happen
 }
 
 } // namespace sg
