@@ -3,8 +3,9 @@
 // 3.1 Def. 8).
 //
 // The union and every pairwise intersection come, for up to 16 workers and
-// 16 parts when the lists hold at least one entry per 16 * 32 keys of the
-// key space per worker on average, from the dense pass of sg_statsd.hip
+// 16 parts when the lists hold at least one entry per 2 * 32 keys of the
+// key space per worker on average (or the bitmaps take at most 64 MB), from
+// the dense pass of sg_statsd.hip
 // (per-worker bitmaps of the whole key space, which also give each worker's
 // counts per part and per class); otherwise, for up to 16 workers and 16
 // hash classes, from the window pass of sg_statsw.hip (per-worker bitmaps of
@@ -138,7 +139,14 @@ static bool stats_windowed(uint32_t n, uint32_t P, bool hashed)
 // no more than 16 times the entries (n * ceil(M/32) words <= 16 * total).
 static bool stats_dense(uint32_t n, uint64_t M, uint64_t total, uint32_t P)
 {
-    return total > 0 && n <= DN_MAXN && P <= DN_MAXP && (uint64_t)n * ceil_div(M, 32) <= 16ull * total;
+    // the dense pass zeroes, writes and reads n bitmaps of the key space; the
+    // window pass reads the lists once (with a few instructions per entry):
+    // the bitmaps must be small next to the lists for the dense pass to win
+    // (measured: 0.6 bitmap words per entry, dense 2x faster; 3.1 words per
+    // entry, windows 1.4x faster), unless the bitmaps are small anyway (up to
+    // 64 MB: a few microseconds of traffic, fewer steps than the windows)
+    const uint64_t words = (uint64_t)n * ceil_div(M, 32);
+    return total > 0 && n <= DN_MAXN && P <= DN_MAXP && (words <= 2ull * total || words <= (16ull << 20));
 }
 
 static void stats_setup(MergeParams* p, uint32_t n, uint64_t M, uint64_t total, uint32_t P, bool windowed)
@@ -179,11 +187,6 @@ static uint64_t stats_carve(Carver& c, MergeParams* p, uint32_t P, StatsCounts* 
         p->bnd = c.take<uint32_t>(R * (p->NT + 1));
         p->nqsets = 1;
         p->queue = c.take<uint32_t>((uint64_t)MG_NQ * MG_QSTRIDE);
-        sw->work = c.take<uint32_t>(p->NT);
-        sw->wcum = c.take<uint64_t>(p->NT);
-        sw->wblk = c.take<uint64_t>(p->nscan);
-        sw->wstart = c.take<uint32_t>(SW_MAX_WAVES + 1);
-        sw->wtotal = c.take<uint64_t>(1);
         sw->rows = c.take<uint64_t>((uint64_t)SW_MAX_WAVES * p->st_row);
     } else {
         merge_carve(c, p, MODE_STATS);
@@ -234,15 +237,6 @@ static int stats_window_run(MergeParams& p, SwParams& sw, hipStream_t st, uint64
     mg_bnd_kernel<<<p.nchunks_max < 65536 ? p.nchunks_max : 65536, 512, 0, st>>>(p);
     SG_TRY_LAUNCH();
     sw.m = p;
-    const unsigned tgrid = (unsigned)(ceil_div(T, 256) < 2048 ? ceil_div(T, 256) : 2048);
-    sw_weight_kernel<<<tgrid, 256, 0, st>>>(sw);
-    SG_TRY_LAUNCH();
-    sw_scan_local_kernel<<<p.nscan, 1024, 0, st>>>(sw);
-    SG_TRY_LAUNCH();
-    sw_scan_top_kernel<<<1, 1024, 0, st>>>(sw, p.nscan);
-    SG_TRY_LAUNCH();
-    sw_starts_kernel<<<tgrid, 256, 0, st>>>(sw, W);
-    SG_TRY_LAUNCH();
     if (ix == 0) {
         if (hashed) sw_stats_kernel<8, true><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);
         else sw_stats_kernel<8, false><<<(unsigned)grid, SW_THREADS, 0, st>>>(sw);

@@ -984,12 +984,15 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
             SG_TRY_LAUNCH();
             probe_end(SG_PROBE_TOPK_FILTER, st);
         } else {
+            // the re-filter of a missed band (rare): a smaller grid, so the
+            // usual launch, which finds nothing to do, ends at once
+            const unsigned rgrid = fgrid < 2048u ? fgrid : 2048u;
             if (p.bf16) {
-                if (rows_aligned) topk_filter_kernel<8, true, true><<<fgrid, TK_THREADS, 0, st>>>(p);
-                else topk_filter_kernel<8, false, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+                if (rows_aligned) topk_filter_kernel<8, true, true><<<rgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<8, false, true><<<rgrid, TK_THREADS, 0, st>>>(p);
             } else {
-                if (rows_aligned) topk_filter_kernel<4, true, true><<<fgrid, TK_THREADS, 0, st>>>(p);
-                else topk_filter_kernel<4, false, true><<<fgrid, TK_THREADS, 0, st>>>(p);
+                if (rows_aligned) topk_filter_kernel<4, true, true><<<rgrid, TK_THREADS, 0, st>>>(p);
+                else topk_filter_kernel<4, false, true><<<rgrid, TK_THREADS, 0, st>>>(p);
             }
             SG_TRY_LAUNCH();
         }

@@ -61,14 +61,16 @@ __device__ __forceinline__ float un_value(uint32_t b)
     return __uint_as_float(VM == VM_BF16 ? b << 16 : b);
 }
 
-// Window tables and the next tile's parts, shared by both passes.
-template <int S>
+// Window tables and the next tile's parts, shared by both passes (WK: with
+// the run of every part, for callers that need it).
+template <int S, bool WK = false>
 struct UnTables {
     uint32_t sb[2 * S];        // bit j set where entry j + 1 of the window begins a part
     uint32_t base[SG_WAVE];    // k-th non-empty part: its first position minus its window start
     uint32_t drop[SG_WAVE];    // entries of the k-th part returned by a cut window
     uint32_t npos[SG_WAVE];    // the next tile: lane w's part, its position
     uint32_t nrem[SG_WAVE];    // and length
+    uint32_t wk[WK ? SG_WAVE : 1]; // k-th non-empty part: its run (worker)
     uint64_t nout, nend;       // the next tile's output slot (write pass)
 };
 
@@ -153,8 +155,8 @@ __device__ __forceinline__ void un_raw_put(const MergeParams& p, const URaw& r, 
 // copied between registers at the top of the tile loop, and a copy of a
 // pending load waits for every vector memory operation in flight, the
 // tile's output stores included (loads and stores share one counter).
-template <bool WRITE, int S>
-__device__ __forceinline__ void un_stash(const MergeParams& p, UnTables<S>& tb, const URaw& nxt)
+template <bool WRITE, int S, bool WK>
+__device__ __forceinline__ void un_stash(const MergeParams& p, UnTables<S, WK>& tb, const URaw& nxt)
 {
     // every vector memory operation issued before the window's loads is
     // done once those loads are (they complete in order), so this wait is
@@ -185,8 +187,8 @@ __device__ __forceinline__ void un_stash(const MergeParams& p, UnTables<S>& tb, 
 // non-empty parts, in worker order; `kr` is the lane's own), sbs[i] the
 // slot's part-end marks.  The loaded registers are not touched here, so the
 // loads stay in flight together until their first use.
-template <int S, int VM>
-__device__ __forceinline__ uint32_t un_window(const MergeParams& p, UnTables<S>& tb, uint32_t pos, uint32_t rem,
+template <int S, int VM, bool WK>
+__device__ __forceinline__ uint32_t un_window(const MergeParams& p, UnTables<S, WK>& tb, uint32_t pos, uint32_t rem,
                                               uint32_t rtot, uint32_t& take, uint32_t& kr, uint32_t (&key)[S],
                                               uint32_t (&vb)[S], uint32_t (&part)[S], uint64_t (&sbs)[S])
 {
@@ -207,6 +209,7 @@ __device__ __forceinline__ uint32_t un_window(const MergeParams& p, UnTables<S>&
     if (take > 0) {
         if (pre > 0) atomicOr(&tb.sb[(pre - 1) >> 5], 1u << ((pre - 1) & 31u)); // the entry before the part
         tb.base[kr] = pos - pre;
+        if (WK) tb.wk[kr] = lane;
     }
     wave_sync();
     const uint32_t last = (uint32_t)(p.total - 1); // total > 0 here
