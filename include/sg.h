@@ -213,10 +213,10 @@ int sg_hash_partition(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uin
  * every output entry) is a fixed device array of the library,
  * SG_PARTITION_SCRATCH_BYTES (16 MiB) per GPU, held until the process ends;
  * the call itself allocates nothing.  It needs 4 * (n + 1) +
- * 4 * P * (ceil(total / 4096) + n) bytes, plus 4 * total when D >= 2 (each
+ * 4 * P * (ceil(total / 2048) + n) bytes, plus 4 * total when D >= 2 (each
  * part rounded up to 256 bytes, plus 256); larger inputs return SG_ECAPACITY
- * before any launch (for P = 16 that is over 10^9 scalar entries, for P = 256
- * about 6.7 * 10^7; rows with D >= 2 up to about 4 * 10^6).
+ * before any launch (for P = 16 that is over 5 * 10^8 scalar entries, for
+ * P = 256 about 3.3 * 10^7; rows with D >= 2 up to about 4 * 10^6).
  * Every call on one GPU uses that GPU's one array: calls that overlap on one
  * GPU (two streams, or two host threads) race and give wrong results; order
  * them on one stream.  The array keeps the last call's contents; a call

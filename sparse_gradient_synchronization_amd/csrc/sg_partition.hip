@@ -5,7 +5,7 @@
 // server.  Zen realises it with slot memory, rehashing and an atomic serial
 // area (Algorithm 1) because its extraction then runs nonzero() over the slot
 // memory.  Here the same membership comes from a stable multi-split with no
-// slot memory and no collisions: per 4096-entry tile a histogram of h0, one
+// slot memory and no collisions: per 2048-entry tile a histogram of h0, one
 // scan of the per-(tile, partition) counts, and a scatter that ranks entries
 // inside the tile with wave64 ballots, stages them partition-sorted in LDS and
 // writes each partition's run with consecutive lanes on consecutive
@@ -16,7 +16,7 @@
 namespace sg {
 
 constexpr int PT_THREADS = 256;
-constexpr int PT_TILE = 4096; // entries per tile
+constexpr int PT_TILE = 2048; // entries per tile (2048: twice the blocks per CU of 4096, whose LDS staging allowed three)
 constexpr int PT_WAVES = PT_THREADS / SG_WAVE;
 constexpr int PT_STRIPS = PT_TILE / PT_THREADS; // 64-entry strips per wave
 
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
     __shared__ uint32_t keys_s[PT_TILE];
     __shared__ VT vals_s[STAGE_VALS ? PT_TILE : 1];
     __shared__ uint8_t part_s[PT_TILE];
-    __shared__ uint16_t rank_s[PT_TILE]; // input order -> staging position
+    __shared__ uint16_t rank_s[STAGE_VALS ? 1 : PT_TILE]; // rows: input order -> staging position
     __shared__ uint32_t wave_cnt[PT_WAVES][256];
     __shared__ uint32_t lps[256];   // staging start of partition q
     __shared__ uint32_t dbase[256]; // global destination of the tile's run of q
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(PT_THREADS) void part_scatter_kernel(PartParams p)
             keys_s[sp] = key_r[s];
             part_s[sp] = (uint8_t)q;
             if (STAGE_VALS) vals_s[sp] = val_r[s];
-            rank_s[le] = (uint16_t)sp;
+            if (!STAGE_VALS) rank_s[le] = (uint16_t)sp;
         }
     }
     __syncthreads();

@@ -58,7 +58,7 @@ def test_noalloc_full_dgc_sized_partition_then_small():
 
 def test_noalloc_refuses_oversized_input():
     need_gpu()
-    # 2^20 entries over 256 partitions need 256 * 260 tiles of counts (fits);
+    # 2^20 entries over 256 partitions need 256 * 520 tiles of counts (fits);
     # rows of 2^23 entries need 32 MiB of sources (does not)
     idx = torch.zeros(1 << 23, dtype=torch.int32, device="cuda")
     val = torch.zeros((1 << 23, 2), dtype=torch.float32, device="cuda")
