@@ -208,10 +208,19 @@ __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
     __shared__ uint64_t offs[257];
     load_agg_offsets(e, offs);
     const uint32_t P = e.L.P;
-    const uint64_t NW = e.L.NW, W = e.L.W;
+    const uint64_t NW = e.L.NW;
+    const uint32_t wsh = (uint32_t)__builtin_ctzll(e.L.W); // W = 32 NCW, a power of two
     const uint64_t nagg = offs[P];
     const uint64_t tid = blockIdx.x * 256ull + threadIdx.x, nthreads = (uint64_t)gridDim.x * 256;
-    for (uint64_t i = tid; i < nagg; i += nthreads) {
+    for (uint64_t i0 = blockIdx.x * 256ull; i0 < nagg; i0 += nthreads) { // uniform per block
+        const uint64_t i = i0 + threadIdx.x;
+        const uint64_t ic = i < nagg ? i : nagg - 1;
+        // the entry's key, and the one before it from the next lane down
+        // (lane 0 loads its own)
+        const uint32_t key = e.agg_idx[ic];
+        const uint32_t up = (uint32_t)__shfl_up((int)key, 1, SG_WAVE);
+        const uint32_t before = lane_id() > 0 ? up : (ic > 0 ? e.agg_idx[ic - 1] : 0u);
+        if (i >= nagg) continue;
         uint32_t lo = 0, hi = P; // largest p with offs[p] <= i
         while (lo + 1 < hi) {
             const uint32_t mid = (lo + hi) >> 1;
@@ -221,28 +230,29 @@ __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
         const uint32_t p = lo;
         const uint64_t s = offs[p], en = offs[p + 1] > s ? offs[p + 1] : s;
         if (i < s || i >= en) continue; // inconsistent offsets
-        uint64_t win = e.agg_idx[i] / W;
+        uint64_t win = (uint64_t)key >> wsh;
         if (win >= NW) win = NW - 1;
         int64_t prev = -1;
         if (i > s) {
-            const uint64_t pw = e.agg_idx[i - 1] / W;
+            const uint64_t pw = (uint64_t)before >> wsh;
             prev = (int64_t)(pw < NW ? pw : NW - 1);
         }
         for (int64_t w = prev + 1; w <= (int64_t)win; ++w) e.cur[(uint64_t)w * P + p] = i;
         if (i == en - 1)
             for (uint64_t w = win + 1; w <= NW; ++w) e.cur[w * P + p] = en;
     }
-    // cursors of empty partitions
-    for (uint64_t i = tid; i < (NW + 1) * P; i += nthreads) {
-        const uint32_t p = (uint32_t)(i % P);
+    // cursors of empty partitions ((NW + 1) P < 2^32: NW < 2^24, P <= 256)
+    const uint32_t tid32 = (uint32_t)tid, nth32 = (uint32_t)nthreads;
+    for (uint32_t i = tid32; i < (uint32_t)((NW + 1) * P); i += nth32) {
+        const uint32_t p = i % P;
         if (offs[p + 1] <= offs[p]) e.cur[i] = offs[p];
     }
     // shared bitmap words
-    for (uint64_t i = tid; i < NW * P; i += nthreads) {
-        const uint64_t w = i / P;
-        const uint32_t p = (uint32_t)(i % P);
+    for (uint32_t i = tid32; i < (uint32_t)(NW * P); i += nth32) {
+        const uint32_t w = i / P;
+        const uint32_t p = i % P;
         if (w == 0) continue;
-        const uint32_t a = e.q.cpre[w * P + p];
+        const uint32_t a = e.q.cpre[(uint64_t)w * P + p];
         if ((a & 31u) == 0 || a >= e.q.class_size[p]) continue;
         const uint64_t gw = e.q.word_off[p] + (a >> 5);
         if (gw < e.bitmap_words) e.bitmap[gw] = 0u;
