@@ -212,9 +212,11 @@ def build_workload(name, torch, sg, gen):
             chk(L.sg_decode(vp(bitmap), words, vp(cmap), cmap.numel(), M, P, vp(dec_idx), total, vp(dec_off), vp(ws_d),
                             ws_d.numel(), stream()), "sg_decode")
 
+        ws_sc = torch.empty(L.sg_scatter_dense_workspace_bytes(M, P), dtype=torch.uint8, device=dev)
+
         def scat():
-            chk(L.sg_scatter_dense(vp(agg_idx), vp(agg_val), D, vp(agg_off), P, total, M, vp(pull_dense), stream()),
-                "sg_scatter_dense")
+            chk(L.sg_scatter_dense(vp(agg_idx), vp(agg_val), D, vp(agg_off), P, total, M, vp(pull_dense), vp(ws_sc),
+                                   ws_sc.numel(), stream()), "sg_scatter_dense")
 
         def fmt():
             out = (C.c_uint64 * 7)()
@@ -285,7 +287,7 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "aggregate": (3, "un_write_kernel", ["sg_union.hip", "sg_merge.hip", "sg_aggregate.hip"]),
     "encode": (4, "enc_kernel", ["sg_encode.hip"]),
     "decode": (9, "dec_emit_kernel", ["sg_decode.hip"]),
-    "scatter_dense": (10, "scatter_kernel", ["sg_decode.hip"]),
+    "scatter_dense": (10, "scatter_window_kernel", ["sg_decode.hip"]),  # scatter_kernel for rows (D > 1)
     "skip_reduce_scatter": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
 }
 COMMON_SOURCES = ["sg_device.h", "sg_host.h"]
@@ -452,9 +454,10 @@ def pull_side(W, L, torch, steps):
         nbytes = algorithmic_bytes(W, nm)
         gbps = nbytes / (kms * 1e-3) / 1e9
         ms = sum(a[s].elapsed_time(b[s]) for s in range(steps)) / steps
-        out[nm] = {"ms": ms, "kernel": PROBES[nm][1], "kernel_ms": kms, "kernel_algorithmic_bytes": nbytes,
+        kname = "scatter_kernel" if nm == "scatter_dense" and W.get("D", 1) > 1 else PROBES[nm][1]
+        out[nm] = {"ms": ms, "kernel": kname, "kernel_ms": kms, "kernel_algorithmic_bytes": nbytes,
                    "kernel_GBps": gbps, "kernel_frac": gbps / HBM_PEAK_GBS}
-        if nm == "scatter_dense":  # the whole call also zero-fills the dense tensor
+        if nm == "scatter_dense":  # the whole call: the dense tensor written, the aggregate read
             U = int(W["agg_off"][-1].item())
             call_bytes = W["M"] * 4 * W.get("D", 1) + U * (4 + 4 * W.get("D", 1))
             out[nm]["call_algorithmic_bytes"] = call_bytes
@@ -625,8 +628,11 @@ def algorithmic_bytes(W, stage):
         return stage_bytes(W, stage)
     if stage == "decode":  # the bitmap words read, the indices written
         return int(W["word_off"][-1].item()) * 4 + union_size(W) * 4
-    if stage == "scatter_dense":  # the scatter pass: the aggregate read, its values written in place
-        return union_size(W) * (4 + 8 * W.get("D", 1))
+    if stage == "scatter_dense":
+        D = W.get("D", 1)
+        if D == 1:  # the window pass: the aggregate read, every dense element written once
+            return W["M"] * 4 + union_size(W) * 8
+        return union_size(W) * (4 + 8 * D)  # rows: the aggregate read, its rows written in place
     raise KeyError(stage)
 
 

@@ -333,7 +333,14 @@ int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg
  * values are copied to their index (for an aggregate: off = agg_off).
  * capacity is the number of entries d_idx holds (offsets are clamped to it).
  * D == 0 only zeroes.  Indices must be distinct and below M (an index >= M is
- * skipped and recorded for sg_device_error).
+ * skipped and recorded for sg_device_error).  Entries in ascending key order
+ * within each partition [off[p], off[p+1]) (as sg_aggregate writes them) take
+ * the fast path for D == 1: every dense element written once by 16-byte
+ * stores; other orders give the same result through a per-entry pass.
+ *   d_ws  sg_scatter_dense_workspace_bytes(M, P) bytes: a flag word per
+ *         block of the cursor pass, and per (key window of 4096, partition)
+ *         the partition's first entry in the window
+ * Limits: 1 <= P <= 256, 1 <= M < 2^32, D <= 65536.
  *
  * sg_format_sizes: bytes of an aggregate (d_agg_idx, d_agg_off as produced
  * by sg_aggregate) with D fp32 values per index and 4-byte indices, written
@@ -352,8 +359,9 @@ size_t sg_decode_workspace_bytes(uint64_t M, uint32_t P);
 int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const void* d_cmap, size_t cmap_bytes, uint64_t M,
               uint32_t P, uint32_t* d_out_idx, uint64_t capacity, uint64_t* d_out_off, void* d_ws, size_t ws_bytes,
               void* stream);
+size_t sg_scatter_dense_workspace_bytes(uint64_t M, uint32_t P);
 int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint32_t D, const uint64_t* d_off, uint32_t P,
-                     uint64_t capacity, uint64_t M, float* d_dense, void* stream);
+                     uint64_t capacity, uint64_t M, float* d_dense, void* d_ws, size_t ws_bytes, void* stream);
 size_t sg_format_sizes_workspace_bytes(uint64_t M);
 int sg_format_sizes(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t capacity, uint64_t M, uint32_t P,
                     uint32_t D, const void* d_cmap, size_t cmap_bytes, uint64_t* h_out, void* d_ws, size_t ws_bytes,

@@ -84,7 +84,8 @@ SIGNATURES = {
     "sg_stats_workspace_bytes": (_sz, [_u32, _u64, _u64, _u32]),
     "sg_decode_workspace_bytes": (_sz, [_u64, _u32]),
     "sg_decode": (_int, [_vp, _u64, _vp, _sz, _u64, _u32, _vp, _u64, _vp, _vp, _sz, _vp]),
-    "sg_scatter_dense": (_int, [_vp, _vp, _u32, _vp, _u32, _u64, _u64, _vp, _vp]),
+    "sg_scatter_dense_workspace_bytes": (_sz, [_u64, _u32]),
+    "sg_scatter_dense": (_int, [_vp, _vp, _u32, _vp, _u32, _u64, _u64, _vp, _vp, _sz, _vp]),
     "sg_format_sizes_workspace_bytes": (_sz, [_u64]),
     "sg_format_sizes": (_int, [_vp, _vp, _u64, _u64, _u32, _u32, _vp, _sz, _vp, _vp, _sz, _vp]),
     "sg_stats": (_int, [_vp, _vp, _u32, _u64, _u64, _u32, _vp, _sz, C.POINTER(StatsOut), _vp, _sz, _vp]),
@@ -295,8 +296,9 @@ def sg_scatter_dense(idx: torch.Tensor, val, off: torch.Tensor, M: int, D: int =
     dense = out if out is not None else torch.empty((M, D) if D > 1 else (max(M, 1),), dtype=torch.float32,
                                                         device=idx.device)
     v = None if val is None else _contig(val.float())
+    ws = _ws(lib().sg_scatter_dense_workspace_bytes(M, P), idx.device)
     _check(lib().sg_scatter_dense(_p(idx.contiguous()), _p(v), D, _p(off.contiguous()), P, idx.numel(), M,
-                                  _p(dense), _stream()), "sg_scatter_dense")
+                                  _p(dense), _p(ws), ws.numel(), _stream()), "sg_scatter_dense")
     return dense
 
 

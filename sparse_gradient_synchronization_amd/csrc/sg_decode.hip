@@ -297,7 +297,27 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
     }
 }
 
-// Pull-side scatter: dense [M][D] zero except entries [off[0], off[P])
+// Pull-side scatter: dense [M][D] zero except entries [off[0], off[P]).
+//
+// Scalar values (D == 1) go through key windows of SC_W keys, since an
+// aggregate's partitions each hold ascending keys:
+//   cursors  one streaming pass over the entries: for each (window,
+//            partition), the first entry of the partition at or after the
+//            window's first key; a partition whose keys do not ascend marks
+//            its pass block's flag word;
+//   window   a block per window zeroes an LDS copy of the window, drops the
+//            window's entries of every partition into it and writes the
+//            window out with 16-byte stores: every dense element is written
+//            once, by coalesced stores;
+//   fix      if any flag word is set, the plain per-entry scatter over the
+//            windows' output (values at distinct keys are written again,
+//            so the result is the same whatever the cursors were).
+// Rows (D > 1) zero the tensor and copy each row with a wave.
+constexpr int SC_W = 4096;          // keys per window
+constexpr int SC_CUR_BLOCKS = 4096; // blocks of the cursor pass, one flag word each
+constexpr int SC_FIX_BLOCKS = 128;  // blocks of the per-entry pass
+constexpr int SC_KB = 8;            // entries per thread per load round of the window kernel
+
 struct ScatterParams {
     const uint32_t* idx;
     const float* val;
@@ -305,21 +325,255 @@ struct ScatterParams {
     uint32_t P, D;
     uint64_t capacity, M;
     float* dense;
+    uint64_t NW;   // windows of SC_W keys over [0, M)
+    uint64_t* cur; // [NW+1][P] first entry of partition p at or after key w SC_W
+    uint32_t* bad; // [SC_CUR_BLOCKS] nonzero: the cursors cannot be trusted
+    uint32_t nbad; // flag words written: the blocks of the cursor pass
 };
 
-__global__ __launch_bounds__(256) void scatter_zero_kernel(ScatterParams s)
+// offsets clamped to the entries held; false if they do not ascend
+__device__ __forceinline__ bool scatter_offsets(const ScatterParams& s, uint64_t* offs)
 {
-    const uint64_t words = s.M * (s.D ? s.D : 1);
-    const uint64_t n4 = words / 4;
-    float4* d4 = reinterpret_cast<float4*>(s.dense);
-    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * 256)
-        d4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (uint64_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < words; i += (uint64_t)gridDim.x * 256)
-        s.dense[i] = 0.f;
+    for (uint32_t p = threadIdx.x; p <= s.P; p += blockDim.x) offs[p] = s.off[p] < s.capacity ? s.off[p] : s.capacity;
+    __syncthreads();
+    bool ok = true;
+    for (uint32_t p = threadIdx.x; p < s.P; p += blockDim.x) ok = ok && offs[p] <= offs[p + 1];
+    return __syncthreads_and(ok) != 0;
 }
 
+// cursors that entry i (key, after prev in its partition p; first: no entry
+// before it) sets: it is the first of p in windows (win(prev), win(key)], and
+// the last entry also closes the windows after its own
+__device__ __forceinline__ void scatter_cursors_of(const ScatterParams& s, uint32_t wsh, uint32_t p, uint64_t i,
+                                                   uint32_t key, uint32_t prev, bool first, bool last, uint64_t pe)
+{
+    const uint32_t NW = (uint32_t)s.NW, P = s.P;
+    uint32_t win = key >> wsh;
+    if (win >= NW) win = NW - 1;
+    uint32_t w = 0;
+    if (!first) {
+        const uint32_t pw = prev >> wsh;
+        w = (pw < NW ? pw : NW - 1) + 1;
+    }
+    for (; w <= win; ++w) s.cur[(uint64_t)w * P + p] = i;
+    if (last)
+        for (w = win + 1; w <= NW; ++w) s.cur[(uint64_t)w * P + p] = pe;
+}
+
+// Chunks of SC_CV * SC_CR * 256 entries: thread t takes SC_CR runs of SC_CV
+// consecutive entries, run r at c0 + r SC_CV 256 + t SC_CV, so that one load
+// instruction reads 256 contiguous entries of a wave (one 16-byte load per
+// lane when VEC: d_idx 16-byte aligned).
+constexpr int SC_CV = 4;
+constexpr int SC_CR = 2;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void scatter_cursor_kernel(ScatterParams s)
+{
+    constexpr uint32_t CH = SC_CV * SC_CR * 256;
+    __shared__ uint64_t offs[257];
+    __shared__ uint32_t lastk[2][256 / SG_WAVE][SC_CR]; // lane 63's last key per wave and run, by chunk parity
+    bool bad = !scatter_offsets(s, offs);
+    const uint32_t P = s.P;
+    const uint32_t NW = (uint32_t)s.NW; // below 2^21
+    const uint32_t wsh = (uint32_t)__builtin_ctz((uint32_t)SC_W);
+    const uint64_t first = offs[0], nagg = offs[P];
+    const uint32_t lane = lane_id(), wv = threadIdx.x / SG_WAVE;
+    if (!bad) {
+        uint32_t par = 0;
+        // chunks start at multiples of SC_CV (aligned runs); entries before
+        // `first` are not the caller's
+        for (uint64_t c0 = (first & ~(uint64_t)(SC_CV - 1)) + blockIdx.x * (uint64_t)CH; c0 < nagg;
+             c0 += (uint64_t)gridDim.x * CH, par ^= 1u) {
+            uint32_t key[SC_CR][SC_CV];
+#pragma unroll
+            for (int r = 0; r < SC_CR; ++r) {
+                const uint64_t g0 = c0 + (uint64_t)r * SC_CV * 256 + threadIdx.x * SC_CV;
+                if (VEC && g0 + SC_CV <= s.capacity) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(s.idx + g0);
+                    key[r][0] = v.x;
+                    key[r][1] = v.y;
+                    key[r][2] = v.z;
+                    key[r][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < SC_CV; ++c) key[r][c] = s.idx[g0 + c < s.capacity ? g0 + c : s.capacity - 1];
+                }
+            }
+            const uint32_t pk0 = threadIdx.x == 0 && c0 > 0 ? s.idx[c0 - 1] : 0u; // the entry before the chunk
+            uint32_t up[SC_CR];
+#pragma unroll
+            for (int r = 0; r < SC_CR; ++r) {
+                up[r] = (uint32_t)__shfl_up((int)key[r][SC_CV - 1], 1, SG_WAVE);
+                if (lane == SG_WAVE - 1) lastk[par][wv][r] = key[r][SC_CV - 1];
+            }
+            __syncthreads();
+            uint32_t p = 0, hi = P;
+            uint64_t ps = 0, pe = 0;
+#pragma unroll
+            for (int r = 0; r < SC_CR; ++r) {
+                const uint64_t g0 = c0 + (uint64_t)r * SC_CV * 256 + threadIdx.x * SC_CV;
+                if (g0 >= nagg) break;
+                // the key before the run: the next lane down's last key;
+                // lane 0 takes the wave before's (the last wave's of the
+                // run before for wave 0, the chunk's predecessor for run 0)
+                uint32_t before = up[r];
+                if (lane == 0)
+                    before = wv > 0 ? lastk[par][wv - 1][r] : (r > 0 ? lastk[par][256 / SG_WAVE - 1][r - 1] : pk0);
+                if (r == 0) {
+                    const uint64_t gs = g0 > first ? g0 : first; // largest p with offs[p] <= gs
+                    while (p + 1 < hi) {
+                        const uint32_t mid = (p + hi) >> 1;
+                        if (offs[mid] <= gs) p = mid;
+                        else hi = mid;
+                    }
+                    ps = offs[p];
+                    pe = offs[p + 1];
+                }
+                if (g0 > ps && g0 >= first && g0 + SC_CV < pe) {
+                    // the usual case: the run inside p, neither its first nor
+                    // its last entry; only a change of window sets cursors
+#pragma unroll
+                    for (int c = 0; c < SC_CV; ++c) {
+                        const uint32_t prev = c == 0 ? before : key[r][c - 1];
+                        bad = bad || key[r][c] <= prev;
+                        if (((key[r][c] ^ prev) >> wsh) != 0u || (key[r][c] >> wsh) >= NW)
+                            scatter_cursors_of(s, wsh, p, g0 + c, key[r][c], prev, false, false, pe);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < SC_CV; ++c) {
+                        const uint64_t i = g0 + c;
+                        if (i >= nagg) break;
+                        if (i < first) continue;
+                        const uint32_t prev = c == 0 ? before : key[r][c - 1];
+                        while (i >= pe) { // into the next non-empty partition
+                            ++p;
+                            ps = offs[p];
+                            pe = offs[p + 1];
+                        }
+                        if (i > ps && key[r][c] <= prev) bad = true;
+                        scatter_cursors_of(s, wsh, p, i, key[r][c], prev, i == ps, i == pe - 1, pe);
+                    }
+                }
+            }
+        }
+        // cursors of empty partitions
+        const uint64_t nthreads = (uint64_t)gridDim.x * 256;
+        for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < ((uint64_t)NW + 1) * P; i += nthreads) {
+            const uint32_t p = (uint32_t)(i % P);
+            if (offs[p + 1] == offs[p]) s.cur[i] = offs[p];
+        }
+    }
+    const int any = __syncthreads_or(bad);
+    if (threadIdx.x == 0) s.bad[blockIdx.x] = any ? 1u : 0u;
+}
+
+// position of the entry j of the window among the partitions' runs: the
+// largest p with pre[p] <= j
+__device__ __forceinline__ uint32_t scatter_run_of(const uint32_t* pre, uint32_t P, uint32_t j)
+{
+    uint32_t lo = 0, hi = P;
+    while (lo + 1 < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (pre[mid] <= j) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// NT: the window's stores bypass the caches (a dense tensor larger than the
+// last-level cache)
+template <bool NT>
+__global__ __launch_bounds__(256) void scatter_window_kernel(ScatterParams s)
+{
+    __shared__ __align__(16) float buf[SC_W];
+    __shared__ uint64_t beg[256];
+    __shared__ uint32_t pre[257];
+    __shared__ uint32_t scan_lds[256 / SG_WAVE + 1];
+    const uint32_t P = s.P, t = threadIdx.x;
+    // windows in launch order: the XCDs write neighbouring windows together
+    // (measured faster than giving each XCD a contiguous run of windows)
+    const uint64_t w = blockIdx.x, k0 = w * SC_W;
+    uint32_t n = 0;
+    if (t < P) {
+        // cursors clamped to the partition's entries (they are only read
+        // inside them, whatever the cursor pass found)
+        const uint64_t lo = s.off[t] < s.capacity ? s.off[t] : s.capacity;
+        uint64_t hi = s.off[t + 1] < s.capacity ? s.off[t + 1] : s.capacity;
+        if (hi < lo) hi = lo;
+        uint64_t b = s.cur[w * P + t], e = s.cur[(w + 1) * P + t];
+        b = b < lo ? lo : (b > hi ? hi : b);
+        e = e < lo ? lo : (e > hi ? hi : e);
+        beg[t] = b;
+        if (e > b) {
+            // an ascending partition holds at most SC_W keys of a window below M
+            n = e - b <= (uint64_t)SC_W ? (uint32_t)(e - b) : (uint32_t)SC_W;
+            if (e - b > (uint64_t)SC_W) s.bad[0] = 1u;
+        }
+    }
+    float4* b4 = reinterpret_cast<float4*>(buf);
+#pragma unroll
+    for (int j = 0; j < SC_W / 4 / 256; ++j) b4[j * 256 + t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<256>(n, scan_lds, &tot);
+    if (t < P) pre[t] = ex;
+    __syncthreads();
+    for (uint32_t j0 = 0; j0 < tot; j0 += 256 * SC_KB) {
+        uint32_t x[SC_KB];
+        float v[SC_KB];
+#pragma unroll
+        for (int r = 0; r < SC_KB; ++r) {
+            const uint32_t j = j0 + r * 256 + t;
+            x[r] = 0xffffffffu;
+            v[r] = 0.f;
+            if (j < tot) {
+                const uint32_t p = scatter_run_of(pre, P, j);
+                const uint64_t i = beg[p] + (j - pre[p]);
+                x[r] = s.idx[i];
+                v[r] = s.val[i];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < SC_KB; ++r) {
+            if (j0 + r * 256 + t >= tot) continue;
+            if (x[r] >= s.M) {
+                report_error(kDevErrIndexRange);
+                continue;
+            }
+            const uint64_t o = (uint64_t)x[r] - k0;
+            if (o < (uint64_t)SC_W) buf[o] = v[r];
+        }
+    }
+    __syncthreads();
+    float4* d4 = reinterpret_cast<float4*>(s.dense + k0);
+    if (w + 1 < s.NW) { // a whole window below M
+        if (NT) {
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            const v4f* bv = reinterpret_cast<const v4f*>(buf);
+            v4f* dv = reinterpret_cast<v4f*>(s.dense + k0);
+#pragma unroll
+            for (int j = 0; j < SC_W / 4 / 256; ++j) __builtin_nontemporal_store(bv[j * 256 + t], &dv[j * 256 + t]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < SC_W / 4 / 256; ++j) d4[j * 256 + t] = b4[j * 256 + t];
+        }
+    } else { // the last window: keys [k0, M), 1 to SC_W of them
+        const uint32_t lim = (uint32_t)(s.M - k0);
+        for (uint32_t j = t; j < lim / 4; j += 256) d4[j] = b4[j];
+        for (uint32_t j = (lim / 4) * 4 + t; j < lim; j += 256) s.dense[k0 + j] = buf[j];
+    }
+}
+
+// the plain scatter: every entry's value to its key (for D == 1 only when a
+// flag word of the cursor pass is set); rows of D > 1 with a wave each
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams s)
 {
+    if (s.bad) {
+        uint32_t any = 0;
+        for (uint32_t j = threadIdx.x; j < s.nbad; j += 256) any |= s.bad[j];
+        if (!__syncthreads_or(any != 0u)) return;
+    }
     uint64_t b = s.off[0], e = s.off[s.P];
     if (e > s.capacity) e = s.capacity;
     if (b > e) b = e;
@@ -345,6 +599,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams s)
             for (uint32_t c = lane; c < s.D; c += SG_WAVE) s.dense[(uint64_t)x * s.D + c] = s.val[i * s.D + c];
         }
     }
+}
+
+__global__ __launch_bounds__(256) void scatter_zero_kernel(ScatterParams s)
+{
+    const uint64_t words = s.M * (s.D ? s.D : 1);
+    const uint64_t n4 = words / 4;
+    float4* d4 = reinterpret_cast<float4*>(s.dense);
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < n4; i += (uint64_t)gridDim.x * 256)
+        d4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (uint64_t i = n4 * 4 + blockIdx.x * 256ull + threadIdx.x; i < words; i += (uint64_t)gridDim.x * 256)
+        s.dense[i] = 0.f;
 }
 
 // non-empty 256-gradient blocks of an aggregate: one bit per block
@@ -419,12 +684,23 @@ extern "C" int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const 
     return SG_OK;
 }
 
-extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint32_t D, const uint64_t* d_off,
-                                uint32_t P, uint64_t capacity, uint64_t M, float* d_dense, void* stream)
+extern "C" size_t sg_scatter_dense_workspace_bytes(uint64_t M, uint32_t P)
 {
-    if (P == 0 || M == 0 || M >= (1ull << 32) || D > 65536 || !d_off || !d_dense) return SG_EINVAL;
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return 0;
+    Carver c(nullptr);
+    c.take<uint32_t>(SC_CUR_BLOCKS);
+    c.take<uint64_t>((ceil_div(M, SC_W) + 1) * P);
+    return (size_t)c.bytes();
+}
+
+extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint32_t D, const uint64_t* d_off,
+                                uint32_t P, uint64_t capacity, uint64_t M, float* d_dense, void* d_ws, size_t ws_bytes,
+                                void* stream)
+{
+    if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32) || D > 65536 || !d_off || !d_dense || !d_ws) return SG_EINVAL;
     if (capacity > 0 && (!d_idx || (D > 0 && !d_val))) return SG_EINVAL;
     if ((uintptr_t)d_dense % 16) return SG_EINVAL;
+    if (ws_bytes < sg_scatter_dense_workspace_bytes(M, P)) return SG_ECAPACITY;
     ScatterParams s;
     s.idx = d_idx;
     s.val = d_val;
@@ -434,8 +710,39 @@ extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint3
     s.capacity = capacity;
     s.M = M;
     s.dense = d_dense;
+    s.NW = ceil_div(M, SC_W);
+    Carver c(d_ws);
+    s.bad = c.take<uint32_t>(SC_CUR_BLOCKS);
+    s.cur = c.take<uint64_t>((s.NW + 1) * P);
     hipStream_t st = as_stream(stream);
+    if (D == 1 && capacity > 0) {
+        // a chunk per block where the entries allow, and enough blocks for
+        // the cursors of empty partitions (every block writes its flag word)
+        uint64_t cb = ceil_div(capacity, (uint64_t)SC_CV * SC_CR * 256);
+        const uint64_t fill = ceil_div((s.NW + 1) * P, 4096);
+        cb = cb > fill ? cb : fill;
+        s.nbad = (uint32_t)(cb < SC_CUR_BLOCKS ? cb : SC_CUR_BLOCKS);
+        if ((uintptr_t)d_idx % 16 == 0)
+            scatter_cursor_kernel<true><<<s.nbad, 256, 0, st>>>(s);
+        else
+            scatter_cursor_kernel<false><<<s.nbad, 256, 0, st>>>(s);
+        SG_TRY_LAUNCH();
+        probe_begin(SG_PROBE_SCATTER, st);
+        if (M * 4 > (256ull << 20)) // beyond the 256 MB last-level cache
+            scatter_window_kernel<true><<<(unsigned)s.NW, 256, 0, st>>>(s);
+        else
+            scatter_window_kernel<false><<<(unsigned)s.NW, 256, 0, st>>>(s);
+        SG_TRY_LAUNCH();
+        probe_end(SG_PROBE_SCATTER, st);
+        // the per-entry pass, needed only after a flag: a small grid
+        const uint64_t fb = ceil_div(capacity, 256);
+        scatter_kernel<<<(unsigned)(fb < SC_FIX_BLOCKS ? fb : SC_FIX_BLOCKS), 256, 0, st>>>(s);
+        SG_TRY_LAUNCH();
+        return SG_OK;
+    }
     const uint64_t words = M * (D ? D : 1);
+    s.bad = nullptr;
+    s.nbad = 0;
     scatter_zero_kernel<<<(unsigned)(ceil_div(words / 4 + 1, 256) < 8192 ? ceil_div(words / 4 + 1, 256) : 8192), 256, 0, st>>>(s);
     SG_TRY_LAUNCH();
     if (capacity > 0) {

@@ -217,9 +217,14 @@ def test_pull_side_host_checks(L):
     assert L.sg_decode(F, 100, F, cb - 1, M, P, F, 10, F, F, dw, N) == SG_ECAPACITY
     assert L.sg_decode(N, 100, F, cb, M, P, F, 10, F, F, dw, N) == SG_EINVAL
     assert L.sg_decode(F, 100, F, cb, M, 0, F, 10, F, F, dw, N) == SG_EINVAL
-    assert L.sg_scatter_dense(F, F, 1, F, P, 10, 0, F, N) == SG_EINVAL            # M = 0
-    assert L.sg_scatter_dense(F, F, 1, N, P, 10, M, F, N) == SG_EINVAL            # no offsets
-    assert L.sg_scatter_dense(F, F, 1, F, P, 10, M, C.c_void_p(0x10004), N) == SG_EINVAL  # misaligned dense
+    sw = L.sg_scatter_dense_workspace_bytes(M, P)
+    assert sw > 0 and L.sg_scatter_dense_workspace_bytes(M, 257) == 0
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, 0, F, F, sw, N) == SG_EINVAL            # M = 0
+    assert L.sg_scatter_dense(F, F, 1, N, P, 10, M, F, F, sw, N) == SG_EINVAL            # no offsets
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, M, C.c_void_p(0x10004), F, sw, N) == SG_EINVAL  # misaligned dense
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, M, F, N, sw, N) == SG_EINVAL            # no workspace
+    assert L.sg_scatter_dense(F, F, 1, F, P, 10, M, F, F, sw - 1, N) == SG_ECAPACITY     # workspace too small
+    assert L.sg_scatter_dense(F, F, 1, F, 257, 10, M, F, F, sw, N) == SG_EINVAL          # P > 256
     fw = L.sg_format_sizes_workspace_bytes(M)
     out = (C.c_uint64 * 7)()
     assert L.sg_format_sizes(F, F, 10, M, P, 1, F, cb, C.cast(out, C.c_void_p), F, fw - 1, N) == SG_ECAPACITY

@@ -97,6 +97,107 @@ def test_scatter_dense_matches_oracle(D):
     assert sg.sg_device_error() == 0
 
 
+def _scatter_case(name):
+    """(idx, val, off, M, capacity) of a scatter edge case; entries outside
+    [off[0], off[P]) hold junk keys that must not be written."""
+    rng = np.random.default_rng(sum(map(ord, name)))
+    W = 4096  # the library's key window
+    if name == "ragged_tail":  # several windows, M neither a window nor a float4 multiple
+        M, P = 3 * W + 5, 4
+        a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.9), P, 3)
+    elif name == "one_key":
+        M, P = 1, 1
+        a, o = np.array([0], np.uint32), np.array([0, 1], np.uint64)
+    elif name == "full_window":  # one partition holds every key of the windows
+        M, P = 2 * W + 100, 1
+        a, o = np.arange(M, dtype=np.uint32), np.array([0, M], np.uint64)
+    elif name == "p256_sparse":  # most partitions empty
+        M, P = 5 * W, 256
+        a, o = _agg_of(rng.choice(M, 40, replace=False), P, 9)
+    elif name == "unsorted":  # descending inside each partition: the per-entry pass
+        M, P = 4 * W + 3, 6
+        a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.3), P, 4)
+        for p in range(P):
+            a[o[p]:o[p + 1]] = a[o[p]:o[p + 1]][::-1]
+    elif name == "one_unsorted_pair":  # a single swapped pair in one partition
+        M, P = 4 * W, 3
+        a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.2), P, 6)
+        i = int(o[1]) + 5
+        a[i], a[i + 1] = a[i + 1], a[i]
+    elif name == "offset_range":  # off[0] > 0, off[P] < capacity: junk around the entries
+        M, P = 3 * W, 5
+        a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.4), P, 8)
+        junk = rng.integers(0, M, 300).astype(np.uint32)
+        a = np.concatenate([junk[:100], a, junk[100:]])
+        o = o + np.uint64(100)
+    elif name == "sparse_gaps":  # partitions whose consecutive keys skip many windows
+        M, P = 200 * W + 17, 4
+        a, o = _agg_of(rng.choice(M, 30, replace=False), P, 2)
+    else:
+        raise KeyError(name)
+    val = rng.standard_normal(a.size).astype(np.float32)
+    return a, val, o, M
+
+
+@pytest.mark.parametrize("name", ["ragged_tail", "one_key", "full_window", "p256_sparse", "unsorted",
+                                  "one_unsorted_pair", "offset_range", "sparse_gaps"])
+def test_scatter_dense_window_edges(name):
+    need_gpu()
+    a, val, o, M = _scatter_case(name)
+    print("scatter case", name, "M", M, "P", o.size - 1, "entries", a.size, flush=True)
+    dense = sg.sg_scatter_dense(to_dev_u32(a), to_dev_vals(val), to_dev_u64(o), M)
+    torch.cuda.synchronize()
+    want = oracle.scatter_dense(a, val, o, M, 1)
+    assert np.array_equal(host_bits(dense).reshape(-1)[:M], want.reshape(-1).view(np.uint32))
+    assert sg.sg_device_error() == 0
+
+
+def test_scatter_dense_key_beyond_m_is_recorded():
+    need_gpu()
+    M, P = 3 * 4096 + 9, 2
+    rng = np.random.default_rng(31)
+    a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.5), P, 5)
+    # an extra key at and past M at the end of partition 1 (still ascending)
+    a = np.concatenate([a, np.array([M, M + 70000], np.uint32)])
+    o = o.copy()
+    o[-1] += np.uint64(2)
+    val = rng.standard_normal(a.size).astype(np.float32)
+    assert sg.sg_device_error() == 0
+    dense = sg.sg_scatter_dense(to_dev_u32(a), to_dev_vals(val), to_dev_u64(o), M)
+    torch.cuda.synchronize()
+    keep = a < M
+    want = oracle.scatter_dense(a[keep], val[keep], np.array([0, keep.sum()], np.uint64), M, 1)
+    assert np.array_equal(host_bits(dense).reshape(-1)[:M], want.reshape(-1).view(np.uint32))
+    assert sg.sg_device_error() != 0
+    assert sg.sg_device_error() == 0
+
+
+def test_scatter_dense_twice_reuses_workspace():
+    """A sorted call after an unsorted one on the same workspace (the flag
+    words of the first must not leak into the second) and the reverse."""
+    need_gpu()
+    M = 6 * 4096 + 1
+    ws = torch.empty(sg.lib().sg_scatter_dense_workspace_bytes(M, 6), dtype=torch.uint8, device="cuda")
+    out = torch.empty(M, dtype=torch.float32, device="cuda")
+    import ctypes as C
+    L = sg.lib()
+    for name in ("unsorted", "ragged_tail", "one_unsorted_pair", "unsorted"):
+        a, val, o, _ = _scatter_case(name)
+        P = o.size - 1
+        if P > 6:
+            continue
+        di, dv, do = to_dev_u32(a), to_dev_vals(val), to_dev_u64(o)
+        out.fill_(7.0)
+        rc = L.sg_scatter_dense(C.c_void_p(di.data_ptr()), C.c_void_p(dv.data_ptr()), 1, C.c_void_p(do.data_ptr()), P,
+                                a.size, M, C.c_void_p(out.data_ptr()), C.c_void_p(ws.data_ptr()), ws.numel(),
+                                C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0
+        torch.cuda.synchronize()
+        want = oracle.scatter_dense(a, val, o, M, 1)
+        assert np.array_equal(host_bits(out).reshape(-1), want.reshape(-1).view(np.uint32)), name
+    assert sg.sg_device_error() == 0
+
+
 def test_scatter_dense_of_gpu_aggregate_is_allreduce():
     need_gpu()
     c = gen.config1(n=4, M=1 << 16)
