@@ -5,16 +5,16 @@
 // of section 3.3.1.
 //
 // Decode, on gfx950: the class map's key windows again.
-//   count  per (window, class), the set bits of the class's bitmap inside the
-//          window's bit range (the bits of class members that fall in it);
-//   scan   per class, an exclusive scan over the windows; the class totals
-//          give the output offsets;
-//   emit   a block per window builds the class masks of its chunks and their
-//          per-class prefixes in LDS (as encode does), numbers the set bits
-//          of the window's bitmap words with a block scan, and maps every set
-//          bit b of class p back to its key: the (b - first)-th class-p
-//          member of the window, found by a search over the chunk prefixes
-//          and a select inside the chunk's 32-bit class mask.
+//   ranks  the output position of a set bit is the number of set bits before
+//          it in the whole encoded bitmap (classes in order, each ascending):
+//          an exclusive prefix over the words' bit counts (block sums, their
+//          scan, then the per-word prefix);
+//   emit   a block per window forms the class masks of its chunks and their
+//          per-class prefix counts (as encode does) and loads the window's
+//          bitmap words.  Per (chunk, class) pair, the class's members in the
+//          chunk are the set bits of its mask, and their bitmap bits are one
+//          run of that many bits; the k-th set bit of the run is the k-th
+//          member, written at the run's rank plus the set bits before it.
 #include "sg_host.h"
 
 namespace sg {
@@ -26,94 +26,157 @@ struct DecParams {
     uint64_t bitmap_words;
     uint32_t* out_idx;
     uint64_t capacity;
-    uint64_t* out_off;  // [P+1]
-    uint32_t* cnt;      // [NW][P] set bits per (window, class), then their exclusive prefix per class
-    uint64_t* tot;      // [P] set bits per class
+    uint64_t* out_off; // [P+1]
+    uint32_t* wpre;    // [words + 1] set bits of the encoded words before each word
+    uint32_t* bsum;    // [NB] set bits per block of DS_WPB words, then their exclusive prefix
+    uint32_t NB;
 };
 
-// set bits of class p's words in bit range [a, b)
-__device__ __forceinline__ uint32_t range_popc(const DecParams& d, uint32_t p, uint32_t a, uint32_t b)
+// Ranks of set bits: the output position of a set bit is the number of set
+// bits before it in the whole encoded bitmap (classes in order, each
+// ascending), so an exclusive prefix over the words gives every window's
+// output offsets.  Padding bits past a class's size are not counted.
+constexpr int DS_ROUNDS = 4;                  // 16-byte loads per thread
+constexpr int DS_WPB = DS_ROUNDS * 4 * 256;   // words per block: round r, thread t holds 4 words at r 1024 + 4 t
+
+// the encoded words the buffer holds
+__device__ __forceinline__ uint64_t dec_words(const DecParams& d)
 {
-    if (b <= a) return 0;
-    const uint64_t base = d.q.word_off[p];
-    uint32_t c = 0;
-    for (uint32_t w = a >> 5; w <= (b - 1) >> 5; ++w) {
-        if (base + w >= d.bitmap_words) break;
-        uint32_t v = d.bitmap[base + w];
-        const uint32_t lo = w * 32 < a ? a - w * 32 : 0u;
-        const uint32_t hi = (w + 1) * 32 > b ? b - w * 32 : 32u;
-        if (hi < 32) v &= (1u << hi) - 1u;
-        v &= ~((1u << lo) - 1u);
-        c += __popc(v);
-    }
-    return c;
+    const uint64_t n = d.q.word_off[d.L.P];
+    return n < d.bitmap_words ? n : d.bitmap_words;
 }
 
-__global__ __launch_bounds__(256) void dec_count_kernel(DecParams d)
+// words g0 .. g0+3 (g0 a multiple of 4; zero past nwords), the bits past each
+// class's size cleared; wo, cs: word offsets and class sizes in LDS.  VEC:
+// the bitmap is 16-byte aligned.
+template <bool VEC>
+__device__ __forceinline__ void dec_load_words(const DecParams& d, const uint64_t* wo, const uint64_t* cs, uint64_t g0,
+                                               uint64_t nwords, uint32_t (&v)[4])
 {
+    if (VEC && g0 + 4 <= nwords) {
+        const uint4 x = *reinterpret_cast<const uint4*>(d.bitmap + g0);
+        v[0] = x.x, v[1] = x.y, v[2] = x.z, v[3] = x.w;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = g0 + c < nwords ? d.bitmap[g0 + c] : 0u;
+    }
+    if (g0 >= nwords) return;
     const uint32_t P = d.L.P;
-    const uint64_t cells = d.L.NW * P;
-    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < cells; i += (uint64_t)gridDim.x * 256) {
-        const uint64_t w = i / P;
-        const uint32_t p = (uint32_t)(i % P);
-        d.cnt[i] = range_popc(d, p, d.q.cpre[w * P + p], d.q.cpre[(w + 1) * P + p]);
+    uint32_t p = 0, hi = P; // largest p with wo[p] <= g0: the class of word g0
+    while (p + 1 < hi) {
+        const uint32_t mid = (p + hi) >> 1;
+        if (wo[mid] <= g0) p = mid;
+        else hi = mid;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint64_t gw = g0 + c;
+        if (gw >= nwords) break;
+        while (p + 1 < P && gw >= wo[p + 1]) ++p;
+        const uint32_t r = (uint32_t)(cs[p] & 31u);
+        if (gw + 1 == wo[p + 1] && r != 0u) v[c] &= (1u << r) - 1u;
     }
 }
 
-// one block per class: exclusive prefix of the window counts, in place
-__global__ __launch_bounds__(1024) void dec_scan_kernel(DecParams d)
+__device__ __forceinline__ void dec_load_class_table(const DecParams& d, uint64_t* wo, uint64_t* cs)
+{
+    for (uint32_t p = threadIdx.x; p <= d.L.P; p += blockDim.x) {
+        wo[p] = d.q.word_off[p];
+        if (p < d.L.P) cs[p] = d.q.class_size[p];
+    }
+    __syncthreads();
+}
+
+// set bits per block of DS_WPB words
+template <bool VEC>
+__global__ __launch_bounds__(256) void dec_wsum_kernel(DecParams d)
+{
+    __shared__ uint64_t wo[257], cs[256];
+    __shared__ uint32_t scan_lds[256 / SG_WAVE + 1];
+    dec_load_class_table(d, wo, cs);
+    const uint64_t nwords = dec_words(d);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int r = 0; r < DS_ROUNDS; ++r) {
+        uint32_t v[4];
+        dec_load_words<VEC>(d, wo, cs, (uint64_t)blockIdx.x * DS_WPB + r * 1024 + threadIdx.x * 4, nwords, v);
+        sum += __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
+    }
+    uint32_t tot;
+    block_excl_scan<256>(sum, scan_lds, &tot);
+    if (threadIdx.x == 0) d.bsum[blockIdx.x] = tot;
+}
+
+// one block: exclusive prefix of the block sums, in place
+__global__ __launch_bounds__(1024) void dec_bscan_kernel(DecParams d)
 {
     constexpr uint32_t PT = 8;
     __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
-    const uint32_t P = d.L.P, p = blockIdx.x;
-    const uint64_t NW = d.L.NW;
-    uint64_t carry = 0;
-    for (uint64_t base = 0; base < NW; base += 1024 * PT) {
-        const uint64_t w0 = base + (uint64_t)threadIdx.x * PT;
+    uint32_t carry = 0; // the encoded bits number below 2^32
+    for (uint32_t base = 0; base < d.NB; base += 1024 * PT) {
+        const uint32_t b0 = base + threadIdx.x * PT;
         uint32_t c[PT], sum = 0;
 #pragma unroll
         for (uint32_t j = 0; j < PT; ++j) {
-            c[j] = w0 + j < NW ? d.cnt[(w0 + j) * P + p] : 0u;
+            c[j] = b0 + j < d.NB ? d.bsum[b0 + j] : 0u;
             sum += c[j];
         }
         uint32_t tot;
         uint32_t ex = block_excl_scan<1024>(sum, scan_lds, &tot);
 #pragma unroll
         for (uint32_t j = 0; j < PT; ++j) {
-            if (w0 + j < NW) d.cnt[(w0 + j) * P + p] = (uint32_t)(carry + ex); // within a class: below 2^32
+            if (b0 + j < d.NB) d.bsum[b0 + j] = carry + ex;
             ex += c[j];
         }
         carry += tot;
         __syncthreads();
     }
-    if (threadIdx.x == 0) d.tot[p] = carry;
 }
 
-__global__ __launch_bounds__(256) void dec_off_kernel(DecParams d)
+// per word, the set bits of the words before it; the entry past the last
+// word holds the total.  One block scan serves the four rounds: the
+// thread's per-round counts (at most 128) packed in 16-bit fields, whose
+// block totals (at most 32768) do not carry into each other.
+template <bool VEC>
+__global__ __launch_bounds__(256) void dec_wpre_kernel(DecParams d)
 {
+    __shared__ uint64_t wo[257], cs[256];
     __shared__ uint64_t scan_lds[256 / SG_WAVE + 1];
-    const uint32_t P = d.L.P;
-    const uint64_t v = threadIdx.x < P ? d.tot[threadIdx.x] : 0ull;
-    uint64_t all;
-    const uint64_t ex = block_excl_scan64<256>(v, scan_lds, &all);
-    if (threadIdx.x < P) d.out_off[threadIdx.x] = ex;
-    if (threadIdx.x == 0) d.out_off[P] = all;
-}
-
-// position of the k-th set bit (k from 0) of v, which has more than k set bits
-__device__ __forceinline__ uint32_t select_bit(uint32_t v, uint32_t k)
-{
-    uint32_t pos = 0;
+    dec_load_class_table(d, wo, cs);
+    const uint64_t nwords = dec_words(d);
+    const uint64_t b0 = (uint64_t)blockIdx.x * DS_WPB;
+    uint32_t v[DS_ROUNDS][4];
+    uint64_t packed = 0;
 #pragma unroll
-    for (uint32_t half = 16; half > 0; half >>= 1) {
-        const uint32_t c = __popc(v & ((1u << half) - 1u));
-        if (k >= c) {
-            k -= c;
-            v >>= half;
-            pos += half;
-        }
+    for (int r = 0; r < DS_ROUNDS; ++r) {
+        dec_load_words<VEC>(d, wo, cs, b0 + r * 1024 + threadIdx.x * 4, nwords, v[r]);
+        const uint64_t sr = __popc(v[r][0]) + __popc(v[r][1]) + __popc(v[r][2]) + __popc(v[r][3]);
+        packed |= sr << (16 * r);
     }
-    return pos;
+    uint64_t tot;
+    const uint64_t ex = block_excl_scan64<256>(packed, scan_lds, &tot);
+    uint32_t before = d.bsum[blockIdx.x]; // set bits of the rounds before
+#pragma unroll
+    for (int r = 0; r < DS_ROUNDS; ++r) {
+        const uint64_t g0 = b0 + r * 1024 + threadIdx.x * 4;
+        uint32_t run = before + (uint32_t)((ex >> (16 * r)) & 0xffffu);
+        uint32_t pre[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pre[c] = run;
+            run += __popc(v[r][c]);
+            if (g0 + c + 1 == nwords) d.wpre[nwords] = run;
+        }
+        if (g0 + 4 <= nwords) {
+            *reinterpret_cast<uint4*>(d.wpre + g0) = make_uint4(pre[0], pre[1], pre[2], pre[3]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (g0 + c < nwords) d.wpre[g0 + c] = pre[c];
+        }
+        before += (uint32_t)((tot >> (16 * r)) & 0xffffu);
+    }
+    if (nwords == 0 && blockIdx.x == 0 && threadIdx.x == 0) d.wpre[0] = 0;
 }
 
 constexpr int DC_THREADS = 256;
@@ -124,9 +187,9 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
     // partition-major [P][NCW]: a thread's 8 chunks of one class are 16-byte
     // accesses, consecutive threads on consecutive addresses
     __shared__ __align__(16) uint32_t masks[2048];
-    __shared__ __align__(16) uint16_t pre[2048];
     __shared__ uint32_t segofs[257], a_bits[256], b_bits[256], cls_first[256];
-    __shared__ uint32_t wex[DC_WORDS];
+    __shared__ uint64_t obase[256];
+    __shared__ uint32_t wex[DC_WORDS], segw[DC_WORDS];
     __shared__ uint32_t scan_lds[DC_THREADS / SG_WAVE + 1];
     const CmapLayout& L = d.L;
     const uint32_t P = L.P, NCW = L.NCW;
@@ -147,7 +210,22 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
         const uint32_t ca = d.q.cpre[win * P + p], cb = d.q.cpre[(win + 1) * P + p];
         a_bits[p] = ca;
         b_bits[p] = cb;
+        // output position of the class's first bit in the window: the set
+        // bits before it (words before its word, and its word's lower bits)
+        if (cb > ca) {
+            const uint64_t nwords = dec_words(d);
+            const uint64_t gw0 = d.q.word_off[p] + (ca >> 5);
+            const uint32_t v0 = gw0 < nwords ? d.bitmap[gw0] : 0u;
+            obase[p] = (uint64_t)d.wpre[gw0 < nwords ? gw0 : nwords] + __popc(v0 & ((1u << (ca & 31u)) - 1u));
+        }
         nw = cb > ca ? ((cb - 1) >> 5) - (ca >> 5) + 1 : 0u;
+    }
+    if (win == 0) { // the classes' offsets
+        const uint64_t nwords = dec_words(d);
+        for (uint32_t p = threadIdx.x; p <= P; p += DC_THREADS) {
+            const uint64_t w = d.q.word_off[p];
+            d.out_off[p] = d.wpre[w < nwords ? w : nwords];
+        }
     }
     uint32_t nseg;
     const uint32_t so = block_excl_scan<DC_THREADS>(nw, scan_lds, &nseg);
@@ -185,15 +263,18 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
         if (threadIdx.x == 0) report_error(kDevErrCmap);
         return;
     }
-    // per-class prefix over the window's chunks: P segments of NCW, 8 per
-    // thread, segmented scan inside a DPP row (NCW/8 <= 16 threads)
+    // per-class prefix over the window's chunks: P segments of NCW, 8
+    // per thread, segmented scan inside a DPP row (NCW/8 <= 16 threads);
+    // the thread keeps its 8 (chunk, class) masks, counts and prefixes
+    const uint32_t e0 = threadIdx.x * 8;
+    const bool act = e0 < NCW * P;
+    uint32_t mw[8], c[8], ex[8];
     {
-        const uint32_t e0 = threadIdx.x * 8;
-        uint32_t c[8], run = 0;
-        const bool act = e0 < NCW * P;
+        uint32_t run = 0;
         const uint4 ma = act ? *reinterpret_cast<const uint4*>(&masks[e0]) : make_uint4(0u, 0u, 0u, 0u);
         const uint4 mb = act ? *reinterpret_cast<const uint4*>(&masks[e0 + 4]) : make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t mw[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w}; // 8 chunks of one class
+        mw[0] = ma.x, mw[1] = ma.y, mw[2] = ma.z, mw[3] = ma.w;
+        mw[4] = mb.x, mw[5] = mb.y, mw[6] = mb.z, mw[7] = mb.w; // 8 chunks of one class
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             c[j] = __popc(mw[j]);
@@ -210,24 +291,16 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
         if (sg > 4 && (inrow & (sg - 1)) >= 4) inc += x;
         x = dpp_move<kDppRowShr8>(0u, inc);
         if (sg > 8 && (inrow & (sg - 1)) >= 8) inc += x;
-        if (act) {
-            uint32_t ex[8];
-            ex[0] = inc - run;
+        ex[0] = inc - run;
 #pragma unroll
-            for (int j = 1; j < 8; ++j) ex[j] = ex[j - 1] + c[j - 1];
-            *reinterpret_cast<uint4*>(&pre[e0]) = make_uint4(ex[0] | (ex[1] << 16), ex[2] | (ex[3] << 16),
-                                                            ex[4] | (ex[5] << 16), ex[6] | (ex[7] << 16));
-        }
+        for (int j = 1; j < 8; ++j) ex[j] = ex[j - 1] + c[j - 1];
     }
-    // the window's words (class-major), their set bits inside the ranges, and
-    // a block scan numbering them
-    uint32_t wv[2], wp[2], wc[2], sum = 0;
+    // the window's words (class-major), masked to the class ranges
+    uint32_t wv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t i = threadIdx.x * 2 + h;
         wv[h] = 0;
-        wp[h] = 0;
-        wc[h] = 0;
         if (i < nseg) {
             uint32_t lo = 0, hi = P; // class of word i
             while (lo + 1 < hi) {
@@ -241,58 +314,58 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
             uint32_t v = gw < d.bitmap_words ? d.bitmap[gw] : 0u;
             const uint32_t lo_b = qw * 32 < a ? a - qw * 32 : 0u;
             const uint32_t hi_b = (qw + 1) * 32 > b ? b - qw * 32 : 32u;
-            if (hi_b < 32) v &= (1u << hi_b) - 1u;
-            v &= ~((1u << lo_b) - 1u);
-            wv[h] = v;
-            wp[h] = p;
-            wc[h] = __popc(v);
-        }
-        sum += wc[h];
-    }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<DC_THREADS>(sum, scan_lds, &tot);
-    {
-        uint32_t e = ex;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t i = threadIdx.x * 2 + h;
-            if (i < DC_WORDS) wex[i] = e;
-            e += wc[h];
+            uint32_t m = ~((1u << lo_b) - 1u);
+            if (hi_b < 32) m &= (1u << hi_b) - 1u;
+            wv[h] = v & m;
         }
     }
-    __syncthreads();
-    if (threadIdx.x < P) cls_first[threadIdx.x] = segofs[threadIdx.x] < nseg ? wex[segofs[threadIdx.x]] : tot;
-    __syncthreads();
-    // every set bit back to its key
+    // the words into LDS, and the exclusive prefix of their set bits
+    uint32_t sum = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t i = threadIdx.x * 2 + h;
-        if (i >= nseg) continue;
-        const uint32_t p = wp[h], a = a_bits[p];
-        const uint32_t qw = (a >> 5) + (i - segofs[p]);
-        uint64_t o = d.out_off[p] + d.cnt[win * P + p] + (wex[i] - cls_first[p]);
-        uint32_t v = wv[h];
-        while (v) {
-            const uint32_t bit = __ffs(v) - 1u;
-            v &= v - 1u;
-            const uint32_t m = qw * 32 + bit - a; // member of class p inside the window
-            const uint16_t* prow = pre + p * NCW;  // class p's prefixes over the chunks
-            uint32_t lo = 0, hi = NCW;            // chunk: last t with prow[t] <= m
-            while (lo + 1 < hi) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (prow[mid] <= m) lo = mid;
-                else hi = mid;
+        if (i < nseg) segw[i] = wv[h];
+        sum += __popc(wv[h]);
+    }
+    uint32_t tot;
+    const uint32_t wx = block_excl_scan<DC_THREADS>(sum, scan_lds, &tot);
+    if (threadIdx.x * 2 < DC_WORDS) wex[threadIdx.x * 2] = wx;
+    if (threadIdx.x * 2 + 1 < DC_WORDS) wex[threadIdx.x * 2 + 1] = wx + __popc(wv[0]);
+    __syncthreads();
+    if (threadIdx.x < P) cls_first[threadIdx.x] = segofs[threadIdx.x] < nseg ? wex[segofs[threadIdx.x]] : tot;
+    __syncthreads();
+    // every set bit back to its key, by (chunk, class) pair: the class-p
+    // members of chunk ch are the set bits of its mask, with window
+    // ranks ex, ex + 1, ...; their bitmap bits are the run of c bits at
+    // a + ex, and the k-th set bit of the run is the member at the k-th
+    // set bit of the mask
+    if (act) {
+        const uint32_t p = e0 / NCW, ch0 = e0 % NCW;
+        const uint32_t a = a_bits[p], so2 = segofs[p], a5 = a >> 5;
+        const uint64_t base = obase[p];
+        const uint32_t first = cls_first[p];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (c[j] == 0) continue;
+            const uint32_t g = a + ex[j];
+            const uint32_t k = so2 + (g >> 5) - a5, bit = g & 31u;
+            const uint32_t w0 = segw[k];
+            uint32_t run = w0 >> bit;
+            if (bit + c[j] > 32) run |= segw[k + 1] << (32 - bit); // bit > 0 here
+            if (c[j] < 32) run &= (1u << c[j]) - 1u;
+            if (run == 0) continue;
+            uint32_t f = wex[k] + __popc(w0 & ((1u << bit) - 1u)); // rank among the window's set bits
+            const uint32_t kbase = (uint32_t)(win * L.W) + (ch0 + j) * 32;
+            uint32_t m = mw[j]; // the members not yet passed, in key order
+            while (run) {
+                const uint32_t z = __ffs(run) - 1u; // members to pass over
+                run = (run >> z) >> 1;
+                for (uint32_t i = 0; i < z; ++i) m &= m - 1u;
+                const uint64_t o = base + (f - first);
+                if (o < d.capacity) d.out_idx[o] = kbase + (__ffs(m) - 1u);
+                m &= m - 1u;
+                ++f;
             }
-            const uint32_t mk = masks[p * NCW + lo];
-            const uint32_t k = m - prow[lo];
-            if (k >= (uint32_t)__popc(mk)) { // bit past the class: cannot happen with the class map's prefixes
-                report_error(kDevErrCmap);
-                ++o;
-                continue;
-            }
-            const uint64_t key = win * L.W + (uint64_t)lo * 32 + select_bit(mk, k);
-            if (o < d.capacity) d.out_idx[o] = (uint32_t)key;
-            ++o;
         }
     }
 }
@@ -645,8 +718,11 @@ using namespace sg;
 extern "C" size_t sg_decode_workspace_bytes(uint64_t M, uint32_t P)
 {
     if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return 0;
-    const CmapLayout L = cmap_layout(M, P);
-    return (size_t)(align_up(4ull * L.NW * P, 256) + 8ull * P);
+    const uint64_t maxw = sg_encode_max_words(M, P);
+    Carver c(nullptr);
+    c.take<uint32_t>(maxw + 1);
+    c.take<uint32_t>(ceil_div(maxw, DS_WPB));
+    return (size_t)c.bytes();
 }
 
 extern "C" int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const void* d_cmap, size_t cmap_bytes,
@@ -666,16 +742,22 @@ extern "C" int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const 
     d.out_idx = d_out_idx;
     d.capacity = capacity;
     d.out_off = d_out_off;
+    const uint64_t maxw = sg_encode_max_words(M, P);
+    const uint64_t words = bitmap_words < maxw ? bitmap_words : maxw; // the scan covers at most these
+    d.bitmap_words = words;
+    d.NB = (uint32_t)ceil_div(words ? words : 1, DS_WPB);
     Carver c(d_ws);
-    d.cnt = c.take<uint32_t>(d.L.NW * P);
-    d.tot = c.take<uint64_t>(P);
+    d.wpre = c.take<uint32_t>(maxw + 1);
+    d.bsum = c.take<uint32_t>(ceil_div(maxw, DS_WPB));
     hipStream_t st = as_stream(stream);
-    const uint64_t cells = d.L.NW * P;
-    dec_count_kernel<<<(unsigned)(ceil_div(cells, 256) < 4096 ? ceil_div(cells, 256) : 4096), 256, 0, st>>>(d);
+    const bool vec = (uintptr_t)d_bitmap % 16 == 0;
+    if (vec) dec_wsum_kernel<true><<<d.NB, 256, 0, st>>>(d);
+    else dec_wsum_kernel<false><<<d.NB, 256, 0, st>>>(d);
     SG_TRY_LAUNCH();
-    dec_scan_kernel<<<P, 1024, 0, st>>>(d);
+    dec_bscan_kernel<<<1, 1024, 0, st>>>(d);
     SG_TRY_LAUNCH();
-    dec_off_kernel<<<1, 256, 0, st>>>(d);
+    if (vec) dec_wpre_kernel<true><<<d.NB, 256, 0, st>>>(d);
+    else dec_wpre_kernel<false><<<d.NB, 256, 0, st>>>(d);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_DECODE, st);
     dec_emit_kernel<<<(unsigned)d.L.NW, DC_THREADS, 0, st>>>(d);
