@@ -414,130 +414,14 @@ __device__ __forceinline__ bool scatter_offsets(const ScatterParams& s, uint64_t
     return __syncthreads_and(ok) != 0;
 }
 
-// cursors that entry i (key, after prev in its partition p; first: no entry
-// before it) sets: it is the first of p in windows (win(prev), win(key)], and
-// the last entry also closes the windows after its own
-__device__ __forceinline__ void scatter_cursors_of(const ScatterParams& s, uint32_t wsh, uint32_t p, uint64_t i,
-                                                   uint32_t key, uint32_t prev, bool first, bool last, uint64_t pe)
-{
-    const uint32_t NW = (uint32_t)s.NW, P = s.P;
-    uint32_t win = key >> wsh;
-    if (win >= NW) win = NW - 1;
-    uint32_t w = 0;
-    if (!first) {
-        const uint32_t pw = prev >> wsh;
-        w = (pw < NW ? pw : NW - 1) + 1;
-    }
-    for (; w <= win; ++w) s.cur[(uint64_t)w * P + p] = i;
-    if (last)
-        for (w = win + 1; w <= NW; ++w) s.cur[(uint64_t)w * P + p] = pe;
-}
-
-// Chunks of SC_CV * SC_CR * 256 entries: thread t takes SC_CR runs of SC_CV
-// consecutive entries, run r at c0 + r SC_CV 256 + t SC_CV, so that one load
-// instruction reads 256 contiguous entries of a wave (one 16-byte load per
-// lane when VEC: d_idx 16-byte aligned).
-constexpr int SC_CV = 4;
-constexpr int SC_CR = 2;
-
 template <bool VEC>
 __global__ __launch_bounds__(256) void scatter_cursor_kernel(ScatterParams s)
 {
-    constexpr uint32_t CH = SC_CV * SC_CR * 256;
     __shared__ uint64_t offs[257];
-    __shared__ uint32_t lastk[2][256 / SG_WAVE][SC_CR]; // lane 63's last key per wave and run, by chunk parity
     bool bad = !scatter_offsets(s, offs);
-    const uint32_t P = s.P;
-    const uint32_t NW = (uint32_t)s.NW; // below 2^21
-    const uint32_t wsh = (uint32_t)__builtin_ctz((uint32_t)SC_W);
-    const uint64_t first = offs[0], nagg = offs[P];
-    const uint32_t lane = lane_id(), wv = threadIdx.x / SG_WAVE;
-    if (!bad) {
-        uint32_t par = 0;
-        // chunks start at multiples of SC_CV (aligned runs); entries before
-        // `first` are not the caller's
-        for (uint64_t c0 = (first & ~(uint64_t)(SC_CV - 1)) + blockIdx.x * (uint64_t)CH; c0 < nagg;
-             c0 += (uint64_t)gridDim.x * CH, par ^= 1u) {
-            uint32_t key[SC_CR][SC_CV];
-#pragma unroll
-            for (int r = 0; r < SC_CR; ++r) {
-                const uint64_t g0 = c0 + (uint64_t)r * SC_CV * 256 + threadIdx.x * SC_CV;
-                if (VEC && g0 + SC_CV <= s.capacity) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(s.idx + g0);
-                    key[r][0] = v.x;
-                    key[r][1] = v.y;
-                    key[r][2] = v.z;
-                    key[r][3] = v.w;
-                } else {
-#pragma unroll
-                    for (int c = 0; c < SC_CV; ++c) key[r][c] = s.idx[g0 + c < s.capacity ? g0 + c : s.capacity - 1];
-                }
-            }
-            const uint32_t pk0 = threadIdx.x == 0 && c0 > 0 ? s.idx[c0 - 1] : 0u; // the entry before the chunk
-            uint32_t up[SC_CR];
-#pragma unroll
-            for (int r = 0; r < SC_CR; ++r) {
-                up[r] = (uint32_t)__shfl_up((int)key[r][SC_CV - 1], 1, SG_WAVE);
-                if (lane == SG_WAVE - 1) lastk[par][wv][r] = key[r][SC_CV - 1];
-            }
-            __syncthreads();
-            uint32_t p = 0, hi = P;
-            uint64_t ps = 0, pe = 0;
-#pragma unroll
-            for (int r = 0; r < SC_CR; ++r) {
-                const uint64_t g0 = c0 + (uint64_t)r * SC_CV * 256 + threadIdx.x * SC_CV;
-                if (g0 >= nagg) break;
-                // the key before the run: the next lane down's last key;
-                // lane 0 takes the wave before's (the last wave's of the
-                // run before for wave 0, the chunk's predecessor for run 0)
-                uint32_t before = up[r];
-                if (lane == 0)
-                    before = wv > 0 ? lastk[par][wv - 1][r] : (r > 0 ? lastk[par][256 / SG_WAVE - 1][r - 1] : pk0);
-                if (r == 0) {
-                    const uint64_t gs = g0 > first ? g0 : first; // largest p with offs[p] <= gs
-                    while (p + 1 < hi) {
-                        const uint32_t mid = (p + hi) >> 1;
-                        if (offs[mid] <= gs) p = mid;
-                        else hi = mid;
-                    }
-                    ps = offs[p];
-                    pe = offs[p + 1];
-                }
-                if (g0 > ps && g0 >= first && g0 + SC_CV < pe) {
-                    // the usual case: the run inside p, neither its first nor
-                    // its last entry; only a change of window sets cursors
-#pragma unroll
-                    for (int c = 0; c < SC_CV; ++c) {
-                        const uint32_t prev = c == 0 ? before : key[r][c - 1];
-                        bad = bad || key[r][c] <= prev;
-                        if (((key[r][c] ^ prev) >> wsh) != 0u || (key[r][c] >> wsh) >= NW)
-                            scatter_cursors_of(s, wsh, p, g0 + c, key[r][c], prev, false, false, pe);
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < SC_CV; ++c) {
-                        const uint64_t i = g0 + c;
-                        if (i >= nagg) break;
-                        if (i < first) continue;
-                        const uint32_t prev = c == 0 ? before : key[r][c - 1];
-                        while (i >= pe) { // into the next non-empty partition
-                            ++p;
-                            ps = offs[p];
-                            pe = offs[p + 1];
-                        }
-                        if (i > ps && key[r][c] <= prev) bad = true;
-                        scatter_cursors_of(s, wsh, p, i, key[r][c], prev, i == ps, i == pe - 1, pe);
-                    }
-                }
-            }
-        }
-        // cursors of empty partitions
-        const uint64_t nthreads = (uint64_t)gridDim.x * 256;
-        for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < ((uint64_t)NW + 1) * P; i += nthreads) {
-            const uint32_t p = (uint32_t)(i % P);
-            if (offs[p + 1] == offs[p]) s.cur[i] = offs[p];
-        }
-    }
+    if (!bad)
+        bad = window_cursor_pass<VEC>(s.idx, s.capacity, offs, s.P, (uint32_t)s.NW,
+                                      (uint32_t)__builtin_ctz((uint32_t)SC_W), s.cur);
     const int any = __syncthreads_or(bad);
     if (threadIdx.x == 0) s.bad[blockIdx.x] = any ? 1u : 0u;
 }
@@ -800,7 +684,7 @@ extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint3
     if (D == 1 && capacity > 0) {
         // a chunk per block where the entries allow, and enough blocks for
         // the cursors of empty partitions (every block writes its flag word)
-        uint64_t cb = ceil_div(capacity, (uint64_t)SC_CV * SC_CR * 256);
+        uint64_t cb = ceil_div(capacity, (uint64_t)WC_CHUNK);
         const uint64_t fill = ceil_div((s.NW + 1) * P, 4096);
         cb = cb > fill ? cb : fill;
         s.nbad = (uint32_t)(cb < SC_CUR_BLOCKS ? cb : SC_CUR_BLOCKS);

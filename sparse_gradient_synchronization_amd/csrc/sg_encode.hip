@@ -198,56 +198,150 @@ __device__ __forceinline__ void load_agg_offsets(const EncParams& e, uint64_t* o
     __syncthreads();
 }
 
-// Window cursors: one streaming pass over the aggregated entries; entry i of
-// partition p is the first of its partition in windows (win(i-1), win(i)].
-// The same launch fills the cursors of empty partitions and zeroes the
-// bitmap words that two neighbouring windows share (the encode kernel merges
-// them with atomicOr).
+// ---------------------------------------------------------------------------
+// Window cursors of sorted partitions (encode and the dense scatter): for key
+// windows of 2^wsh keys, cur[w P + p] is the first entry of partition p
+// (entries [offs[p], offs[p+1]) of idx, ascending keys) whose key is at or
+// after window w's first key, for w in [0, NW]; cur[NW P + p] = offs[p+1].
+// ---------------------------------------------------------------------------
+// cursors that entry i (key, after prev in its partition p; first: no entry
+// before it) sets: it is the first of p in windows (win(prev), win(key)], and
+// the last entry also closes the windows after its own
+__device__ __forceinline__ void window_cursors_of(uint64_t* cur, uint32_t P, uint32_t NW, uint32_t wsh, uint32_t p,
+                                                  uint64_t i, uint32_t key, uint32_t prev, bool first, bool last,
+                                                  uint64_t pe)
+{
+    uint32_t win = key >> wsh;
+    if (win >= NW) win = NW - 1;
+    uint32_t w = 0;
+    if (!first) {
+        const uint32_t pw = prev >> wsh;
+        w = (pw < NW ? pw : NW - 1) + 1;
+    }
+    for (; w <= win; ++w) cur[(uint64_t)w * P + p] = i;
+    if (last)
+        for (w = win + 1; w <= NW; ++w) cur[(uint64_t)w * P + p] = pe;
+}
+
+// Chunks of WC_CV * WC_CR * 256 entries: thread t takes WC_CR runs of WC_CV
+// consecutive entries, run r at c0 + r WC_CV 256 + t WC_CV, so that one load
+// instruction reads 256 contiguous entries of a wave (one 16-byte load per
+// lane when VEC: idx 16-byte aligned).
+constexpr int WC_CV = 4;
+constexpr int WC_CR = 2;
+constexpr uint32_t WC_CHUNK = WC_CV * WC_CR * 256;
+
+// The block's share of the pass (256 threads, every thread calls it; offs in
+// LDS).  Returns true when a partition's keys do not ascend (the cursors are
+// then not those of the definition).  Also fills the cursors of empty
+// partitions.
+template <bool VEC>
+__device__ bool window_cursor_pass(const uint32_t* idx, uint64_t capacity, const uint64_t* offs, uint32_t P,
+                                   uint32_t NW, uint32_t wsh, uint64_t* cur)
+{
+    __shared__ uint32_t lastk[2][256 / SG_WAVE][WC_CR]; // lane 63's last key per wave and run, by chunk parity
+    const uint64_t first = offs[0], nagg = offs[P];
+    const uint32_t lane = lane_id(), wv = threadIdx.x / SG_WAVE;
+    bool bad = false;
+    uint32_t par = 0;
+    // chunks start at multiples of WC_CV (aligned runs); entries before
+    // `first` are not the caller's
+    for (uint64_t c0 = (first & ~(uint64_t)(WC_CV - 1)) + blockIdx.x * (uint64_t)WC_CHUNK; c0 < nagg;
+         c0 += (uint64_t)gridDim.x * WC_CHUNK, par ^= 1u) {
+        uint32_t key[WC_CR][WC_CV];
+#pragma unroll
+        for (int r = 0; r < WC_CR; ++r) {
+            const uint64_t g0 = c0 + (uint64_t)r * WC_CV * 256 + threadIdx.x * WC_CV;
+            if (VEC && g0 + WC_CV <= capacity) {
+                const uint4 v = *reinterpret_cast<const uint4*>(idx + g0);
+                key[r][0] = v.x;
+                key[r][1] = v.y;
+                key[r][2] = v.z;
+                key[r][3] = v.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < WC_CV; ++c) key[r][c] = idx[g0 + c < capacity ? g0 + c : capacity - 1];
+            }
+        }
+        const uint32_t pk0 = threadIdx.x == 0 && c0 > 0 ? idx[c0 - 1] : 0u; // the entry before the chunk
+        uint32_t up[WC_CR];
+#pragma unroll
+        for (int r = 0; r < WC_CR; ++r) {
+            up[r] = (uint32_t)__shfl_up((int)key[r][WC_CV - 1], 1, SG_WAVE);
+            if (lane == SG_WAVE - 1) lastk[par][wv][r] = key[r][WC_CV - 1];
+        }
+        __syncthreads();
+        uint32_t p = 0, hi = P;
+        uint64_t ps = 0, pe = 0;
+#pragma unroll
+        for (int r = 0; r < WC_CR; ++r) {
+            const uint64_t g0 = c0 + (uint64_t)r * WC_CV * 256 + threadIdx.x * WC_CV;
+            if (g0 >= nagg) break;
+            // the key before the run: the next lane down's last key; lane 0
+            // takes the wave before's (the last wave's of the run before for
+            // wave 0, the chunk's predecessor for run 0)
+            uint32_t before = up[r];
+            if (lane == 0)
+                before = wv > 0 ? lastk[par][wv - 1][r] : (r > 0 ? lastk[par][256 / SG_WAVE - 1][r - 1] : pk0);
+            if (r == 0) {
+                const uint64_t gs = g0 > first ? g0 : first; // largest p with offs[p] <= gs
+                while (p + 1 < hi) {
+                    const uint32_t mid = (p + hi) >> 1;
+                    if (offs[mid] <= gs) p = mid;
+                    else hi = mid;
+                }
+                ps = offs[p];
+                pe = offs[p + 1];
+            }
+            if (g0 > ps && g0 >= first && g0 + WC_CV < pe) {
+                // the usual case: the run inside p, neither its first nor its
+                // last entry; only a change of window sets cursors
+#pragma unroll
+                for (int c = 0; c < WC_CV; ++c) {
+                    const uint32_t prev = c == 0 ? before : key[r][c - 1];
+                    bad = bad || key[r][c] <= prev;
+                    if (((key[r][c] ^ prev) >> wsh) != 0u || (key[r][c] >> wsh) >= NW)
+                        window_cursors_of(cur, P, NW, wsh, p, g0 + c, key[r][c], prev, false, false, pe);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < WC_CV; ++c) {
+                    const uint64_t i = g0 + c;
+                    if (i >= nagg) break;
+                    if (i < first) continue;
+                    const uint32_t prev = c == 0 ? before : key[r][c - 1];
+                    while (i >= pe) { // into the next non-empty partition
+                        ++p;
+                        ps = offs[p];
+                        pe = offs[p + 1];
+                    }
+                    if (i > ps && key[r][c] <= prev) bad = true;
+                    window_cursors_of(cur, P, NW, wsh, p, i, key[r][c], prev, i == ps, i == pe - 1, pe);
+                }
+            }
+        }
+    }
+    // cursors of empty partitions
+    const uint64_t nthreads = (uint64_t)gridDim.x * 256;
+    for (uint64_t i = blockIdx.x * 256ull + threadIdx.x; i < ((uint64_t)NW + 1) * P; i += nthreads) {
+        const uint32_t p = (uint32_t)(i % P);
+        if (offs[p + 1] == offs[p]) cur[i] = offs[p];
+    }
+    return bad;
+}
+
+// Window cursors (the pass above, at the class map's window size), the
+// cursors of empty partitions, and the bitmap words that two neighbouring
+// windows share zeroed (the encode kernel merges them with atomicOr).
+template <bool VEC>
 __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
 {
     __shared__ uint64_t offs[257];
     load_agg_offsets(e, offs);
     const uint32_t P = e.L.P;
     const uint64_t NW = e.L.NW;
-    const uint32_t wsh = (uint32_t)__builtin_ctzll(e.L.W); // W = 32 NCW, a power of two
-    const uint64_t nagg = offs[P];
-    const uint64_t tid = blockIdx.x * 256ull + threadIdx.x, nthreads = (uint64_t)gridDim.x * 256;
-    for (uint64_t i0 = blockIdx.x * 256ull; i0 < nagg; i0 += nthreads) { // uniform per block
-        const uint64_t i = i0 + threadIdx.x;
-        const uint64_t ic = i < nagg ? i : nagg - 1;
-        // the entry's key, and the one before it from the next lane down
-        // (lane 0 loads its own)
-        const uint32_t key = e.agg_idx[ic];
-        const uint32_t up = (uint32_t)__shfl_up((int)key, 1, SG_WAVE);
-        const uint32_t before = lane_id() > 0 ? up : (ic > 0 ? e.agg_idx[ic - 1] : 0u);
-        if (i >= nagg) continue;
-        uint32_t lo = 0, hi = P; // largest p with offs[p] <= i
-        while (lo + 1 < hi) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (offs[mid] <= i) lo = mid;
-            else hi = mid;
-        }
-        const uint32_t p = lo;
-        const uint64_t s = offs[p], en = offs[p + 1] > s ? offs[p + 1] : s;
-        if (i < s || i >= en) continue; // inconsistent offsets
-        uint64_t win = (uint64_t)key >> wsh;
-        if (win >= NW) win = NW - 1;
-        int64_t prev = -1;
-        if (i > s) {
-            const uint64_t pw = (uint64_t)before >> wsh;
-            prev = (int64_t)(pw < NW ? pw : NW - 1);
-        }
-        for (int64_t w = prev + 1; w <= (int64_t)win; ++w) e.cur[(uint64_t)w * P + p] = i;
-        if (i == en - 1)
-            for (uint64_t w = win + 1; w <= NW; ++w) e.cur[w * P + p] = en;
-    }
-    // cursors of empty partitions ((NW + 1) P < 2^32: NW < 2^24, P <= 256)
-    const uint32_t tid32 = (uint32_t)tid, nth32 = (uint32_t)nthreads;
-    for (uint32_t i = tid32; i < (uint32_t)((NW + 1) * P); i += nth32) {
-        const uint32_t p = i % P;
-        if (offs[p + 1] <= offs[p]) e.cur[i] = offs[p];
-    }
-    // shared bitmap words
+    window_cursor_pass<VEC>(e.agg_idx, e.agg_cap, offs, P, (uint32_t)NW, (uint32_t)__builtin_ctzll(e.L.W), e.cur);
+    const uint32_t tid32 = blockIdx.x * 256 + threadIdx.x, nth32 = gridDim.x * 256;
     for (uint32_t i = tid32; i < (uint32_t)(NW * P); i += nth32) {
         const uint32_t w = i / P;
         const uint32_t p = i % P;
@@ -527,9 +621,16 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     // a window's words never exceed W/32 + P
     if (e.L.W / 32 + P + 2 > (uint64_t)EN_SEG_WORDS) return SG_EUNSUPPORTED;
     hipStream_t st = as_stream(stream);
-    const uint64_t work = agg_capacity > (e.L.NW + 1) * P ? agg_capacity : (e.L.NW + 1) * P;
-    const uint64_t pblocks = ceil_div(work, 256);
-    enc_prep_kernel<<<(unsigned)(pblocks < 4096 ? (pblocks ? pblocks : 1) : 4096), 256, 0, st>>>(e);
+    // a chunk of entries per block where they allow, and enough blocks for
+    // the per-window work
+    uint64_t pblocks = ceil_div(agg_capacity, (uint64_t)WC_CHUNK);
+    const uint64_t fill = ceil_div((e.L.NW + 1) * P, 1024);
+    pblocks = pblocks > fill ? pblocks : fill;
+    pblocks = pblocks < 4096 ? (pblocks ? pblocks : 1) : 4096;
+    if ((uintptr_t)d_agg_idx % 16 == 0)
+        enc_prep_kernel<true><<<(unsigned)pblocks, 256, 0, st>>>(e);
+    else
+        enc_prep_kernel<false><<<(unsigned)pblocks, 256, 0, st>>>(e);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_ENCODE, st);
     enc_kernel<<<(unsigned)e.L.NW, EN_THREADS, 0, st>>>(e);
