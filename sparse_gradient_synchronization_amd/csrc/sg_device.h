@@ -251,4 +251,16 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// LDS written by some lanes of a wave and read by others: a wave executes its
+// LDS operations in order; this keeps the compiler from moving them.  The
+// fences name LDS only: a fence on every address space would also wait for
+// the wave's outstanding global loads and stores (vmcnt 0), which takes the
+// latency of prefetched loads and of written output onto every such point.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 } // namespace sg

@@ -123,18 +123,6 @@ __device__ __forceinline__ void run_range(const MergeParams& p, uint32_t g, uint
     e = b;
 }
 
-// LDS written by some lanes of a wave and read by others: a wave executes its
-// LDS operations in order; this keeps the compiler from moving them.  The
-// fences name LDS only: a fence on every address space would also wait for
-// the wave's outstanding global loads and stores (vmcnt 0), which takes the
-// latency of prefetched loads and of written output onto every such point.
-__device__ __forceinline__ void wave_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
 // runs in position order: r' = w*G + g
 __global__ __launch_bounds__(512) void mg_plan_kernel(MergeParams p)
 {

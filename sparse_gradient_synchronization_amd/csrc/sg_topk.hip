@@ -312,7 +312,8 @@ __device__ __forceinline__ void filter_tile(const TopkParams& p, uint32_t w, uin
 // has one.
 template <int EPV>
 __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w, uint32_t t, uint32_t lo, uint32_t hi,
-                                                 const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+                                                 const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)], uint16_t* lidx,
+                                                 uint32_t* lval)
 {
     constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
     constexpr int CB = EPV == 4 ? 3 : 4; // bits of a per-lane count in [0, EPV]
@@ -322,9 +323,10 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
     char* const sval = reinterpret_cast<char*>(p.slot_val + g * TK_TILE);
     char* const skey = reinterpret_cast<char*>(p.slot_key + g * TK_TILE);
     uint32_t run_ge = 0, run_ca = 0;
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        uint32_t bits[EPV];
+    // the lane's selected elements of every iteration first, their counts
+    // two to a register (16-bit fields: a wave total is at most 64 EPV), and
+    // one DPP scan per register places them all
+    auto unpack = [&](int i, uint32_t (&bits)[EPV]) {
         if constexpr (EPV == 4) {
             bits[0] = x[i].x;
             bits[1] = x[i].y;
@@ -335,36 +337,53 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
 #pragma unroll
             for (int v = 0; v < EPV; ++v) bits[v] = (q[v / 2] >> (16 * (v % 2))) & 0xffffu;
         }
-        const uint32_t e0 = i * (SG_WAVE * EPV) + lane * EPV; // in the tile
-        uint32_t fge = 0, fca = 0;
+    };
+    constexpr int NPK = (ITERS + 1) / 2;
+    uint32_t fge[ITERS], fca[ITERS], pk[NPK];
+#pragma unroll
+    for (int h = 0; h < NPK; ++h) pk[h] = 0;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        uint32_t bits[EPV];
+        unpack(i, bits);
+        fge[i] = 0;
+        fca[i] = 0;
 #pragma unroll
         for (int v = 0; v < EPV; ++v) {
             const uint32_t key = key_of_bits(bits[v], p.bf16);
-            fge |= (uint32_t)(key >= lo) << v;
-            fca |= (uint32_t)(key >= lo && key <= hi) << v;
+            fge[i] |= (uint32_t)(key >= lo) << v;
+            fca[i] |= (uint32_t)(key >= lo && key <= hi) << v;
         }
-        const uint32_t c = (uint32_t)__popc(fge);
-        uint32_t pos = run_ge;
+        pk[i / 2] |= (uint32_t)__popc(fge[i]) << (16 * (i % 2));
+    }
+    uint32_t ex[NPK], tot[NPK];
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            const uint64_t m = ballot((c >> b) & 1u);
-            pos += count_below(m) << b;
-            run_ge += popc64(m) << b;
-        }
-        for (uint32_t f = fge; ballot(f != 0);) {
+    for (int h = 0; h < NPK; ++h) {
+        const uint32_t inc = wave_incl_scan(pk[h]);
+        tot[h] = (uint32_t)__builtin_amdgcn_readlane((int)inc, SG_WAVE - 1);
+        ex[h] = inc - pk[h];
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        uint32_t bits[EPV];
+        unpack(i, bits);
+        const uint32_t e0 = i * (SG_WAVE * EPV) + lane * EPV; // in the tile
+        uint32_t pos = run_ge + ((ex[i / 2] >> (16 * (i % 2))) & 0xffffu);
+        run_ge += (tot[i / 2] >> (16 * (i % 2))) & 0xffffu;
+        for (uint32_t f = fge[i]; ballot(f != 0);) { // into the wave's LDS copy of the tile's slots
             if (f) {
                 const uint32_t v = (uint32_t)__builtin_ctz(f);
                 uint32_t b = bits[0];
 #pragma unroll
                 for (int u = 1; u < EPV; ++u) b = v == (uint32_t)u ? bits[u] : b;
-                *reinterpret_cast<uint16_t*>(sidx + pos * 2u) = (uint16_t)(e0 + v);
-                *reinterpret_cast<uint32_t*>(sval + pos * 4u) = b;
+                lidx[pos] = (uint16_t)(e0 + v);
+                lval[pos] = b;
                 ++pos;
                 f &= f - 1u;
             }
         }
-        if (ballot(fca != 0)) { // candidates are rare: the band is narrow
-            const uint32_t cc = (uint32_t)__popc(fca);
+        if (ballot(fca[i] != 0)) { // candidates are rare: the band is narrow
+            const uint32_t cc = (uint32_t)__popc(fca[i]);
             uint32_t cpos = run_ca;
 #pragma unroll
             for (int b = 0; b < CB; ++b) {
@@ -372,7 +391,7 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
                 cpos += count_below(m) << b;
                 run_ca += popc64(m) << b;
             }
-            for (uint32_t f = fca; ballot(f != 0);) {
+            for (uint32_t f = fca[i]; ballot(f != 0);) {
                 if (f) {
                     const uint32_t v = (uint32_t)__builtin_ctz(f);
                     uint32_t b = bits[0];
@@ -385,6 +404,13 @@ __device__ __forceinline__ void filter_full_tile(const TopkParams& p, uint32_t w
             }
         }
     }
+    // the selected slots out with contiguous stores
+    wave_sync();
+    for (uint32_t j = lane; j < run_ge; j += SG_WAVE) {
+        *reinterpret_cast<uint16_t*>(sidx + j * 2u) = lidx[j];
+        *reinterpret_cast<uint32_t*>(sval + j * 4u) = lval[j];
+    }
+    wave_sync(); // the LDS copy is reused by the wave's next tile
     if (lane == 0) {
         p.tcnt[g] = run_ge;
         p.ccnt[g] = run_ca;
@@ -441,9 +467,10 @@ __device__ __forceinline__ void prefetch_tile(const TopkParams& p, const TileWal
 
 template <int EPV>
 __device__ __forceinline__ void filter_step(const TopkParams& p, const TileWalk& c, uint32_t full_tiles, uint32_t lo,
-                                            uint32_t hi, const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)])
+                                            uint32_t hi, const u32x4 (&x)[TK_TILE / (SG_WAVE * EPV)], uint16_t* lidx,
+                                            uint32_t* lval)
 {
-    if (c.t < full_tiles) filter_full_tile<EPV>(p, c.w, c.t, lo, hi, x);
+    if (c.t < full_tiles) filter_full_tile<EPV>(p, c.w, c.t, lo, hi, x, lidx, lval);
     else filter_tile<EPV, false>(p, c.w, c.t, lo, hi);
 }
 
@@ -451,6 +478,11 @@ template <int EPV>
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_pipe_kernel(TopkParams p)
 {
     constexpr int ITERS = TK_TILE / (SG_WAVE * EPV);
+    // per wave, an LDS copy of a tile's selected slots
+    __shared__ uint16_t sl_idx[TK_THREADS / SG_WAVE][TK_TILE];
+    __shared__ uint32_t sl_val[TK_THREADS / SG_WAVE][TK_TILE];
+    uint16_t* const lidx = sl_idx[threadIdx.x / SG_WAVE];
+    uint32_t* const lval = sl_val[threadIdx.x / SG_WAVE];
     const uint32_t full_tiles = (uint32_t)(p.M / TK_TILE); // tiles t < full_tiles of a row are full
     const uint32_t g0 = blockIdx.x * (TK_THREADS / SG_WAVE) + uniform(threadIdx.x / SG_WAVE);
     const uint32_t stride = gridDim.x * (TK_THREADS / SG_WAVE);
@@ -462,12 +494,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_pipe_kernel(TopkParams
         TileWalk nx = cur;
         nx.next();
         prefetch_tile<EPV>(p, nx, full_tiles, lo_b, hi_b, b);
-        filter_step<EPV>(p, cur, full_tiles, lo_a, hi_a, a);
+        filter_step<EPV>(p, cur, full_tiles, lo_a, hi_a, a, lidx, lval);
         cur = nx;
         if (!cur.valid()) break;
         nx.next();
         prefetch_tile<EPV>(p, nx, full_tiles, lo_a, hi_a, a);
-        filter_step<EPV>(p, cur, full_tiles, lo_b, hi_b, b);
+        filter_step<EPV>(p, cur, full_tiles, lo_b, hi_b, b, lidx, lval);
         cur = nx;
     }
 }
