@@ -305,13 +305,13 @@ def kernel_source_digest(stage):
     return h.hexdigest()
 
 
-def recorded_traffic(stage, workload):
+def recorded_traffic(stage, workload, kernel=None):
     """HBM bytes per launch of the probed kernel, from the rocprofv3 counter
     summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what
     the same counter reads for a plain copy of known size).  None when no
     summary exists for this kernel and workload, or when the kernel's source
     has changed since the counters were taken."""
-    path = os.path.join(HERE, "profiles", "traffic_%s_%s.txt" % (PROBES[stage][1], workload))
+    path = os.path.join(HERE, "profiles", "traffic_%s_%s.txt" % (kernel or PROBES[stage][1], workload))
     if not os.path.exists(path):
         return None
     rec = {}
@@ -866,7 +866,7 @@ def measure_workload(name, args, torch, sg, gen, headline):
         "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, name),
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom, name, prim[dom]),
             "kernel": prim[dom], "stage": dom, "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": dom_avg,
         },
