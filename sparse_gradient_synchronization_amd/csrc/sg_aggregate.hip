@@ -62,6 +62,8 @@ static uint64_t merge_carve(Carver& c, MergeParams* p, int mode)
 // Scalar values and bare indices (D <= 1): tiles of 2^tb keys holding about
 // UN_TARGET entries on average (2^tb the power of two nearest to the span
 // that holds that many), within [2^5, 2^UN_SPAN_LOG_MAX] keys.
+constexpr uint64_t UN_MIN_TILES = 2048;
+
 static void union_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, uint32_t* NT)
 {
     uint32_t b = UN_SPAN_LOG_MAX;
@@ -72,6 +74,9 @@ static void union_tiles(uint32_t G, uint64_t M, uint64_t total, uint32_t* tb, ui
         if (want >= 1.4142135623730951 * (double)(1ull << b)) ++b;
         if (b < 5) b = 5;
         if (b > UN_SPAN_LOG_MAX) b = UN_SPAN_LOG_MAX;
+        // small inputs: enough tiles for every SIMD of the chip to take one
+        // or two, rather than a few long tiles
+        while (b > 5 && (uint64_t)G * ((M + (1ull << b) - 1) >> b) < UN_MIN_TILES) --b;
     }
     *tb = b;
     uint64_t nt = (M + (1ull << b) - 1) >> b;

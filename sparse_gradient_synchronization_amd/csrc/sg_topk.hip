@@ -97,6 +97,21 @@ __global__ __launch_bounds__(256) void topk_gather_kernel(TopkParams p)
     p.samples[(uint64_t)w * TK_SAMPLES + i] = key_of_bits(load_bits(p, (uint64_t)w * M + pos), p.bf16);
 }
 
+// LDS histogram increment by a whole wave (every lane calls it): the lanes
+// that share the first active lane's digit add their count with one atomic,
+// the others one each.  A sample of mostly equal keys (a gradient that is
+// mostly zero) would otherwise queue every lane on one LDS address.
+__device__ __forceinline__ void hist_add_wave(uint32_t* h, bool act, uint32_t d)
+{
+    const uint64_t am = ballot(act);
+    if (am == 0) return;
+    const uint32_t leader = (uint32_t)__builtin_ctzll(am);
+    const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, (int)leader);
+    const uint64_t same = ballot(act && d == dl);
+    if (lane_id() == leader) atomicAdd(&h[dl], popc64(same));
+    if (act && d != dl) atomicAdd(&h[d], 1u);
+}
+
 // Two order statistics of the sample (the band's ends) by MSD radix select in
 // LDS: 11-bit digits, both ranks at once, one block per worker.  Two digits
 // suffice: the band only has to hold the k-th key, so its low end is the
@@ -149,12 +164,15 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
         const uint32_t width = top - shift;
         for (uint32_t i = threadIdx.x; i < 2 * TK_BINS; i += 1024) (&hist[0][0])[i] = 0;
         __syncthreads();
-        for (uint32_t i = threadIdx.x; i < S; i += 1024) {
-            const uint32_t key = s[i];
+        for (uint32_t i0 = 0; i0 < S; i0 += 1024) { // uniform: the waves' ballots below
+            const uint32_t i = i0 + threadIdx.x;
+            const bool valid = i < S;
+            const uint32_t key = valid ? s[i] : 0u;
             const uint32_t d = (key >> shift) & ((1u << width) - 1u);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                if ((top >= 32 ? 0u : (key >> top)) == (top >= 32 ? 0u : (prefix[t] >> top))) atomicAdd(&hist[t][d], 1u);
+                hist_add_wave(hist[t], valid && (top >= 32 ? 0u : (key >> top)) == (top >= 32 ? 0u : (prefix[t] >> top)),
+                              d);
         }
         __syncthreads();
 #pragma unroll
