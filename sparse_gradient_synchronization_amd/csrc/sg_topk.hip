@@ -742,6 +742,204 @@ __global__ __launch_bounds__(TK_THREADS) void topk_pick_kernel(TopkParams p)
     }
 }
 
+// Small inputs (a worker's tiles in at most TK_SMALL_GROUPS groups of 64):
+// every digit pass of the selection in one block per worker, then the tile
+// counts and the group scan, instead of a histogram and a pick launch per
+// digit and two more launches.  The worker's candidates are gathered into
+// LDS once (up to TK_SMALL_CAP of them; more are read from the slots in
+// every pass).
+constexpr uint32_t TK_SMALL_GROUPS = 32;
+constexpr uint32_t TK_SMALL_TILES = TK_SMALL_GROUPS * TK_GROUP;
+constexpr uint32_t TK_SMALL_CAP = 24576;
+__global__ __launch_bounds__(1024) void topk_select_small_kernel(TopkParams p)
+{
+    __shared__ uint32_t h[TK_BINS];
+    __shared__ uint32_t cand[TK_SMALL_CAP];
+    __shared__ uint32_t toff[TK_SMALL_TILES + 1];
+    __shared__ uint32_t scan_lds[1024 / SG_WAVE + 1];
+    __shared__ uint32_t pick_d, pick_above;
+    __shared__ uint32_t sgt[TK_SMALL_GROUPS], seq[TK_SMALL_GROUPS];
+    const uint32_t w = blockIdx.x;
+    const uint32_t wid = uniform(threadIdx.x / SG_WAVE), lane = lane_id();
+    const uint64_t t0 = (uint64_t)w * p.NT; // the worker's first tile
+    SelState st = p.st[w];
+    // the tiles' candidate offsets (two tiles per thread)
+    uint32_t cc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t t = threadIdx.x * 2 + u;
+        cc[u] = t < p.NT ? p.ccnt[t0 + t] : 0u;
+    }
+    uint32_t C;
+    const uint32_t ex = block_excl_scan<1024>(cc[0] + cc[1], scan_lds, &C);
+    if (threadIdx.x * 2 < TK_SMALL_TILES) toff[threadIdx.x * 2] = ex;
+    if (threadIdx.x * 2 + 1 < TK_SMALL_TILES) toff[threadIdx.x * 2 + 1] = ex + cc[0];
+    if (threadIdx.x == 0) toff[p.NT] = C;
+    const bool staged = C <= TK_SMALL_CAP; // uniform
+    __syncthreads();
+    if (staged) { // gather: a wave per tile group, 16 tiles' loads at a time
+        for (uint32_t grp = wid; grp < p.NG; grp += 1024 / SG_WAVE) {
+            const uint32_t tg = grp * TK_GROUP;
+            const uint32_t c = tg + lane < p.NT ? p.ccnt[t0 + tg + lane] : 0u;
+            for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 16) {
+                uint32_t kk[16], k2[16], cj[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
+                    const uint32_t* sk = p.slot_key + (t0 + tg + j0 + u) * TK_TILE;
+                    kk[u] = lane < cj[u] ? sk[lane] : 0u;
+                    k2[u] = SG_WAVE + lane < cj[u] ? sk[SG_WAVE + lane] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    if (cj[u] == 0) continue;
+                    uint32_t* dst = cand + toff[tg + j0 + u];
+                    if (lane < cj[u]) dst[lane] = kk[u];
+                    if (SG_WAVE + lane < cj[u]) dst[SG_WAVE + lane] = k2[u];
+                    for (uint32_t i = 2 * SG_WAVE + lane; i < cj[u]; i += SG_WAVE)
+                        dst[i] = p.slot_key[(t0 + tg + j0 + u) * TK_TILE + i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // the digit passes
+    bool fail = false;
+    while (st.R != 0 && st.top != 0) { // uniform: st is the same in every thread
+        uint32_t shift, width;
+        digit_window(st.top, shift, width);
+        for (uint32_t i = threadIdx.x; i < TK_BINS; i += 1024) h[i] = 0;
+        __syncthreads();
+        if (staged) {
+            for (uint32_t i = threadIdx.x; i < C; i += 1024) {
+                const uint32_t d = cand_digit(st, cand[i], shift, width);
+                if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+            }
+        } else {
+            for (uint32_t grp = wid; grp < p.NG; grp += 1024 / SG_WAVE) {
+                const uint32_t tg = grp * TK_GROUP;
+                const uint32_t c = tg + lane < p.NT ? p.ccnt[t0 + tg + lane] : 0u;
+                for (uint32_t j0 = 0; j0 < (uint32_t)TK_GROUP; j0 += 16) {
+                    uint32_t kk[16], k2[16], cj[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        cj[u] = (uint32_t)__builtin_amdgcn_readlane((int)c, (int)(j0 + u));
+                        const uint32_t* sk = p.slot_key + (t0 + tg + j0 + u) * TK_TILE;
+                        kk[u] = lane < cj[u] ? sk[lane] : 0u;
+                        k2[u] = SG_WAVE + lane < cj[u] ? sk[SG_WAVE + lane] : 0u;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        if (lane < cj[u]) {
+                            const uint32_t d = cand_digit(st, kk[u], shift, width);
+                            if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                        }
+                        if (SG_WAVE + lane < cj[u]) {
+                            const uint32_t d = cand_digit(st, k2[u], shift, width);
+                            if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                        }
+                        for (uint32_t i = 2 * SG_WAVE + lane; i < cj[u]; i += SG_WAVE) { // tiles with more than 128 candidates
+                            const uint32_t d = cand_digit(st, p.slot_key[(t0 + tg + j0 + u) * TK_TILE + i], shift, width);
+                            if (d < (uint32_t)TK_BINS) atomicAdd(&h[d], 1u);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // the digit holding rank R, counted from the top digit down: thread j
+        // owns digits [2j, 2j+2) of the reversed order
+        const uint32_t nbins = 1u << width;
+        constexpr int PER = TK_BINS / 1024;
+        uint32_t loc[PER], sum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint32_t rd = threadIdx.x * PER + i;
+            loc[i] = rd < nbins ? h[nbins - 1u - rd] : 0u;
+            sum += loc[i];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan<1024>(sum, scan_lds, &tot);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint32_t rd = threadIdx.x * PER + i;
+            if (rd < nbins && run < st.R && st.R <= run + loc[i]) {
+                pick_d = nbins - 1u - rd;
+                pick_above = run;
+            }
+            run += loc[i];
+        }
+        __syncthreads();
+        if (tot < st.R) { // cannot happen: candidates were counted
+            fail = true;
+            break;
+        }
+        st.prefix |= pick_d << shift;
+        st.R -= pick_above;
+        st.top = shift;
+        if (shift == 0) {
+            st.T = st.lo + st.prefix;
+            st.need = st.R;
+        }
+        __syncthreads(); // h and the pick are reused by the next digit
+    }
+    if (threadIdx.x == 0) {
+        SelState& g = p.st[w];
+        if (fail) {
+            report_error(kDevErrPartition);
+            g.R = 0;
+        } else {
+            g.prefix = st.prefix;
+            g.R = st.R;
+            g.top = st.top;
+            g.T = st.T;
+            g.need = st.need;
+        }
+    }
+    // then, as the tile-count and scan passes do: per tile the entries above
+    // T and equal to T, per group their sums, and the groups' exclusive
+    // prefixes.  A wave per group, a lane per tile.
+    const uint32_t T = st.T;
+    for (uint32_t grp = wid; grp < p.NG; grp += 1024 / SG_WAVE) {
+        const uint32_t t = grp * TK_GROUP + lane;
+        const bool valid = t < p.NT;
+        uint32_t my_gt = 0, my_eq = 0;
+        if (valid) {
+            const uint32_t c = p.ccnt[t0 + t];
+            my_gt = p.tcnt[t0 + t] - c;
+            if (staged) {
+                for (uint32_t i = toff[t]; i < toff[t] + c; ++i) {
+                    my_gt += cand[i] > T;
+                    my_eq += cand[i] == T;
+                }
+            } else {
+                const uint32_t* sk = p.slot_key + (t0 + t) * TK_TILE;
+                for (uint32_t i = 0; i < c; ++i) {
+                    const uint32_t key = sk[i];
+                    my_gt += key > T;
+                    my_eq += key == T;
+                }
+            }
+            p.gtx[t0 + t] = my_gt;
+            p.eqx[t0 + t] = my_eq;
+        }
+        const uint32_t sg = wave_sum(my_gt), se = wave_sum(my_eq);
+        if (lane == 0) {
+            sgt[grp] = sg;
+            seq[grp] = se;
+        }
+    }
+    __syncthreads();
+    if (wid == 0) { // at most TK_SMALL_GROUPS < 64 groups: one wave scan each
+        const uint32_t a = lane < p.NG ? sgt[lane] : 0u, b = lane < p.NG ? seq[lane] : 0u;
+        const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+        if (lane < p.NG) {
+            p.ggt[(uint64_t)w * p.NG + lane] = ia - a;
+            p.geq[(uint64_t)w * p.NG + lane] = ib - b;
+        }
+    }
+}
+
 // --------------------------------------------------------------------------
 // 5. counts per tile, per-worker scan, ordered write
 // --------------------------------------------------------------------------
@@ -1049,18 +1247,25 @@ extern "C" int sg_topk_to_coo(const void* d_dense, sg_dtype dt, uint32_t n, uint
         topk_totals_kernel<<<n, 1024, 0, st>>>(p, pass);
         SG_TRY_LAUNCH();
     }
-    const unsigned hgrid = n * (unsigned)ceil_div((uint64_t)p.NG * (TK_GROUP / TK_HIST_TPW), TK_THREADS / SG_WAVE);
-    for (int pass = 0; pass < 3; ++pass) {
-        topk_hist_kernel<<<hgrid, TK_THREADS, 0, st>>>(p);
+    if (p.NG <= TK_SMALL_GROUPS) {
+        topk_select_small_kernel<<<n, 1024, 0, st>>>(p);
         SG_TRY_LAUNCH();
-        topk_pick_kernel<<<n, TK_THREADS, 0, st>>>(p);
-        SG_TRY_LAUNCH();
+    } else {
+        const unsigned hgrid = n * (unsigned)ceil_div((uint64_t)p.NG * (TK_GROUP / TK_HIST_TPW), TK_THREADS / SG_WAVE);
+        for (int pass = 0; pass < 3; ++pass) {
+            topk_hist_kernel<<<hgrid, TK_THREADS, 0, st>>>(p);
+            SG_TRY_LAUNCH();
+            topk_pick_kernel<<<n, TK_THREADS, 0, st>>>(p);
+            SG_TRY_LAUNCH();
+        }
     }
     const unsigned wgridw = (unsigned)ceil_div((uint64_t)n * p.NG * TK_WRITE_WAVES, TK_THREADS / SG_WAVE);
-    topk_tilecount_kernel<<<(unsigned)ceil_div((uint64_t)n * p.NG, TK_THREADS / SG_WAVE), TK_THREADS, 0, st>>>(p);
-    SG_TRY_LAUNCH();
-    topk_scan_kernel<<<n, 1024, 0, st>>>(p);
-    SG_TRY_LAUNCH();
+    if (p.NG > TK_SMALL_GROUPS) { // the small-input selection also counted the tiles
+        topk_tilecount_kernel<<<(unsigned)ceil_div((uint64_t)n * p.NG, TK_THREADS / SG_WAVE), TK_THREADS, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+        topk_scan_kernel<<<n, 1024, 0, st>>>(p);
+        SG_TRY_LAUNCH();
+    }
     probe_begin(SG_PROBE_TOPK_WRITE, st);
     if (p.bf16) topk_write_kernel<true><<<wgridw, TK_THREADS, 0, st>>>(p);
     else topk_write_kernel<false><<<wgridw, TK_THREADS, 0, st>>>(p);
