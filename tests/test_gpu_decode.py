@@ -66,6 +66,33 @@ def test_decode_empty_full_and_ragged():
     _roundtrip(*_agg_of(np.array([0, M - 1]), P, 4), M, 4)
 
 
+def test_decode_ignores_padding_bits():
+    """Bits past a class's size in its last word (never set by the encoder)
+    are not indices: decode counts and emits only the class's members."""
+    need_gpu()
+    M, P, seed = 50021, 7, 12
+    rng = np.random.default_rng(77)
+    a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.4), P, seed)
+    cmap = sg.sg_classmap_build(M, P, seed)
+    bm, wo = sg.sg_encode(to_dev_u32(a), to_dev_u64(o), M, cmap)
+    torch.cuda.synchronize()
+    words = host_u32(bm).copy()
+    woff = host_u64(wo)
+    sizes = np.bincount(oracle.h0(np.arange(M, dtype=np.uint32), seed, P), minlength=P)
+    dirty = 0
+    for p in range(P):
+        r = int(sizes[p]) % 32
+        if r and woff[p + 1] > woff[p]:
+            words[woff[p + 1] - 1] |= np.uint32(0xffffffff) << np.uint32(r)  # every padding bit set
+            dirty += 1
+    assert dirty > 0
+    out, off = sg.sg_decode(to_dev_u32(words), M, P, cmap, capacity=max(a.size, 1))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u64(off), o)
+    assert np.array_equal(host_u32(out)[: a.size], a)
+    assert sg.sg_device_error() == 0
+
+
 def test_decode_config3_aggregate():
     # the DGC-style workload's aggregate, from the oracle, through encode and decode
     c = gen.config3(rows=512, cols=11008)
