@@ -170,6 +170,7 @@ struct EncParams {
     uint64_t bitmap_words;
     uint64_t* word_off_out;
     uint64_t* cur;     // [(NW+1) * P] first aggregated entry of partition p at or after window w's first key
+    uint32_t* side;    // group encode: [groups][P][2] a group's bits in its first and last word when shared
 };
 
 // class-p mask of one chunk from its planes (valid = keys of the chunk below M)
@@ -332,9 +333,10 @@ __device__ bool window_cursor_pass(const uint32_t* idx, uint64_t capacity, const
 
 // Window cursors (the pass above, at the class map's window size), the
 // cursors of empty partitions, and the bitmap words that two neighbouring
-// windows share zeroed (the encode kernel merges them with atomicOr).
+// groups of gw windows share zeroed (the encode kernels merge them with
+// atomicOr).
 template <bool VEC>
-__global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
+__global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e, uint32_t gw)
 {
     __shared__ uint64_t offs[257];
     load_agg_offsets(e, offs);
@@ -342,10 +344,10 @@ __global__ __launch_bounds__(256) void enc_prep_kernel(EncParams e)
     const uint64_t NW = e.L.NW;
     window_cursor_pass<VEC>(e.agg_idx, e.agg_cap, offs, P, (uint32_t)NW, (uint32_t)__builtin_ctzll(e.L.W), e.cur);
     const uint32_t tid32 = blockIdx.x * 256 + threadIdx.x, nth32 = gridDim.x * 256;
-    for (uint32_t i = tid32; i < (uint32_t)(NW * P); i += nth32) {
+    for (uint32_t i = tid32; gw != 0 && i < (uint32_t)(NW * P); i += nth32) {
         const uint32_t w = i / P;
         const uint32_t p = i % P;
-        if (w == 0) continue;
+        if (gw == 0 || w == 0 || w % gw != 0) continue; // only words shared by two groups of gw windows
         const uint32_t a = e.q.cpre[(uint64_t)w * P + p];
         if ((a & 31u) == 0 || a >= e.q.class_size[p]) continue;
         const uint64_t gw = e.q.word_off[p] + (a >> 5);
@@ -564,6 +566,419 @@ __global__ __launch_bounds__(EN_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 }
 
 
+// ---------------------------------------------------------------------------
+// Group encode, 2 <= P <= 16 and at least 2048 groups: a wave per group of
+// G consecutive windows (G = 4 for 9..16 classes, else 1), no block barrier.
+// Loads run a window ahead (planes, cursors, the first rounds of keys).  Per
+// window the wave
+//   a) splits the planes of the window's 128 chunks (two per lane) into the
+//      class masks of both chunks (one AND per mask and plane level), counts
+//      every class in them as 16-bit fields packed two classes to a register
+//      and scans those registers over the lanes: each chunk's LDS record holds
+//      its planes and its per-class count of the window's keys before it;
+//   b) takes the window's aggregated keys in rounds of 64 per partition: a
+//      round's keys are laid end to end in LDS with their class, and each
+//      lane then takes a run of them (the lanes of one step far apart, so
+//      their bits rarely share a word): a key's bit is its rank in its class
+//      (the class's bits before the window, the chunk's prefix, the class
+//      members before it in the chunk), OR-ed into an LDS copy of the group's
+//      bitmap words.
+// After the group the words go out class by class, each class's bits of the
+// group one contiguous run written with consecutive lanes on consecutive
+// words (for 16 classes and G = 4 about 32 words, 128 bytes).  The first and
+// last word of a run may hold bits of a neighbouring group: those go to a
+// side buffer, and enc_fix_kernel writes each such word once, as the OR of
+// every group's part (no global atomics, nothing zeroed beforehand).
+// ---------------------------------------------------------------------------
+constexpr int EG_WAVES = 4; // waves per block, each on a group of its own
+constexpr uint32_t EG_NCW = 128; // chunks of a class-map window (P <= 16)
+
+template <int NB>
+struct EgShape {
+    static constexpr int NCLS = 1 << NB;                            // class ids the planes can hold
+    static constexpr int STRIDE = NB == 1 ? 1 : (NB == 2 ? 2 : 4);  // plane words per chunk in the class map
+    static constexpr int NPK = NCLS / 2;                            // prefix words per chunk: two 16-bit counts
+    static constexpr int REC = STRIDE + NPK;                        // LDS words per chunk record
+    static constexpr uint32_t G = NB == 4 ? 4 : 1;                  // windows per group (measured best)
+    static constexpr uint32_t SEG = G * EG_NCW + 2 * NCLS;          // bitmap words of a group, at most
+};
+
+// plane words of chunk c (c <= NC: the class map holds NC + 1 chunks)
+template <int NB>
+__device__ __forceinline__ void eg_load_planes(const uint32_t* planes, uint64_t c, uint32_t (&pl)[4])
+{
+    using S = EgShape<NB>;
+    if (S::STRIDE == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(planes + c * 4);
+        pl[0] = v.x; pl[1] = v.y; pl[2] = v.z; pl[3] = v.w;
+    } else if (S::STRIDE == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(planes + c * 2);
+        pl[0] = v.x; pl[1] = v.y; pl[2] = 0u; pl[3] = 0u;
+    } else {
+        pl[0] = planes[c]; pl[1] = 0u; pl[2] = 0u; pl[3] = 0u;
+    }
+}
+
+// class masks of one chunk: m[k] = the chunk's keys of class k
+template <int NB>
+__device__ __forceinline__ void eg_masks(const uint32_t (&pl)[4], uint32_t valid, uint32_t (&m)[1 << NB])
+{
+    m[0] = valid;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int k = (1 << b) - 1; k >= 0; --k) { // class id bit b set: m & plane_b
+            m[k + (1 << b)] = m[k] & pl[b];
+            m[k] &= ~pl[b];
+        }
+    }
+}
+
+// rounds 0 .. KR-1 of every partition's keys of a window whose entries start
+// at tlo[p] (LDS; partitions past P hold entry 0 and are never used)
+template <int NB, int KR>
+__device__ __forceinline__ void eg_first_loads(const uint32_t* keys, uint64_t last, const uint64_t* tlo,
+                                               uint32_t (&kreg)[1 << NB][KR])
+{
+#pragma unroll
+    for (int p = 0; p < (1 << NB); ++p)
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const uint64_t i = tlo[p] + (uint64_t)r * SG_WAVE + lane_id();
+            kreg[p][r] = keys[i < last ? i : last];
+        }
+}
+
+// RR rounds of a window's keys: entries 64 r0 .. 64 (r0 + RR) - 1 of every
+// partition's range (key[p][q] in lane l: entry 64 (r0 + q) + l of partition
+// p; cnt in lane p: the window's count of partition p).  The keys are first
+// laid end to end in LDS, each as its window offset and its class
+// (o | p << 16; offset 0xffff: outside the window), then every lane takes
+// whole staged keys, four at a time with all their LDS reads issued
+// together: the bit of a key is its rank in its class (the class's bits
+// before the window, tab[p].x, plus the chunk's prefix and the class members
+// before it inside the chunk), OR-ed into the group's LDS words.  A key
+// outside the window, not of its class, or with a bit outside its class's
+// words sets `bad`.
+template <int NB, int RR>
+__device__ __forceinline__ void eg_rounds(const uint4* tab, const uint32_t* rec, uint32_t* seg, uint32_t* stage,
+                                          uint32_t wstart, uint32_t r0, const uint32_t (&key)[1 << NB][RR],
+                                          uint32_t cnt, bool cl, bool& bad)
+{
+    using S = EgShape<NB>;
+    constexpr uint32_t W = EG_NCW * 32u;
+    constexpr uint32_t SKIP = 0xffffffffu;
+    const uint32_t lane = lane_id();
+    const uint32_t rem = cl && cnt > r0 * SG_WAVE ? cnt - r0 * SG_WAVE : 0u;
+    const uint32_t c = rem < RR * SG_WAVE ? rem : RR * SG_WAVE;
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t off = incl - c;
+    const uint32_t K = lane_value(incl, SG_WAVE - 1);
+#pragma unroll
+    for (int p = 0; p < (1 << NB); ++p) {
+        const uint32_t cp = lane_value(c, p), op = lane_value(off, p);
+#pragma unroll
+        for (int q = 0; q < RR; ++q) {
+            const uint32_t o = key[p][q] - wstart;
+            if (q * SG_WAVE + lane < cp) stage[op + q * SG_WAVE + lane] = (o < W ? o : 0xffffu) | ((uint32_t)p << 16);
+        }
+    }
+    wave_sync();
+    // lane l takes staged keys l Kq .. l Kq + Kq - 1 (Kq odd): the lanes of
+    // one step hold keys Kq apart, so their bits rarely share an LDS word
+    // (same-word atomics serialize), and the stage reads hit distinct banks
+    const uint32_t Kq = ((K + SG_WAVE - 1) / SG_WAVE) | 1u;
+    for (uint32_t i0 = 0; i0 < Kq; i0 += 4) {
+        uint32_t u[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t j = lane * Kq + i0 + q;
+            const bool in = i0 + q < Kq && j < K;
+            u[q] = stage[in ? j : 0];
+            u[q] = in ? u[q] : SKIP;
+        }
+        uint4 t[4], pv[4];
+        uint32_t pre[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t o = u[q] & 0xffffu, p = (u[q] >> 16) & 0xffu;
+            const uint32_t ch = o < W ? (o >> 5) : 0u;
+            const uint32_t* rp = rec + ch * S::REC;
+            t[q] = tab[p < (1u << NB) ? p : 0u]; // x: base bit, y: first word, z: words
+            if (S::STRIDE == 4) pv[q] = *reinterpret_cast<const uint4*>(rp);
+            else if (S::STRIDE == 2) pv[q] = make_uint4(rp[0], rp[1], 0u, 0u);
+            else pv[q] = make_uint4(rp[0], 0u, 0u, 0u);
+            pre[q] = reinterpret_cast<const uint16_t*>(rp + S::STRIDE)[p < (1u << NB) ? p : 0u];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (u[q] == SKIP) continue;
+            const uint32_t o = u[q] & 0xffffu, p = u[q] >> 16;
+            const uint32_t pl[4] = {pv[q].x, pv[q].y, pv[q].z, pv[q].w};
+            // the class-p members of the chunk: plane b where p has bit b, else its complement
+            uint32_t m = 0xffffffffu;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) m &= pl[b] ^ (((p >> b) & 1u) - 1u);
+            const uint32_t bit = o & 31u;
+            const uint32_t pos = t[q].x + pre[q] + __popc(m & ((1u << bit) - 1u));
+            if (o >= W || !((m >> bit) & 1u) || (pos >> 5) - t[q].y >= t[q].z) {
+                bad = true;
+                continue;
+            }
+            atomicOr(&seg[pos >> 5], 1u << (pos & 31u));
+        }
+    }
+    wave_sync(); // the stage is read before the next round writes it
+}
+
+template <int NB, int KR>
+__global__ __launch_bounds__(EG_WAVES * SG_WAVE) void enc_group_kernel(EncParams e, uint64_t NG)
+{
+    using S = EgShape<NB>;
+    constexpr int NCLS = S::NCLS;
+    constexpr uint32_t W = EG_NCW * 32u;
+    __shared__ __align__(16) uint32_t rec_all[EG_WAVES][EG_NCW * S::REC];
+    __shared__ __align__(16) uint32_t seg_all[EG_WAVES][S::SEG];
+    __shared__ __align__(16) uint32_t stage_all[EG_WAVES][NCLS * SG_WAVE * KR];
+    __shared__ __align__(16) uint4 tab_all[EG_WAVES][NCLS];
+    __shared__ uint64_t tlo_all[EG_WAVES][2][NCLS];
+    const uint32_t wv = threadIdx.x / SG_WAVE, lane = lane_id();
+    uint32_t* rec = rec_all[wv];
+    uint32_t* seg = seg_all[wv];
+    uint32_t* stage = stage_all[wv];
+    uint4* tab = tab_all[wv];
+    const uint64_t g = (uint64_t)blockIdx.x * EG_WAVES + wv;
+    if (g >= NG) return; // the whole wave: nothing below waits for other waves
+    const CmapLayout& L = e.L;
+    const uint32_t P = L.P;
+    const uint64_t NW = L.NW;
+    const uint64_t w0 = g * S::G;
+    const uint64_t w1 = w0 + S::G < NW ? w0 + S::G : NW;
+    const uint64_t cap = e.agg_cap;
+    const bool cl = lane < P; // lane p holds class p's values
+    const uint32_t pc = cl ? lane : 0u;
+
+    if (g == 0) {
+        if (lane <= P) e.word_off_out[lane] = e.q.word_off[lane];
+        if (lane == 0) {
+            const CmapHeader h = *e.q.hdr;
+            if (h.magic != CM_MAGIC || h.P != P || h.M != L.M) report_error(kDevErrCmap);
+        }
+    }
+
+    // the class's bits [A, B) of the group, its words, the partition's entries
+    uint32_t A = e.q.cpre[w0 * P + pc], B = e.q.cpre[w1 * P + pc];
+    uint64_t s = e.agg_off[pc], en = e.agg_off[pc + 1];
+    uint64_t lo = e.cur[w0 * P + pc], hi = e.cur[(w0 + 1) * P + pc];
+    if (!cl) { // lanes past P: an empty class
+        A = B = 0;
+        s = en = lo = hi = 0;
+    }
+    s = s > cap ? cap : s;
+    en = en > cap ? cap : (en < s ? s : en);
+    lo = lo < s ? s : (lo > en ? en : lo);
+    hi = hi < lo ? lo : (hi > en ? en : hi);
+    const uint32_t nw = B > A ? ((B - 1u) >> 5) - (A >> 5) + 1u : 0u;
+    const uint32_t nincl = wave_incl_scan(nw);
+    const uint32_t so = nincl - nw;
+    const uint32_t nseg = lane_value(nincl, SG_WAVE - 1);
+    if (nseg > S::SEG) { // cannot happen with a valid class map
+        if (lane == 0) report_error(kDevErrCmap);
+        return;
+    }
+    uint32_t cw = A; // the class's bits before the window
+    const uint32_t segbase = 32u * so - 32u * (A >> 5);
+
+    // Loads run a window ahead: window w's planes, cursors and first key
+    // rounds are issued while window w - 1 is worked on.  The window loop is
+    // unrolled with two register sets used in turn, so no loaded register
+    // is copied (a copy would wait for the load at once).
+    uint32_t pl[2][8];
+    uint32_t kreg[2][NCLS][KR];
+    uint64_t hin[2];
+    uint32_t cwn[2];
+    // every load below is unconditional (clamped indices, a one-word stand-in
+    // for an empty aggregate), so the compiler waits for each where it is
+    // used and not at a branch
+    const uint32_t* keys = cap > 0 ? e.agg_idx : reinterpret_cast<const uint32_t*>(e.q.word_off);
+    const uint64_t klast = cap > 0 ? cap - 1 : 0;
+    auto issue = [&](int set, uint64_t w, uint64_t* tl) {
+        w = w < NW ? w : NW - 1;
+        const uint64_t ca = w * EG_NCW + 2 * lane, cb = ca + 1;
+        uint32_t pa[4], pb[4];
+        eg_load_planes<NB>(e.q.planes, ca < L.NC ? ca : L.NC, pa);
+        eg_load_planes<NB>(e.q.planes, cb < L.NC ? cb : L.NC, pb);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pl[set][b] = pa[b];
+            pl[set][4 + b] = pb[b];
+        }
+        eg_first_loads<NB, KR>(keys, klast, tl, kreg[set]);
+        hin[set] = e.cur[((w + 2 <= NW ? w + 2 : NW)) * P + pc];
+        cwn[set] = e.q.cpre[(w + 1) * P + pc];
+    };
+    for (uint32_t i = lane * 4; i < nseg; i += SG_WAVE * 4)
+        *reinterpret_cast<uint4*>(&seg[i]) = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < (uint32_t)NCLS) tlo_all[wv][0][lane] = lo;
+    wave_sync();
+    issue(0, w0, tlo_all[wv][0]);
+
+    bool bad = false;
+#pragma unroll
+    for (uint32_t wi = 0; wi < S::G; ++wi) {
+        const uint64_t w = w0 + wi;
+        if (w >= w1) break;
+        const int cs = wi & 1, ns = cs ^ 1;
+        const uint32_t wstart = (uint32_t)(w * W);
+        const uint64_t* tlo = tlo_all[wv][cs];
+        const uint32_t cnt = (uint32_t)(hi - lo > W ? W : hi - lo); // at most W keys fall in a window (valid input)
+        // the next window's loads (its keys start where this window's end)
+        if (wi + 1 < S::G) { // (past the group's last window: loads of a window not used)
+            if (lane < (uint32_t)NCLS) tlo_all[wv][ns][lane] = hi;
+            wave_sync();
+            issue(ns, w + 1, tlo_all[wv][ns]);
+        }
+        // a) class counts of the lane's two chunks, 16-bit fields two classes
+        //    to a register; their exclusive scan over the lanes
+        const uint64_t ca = w * EG_NCW + 2 * lane, cb = ca + 1;
+        uint32_t pa[4], pb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pa[b] = pl[cs][b];
+            pb[b] = pl[cs][4 + b];
+        }
+        uint32_t cpa[S::NPK], tot[S::NPK];
+        {
+            uint32_t m[NCLS];
+            eg_masks<NB>(pa, chunk_valid(L, ca), m);
+#pragma unroll
+            for (int i = 0; i < S::NPK; ++i) cpa[i] = __popc(m[2 * i]) | (__popc(m[2 * i + 1]) << 16);
+            eg_masks<NB>(pb, chunk_valid(L, cb), m);
+#pragma unroll
+            for (int i = 0; i < S::NPK; ++i) tot[i] = cpa[i] + (__popc(m[2 * i]) | (__popc(m[2 * i + 1]) << 16));
+        }
+        if (lane < (uint32_t)NCLS) tab[lane] = make_uint4(segbase + cw, so, nw, 0u);
+        {
+            uint32_t* ra = rec + (2 * lane) * S::REC;
+            uint32_t* rb = ra + S::REC;
+            uint32_t va[S::REC], vb[S::REC];
+#pragma unroll
+            for (int b = 0; b < S::STRIDE; ++b) {
+                va[b] = pa[b];
+                vb[b] = pb[b];
+            }
+#pragma unroll
+            for (int i = 0; i < S::NPK; ++i) {
+                const uint32_t ex = wave_incl_scan(tot[i]) - tot[i];
+                va[S::STRIDE + i] = ex;
+                vb[S::STRIDE + i] = ex + cpa[i];
+            }
+            if (S::REC % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < S::REC; q += 4) {
+                    *reinterpret_cast<uint4*>(ra + q) = make_uint4(va[q], va[q + 1], va[q + 2], va[q + 3]);
+                    *reinterpret_cast<uint4*>(rb + q) = make_uint4(vb[q], vb[q + 1], vb[q + 2], vb[q + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < S::REC; ++q) {
+                    ra[q] = va[q];
+                    rb[q] = vb[q];
+                }
+            }
+        }
+        wave_sync();
+        // b) the keys, 64 entries of every partition per round: the rounds
+        //    loaded ahead, then any further rounds (dense windows)
+        const uint32_t maxcnt = wave_max(cl ? cnt : 0u);
+        eg_rounds<NB, KR>(tab, rec, seg, stage, wstart, 0, kreg[cs], cnt, cl, bad);
+        for (uint32_t r = KR; r * SG_WAVE < maxcnt; ++r) {
+            uint32_t kr[NCLS][1];
+#pragma unroll
+            for (int p = 0; p < NCLS; ++p) {
+                const uint64_t i = tlo[p] + r * SG_WAVE + lane;
+                kr[p][0] = keys[i < klast ? i : klast];
+            }
+            eg_rounds<NB, 1>(tab, rec, seg, stage, wstart, r, kr, cnt, cl, bad);
+        }
+        // next window
+        lo = hi;
+        hi = hin[cs] < lo ? lo : (hin[cs] > en ? en : hin[cs]);
+        cw = cwn[cs];
+    }
+    if (bad) report_error(kDevErrPartition);
+    wave_sync();
+    // the group's words, class by class
+    uint64_t csz = 0, wbv = 0;
+    if (cl) {
+        csz = e.q.class_size[pc];
+        wbv = e.q.word_off[pc] + (A >> 5);
+    }
+#pragma unroll
+    for (int p = 0; p < NCLS; ++p) {
+        if ((uint32_t)p >= P) continue;
+        const uint32_t nwp = lane_value(nw, p), sop = lane_value(so, p);
+        const uint32_t Ap = lane_value(A, p), Bp = lane_value(B, p);
+        const uint64_t csize = lane_value64(csz, p), wbase = lane_value64(wbv, p);
+        for (uint32_t j = lane; j < nwp; j += SG_WAVE) {
+            const uint32_t val = seg[sop + j];
+            // a word is shared when it also holds bits of the group before
+            // (its first) or after (its last, unless the class ends there)
+            const bool first = j == 0 && (Ap & 31u) != 0u;
+            const bool last = j == nwp - 1 && (Bp & 31u) != 0u && (uint64_t)Bp < csize;
+            uint32_t* sd = e.side + (g * P + p) * 2;
+            if (first) sd[0] = val;
+            if (last) sd[1] = val;
+            const uint64_t gw = wbase + j;
+            if (!first && !last && gw < e.bitmap_words) e.bitmap[gw] = val;
+        }
+    }
+}
+
+// The words the group encode shares between groups: the word X holding a
+// group's first bit A when A is not at a word start.  The last group with
+// bits in X (its bits run past X, or the class ends in X) writes it: its own
+// first-word bits OR the last-word bits of the groups before it that reach
+// into X.  A thread per (group, class).
+__global__ __launch_bounds__(256) void enc_fix_kernel(EncParams e, uint64_t NG, uint32_t G)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    const uint32_t P = e.L.P;
+    if (t >= NG * P) return;
+    const uint64_t g = t / P;
+    const uint32_t p = (uint32_t)(t % P);
+    const uint64_t NW = e.L.NW;
+    auto start = [&](uint64_t h) -> uint32_t { // class-p bits before group h
+        const uint64_t w = h * G < NW ? h * G : NW;
+        return e.q.cpre[w * P + p];
+    };
+    const uint32_t A = start(g), B = start(g + 1);
+    const uint64_t csize = e.q.class_size[p];
+    if (B <= A || (A & 31u) == 0u) return;
+    const uint32_t X = A >> 5;
+    if (!((uint64_t)B >= 32ull * (X + 1) || (uint64_t)B == csize)) return; // a later group writes X
+    uint32_t v = e.side[(g * P + p) * 2];
+    for (uint64_t h = g; h-- > 0;) {
+        const uint32_t a = start(h), b = start(h + 1);
+        if (b <= 32u * X) break; // no bits in X
+        if (b <= a) continue;    // no bits at all
+        v |= e.side[(h * P + p) * 2 + 1];
+        if ((a >> 5) < X || (a & 31u) == 0u) break; // it starts at or before X's first bit
+    }
+    const uint64_t gw = e.q.word_off[p] + X;
+    if (gw < e.bitmap_words) e.bitmap[gw] = v;
+}
+
+// windows per group of the group encode for this layout (0: the block-per-
+// window encode, for P = 1, P > 16 or fewer windows than fill the chip)
+static uint32_t enc_group_windows(const CmapLayout& L)
+{
+    if (L.P < 2 || L.P > 16 || L.NCW != EG_NCW) return 0;
+    const uint32_t G = L.nbits == 4 ? EgShape<4>::G : (L.nbits == 3 ? EgShape<3>::G : 1u);
+    if (ceil_div(L.NW, G) < 2048) return 0;
+    return G;
+}
+
 } // namespace sg
 
 using namespace sg;
@@ -596,7 +1011,9 @@ extern "C" size_t sg_encode_workspace_bytes(uint64_t M, uint32_t P)
 {
     if (P == 0 || P > 256 || M == 0 || M >= (1ull << 32)) return 0;
     const CmapLayout L = cmap_layout(M, P);
-    return (size_t)(8ull * (L.NW + 1) * P);
+    const uint64_t cur = align_up(8ull * (L.NW + 1) * P, 256);
+    const uint32_t G = enc_group_windows(L);
+    return (size_t)(cur + (G ? 8ull * ceil_div(L.NW, G) * P : 0));
 }
 
 extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, uint64_t agg_capacity, uint64_t M,
@@ -618,6 +1035,7 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     e.bitmap_words = bitmap_words;
     e.word_off_out = d_word_off;
     e.cur = static_cast<uint64_t*>(d_ws);
+    e.side = reinterpret_cast<uint32_t*>(static_cast<char*>(d_ws) + align_up(8ull * (e.L.NW + 1) * P, 256));
     // a window's words never exceed W/32 + P
     if (e.L.W / 32 + P + 2 > (uint64_t)EN_SEG_WORDS) return SG_EUNSUPPORTED;
     hipStream_t st = as_stream(stream);
@@ -627,13 +1045,40 @@ extern "C" int sg_encode(const uint32_t* d_agg_idx, const uint64_t* d_agg_off, u
     const uint64_t fill = ceil_div((e.L.NW + 1) * P, 1024);
     pblocks = pblocks > fill ? pblocks : fill;
     pblocks = pblocks < 4096 ? (pblocks ? pblocks : 1) : 4096;
+    // 2 <= P <= 16 and enough windows: a wave per group of windows, the
+    // shared words merged by a fix-up pass; otherwise a block per window, the
+    // shared words zeroed here and merged with atomicOr
+    const uint32_t nb = e.L.nbits;
+    const uint32_t G = enc_group_windows(e.L);
+    const bool group = G != 0;
     if ((uintptr_t)d_agg_idx % 16 == 0)
-        enc_prep_kernel<true><<<(unsigned)pblocks, 256, 0, st>>>(e);
+        enc_prep_kernel<true><<<(unsigned)pblocks, 256, 0, st>>>(e, group ? 0u : 1u);
     else
-        enc_prep_kernel<false><<<(unsigned)pblocks, 256, 0, st>>>(e);
+        enc_prep_kernel<false><<<(unsigned)pblocks, 256, 0, st>>>(e, group ? 0u : 1u);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_ENCODE, st);
-    enc_kernel<<<(unsigned)e.L.NW, EN_THREADS, 0, st>>>(e);
+    if (group) {
+        const uint64_t NG = ceil_div(e.L.NW, G);
+        const unsigned blocks = (unsigned)ceil_div(NG, (uint64_t)EG_WAVES);
+        // two rounds of 64 keys per partition loaded ahead when the entries
+        // (an upper bound on the union) average more than 80 per partition
+        // and window
+        const bool kr2 = agg_capacity > 80ull * e.L.NW * P;
+        switch (nb * 2 + (kr2 ? 1 : 0)) {
+        case 2: enc_group_kernel<1, 1><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 3: enc_group_kernel<1, 2><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 4: enc_group_kernel<2, 1><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 5: enc_group_kernel<2, 2><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 6: enc_group_kernel<3, 1><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 7: enc_group_kernel<3, 2><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        case 8: enc_group_kernel<4, 1><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        default: enc_group_kernel<4, 2><<<blocks, EG_WAVES * SG_WAVE, 0, st>>>(e, NG); break;
+        }
+        SG_TRY_LAUNCH();
+        enc_fix_kernel<<<(unsigned)ceil_div(NG * P, 256), 256, 0, st>>>(e, NG, G);
+    } else {
+        enc_kernel<<<(unsigned)e.L.NW, EN_THREADS, 0, st>>>(e);
+    }
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_ENCODE, st);
     return SG_OK;

@@ -87,3 +87,32 @@ def test_encode_config1_full():
     oi, ov, po = oracle.hash_partition(c["idx"], None, c["in_off"], c["P"], c["seed"])
     ai, _, _, ao = oracle.aggregate(oi, None, po, c["M"])
     _check(ai, ao, c["M"], c["seed"])
+
+
+# The group encode (2 <= P <= 16 with at least 2048 groups of windows): sizes
+# just past that threshold with a ragged last window, sparse and dense
+# stretches (a window of all keys takes many rounds of 64 per partition),
+# classes with no aggregated key at all.
+_GROUP_M = {2: 2048 * 4096 + 12345, 4: 2048 * 4096 + 1, 5: 2 * 2048 * 4096 + 777, 8: 2 * 2048 * 4096 + 4095,
+            9: 4 * 2048 * 4096 + 4097, 16: 4 * 2048 * 4096 + 31}
+
+
+@pytest.mark.parametrize("P", sorted(_GROUP_M))
+def test_encode_group_path(P):
+    M = _GROUP_M[P]
+    rng = np.random.default_rng(1000 + P)
+    dens = np.where(np.arange(M) < M // 16, 0.6, 0.03)
+    keys = np.flatnonzero(rng.random(M) < dens)
+    dense_run = np.arange(M // 2, M // 2 + 3 * 4096 + 17) # every key of a few windows
+    keys = np.union1d(keys, dense_run)
+    a, o = _agg_of(keys, P, 40 + P)
+    _check(a, o, M, 40 + P)
+
+
+def test_encode_group_path_empty_classes():
+    M, P, seed = 4 * 2048 * 4096 + 100, 16, 9
+    rng = np.random.default_rng(3)
+    keys = np.flatnonzero(rng.random(M) < 0.1).astype(np.uint32)
+    keys = keys[oracle.h0(keys, seed, P) % 3 == 0] # classes 1, 2, 4, 5, ... have nothing
+    a, o = _agg_of(keys, P, seed)
+    _check(a, o, M, seed)
