@@ -291,6 +291,18 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "skip_reduce_scatter": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
 }
 COMMON_SOURCES = ["sg_device.h", "sg_host.h"]
+
+
+def encode_kernel_name(W):
+    """The encode kernel the library picks for the workload: a wave per group
+    of class-map windows (enc_group_kernel, then enc_fix_kernel) for 2..16
+    classes and at least 2048 groups, else a block per window (enc_kernel)."""
+    P, M = W["P"], W["M"]
+    if P < 2 or P > 16:
+        return "enc_kernel"
+    windows = -(-M // 4096)
+    G = 4 if P > 8 else 1
+    return "enc_group_kernel" if -(-windows // G) >= 2048 else "enc_kernel"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -786,6 +798,8 @@ def measure_workload(name, args, torch, sg, gen, headline):
             continue
         if rows and kname == "un_write_kernel":
             kname = "mg_merge_kernel"  # rows (D >= 2) take the merge engine
+        if kname == "enc_kernel":
+            kname = encode_kernel_name(W)
         for s in range(steps):
             L.sg_probe_set(pid, evs[s].start, evs[s].stop)
             step()
@@ -798,6 +812,8 @@ def measure_workload(name, args, torch, sg, gen, headline):
     prim = {nm: PROBES[nm][1] for nm in have if nm in PROBES}
     if rows and "aggregate" in prim:
         prim["aggregate"] = "mg_merge_kernel"
+    if "encode" in prim:
+        prim["encode"] = encode_kernel_name(W)
     dom = args.probe or max(prim, key=lambda nm: kernels[prim[nm]]["avg_ms"])
     log("kernels (ms):", {k: round(v["avg_ms"], 4) for k, v in kernels.items()}, "dominant stage:", dom)
 

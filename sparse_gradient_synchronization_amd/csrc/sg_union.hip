@@ -19,8 +19,8 @@
 //          order (below); keys and sums are then written once, in order, at
 //          the tile's offset, with consecutive lanes on consecutive
 //          addresses.
-// A window holds at most 64 S entries (S slots per lane: 16 in the count
-// pass, 8 in the write pass): the run parts of the tile laid end to end, lane
+// A window holds at most 64 S entries (S = 8 slots per lane in both passes;
+// 16 in the count pass was slower on sparse spans): the run parts of the tile laid end to end, lane
 // l taking entries l, l + 64, l + 128, ... of the window, so every load
 // instruction reads 256 consecutive bytes (split only where one run's part
 // ends and the next begins).  A tile with more entries is taken in several
@@ -40,7 +40,7 @@ namespace sg {
 
 constexpr int UN_WPB = 4;                    // waves per block (each on tiles of its own)
 constexpr int UN_THREADS = UN_WPB * SG_WAVE; // threads per block
-constexpr int UN_SC = 16;                    // entry slots per lane, count pass
+constexpr int UN_SC = 8;                     // entry slots per lane, count pass
 constexpr int UN_SW = 8;                     // entry slots per lane, write pass
 constexpr int UN_CAP = UN_SW * SG_WAVE;      // entries of a write window (distinct keys of a window, at most)
 #ifndef SG_UN_TARGET
