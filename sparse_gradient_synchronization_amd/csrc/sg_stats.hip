@@ -259,8 +259,19 @@ static int stats_dense_run(MergeParams& p, DnParams& d, hipStream_t st, uint64_t
 {
     int rc = fill_u32(d.bm, (uint64_t)d.n * d.words, 0, st);
     if (rc) return rc;
-    const uint64_t chunks = ceil_div(d.total, DN_CHUNK);
-    dn_build_kernel<<<(unsigned)(chunks < DN_BUILD_BLOCKS ? chunks : DN_BUILD_BLOCKS), 256, 0, st>>>(d);
+    // entries per thread: the largest of 16, 8, 4, 2, 1 that still makes
+    // 512 chunks (short lists), 16 otherwise
+    uint32_t u = 16;
+    while (u > 1 && ceil_div(d.total, 256ull * u) < 512) u >>= 1;
+    const uint64_t chunks = ceil_div(d.total, 256ull * u);
+    const unsigned bgrid = (unsigned)(chunks < DN_BUILD_BLOCKS ? chunks : DN_BUILD_BLOCKS);
+    switch (u) {
+    case 16: dn_build_kernel<16><<<bgrid, 256, 0, st>>>(d); break;
+    case 8: dn_build_kernel<8><<<bgrid, 256, 0, st>>>(d); break;
+    case 4: dn_build_kernel<4><<<bgrid, 256, 0, st>>>(d); break;
+    case 2: dn_build_kernel<2><<<bgrid, 256, 0, st>>>(d); break;
+    default: dn_build_kernel<1><<<bgrid, 256, 0, st>>>(d); break;
+    }
     SG_TRY_LAUNCH();
     uint64_t W = ceil_div(d.words, SG_WAVE);
     if (W > DN_MAX_WAVES) W = DN_MAX_WAVES;

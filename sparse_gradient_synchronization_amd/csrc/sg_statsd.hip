@@ -36,7 +36,7 @@ namespace sg {
 constexpr uint32_t DN_MAXN = 16;          // workers
 constexpr uint32_t DN_MAXP = 16;          // parts and hash classes
 constexpr uint32_t DN_MAX_WAVES = 2048;   // waves (partial rows) of the count pass, at most
-constexpr uint32_t DN_CHUNK = 4096;       // list entries per chunk of the build
+constexpr uint32_t DN_CHUNK = 4096;       // list entries per chunk of the build, at most (16 per thread)
 constexpr uint32_t DN_BUILD_BLOCKS = 1024; // build blocks (they stride over the chunks), at most
 constexpr uint32_t DN_SPAN = 8192;        // LDS words of a build block's window of keys
 constexpr uint32_t DN_WINDOWS = 64;       // windows of a worker's run in a build block, at most
@@ -60,7 +60,7 @@ struct DnParams {
     uint64_t wpw;             // words per wave (a multiple of 64)
 };
 
-// A block takes chunks of DN_CHUNK consecutive list entries (all loads of a
+// A block takes chunks of 256 U consecutive list entries (all loads of a
 // chunk at once; blocks stride over the chunks, so the class counts are
 // added to the result once per block) and,
 // for each worker's part of them (a sorted run of keys), ORs their bits into
@@ -69,9 +69,13 @@ struct DnParams {
 // falls there), atomic ORs at its two ends (the neighbouring chunks may have
 // entries in the same words).  A run spanning more than DN_WINDOWS windows,
 // or not ascending, ORs its bits into the bitmap one entry at a time.
+// U entries per thread: 16 for large lists; fewer (chunks of 256 U entries)
+// when the lists are short, so that a small input still spreads over many
+// blocks instead of zeroing and scanning a wide LDS span in a few.
+template <uint32_t U>
 __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
 {
-    constexpr uint32_t U = DN_CHUNK / 256;
+    constexpr uint32_t CHUNK = 256 * U;
     __shared__ uint64_t off[DN_MAXN + 1];
     __shared__ uint32_t hh[DN_MAXN * DN_MAXP];
     __shared__ uint32_t span[DN_SPAN];
@@ -89,8 +93,8 @@ __global__ __launch_bounds__(256) void dn_build_kernel(DnParams d)
     for (uint32_t i = threadIdx.x; i < DN_MAXN * DN_MAXP; i += 256) hh[i] = 0;
     __syncthreads();
     const uint32_t hseed = classes ? d.seed_at[0] : 0u;
-    for (uint64_t c0 = (uint64_t)blockIdx.x * DN_CHUNK; c0 < d.total; c0 += (uint64_t)gridDim.x * DN_CHUNK) {
-        const uint32_t len_c = (uint32_t)(d.total - c0 < DN_CHUNK ? d.total - c0 : DN_CHUNK);
+    for (uint64_t c0 = (uint64_t)blockIdx.x * CHUNK; c0 < d.total; c0 += (uint64_t)gridDim.x * CHUNK) {
+        const uint32_t len_c = (uint32_t)(d.total - c0 < CHUNK ? d.total - c0 : CHUNK);
         const uint32_t* const src = d.idx + c0;
         uint32_t key[U]; // entry r = j * 256 + threadIdx.x of the chunk
 #pragma unroll
