@@ -93,8 +93,8 @@ def test_encode_config1_full():
 # just past that threshold with a ragged last window, sparse and dense
 # stretches (a window of all keys takes many rounds of 64 per partition),
 # classes with no aggregated key at all.
-_GROUP_M = {2: 2048 * 4096 + 12345, 4: 2048 * 4096 + 1, 5: 2 * 2048 * 4096 + 777, 8: 2 * 2048 * 4096 + 4095,
-            9: 4 * 2048 * 4096 + 4097, 16: 4 * 2048 * 4096 + 31}
+_GROUP_M = {2: 2048 * 4096 + 12345, 3: 2048 * 4096 + 5, 4: 2048 * 4096 + 1, 5: 2048 * 4096 + 777,
+            8: 2048 * 4096 + 4095, 9: 4 * 2048 * 4096 + 4097, 13: 4 * 2048 * 4096 + 999, 16: 4 * 2048 * 4096 + 31}
 
 
 @pytest.mark.parametrize("P", sorted(_GROUP_M))
