@@ -571,6 +571,73 @@ def next_rows(name, W, L, torch, sg, steps):
     return out
 
 
+def batched_mode(name, L, torch, sg, steps):
+    """Batched mode of the two latency-bound workloads, labelled as such (one
+    step of one instance leaves the GPU mostly idle): B independent
+    instances of the workload's first stage in one launch, since a call
+    takes any number of workers.  Workload 1: top-k of B x 4 dense gradients
+    (instance b's four workers draw their Zipf(1.1) nonzeros from seed
+    namespace 1000 + b); workload 2: the hash partition of B x 8 workers'
+    64-wide rows (namespace 2000 + b).  Two instances are checked against the
+    same call on that instance alone (bit-exact)."""
+    import numpy as np
+    import gen
+    dev = torch.device("cuda", 0)
+    res = {"label": "batched mode: B independent instances of the first stage in one launch"}
+    if name == "cfg1":
+        B, n, M = 64, 4, 1 << 20
+        k = M // 100
+        dense_h = np.empty((B * n, M), dtype=np.float32)
+        for b in range(B):
+            idx, off, val = gen.coo_zipf(1000 + b, n, M, k, 1.1, nonzero=True)
+            dense_h[b * n:(b + 1) * n] = gen.dense_from_coo(n, M, idx, off, val)
+        dense = torch.from_numpy(dense_h).to(dev)
+        del dense_h
+        box = {}
+        ws = torch.empty(L.sg_topk_workspace_bytes(B * n, M, k, 0), dtype=torch.uint8, device=dev)
+
+        def run():
+            box["r"] = sg.sg_topk_to_coo(dense, k, workspace=ws)
+        ms, _ = time_call(L, torch, run, steps)
+        bi, bv = box["r"]
+        same = True
+        for b in (0, B - 1):
+            si, sv = sg.sg_topk_to_coo(dense[b * n:(b + 1) * n].contiguous(), k)
+            same = same and torch.equal(si, bi[b * n:(b + 1) * n]) and torch.equal(sv, bv[b * n:(b + 1) * n])
+        nbytes = B * n * M * 4 + B * n * k * 8
+        res.update({"stage": "topk_to_coo", "B": B, "workers": B * n, "ms": ms, "us_per_instance": ms * 1e3 / B,
+                    "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "matches_single_instance": bool(same)})
+    elif name == "cfg2":
+        B, n, R, cnt, D, P, seed = 32, 8, 1_000_000, 4096, 64, 8, 2
+        idxs, vals = [], []
+        for b in range(B):
+            idx, off, val = gen.coo_zipf(2000 + b, n, R, cnt, 1.05, D=D, sigma=0.01)
+            idxs.append(idx)
+            vals.append(val)
+        idx = torch.from_numpy(np.concatenate(idxs).view(np.int32)).to(dev)
+        val = torch.from_numpy(np.concatenate(vals)).to(dev)
+        in_off = torch.arange(B * n + 1, dtype=torch.int64, device=dev) * cnt
+        box = {}
+
+        def run():
+            box["r"] = sg.sg_hash_partition(idx, val, in_off, P, seed)
+        ms, _ = time_call(L, torch, run, steps)
+        pi, pv, po = box["r"]
+        same = True
+        e = n * cnt
+        for b in (0, B - 1):
+            si, sv, so = sg.sg_hash_partition(idx[b * e:(b + 1) * e].contiguous(), val[b * e:(b + 1) * e].contiguous(),
+                                              torch.arange(n + 1, dtype=torch.int64, device=dev) * cnt, P, seed)
+            same = (same and torch.equal(si, pi[b * e:(b + 1) * e]) and torch.equal(sv, pv[b * e:(b + 1) * e])
+                    and torch.equal(so + b * e, po[b * n:(b + 1) * n]))
+        nbytes = 2 * B * n * cnt * (4 + D * 4)
+        res.update({"stage": "hash_partition", "B": B, "workers": B * n, "ms": ms, "us_per_instance": ms * 1e3 / B,
+                    "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "matches_single_instance": bool(same)})
+    return res
+
+
 def alg1_study(L, torch, sg, steps):
     """Algorithm 1's parameter study on a synthetic 214M-element tensor (one
     worker, 1% density, uniform distinct indices, 16 partitions): the time of
@@ -894,6 +961,7 @@ def measure_workload(name, args, torch, sg, gen, headline):
         # each step alone after a cache-flushing write
         rec["cold_ms_per_step"] = cold_steps(torch, run_step, steps)
         rec["cold_value"] = units / (rec["cold_ms_per_step"] * 1e-3)
+        rec["batched"] = batched_mode(name, L, torch, sg, steps)
     if headline and "pull" in W:
         rec["pull_side"] = pull_side(W, L, torch, steps)
     nr = next_rows(name, W, L, torch, sg, steps)
