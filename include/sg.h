@@ -301,7 +301,10 @@ int sg_aggregate(const uint32_t* d_idx, const void* d_val, sg_dtype dt, uint32_t
  *   d_word_off [P+1] uint64 out
  *   d_ws       sg_encode_workspace_bytes(M, P) bytes: per key window of the
  *              class map and partition, where the partition's aggregated
- *              entries of that window begin
+ *              entries of that window begin; for 2 <= P <= 16 over a large
+ *              key space also two words per (group of windows, class): the
+ *              group's bits in bitmap words it shares with its neighbours,
+ *              merged by a second kernel (no global atomics)
  * Limits: 1 <= P <= 256, 1 <= M < 2^32.
  * ------------------------------------------------------------------------ */
 size_t sg_classmap_bytes(uint64_t M, uint32_t P);
