@@ -14,7 +14,11 @@
 //          bitmap words.  Per (chunk, class) pair, the class's members in the
 //          chunk are the set bits of its mask, and their bitmap bits are one
 //          run of that many bits; the k-th set bit of the run is the k-th
-//          member, written at the run's rank plus the set bits before it.
+//          member, written at the run's rank plus the set bits before it;
+//   group  for 2..16 classes and enough windows, a wave per group of
+//          consecutive windows does the emit with no block barrier, each
+//          class's bits of the group loaded once as one contiguous run
+//          (dec_group_kernel below).
 #include "sg_host.h"
 
 namespace sg {
@@ -370,6 +374,243 @@ __global__ __launch_bounds__(DC_THREADS) void dec_emit_kernel(DecParams d)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Group decode, 2 <= P <= 16 and enough groups to fill the chip: a wave per
+// group of G consecutive windows, no block barrier (the mirror image of the
+// group encode).  A class's bits of the group are one contiguous run of its
+// bitmap, so the wave first loads every class's run (all classes' loads in
+// flight together), masked to the class's bits of the group, into LDS with
+// the set bits before each word of the run; the output position of the
+// class's first bit of the group is the ranks pass's prefix of its word plus
+// the set bits below it in that word.  Per window (its planes and class
+// offsets loaded a window ahead, in two register sets used in turn) the
+// lane's two chunks are split into class masks and counted per class, as
+// 16-bit fields two classes to a register, scanned over the lanes; the
+// class-p members of a chunk then own the run of class-p bits at the
+// window's class offset plus the chunk's prefix, and each set bit of that
+// run is written as the key of the matching member.
+// ---------------------------------------------------------------------------
+constexpr int DG_WAVES = 4; // waves per block, each on a group of its own
+
+// windows per group for class ids of nbits bits (measured best: 4 for 9..16
+// classes, where a window's class runs are short; 1 below)
+constexpr int dg_group(uint32_t nbits) { return nbits >= 4 ? 4 : 1; }
+
+template <int NB, int G>
+struct DgShape {
+    static constexpr int NCLS = 1 << NB;
+    static constexpr int NPK = NCLS / 2;                         // prefix registers: two 16-bit counts each
+    static constexpr uint32_t SEG = G * EG_NCW + 2 * NCLS;       // words of a group's class runs, at most
+};
+
+template <int NB, int G>
+__global__ __launch_bounds__(DG_WAVES * SG_WAVE) void dec_group_kernel(DecParams d, uint64_t NG)
+{
+    using S = DgShape<NB, G>;
+    constexpr int NCLS = S::NCLS;
+    constexpr uint32_t W = EG_NCW * 32u;
+    // the runs, and per word the run's set bits before it; two words of
+    // slack past the longest runs: a member run read at a class's end
+    // touches at most the word after it, and is masked to nothing there
+    __shared__ __align__(16) uint32_t seg_all[DG_WAVES][S::SEG + 2];
+    __shared__ __align__(16) uint32_t sx_all[DG_WAVES][S::SEG + 2];
+    const uint32_t wv = threadIdx.x / SG_WAVE, lane = lane_id();
+    uint32_t* seg = seg_all[wv];
+    uint32_t* sx = sx_all[wv];
+    const uint64_t g = (uint64_t)blockIdx.x * DG_WAVES + wv;
+    if (g >= NG) return; // the whole wave: nothing below waits for other waves
+    const CmapLayout& L = d.L;
+    const uint32_t P = L.P;
+    const uint64_t NW = L.NW;
+    const uint64_t w0 = g * G;
+    const uint64_t w1 = w0 + G < NW ? w0 + G : NW;
+    const bool cl = lane < P; // lane p holds class p's values
+    const uint32_t pc = cl ? lane : 0u;
+    const uint64_t nwords = dec_words(d);
+    // every global load is unconditional (clamped index; a one-word stand-in
+    // when the buffer holds no words, whose value is never used), so the
+    // compiler waits for each where it is used and not at a branch
+    const uint32_t* bm = nwords ? d.bitmap : reinterpret_cast<const uint32_t*>(d.q.word_off);
+    const uint64_t blast = nwords ? nwords - 1 : 0;
+
+    uint32_t pl[2][8];
+    uint32_t cwn[2];
+    auto issue = [&](int set, uint64_t w) {
+        w = w < NW ? w : NW - 1;
+        const uint64_t ca = w * EG_NCW + 2 * lane, cb = ca + 1;
+        uint32_t pa[4], pb[4];
+        eg_load_planes<NB>(d.q.planes, ca < L.NC ? ca : L.NC, pa);
+        eg_load_planes<NB>(d.q.planes, cb < L.NC ? cb : L.NC, pb);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pl[set][b] = pa[b];
+            pl[set][4 + b] = pb[b];
+        }
+        cwn[set] = d.q.cpre[(w + 1) * P + pc];
+    };
+    issue(0, w0);
+
+    if (g == 0 && lane <= P) { // the classes' output offsets
+        const uint64_t wo = d.q.word_off[lane];
+        d.out_off[lane] = d.wpre[wo < nwords ? wo : nwords];
+    }
+    // the class's bits [A, B) of the group, its words, their place in LDS
+    uint32_t A = d.q.cpre[w0 * P + pc], B = d.q.cpre[w1 * P + pc];
+    const uint64_t wof = d.q.word_off[pc];
+    if (!cl) A = B = 0; // lanes past P: an empty class
+    const uint32_t nw = B > A ? ((B - 1u) >> 5) - (A >> 5) + 1u : 0u;
+    const uint32_t nincl = wave_incl_scan(nw);
+    const uint32_t so = nincl - nw;
+    const uint32_t nseg = lane_value(nincl, SG_WAVE - 1);
+    if (nseg > S::SEG) { // cannot happen with a valid class map
+        if (lane == 0) report_error(kDevErrCmap);
+        return;
+    }
+    const uint64_t wb = wof + (A >> 5); // the class's first word of the group
+    // first round of every class's run (64 words; a run is about 32 G / P
+    // words long, a longer one takes further rounds below)
+    uint32_t v[NCLS];
+#pragma unroll
+    for (int p = 0; p < NCLS; ++p) {
+        const uint64_t gw = lane_value64(wb, p) + lane;
+        v[p] = bm[gw < blast ? gw : blast];
+    }
+    // output position of the class's first bit of the group
+    uint32_t ob;
+    {
+        const uint32_t f0 = bm[wb < blast ? wb : blast];
+        const uint32_t pre = d.wpre[wb < nwords ? wb : nwords];
+        ob = pre + (uint32_t)__popc((wb < nwords ? f0 : 0u) & ((1u << (A & 31u)) - 1u));
+    }
+    // a class's word j holds class bits [32 q, 32 q + 32), q = A / 32 + j:
+    // keep those in [A, B); words past the buffer's end read as zero
+    auto keep = [&](uint32_t x, uint32_t j, uint32_t nwp, uint32_t Ap, uint32_t Bp, uint64_t wbp) -> uint32_t {
+        const uint32_t base = ((Ap >> 5) + j) << 5;
+        const uint32_t lo = Ap > base ? Ap - base : 0u;
+        const uint32_t rest = Bp - base;
+        uint32_t m = ~((1u << lo) - 1u);
+        if (rest < 32u) m &= (1u << rest) - 1u;
+        return j < nwp && wbp + j < nwords ? x & m : 0u;
+    };
+#pragma unroll
+    for (int p = 0; p < NCLS; ++p) {
+        if ((uint32_t)p >= P) continue; // uniform (a constant trip count: the loop unrolls)
+        const uint32_t nwp = lane_value(nw, p), sop = lane_value(so, p);
+        const uint32_t Ap = lane_value(A, p), Bp = lane_value(B, p);
+        const uint64_t wbp = lane_value64(wb, p);
+        const uint32_t x = keep(v[p], lane, nwp, Ap, Bp, wbp);
+        const uint32_t c = (uint32_t)__popc(x);
+        const uint32_t inc = wave_incl_scan(c);
+        if (lane < nwp) {
+            seg[sop + lane] = x;
+            sx[sop + lane] = inc - c;
+        }
+    }
+    // further rounds of long runs (a class holding most of the group's keys)
+    if (wave_max(nw) > (uint32_t)SG_WAVE) {
+        wave_sync();
+        for (uint32_t p = 0; p < P; ++p) {
+            const uint32_t nwp = lane_value(nw, p), sop = lane_value(so, p);
+            const uint32_t Ap = lane_value(A, p), Bp = lane_value(B, p);
+            const uint64_t wbp = lane_value64(wb, p);
+            for (uint32_t j0 = SG_WAVE; j0 < nwp; j0 += SG_WAVE) { // uniform
+                const uint32_t carry = sx[sop + j0 - 1] + (uint32_t)__popc(seg[sop + j0 - 1]);
+                const uint32_t j = j0 + lane;
+                const uint64_t gw = wbp + j;
+                const uint32_t x = keep(bm[gw < blast ? gw : blast], j, nwp, Ap, Bp, wbp);
+                const uint32_t c = (uint32_t)__popc(x);
+                const uint32_t inc = wave_incl_scan(c);
+                if (j < nwp) {
+                    seg[sop + j] = x;
+                    sx[sop + j] = carry + inc - c;
+                }
+                wave_sync();
+            }
+        }
+    }
+    wave_sync();
+
+    // output positions are ranks of encoded bits, below M < 2^32
+    const uint32_t cap = d.capacity < 0xffffffffull ? (uint32_t)d.capacity : 0xffffffffu;
+    uint32_t cw = A; // the class's bits before the window
+#pragma unroll
+    for (uint32_t wi = 0; wi < (uint32_t)G; ++wi) {
+        const uint64_t w = w0 + wi;
+        if (w >= w1) break;
+        const int cs = wi & 1, ns = cs ^ 1;
+        if (wi + 1 < (uint32_t)G) issue(ns, w + 1); // (past the group's last window: loads not used)
+        const uint64_t ca = w * EG_NCW + 2 * lane, cb = ca + 1;
+        uint32_t pa[4], pb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pa[b] = pl[cs][b];
+            pb[b] = pl[cs][4 + b];
+        }
+        const uint32_t va = chunk_valid(L, ca), vb = chunk_valid(L, cb);
+        // class counts of the lane's two chunks, and their exclusive scan
+        uint32_t cpa[S::NPK], ex[S::NPK];
+        {
+            uint32_t m[NCLS];
+            eg_masks<NB>(pa, va, m);
+#pragma unroll
+            for (int i = 0; i < S::NPK; ++i) cpa[i] = __popc(m[2 * i]) | (__popc(m[2 * i + 1]) << 16);
+            eg_masks<NB>(pb, vb, m);
+#pragma unroll
+            for (int i = 0; i < S::NPK; ++i) {
+                const uint32_t tot = cpa[i] + (__popc(m[2 * i]) | (__popc(m[2 * i + 1]) << 16));
+                ex[i] = wave_incl_scan(tot) - tot;
+            }
+        }
+        // the window's first class bit, from the start of the class's run
+        const uint32_t rb = cw - (A & ~31u);
+#pragma unroll
+        for (int p = 0; p < NCLS; ++p) {
+            if ((uint32_t)p >= P) continue; // uniform (a constant trip count: the loop unrolls)
+            const uint32_t rbp = lane_value(rb, p), sop = lane_value(so, p), obp = lane_value(ob, p);
+            const uint32_t sh = 16u * (p & 1);
+            const uint32_t ea = (ex[p >> 1] >> sh) & 0xffffu;
+            const uint32_t na = (cpa[p >> 1] >> sh) & 0xffffu;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // the chunk's class-p members: plane b where p has bit b, else its complement
+                uint32_t m = h ? vb : va;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) m &= (h ? pb[b] : pa[b]) ^ (((p >> b) & 1u) - 1u);
+                const uint32_t c = (uint32_t)__popc(m);
+                const uint32_t gb = rbp + ea + (h ? na : 0u);
+                const uint32_t k = sop + (gb >> 5), bit = gb & 31u;
+                const uint32_t lo = seg[k], hi = seg[k + 1];
+                uint32_t run = (uint32_t)(((((uint64_t)hi) << 32) | lo) >> bit);
+                if (c < 32u) run &= (1u << c) - 1u;
+                if (run == 0u) continue;
+                // the k-th set bit of the run is the k-th member, at the run's
+                // output position plus the set bits before it
+                uint32_t o = obp + sx[k] + (uint32_t)__popc(lo & ((1u << bit) - 1u));
+                const uint32_t kb = (uint32_t)(w * W) + (2 * lane + h) * 32u;
+                while (run) {
+                    const uint32_t z = __builtin_ctz(run); // members to pass over
+                    run = (run >> z) >> 1;
+                    for (uint32_t i = 0; i < z; ++i) m &= m - 1u;
+                    if (o < cap) d.out_idx[o] = kb + __builtin_ctz(m);
+                    m &= m - 1u;
+                    ++o;
+                }
+            }
+        }
+        cw = cwn[cs];
+    }
+}
+
+// windows per group of the group decode for this layout (0: the block-per-
+// window decode, for P = 1, P > 16 or fewer groups than fill the chip)
+static uint32_t dec_group_windows(const CmapLayout& L)
+{
+    if (L.P < 2 || L.P > 16 || L.NCW != EG_NCW) return 0;
+    const uint32_t G = (uint32_t)dg_group(L.nbits);
+    if (ceil_div(L.NW, G) < 2048) return 0;
+    return G;
+}
+
 // Pull-side scatter: dense [M][D] zero except entries [off[0], off[P]).
 //
 // Scalar values (D == 1) go through key windows of SC_W keys, since an
@@ -644,7 +885,19 @@ extern "C" int sg_decode(const uint32_t* d_bitmap, uint64_t bitmap_words, const 
     else dec_wpre_kernel<false><<<d.NB, 256, 0, st>>>(d);
     SG_TRY_LAUNCH();
     probe_begin(SG_PROBE_DECODE, st);
-    dec_emit_kernel<<<(unsigned)d.L.NW, DC_THREADS, 0, st>>>(d);
+    const uint32_t G = dec_group_windows(d.L);
+    if (G) {
+        const uint64_t NG = ceil_div(d.L.NW, G);
+        const unsigned blocks = (unsigned)ceil_div(NG, DG_WAVES);
+        switch (d.L.nbits) {
+        case 1: dec_group_kernel<1, dg_group(1)><<<blocks, DG_WAVES * SG_WAVE, 0, st>>>(d, NG); break;
+        case 2: dec_group_kernel<2, dg_group(2)><<<blocks, DG_WAVES * SG_WAVE, 0, st>>>(d, NG); break;
+        case 3: dec_group_kernel<3, dg_group(3)><<<blocks, DG_WAVES * SG_WAVE, 0, st>>>(d, NG); break;
+        default: dec_group_kernel<4, dg_group(4)><<<blocks, DG_WAVES * SG_WAVE, 0, st>>>(d, NG); break;
+        }
+    } else {
+        dec_emit_kernel<<<(unsigned)d.L.NW, DC_THREADS, 0, st>>>(d);
+    }
     SG_TRY_LAUNCH();
     probe_end(SG_PROBE_DECODE, st);
     return SG_OK;

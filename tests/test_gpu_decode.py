@@ -66,11 +66,13 @@ def test_decode_empty_full_and_ragged():
     _roundtrip(*_agg_of(np.array([0, M - 1]), P, 4), M, 4)
 
 
-def test_decode_ignores_padding_bits():
+@pytest.mark.parametrize("M,P", [(50021, 7), (2048 * 4096 + 77, 3)])
+def test_decode_ignores_padding_bits(M, P):
     """Bits past a class's size in its last word (never set by the encoder)
-    are not indices: decode counts and emits only the class's members."""
+    are not indices: decode counts and emits only the class's members (the
+    block-per-window and the group decode)."""
     need_gpu()
-    M, P, seed = 50021, 7, 12
+    seed = 12
     rng = np.random.default_rng(77)
     a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.4), P, seed)
     cmap = sg.sg_classmap_build(M, P, seed)
@@ -90,6 +92,61 @@ def test_decode_ignores_padding_bits():
     torch.cuda.synchronize()
     assert np.array_equal(host_u64(off), o)
     assert np.array_equal(host_u32(out)[: a.size], a)
+    assert sg.sg_device_error() == 0
+
+
+# key spaces just past the group decode's threshold (2048 groups of 1
+# window of 4096 keys for 2..8 classes, of 4 windows for 9..16), ragged tails
+_GROUP_M = {2: 2048 * 4096 + 12345, 3: 2048 * 4096 + 5, 4: 2048 * 4096 + 1, 5: 2048 * 4096 + 777,
+            8: 2048 * 4096 + 4095, 9: 4 * 2048 * 4096 + 4097, 13: 4 * 2048 * 4096 + 999,
+            16: 4 * 2048 * 4096 + 31}
+
+
+@pytest.mark.parametrize("P", sorted(_GROUP_M))
+def test_decode_group_path(P):
+    M = _GROUP_M[P]
+    rng = np.random.default_rng(2000 + P)
+    dens = np.where(np.arange(M) < M // 16, 0.6, 0.03)
+    keys = np.flatnonzero(rng.random(M) < dens)
+    keys = np.union1d(keys, np.arange(M // 2, M // 2 + 3 * 4096 + 17))  # every key of a few windows
+    keys = np.union1d(keys, [0, M - 1])
+    a, o = _agg_of(keys, P, 50 + P)
+    _roundtrip(a, o, M, 50 + P)
+
+
+@pytest.mark.parametrize("P", [2, 16])
+def test_decode_group_path_every_key(P):
+    # every bit set: with 2 classes a class's run of a group is 64 or 65
+    # words, past one round of a wave's lanes
+    M = _GROUP_M[P]
+    a, o = _agg_of(np.arange(M), P, 3)
+    _roundtrip(a, o, M, 3)
+
+
+def test_decode_group_path_empty_classes():
+    M, P, seed = 4 * 2048 * 4096 + 100, 16, 9
+    rng = np.random.default_rng(3)
+    keys = np.flatnonzero(rng.random(M) < 0.1).astype(np.uint32)
+    keys = keys[oracle.h0(keys, seed, P) % 3 == 0]  # classes 1, 2, 4, 5, ... have nothing
+    a, o = _agg_of(keys, P, seed)
+    _roundtrip(a, o, M, seed)
+
+
+@pytest.mark.parametrize("M,P", [(100003, 16), (4 * 2048 * 4096 + 31, 16)])
+def test_decode_capacity_short(M, P):
+    """With room for fewer indices than the bitmap holds, decode writes the
+    first `capacity` of them and the full offsets."""
+    need_gpu()
+    seed = 5
+    rng = np.random.default_rng(11)
+    a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.2), P, seed)
+    cmap = sg.sg_classmap_build(M, P, seed)
+    bm, wo = sg.sg_encode(to_dev_u32(a), to_dev_u64(o), M, cmap)
+    cap = a.size // 3 + 7
+    out, off = sg.sg_decode(bm, M, P, cmap, capacity=cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u64(off), o)
+    assert np.array_equal(host_u32(out)[:cap], a[:cap])
     assert sg.sg_device_error() == 0
 
 
