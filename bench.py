@@ -287,7 +287,7 @@ PROBES = {  # stage -> (probe id, kernel name, source files the kernel is built 
     "aggregate": (3, "un_write_kernel", ["sg_union.hip", "sg_merge.hip", "sg_aggregate.hip"]),
     "encode": (4, "enc_kernel", ["sg_encode.hip"]),
     "decode": (9, "dec_emit_kernel", ["sg_decode.hip"]),
-    "scatter_dense": (10, "scatter_window_kernel", ["sg_decode.hip"]),  # scatter_kernel for rows (D > 1)
+    "scatter_dense": (10, "scatter_window_kernel", ["sg_decode.hip"]),  # scatter_rows_kernel for rows (D > 1)
     "skip_reduce_scatter": (5, "skip_rs_kernel", ["sg_skiprs.hip"]),
 }
 COMMON_SOURCES = ["sg_device.h", "sg_host.h"]
@@ -303,6 +303,20 @@ def encode_kernel_name(W):
     windows = -(-M // 4096)
     G = 4 if P > 8 else 1
     return "enc_group_kernel" if -(-windows // G) >= 2048 else "enc_kernel"
+
+
+def decode_kernel_name(W):
+    """The decode emit kernel the library picks: a wave per group of windows
+    (dec_group_kernel; 4 windows for 9..16 classes, else 1) for 2..16 classes
+    and at least 2048 groups, else a block per window (dec_emit_kernel)."""
+    P, M = W["P"], W["M"]
+    if P < 2 or P > 16:
+        return "dec_emit_kernel"
+    windows = -(-M // 4096)
+    G = 4 if P > 8 else 1
+    return "dec_group_kernel" if -(-windows // G) >= 2048 else "dec_emit_kernel"
+
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -466,7 +480,11 @@ def pull_side(W, L, torch, steps):
         nbytes = algorithmic_bytes(W, nm)
         gbps = nbytes / (kms * 1e-3) / 1e9
         ms = sum(a[s].elapsed_time(b[s]) for s in range(steps)) / steps
-        kname = "scatter_kernel" if nm == "scatter_dense" and W.get("D", 1) > 1 else PROBES[nm][1]
+        kname = PROBES[nm][1]
+        if nm == "scatter_dense" and W.get("D", 1) > 1:
+            kname = "scatter_rows_kernel"
+        elif nm == "decode":
+            kname = decode_kernel_name(W)
         out[nm] = {"ms": ms, "kernel": kname, "kernel_ms": kms, "kernel_algorithmic_bytes": nbytes,
                    "kernel_GBps": gbps, "kernel_frac": gbps / HBM_PEAK_GBS}
         if nm == "scatter_dense":  # the whole call: the dense tensor written, the aggregate read

@@ -626,7 +626,8 @@ static uint32_t dec_group_windows(const CmapLayout& L)
 //   fix      if any flag word is set, the plain per-entry scatter over the
 //            windows' output (values at distinct keys are written again,
 //            so the result is the same whatever the cursors were).
-// Rows (D > 1) zero the tensor and copy each row with a wave.
+// Rows (D > 1) zero the tensor, then a thread per 16 bytes (or value) of
+// every row copies it.
 constexpr int SC_W = 4096;          // keys per window
 constexpr int SC_CUR_BLOCKS = 4096; // blocks of the cursor pass, one flag word each
 constexpr int SC_FIX_BLOCKS = 128;  // blocks of the per-entry pass
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(256) void scatter_window_kernel(ScatterParams s)
 }
 
 // the plain scatter: every entry's value to its key (for D == 1 only when a
-// flag word of the cursor pass is set); rows of D > 1 with a wave each
+// flag word of the cursor pass is set; D == 0 checks the keys only)
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams s)
 {
     if (s.bad) {
@@ -775,27 +776,43 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams s)
     uint64_t b = s.off[0], e = s.off[s.P];
     if (e > s.capacity) e = s.capacity;
     if (b > e) b = e;
-    if (s.D <= 1) {
-        for (uint64_t i = b + blockIdx.x * 256ull + threadIdx.x; i < e; i += (uint64_t)gridDim.x * 256) {
-            const uint32_t x = s.idx[i];
-            if (x >= s.M) {
-                report_error(kDevErrIndexRange);
-                continue;
-            }
-            if (s.D == 1) s.dense[x] = s.val[i];
+    for (uint64_t i = b + blockIdx.x * 256ull + threadIdx.x; i < e; i += (uint64_t)gridDim.x * 256) {
+        const uint32_t x = s.idx[i];
+        if (x >= s.M) {
+            report_error(kDevErrIndexRange);
+            continue;
         }
-    } else {
-        // rows: one wave per entry, lanes across the row
-        const uint32_t lane = lane_id();
-        for (uint64_t i = b + (blockIdx.x * 256ull + threadIdx.x) / SG_WAVE; i < e;
-             i += (uint64_t)gridDim.x * (256 / SG_WAVE)) {
-            const uint32_t x = s.idx[i];
-            if (x >= s.M) {
-                if (lane == 0) report_error(kDevErrIndexRange);
-                continue;
-            }
-            for (uint32_t c = lane; c < s.D; c += SG_WAVE) s.dense[(uint64_t)x * s.D + c] = s.val[i * s.D + c];
+        if (s.D == 1) s.dense[x] = s.val[i];
+    }
+}
+
+// rows of D > 1: a thread per 16 bytes of a row (VEC: D a multiple of 4 and
+// the values 16-byte aligned) or per value, the grid over every thread of
+// the entries held, so each thread makes one index load, one value load and
+// one store (a wave per row walking many rows waits on each row in turn)
+template <bool VEC>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(ScatterParams s)
+{
+    uint64_t b = s.off[0], e = s.off[s.P];
+    if (e > s.capacity) e = s.capacity;
+    if (b > e) b = e;
+    const uint32_t per = VEC ? s.D / 4 : s.D; // threads per row
+    const uint64_t n = (e - b) * per;
+    const bool narrow = n <= 0xffffffffull; // 32-bit division
+    for (uint64_t t = blockIdx.x * 256ull + threadIdx.x; t < n; t += (uint64_t)gridDim.x * 256) {
+        const uint64_t r = narrow ? (uint64_t)((uint32_t)t / per) : t / per;
+        const uint32_t c = (uint32_t)(t - r * per);
+        const uint64_t i = b + r;
+        const uint32_t x = s.idx[i];
+        if (x >= s.M) {
+            if (c == 0) report_error(kDevErrIndexRange);
+            continue;
         }
+        if (VEC)
+            reinterpret_cast<float4*>(s.dense + (uint64_t)x * s.D)[c] =
+                reinterpret_cast<const float4*>(s.val + i * s.D)[c];
+        else
+            s.dense[(uint64_t)x * s.D + c] = s.val[i * s.D + c];
     }
 }
 
@@ -966,7 +983,15 @@ extern "C" int sg_scatter_dense(const uint32_t* d_idx, const float* d_val, uint3
     SG_TRY_LAUNCH();
     if (capacity > 0) {
         probe_begin(SG_PROBE_SCATTER, st);
-        scatter_kernel<<<(unsigned)(ceil_div(capacity, 256) < 8192 ? ceil_div(capacity, 256) : 8192), 256, 0, st>>>(s);
+        if (D > 1) {
+            const bool vec = D % 4 == 0 && (uintptr_t)d_val % 16 == 0;
+            const uint64_t nb = ceil_div(capacity * (vec ? D / 4 : D), 256);
+            const unsigned blocks = (unsigned)(nb < 65536 ? nb : 65536);
+            if (vec) scatter_rows_kernel<true><<<blocks, 256, 0, st>>>(s);
+            else scatter_rows_kernel<false><<<blocks, 256, 0, st>>>(s);
+        } else {
+            scatter_kernel<<<(unsigned)(ceil_div(capacity, 256) < 8192 ? ceil_div(capacity, 256) : 8192), 256, 0, st>>>(s);
+        }
         SG_TRY_LAUNCH();
         probe_end(SG_PROBE_SCATTER, st);
     }

@@ -181,6 +181,35 @@ def test_scatter_dense_matches_oracle(D):
     assert sg.sg_device_error() == 0
 
 
+@pytest.mark.parametrize("D,shift", [(8, 1), (6, 0), (4, 0), (132, 0)])
+def test_scatter_dense_rows_layouts(D, shift):
+    """Rows copied 16 bytes per thread (D a multiple of 4, aligned values) or
+    a value per thread (D not a multiple of 4, or values starting 4 bytes
+    past a 16-byte boundary); a truncated last row range and a short
+    capacity."""
+    need_gpu()
+    rng = np.random.default_rng(D * 7 + shift)
+    M, P = 50021, 4
+    a, o = _agg_of(np.flatnonzero(rng.random(M) < 0.2), P, 2)
+    vals = rng.standard_normal((a.size, D)).astype(np.float32)
+    buf = torch.empty(a.size * D + shift, dtype=torch.float32, device="cuda")
+    buf[shift:] = torch.from_numpy(vals.reshape(-1)).cuda()
+    dv = buf[shift:].view(a.size, D)
+    assert (dv.data_ptr() % 16 != 0) == (shift != 0)
+    dense = sg.sg_scatter_dense(to_dev_u32(a), dv, to_dev_u64(o), M, D=D)
+    torch.cuda.synchronize()
+    want = oracle.scatter_dense(a, vals, o, M, D)
+    assert np.array_equal(host_bits(dense).reshape(-1), want.reshape(-1).view(np.uint32))
+    # entries past off[P] are not written
+    o2 = o.copy()
+    o2[-1] -= np.uint64(5)
+    dense = sg.sg_scatter_dense(to_dev_u32(a), dv, to_dev_u64(o2), M, D=D)
+    torch.cuda.synchronize()
+    want = oracle.scatter_dense(a[:-5], vals[:-5], o2, M, D)
+    assert np.array_equal(host_bits(dense).reshape(-1), want.reshape(-1).view(np.uint32))
+    assert sg.sg_device_error() == 0
+
+
 def _scatter_case(name):
     """(idx, val, off, M, capacity) of a scatter edge case; entries outside
     [off[0], off[P]) hold junk keys that must not be written."""
