@@ -162,6 +162,9 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
     for (int pass = 0; pass < 2 && top > 0; ++pass) {
         const uint32_t shift = top > (uint32_t)TK_DIGIT_BITS ? top - TK_DIGIT_BITS : 0u;
         const uint32_t width = top - shift;
+        // both ranks under one prefix (always in the first pass, and in the
+        // second when they share a top digit): one histogram serves both
+        const bool same = prefix[0] == prefix[1]; // uniform
         for (uint32_t i = threadIdx.x; i < 2 * TK_BINS; i += 1024) (&hist[0][0])[i] = 0;
         __syncthreads();
         for (uint32_t i0 = 0; i0 < S; i0 += 1024) { // uniform: the waves' ballots below
@@ -170,15 +173,18 @@ __global__ __launch_bounds__(1024) void topk_sample_kernel(TopkParams p)
             const uint32_t key = valid ? s[i] : 0u;
             const uint32_t d = (key >> shift) & ((1u << width) - 1u);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                if (t == 1 && same) continue;
                 hist_add_wave(hist[t], valid && (top >= 32 ? 0u : (key >> top)) == (top >= 32 ? 0u : (prefix[t] >> top)),
                               d);
+            }
         }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+            const uint32_t* ht = hist[same ? 0 : t];
             const uint32_t d0 = 2 * threadIdx.x;
-            const uint32_t c0 = hist[t][d0], c1 = hist[t][d0 + 1];
+            const uint32_t c0 = ht[d0], c1 = ht[d0 + 1];
             uint32_t tot;
             const uint32_t ex = block_excl_scan<1024>(c0 + c1, scan_lds, &tot);
             if (ex < R[t] && R[t] <= ex + c0) {
