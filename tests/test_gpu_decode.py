@@ -150,6 +150,15 @@ def test_decode_capacity_short(M, P):
     assert sg.sg_device_error() == 0
 
 
+def test_decode_config4_full():
+    # the skewed 2^28-key workload's aggregate (16 classes: the group decode
+    # with groups of 4 windows), from the oracle, through encode and decode
+    c = gen.config4()
+    oi, _, po = oracle.hash_partition(c["idx"], None, c["in_off"], c["P"], c["seed"])
+    ai, _, _, ao = oracle.aggregate(oi, None, po, c["M"])
+    _roundtrip(ai, ao, c["M"], c["seed"])
+
+
 def test_decode_config3_aggregate():
     # the DGC-style workload's aggregate, from the oracle, through encode and decode
     c = gen.config3(rows=512, cols=11008)
